@@ -1,0 +1,145 @@
+// Launch argument structs passed by value from the host layer to kernels,
+// and the host-side launcher declarations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+constexpr int kMaxGroups = 64;   // KV heads supported per call
+
+// The KV groups a kernel works on (retrieval, routed or local groups).
+struct GroupList {
+  int32_t n;
+  int32_t ids[kMaxGroups];
+};
+
+// ---------------------------------------------------------------- index
+struct IndexLowrankArgs {
+  const void* k_pre;     // [B,Hkv,n_cap,d]
+  const void* q_pre;     // [B,Hq,d] or nullptr
+  const float* proj_q;   // [Hkv,16,d]
+  const float* proj_k;   // [Hkv,16,d]
+  void* k_idx;           // [B,Hkv,n_cap,16]
+  float* q_idx;          // [B,Hq,16]
+  int32_t B, Hq, Hkv, n_cap, G, t0, t1;
+  GroupList groups;
+};
+
+struct SummaryArgs {
+  const void* k_pre;     // [B,Hkv,n_cap,d]
+  void* chunk_sum;       // [B,Hkv,n_cap/chunk,d]
+  void* group_sum;       // [B,Hkv,n_cap/group,d]
+  int32_t B, Hkv, n_cap, chunk, group;
+  int32_t c0, c1;        // chunk range [c0, c1) to build
+  int32_t g0, g1;        // group range [g0, g1) to build
+  double rope_base;
+  GroupList groups;
+};
+
+struct PyramidArgs {
+  const void* q; const void* k; const void* v;     // [B,H,N,d]
+  void* pq; void* pk; void* pv;                    // [B,H,Nc,d]
+  float* scores;                                   // [B,H,Nt]
+  int32_t B, H, N, levels, factor, Nc, Nt;
+};
+
+// ---------------------------------------------------------------- select
+// Per-row (sequence, retrieval group) state of the radix selector.
+struct RowState {
+  double R;             // reference logit: masses are exp(l - R)
+  double target_mass;   // p * total mass
+  double mass_above;    // mass of tokens above the current key prefix
+  int64_t count_above;  // tokens above the current key prefix
+  int32_t target_count; // min_tokens or k
+  uint32_t prefix;      // key bits fixed so far
+  int32_t crit;         // bit0: mass criterion live, bit1: count criterion live
+  int32_t all;          // 1: every token is selected
+  uint32_t cut_key;     // final key of the last selected token
+  int32_t need;         // tokens taken among those whose key == cut_key
+  int32_t m;            // selected count
+  int32_t err;
+};
+
+struct SelectArgs {
+  const float* q_idx;    // [B,Hq,16]
+  const void* k_idx;     // [B,Hkv,n_cap,16]
+  int32_t* sel_idx;      // [B,Hkv,n_cap]
+  int32_t* sel_count;    // [B,Hkv]
+  int32_t B, Hq, Hkv, n, n_cap, G;
+  int32_t use_mass;      // 1 = top-p, 0 = top-k
+  int32_t select_all;    // every token is kept (no ranking needed)
+  double top_p;
+  int32_t target_count;  // top-k: k ; top-p: min_tokens (0 = none)
+  int32_t tiles;         // tiles per row
+  int64_t row_stride;    // logits stride per row (tiles * tile)
+  // workspace
+  float* logits;         // [rows, row_stride]
+  uint32_t* cnt1; double* mass1;   // [rows, 4096]
+  uint32_t* cnt2; double* mass2;   // [rows, 4096]
+  uint32_t* cnt3; double* mass3;   // [rows, 256]
+  RowState* state;       // [rows]
+  uint32_t* done;        // [rows, 4]
+  uint64_t* lookback;    // [rows, tiles]
+  GroupList groups;
+};
+
+struct RouteArgs {
+  const void* q;          // [B,Hq,d] post-RoPE
+  const void* chunk_sum;  // [B,Hkv,n_cap/chunk,d]
+  const void* group_sum;  // [B,Hkv,n_cap/group,d]
+  int32_t* sel_idx; int32_t* sel_count;
+  int32_t B, Hq, Hkv, n, n_cap, G, chunk, group, top_chunks, top_groups,
+      sink_chunks, local_chunks;
+  int32_t n_cs_cap, n_gs_cap;   // rows per (b,g) in chunk_sum / group_sum
+  float* scratch;               // [rows, n_cs_cap] chunk scores
+  GroupList groups;
+};
+
+struct PyrSelectArgs {
+  const float* scores;   // [B,H,Nt]
+  int32_t* blk_idx;      // [B,H,nblk,K]
+  int32_t* blk_count;    // [B,H,nblk]
+  int32_t B, H, N, levels, factor, q_block, K, nblk, Nt;
+  uint32_t* ws;          // scratch
+  int64_t ws_per_head;
+};
+
+// ---------------------------------------------------------------- attention
+struct DecodeArgs {
+  const void* q;          // [B,Hq,d]
+  const void* k;          // [B,Hkv,n_cap,d]
+  const void* v;
+  const int32_t* sel_idx; // [B,Hkv,n_cap]
+  const int32_t* sel_count;
+  float* out;             // [B,Hq,d]
+  float* partial;         // [B,Hq,max_splits,d+2]
+  uint32_t* counters;     // [B,Hkv] finished splits (zero between calls)
+  int32_t B, Hq, Hkv, n, n_cap, G, sinks, window;
+  int32_t tps;            // tokens per split
+  int32_t max_splits;
+  float scale_log2;       // log2(e) / sqrt(d)
+  uint64_t local_mask;    // bit g set: group g is local
+};
+
+struct PrefillArgs {
+  const void* q; const void* k; const void* v;   // [B,H,N,d]
+  const void* pk; const void* pv;                // [B,H,Nc,d]
+  const int32_t* blk_idx; const int32_t* blk_count;
+  float* out;                                    // [B,H,N,d]
+  int32_t B, H, N, Nc, nblk, K, q_block;
+  float scale_log2;
+};
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_index_lowrank(const IndexLowrankArgs& a, int dtype, int d, hipStream_t s);
+hipError_t launch_summary(const SummaryArgs& a, int dtype, int d, hipStream_t s);
+hipError_t launch_pyramid(const PyramidArgs& a, int dtype, int d, hipStream_t s);
+hipError_t launch_select_lowrank(const SelectArgs& a, int dtype, hipStream_t s);
+hipError_t launch_route(const RouteArgs& a, int dtype, int d, hipStream_t s);
+hipError_t launch_pyramid_select(const PyrSelectArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, int d, hipStream_t s);
+
+}  // namespace sa

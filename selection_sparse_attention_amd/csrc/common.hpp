@@ -1,0 +1,151 @@
+// Device helpers shared by the gfx950 kernels: element access, order-keys
+// for radix selection, wave/block reductions, and launch argument structs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- elements
+// bf16 values are handled as raw 16-bit patterns: widening is a shift, and
+// narrowing rounds to nearest even.
+struct bf16_t { uint16_t v; };
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);   // round to nearest, ties to even
+  return uint16_t(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<bf16_t> {
+  static constexpr int bytes = 2;
+  __device__ static float load(const void* p, int64_t i) {
+    return bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+  }
+  __device__ static void store(void* p, int64_t i, float x) {
+    reinterpret_cast<uint16_t*>(p)[i] = f32_to_bf16(x);
+  }
+};
+template <> struct Elem<float> {
+  static constexpr int bytes = 4;
+  __device__ static float load(const void* p, int64_t i) {
+    return reinterpret_cast<const float*>(p)[i];
+  }
+  __device__ static void store(void* p, int64_t i, float x) {
+    reinterpret_cast<float*>(p)[i] = x;
+  }
+};
+
+// Load N consecutive elements starting at element offset i (16-byte chunks;
+// the caller guarantees alignment) and widen them to fp32.
+template <typename T, int N> struct VecLoad;
+template <int N> struct VecLoad<bf16_t, N> {
+  static_assert(N % 8 == 0 || N == 4, "bf16 vector loads are 8 or 4 elements");
+  __device__ static void run(const void* base, int64_t i, float* out) {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(base) + i;
+    if constexpr (N == 4) {
+      uint2 w = *reinterpret_cast<const uint2*>(p);
+      out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x);
+      out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
+    } else {
+#pragma unroll
+      for (int c = 0; c < N / 8; ++c) {
+        uint4 w = *reinterpret_cast<const uint4*>(p + 8 * c);
+        out[8 * c + 0] = bf16_lo(w.x); out[8 * c + 1] = bf16_hi(w.x);
+        out[8 * c + 2] = bf16_lo(w.y); out[8 * c + 3] = bf16_hi(w.y);
+        out[8 * c + 4] = bf16_lo(w.z); out[8 * c + 5] = bf16_hi(w.z);
+        out[8 * c + 6] = bf16_lo(w.w); out[8 * c + 7] = bf16_hi(w.w);
+      }
+    }
+  }
+};
+template <int N> struct VecLoad<float, N> {
+  static_assert(N % 4 == 0, "fp32 vector loads are multiples of 4 elements");
+  __device__ static void run(const void* base, int64_t i, float* out) {
+    const float* p = reinterpret_cast<const float*>(base) + i;
+#pragma unroll
+    for (int c = 0; c < N / 4; ++c) {
+      float4 w = *reinterpret_cast<const float4*>(p + 4 * c);
+      out[4 * c + 0] = w.x; out[4 * c + 1] = w.y; out[4 * c + 2] = w.z; out[4 * c + 3] = w.w;
+    }
+  }
+};
+
+// ---------------------------------------------------------------- order keys
+// Monotone map float -> uint32: a > b  <=>  key(a) > key(b) for finite
+// values (+0 and -0 are folded to the same key by the caller).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// ---------------------------------------------------------------- reductions
+template <typename T>
+__device__ __forceinline__ T shfl_xor(T v, int m, int width = kWave) {
+  return __shfl_xor(v, m, width);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// Exclusive prefix sum over a block of NT threads (NT a multiple of 64),
+// using `scratch` (NT/64 entries of T in LDS).  Returns the exclusive value
+// and writes the block total to *total.
+template <typename T, int NT>
+__device__ __forceinline__ T block_exclusive_scan(T v, T* scratch, T* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  T incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    T y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) scratch[wid] = incl;
+  __syncthreads();
+  T base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    T s = scratch[w];
+    if (w < wid) base += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - v;
+}
+
+// Agent-scope relaxed atomics used for cross-workgroup counters.
+__device__ __forceinline__ uint64_t ld_agent(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double ld_agent(const double* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace sa
