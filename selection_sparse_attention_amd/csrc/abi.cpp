@@ -117,7 +117,7 @@ constexpr int kSelTile = 1024;
 
 struct SelectWs {
   float* logits; uint32_t* cnt1; double* mass1; uint32_t* cnt2; double* mass2;
-  uint32_t* cnt3; double* mass3; sa::RowState* state; uint32_t* done; uint64_t* lookback;
+  uint32_t* cnt3; double* mass3; sa::RowState* state; uint64_t* lookback;
   int tiles; int64_t row_stride; size_t bytes;
 };
 
@@ -134,14 +134,15 @@ SelectWs carve_select(void* ws, int rows, int n) {
   s.cnt3 = c.take<uint32_t>((size_t)rows * 256);
   s.mass3 = c.take<double>((size_t)rows * 256);
   s.state = c.take<sa::RowState>((size_t)rows);
-  s.done = c.take<uint32_t>((size_t)rows * 4);
   s.lookback = c.take<uint64_t>((size_t)rows * s.tiles);
   s.bytes = c.size();
   return s;
 }
 
 // ---------------------------------------------------------------- decode ws
-constexpr int kDecodeTps = 256;
+constexpr int kDecodeTps = 256;           // fp32 caches: list entries per split
+constexpr int kDecodeTpsMfma = 256;       // bf16 caches
+constexpr int kMaxDecodeSplits = 8192;     // contexts up to 2M tokens
 
 int decode_max_count(const sa_params* p, const int8_t* kinds) {
   int mc = 0;
@@ -289,7 +290,7 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
     }
     a.tiles = sw.tiles; a.row_stride = sw.row_stride;
     a.logits = sw.logits; a.cnt1 = sw.cnt1; a.mass1 = sw.mass1; a.cnt2 = sw.cnt2; a.mass2 = sw.mass2;
-    a.cnt3 = sw.cnt3; a.mass3 = sw.mass3; a.state = sw.state; a.done = sw.done;
+    a.cnt3 = sw.cnt3; a.mass3 = sw.mass3; a.state = sw.state;
     a.lookback = sw.lookback; a.groups = gl;
     return hip_status(sa::launch_select_lowrank(a, p->dtype, s));
   }
@@ -298,14 +299,19 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
     const int gpc = p->chunk / p->group;
     if (p->top_chunks < 1 || p->top_groups < 1 || p->top_groups > gpc) return SA_ERR_INVALID_ARG;
     if (p->sink_chunks < 0 || p->local_chunks < 0) return SA_ERR_INVALID_ARG;
-    if (p->top_chunks > 256 || gpc > 64) return SA_ERR_UNSUPPORTED;
+    if (p->top_chunks > 256 || gpc > 64 || p->top_chunks * p->top_groups > 4096)
+      return SA_ERR_UNSUPPORTED;
     if (p->n_ctx / p->chunk > 16384) return SA_ERR_UNSUPPORTED;
     GroupList gl = groups_of_kind(p, kinds, SA_HEAD_ROUTED);
     Carver c(ws);
     c.take<uint32_t>(1);
     if ((st = workspace_gate(ws, ws_bytes, c.size()))) return st < 0 ? st : SA_OK;
     if (gl.n == 0) return SA_OK;
-    if (!b->q || !b->chunk_sum || !b->group_sum || !b->sel_idx || !b->sel_count) return SA_ERR_INVALID_ARG;
+    // summaries are read only when some complete chunk can be a candidate
+    const int kappa = (p->n_ctx - 1) / p->chunk;
+    const bool has_cand = kappa - p->local_chunks > p->sink_chunks;
+    if (!b->q || !b->sel_idx || !b->sel_count) return SA_ERR_INVALID_ARG;
+    if (has_cand && (!b->chunk_sum || !b->group_sum)) return SA_ERR_INVALID_ARG;
     sa::RouteArgs a{};
     a.q = b->q; a.chunk_sum = b->chunk_sum; a.group_sum = b->group_sum;
     a.sel_idx = b->sel_idx; a.sel_count = b->sel_count;
@@ -336,9 +342,10 @@ int32_t sparse_attn_decode(const sa_params* p, const sa_buffers* b, void* ws, si
   if (any_local && (p->sinks < 0 || p->window < 0 || (int64_t)p->sinks + p->window < 1))
     return SA_ERR_INVALID_ARG;
   const int max_count = decode_max_count(p, kinds);
-  const int max_splits = (max_count + kDecodeTps - 1) / kDecodeTps;
+  const int tps = (p->dtype == SA_BF16) ? kDecodeTpsMfma : kDecodeTps;
+  const int max_splits = (max_count + tps - 1) / tps;
+  if (max_splits > kMaxDecodeSplits) return SA_ERR_UNSUPPORTED;
   Carver c(ws);
-  uint32_t* counters = c.take<uint32_t>((size_t)p->batch * p->n_kv_heads);
   float* partial = c.take<float>((size_t)p->batch * p->n_q_heads * max_splits * (p->head_dim + 2));
   if ((st = workspace_gate(ws, ws_bytes, c.size()))) return st < 0 ? st : SA_OK;
   if (!b->q || !b->k_cache || !b->v_cache || !b->out) return SA_ERR_INVALID_ARG;
@@ -346,9 +353,9 @@ int32_t sparse_attn_decode(const sa_params* p, const sa_buffers* b, void* ws, si
   if (!aligned16(b->q) || !aligned16(b->k_cache) || !aligned16(b->v_cache)) return SA_ERR_INVALID_ARG;
   sa::DecodeArgs a{};
   a.q = b->q; a.k = b->k_cache; a.v = b->v_cache; a.sel_idx = b->sel_idx; a.sel_count = b->sel_count;
-  a.out = b->out; a.partial = partial; a.counters = counters;
+  a.out = b->out; a.partial = partial;
   a.B = p->batch; a.Hq = p->n_q_heads; a.Hkv = p->n_kv_heads; a.n = p->n_ctx; a.n_cap = p->n_cap;
-  a.G = G; a.sinks = p->sinks; a.window = p->window; a.tps = kDecodeTps; a.max_splits = max_splits;
+  a.G = G; a.sinks = p->sinks; a.window = p->window; a.tps = tps; a.max_splits = max_splits;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->head_dim));
   a.local_mask = local_mask;
   return hip_status(sa::launch_decode(a, p->dtype, p->head_dim, static_cast<hipStream_t>(stream)));

@@ -8,6 +8,7 @@
 namespace sa {
 
 constexpr int kMaxGroups = 64;   // KV heads supported per call
+constexpr int kMaxTps = 1024;    // decode: most list entries per split
 
 // The KV groups a kernel works on (retrieval, routed or local groups).
 struct GroupList {
@@ -80,7 +81,6 @@ struct SelectArgs {
   uint32_t* cnt2; double* mass2;   // [rows, 4096]
   uint32_t* cnt3; double* mass3;   // [rows, 256]
   RowState* state;       // [rows]
-  uint32_t* done;        // [rows, 4]
   uint64_t* lookback;    // [rows, tiles]
   GroupList groups;
 };
@@ -115,7 +115,6 @@ struct DecodeArgs {
   const int32_t* sel_count;
   float* out;             // [B,Hq,d]
   float* partial;         // [B,Hq,max_splits,d+2]
-  uint32_t* counters;     // [B,Hkv] finished splits (zero between calls)
   int32_t B, Hq, Hkv, n, n_cap, G, sinks, window;
   int32_t tps;            // tokens per split
   int32_t max_splits;
@@ -140,6 +139,7 @@ hipError_t launch_select_lowrank(const SelectArgs& a, int dtype, hipStream_t s);
 hipError_t launch_route(const RouteArgs& a, int dtype, int d, hipStream_t s);
 hipError_t launch_pyramid_select(const PyrSelectArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int d, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int d, hipStream_t s);
 
 }  // namespace sa

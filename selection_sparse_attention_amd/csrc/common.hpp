@@ -24,6 +24,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return uint16_t(u >> 16);
 }
 
+// Round a double once to the nearest bf16 (ties to even), for normal values
+// in range: the low 45 bits of the double's significand are rounded away.
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+  uint64_t u = __double_as_longlong(x);
+  u += 0x0FFFFFFFFFFFull + ((u >> 45) & 1ull);
+  u &= ~0x1FFFFFFFFFFFull;
+  return uint16_t(__float_as_uint((float)__longlong_as_double(u)) >> 16);
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<bf16_t> {
   static constexpr int bytes = 2;
@@ -33,6 +42,9 @@ template <> struct Elem<bf16_t> {
   __device__ static void store(void* p, int64_t i, float x) {
     reinterpret_cast<uint16_t*>(p)[i] = f32_to_bf16(x);
   }
+  __device__ static void store_d(void* p, int64_t i, double x) {
+    reinterpret_cast<uint16_t*>(p)[i] = f64_to_bf16(x);
+  }
 };
 template <> struct Elem<float> {
   static constexpr int bytes = 4;
@@ -41,6 +53,9 @@ template <> struct Elem<float> {
   }
   __device__ static void store(void* p, int64_t i, float x) {
     reinterpret_cast<float*>(p)[i] = x;
+  }
+  __device__ static void store_d(void* p, int64_t i, double x) {
+    reinterpret_cast<float*>(p)[i] = (float)x;
   }
 };
 

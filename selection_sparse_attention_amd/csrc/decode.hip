@@ -11,10 +11,13 @@
 // on 4 rows at a time, 16 lanes per row, each lane owning d/16 consecutive
 // dims; it keeps 4 rows x U rounds of loads in flight before computing.  The
 // (m, l, acc) state is merged across lane groups with shuffles, across waves
-// through LDS, and written as a split partial; the last workgroup of a group
-// to finish (a per-group counter) merges that group's splits and writes the
-// outputs, and resets the counter to zero for the next call.  Scores use exp2
-// with log2(e)/sqrt(d) folded into the scale.
+// through LDS, and written as a split partial.  A second launch merges each
+// head's splits, every thread owning one output dim and a share of the splits.
+// (Cross-workgroup merging at the kernel boundary avoids agent-scope fences,
+// each of which writes back the whole L2 of its die on this chip.)  Scores use
+// exp2 with log2(e)/sqrt(d) folded into the scale.
+#include <type_traits>
+
 #include "args.hpp"
 #include "common.hpp"
 
@@ -22,6 +25,7 @@ namespace sa {
 
 constexpr int kDecThreads = 256;
 constexpr int kDecRounds = 4;        // rows in flight per lane group
+constexpr int kMaxSplitsLds = 8192;  // splits merged by one combine workgroup
 
 __device__ __forceinline__ float safe_exp2_diff(float x, float m) {
   return (x == -INFINITY) ? 0.f : exp2f(x - m);
@@ -45,14 +49,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a)
     count = min(max(a.sel_count[(int64_t)b * a.Hkv + g], 0), n);
   }
   const int start = split * a.tps;
-  if (count == 0 && split == 0) {            // nothing visible: a zero output
-    for (int idx = tid; idx < G * D; idx += kDecThreads)
-      a.out[((int64_t)b * a.Hq + g * G) * D + idx] = 0.f;
-    return;
-  }
   if (start >= count) return;
   const int end = min(count, start + a.tps);
-  const int nsplit = (count + a.tps - 1) / a.tps;
 
   float q[G][EPL];
 #pragma unroll
@@ -168,46 +166,78 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a)
     pp[e] = av;
     if (e == 0) { pp[D] = M; pp[D + 1] = lv; }
   }
+}
 
-  // the group's last split merges every split's (m, l, acc)
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t* ctr = a.counters + (int64_t)b * a.Hkv + g;
-    const uint32_t prev = atomicAdd(ctr, 1u);
-    s_last = (prev == (uint32_t)nsplit - 1);
-    if (s_last) atomicExch(ctr, 0u);
+// Merge the splits of one (sequence, query head): weights 2^(m_s - M) per
+// split, then every thread sums one output dim over its share of the splits.
+template <int D>
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
+  constexpr int P = 256 / D;                 // split shares per output dim
+  __shared__ float s_w[kMaxSplitsLds];
+  __shared__ float s_red[256];
+  __shared__ float s_M, s_L;
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int b = bh / a.Hq, h = bh % a.Hq, g = h / a.G;
+  int count;
+  if ((a.local_mask >> g) & 1ull) {
+    const int s_eff = min(a.sinks, a.n);
+    count = s_eff + (a.n - max(s_eff, a.n - a.window));
+  } else {
+    count = min(max(a.sel_count[(int64_t)b * a.Hkv + g], 0), a.n);
   }
+  const int ns = (count + a.tps - 1) / a.tps;
+  const float* base = a.partial + (int64_t)bh * a.max_splits * (D + 2);
+  float mx = -INFINITY;
+  for (int sp = tid; sp < ns; sp += 256) mx = fmaxf(mx, base[(int64_t)sp * (D + 2) + D]);
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) s_red[tid >> 6] = mx;
   __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  for (int idx = tid; idx < G * D; idx += kDecThreads) {
-    const int h = idx / D, e = idx % D;
-    const float* base = a.partial + ((int64_t)b * a.Hq + g * G + h) * a.max_splits * (D + 2);
-    float M = -INFINITY;
-    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, __builtin_nontemporal_load(base + (int64_t)sp * (D + 2) + D));
-    float av = 0.f, lv = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float* q = base + (int64_t)sp * (D + 2);
-      const float wt = safe_exp2_diff(__builtin_nontemporal_load(q + D), M);
-      av += wt * __builtin_nontemporal_load(q + e);
-      lv += wt * __builtin_nontemporal_load(q + D + 1);
-    }
-    a.out[((int64_t)b * a.Hq + g * G + h) * D + e] = (lv > 0.f) ? av / lv : 0.f;
+  if (tid == 0) s_M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  __syncthreads();
+  const float M = s_M;
+  float lsum = 0.f;
+  for (int sp = tid; sp < ns; sp += 256) {
+    const float* q = base + (int64_t)sp * (D + 2);
+    const float w = (q[D] == -INFINITY) ? 0.f : exp2f(q[D] - M);
+    s_w[sp] = w;
+    lsum += w * q[D + 1];
+  }
+  lsum = wave_sum(lsum);
+  __syncthreads();
+  if ((tid & 63) == 0) s_red[tid >> 6] = lsum;
+  __syncthreads();
+  if (tid == 0) s_L = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+  __syncthreads();
+  const int e = tid % D, part = tid / D;
+  float acc = 0.f;
+#pragma unroll 8
+  for (int sp = part; sp < ns; sp += P) acc = fmaf(s_w[sp], base[(int64_t)sp * (D + 2) + e], acc);
+  s_red[tid] = acc;
+  __syncthreads();
+  if (part == 0) {
+    float v = acc;
+#pragma unroll
+    for (int q = 1; q < P; ++q) v += s_red[q * D + e];
+    const float L = s_L;
+    a.out[(int64_t)bh * D + e] = (L > 0.f) ? v / L : 0.f;
   }
 }
 
 template <typename T, int D>
 static hipError_t run_decode(const DecodeArgs& a, hipStream_t s) {
   dim3 grid(a.max_splits, a.Hkv, a.B);
-  switch (a.G) {
+  if (std::is_same<T, bf16_t>::value) {        // bf16 caches: matrix-core kernel
+    const hipError_t e = launch_decode_mfma(a, D, s);
+    if (e != hipSuccess) return e;
+  } else switch (a.G) {
     case 1: hipLaunchKernelGGL((decode_split_kernel<T, D, 1>), grid, dim3(kDecThreads), 0, s, a); break;
     case 2: hipLaunchKernelGGL((decode_split_kernel<T, D, 2>), grid, dim3(kDecThreads), 0, s, a); break;
     case 4: hipLaunchKernelGGL((decode_split_kernel<T, D, 4>), grid, dim3(kDecThreads), 0, s, a); break;
     case 8: hipLaunchKernelGGL((decode_split_kernel<T, D, 8>), grid, dim3(kDecThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
+  if (a.max_splits > kMaxSplitsLds) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.Hq), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

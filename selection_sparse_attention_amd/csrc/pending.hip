@@ -2,8 +2,6 @@
 #include "args.hpp"
 
 namespace sa {
-hipError_t launch_summary(const SummaryArgs&, int, int, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_route(const RouteArgs&, int, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_pyramid(const PyramidArgs&, int, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_pyramid_select(const PyrSelectArgs&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_prefill(const PrefillArgs&, int, hipStream_t) { return hipErrorNotSupported; }

@@ -1,0 +1,202 @@
+// Two-level routing of the decode query over chunk and group key summaries
+// (HGA summary, Core mechanism item 2).
+//
+// For each (sequence b, routed KV group g), with t = n - 1 and kappa = t / C:
+//   * qbar = mean of the group's post-RoPE query heads;
+//   * level 1: every complete chunk c in [sink_chunks, kappa - local_chunks)
+//     is scored by qbar . chunk_sum[c]; the top_chunks highest (ties to the
+//     lower chunk) are kept;
+//   * level 2: inside each kept chunk the top_groups groups by
+//     qbar . group_sum (ties to the lower group);
+//   * the visible list is the union of the sink chunks [0, sink_chunks), the
+//     local chunks [kappa - local_chunks, kappa), the current chunk's tokens
+//     kappa*C .. t, and the routed groups' tokens - written ascending.
+// Scores are ranked on the raw dot product: dividing by sqrt(d) does not
+// change the order.
+//
+// One 256-thread workgroup per (KV group, sequence).  Rows are scored with 16
+// lanes each (d/16 elements per lane, a 16-lane DPP reduction), chunk scores
+// stay in LDS, and the top chunks are extracted by repeated block-wide arg-max
+// over (score key, inverted index) 64-bit keys.
+#include <algorithm>
+
+#include "args.hpp"
+#include "common.hpp"
+
+namespace sa {
+
+constexpr int kRouteThreads = 256;
+constexpr int kMaxRoutedGroups = 4096;     // top_chunks * top_groups
+
+template <int CTRL>
+__device__ __forceinline__ float rdpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum_r(float v) {
+  v += rdpp<0x128>(v);
+  v += rdpp<0x124>(v);
+  v += rdpp<0x122>(v);
+  v += rdpp<0x121>(v);
+  return v;
+}
+
+// Scores qbar . rows[r] for r in [0, nrows) into out[r]; rows are d wide.
+template <typename T, int D>
+__device__ void score_rows(const void* base, int64_t row_of0, int nrows, const float* s_q,
+                           float* out, const int* row_map) {
+  constexpr int EPL = D / 16;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int sub = lane & 15, rg = lane >> 4;
+  float q[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) q[e] = s_q[sub * EPL + e];
+  for (int r0 = 0; r0 < nrows; r0 += 16) {
+    const int r = r0 + wid * 4 + rg;
+    float p = 0.f;
+    if (r < nrows) {
+      const int64_t row = row_map ? (int64_t)row_map[r] : (row_of0 + r);
+      float kv[EPL];
+      VecLoad<T, EPL>::run(base, row * D + sub * EPL, kv);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) p = fmaf(q[e], kv[e], p);
+    }
+    p = row16_sum_r(p);
+    if (r < nrows && sub == 0) out[r] = p;
+  }
+}
+
+__device__ __forceinline__ uint64_t score_key(float s, int idx) {
+  if (s == 0.f) s = 0.f;
+  return ((uint64_t)order_key(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
+  extern __shared__ float dyn[];                 // chunk scores, then group scores
+  __shared__ float s_q[D];
+  __shared__ uint32_t s_taken[16384 / 32];
+  __shared__ int s_chunks[256], s_sorted[256];
+  __shared__ int s_groups[kMaxRoutedGroups];
+  __shared__ uint64_t s_red[kRouteThreads / 64];
+  __shared__ int s_rowmap[kMaxRoutedGroups];
+  const int gi = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int g = a.groups.ids[gi];
+  const int n = a.n, C = a.chunk, GR = a.group, gpc = C / GR;
+  const int t = n - 1, kappa = t / C;
+  const int c_lo = a.sink_chunks;
+  const int c_hi = max(c_lo, kappa - a.local_chunks);
+  const int ncand = c_hi - c_lo;
+  const int nT = min(a.top_chunks, ncand);
+  const int TG = a.top_groups;
+
+  for (int e = tid; e < D; e += kRouteThreads) {
+    float s = 0.f;
+    for (int h = 0; h < a.G; ++h) s += Elem<T>::load(a.q, ((int64_t)b * a.Hq + g * a.G + h) * D + e);
+    s_q[e] = s * (1.0f / (float)a.G);
+  }
+  for (int i = tid; i < 16384 / 32; i += kRouteThreads) s_taken[i] = 0;
+  __syncthreads();
+
+  const int64_t bg = (int64_t)b * a.Hkv + g;
+  if (nT > 0) {
+    score_rows<T, D>(a.chunk_sum, bg * a.n_cs_cap + c_lo, ncand, s_q, dyn, nullptr);
+    __syncthreads();
+    // level 1: nT rounds of block arg-max
+    for (int r = 0; r < nT; ++r) {
+      uint64_t best = 0;
+      for (int i = tid; i < ncand; i += kRouteThreads)
+        if (!((s_taken[i >> 5] >> (i & 31)) & 1u)) {
+          const uint64_t k = score_key(dyn[i], i);
+          best = k > best ? k : best;
+        }
+      best = wave_max_u64(best);
+      if ((tid & 63) == 0) s_red[tid >> 6] = best;
+      __syncthreads();
+      if (tid == 0) {
+        uint64_t m = s_red[0];
+        for (int w = 1; w < kRouteThreads / 64; ++w) m = s_red[w] > m ? s_red[w] : m;
+        const int i = (int)(0xFFFFFFFFu - (uint32_t)m);
+        s_chunks[r] = c_lo + i;
+        s_taken[i >> 5] |= 1u << (i & 31);
+      }
+      __syncthreads();
+    }
+    // chosen chunks in ascending order
+    if (tid < nT) {
+      const int c = s_chunks[tid];
+      int rank = 0;
+      for (int j = 0; j < nT; ++j) rank += (s_chunks[j] < c);
+      s_sorted[rank] = c;
+    }
+    __syncthreads();
+    // level 2: score every group of every chosen chunk
+    for (int i = tid; i < nT * gpc; i += kRouteThreads)
+      s_rowmap[i] = (int)(bg * a.n_gs_cap + (int64_t)s_sorted[i / gpc] * gpc + (i % gpc));
+    __syncthreads();
+    score_rows<T, D>(a.group_sum, 0, nT * gpc, s_q, dyn, s_rowmap);
+    __syncthreads();
+    if (tid < nT) {
+      // top TG of this chunk's gpc groups, then ascending
+      uint64_t picked_mask = 0;
+      for (int r = 0; r < TG; ++r) {
+        uint64_t best = 0;
+        int bj = 0;
+        for (int j = 0; j < gpc; ++j) {
+          if ((picked_mask >> j) & 1ull) continue;
+          const uint64_t k = score_key(dyn[tid * gpc + j], j);
+          if (k > best) { best = k; bj = j; }
+        }
+        picked_mask |= 1ull << bj;
+      }
+      int o = 0;
+      for (int j = 0; j < gpc; ++j)
+        if ((picked_mask >> j) & 1ull) s_groups[tid * TG + (o++)] = s_sorted[tid] * gpc + j;
+    }
+    __syncthreads();
+  }
+
+  // assemble the ascending token list
+  const int sinks_end = min(c_lo, kappa) * C;                // [0, sinks_end)
+  const int n_routed = max(nT, 0) * TG * GR;
+  const int loc_lo = max(c_lo, kappa - a.local_chunks);      // local chunks [loc_lo, kappa)
+  const int n_local = max(0, kappa - loc_lo) * C;
+  const int cur0 = kappa * C;
+  const int o_routed = sinks_end, o_local = o_routed + n_routed, o_cur = o_local + n_local;
+  const int total = o_cur + (n - cur0);
+  int32_t* out = a.sel_idx + bg * a.n_cap;
+  for (int i = tid; i < sinks_end; i += kRouteThreads) out[i] = i;
+  for (int i = tid; i < n_routed; i += kRouteThreads) out[o_routed + i] = s_groups[i / GR] * GR + (i % GR);
+  for (int i = tid; i < n_local; i += kRouteThreads) out[o_local + i] = loc_lo * C + i;
+  for (int i = tid; i < n - cur0; i += kRouteThreads) out[o_cur + i] = cur0 + i;
+  if (tid == 0) a.sel_count[bg] = total;
+}
+
+hipError_t launch_route(const RouteArgs& a, int dtype, int d, hipStream_t s) {
+  if (a.groups.n == 0) return hipSuccess;
+  const int gpc = a.chunk / a.group;
+  if (a.top_chunks * a.top_groups > kMaxRoutedGroups || a.top_chunks > 256 || gpc > 64)
+    return hipErrorInvalidValue;
+  const int ncand_max = a.n / a.chunk + 1;
+  if (ncand_max > 16384) return hipErrorInvalidValue;
+  const size_t dyn = 4 * (size_t)std::max(ncand_max, a.top_chunks * gpc);
+  dim3 grid(a.groups.n, a.B), block(kRouteThreads);
+  if (dtype == 0 && d == 128) hipLaunchKernelGGL((route_kernel<bf16_t, 128>), grid, block, dyn, s, a);
+  else if (dtype == 0 && d == 64) hipLaunchKernelGGL((route_kernel<bf16_t, 64>), grid, block, dyn, s, a);
+  else if (dtype == 1 && d == 128) hipLaunchKernelGGL((route_kernel<float, 128>), grid, block, dyn, s, a);
+  else if (dtype == 1 && d == 64) hipLaunchKernelGGL((route_kernel<float, 64>), grid, block, dyn, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace sa
