@@ -192,7 +192,11 @@ int32_t sparse_attn_index_build(const sa_params* p, const sa_buffers* b, int32_t
     a.q = b->q; a.k = b->k_cache; a.v = b->v_cache;
     a.pq = b->pyr_q; a.pk = b->pyr_k; a.pv = b->pyr_v; a.scores = b->pyr_scores;
     a.B = p->batch; a.H = p->n_q_heads; a.N = p->n_ctx; a.levels = p->levels; a.factor = p->factor;
-    a.Nc = pg.Nc; a.Nt = pg.Nt;
+    a.Nc = pg.Nc; a.Nt = pg.Nt; a.top_span = pg.top_span;
+    for (int l = 0; l < 8; ++l) {
+      a.soff[l] = l < p->levels ? pg.off[l] : 0;
+      a.coff[l] = l < p->levels && l > 0 ? pg.off[l] - p->n_ctx : 0;
+    }
     return hip_status(sa::launch_pyramid(a, p->dtype, p->head_dim, s));
   }
   int8_t kinds[sa::kMaxGroups];
@@ -257,6 +261,14 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
     a.scores = b->pyr_scores; a.blk_idx = b->blk_idx; a.blk_count = b->blk_count;
     a.B = p->batch; a.H = p->n_q_heads; a.N = p->n_ctx; a.levels = p->levels; a.factor = p->factor;
     a.q_block = p->q_block; a.K = p->block_top_k; a.nblk = pg.nblk; a.Nt = pg.Nt;
+    {
+      int m = p->n_ctx;
+      for (int l = 0; l < 8; ++l) {
+        a.len[l] = l < p->levels ? m : 0;
+        a.soff[l] = l < p->levels ? pg.off[l] : 0;
+        if (l < p->levels) m /= p->factor;
+      }
+    }
     return hip_status(sa::launch_pyramid_select(a, s));
   }
   int8_t kinds[sa::kMaxGroups];

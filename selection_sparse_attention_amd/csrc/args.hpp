@@ -44,6 +44,9 @@ struct PyramidArgs {
   void* pq; void* pk; void* pv;                    // [B,H,Nc,d]
   float* scores;                                   // [B,H,Nt]
   int32_t B, H, N, levels, factor, Nc, Nt;
+  int32_t top_span;                                // p^(L-1)
+  int64_t coff[8];                                 // row of level l's first entry in pq/pk/pv
+  int64_t soff[8];                                 // flat id of level l's first entry
 };
 
 // ---------------------------------------------------------------- select
@@ -102,8 +105,8 @@ struct PyrSelectArgs {
   int32_t* blk_idx;      // [B,H,nblk,K]
   int32_t* blk_count;    // [B,H,nblk]
   int32_t B, H, N, levels, factor, q_block, K, nblk, Nt;
-  uint32_t* ws;          // scratch
-  int64_t ws_per_head;
+  int32_t len[8];        // entries of each level
+  int64_t soff[8];       // flat id of each level's first entry
 };
 
 // ---------------------------------------------------------------- attention

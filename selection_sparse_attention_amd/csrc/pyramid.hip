@@ -1,0 +1,89 @@
+// Symmetric mean pyramid over Q, K, V and the parameter-free entry scores
+// (Lighthouse summary, Methodology 2A and 2B).
+//
+// Level 0 is the full-resolution sequence; an entry of level l is the mean of
+// p consecutive entries of level l-1, i.e. of its p^l level-0 rows.  Each
+// stored coarse entry is that exact mean (accumulated in fp64) rounded once to
+// the element type.  The score of a level-0 entry is |q|^2 + |k|^2 (the
+// squared l2 norm of the projected query and key: the ranking the norm gives);
+// a coarse entry inherits the largest score among the entries it covers.
+//
+// One workgroup (d threads, one per dim) per span of p^(L-1) level-0 rows of
+// one (sequence, head): it streams the span once, emits every coarse entry of
+// every level inside it, and the span's scores.
+#include "args.hpp"
+#include "common.hpp"
+
+namespace sa {
+
+template <typename T, int D>
+__global__ __launch_bounds__(D) void pyramid_kernel(PyramidArgs a) {
+  constexpr int NW = D / 64;
+  __shared__ float s_part[NW][256];
+  __shared__ float s_score[256];
+  const int span = blockIdx.x, bh = blockIdx.y, e = threadIdx.x;
+  const int lane = e & 63, wid = e >> 6;
+  const int P = a.top_span;
+  const int64_t r0 = (int64_t)span * P;                  // first level-0 row
+  const int64_t base = (int64_t)bh * a.N + r0;
+  double aq[8], ak[8], av[8];
+#pragma unroll
+  for (int l = 0; l < 8; ++l) { aq[l] = 0.0; ak[l] = 0.0; av[l] = 0.0; }
+  for (int r = 0; r < P; ++r) {
+    const float xq = Elem<T>::load(a.q, (base + r) * D + e);
+    const float xk = Elem<T>::load(a.k, (base + r) * D + e);
+    const float xv = Elem<T>::load(a.v, (base + r) * D + e);
+    const float sq = wave_sum(xq * xq + xk * xk);
+    if (lane == 0) s_part[wid][r] = sq;
+    int width = 1;
+#pragma unroll
+    for (int l = 1; l < 8; ++l) {
+      if (l >= a.levels) break;
+      width *= a.factor;
+      aq[l] += xq; ak[l] += xk; av[l] += xv;
+      if ((r + 1) % width == 0) {
+        const int64_t j = (r0 + r + 1) / width - 1;     // entry index inside level l
+        const int64_t row = (int64_t)bh * a.Nc + a.coff[l] + j;
+        const double inv = 1.0 / (double)width;
+        Elem<T>::store_d(a.pq, row * D + e, aq[l] * inv);
+        Elem<T>::store_d(a.pk, row * D + e, ak[l] * inv);
+        Elem<T>::store_d(a.pv, row * D + e, av[l] * inv);
+        aq[l] = 0.0; ak[l] = 0.0; av[l] = 0.0;
+      }
+    }
+  }
+  __syncthreads();
+  float* sc = a.scores + (int64_t)bh * a.Nt;
+  for (int r = e; r < P; r += D) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) s += s_part[w][r];
+    s_score[r] = s;
+    sc[r0 + r] = s;
+  }
+  __syncthreads();
+  // coarse scores: the max over each entry's level-0 rows
+  int width = 1;
+  for (int l = 1; l < a.levels; ++l) {
+    width *= a.factor;
+    const int cnt = P / width;
+    for (int j = e; j < cnt; j += D) {
+      float m = s_score[j * width];
+      for (int r = 1; r < width; ++r) m = fmaxf(m, s_score[j * width + r]);
+      sc[a.soff[l] + r0 / width + j] = m;
+    }
+  }
+}
+
+hipError_t launch_pyramid(const PyramidArgs& a, int dtype, int d, hipStream_t s) {
+  if (a.top_span > 256 || a.levels > 8) return hipErrorInvalidValue;
+  dim3 grid(a.N / a.top_span, a.B * a.H);
+  if (dtype == 0 && d == 128) hipLaunchKernelGGL((pyramid_kernel<bf16_t, 128>), grid, dim3(128), 0, s, a);
+  else if (dtype == 0 && d == 64) hipLaunchKernelGGL((pyramid_kernel<bf16_t, 64>), grid, dim3(64), 0, s, a);
+  else if (dtype == 1 && d == 128) hipLaunchKernelGGL((pyramid_kernel<float, 128>), grid, dim3(128), 0, s, a);
+  else if (dtype == 1 && d == 64) hipLaunchKernelGGL((pyramid_kernel<float, 64>), grid, dim3(64), 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -103,3 +103,47 @@ def max_err(got, ref):
 def np_inputs(inp):
     return {k: (np64(v) if torch.is_tensor(v) and v.is_floating_point() else
                 (v.numpy() if torch.is_tensor(v) else v)) for k, v in inp.items()}
+
+
+class PrefillRun:
+    """Device buffers of one pyramid-selection prefill and the calls that
+    fill them."""
+
+    def __init__(self, cfg, inp):
+        self.cfg = cfg
+        B, H, N, d = cfg.batch, cfg.n_heads, cfg.n_ctx, cfg.head_dim
+        dt = tdt(cfg.dtype)
+        self.t = {k: to_dev(inp[k], cfg.dtype) for k in ("q", "k", "v")}
+        nc, nt, m = 0, 0, N
+        for lvl in range(cfg.levels):
+            nt += m
+            if lvl:
+                nc += m
+            m //= cfg.factor
+        self.nc, self.nt = nc, nt
+        self.nblk = (N + cfg.q_block - 1) // cfg.q_block
+        for k in ("pq", "pk", "pv"):
+            self.t[k] = torch.zeros(B, H, max(nc, 1), d, dtype=dt, device=DEV)
+        self.t["scores"] = torch.zeros(B, H, nt, dtype=torch.float32, device=DEV)
+        self.t["blk_idx"] = torch.full((B, H, self.nblk, cfg.block_top_k), -1, dtype=torch.int32,
+                                       device=DEV)
+        self.t["blk_count"] = torch.full((B, H, self.nblk), -1, dtype=torch.int32, device=DEV)
+        self.t["out"] = torch.full((B, H, N, d), float("nan"), dtype=torch.float32, device=DEV)
+        self.params = sa.params_from_config(cfg)
+        self.ws_sel = sa.Workspace(DEV)
+        self.ws_pf = sa.Workspace(DEV)
+
+    def bufs(self):
+        t = self.t
+        return sa.make_buffers(q=t["q"], k_cache=t["k"], v_cache=t["v"], pyr_q=t["pq"],
+                               pyr_k=t["pk"], pyr_v=t["pv"], pyr_scores=t["scores"],
+                               blk_idx=t["blk_idx"], blk_count=t["blk_count"], out=t["out"])
+
+    def pyramid(self):
+        sa.index_build(self.params, self.bufs(), sa.IDX_PYRAMID, 0, self.cfg.n_ctx)
+
+    def select(self):
+        sa.select(self.params, self.bufs(), sa.SEL_PYRAMID_TOPK, self.ws_sel)
+
+    def prefill(self):
+        sa.prefill_chunked(self.params, self.bufs(), self.ws_pf)

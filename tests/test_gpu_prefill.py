@@ -1,0 +1,215 @@
+"""GPU parity of pyramid-selection prefill (pyramid build -> per-block joint
+top-K -> chunked MFMA attention) against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from oracle import lighthouse as LH
+from gpu_harness import DEV, PrefillRun, log, max_err, np64
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-3
+SMALL = workloads.PYRAMID_128K.with_(n_heads=2, n_ctx=2048, block_top_k=300)
+
+
+def _np(inp):
+    return {k: np64(v) for k, v in inp.items() if torch.is_tensor(v) and v.is_floating_point()}
+
+
+def _oracle_head(cfg, ni, b, h):
+    Q, K, V = ni["q"][b, h], ni["k"][b, h], ni["v"][b, h]
+    kc = oracle.pyramid_levels(K, cfg.levels, cfg.factor, cfg.dtype)
+    vc = oracle.pyramid_levels(V, cfg.levels, cfg.factor, cfg.dtype)
+    qc = oracle.pyramid_levels(Q, cfg.levels, cfg.factor, cfg.dtype)
+    sc = oracle.pyramid_scores(Q, K, cfg.levels, cfg.factor)
+    return qc, kc, vc, sc
+
+
+def _coarse(run, b, h, cfg, name):
+    """Split a device coarse buffer into its levels."""
+    x = np64(run.t[name][b, h])
+    out, o, m = [], 0, cfg.n_ctx
+    for _ in range(1, cfg.levels):
+        m //= cfg.factor
+        out.append(x[o:o + m])
+        o += m
+    return out
+
+
+@pytest.mark.parametrize("cfg", [
+    SMALL,
+    SMALL.with_(levels=2, factor=2, n_ctx=1024 + 256),
+    SMALL.with_(levels=4, factor=2, n_ctx=1024),
+])
+def test_pyramid_matches_oracle_exactly_on_lattice(cfg):
+    """Lattice inputs: coarse means (accumulated exactly, rounded once) and
+    squared-norm scores are exact on both sides."""
+    inp = workloads.prefill_inputs(cfg, 1)
+    run = PrefillRun(cfg, inp)
+    run.pyramid()
+    torch.cuda.synchronize()
+    ni = _np(inp)
+    for b in range(cfg.batch):
+        for h in range(cfg.n_heads):
+            qc, kc, vc, sc = _oracle_head(cfg, ni, b, h)
+            for name, ref in (("pq", qc), ("pk", kc), ("pv", vc)):
+                for lvl, (got, exp) in enumerate(zip(_coarse(run, b, h, cfg, name), ref)):
+                    assert np.array_equal(got, exp), (name, lvl)
+            got_s = np64(run.t["scores"][b, h])
+            assert np.array_equal(got_s, np.concatenate(sc))
+
+
+def test_pyramid_gaussian_within_one_ulp():
+    cfg = SMALL
+    g = torch.Generator().manual_seed(5)
+    inp = {k: torch.randn(1, 2, cfg.n_ctx, 128, generator=g).to(torch.bfloat16).float()
+           for k in ("q", "k", "v")}
+    run = PrefillRun(cfg, inp)
+    run.pyramid()
+    torch.cuda.synchronize()
+    ni = _np(inp)
+    qc, kc, vc, sc = _oracle_head(cfg, ni, 0, 1)
+    for name, ref in (("pk", kc), ("pv", vc)):
+        for got, exp in zip(_coarse(run, 0, 1, cfg, name), ref):
+            assert np.all(np.abs(got - exp) <= oracle.bf16_ulp(exp) * 1.0001)
+    np.testing.assert_allclose(np64(run.t["scores"][0, 1]), np.concatenate(sc), rtol=2e-6)
+
+
+SELECT_CASES = [
+    SMALL,
+    SMALL.with_(block_top_k=64),
+    SMALL.with_(block_top_k=5000),                       # every visible entry
+    SMALL.with_(n_ctx=2048 + 16 * 9, block_top_k=500),   # ragged last block
+    SMALL.with_(levels=2, factor=2, n_ctx=1024, block_top_k=100),
+]
+
+
+@pytest.mark.parametrize("cfg", SELECT_CASES,
+                         ids=lambda c: f"N{c.n_ctx}-L{c.levels}-p{c.factor}-K{c.block_top_k}")
+def test_block_select_exact_on_lattice(cfg):
+    inp = workloads.prefill_inputs(cfg, 2)
+    run = PrefillRun(cfg, inp)
+    run.pyramid()
+    run.select()
+    torch.cuda.synchronize()
+    idx = run.t["blk_idx"].cpu().numpy()
+    cnt = run.t["blk_count"].cpu().numpy()
+    ni = _np(inp)
+    for b in range(cfg.batch):
+        for h in range(cfg.n_heads):
+            sc = oracle.pyramid_scores(ni["q"][b, h], ni["k"][b, h], cfg.levels, cfg.factor)
+            for blk in range(run.nblk):
+                ref = oracle.block_select(sc, blk, cfg.n_ctx, cfg.levels, cfg.factor,
+                                          cfg.q_block, cfg.block_top_k)
+                c = cnt[b, h, blk]
+                assert c == len(ref), (h, blk, c, len(ref))
+                got = idx[b, h, blk, :c]
+                assert np.all(np.diff(got) > 0)            # ascending flat ids
+                assert np.array_equal(np.sort(got), np.sort(ref)), (h, blk)
+
+
+def _check_prefill(cfg, run, ni, blocks_of_head):
+    out = np64(run.t["out"])
+    idx = run.t["blk_idx"].cpu().numpy()
+    cnt = run.t["blk_count"].cpu().numpy()
+    worst = 0.0
+    for (b, h), blocks in blocks_of_head.items():
+        qc, kc, vc, sc = _oracle_head(cfg, ni, b, h)
+        for blk in blocks:
+            sel = oracle.block_select(sc, blk, cfg.n_ctx, cfg.levels, cfg.factor, cfg.q_block,
+                                      cfg.block_top_k)
+            got_sel = idx[b, h, blk, :cnt[b, h, blk]]
+            assert np.array_equal(np.sort(got_sel), np.sort(sel)), (h, blk)
+            ref = LH.prefill_block(ni["q"][b, h], ni["k"][b, h], ni["v"][b, h], kc, vc, sel, blk,
+                                   cfg.q_block, cfg.levels, cfg.factor)
+            lo = blk * cfg.q_block
+            worst = max(worst, max_err(out[b, h, lo:lo + len(ref)], ref))
+    log("prefill max err", worst)
+    return worst
+
+
+def test_prefill_end_to_end_small():
+    cfg = SMALL.with_(n_ctx=2048 + 64)
+    inp = workloads.prefill_inputs(cfg, 3)
+    run = PrefillRun(cfg, inp)
+    run.pyramid(); run.select(); run.prefill()
+    torch.cuda.synchronize()
+    ni = _np(inp)
+    blocks = {(0, h): list(range(run.nblk)) for h in range(cfg.n_heads)}
+    assert _check_prefill(cfg, run, ni, blocks) <= BF16_TOL
+
+
+def test_prefill_over_given_selection():
+    """The attention stage alone: blk_idx filled with random visible entries
+    drawn by the test's generator, unsorted."""
+    cfg = SMALL.with_(block_top_k=200)
+    inp = workloads.prefill_inputs(cfg, 4)
+    run = PrefillRun(cfg, inp)
+    run.pyramid()
+    torch.cuda.synchronize()
+    gen = np.random.default_rng(8)
+    sels = {}
+    for blk in range(run.nblk):
+        vis = oracle.visible_entries(blk, cfg.n_ctx, cfg.levels, cfg.factor, cfg.q_block)
+        offs = LH.level_offsets(cfg.n_ctx, cfg.levels, cfg.factor)
+        flat = np.array([offs[l] + j for l, j in vis], np.int64)
+        m = int(gen.integers(0, min(len(flat), cfg.block_top_k) + 1))
+        pick = gen.permutation(flat)[:m]
+        sels[blk] = pick
+        for h in range(cfg.n_heads):
+            run.t["blk_idx"][0, h, blk, :m] = torch.tensor(pick, dtype=torch.int32)
+            run.t["blk_count"][0, h, blk] = m
+    run.prefill()
+    torch.cuda.synchronize()
+    out = np64(run.t["out"])
+    ni = _np(inp)
+    worst = 0.0
+    for h in range(cfg.n_heads):
+        _, kc, vc, _ = _oracle_head(cfg, ni, 0, h)
+        for blk, sel in sels.items():
+            ref = LH.prefill_block(ni["q"][0, h], ni["k"][0, h], ni["v"][0, h], kc, vc, sel, blk,
+                                   cfg.q_block, cfg.levels, cfg.factor)
+            lo = blk * cfg.q_block
+            worst = max(worst, max_err(out[0, h, lo:lo + len(ref)], ref))
+    log("given-selection max err", worst)
+    assert worst <= BF16_TOL
+
+
+def test_prefill_one_level_full_budget_is_dense_causal():
+    cfg = SMALL.with_(levels=1, n_ctx=1024, block_top_k=1024)
+    inp = workloads.prefill_inputs(cfg, 6)
+    run = PrefillRun(cfg, inp)
+    run.pyramid(); run.select(); run.prefill()
+    torch.cuda.synchronize()
+    ni = _np(inp)
+    out = np64(run.t["out"])
+    for h in range(cfg.n_heads):
+        ref = oracle.dense_causal(ni["q"][0, h], ni["k"][0, h], ni["v"][0, h])
+        assert max_err(out[0, h], ref) <= BF16_TOL
+
+
+def test_prefill_full_size_sampled():
+    """The 128K, 16-head workload at full size, inputs drawn on the GPU;
+    every head's pyramid and scores, and sampled blocks of two heads, are
+    checked against the oracle."""
+    cfg = workloads.PYRAMID_128K
+    inp = workloads.prefill_inputs(cfg, 7, device=DEV)
+    run = PrefillRun(cfg, inp)
+    run.pyramid(); run.select(); run.prefill()
+    torch.cuda.synchronize()
+    heads = [0, 11]
+    ni = {k: np64(inp[k][:, heads]) for k in ("q", "k", "v")}
+    sub = cfg.with_(n_heads=2)
+    for i, h in enumerate(heads):
+        sc = oracle.pyramid_scores(ni["q"][0, i], ni["k"][0, i], cfg.levels, cfg.factor)
+        assert np.array_equal(np64(run.t["scores"][0, h]), np.concatenate(sc))
+    rng = np.random.default_rng(1)
+    blocks = sorted(set([0, 1, 24, 25, run.nblk - 1] + rng.integers(0, run.nblk, 5).tolist()))
+
+    class Sub:                       # the two sampled heads as a 2-head run
+        t = {k: run.t[k][:, heads] for k in ("out", "blk_idx", "blk_count")}
+    worst = _check_prefill(sub, Sub, ni, {(0, i): blocks for i in range(2)})
+    assert worst <= BF16_TOL
