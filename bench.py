@@ -44,7 +44,12 @@ def parse():
     ap.add_argument("--instances", type=int, default=4,
                     help="independent input sets rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the other workloads (128K decode, routed decode, prefill)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain elementwise copy of known size (for scaling HBM "
+                         "byte counters) and exit")
     return ap.parse_args()
 
 
@@ -146,28 +151,36 @@ def decode_bytes(cfg, counts, kinds):
     return attn, step
 
 
-def run_decode(args, torch, sa, workloads):
-    cfg = {
-        "llama3_8b_decode_32k": workloads.LLAMA_32K,
-        "llama3_8b_decode_128k": workloads.LLAMA_128K,
-        "llama3_8b_decode_128k_topk": workloads.LLAMA_128K_TOPK,
-        "hga_route_decode_64k": workloads.HGA_64K,
-    }[args.workload]
-    log(f"[bench] generating {args.instances} instance(s) of {cfg.name}")
-    insts = [DecodeInstance(cfg, 1000 + i, sa, torch, workloads) for i in range(args.instances)]
+DECODE_CONFIGS = {
+    "llama3_8b_decode_32k": "LLAMA_32K",
+    "llama3_8b_decode_128k": "LLAMA_128K",
+    "llama3_8b_decode_128k_topk": "LLAMA_128K_TOPK",
+    "hga_route_decode_64k": "HGA_64K",
+}
+
+
+def run_decode(args, torch, sa, workloads, workload=None, steps=None, warmup=None,
+               instances=None, cpu=True):
+    workload = workload or args.workload
+    steps = steps or args.steps
+    warmup = args.warmup if warmup is None else warmup
+    instances = instances or args.instances
+    cfg = getattr(workloads, DECODE_CONFIGS[workload])
+    log(f"[bench] generating {instances} instance(s) of {cfg.name}")
+    insts = [DecodeInstance(cfg, 1000 + i, sa, torch, workloads) for i in range(instances)]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    for i in range(args.warmup):
+    for i in range(warmup):
         x = insts[i % len(insts)]
         x.index_and_select()
         x.decode()
     torch.cuda.synchronize()
-    log(f"[bench] warmup done ({args.warmup} steps)")
+    log(f"[bench] warmup done ({warmup} steps)")
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+          for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         x = insts[i % len(insts)]
         x.index_and_select()
         ev[i][0].record(stream)
@@ -175,10 +188,10 @@ def run_decode(args, torch, sa, workloads):
         ev[i][1].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
-    t_step = start.elapsed_time(end) / args.steps * 1e-3
-    t_kernel = sum(a.elapsed_time(b) for a, b in ev) / args.steps * 1e-3
-    log(f"[bench] timed {args.steps} steps: {t_step * 1e6:.1f} us/step, "
-        f"attention kernel {t_kernel * 1e6:.1f} us")
+    t_step = start.elapsed_time(end) / steps * 1e-3
+    t_kernel = sum(a.elapsed_time(b) for a, b in ev) / steps * 1e-3
+    log(f"[bench] {cfg.name}: timed {steps} steps: {t_step * 1e6:.1f} us/step, "
+        f"attention call {t_kernel * 1e6:.1f} us")
     kinds = cfg.head_kind()
     attn_b, step_b = 0, 0
     sel_frac = []
@@ -194,12 +207,12 @@ def run_decode(args, torch, sa, workloads):
     attn_b /= len(insts)
     step_b /= len(insts)
     tokens = cfg.batch * cfg.n_q_heads * cfg.n_ctx
-    kernel = "decode_split_kernel"
-    sha = source_sha(["decode.hip", "common.hpp", "args.hpp"])
+    kernel = "sparse_attn_decode (decode_mfma_kernel + decode_combine_kernel)"
+    sha = source_sha(["decode.hip", "decode_mfma.hip", "common.hpp", "args.hpp"])
     achieved = attn_b / t_kernel / 1e9
     res = {
         "metric": METRIC, "value": tokens / t_step, "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": t_step * 1e3, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "batch": cfg.batch, "n_q_heads": cfg.n_q_heads,
@@ -217,9 +230,20 @@ def run_decode(args, torch, sa, workloads):
                      "bytes_per_launch": attn_b, "launch_us": t_kernel * 1e6,
                      "source_sha": sha},
     }
-    if not args.no_cpu_baseline:
+    if cpu and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_decode(cfg, insts[0], args.cpu_seconds, torch)
+    del insts
+    torch.cuda.empty_cache()
     return res
+
+
+def blas_threads():
+    """Threads numpy's BLAS uses (the oracle's only parallel part)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max((p.get("num_threads", 1) for p in threadpool_info()), default=1))
+    except Exception:
+        return 1
 
 
 def cpu_baseline_decode(cfg, inst, budget_s, torch):
@@ -227,16 +251,12 @@ def cpu_baseline_decode(cfg, inst, budget_s, torch):
     until ``budget_s`` of CPU time is spent; scaled to tokens/s."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    except Exception:
-        blas = 1
+    blas = blas_threads()
     G = cfg.gqa
     groups = [(b, g) for b in range(cfg.batch) for g in range(cfg.n_kv_heads)]
     t = inst.t
     done_heads, spent, i = 0, 0.0, 0
-    while (spent < budget_s or done_heads == 0) and i < 4 * len(groups):
+    while spent < budget_s or done_heads == 0:
         b, g = groups[(i * 7) % len(groups)]
         i += 1
         sl = {"q_pre": t["q_pre"][b:b + 1], "q": t["q"][b:b + 1],
@@ -260,6 +280,12 @@ def cpu_baseline_decode(cfg, inst, budget_s, torch):
             "host_cpus": os.cpu_count()}
 
 
+def compact(r):
+    keep = ("value", "unit", "ms_per_step", "step_hbm_gbps", "selected_frac_mean", "config",
+            "roofline", "step_tflops")
+    return {k: r[k] for k in keep if k in r}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -273,15 +299,151 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
     if args.workload == "pyramid_prefill_128k":
         res = run_prefill(args, torch, sa, workloads)
     else:
         res = run_decode(args, torch, sa, workloads)
+    if not args.no_extras and args.workload == "llama3_8b_decode_32k":
+        other = {}
+        for w in ("llama3_8b_decode_128k_topk", "llama3_8b_decode_128k", "hga_route_decode_64k"):
+            other[w] = compact(run_decode(args, torch, sa, workloads, workload=w, steps=20,
+                                          warmup=3, instances=2, cpu=False))
+        other["pyramid_prefill_128k"] = compact(run_prefill(args, torch, sa, workloads, steps=5,
+                                                            warmup=1, cpu=False))
+        res["other_workloads"] = other
     print(json.dumps(res), flush=True)
 
 
-def run_prefill(args, torch, sa, workloads):
-    raise SystemExit("pyramid prefill benchmark is not wired yet")
+def calibrate_copy(torch):
+    """A 1 GiB bf16 negation (reads 1 GiB, writes 1 GiB) run five times: the
+    ratio of a byte counter to these sizes scales the counter to bytes."""
+    n = 1 << 29
+    x = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(5):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"kernel": "neg", "bytes_read": 2 * n, "bytes_written": 2 * n,
+                      "launches": 5}), flush=True)
+
+
+def prefill_flops(cfg, counts):
+    """Algorithmic FLOP of the prefill attention: 4 d per (query, visible
+    key) pair - QK^T and PV - with the causal block counted as a triangle."""
+    pairs = 0
+    N, qb = cfg.n_ctx, cfg.q_block
+    for per_head in counts:
+        for blk, c in enumerate(per_head):
+            nq = min(qb, N - blk * qb)
+            pairs += nq * int(c) + nq * (nq + 1) // 2
+    return 4 * cfg.head_dim * pairs
+
+
+def run_prefill(args, torch, sa, workloads, steps=None, warmup=None, cpu=True):
+    cfg = workloads.PYRAMID_128K
+    steps = steps or max(3, min(args.steps, 10))
+    warmup = 1 if warmup is None else warmup
+    B, H, N, d = cfg.batch, cfg.n_heads, cfg.n_ctx, cfg.head_dim
+    log(f"[bench] generating {cfg.name}")
+    inp = workloads.prefill_inputs(cfg, 2000, device="cuda")
+    t = {k: inp[k].to(torch.bfloat16).contiguous() for k in ("q", "k", "v")}
+    del inp
+    nc, nt, m = 0, 0, N
+    for lvl in range(cfg.levels):
+        nt += m
+        nc += m if lvl else 0
+        m //= cfg.factor
+    nblk = (N + cfg.q_block - 1) // cfg.q_block
+    for k in ("pq", "pk", "pv"):
+        t[k] = torch.zeros(B, H, max(nc, 1), d, dtype=torch.bfloat16, device="cuda")
+    t["scores"] = torch.zeros(B, H, nt, dtype=torch.float32, device="cuda")
+    t["blk_idx"] = torch.zeros(B, H, nblk, cfg.block_top_k, dtype=torch.int32, device="cuda")
+    t["blk_count"] = torch.zeros(B, H, nblk, dtype=torch.int32, device="cuda")
+    t["out"] = torch.zeros(B, H, N, d, dtype=torch.float32, device="cuda")
+    p = sa.params_from_config(cfg)
+    bufs = sa.make_buffers(q=t["q"], k_cache=t["k"], v_cache=t["v"], pyr_q=t["pq"],
+                           pyr_k=t["pk"], pyr_v=t["pv"], pyr_scores=t["scores"],
+                           blk_idx=t["blk_idx"], blk_count=t["blk_count"], out=t["out"])
+    ws_s, ws_p = sa.Workspace("cuda"), sa.Workspace("cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        sa.index_build(p, bufs, sa.IDX_PYRAMID, 0, N)
+        sa.select(p, bufs, sa.SEL_PYRAMID_TOPK, ws_s)
+        if ev:
+            ev[0].record(stream)
+        sa.prefill_chunked(p, bufs, ws_p)
+        if ev:
+            ev[1].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        step(ev[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_step = start.elapsed_time(end) / steps * 1e-3
+    t_kernel = sum(a.elapsed_time(b) for a, b in ev) / steps * 1e-3
+    counts = t["blk_count"].reshape(B * H, nblk).cpu().tolist()
+    flops = prefill_flops(cfg, counts)
+    log(f"[bench] {cfg.name}: {t_step * 1e3:.3f} ms/step, prefill kernel {t_kernel * 1e3:.3f} ms, "
+        f"{flops / t_kernel / 1e12:.1f} TFLOP/s")
+    sha = source_sha(["prefill.hip", "common.hpp", "args.hpp"])
+    achieved = flops / t_kernel / 1e12
+    res = {
+        "metric": "pyramid-selection prefill tokens/s + achieved bf16 MFMA TFLOP/s vs peak",
+        "value": B * H * N / t_step, "unit": "tokens/s (B x heads x N per step)",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": t_step * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": B, "n_heads": H, "head_dim": d, "n_ctx": N,
+                   "levels": cfg.levels, "factor": cfg.factor, "q_block": cfg.q_block,
+                   "block_top_k": cfg.block_top_k},
+        "step_tflops": flops / t_step / 1e12,
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic_record("prefill_kernel", cfg.name, sha),
+                     "flops_per_launch": flops, "launch_us": t_kernel * 1e6, "source_sha": sha},
+    }
+    if cpu and not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(cfg, t, args.cpu_seconds, torch)
+    del t
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline_prefill(cfg, t, budget_s, torch):
+    """The fp64 oracle on whole query blocks of head 0 (pyramid + scores once,
+    then per block: selection and attention) until ``budget_s`` is spent."""
+    import oracle
+    from oracle import lighthouse as LH
+    Q, K, V = (t[k][0, 0].to("cpu", torch.float64).numpy() for k in ("q", "k", "v"))
+    t0 = time.perf_counter()
+    kc = oracle.pyramid_levels(K, cfg.levels, cfg.factor, cfg.dtype)
+    vc = oracle.pyramid_levels(V, cfg.levels, cfg.factor, cfg.dtype)
+    sc = oracle.pyramid_scores(Q, K, cfg.levels, cfg.factor)
+    nblk = cfg.n_ctx // cfg.q_block
+    done = 0
+    while time.perf_counter() - t0 < budget_s or done == 0:
+        blk = nblk - 1 - (done * 37) % nblk
+        sel = oracle.block_select(sc, blk, cfg.n_ctx, cfg.levels, cfg.factor, cfg.q_block,
+                                  cfg.block_top_k)
+        LH.prefill_block(Q, K, V, kc, vc, sel, blk, cfg.q_block, cfg.levels, cfg.factor)
+        done += 1
+    spent = time.perf_counter() - t0
+    return {"value": done * cfg.q_block / spent, "unit": "tokens/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"{done} query blocks of one head of {cfg.name} (pyramid and scores of "
+                      f"the head once, then selection + attention per block), fp64 numpy, "
+                      f"{spent:.1f} s"}
 
 
 if __name__ == "__main__":
