@@ -39,11 +39,16 @@ constexpr int kD = 128;                 // head dim
 constexpr int kKRow = kD + 8;           // K tile row stride (bf16 elements) = 272 B
 constexpr int kVRow = 36;               // V^T tile row stride (bf16 elements) = 72 B
 
-__device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
-  return (uint32_t)lo | ((uint32_t)hi << 16);
+typedef float f32x2p __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2p __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> packed bf16 pair (round to nearest even, one instruction
+// on gfx950), and the fp32 value of each half.
+__device__ __forceinline__ uint32_t pk_bf16(float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2p){x, y}, bf16x2p));
 }
 
-__global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kKT * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kD * kVRow];
 
@@ -85,23 +90,34 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a) {
   }
 
   // ---- gather roles: K (thread -> key t/8, 16 dims at 16*(t%8)),
-  //      V (thread -> key pair t%16, 8 dims at 8*(t/16))
+  //      V (thread -> keys 2(t%16), 2(t%16)+1, 8 dims at 8*(t/16)).
+  //      Entry e of the block's key sequence is selected entry e (a flat id)
+  //      for e < c_sel, the block's own level-0 key q0 + e - c_sel below T,
+  //      and nothing (a zero row) past T.  A flat id outside the pyramid is
+  //      malformed and also reads as a zero row.
   const int gk_key = tid >> 3, gk_seg = tid & 7;
   const int gv_kp = tid & 15, gv_seg = tid >> 4;
-  auto row_ptr = [&](int e, bool is_v) -> const uint16_t* {
-    if (e < c_sel) {
-      const int f = list[e];
-      if ((unsigned)f >= (unsigned)(a.N + a.Nc)) return nullptr;   // malformed id: a zero row
-      if (f < a.N) return (is_v ? vb : kb) + (int64_t)f * kD;
-      return (is_v ? pvb : pkb) + (int64_t)(f - a.N) * kD;
-    }
-    if (e < T) return (is_v ? vb : kb) + (int64_t)(q0 + e - c_sel) * kD;
-    return nullptr;
+  auto entry_id = [&](int e) -> int {
+    if (e < c_sel) return list[e];
+    if (e < T) return q0 + e - c_sel;
+    return -1;
+  };
+  auto row_ptr = [&](int f, bool is_v) -> const uint16_t* {
+    if ((unsigned)f >= (unsigned)(a.N + a.Nc)) return nullptr;
+    if (f < a.N) return (is_v ? vb : kb) + (int64_t)f * kD;
+    return (is_v ? pvb : pkb) + (int64_t)(f - a.N) * kD;
+  };
+  // ids run two tiles ahead of the rows, rows one tile ahead of the math
+  int id_c[3], id_n[3];
+  auto load_ids = [&](int tile, int* id) {
+    const int e0 = tile * kKT;
+    id[0] = entry_id(e0 + gk_key);
+    id[1] = entry_id(e0 + 2 * gv_kp);
+    id[2] = entry_id(e0 + 2 * gv_kp + 1);
   };
   uint4 rk[2], rv[2];
-  auto gather = [&](int tile) {
-    const int e0 = tile * kKT;
-    const uint16_t* pk = row_ptr(e0 + gk_key, false);
+  auto gather = [&](const int* id) {
+    const uint16_t* pk = row_ptr(id[0], false);
     if (pk) {
       rk[0] = *reinterpret_cast<const uint4*>(pk + 16 * gk_seg);
       rk[1] = *reinterpret_cast<const uint4*>(pk + 16 * gk_seg + 8);
@@ -110,7 +126,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a) {
     }
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const uint16_t* pv = row_ptr(e0 + 2 * gv_kp + r, true);
+      const uint16_t* pv = row_ptr(id[1 + r], true);
       rv[r] = pv ? *reinterpret_cast<const uint4*>(pv + 8 * gv_seg) : make_uint4(0, 0, 0, 0);
     }
   };
@@ -125,8 +141,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t a0 = v0[i], a1 = v1[i];
-      *reinterpret_cast<uint32_t*>(vdst + (2 * i) * kVRow) = pack2(a0 & 0xFFFF, a1 & 0xFFFF);
-      *reinterpret_cast<uint32_t*>(vdst + (2 * i + 1) * kVRow) = pack2(a0 >> 16, a1 >> 16);
+      *reinterpret_cast<uint32_t*>(vdst + (2 * i) * kVRow) = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+      *reinterpret_cast<uint32_t*>(vdst + (2 * i + 1) * kVRow) = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
     }
   };
 
@@ -139,11 +155,17 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a) {
     for (int nt = 0; nt < 2; ++nt) o[dt][nt] = (f32x4p){0.f, 0.f, 0.f, 0.f};
   const float sc = a.scale_log2;
 
-  if (ntiles > 0) { gather(0); stash(0); }
+  if (ntiles > 0) {
+    load_ids(0, id_c);
+    gather(id_c);
+    if (ntiles > 1) load_ids(1, id_c);
+    stash(0);
+  }
   __syncthreads();
   for (int tile = 0; tile < ntiles; ++tile) {
     const int buf = tile & 1;
-    if (tile + 1 < ntiles) gather(tile + 1);
+    if (tile + 2 < ntiles) load_ids(tile + 2, id_n);
+    if (tile + 1 < ntiles) gather(id_c);
     const uint16_t* kt = s_k[buf];
     const uint16_t* vt = s_vt[buf];
     // S^T[key = 16 mt + 4 jg + i][q = 16 nt + l16]
@@ -163,45 +185,73 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a) {
         s[mt][nt] = c;
       }
     }
-    // mask, scale, online softmax per query
+    // scale (log2 domain), mask only on tiles that reach past the selection
     const int e0 = tile * kKT;
-    uint4 ph[2], pl[2];                              // P^T fragments, hi and lo
+    float x[2][2][4];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int ql = 32 * wid + 16 * nt + l16;
-      float x[2][4];
-      float tmax = -INFINITY;
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = e0 + 16 * mt + 4 * jg + i;
-          const bool ok = (e < c_sel) || (e < T && (e - c_sel) <= ql);
-          x[mt][i] = ok ? s[mt][nt][i] * sc : -INFINITY;
-          tmax = fmaxf(tmax, x[mt][i]);
-        }
+        for (int i = 0; i < 4; ++i) x[nt][mt][i] = s[mt][nt][i] * sc;
+    if (e0 + kKT > c_sel) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int ql = 32 * wid + 16 * nt + l16;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = e0 + 16 * mt + 4 * jg + i;
+            const bool ok = (e < c_sel) || (e < T && (e - c_sel) <= ql);
+            if (!ok) x[nt][mt][i] = -INFINITY;
+          }
+      }
+    }
+    // online softmax per query; P^T fragments as a bf16 high part and a bf16
+    // remainder (the weights keep ~16 bits through the second product)
+    uint4 ph[2], pl[2];
+    float alpha[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float tmax = x[nt][0][0];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, x[nt][mt][i]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
       const float mn = fmaxf(m[nt], tmax);
-      const float alpha = (mn == -INFINITY || m[nt] == mn) ? 1.f : exp2f(m[nt] - mn);
+      const float msub = (mn == -INFINITY) ? 0.f : mn;   // a fully masked row stays at p = 0
+      alpha[nt] = __builtin_amdgcn_exp2f(m[nt] - msub);
       m[nt] = mn;
-      float ps = 0.f;
-      uint16_t hb[8], lb[8];
+      float p[8];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = (x[mt][i] == -INFINITY) ? 0.f : exp2f(x[mt][i] - mn);
-          ps += p;
-          const uint16_t h = f32_to_bf16(p);
-          hb[4 * mt + i] = h;
-          lb[4 * mt + i] = f32_to_bf16(p - bf16_to_f32(h));
-        }
-      lpart[nt] = lpart[nt] * alpha + ps;
+        for (int i = 0; i < 4; ++i) p[4 * mt + i] = __builtin_amdgcn_exp2f(x[nt][mt][i] - msub);
+      float ps = 0.f;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[dt][nt] *= alpha;
-      ph[nt] = make_uint4(pack2(hb[0], hb[1]), pack2(hb[2], hb[3]), pack2(hb[4], hb[5]), pack2(hb[6], hb[7]));
-      pl[nt] = make_uint4(pack2(lb[0], lb[1]), pack2(lb[2], lb[3]), pack2(lb[4], lb[5]), pack2(lb[6], lb[7]));
+      for (int j = 0; j < 8; ++j) ps += p[j];
+      lpart[nt] = lpart[nt] * alpha[nt] + ps;
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t h = pk_bf16(p[2 * j], p[2 * j + 1]);
+        const float r0 = p[2 * j] - __builtin_bit_cast(float, h << 16);
+        const float r1 = p[2 * j + 1] - __builtin_bit_cast(float, h & 0xFFFF0000u);
+        hw[j] = h;
+        lw[j] = pk_bf16(r0, r1);
+      }
+      ph[nt] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      pl[nt] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    }
+    // rescale the accumulators only when some query's running max moved
+    if (!__all(alpha[0] == 1.f && alpha[1] == 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) o[dt][nt] *= alpha[nt];
     }
     // O^T += V^T P^T over the tile's 32 keys: k-slot j of lane group jg is
     // key 4 jg + j (j < 4) or 16 + 4 jg + (j - 4)
@@ -217,7 +267,11 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a) {
         o[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, __builtin_bit_cast(bf16x8p, pl[nt]), o[dt][nt], 0, 0, 0);
       }
     }
-    if (tile + 1 < ntiles) stash(buf ^ 1);
+    if (tile + 1 < ntiles) {
+      stash(buf ^ 1);
+#pragma unroll
+      for (int j = 0; j < 3; ++j) id_c[j] = id_n[j];
+    }
     __syncthreads();
   }
 
