@@ -112,6 +112,16 @@ __device__ __forceinline__ T shfl_xor(T v, int m, int width = kWave) {
   return __shfl_xor(v, m, width);
 }
 
+// Workgroup barrier that orders LDS only: the release/acquire fences are
+// restricted to the local address space, so the barrier waits for the
+// wave's LDS operations but leaves its global loads in flight (a plain
+// __syncthreads also drains every outstanding global load).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));

@@ -38,6 +38,7 @@ constexpr int kKT = 32;                 // keys per tile
 constexpr int kD = 128;                 // head dim
 constexpr int kKRow = kD + 8;           // K tile row stride (bf16 elements) = 272 B
 constexpr int kVRow = 36;               // V^T tile row stride (bf16 elements) = 72 B
+constexpr int kListMax = 8192;          // largest block_top_k the kernel stages in LDS
 
 typedef float f32x2p __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2p __attribute__((ext_vector_type(2)));
@@ -51,6 +52,7 @@ __device__ __forceinline__ uint32_t pk_bf16(float x, float y) {
 __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kKT * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kD * kVRow];
+  __shared__ __attribute__((aligned(16))) int32_t s_list[kListMax];
 
   // ---- which (head, block): die-major, two heads per die, heavy first
   const int nh = a.B * a.H;
@@ -65,7 +67,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int l16 = lane & 15, jg = lane >> 4;
   const int q0 = blk * a.q_block;
   const int nq = min(a.q_block, a.N - q0);
-  const int c_sel = min(max(a.blk_count[(int64_t)bh * a.nblk + blk], 0), a.K);
+  const int c_sel = min(max(a.blk_count[(int64_t)bh * a.nblk + blk], 0), min(a.K, kListMax));
   const int32_t* list = a.blk_idx + ((int64_t)bh * a.nblk + blk) * a.K;
   const int T = c_sel + nq;
   const int ntiles = (T + kKT - 1) / kKT;
@@ -89,54 +91,58 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     }
   }
 
+  // ---- the block's selection, staged once in LDS
+  for (int i = tid; i < c_sel; i += kPfThreads) s_list[i] = list[i];
+
   // ---- gather roles: K (thread -> key t/8, 16 dims at 16*(t%8)),
   //      V (thread -> keys 2(t%16), 2(t%16)+1, 8 dims at 8*(t/16)).
   //      Entry e of the block's key sequence is selected entry e (a flat id)
   //      for e < c_sel, the block's own level-0 key q0 + e - c_sel below T,
-  //      and nothing (a zero row) past T.  A flat id outside the pyramid is
-  //      malformed and also reads as a zero row.
+  //      and nothing past T (masked out of the softmax).  A flat id outside
+  //      the pyramid is never dereferenced: it reads as a zero row.  Every
+  //      load goes to a valid row (row 0 stands in for the missing ones and
+  //      is zeroed), so the loads are unconditional and their waits exact.
   const int gk_key = tid >> 3, gk_seg = tid & 7;
   const int gv_kp = tid & 15, gv_seg = tid >> 4;
-  auto entry_id = [&](int e) -> int {
-    if (e < c_sel) return list[e];
-    if (e < T) return q0 + e - c_sel;
-    return -1;
+  auto entry_id = [&](int e, int listed) -> int {
+    return e < c_sel ? listed : (e < T ? q0 + e - c_sel : -1);
   };
-  auto row_ptr = [&](int f, bool is_v) -> const uint16_t* {
-    if ((unsigned)f >= (unsigned)(a.N + a.Nc)) return nullptr;
-    if (f < a.N) return (is_v ? vb : kb) + (int64_t)f * kD;
-    return (is_v ? pvb : pkb) + (int64_t)(f - a.N) * kD;
+  auto row_ptr = [&](int f, const uint16_t* b0, const uint16_t* bc, bool& ok) -> const uint16_t* {
+    const bool l0 = (unsigned)f < (unsigned)a.N;
+    const bool cr = (unsigned)(f - a.N) < (unsigned)a.Nc;
+    ok = l0 || cr;
+    const uint16_t* base = cr ? bc : b0;
+    const unsigned row = l0 ? (unsigned)f : (cr ? (unsigned)(f - a.N) : 0u);
+    return base + (size_t)row * kD;
   };
-  // ids run two tiles ahead of the rows, rows one tile ahead of the math
-  int id_c[3], id_n[3];
-  auto load_ids = [&](int tile, int* id) {
+  auto zero_if = [](bool ok, uint4 w) -> uint4 {
+    return make_uint4(ok ? w.x : 0u, ok ? w.y : 0u, ok ? w.z : 0u, ok ? w.w : 0u);
+  };
+  uint4 rk[2][2], rv[2][2];
+  bool okk[2], okv[2][2];
+  // issue the loads of one tile into a register set; tiles past the end load
+  // (and later discard) row 0
+  auto gather = [&](int tile, uint4* k2, uint4* v2, bool& ok_k, bool* ok_v) {
     const int e0 = tile * kKT;
-    id[0] = entry_id(e0 + gk_key);
-    id[1] = entry_id(e0 + 2 * gv_kp);
-    id[2] = entry_id(e0 + 2 * gv_kp + 1);
+    const int ek = e0 + gk_key, ev = e0 + 2 * gv_kp;
+    const int lk = s_list[min(ek, kListMax - 1)];
+    const int2 lv = *reinterpret_cast<const int2*>(&s_list[min(ev, kListMax - 2)]);
+    const uint16_t* pk = row_ptr(entry_id(ek, lk), kb, pkb, ok_k);
+    k2[0] = *reinterpret_cast<const uint4*>(pk + 16 * gk_seg);
+    k2[1] = *reinterpret_cast<const uint4*>(pk + 16 * gk_seg + 8);
+    const uint16_t* pv0 = row_ptr(entry_id(ev, lv.x), vb, pvb, ok_v[0]);
+    const uint16_t* pv1 = row_ptr(entry_id(ev + 1, lv.y), vb, pvb, ok_v[1]);
+    v2[0] = *reinterpret_cast<const uint4*>(pv0 + 8 * gv_seg);
+    v2[1] = *reinterpret_cast<const uint4*>(pv1 + 8 * gv_seg);
   };
-  uint4 rk[2], rv[2];
-  auto gather = [&](const int* id) {
-    const uint16_t* pk = row_ptr(id[0], false);
-    if (pk) {
-      rk[0] = *reinterpret_cast<const uint4*>(pk + 16 * gk_seg);
-      rk[1] = *reinterpret_cast<const uint4*>(pk + 16 * gk_seg + 8);
-    } else {
-      rk[0] = rk[1] = make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const uint16_t* pv = row_ptr(id[1 + r], true);
-      rv[r] = pv ? *reinterpret_cast<const uint4*>(pv + 8 * gv_seg) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto stash = [&](int buf) {
+  auto stash = [&](int buf, const uint4* k2, const uint4* v2, bool ok_k, const bool* ok_v) {
     uint16_t* kdst = s_k[buf] + gk_key * kKRow + 16 * gk_seg;
-    *reinterpret_cast<uint4*>(kdst) = rk[0];
-    *reinterpret_cast<uint4*>(kdst + 8) = rk[1];
+    *reinterpret_cast<uint4*>(kdst) = zero_if(ok_k, k2[0]);
+    *reinterpret_cast<uint4*>(kdst + 8) = zero_if(ok_k, k2[1]);
     // V^T: dims 8 gv_seg + i, keys 2 gv_kp and 2 gv_kp + 1 packed in one dword
-    const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&rv[0]);
-    const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&rv[1]);
+    const uint4 w0 = zero_if(ok_v[0], v2[0]), w1 = zero_if(ok_v[1], v2[1]);
+    const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&w0);
+    const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&w1);
     uint16_t* vdst = s_vt[buf] + (8 * gv_seg) * kVRow + 2 * gv_kp;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -155,17 +161,12 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     for (int nt = 0; nt < 2; ++nt) o[dt][nt] = (f32x4p){0.f, 0.f, 0.f, 0.f};
   const float sc = a.scale_log2;
 
-  if (ntiles > 0) {
-    load_ids(0, id_c);
-    gather(id_c);
-    if (ntiles > 1) load_ids(1, id_c);
-    stash(0);
-  }
-  __syncthreads();
-  for (int tile = 0; tile < ntiles; ++tile) {
+  // one tile of math; `set` (0 or 1, a constant after inlining) is the
+  // register set that held this tile and now takes tile + 2, so a tile's
+  // rows have two tiles of math to arrive
+  auto body = [&](const int tile, const int set) {
     const int buf = tile & 1;
-    if (tile + 2 < ntiles) load_ids(tile + 2, id_n);
-    if (tile + 1 < ntiles) gather(id_c);
+    gather(tile + 2, rk[set], rv[set], okk[set], okv[set]);
     const uint16_t* kt = s_k[buf];
     const uint16_t* vt = s_vt[buf];
     // S^T[key = 16 mt + 4 jg + i][q = 16 nt + l16]
@@ -185,15 +186,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
         s[mt][nt] = c;
       }
     }
-    // scale (log2 domain), mask only on tiles that reach past the selection
+    // mask only on tiles that reach past the selection
     const int e0 = tile * kKT;
-    float x[2][2][4];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[nt][mt][i] = s[mt][nt][i] * sc;
     if (e0 + kKT > c_sel) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
@@ -204,24 +198,25 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
           for (int i = 0; i < 4; ++i) {
             const int e = e0 + 16 * mt + 4 * jg + i;
             const bool ok = (e < c_sel) || (e < T && (e - c_sel) <= ql);
-            if (!ok) x[nt][mt][i] = -INFINITY;
+            if (!ok) s[mt][nt][i] = -INFINITY;
           }
       }
     }
-    // online softmax per query; P^T fragments as a bf16 high part and a bf16
-    // remainder (the weights keep ~16 bits through the second product)
+    // online softmax per query (log2 domain: p = 2^(s sc - m)); P^T
+    // fragments as a bf16 high part and a bf16 remainder (the weights keep
+    // ~16 bits through the second product)
     uint4 ph[2], pl[2];
     float alpha[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      float tmax = x[nt][0][0];
+      float tmax = s[0][nt][0];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, x[nt][mt][i]);
+        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[mt][nt][i]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mn = fmaxf(m[nt], tmax);
+      const float mn = fmaxf(m[nt], tmax * sc);
       const float msub = (mn == -INFINITY) ? 0.f : mn;   // a fully masked row stays at p = 0
       alpha[nt] = __builtin_amdgcn_exp2f(m[nt] - msub);
       m[nt] = mn;
@@ -229,7 +224,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[4 * mt + i] = __builtin_amdgcn_exp2f(x[nt][mt][i] - msub);
+        for (int i = 0; i < 4; ++i) p[4 * mt + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][nt][i], sc, -msub));
       float ps = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) ps += p[j];
@@ -267,13 +262,26 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
         o[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, __builtin_bit_cast(bf16x8p, pl[nt]), o[dt][nt], 0, 0, 0);
       }
     }
-    if (tile + 1 < ntiles) {
-      stash(buf ^ 1);
-#pragma unroll
-      for (int j = 0; j < 3; ++j) id_c[j] = id_n[j];
-    }
-    __syncthreads();
+    // unconditional (past the end it stages rows nobody reads), so that the
+    // wait for this set's loads is the same on every path
+    stash(buf ^ 1, rk[set ^ 1], rv[set ^ 1], okk[set ^ 1], okv[set ^ 1]);
+    lds_barrier();
+  };
+
+  // prologue: tiles 0 and 1 in flight, tile 0 staged
+  lds_barrier();                                    // s_list complete
+  gather(0, rk[0], rv[0], okk[0], okv[0]);
+  gather(1, rk[1], rv[1], okk[1], okv[1]);
+  stash(0, rk[0], rv[0], okk[0], okv[0]);
+  lds_barrier();
+  // pairs of tiles, then an odd last one: every path back to the loop head
+  // passes both bodies, so the loads in flight there are always set 1's
+  int tile = 0;
+  for (; tile + 1 < ntiles; tile += 2) {
+    body(tile, 0);
+    body(tile + 1, 1);
   }
+  if (tile < ntiles) body(tile, 0);
 
   // ---- normalise and write: lane holds d = 16 dt + 4 jg + 0..3 of query
   //      32w + 16 nt + l16
@@ -297,7 +305,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int d, hipStream_t s) {
-  if (d != kD || a.q_block != 128) return hipErrorInvalidValue;
+  if (d != kD || a.q_block != 128 || a.K > kListMax) return hipErrorInvalidValue;
   const int nh = a.B * a.H;
   const int hpx = (nh + 7) / 8;
   dim3 grid(8 * hpx * a.nblk);

@@ -182,3 +182,21 @@ def test_pyramid_validation():
     pf = mk(dtype="fp32")
     assert sa.raw_call("prefill_chunked", ctypes.byref(pf), ctypes.byref(b), None,
                        ctypes.byref(n), None) == sa.SA_ERR_UNSUPPORTED
+
+
+def test_prefill_limits():
+    """The chunked prefill stages a block's selection in LDS: block_top_k
+    above 8192 is refused before anything is launched."""
+    b = _full_bufs()
+    ok = dict(batch=1, n_q_heads=4, n_kv_heads=4, head_dim=128, n_ctx=1024, levels=3, factor=4,
+              q_block=128, block_top_k=8192)
+    n = ctypes.c_size_t(0)
+    pf = sa.make_params(**ok)
+    assert sa.raw_call("prefill_chunked", ctypes.byref(pf), ctypes.byref(b), None,
+                       ctypes.byref(n), None) == sa.SA_OK
+    pf = sa.make_params(**{**ok, "block_top_k": 8193})
+    assert sa.raw_call("prefill_chunked", ctypes.byref(pf), ctypes.byref(b), None,
+                       ctypes.byref(n), None) == sa.SA_ERR_UNSUPPORTED
+    pf = sa.make_params(**{**ok, "head_dim": 64})
+    assert sa.raw_call("prefill_chunked", ctypes.byref(pf), ctypes.byref(b), None,
+                       ctypes.byref(n), None) == sa.SA_ERR_UNSUPPORTED
