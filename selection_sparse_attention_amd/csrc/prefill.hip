@@ -32,6 +32,7 @@ namespace sa {
 
 typedef __bf16 bf16x8p __attribute__((ext_vector_type(8)));
 typedef float f32x4p __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4p __attribute__((ext_vector_type(4)));
 
 constexpr int kPfThreads = 256;
 constexpr int kKT = 32;                 // keys per tile
@@ -39,6 +40,8 @@ constexpr int kD = 128;                 // head dim
 constexpr int kKRow = kD + 8;           // K tile row stride (bf16 elements) = 272 B
 constexpr int kVRow = 36;               // V^T tile row stride (bf16 elements) = 72 B
 constexpr int kListMax = 8192;          // largest block_top_k the kernel stages in LDS
+constexpr int kSeqMax = kListMax + 128 + 4 * kKT;   // + own keys + tail the gathers run past
+constexpr uint32_t kCoarse = 0x80000000u;           // staged entry: coarse row flag
 
 typedef float f32x2p __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2p __attribute__((ext_vector_type(2)));
@@ -49,10 +52,22 @@ __device__ __forceinline__ uint32_t pk_bf16(float x, float y) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2p){x, y}, bf16x2p));
 }
 
+// max over the four lanes l16 + 16 jg (jg = 0..3) that hold one query's
+// scores: a swap of the wave's halves, then of neighbouring 16-lane rows
+// (both VALU, no LDS round trip)
+__device__ __forceinline__ float max_over_lane_groups(float v) {
+  const auto h = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
+                                                  __builtin_bit_cast(uint32_t, v), false, false);
+  v = fmaxf(__builtin_bit_cast(float, h[0]), __builtin_bit_cast(float, h[1]));
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
+                                                  __builtin_bit_cast(uint32_t, v), false, false);
+  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+
 __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kKT * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kD * kVRow];
-  __shared__ __attribute__((aligned(16))) int32_t s_list[kListMax];
+  __shared__ __attribute__((aligned(16))) uint32_t s_seq[kSeqMax];
 
   // ---- which (head, block): die-major, two heads per die, heavy first
   const int nh = a.B * a.H;
@@ -91,65 +106,63 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     }
   }
 
-  // ---- the block's selection, staged once in LDS
-  for (int i = tid; i < c_sel; i += kPfThreads) s_list[i] = list[i];
+  // ---- the block's key sequence, staged once in LDS as row references:
+  //      selected entry e < c_sel (a flat id: level-0 row, or coarse row
+  //      flagged kCoarse), then the block's own level-0 keys q0 .. q0+nq-1,
+  //      then row 0 for the tail that the two-ahead gathers run past (masked
+  //      out of the softmax).  A flat id outside the pyramid is clamped to
+  //      level-0 row 0 - never dereferenced out of bounds; its contribution
+  //      is unspecified.
+  {
+    const int n_stage = (ntiles + 2) * kKT;
+    for (int e = tid; e < n_stage; e += kPfThreads) {
+      uint32_t r = 0u;
+      if (e < c_sel) {
+        const int f = list[e];
+        if ((unsigned)f < (unsigned)a.N) r = (uint32_t)f;
+        else if ((unsigned)(f - a.N) < (unsigned)a.Nc) r = (uint32_t)(f - a.N) | kCoarse;
+      } else if (e < T) {
+        r = (uint32_t)(q0 + e - c_sel);
+      }
+      s_seq[e] = r;
+    }
+  }
 
   // ---- gather roles: K (thread -> key t/8, 16 dims at 16*(t%8)),
   //      V (thread -> keys 2(t%16), 2(t%16)+1, 8 dims at 8*(t/16)).
-  //      Entry e of the block's key sequence is selected entry e (a flat id)
-  //      for e < c_sel, the block's own level-0 key q0 + e - c_sel below T,
-  //      and nothing past T (masked out of the softmax).  A flat id outside
-  //      the pyramid is never dereferenced: it reads as a zero row.  Every
-  //      load goes to a valid row (row 0 stands in for the missing ones and
-  //      is zeroed), so the loads are unconditional and their waits exact.
   const int gk_key = tid >> 3, gk_seg = tid & 7;
   const int gv_kp = tid & 15, gv_seg = tid >> 4;
-  auto entry_id = [&](int e, int listed) -> int {
-    return e < c_sel ? listed : (e < T ? q0 + e - c_sel : -1);
+  auto row_ptr = [](uint32_t r, const uint16_t* b0, const uint16_t* bc) -> const uint16_t* {
+    const uint16_t* base = (r & kCoarse) ? bc : b0;
+    return base + (size_t)(r & ~kCoarse) * kD;
   };
-  auto row_ptr = [&](int f, const uint16_t* b0, const uint16_t* bc, bool& ok) -> const uint16_t* {
-    const bool l0 = (unsigned)f < (unsigned)a.N;
-    const bool cr = (unsigned)(f - a.N) < (unsigned)a.Nc;
-    ok = l0 || cr;
-    const uint16_t* base = cr ? bc : b0;
-    const unsigned row = l0 ? (unsigned)f : (cr ? (unsigned)(f - a.N) : 0u);
-    return base + (size_t)row * kD;
-  };
-  auto zero_if = [](bool ok, uint4 w) -> uint4 {
-    return make_uint4(ok ? w.x : 0u, ok ? w.y : 0u, ok ? w.z : 0u, ok ? w.w : 0u);
-  };
-  uint4 rk[2][2], rv[2][2];
-  bool okk[2], okv[2][2];
-  // issue the loads of one tile into a register set; tiles past the end load
-  // (and later discard) row 0
-  auto gather = [&](int tile, uint4* k2, uint4* v2, bool& ok_k, bool* ok_v) {
+  struct Rows { u32x4p k0, k1, v0, v1; };         // one tile's loads for this thread
+  // issue the loads of one tile (unconditionally: past the end they read
+  // row 0, which is never used)
+  auto gather = [&](int tile, Rows& r) __attribute__((always_inline)) {
     const int e0 = tile * kKT;
-    const int ek = e0 + gk_key, ev = e0 + 2 * gv_kp;
-    const int lk = s_list[min(ek, kListMax - 1)];
-    const int2 lv = *reinterpret_cast<const int2*>(&s_list[min(ev, kListMax - 2)]);
-    const uint16_t* pk = row_ptr(entry_id(ek, lk), kb, pkb, ok_k);
-    k2[0] = *reinterpret_cast<const uint4*>(pk + 16 * gk_seg);
-    k2[1] = *reinterpret_cast<const uint4*>(pk + 16 * gk_seg + 8);
-    const uint16_t* pv0 = row_ptr(entry_id(ev, lv.x), vb, pvb, ok_v[0]);
-    const uint16_t* pv1 = row_ptr(entry_id(ev + 1, lv.y), vb, pvb, ok_v[1]);
-    v2[0] = *reinterpret_cast<const uint4*>(pv0 + 8 * gv_seg);
-    v2[1] = *reinterpret_cast<const uint4*>(pv1 + 8 * gv_seg);
+    const uint32_t lk = s_seq[e0 + gk_key];
+    const uint2 lv = *reinterpret_cast<const uint2*>(&s_seq[e0 + 2 * gv_kp]);
+    const uint16_t* pk = row_ptr(lk, kb, pkb);
+    r.k0 = *reinterpret_cast<const u32x4p*>(pk + 16 * gk_seg);
+    r.k1 = *reinterpret_cast<const u32x4p*>(pk + 16 * gk_seg + 8);
+    r.v0 = *reinterpret_cast<const u32x4p*>(row_ptr(lv.x, vb, pvb) + 8 * gv_seg);
+    r.v1 = *reinterpret_cast<const u32x4p*>(row_ptr(lv.y, vb, pvb) + 8 * gv_seg);
   };
-  auto stash = [&](int buf, const uint4* k2, const uint4* v2, bool ok_k, const bool* ok_v) {
+  auto stash = [&](int buf, const Rows& r) __attribute__((always_inline)) {
     uint16_t* kdst = s_k[buf] + gk_key * kKRow + 16 * gk_seg;
-    *reinterpret_cast<uint4*>(kdst) = zero_if(ok_k, k2[0]);
-    *reinterpret_cast<uint4*>(kdst + 8) = zero_if(ok_k, k2[1]);
+    *reinterpret_cast<u32x4p*>(kdst) = r.k0;
+    *reinterpret_cast<u32x4p*>(kdst + 8) = r.k1;
     // V^T: dims 8 gv_seg + i, keys 2 gv_kp and 2 gv_kp + 1 packed in one dword
-    const uint4 w0 = zero_if(ok_v[0], v2[0]), w1 = zero_if(ok_v[1], v2[1]);
-    const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&w0);
-    const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&w1);
     uint16_t* vdst = s_vt[buf] + (8 * gv_seg) * kVRow + 2 * gv_kp;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t a0 = v0[i], a1 = v1[i];
-      *reinterpret_cast<uint32_t*>(vdst + (2 * i) * kVRow) = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-      *reinterpret_cast<uint32_t*>(vdst + (2 * i + 1) * kVRow) = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
-    }
+    auto put = [&](int i, uint32_t x0, uint32_t x1) __attribute__((always_inline)) {
+      *reinterpret_cast<uint32_t*>(vdst + (2 * i) * kVRow) = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
+      *reinterpret_cast<uint32_t*>(vdst + (2 * i + 1) * kVRow) = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
+    };
+    put(0, r.v0[0], r.v1[0]);
+    put(1, r.v0[1], r.v1[1]);
+    put(2, r.v0[2], r.v1[2]);
+    put(3, r.v0[3], r.v1[3]);
   };
 
   // ---- running state for queries 32w + 16nt + l16
@@ -161,12 +174,12 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     for (int nt = 0; nt < 2; ++nt) o[dt][nt] = (f32x4p){0.f, 0.f, 0.f, 0.f};
   const float sc = a.scale_log2;
 
-  // one tile of math; `set` (0 or 1, a constant after inlining) is the
-  // register set that held this tile and now takes tile + 2, so a tile's
-  // rows have two tiles of math to arrive
-  auto body = [&](const int tile, const int set) {
+  // one tile of math: `mine` held this tile's rows and now takes those of
+  // tile + 2 (so a tile's rows have two tiles of math to arrive); `next`
+  // holds tile + 1, staged at the end
+  auto body = [&](const int tile, Rows& mine, const Rows& next) __attribute__((always_inline)) {
     const int buf = tile & 1;
-    gather(tile + 2, rk[set], rv[set], okk[set], okv[set]);
+    gather(tile + 2, mine);
     const uint16_t* kt = s_k[buf];
     const uint16_t* vt = s_vt[buf];
     // S^T[key = 16 mt + 4 jg + i][q = 16 nt + l16]
@@ -214,8 +227,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[mt][nt][i]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      tmax = max_over_lane_groups(tmax);
       const float mn = fmaxf(m[nt], tmax * sc);
       const float msub = (mn == -INFINITY) ? 0.f : mn;   // a fully masked row stays at p = 0
       alpha[nt] = __builtin_amdgcn_exp2f(m[nt] - msub);
@@ -264,24 +276,25 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     }
     // unconditional (past the end it stages rows nobody reads), so that the
     // wait for this set's loads is the same on every path
-    stash(buf ^ 1, rk[set ^ 1], rv[set ^ 1], okk[set ^ 1], okv[set ^ 1]);
+    stash(buf ^ 1, next);
     lds_barrier();
   };
 
   // prologue: tiles 0 and 1 in flight, tile 0 staged
-  lds_barrier();                                    // s_list complete
-  gather(0, rk[0], rv[0], okk[0], okv[0]);
-  gather(1, rk[1], rv[1], okk[1], okv[1]);
-  stash(0, rk[0], rv[0], okk[0], okv[0]);
+  lds_barrier();                                    // s_seq complete
+  Rows ra, rb;
+  gather(0, ra);
+  gather(1, rb);
+  stash(0, ra);
   lds_barrier();
   // pairs of tiles, then an odd last one: every path back to the loop head
   // passes both bodies, so the loads in flight there are always set 1's
   int tile = 0;
   for (; tile + 1 < ntiles; tile += 2) {
-    body(tile, 0);
-    body(tile + 1, 1);
+    body(tile, ra, rb);
+    body(tile + 1, rb, ra);
   }
-  if (tile < ntiles) body(tile, 0);
+  if (tile < ntiles) body(tile, ra, rb);
 
   // ---- normalise and write: lane holds d = 16 dt + 4 jg + 0..3 of query
   //      32w + 16 nt + l16
