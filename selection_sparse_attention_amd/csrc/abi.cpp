@@ -3,6 +3,7 @@
 // allocates, frees, copies to the host or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -141,8 +142,21 @@ SelectWs carve_select(void* ws, int rows, int n) {
 
 // ---------------------------------------------------------------- decode ws
 constexpr int kDecodeTps = 256;           // fp32 caches: list entries per split
-constexpr int kDecodeTpsMfma = 256;       // bf16 caches
+constexpr int kDecodeMinChunk = 128;      // bf16 caches: smallest work item (list entries)
+constexpr int kMaxDecodeItems = 8192;     // bf16 caches: work items one launch may hold
 constexpr int kMaxDecodeSplits = 8192;     // contexts up to 2M tokens
+
+// Compute units of the current device (queried once per device).
+int compute_units() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cache[dev] = n;
+  return n;
+}
 
 int decode_max_count(const sa_params* p, const int8_t* kinds) {
   int mc = 0;
@@ -353,12 +367,24 @@ int32_t sparse_attn_decode(const sa_params* p, const sa_buffers* b, void* ws, si
   }
   if (any_local && (p->sinks < 0 || p->window < 0 || (int64_t)p->sinks + p->window < 1))
     return SA_ERR_INVALID_ARG;
-  const int max_count = decode_max_count(p, kinds);
-  const int tps = (p->dtype == SA_BF16) ? kDecodeTpsMfma : kDecodeTps;
-  const int max_splits = (max_count + tps - 1) / tps;
-  if (max_splits > kMaxDecodeSplits) return SA_ERR_UNSUPPORTED;
+  int tps = kDecodeTps, max_splits, target_items = 0;
+  size_t n_partial;
+  if (p->dtype == SA_BF16) {
+    // work items: the step's visible tokens spread over about two
+    // workgroups per compute unit; the plan itself is made on the device
+    const int groups = p->batch * p->n_kv_heads;
+    target_items = std::max(64, 2 * compute_units() - groups);
+    max_splits = target_items + groups;        // bound on the item count
+    if (max_splits > kMaxDecodeItems) return SA_ERR_UNSUPPORTED;
+    n_partial = (size_t)max_splits * G * (p->head_dim + 2);
+  } else {
+    const int max_count = decode_max_count(p, kinds);
+    max_splits = (max_count + tps - 1) / tps;
+    if (max_splits > kMaxDecodeSplits) return SA_ERR_UNSUPPORTED;
+    n_partial = (size_t)p->batch * p->n_q_heads * max_splits * (p->head_dim + 2);
+  }
   Carver c(ws);
-  float* partial = c.take<float>((size_t)p->batch * p->n_q_heads * max_splits * (p->head_dim + 2));
+  float* partial = c.take<float>(n_partial);
   if ((st = workspace_gate(ws, ws_bytes, c.size()))) return st < 0 ? st : SA_OK;
   if (!b->q || !b->k_cache || !b->v_cache || !b->out) return SA_ERR_INVALID_ARG;
   if (any_list && (!b->sel_idx || !b->sel_count)) return SA_ERR_INVALID_ARG;
@@ -370,6 +396,8 @@ int32_t sparse_attn_decode(const sa_params* p, const sa_buffers* b, void* ws, si
   a.G = G; a.sinks = p->sinks; a.window = p->window; a.tps = tps; a.max_splits = max_splits;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->head_dim));
   a.local_mask = local_mask;
+  a.target_items = target_items;
+  a.min_chunk = kDecodeMinChunk;
   return hip_status(sa::launch_decode(a, p->dtype, p->head_dim, static_cast<hipStream_t>(stream)));
 }
 

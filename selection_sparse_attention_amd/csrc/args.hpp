@@ -119,10 +119,12 @@ struct DecodeArgs {
   float* out;             // [B,Hq,d]
   float* partial;         // [B,Hq,max_splits,d+2]
   int32_t B, Hq, Hkv, n, n_cap, G, sinks, window;
-  int32_t tps;            // tokens per split
-  int32_t max_splits;
+  int32_t tps;            // tokens per split (fp32 path)
+  int32_t max_splits;     // fp32 path: splits per group; bf16 path: work items
   float scale_log2;       // log2(e) / sqrt(d)
   uint64_t local_mask;    // bit g set: group g is local
+  int32_t target_items;   // bf16 path: work items the visible tokens are spread over
+  int32_t min_chunk;      // bf16 path: smallest item (list entries)
 };
 
 struct PrefillArgs {

@@ -226,10 +226,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 template <typename T, int D>
 static hipError_t run_decode(const DecodeArgs& a, hipStream_t s) {
   dim3 grid(a.max_splits, a.Hkv, a.B);
-  if (std::is_same<T, bf16_t>::value) {        // bf16 caches: matrix-core kernel
-    const hipError_t e = launch_decode_mfma(a, D, s);
-    if (e != hipSuccess) return e;
-  } else switch (a.G) {
+  switch (a.G) {
     case 1: hipLaunchKernelGGL((decode_split_kernel<T, D, 1>), grid, dim3(kDecThreads), 0, s, a); break;
     case 2: hipLaunchKernelGGL((decode_split_kernel<T, D, 2>), grid, dim3(kDecThreads), 0, s, a); break;
     case 4: hipLaunchKernelGGL((decode_split_kernel<T, D, 4>), grid, dim3(kDecThreads), 0, s, a); break;
@@ -242,8 +239,7 @@ static hipError_t run_decode(const DecodeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, hipStream_t s) {
-  if (dtype == 0 && d == 128) return run_decode<bf16_t, 128>(a, s);
-  if (dtype == 0 && d == 64) return run_decode<bf16_t, 64>(a, s);
+  if (dtype == 0) return launch_decode_mfma(a, d, s);      // bf16 caches: matrix-core path
   if (dtype == 1 && d == 128) return run_decode<float, 128>(a, s);
   if (dtype == 1 && d == 64) return run_decode<float, 64>(a, s);
   return hipErrorInvalidValue;

@@ -8,6 +8,14 @@
 // non-contiguous rows): for every query head h of KV group g,
 //   o_h = sum_{j in T_g} softmax_j(q_h . k_j / sqrt(d)) v_j .
 //
+// Work plan: the visible tokens of all (sequence, KV group) pairs are cut into
+// items of `chunk` consecutive list entries, with chunk = total / target
+// (rounded up to 64), so that the items of the whole step - however the
+// selected counts are distributed - fill the chip about once.  Every
+// workgroup derives the same plan from the counts (a block reduction and a
+// scan over the groups, no extra launch) and takes item blockIdx.x; the
+// combine launch re-derives it to find each head's items.
+//
 // Layout per wave, one 16-token tile at a time:
 //   * lane l gathers d/4 consecutive K elements of token (l % 16): the four
 //     lanes of a token cover its row, and they are exactly the B operand of
@@ -20,8 +28,10 @@
 //   * lane l owns output dims 2(l % (d/2)) .. +1 and, for d = 64, every
 //     second token of the tile; it gathers those V pairs with 4-byte loads
 //     (one 256-byte row per wave instruction) and accumulates G heads in fp32.
-//   * the next tile's K and V loads are in flight while a tile is computed.
-// Splits are merged by the same combine kernel as the fp32 path.
+//   * token ids stream from the list three tiles ahead and K/V rows two tiles
+//     ahead (three register sets in rotation); every load is unconditional
+//     (rows past the end read the group's row 0 and are masked), so each wait
+//     is a partial one and two tiles of loads stay in flight.
 #include "args.hpp"
 #include "common.hpp"
 
@@ -29,8 +39,10 @@ namespace sa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaThreads = 256;
+constexpr int kMaxItemsLds = 8192;           // items one combine workgroup merges
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
@@ -53,6 +65,52 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// ---------------------------------------------------------------- work plan
+__device__ __forceinline__ int group_count(const DecodeArgs& a, int bg) {
+  const int g = bg % a.Hkv;
+  if ((a.local_mask >> g) & 1ull) {
+    const int s = min(a.sinks, a.n);
+    return s + (a.n - max(s, a.n - a.window));
+  }
+  return min(max(a.sel_count[bg], 0), a.n);
+}
+
+// The item size: all visible tokens over target_items items, rounded up to
+// 64 entries, at least min_chunk.  Identical in every workgroup.
+__device__ int plan_chunk(const DecodeArgs& a, int64_t* s_scan) {
+  int64_t t = 0;
+  for (int bg = threadIdx.x; bg < a.B * a.Hkv; bg += kMfmaThreads) t += group_count(a, bg);
+  int64_t tot;
+  (void)block_exclusive_scan<int64_t, kMfmaThreads>(t, s_scan, &tot);
+  int64_t c = (tot + a.target_items - 1) / a.target_items;
+  c = (c + 63) / 64 * 64;
+  return (int)(c > a.min_chunk ? c : a.min_chunk);
+}
+
+// Number the items group by group (ceil(count / chunk) each).  Leaves in
+// s_out: [0] the group of item `item` (-1 when the plan has fewer items),
+// [1] its split within the group, [2] the first item of group `want`, [3]
+// that group's item count.
+__device__ void plan_walk(const DecodeArgs& a, int chunk, int item, int want, int* s_scan,
+                          int* s_out) {
+  if (threadIdx.x == 0) { s_out[0] = -1; s_out[1] = 0; s_out[2] = 0; s_out[3] = 0; }
+  __syncthreads();
+  const int ng = a.B * a.Hkv;
+  int carry = 0;
+  for (int base = 0; base < ng; base += kMfmaThreads) {
+    const int bg = base + threadIdx.x;
+    const int ns = (bg < ng) ? (group_count(a, bg) + chunk - 1) / chunk : 0;
+    int tot;
+    const int first = carry + block_exclusive_scan<int, kMfmaThreads>(ns, s_scan, &tot);
+    if (bg < ng) {
+      if (item >= first && item < first + ns) { s_out[0] = bg; s_out[1] = item - first; }
+      if (bg == want) { s_out[2] = first; s_out[3] = ns; }
+    }
+    carry += tot;
+  }
+  __syncthreads();
+}
+
 template <int D>
 struct Tile {
   static constexpr int KS = D / 32;            // MFMA k-steps
@@ -60,99 +118,90 @@ struct Tile {
   static constexpr int VT = 16 / NCLS;         // V rows per lane per tile
   bf16x8 k[KS];
   uint32_t v[VT];
+  int tok;                                     // this lane's K-role token, -1 if none
 };
 
 template <int D, int G>
-__global__ __launch_bounds__(kMfmaThreads) void decode_mfma_kernel(DecodeArgs a) {
+struct DecodeShared {
+  int64_t scan64[kMfmaThreads / 64];
+  int scan32[kMfmaThreads / 64];
+  int plan[4];
+  float p[4][16][8];                           // per wave: p[token][head]
+  float m[4][8], l[4][8];
+  float acc[4][8][D];
+};
+
+template <int D, int G, bool LOCAL>
+__device__ __forceinline__ void decode_item(const DecodeArgs& a, DecodeShared<D, G>& sh, int item,
+                                            int bg, int split, int chunk) {
   using TL = Tile<D>;
   constexpr int KS = TL::KS, NCLS = TL::NCLS, VT = TL::VT;
   constexpr int DPL = D / 4;                   // K elements per lane
-  constexpr int HG = (G + 3) / 4;              // lane groups holding heads
   static_assert(G <= 8, "at most 8 query heads per KV group");
-  __shared__ int s_list[kMaxTps + 64];
-  __shared__ float s_p[4][16][8];              // per wave: p[token][head]
-  __shared__ float s_m[4][8], s_l[4][8];
-  __shared__ float s_acc[4][8][D];
-
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const bool local = (a.local_mask >> g) & 1ull;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int n = a.n;
-  int count, s_eff = 0, ws = 0;
-  if (local) {
+  int s_eff = 0, wst = 0, count;
+  if (LOCAL) {
     s_eff = min(a.sinks, n);
-    ws = max(s_eff, n - a.window);
-    count = s_eff + (n - ws);
+    wst = max(s_eff, n - a.window);
+    count = s_eff + (n - wst);
   } else {
-    count = min(max(a.sel_count[(int64_t)b * a.Hkv + g], 0), n);
+    count = min(max(a.sel_count[bg], 0), n);
   }
-  const int start = split * a.tps;
-  if (start >= count) return;
-  const int end = min(count, start + a.tps);
-  const int64_t row0 = ((int64_t)b * a.Hkv + g) * a.n_cap;
+  const int start = split * chunk;
+  const int len = min(chunk, count - start);
+  const int64_t row0 = (int64_t)bg * a.n_cap;
 
-  // this split's token positions, staged once
-  for (int i = tid; i < end - start; i += kMfmaThreads) {
-    const int e = start + i;
-    int tok = local ? (e < s_eff ? e : ws + (e - s_eff)) : a.sel_idx[row0 + e];
-    s_list[i] = ((unsigned)tok < (unsigned)n) ? tok : -1;
-  }
   // query fragment: head (lane % 16), this lane's slice of the k mapping
   bf16x8 qf[KS];
   {
-    const int h = lane & 15, jg = lane >> 4;
+    const int h = lane & 15, jq = lane >> 4;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
+      u32x4 w = {0u, 0u, 0u, 0u};
       if (h < G) {
         const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                             ((int64_t)b * a.Hq + g * G + h) * D + jg * DPL + 8 * s;
-        uint4 w = *reinterpret_cast<const uint4*>(qp);
-        qf[s] = __builtin_bit_cast(bf16x8, w);
-      } else {
-        qf[s] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+                             ((int64_t)b * a.Hq + g * G + h) * D + jq * DPL + 8 * s;
+        w = *reinterpret_cast<const u32x4*>(qp);
       }
+      qf[s] = __builtin_bit_cast(bf16x8, w);
     }
   }
-  __syncthreads();
 
-  // this wave's contiguous share of the split
-  const int len = end - start;
-  const int per_wave = (((len + 3) / 4) + 15) & ~15;   // whole 16-token tiles
-  const int w0 = wid * per_wave, w1 = min(len, w0 + per_wave);
+  // this wave's contiguous share of the item, in whole 16-token tiles
+  const int per_wave = (((len + 3) / 4) + 15) & ~15;
+  const int w0 = start + wid * per_wave, w1 = min(start + len, w0 + per_wave);
   const int ntiles = (w1 > w0) ? (w1 - w0 + 15) / 16 : 0;
 
   const int kt = lane & 15, jg = lane >> 4;            // K role
   const int vd = 2 * (lane % (D / 2)), vc = lane / (D / 2);   // V role
-  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k);
-  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v);
+  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + row0 * D + jg * DPL;
+  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v) + row0 * D + vd;
 
-  auto load_tile = [&](TL& t, int tile) {
-    const int i0 = w0 + tile * 16;
-    const int ik = i0 + kt;
-    const int tok = (ik < w1) ? s_list[ik] : -1;
-    if (tok >= 0) {
-      const uint16_t* kp = kbase + (row0 + tok) * D + jg * DPL;
+  // raw list entry of this lane's token in a tile (a load for listed groups,
+  // in bounds even past the end; checked when it is used)
+  auto raw_id = [&](int tile) __attribute__((always_inline)) -> int {
+    const int e = w0 + tile * 16 + kt;
+    if (LOCAL) return (e < s_eff) ? e : wst + (e - s_eff);
+    return a.sel_idx[row0 + min(e, w1 - 1)];
+  };
+  // issue a tile's K and V loads
+  auto issue = [&](int tile, TL& t, int raw) __attribute__((always_inline)) {
+    const int e = w0 + tile * 16 + kt;
+    const int tok = (e < w1 && (unsigned)raw < (unsigned)n) ? raw : -1;
+    t.tok = tok;
+    const uint16_t* kp = kbase + (int64_t)max(tok, 0) * D;
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        t.k[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kp + 8 * s));
-    } else {
-#pragma unroll
-      for (int s = 0; s < KS; ++s) t.k[s] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-    }
-    // the tile's 16 positions, read as a broadcast (i0 is a multiple of 16)
-    int idx16[16];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int4 w = *reinterpret_cast<const int4*>(&s_list[i0 + 4 * q4]);
-      idx16[4 * q4 + 0] = w.x; idx16[4 * q4 + 1] = w.y;
-      idx16[4 * q4 + 2] = w.z; idx16[4 * q4 + 3] = w.w;
-    }
+    for (int s = 0; s < KS; ++s) t.k[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + 8 * s));
 #pragma unroll
     for (int r = 0; r < VT; ++r) {
-      const int iv = i0 + r * NCLS + vc;
-      const int tv0 = idx16[r * NCLS], tv1 = idx16[r * NCLS + (NCLS - 1)];
-      const int tv = (iv < w1) ? (vc ? tv1 : tv0) : -1;
-      t.v[r] = (tv >= 0) ? *reinterpret_cast<const uint32_t*>(vbase + (row0 + tv) * D + vd) : 0u;
+      int tv = __builtin_amdgcn_readlane(tok, r * NCLS);
+      if (NCLS == 2) {
+        const int tv1 = __builtin_amdgcn_readlane(tok, r * NCLS + 1);
+        tv = vc ? tv1 : tv;
+      }
+      t.v[r] = *reinterpret_cast<const uint32_t*>(vbase + (int64_t)max(tv, 0) * D);
     }
   };
 
@@ -163,16 +212,16 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma_kernel(DecodeArgs a)
   for (int i = 0; i < 4; ++i) lsum[i] = 0.f;
   const float sc = a.scale_log2;
 
-  auto compute_tile = [&](const TL& t, int tile) {
+  auto compute = [&](const TL& t) __attribute__((always_inline)) {
     f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[s], t.k[s], c, 0, 0, 0);
-    const int i0 = w0 + tile * 16;
-    const bool valid = (i0 + kt < w1) && (s_list[i0 + kt] >= 0);
+    const bool valid = t.tok >= 0;
     float sv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sv[i] = valid ? c[i] * sc : -INFINITY;
     float alpha[G];
+    bool moved = false;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const int grp = h >> 2, r = h & 3;
@@ -181,23 +230,26 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma_kernel(DecodeArgs a)
           __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tm), 16 * grp));
       const float mn = fmaxf(m[h], tmax);
       alpha[h] = (m[h] == mn) ? 1.f : exp2f(m[h] - mn);
+      moved |= (m[h] != mn);
       m[h] = mn;
       if (jg == grp) {
         const float p = (sv[r] == -INFINITY) ? 0.f : exp2f(sv[r] - mn);
         lsum[r] = lsum[r] * alpha[h] + p;
-        s_p[wid][kt][h] = p;
+        sh.p[wid][kt][h] = p;
       }
     }
     __builtin_amdgcn_wave_barrier();
+    if (moved) {                                 // wave-uniform: m is uniform
 #pragma unroll
-    for (int h = 0; h < G; ++h) { acc[h][0] *= alpha[h]; acc[h][1] *= alpha[h]; }
+      for (int h = 0; h < G; ++h) { acc[h][0] *= alpha[h]; acc[h][1] *= alpha[h]; }
+    }
 #pragma unroll
     for (int r = 0; r < VT; ++r) {
       const int tt = r * NCLS + vc;
       const float v0 = bf16_lo(t.v[r]), v1 = bf16_hi(t.v[r]);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float p = s_p[wid][tt][h];
+        const float p = sh.p[wid][tt][h];
         acc[h][0] = fmaf(p, v0, acc[h][0]);
         acc[h][1] = fmaf(p, v1, acc[h][1]);
       }
@@ -205,15 +257,29 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma_kernel(DecodeArgs a)
     __builtin_amdgcn_wave_barrier();
   };
 
-  TL ta, tb;
-  if (ntiles > 0) load_tile(ta, 0);
-  for (int tile = 0; tile < ntiles; tile += 2) {
-    if (tile + 1 < ntiles) load_tile(tb, tile + 1);
-    compute_tile(ta, tile);
-    if (tile + 1 < ntiles) {
-      if (tile + 2 < ntiles) load_tile(ta, tile + 2);
-      compute_tile(tb, tile + 1);
+  if (ntiles > 0) {
+    TL ta, tb, tc;
+    const int r0 = raw_id(0);
+    const int r1 = raw_id(1);
+    issue(0, ta, r0);
+    issue(1, tb, r1);
+    int rawp = raw_id(2);
+    // one step: ids of tile t+3 requested, rows of tile t+2 issued, tile t
+    // computed
+    auto step = [&](int tl, TL& cur, TL& ahead2) __attribute__((always_inline)) {
+      const int rn = raw_id(tl + 3);
+      issue(tl + 2, ahead2, rawp);
+      rawp = rn;
+      compute(cur);
+    };
+    int t = 0;
+    for (; t + 2 < ntiles; t += 3) {
+      step(t, ta, tc);
+      step(t + 1, tb, ta);
+      step(t + 2, tc, tb);
     }
+    if (t < ntiles) step(t, ta, tc);
+    if (t + 1 < ntiles) step(t + 1, tb, ta);
   }
 
   // wave result: l from the lanes of each head's group, acc from all lanes
@@ -232,45 +298,107 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma_kernel(DecodeArgs a)
     const float ls = row16_sum(lsum[r]);
     lw[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ls), 16 * grp));
   }
-  (void)HG;
   if (lane < D / 2) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      s_acc[wid][h][vd] = acc[h][0];
-      s_acc[wid][h][vd + 1] = acc[h][1];
+      sh.acc[wid][h][vd] = acc[h][0];
+      sh.acc[wid][h][vd + 1] = acc[h][1];
     }
   }
   if (lane == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) { s_m[wid][h] = m[h]; s_l[wid][h] = (ntiles > 0) ? lw[h] : 0.f; }
-    if (ntiles == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) s_m[wid][h] = -INFINITY;
+    for (int h = 0; h < G; ++h) {
+      sh.m[wid][h] = (ntiles > 0) ? m[h] : -INFINITY;
+      sh.l[wid][h] = (ntiles > 0) ? lw[h] : 0.f;
     }
   }
   __syncthreads();
   for (int idx = tid; idx < G * D; idx += kMfmaThreads) {
     const int h = idx / D, e = idx % D;
-    float M = s_m[0][h];
+    float M = sh.m[0][h];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, s_m[w][h]);
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, sh.m[w][h]);
     float av = 0.f, lv = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float mw = s_m[w][h];
+      const float mw = sh.m[w][h];
       const float wt = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-      av += wt * s_acc[w][h][e];
-      lv += wt * s_l[w][h];
+      av += wt * sh.acc[w][h][e];
+      lv += wt * sh.l[w][h];
     }
-    float* pp = a.partial + (((int64_t)b * a.Hq + g * G + h) * a.max_splits + split) * (D + 2);
+    float* pp = a.partial + ((int64_t)item * G + h) * (D + 2);
     pp[e] = av;
     if (e == 0) { pp[D] = M; pp[D + 1] = lv; }
   }
 }
 
+template <int D, int G>
+__global__ __launch_bounds__(kMfmaThreads, (G > 4 ? 1 : 2)) void decode_mfma_kernel(DecodeArgs a) {
+  __shared__ DecodeShared<D, G> sh;
+  const int chunk = plan_chunk(a, sh.scan64);
+  plan_walk(a, chunk, blockIdx.x, -1, sh.scan32, sh.plan);
+  const int bg = sh.plan[0], split = sh.plan[1];
+  if (bg < 0) return;
+  if ((a.local_mask >> (bg % a.Hkv)) & 1ull) decode_item<D, G, true>(a, sh, blockIdx.x, bg, split, chunk);
+  else decode_item<D, G, false>(a, sh, blockIdx.x, bg, split, chunk);
+}
+
+// Merge the items of one (sequence, query head): weights 2^(m_i - M) per
+// item, then every thread sums one output dim over its share of the items.
+template <int D>
+__global__ __launch_bounds__(kMfmaThreads) void decode_item_combine_kernel(DecodeArgs a) {
+  constexpr int P = kMfmaThreads / D;          // item shares per output dim
+  __shared__ int64_t s_scan64[kMfmaThreads / 64];
+  __shared__ int s_scan32[kMfmaThreads / 64];
+  __shared__ int s_plan[4];
+  __shared__ float s_w[kMaxItemsLds];
+  __shared__ float s_red[kMfmaThreads];
+  __shared__ float s_M, s_L;
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int b = bh / a.Hq, h = bh % a.Hq, g = h / a.G, hh = h % a.G;
+  const int chunk = plan_chunk(a, s_scan64);
+  plan_walk(a, chunk, -1, b * a.Hkv + g, s_scan32, s_plan);
+  const int first = s_plan[2], ns = min(s_plan[3], kMaxItemsLds);
+  const int64_t stride = (int64_t)a.G * (D + 2);
+  const float* base = a.partial + ((int64_t)first * a.G + hh) * (D + 2);
+  float mx = -INFINITY;
+  for (int sp = tid; sp < ns; sp += kMfmaThreads) mx = fmaxf(mx, base[sp * stride + D]);
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) s_red[tid >> 6] = mx;
+  __syncthreads();
+  if (tid == 0) s_M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  __syncthreads();
+  const float M = s_M;
+  float lsum = 0.f;
+  for (int sp = tid; sp < ns; sp += kMfmaThreads) {
+    const float* q = base + sp * stride;
+    const float w = (q[D] == -INFINITY) ? 0.f : exp2f(q[D] - M);
+    s_w[sp] = w;
+    lsum += w * q[D + 1];
+  }
+  lsum = wave_sum(lsum);
+  __syncthreads();
+  if ((tid & 63) == 0) s_red[tid >> 6] = lsum;
+  __syncthreads();
+  if (tid == 0) s_L = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+  __syncthreads();
+  const int e = tid % D, part = tid / D;
+  float acc = 0.f;
+  for (int sp = part; sp < ns; sp += P) acc = fmaf(s_w[sp], base[sp * stride + e], acc);
+  s_red[tid] = acc;
+  __syncthreads();
+  if (part == 0) {
+    float v = acc;
+#pragma unroll
+    for (int q = 1; q < P; ++q) v += s_red[q * D + e];
+    const float L = s_L;
+    a.out[(int64_t)bh * D + e] = (L > 0.f) ? v / L : 0.f;
+  }
+}
+
 hipError_t launch_decode_mfma(const DecodeArgs& a, int d, hipStream_t s) {
-  dim3 grid(a.max_splits, a.Hkv, a.B), block(kMfmaThreads);
-  if (a.tps > kMaxTps) return hipErrorInvalidValue;
+  if (a.max_splits < 1 || a.max_splits > kMaxItemsLds || a.target_items < 1) return hipErrorInvalidValue;
+  dim3 grid(a.max_splits), block(kMfmaThreads);
 #define SA_DEC(D_, G_) hipLaunchKernelGGL((decode_mfma_kernel<D_, G_>), grid, block, 0, s, a)
   if (d == 128) {
     switch (a.G) {
@@ -292,6 +420,10 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int d, hipStream_t s) {
     return hipErrorInvalidValue;
   }
 #undef SA_DEC
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (d == 128) hipLaunchKernelGGL((decode_item_combine_kernel<128>), dim3(a.B * a.Hq), block, 0, s, a);
+  else hipLaunchKernelGGL((decode_item_combine_kernel<64>), dim3(a.B * a.Hq), block, 0, s, a);
   return hipGetLastError();
 }
 
