@@ -385,6 +385,7 @@ int32_t sparse_attn_decode(const sa_params* p, const sa_buffers* b, void* ws, si
   }
   Carver c(ws);
   float* partial = c.take<float>(n_partial);
+  int2* plan = (p->dtype == SA_BF16) ? c.take<int2>((size_t)p->batch * p->n_kv_heads) : nullptr;
   if ((st = workspace_gate(ws, ws_bytes, c.size()))) return st < 0 ? st : SA_OK;
   if (!b->q || !b->k_cache || !b->v_cache || !b->out) return SA_ERR_INVALID_ARG;
   if (any_list && (!b->sel_idx || !b->sel_count)) return SA_ERR_INVALID_ARG;
@@ -398,6 +399,7 @@ int32_t sparse_attn_decode(const sa_params* p, const sa_buffers* b, void* ws, si
   a.local_mask = local_mask;
   a.target_items = target_items;
   a.min_chunk = kDecodeMinChunk;
+  a.plan = plan;
   return hip_status(sa::launch_decode(a, p->dtype, p->head_dim, static_cast<hipStream_t>(stream)));
 }
 

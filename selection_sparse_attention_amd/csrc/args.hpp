@@ -125,6 +125,7 @@ struct DecodeArgs {
   uint64_t local_mask;    // bit g set: group g is local
   int32_t target_items;   // bf16 path: work items the visible tokens are spread over
   int32_t min_chunk;      // bf16 path: smallest item (list entries)
+  int2* plan;             // bf16 path: per group (first item, item count) [B*Hkv]
 };
 
 struct PrefillArgs {

@@ -17,11 +17,11 @@
 // combine launch re-derives it to find each head's items.
 //
 // Layout per wave, one 16-token tile at a time:
-//   * lane l gathers d/4 consecutive K elements of token (l % 16): the four
-//     lanes of a token cover its row, and they are exactly the B operand of
-//     v_mfma_f32_16x16x32_bf16 (k-step s uses elements 8s..8s+7 of each lane's
-//     slice; the query fragment in the A operand follows the same mapping, one
-//     head per row, rows >= G zero).  The product leaves head h's 16 scores in
+//   * lane l gathers token (l % 16): at k-step s the four lanes of a token
+//     hold dims 32 s + 8 (l / 16) .. +8, so each load instruction reads 64
+//     contiguous bytes of every row, and the registers are exactly the B
+//     operand of v_mfma_f32_16x16x32_bf16 (the query fragment in the A operand
+//     follows the same dim mapping, one head per row, rows >= G zero).  The product leaves head h's 16 scores in
 //     lane group h/4, register h%4 - no cross-lane sum for q.k at all.
 //   * the tile max is a 16-lane DPP rotation reduction, broadcast with
 //     readlane; probabilities go through a small LDS buffer to every lane.
@@ -42,7 +42,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaThreads = 256;
-constexpr int kMaxItemsLds = 8192;           // items one combine workgroup merges
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
@@ -90,9 +89,10 @@ __device__ int plan_chunk(const DecodeArgs& a, int64_t* s_scan) {
 // Number the items group by group (ceil(count / chunk) each).  Leaves in
 // s_out: [0] the group of item `item` (-1 when the plan has fewer items),
 // [1] its split within the group, [2] the first item of group `want`, [3]
-// that group's item count.
+// that group's item count; with `table`, also writes (first item, item
+// count) of every group there.
 __device__ void plan_walk(const DecodeArgs& a, int chunk, int item, int want, int* s_scan,
-                          int* s_out) {
+                          int* s_out, int2* table) {
   if (threadIdx.x == 0) { s_out[0] = -1; s_out[1] = 0; s_out[2] = 0; s_out[3] = 0; }
   __syncthreads();
   const int ng = a.B * a.Hkv;
@@ -105,6 +105,7 @@ __device__ void plan_walk(const DecodeArgs& a, int chunk, int item, int want, in
     if (bg < ng) {
       if (item >= first && item < first + ns) { s_out[0] = bg; s_out[1] = item - first; }
       if (bg == want) { s_out[2] = first; s_out[3] = ns; }
+      if (table) table[bg] = make_int2(first, ns);
     }
     carry += tot;
   }
@@ -136,7 +137,6 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, DecodeShared<D,
                                             int bg, int split, int chunk) {
   using TL = Tile<D>;
   constexpr int KS = TL::KS, NCLS = TL::NCLS, VT = TL::VT;
-  constexpr int DPL = D / 4;                   // K elements per lane
   static_assert(G <= 8, "at most 8 query heads per KV group");
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
@@ -162,7 +162,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, DecodeShared<D,
       u32x4 w = {0u, 0u, 0u, 0u};
       if (h < G) {
         const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                             ((int64_t)b * a.Hq + g * G + h) * D + jq * DPL + 8 * s;
+                             ((int64_t)b * a.Hq + g * G + h) * D + 32 * s + 8 * jq;
         w = *reinterpret_cast<const u32x4*>(qp);
       }
       qf[s] = __builtin_bit_cast(bf16x8, w);
@@ -176,7 +176,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, DecodeShared<D,
 
   const int kt = lane & 15, jg = lane >> 4;            // K role
   const int vd = 2 * (lane % (D / 2)), vc = lane / (D / 2);   // V role
-  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + row0 * D + jg * DPL;
+  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + row0 * D + 8 * jg;
   const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v) + row0 * D + vd;
 
   // raw list entry of this lane's token in a tile (a load for listed groups,
@@ -193,7 +193,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, DecodeShared<D,
     t.tok = tok;
     const uint16_t* kp = kbase + (int64_t)max(tok, 0) * D;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) t.k[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + 8 * s));
+    for (int s = 0; s < KS; ++s) t.k[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + 32 * s));
 #pragma unroll
     for (int r = 0; r < VT; ++r) {
       int tv = __builtin_amdgcn_readlane(tok, r * NCLS);
@@ -336,68 +336,82 @@ template <int D, int G>
 __global__ __launch_bounds__(kMfmaThreads, (G > 4 ? 1 : 2)) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ DecodeShared<D, G> sh;
   const int chunk = plan_chunk(a, sh.scan64);
-  plan_walk(a, chunk, blockIdx.x, -1, sh.scan32, sh.plan);
+  // workgroup 0 also records every group's items for the combine launch
+  plan_walk(a, chunk, blockIdx.x, -1, sh.scan32, sh.plan, blockIdx.x == 0 ? a.plan : nullptr);
   const int bg = sh.plan[0], split = sh.plan[1];
   if (bg < 0) return;
   if ((a.local_mask >> (bg % a.Hkv)) & 1ull) decode_item<D, G, true>(a, sh, blockIdx.x, bg, split, chunk);
   else decode_item<D, G, false>(a, sh, blockIdx.x, bg, split, chunk);
 }
 
-// Merge the items of one (sequence, query head): weights 2^(m_i - M) per
-// item, then every thread sums one output dim over its share of the items.
-template <int D>
+// Merge the items of one (sequence, query head).  Thread (e, part) owns
+// output dim e for a share of the items; per round of P x CH items every
+// thread issues all its acc loads and the m / l loads at once (one memory
+// latency per round), the round's m / l go through LDS, and the (M, L, A)
+// state is merged online across rounds.  The head's item range comes from
+// the table the decode launch wrote.
+template <int D, int G>
 __global__ __launch_bounds__(kMfmaThreads) void decode_item_combine_kernel(DecodeArgs a) {
   constexpr int P = kMfmaThreads / D;          // item shares per output dim
-  __shared__ int64_t s_scan64[kMfmaThreads / 64];
-  __shared__ int s_scan32[kMfmaThreads / 64];
-  __shared__ int s_plan[4];
-  __shared__ float s_w[kMaxItemsLds];
-  __shared__ float s_red[kMfmaThreads];
-  __shared__ float s_M, s_L;
-  const int bh = blockIdx.x, tid = threadIdx.x;
-  const int b = bh / a.Hq, h = bh % a.Hq, g = h / a.G, hh = h % a.G;
-  const int chunk = plan_chunk(a, s_scan64);
-  plan_walk(a, chunk, -1, b * a.Hkv + g, s_scan32, s_plan);
-  const int first = s_plan[2], ns = min(s_plan[3], kMaxItemsLds);
-  const int64_t stride = (int64_t)a.G * (D + 2);
-  const float* base = a.partial + ((int64_t)first * a.G + hh) * (D + 2);
-  float mx = -INFINITY;
-  for (int sp = tid; sp < ns; sp += kMfmaThreads) mx = fmaxf(mx, base[sp * stride + D]);
-  mx = wave_max(mx);
-  if ((tid & 63) == 0) s_red[tid >> 6] = mx;
-  __syncthreads();
-  if (tid == 0) s_M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  __syncthreads();
-  const float M = s_M;
-  float lsum = 0.f;
-  for (int sp = tid; sp < ns; sp += kMfmaThreads) {
-    const float* q = base + sp * stride;
-    const float w = (q[D] == -INFINITY) ? 0.f : exp2f(q[D] - M);
-    s_w[sp] = w;
-    lsum += w * q[D + 1];
+  constexpr int CH = 16;                       // items per thread per round
+  constexpr int R = P * CH;                    // items per round
+  __shared__ float s_m[R], s_l[R];
+  __shared__ float s_a[kMfmaThreads];
+  const int bgh = blockIdx.x;
+  const int bg = bgh / G, h = bgh - bg * G;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int2 fr = a.plan[bg];
+  const int first = fr.x, ns = fr.y;
+  const int tid = threadIdx.x, e = tid % D, part = tid / D;
+  const int64_t stride = (int64_t)G * (D + 2);
+  const float* base = a.partial + ((int64_t)first * G + h) * (D + 2);
+  float M = -INFINITY, L = 0.f, A = 0.f;
+  for (int c0 = 0; c0 < ns; c0 += R) {
+    float av[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int i = c0 + part * CH + j;
+      const float x = base[min(i, ns - 1) * stride + e];
+      av[j] = (i < ns) ? x : 0.f;
+    }
+    if (tid < R) {
+      const int i = c0 + tid;
+      const float* q = base + min(i, ns - 1) * stride;
+      const float mi = q[D], li = q[D + 1];
+      s_m[tid] = (i < ns) ? mi : -INFINITY;
+      s_l[tid] = (i < ns) ? li : 0.f;
+    }
+    __syncthreads();
+    float Mr = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < R; ++j) Mr = fmaxf(Mr, s_m[j]);
+    const float Mn = fmaxf(M, Mr);
+    if (Mn != -INFINITY) {
+      const float sc = (M == -INFINITY) ? 0.f : exp2f(M - Mn);
+      A *= sc;
+      L *= sc;
+      float Lr = 0.f;
+#pragma unroll
+      for (int j = 0; j < R; ++j) Lr = fmaf(exp2f(s_m[j] - Mn), s_l[j], Lr);   // 0 for m = -inf
+      L += Lr;
+#pragma unroll
+      for (int j = 0; j < CH; ++j) A = fmaf(exp2f(s_m[part * CH + j] - Mn), av[j], A);
+      M = Mn;
+    }
+    __syncthreads();
   }
-  lsum = wave_sum(lsum);
-  __syncthreads();
-  if ((tid & 63) == 0) s_red[tid >> 6] = lsum;
-  __syncthreads();
-  if (tid == 0) s_L = s_red[0] + s_red[1] + s_red[2] + s_red[3];
-  __syncthreads();
-  const int e = tid % D, part = tid / D;
-  float acc = 0.f;
-  for (int sp = part; sp < ns; sp += P) acc = fmaf(s_w[sp], base[sp * stride + e], acc);
-  s_red[tid] = acc;
+  s_a[tid] = A;
   __syncthreads();
   if (part == 0) {
-    float v = acc;
+    float v = A;
 #pragma unroll
-    for (int q = 1; q < P; ++q) v += s_red[q * D + e];
-    const float L = s_L;
-    a.out[(int64_t)bh * D + e] = (L > 0.f) ? v / L : 0.f;
+    for (int q = 1; q < P; ++q) v += s_a[q * D + e];
+    a.out[((int64_t)b * a.Hq + g * G + h) * D + e] = (L > 0.f) ? v / L : 0.f;
   }
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int d, hipStream_t s) {
-  if (a.max_splits < 1 || a.max_splits > kMaxItemsLds || a.target_items < 1) return hipErrorInvalidValue;
+  if (a.max_splits < 1 || a.target_items < 1 || !a.plan) return hipErrorInvalidValue;
   dim3 grid(a.max_splits), block(kMfmaThreads);
 #define SA_DEC(D_, G_) hipLaunchKernelGGL((decode_mfma_kernel<D_, G_>), grid, block, 0, s, a)
   if (d == 128) {
@@ -422,8 +436,20 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int d, hipStream_t s) {
 #undef SA_DEC
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (d == 128) hipLaunchKernelGGL((decode_item_combine_kernel<128>), dim3(a.B * a.Hq), block, 0, s, a);
-  else hipLaunchKernelGGL((decode_item_combine_kernel<64>), dim3(a.B * a.Hq), block, 0, s, a);
+  dim3 cgrid(a.B * a.Hq);
+#define SA_CMB(D_, G_) hipLaunchKernelGGL((decode_item_combine_kernel<D_, G_>), cgrid, block, 0, s, a)
+  switch (a.G * 1000 + d) {
+    case 1128: SA_CMB(128, 1); break;
+    case 2128: SA_CMB(128, 2); break;
+    case 4128: SA_CMB(128, 4); break;
+    case 8128: SA_CMB(128, 8); break;
+    case 1064: SA_CMB(64, 1); break;
+    case 2064: SA_CMB(64, 2); break;
+    case 4064: SA_CMB(64, 4); break;
+    case 8064: SA_CMB(64, 8); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef SA_CMB
   return hipGetLastError();
 }
 
