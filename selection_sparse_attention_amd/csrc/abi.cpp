@@ -117,8 +117,7 @@ int32_t pyramid_geom(const sa_params* p, PyrGeom* g) {
 constexpr int kSelTile = 1024;
 
 struct SelectWs {
-  float* logits; uint32_t* cnt1; double* mass1; uint32_t* cnt2; double* mass2;
-  uint32_t* cnt3; double* mass3; sa::RowState* state; uint64_t* lookback;
+  float* logits; uint32_t* cnt1; double* mass1; sa::RowState* state; uint64_t* lookback;
   int tiles; int64_t row_stride; size_t bytes;
 };
 
@@ -130,10 +129,6 @@ SelectWs carve_select(void* ws, int rows, int n) {
   s.logits = c.take<float>((size_t)rows * s.row_stride);
   s.cnt1 = c.take<uint32_t>((size_t)rows * 4096);
   s.mass1 = c.take<double>((size_t)rows * 4096);
-  s.cnt2 = c.take<uint32_t>((size_t)rows * 4096);
-  s.mass2 = c.take<double>((size_t)rows * 4096);
-  s.cnt3 = c.take<uint32_t>((size_t)rows * 256);
-  s.mass3 = c.take<double>((size_t)rows * 256);
   s.state = c.take<sa::RowState>((size_t)rows);
   s.lookback = c.take<uint64_t>((size_t)rows * s.tiles);
   s.bytes = c.size();
@@ -315,8 +310,7 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
       a.select_all = (p->top_k >= p->n_ctx) ? 1 : 0;
     }
     a.tiles = sw.tiles; a.row_stride = sw.row_stride;
-    a.logits = sw.logits; a.cnt1 = sw.cnt1; a.mass1 = sw.mass1; a.cnt2 = sw.cnt2; a.mass2 = sw.mass2;
-    a.cnt3 = sw.cnt3; a.mass3 = sw.mass3; a.state = sw.state;
+    a.logits = sw.logits; a.cnt1 = sw.cnt1; a.mass1 = sw.mass1; a.state = sw.state;
     a.lookback = sw.lookback; a.groups = gl;
     return hip_status(sa::launch_select_lowrank(a, p->dtype, s));
   }

@@ -80,11 +80,9 @@ struct SelectArgs {
   int64_t row_stride;    // logits stride per row (tiles * tile)
   // workspace
   float* logits;         // [rows, row_stride]
-  uint32_t* cnt1; double* mass1;   // [rows, 4096]
-  uint32_t* cnt2; double* mass2;   // [rows, 4096]
-  uint32_t* cnt3; double* mass3;   // [rows, 256]
-  RowState* state;       // [rows]
-  uint64_t* lookback;    // [rows, tiles]
+  uint32_t* cnt1; double* mass1;   // [rows, 4096]: level-1 histogram, zero between calls
+  RowState* state;       // [rows]: the cut found by the row kernel
+  uint64_t* lookback;    // [rows, tiles]: compaction prefix flags
   GroupList groups;
 };
 
