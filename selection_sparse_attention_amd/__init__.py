@@ -3,7 +3,7 @@
 Argument marshalling only: tensors are passed to the C ABI as raw device
 pointers together with torch's current HIP stream; every step of the method
 runs inside the library's HIP kernels.  The library must have been built
-(``python -m selection_sparse_attention_amd.build``); importing this module
+(``python selection_sparse_attention_amd/build.py``); importing this module
 without it raises ImportError - there is no fallback implementation.
 """
 from __future__ import annotations
@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libsparse_attn.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      "`python -m selection_sparse_attention_amd.build`")
+                      "`python selection_sparse_attention_amd/build.py`")
 _lib = ctypes.CDLL(LIB_PATH)
 
 # status codes (sa_status)

@@ -2,7 +2,9 @@
 
 Every HIP source under csrc/ is compiled to an object in _build/ (in
 parallel) and linked into selection_sparse_attention_amd/libsparse_attn.so.
-Always recompiles: callers that only need a library use ``library_path()``.
+Always recompiles.  Run it as a script (``python
+selection_sparse_attention_amd/build.py``): it imports nothing from the
+package, whose import requires the built library.
 """
 import concurrent.futures as cf
 import os
