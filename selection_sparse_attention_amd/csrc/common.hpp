@@ -133,18 +133,44 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Move a 32- or 64-bit value across lanes with a DPP control (rows outside
+// ROWMASK and lanes whose source lies outside the row read 0).
+template <int CTRL, int ROWMASK, typename T>
+__device__ __forceinline__ T dpp_move(T v) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                             ROWMASK, 0xF, false));
+  } else {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROWMASK, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROWMASK,
+                                                              0xF, false);
+    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+  }
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts by 1, 2,
+// 4, 8 inside each 16-lane row, then row 0's total broadcast into row 1 and
+// row 2 (row_bcast:15), and rows 0-1's total into rows 2-3 (row_bcast:31).
+template <typename T>
+__device__ __forceinline__ T wave_inclusive_scan(T v) {
+  v += dpp_move<0x111, 0xF>(v);     // row_shr:1
+  v += dpp_move<0x112, 0xF>(v);     // row_shr:2
+  v += dpp_move<0x114, 0xF>(v);     // row_shr:4
+  v += dpp_move<0x118, 0xF>(v);     // row_shr:8
+  v += dpp_move<0x142, 0xA>(v);     // row_bcast:15 into rows 1 and 3
+  v += dpp_move<0x143, 0xC>(v);     // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 // Exclusive prefix sum over a block of NT threads (NT a multiple of 64),
 // using `scratch` (NT/64 entries of T in LDS).  Returns the exclusive value
 // and writes the block total to *total.
 template <typename T, int NT>
 __device__ __forceinline__ T block_exclusive_scan(T v, T* scratch, T* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  T incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    T y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
+  const T incl = wave_inclusive_scan(v);
   if (lane == 63) scratch[wid] = incl;
   __syncthreads();
   T base = 0, tot = 0;
