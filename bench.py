@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the other workloads (128K decode, routed decode, prefill)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--graph", action="store_true",
+                    help="replay HIP graphs of the step instead of launching every call "
+                         "(measured slower here: graph replay adds time between kernels)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain elementwise copy of known size (for scaling HBM "
                          "byte counters) and exit")
@@ -124,6 +127,14 @@ class DecodeInstance:
     def decode(self):
         self.sa.decode(self.params, self.bufs, self.ws_dec)
 
+    def capture(self, torch):
+        """Record the step's two halves into HIP graphs (after a warm-up)."""
+        self.g_sel, self.g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g_sel):
+            self.index_and_select()
+        with torch.cuda.graph(self.g_dec):
+            self.decode()
+
 
 def decode_bytes(cfg, counts, kinds):
     """Algorithmic bytes of one decode step and of its attention kernel."""
@@ -175,16 +186,30 @@ def run_decode(args, torch, sa, workloads, workload=None, steps=None, warmup=Non
         x.index_and_select()
         x.decode()
     torch.cuda.synchronize()
-    log(f"[bench] warmup done ({warmup} steps)")
+    use_graph = args.graph
+    if use_graph:
+        # one graph for index append + selection and one for the attention call
+        # per instance: the step is replayed with two launches, so the host
+        # never starves the GPU between calls
+        for x in insts:
+            x.capture(torch)
+        torch.cuda.synchronize()
+    log(f"[bench] warmup done ({warmup} steps){' - replaying HIP graphs' if use_graph else ''}")
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(steps):
         x = insts[i % len(insts)]
-        x.index_and_select()
+        if use_graph:
+            x.g_sel.replay()
+        else:
+            x.index_and_select()
         ev[i][0].record(stream)
-        x.decode()
+        if use_graph:
+            x.g_dec.replay()
+        else:
+            x.decode()
         ev[i][1].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
@@ -220,7 +245,8 @@ def run_decode(args, torch, sa, workloads, workload=None, steps=None, warmup=Non
                    "n_ctx": cfg.n_ctx, "top_p": cfg.top_p if not cfg.top_k else None,
                    "top_k": cfg.top_k or None, "min_tokens": cfg.min_tokens,
                    "sinks": cfg.sinks, "window": cfg.window, "routed": cfg.routed,
-                   "instances_rotated": len(insts)},
+                   "instances_rotated": len(insts),
+                   "launch": "hip_graph" if args.graph else "eager"},
         "step_hbm_gbps": step_b / t_step / 1e9,
         "step_bytes": step_b,
         "selected_frac_mean": (sum(sel_frac) / len(sel_frac)) if sel_frac else None,

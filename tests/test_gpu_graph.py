@@ -1,0 +1,113 @@
+"""A decode step (index append, selection, attention) and a prefill
+(pyramid, block selection, attention) recorded into HIP graphs: every replay,
+with the program's own eager work and synchronisations between replays, must
+reproduce the eager result exactly (the kernels are deterministic, and the
+library records only kernel launches)."""
+import pytest
+import torch
+
+import workloads
+from gpu_harness import DEV, DecodeRun, PrefillRun
+
+pytestmark = pytest.mark.gpu
+
+
+def _snapshot(run, keys):
+    return {k: run.t[k].clone() for k in keys}
+
+
+def _same(a, b, groups=None):
+    """Equal outputs; for the lists, only the selecting groups' counts and
+    their first sel_count entries are defined (local groups are not listed)."""
+    for k in a:
+        if k in ("sel_idx", "sel_count"):
+            cnt = a["sel_count"].cpu()
+            for bb in range(cnt.shape[0]):
+                for g in groups:
+                    c = int(cnt[bb, g])
+                    assert c == int(b["sel_count"][bb, g]), ("sel_count", bb, g)
+                    assert torch.equal(a["sel_idx"][bb, g, :c], b["sel_idx"][bb, g, :c]), (k, bb, g)
+        else:
+            assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("cfg", [
+    workloads.LLAMA_32K.with_(batch=2, n_ctx=8192 + 77),
+    workloads.LLAMA_32K.with_(batch=2, n_ctx=4096, top_p=1.0, top_k=300),
+    workloads.HGA_64K.with_(batch=2, n_ctx=8192),
+], ids=["topp", "topk", "routed"])
+def test_decode_step_graph_replays_match_eager(cfg):
+    inp = workloads.decode_inputs(cfg, 21, device=DEV)
+    run = DecodeRun(cfg, inp)
+    n = cfg.n_ctx
+    if cfg.routed:
+        run.summaries(0, n)
+    else:
+        run.index(0, n)
+
+    def step():
+        if cfg.routed:
+            t0 = (n // cfg.chunk) * cfg.chunk - 1 if n % cfg.chunk == 0 else n - 1
+            run.summaries(max(0, t0), n)
+        else:
+            run.index(n - 1, n)
+        run.select()
+        run.decode()
+
+    keys = ["sel_idx", "sel_count", "out"]
+    kinds = cfg.head_kind()
+    groups = [g for g in range(cfg.n_kv_heads) if kinds[g * cfg.gqa] != workloads.HEAD_LOCAL]
+    step()
+    torch.cuda.synchronize()
+    eager = _snapshot(run, keys)
+    step()                                  # warm-up right before capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for k in keys:                      # eager work between replays
+            run.t[k].fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _same(_snapshot(run, keys), eager, groups)
+    step()                                  # and eager calls still agree afterwards
+    torch.cuda.synchronize()
+    _same(_snapshot(run, keys), eager, groups)
+
+
+def test_prefill_graph_replays_match_eager():
+    cfg = workloads.PYRAMID_128K.with_(n_heads=2, n_ctx=4096, block_top_k=700)
+    inp = workloads.prefill_inputs(cfg, 22)
+    run = PrefillRun(cfg, inp)
+
+    def step():
+        run.pyramid(); run.select(); run.prefill()
+
+    keys = ["scores", "blk_idx", "blk_count", "out"]
+
+    def same_prefill(a, b):
+        for k in ("scores", "blk_count", "out"):
+            assert torch.equal(a[k], b[k]), k
+        cnt = a["blk_count"].cpu()                  # entries past the count are not defined
+        for h in range(cnt.shape[1]):
+            for blk in range(cnt.shape[2]):
+                c = int(cnt[0, h, blk])
+                assert torch.equal(a["blk_idx"][0, h, blk, :c], b["blk_idx"][0, h, blk, :c]), (h, blk)
+
+    step()
+    torch.cuda.synchronize()
+    eager = _snapshot(run, keys)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for k in keys:
+            run.t[k].fill_(-3)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        same_prefill(_snapshot(run, keys), eager)
