@@ -194,7 +194,8 @@ int32_t sparse_attn_index_build(const sa_params* params, const sa_buffers* bufs,
  *   ranked by qbar . chunk_sum (ties to the lower chunk), the top top_chunks
  *   kept, and in each the top top_groups groups by qbar . group_sum.  The list
  *   is the union of sink chunks, local chunks, tokens kappa*chunk .. t, and
- *   the routed groups, ascending.  Needs n_cap >= the list length.
+ *   the routed groups, ascending.  Needs n_cap >= the list length;
+ *   top_chunks <= 64 and chunk / group <= 64 (SA_ERR_UNSUPPORTED otherwise).
  * SA_SEL_PYRAMID_TOPK (Lighthouse summary, 2B-2C): for every block of q_block
  *   queries, among entries (l, j) with (j + 1) p^l <= q_block * block, keeps
  *   the block_top_k largest pyr_scores (ties: lower level, then lower j) as

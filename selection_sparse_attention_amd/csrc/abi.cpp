@@ -319,7 +319,7 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
     const int gpc = p->chunk / p->group;
     if (p->top_chunks < 1 || p->top_groups < 1 || p->top_groups > gpc) return SA_ERR_INVALID_ARG;
     if (p->sink_chunks < 0 || p->local_chunks < 0) return SA_ERR_INVALID_ARG;
-    if (p->top_chunks > 256 || gpc > 64 || p->top_chunks * p->top_groups > 4096)
+    if (p->top_chunks > 64 || gpc > 64 || p->top_chunks * p->top_groups > 4096)
       return SA_ERR_UNSUPPORTED;
     if (p->n_ctx / p->chunk > 16384) return SA_ERR_UNSUPPORTED;
     GroupList gl = groups_of_kind(p, kinds, SA_HEAD_ROUTED);

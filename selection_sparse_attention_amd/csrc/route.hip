@@ -15,9 +15,10 @@
 // change the order.
 //
 // One 256-thread workgroup per (KV group, sequence).  Rows are scored with 16
-// lanes each (d/16 elements per lane, a 16-lane DPP reduction), chunk scores
-// stay in LDS, and the top chunks are extracted by repeated block-wide arg-max
-// over (score key, inverted index) 64-bit keys.
+// lanes each (d/16 elements per lane, a 16-lane DPP reduction, four rounds of
+// loads in flight), chunk scores stay in LDS, and the top chunks come from
+// per-wave arg-max rounds over (score key, inverted index) 64-bit keys
+// merged by one wave - no block barrier per extracted chunk.
 #include <algorithm>
 
 #include "args.hpp"
@@ -42,27 +43,35 @@ __device__ __forceinline__ float row16_sum_r(float v) {
 }
 
 // Scores qbar . rows[r] for r in [0, nrows) into out[r]; rows are d wide.
+// A wave scores 4 rows per round (16 lanes per row) and keeps the loads of
+// 4 rounds in flight.
 template <typename T, int D>
 __device__ void score_rows(const void* base, int64_t row_of0, int nrows, const float* s_q,
                            float* out, const int* row_map) {
   constexpr int EPL = D / 16;
+  constexpr int U = 4;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int sub = lane & 15, rg = lane >> 4;
   float q[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) q[e] = s_q[sub * EPL + e];
-  for (int r0 = 0; r0 < nrows; r0 += 16) {
-    const int r = r0 + wid * 4 + rg;
-    float p = 0.f;
-    if (r < nrows) {
-      const int64_t row = row_map ? (int64_t)row_map[r] : (row_of0 + r);
-      float kv[EPL];
-      VecLoad<T, EPL>::run(base, row * D + sub * EPL, kv);
+  for (int r0 = 0; r0 < nrows; r0 += 16 * U) {
+    float kv[U][EPL];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) p = fmaf(q[e], kv[e], p);
+    for (int u = 0; u < U; ++u) {
+      const int r = min(r0 + u * 16 + wid * 4 + rg, nrows - 1);
+      const int64_t row = row_map ? (int64_t)row_map[r] : (row_of0 + r);
+      VecLoad<T, EPL>::run(base, row * D + sub * EPL, kv[u]);
     }
-    p = row16_sum_r(p);
-    if (r < nrows && sub == 0) out[r] = p;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = r0 + u * 16 + wid * 4 + rg;
+      float p = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) p = fmaf(q[e], kv[u][e], p);
+      p = row16_sum_r(p);
+      if (r < nrows && sub == 0) out[r] = p;
+    }
   }
 }
 
@@ -71,24 +80,27 @@ __device__ __forceinline__ uint64_t score_key(float s, int idx) {
   return ((uint64_t)order_key(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
 }
 
+// Largest 64-bit key over the wave (DPP max scan, then lane 63's value).
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+  uint64_t o;
+  o = dpp_move<0x111, 0xF>(v); v = o > v ? o : v;     // row_shr:1
+  o = dpp_move<0x112, 0xF>(v); v = o > v ? o : v;     // row_shr:2
+  o = dpp_move<0x114, 0xF>(v); v = o > v ? o : v;     // row_shr:4
+  o = dpp_move<0x118, 0xF>(v); v = o > v ? o : v;     // row_shr:8
+  o = dpp_move<0x142, 0xA>(v); v = o > v ? o : v;     // row_bcast:15
+  o = dpp_move<0x143, 0xC>(v); v = o > v ? o : v;     // row_bcast:31
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 template <typename T, int D>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   extern __shared__ float dyn[];                 // chunk scores, then group scores
   __shared__ float s_q[D];
-  __shared__ uint32_t s_taken[16384 / 32];
   __shared__ int s_chunks[256], s_sorted[256];
+  __shared__ uint64_t s_wtop[kRouteThreads / 64][64];
   __shared__ int s_groups[kMaxRoutedGroups];
-  __shared__ uint64_t s_red[kRouteThreads / 64];
   __shared__ int s_rowmap[kMaxRoutedGroups];
   const int gi = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int g = a.groups.ids[gi];
@@ -105,33 +117,49 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     for (int h = 0; h < a.G; ++h) s += Elem<T>::load(a.q, ((int64_t)b * a.Hq + g * a.G + h) * D + e);
     s_q[e] = s * (1.0f / (float)a.G);
   }
-  for (int i = tid; i < 16384 / 32; i += kRouteThreads) s_taken[i] = 0;
   __syncthreads();
 
   const int64_t bg = (int64_t)b * a.Hkv + g;
   if (nT > 0) {
     score_rows<T, D>(a.chunk_sum, bg * a.n_cs_cap + c_lo, ncand, s_q, dyn, nullptr);
     __syncthreads();
-    // level 1: nT rounds of block arg-max
-    for (int r = 0; r < nT; ++r) {
-      uint64_t best = 0;
-      for (int i = tid; i < ncand; i += kRouteThreads)
-        if (!((s_taken[i >> 5] >> (i & 31)) & 1u)) {
-          const uint64_t k = score_key(dyn[i], i);
-          best = k > best ? k : best;
+    // level 1: every wave extracts the top nT of its candidates (i = tid +
+    // 256 k) by nT rounds of wave arg-max over (score key, inverted index)
+    // keys; wave 0 then takes the top nT of those 4 nT in order
+    {
+      const int lane = tid & 63, wid = tid >> 6;
+      uint64_t done_mask = 0;                        // bit k: candidate tid + 256 k taken
+      for (int r = 0; r < nT; ++r) {
+        uint64_t best = 0;
+        for (int k = 0, i = tid; i < ncand; ++k, i += kRouteThreads)
+          if (!((done_mask >> k) & 1ull)) {
+            const uint64_t key = score_key(dyn[i], i);     // never 0
+            best = key > best ? key : best;
+          }
+        const uint64_t m = wave_max_u64(best);
+        if (m != 0) {
+          const int i = (int)(0xFFFFFFFFu - (uint32_t)m);
+          if (i % kRouteThreads == tid) done_mask |= 1ull << (i / kRouteThreads);
         }
-      best = wave_max_u64(best);
-      if ((tid & 63) == 0) s_red[tid >> 6] = best;
-      __syncthreads();
-      if (tid == 0) {
-        uint64_t m = s_red[0];
-        for (int w = 1; w < kRouteThreads / 64; ++w) m = s_red[w] > m ? s_red[w] : m;
-        const int i = (int)(0xFFFFFFFFu - (uint32_t)m);
-        s_chunks[r] = c_lo + i;
-        s_taken[i >> 5] |= 1u << (i & 31);
+        if (lane == 0) s_wtop[wid][r] = m;
       }
       __syncthreads();
+      if (wid == 0) {
+        uint64_t c[kRouteThreads / 64];
+#pragma unroll
+        for (int w = 0; w < kRouteThreads / 64; ++w) c[w] = (lane < nT) ? s_wtop[w][lane] : 0ull;
+        for (int r = 0; r < nT; ++r) {
+          uint64_t best = 0;
+#pragma unroll
+          for (int w = 0; w < kRouteThreads / 64; ++w) best = c[w] > best ? c[w] : best;
+          const uint64_t m = wave_max_u64(best);
+#pragma unroll
+          for (int w = 0; w < kRouteThreads / 64; ++w) if (c[w] == m) c[w] = 0;
+          if (lane == 0) s_chunks[r] = c_lo + (int)(0xFFFFFFFFu - (uint32_t)m);
+        }
+      }
     }
+    __syncthreads();
     // chosen chunks in ascending order
     if (tid < nT) {
       const int c = s_chunks[tid];
@@ -185,7 +213,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
 hipError_t launch_route(const RouteArgs& a, int dtype, int d, hipStream_t s) {
   if (a.groups.n == 0) return hipSuccess;
   const int gpc = a.chunk / a.group;
-  if (a.top_chunks * a.top_groups > kMaxRoutedGroups || a.top_chunks > 256 || gpc > 64)
+  if (a.top_chunks * a.top_groups > kMaxRoutedGroups || a.top_chunks > 64 || gpc > 64)
     return hipErrorInvalidValue;
   const int ncand_max = a.n / a.chunk + 1;
   if (ncand_max > 16384) return hipErrorInvalidValue;
