@@ -262,11 +262,12 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
     if ((st = pyramid_geom(p, &pg))) return st;
     if (p->q_block < 1 || p->q_block % pg.top_span || p->block_top_k < 1) return SA_ERR_INVALID_ARG;
     Carver c(ws);
-    c.take<uint32_t>(1);
+    uint2* prefix = c.take<uint2>((size_t)p->batch * p->n_q_heads);
     const size_t need = c.size();
     if ((st = workspace_gate(ws, ws_bytes, need))) return st < 0 ? st : SA_OK;
     if (!b->pyr_scores || !b->blk_idx || !b->blk_count) return SA_ERR_INVALID_ARG;
     sa::PyrSelectArgs a{};
+    a.prefix = prefix;
     a.scores = b->pyr_scores; a.blk_idx = b->blk_idx; a.blk_count = b->blk_count;
     a.B = p->batch; a.H = p->n_q_heads; a.N = p->n_ctx; a.levels = p->levels; a.factor = p->factor;
     a.q_block = p->q_block; a.K = p->block_top_k; a.nblk = pg.nblk; a.Nt = pg.Nt;

@@ -105,6 +105,7 @@ struct PyrSelectArgs {
   int32_t B, H, N, levels, factor, q_block, K, nblk, Nt;
   int32_t len[8];        // entries of each level
   int64_t soff[8];       // flat id of each level's first entry
+  uint2* prefix;         // workspace [B*H]: (AND, OR) of the head's score keys
 };
 
 // ---------------------------------------------------------------- attention
