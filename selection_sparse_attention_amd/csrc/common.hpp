@@ -59,37 +59,50 @@ template <> struct Elem<float> {
   }
 };
 
+typedef uint32_t vl_u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t vl_u32x4 __attribute__((ext_vector_type(4)));
+typedef float vl_f32x4 __attribute__((ext_vector_type(4)));
+
+// A plain load, or a non-temporal one (streamed data read once: it does not
+// displace reused lines in the caches).
+template <bool NT, typename V>
+__device__ __forceinline__ V vl_load(const V* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
 // Load N consecutive elements starting at element offset i (16-byte chunks;
 // the caller guarantees alignment) and widen them to fp32.
-template <typename T, int N> struct VecLoad;
-template <int N> struct VecLoad<bf16_t, N> {
+template <typename T, int N, bool NT = false> struct VecLoad;
+template <int N, bool NT> struct VecLoad<bf16_t, N, NT> {
   static_assert(N % 8 == 0 || N == 4, "bf16 vector loads are 8 or 4 elements");
   __device__ static void run(const void* base, int64_t i, float* out) {
     const uint16_t* p = reinterpret_cast<const uint16_t*>(base) + i;
     if constexpr (N == 4) {
-      uint2 w = *reinterpret_cast<const uint2*>(p);
-      out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x);
-      out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
+      const vl_u32x2 w = vl_load<NT>(reinterpret_cast<const vl_u32x2*>(p));
+      out[0] = bf16_lo(w[0]); out[1] = bf16_hi(w[0]);
+      out[2] = bf16_lo(w[1]); out[3] = bf16_hi(w[1]);
     } else {
 #pragma unroll
       for (int c = 0; c < N / 8; ++c) {
-        uint4 w = *reinterpret_cast<const uint4*>(p + 8 * c);
-        out[8 * c + 0] = bf16_lo(w.x); out[8 * c + 1] = bf16_hi(w.x);
-        out[8 * c + 2] = bf16_lo(w.y); out[8 * c + 3] = bf16_hi(w.y);
-        out[8 * c + 4] = bf16_lo(w.z); out[8 * c + 5] = bf16_hi(w.z);
-        out[8 * c + 6] = bf16_lo(w.w); out[8 * c + 7] = bf16_hi(w.w);
+        const vl_u32x4 w = vl_load<NT>(reinterpret_cast<const vl_u32x4*>(p + 8 * c));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          out[8 * c + 2 * e] = bf16_lo(w[e]);
+          out[8 * c + 2 * e + 1] = bf16_hi(w[e]);
+        }
       }
     }
   }
 };
-template <int N> struct VecLoad<float, N> {
+template <int N, bool NT> struct VecLoad<float, N, NT> {
   static_assert(N % 4 == 0, "fp32 vector loads are multiples of 4 elements");
   __device__ static void run(const void* base, int64_t i, float* out) {
     const float* p = reinterpret_cast<const float*>(base) + i;
 #pragma unroll
     for (int c = 0; c < N / 4; ++c) {
-      float4 w = *reinterpret_cast<const float4*>(p + 4 * c);
-      out[4 * c + 0] = w.x; out[4 * c + 1] = w.y; out[4 * c + 2] = w.z; out[4 * c + 3] = w.w;
+      const vl_f32x4 w = vl_load<NT>(reinterpret_cast<const vl_f32x4*>(p + 4 * c));
+      out[4 * c + 0] = w[0]; out[4 * c + 1] = w[1]; out[4 * c + 2] = w[2]; out[4 * c + 3] = w[3];
     }
   }
 };

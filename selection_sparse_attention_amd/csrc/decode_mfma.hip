@@ -177,7 +177,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, DecodeShared<D,
   const int kt = lane & 15, jg = lane >> 4;            // K role
   const int vd = 2 * (lane % (D / 2)), vc = lane / (D / 2);   // V role
   const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + row0 * D + 8 * jg;
-  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v) + row0 * D + vd;
+  // V rows: a wave-uniform row address (scalar) plus this lane's dims
+  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v) + row0 * D;
 
   // raw list entry of this lane's token in a tile (a load for listed groups,
   // in bounds even past the end; checked when it is used)
@@ -193,7 +194,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, DecodeShared<D,
     t.tok = tok;
     const uint16_t* kp = kbase + (int64_t)max(tok, 0) * D;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) t.k[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + 32 * s));
+    for (int s = 0; s < KS; ++s)
+      t.k[s] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 32 * s)));
 #pragma unroll
     for (int r = 0; r < VT; ++r) {
       int tv = __builtin_amdgcn_readlane(tok, r * NCLS);
@@ -201,7 +203,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, DecodeShared<D,
         const int tv1 = __builtin_amdgcn_readlane(tok, r * NCLS + 1);
         tv = vc ? tv1 : tv;
       }
-      t.v[r] = *reinterpret_cast<const uint32_t*>(vbase + (int64_t)max(tv, 0) * D);
+      const uint16_t* vrow = vbase + (int64_t)max(tv, 0) * D;
+      t.v[r] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vrow + vd));
     }
   };
 

@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void select_scan_kernel(SelectArgs a) {
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {                 // all loads in flight first
     const int j = tile * kTile + i * kThreads + tid;
-    if (j < a.n) VecLoad<T, 16>::run(a.k_idx, (krow + j) * 16, kv[i]);
+    if (j < a.n) VecLoad<T, 16, true>::run(a.k_idx, (krow + j) * 16, kv[i]);
   }
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
