@@ -239,7 +239,7 @@ def run_decode(args, torch, sa, workloads, workload=None, steps=None, warmup=Non
     attn_b /= len(insts)
     step_b /= len(insts)
     tokens = cfg.batch * cfg.n_q_heads * cfg.n_ctx
-    kernel = "sparse_attn_decode (decode_mfma_kernel + decode_combine_kernel)"
+    kernel = "sparse_attn_decode (decode_mfma_kernel + decode_item_combine_kernel)"
     sha = source_sha(["decode.hip", "decode_mfma.hip", "common.hpp", "args.hpp"])
     achieved = attn_b / t_kernel / 1e9
     res = {

@@ -41,9 +41,11 @@
  *    launched); otherwise *workspace_bytes must hold the size of the buffer
  *    given, and a smaller value returns SA_ERR_WORKSPACE.  A workspace must be
  *    zero-filled before its first use and left untouched by the caller between
- *    calls: it carries per-group completion counters that every completed call
- *    returns to zero (after SA_ERR_HIP, zero-fill it again).  Calls that may
- *    run concurrently need distinct workspaces.
+ *    calls: it carries histograms and counters that every completed call
+ *    returns to zero (after SA_ERR_HIP, zero-fill it again).  Their offsets
+ *    depend on batch, the head counts and the head kinds (not on n_ctx): after
+ *    a call with different values of those, zero-fill it again.  Calls that
+ *    may run concurrently need distinct workspaces.
  *  - Errors: arguments are validated on the host before anything is launched;
  *    an invalid argument launches nothing.  A failed launch returns SA_ERR_HIP
  *    (work enqueued before it may still run).  Faults inside kernels surface at

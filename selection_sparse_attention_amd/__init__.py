@@ -162,17 +162,29 @@ def _check(status, where):
 
 class Workspace:
     """A reusable device workspace (a zero-filled torch uint8 tensor, grown on
-    demand).  Use one per stream; the library leaves it zero-filled."""
+    demand).  Use one per stream.  The library returns the parts it needs zero
+    to zero after every call; when the layout changes (batch, head counts or
+    head kinds), the buffer is zero-filled again."""
 
     def __init__(self, device="cuda"):
         self.device = device
         self.buf = None
+        self.layout = None
 
-    def get(self, nbytes: int) -> torch.Tensor:
-        # zero-filled on allocation, as the library's counters require
+    def get(self, nbytes: int, layout=None) -> torch.Tensor:
         if self.buf is None or self.buf.numel() < nbytes:
             self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+        elif layout != self.layout:
+            self.buf.zero_()
+        self.layout = layout
         return self.buf
+
+
+def _layout(params: Params):
+    """What fixes the offsets of a workspace's zero-carrying regions."""
+    kinds = (ctypes.string_at(params.head_kind, params.n_q_heads)
+             if params.head_kind and params.n_q_heads > 0 else None)
+    return (params.batch, params.n_q_heads, params.n_kv_heads, kinds)
 
 
 _default_ws = {}
@@ -215,7 +227,7 @@ def index_build(params: Params, bufs: Buffers, mode: int, t_begin: int, t_end: i
 def select(params: Params, bufs: Buffers, mode: int, ws: Optional[Workspace] = None,
            stream=None):
     need = workspace_size("select", params, bufs, mode)
-    w = _workspace(ws, "select").get(need)
+    w = _workspace(ws, "select").get(need, _layout(params))
     n = ctypes.c_size_t(w.numel())
     _check(_lib.sparse_attn_select(ctypes.byref(params), ctypes.byref(bufs), mode,
                                    w.data_ptr(), ctypes.byref(n), _stream(stream)), "select")

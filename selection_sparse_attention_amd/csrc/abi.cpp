@@ -117,20 +117,25 @@ int32_t pyramid_geom(const sa_params* p, PyrGeom* g) {
 constexpr int kSelTile = 1024;
 
 struct SelectWs {
-  float* logits; uint32_t* cnt1; double* mass1; sa::RowState* state; uint64_t* lookback;
+  float* logits; uint32_t* cnt1; double* mass1; uint32_t* maxkey; sa::RowState* state;
+  uint64_t* lookback;
   int tiles; int64_t row_stride; size_t bytes;
 };
 
+// The regions that must be zero when a call starts (the level-1 histogram and
+// the row maxima, returned to zero by every call) come first, so their
+// offsets depend on the number of rows only, not on n_ctx.
 SelectWs carve_select(void* ws, int rows, int n) {
   SelectWs s{};
   s.tiles = (n + kSelTile - 1) / kSelTile;
   s.row_stride = (int64_t)s.tiles * kSelTile;
   Carver c(ws);
-  s.logits = c.take<float>((size_t)rows * s.row_stride);
   s.cnt1 = c.take<uint32_t>((size_t)rows * 4096);
   s.mass1 = c.take<double>((size_t)rows * 4096);
+  s.maxkey = c.take<uint32_t>((size_t)rows);
   s.state = c.take<sa::RowState>((size_t)rows);
   s.lookback = c.take<uint64_t>((size_t)rows * s.tiles);
+  s.logits = c.take<float>((size_t)rows * s.row_stride);
   s.bytes = c.size();
   return s;
 }
@@ -311,7 +316,8 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
       a.select_all = (p->top_k >= p->n_ctx) ? 1 : 0;
     }
     a.tiles = sw.tiles; a.row_stride = sw.row_stride;
-    a.logits = sw.logits; a.cnt1 = sw.cnt1; a.mass1 = sw.mass1; a.state = sw.state;
+    a.logits = sw.logits; a.cnt1 = sw.cnt1; a.mass1 = sw.mass1; a.maxkey = sw.maxkey;
+    a.state = sw.state;
     a.lookback = sw.lookback; a.groups = gl;
     return hip_status(sa::launch_select_lowrank(a, p->dtype, s));
   }

@@ -81,6 +81,7 @@ struct SelectArgs {
   // workspace
   float* logits;         // [rows, row_stride]
   uint32_t* cnt1; double* mass1;   // [rows, 4096]: level-1 histogram, zero between calls
+  uint32_t* maxkey;      // [rows]: largest order key of the row's logits, zero between calls
   RowState* state;       // [rows]: the cut found by the row kernel
   uint64_t* lookback;    // [rows, tiles]: compaction prefix flags
   GroupList groups;

@@ -15,19 +15,22 @@
 //   scan (tiles x rows)  logits to the workspace (4 B/token) + level-1
 //                        histogram of counts and fp64 masses, merged into the
 //                        row's histogram with atomics
-//   row  (rows)          one 1024-thread workgroup per row: the level-1 cut,
-//                        then the logits of the cut bucket gathered into LDS
-//                        and levels 2 and 3 over them (LDS histograms): the
-//                        exact cut key and how many of its ties to keep
+//   row  (rows)          one 1024-thread workgroup per row: the level-1 cut
+//                        from the merged histogram held in registers, then
+//                        the logits of the cut bucket gathered into LDS and
+//                        levels 2 and 3 over them (LDS histograms): the exact
+//                        cut key and how many of its ties to keep
 //   compact (tiles x rows) ascending positions, via a decoupled look-back
 //
 // Only the scan reads the 32 B/token index; the row kernel and the
 // compaction read the row's 4 B/token logits once each.  Level-1 masses are taken relative
 // to each bucket's upper bound - a data-independent reference, so tile
 // histograms add without knowing the maximum - and rescaled to the top
-// bucket's bound R when the row kernel reads them; later levels use R
-// directly.  The row kernel zeroes the row's level-1 histogram after reading
-// it, so a workspace that starts zero-filled stays reusable.
+// bucket's bound R when the row kernel reads them (the scan also records the
+// row's largest key); later levels use R directly.  The row kernel zeroes the
+// row's level-1 histogram and largest key after reading them, and the scan
+// clears the compaction's look-back words, so a workspace that starts
+// zero-filled stays reusable.
 #include "args.hpp"
 #include "common.hpp"
 
@@ -69,10 +72,13 @@ template <typename T, bool MASS>
 __global__ __launch_bounds__(kThreads) void select_scan_kernel(SelectArgs a) {
   __shared__ uint32_t lc[4096];
   __shared__ double lw[MASS ? 4096 : 1];
+  __shared__ uint32_t s_kmax[kThreads / 64];
   const int row = blockIdx.y, tile = blockIdx.x, tid = threadIdx.x;
   int b, g;
   row_coords(a, row, b, g);
   for (int i = tid; i < 4096; i += kThreads) { lc[i] = 0; if (MASS) lw[i] = 0.0; }
+  // the compaction's look-back words of this call start empty
+  if (tid == 0) a.lookback[(int64_t)row * a.tiles + tile] = 0;
 
   // qbar: mean of the group's index queries (exact for power-of-two G on
   // lattice inputs)
@@ -97,6 +103,7 @@ __global__ __launch_bounds__(kThreads) void select_scan_kernel(SelectArgs a) {
     const int j = tile * kTile + i * kThreads + tid;
     if (j < a.n) VecLoad<T, 16, true>::run(a.k_idx, (krow + j) * 16, kv[i]);
   }
+  uint32_t kmax = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int j = tile * kTile + i * kThreads + tid;
@@ -107,162 +114,244 @@ __global__ __launch_bounds__(kThreads) void select_scan_kernel(SelectArgs a) {
       float l = acc * 0.25f;
       if (l == 0.f) l = 0.f;                       // fold -0 into +0
       lg[j] = l;
-      const uint32_t bk = order_key(l) >> 20;
+      const uint32_t key = order_key(l);
+      kmax = max(kmax, key);
+      const uint32_t bk = key >> 20;
       atomicAdd(&lc[bk], 1u);
       if (MASS) atomicAdd(&lw[bk], exp((double)l - bucket_hi(bk, 20)));
     }
   }
+  // the row's largest key (its top bucket's bound is the row kernel's
+  // reference for the masses): one atomic per workgroup
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, m));
+  if ((tid & 63) == 0) s_kmax[tid >> 6] = kmax;
   __syncthreads();
+  if (tid == 0) {
+    uint32_t km = s_kmax[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) km = max(km, s_kmax[w]);
+    if (km) atomicMax(a.maxkey + row, km);
+  }
   merge_hist<4096>(lc, lw, a.cnt1 + (int64_t)row * 4096, a.mass1 + (int64_t)row * 4096, MASS);
 }
 
 // ------------------------------------------------------------------ row
 constexpr int kRowThreads = 1024;
+constexpr int kRowWaves = kRowThreads / 64;
+constexpr int kRowU = 8;                              // float4 per thread per chunk
+constexpr int kRowChunk = kRowThreads * kRowU * 4;    // tokens per chunk (32 per thread)
+constexpr int kCand = 8192;        // logits of the level-1 cut bucket kept in LDS
 
-struct FindScratch {
-  double scan_d[kRowThreads / 64];
-  int64_t scan_i[kRowThreads / 64];
-  int top, bm, bc;
-  double bm_w, bc_w;          // mass above the crossing buckets
-  int64_t bm_c, bc_c;         // count above the crossing buckets
+typedef uint32_t sel_u32x4 __attribute__((ext_vector_type(4)));
+typedef double sel_f64x2 __attribute__((ext_vector_type(2)));
+typedef float sel_f32x4 __attribute__((ext_vector_type(4)));
+
+// Buckets of one level where the mass and the count targets are crossed, as
+// published by the threads that own them (-1: not crossed in this level).
+struct Cross {
+  int bm, bc;
+  double bm_w, bc_w;          // mass above the crossing bucket
+  int64_t bm_c, bc_c;         // count above the crossing bucket
 };
 
-// Cut of one radix level from the LDS histogram (s_c counts, s_w masses) of
-// the keys under the current prefix: finds the bucket holding the cut under
-// the live criteria, folds every bucket above it into the row state, and at
-// level 3 fixes the cut key and the number of its ties to keep.
-template <int LEVEL, bool MASS>
-__device__ void find_cut(const SelectArgs& a, const uint32_t* s_c, double* s_w, RowState& st,
-                         FindScratch& fs) {
-  constexpr int NT = kRowThreads;
-  constexpr int NB = (LEVEL == 3) ? 256 : 4096;
-  constexpr int PER = (NB >= NT) ? NB / NT : 1;     // buckets per owning thread
-  constexpr int BITS = (NB == 4096) ? 12 : 8;
-  const int tid = threadIdx.x;
-  const bool owns = PER * tid < NB;
-  if (tid == 0) { fs.top = -1; fs.bm = -1; fs.bc = -1; }
-  __syncthreads();
-  if (LEVEL == 1 && MASS) {
-    // reference R = upper bound of the highest non-empty bucket
-    for (int i = tid; i < NB; i += NT) if (s_c[i]) atomicMax(&fs.top, i);
-    __syncthreads();
-    const double R = bucket_hi((uint32_t)max(fs.top, 0), 20);
-    for (int i = tid; i < NB; i += NT)
-      if (s_c[i]) s_w[i] = s_w[i] * exp(bucket_hi((uint32_t)i, 20) - R);
-    if (tid == 0) st.R = R;
-    __syncthreads();
+struct RowShared {
+  double wave_w[3][kRowWaves];     // per level: inclusive wave totals
+  int64_t wave_c[3][kRowWaves];
+  uint32_t cand_w[2][kRowWaves];   // candidate counts, alternating per chunk
+  Cross x[3];
+};
+
+// A 32- or 64-bit value of one lane (the lane index is wave-uniform), or of
+// the first active lane: the result lives in scalar registers.
+template <typename T>
+__device__ __forceinline__ T lane_value(T v, int src) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
+  } else {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, src);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), src);
+    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
   }
-  // thread t owns buckets NB-1-PER*t ... NB-PER*t (descending key order)
+}
+template <typename T>
+__device__ __forceinline__ T uniform(T v) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+  } else {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+  }
+}
+
+// One radix level.  Thread t owns the PER buckets NB-1-PER*t ... NB-PER*t
+// (descending key order), their counts c[] and masses w[] in registers.  The
+// prefix above each thread's buckets comes from wave scans and, across the
+// workgroup's waves, one barrier and a 16-lane scan of the wave totals (with
+// ONE_WAVE a single wave owns every bucket and no barrier is needed).  The
+// owners of the crossing buckets publish them and every thread takes the same
+// decision, in scalar registers, into its copy of the row state `st`.  The
+// histogram hc / hw in LDS is read only by the rare fallback below and, at
+// level 3, for the tie count.
+template <int LEVEL, bool MASS, int PER, int NB, bool ONE_WAVE>
+__device__ __forceinline__ void cut_level(const SelectArgs& a, const uint32_t (&c)[PER],
+                                          const double (&w)[PER], bool owns, RowState& st,
+                                          RowShared& sh, const uint32_t* hc, const double* hw) {
+  constexpr int BITS = (NB == 4096) ? 12 : 8;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int owner = ONE_WAVE ? lane : tid;
   double tw = 0.0;
   int64_t tc = 0;
   if (owns) {
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int bk = NB - 1 - (PER * tid + k);
-      if (MASS) tw += s_w[bk];
-      tc += s_c[bk];
+      if (MASS) tw += w[k];
+      tc += c[k];
     }
   }
-  double totw;
-  int64_t totc;
-  const double pre_w = block_exclusive_scan<double, NT>(tw, fs.scan_d, &totw);
-  const int64_t pre_c = block_exclusive_scan<int64_t, NT>(tc, fs.scan_i, &totc);
+  const double iw = wave_inclusive_scan(tw);
+  const int64_t ic = wave_inclusive_scan(tc);
+  double pre_w, totw;
+  int64_t pre_c, totc;
+  if constexpr (ONE_WAVE) {
+    pre_w = iw - tw;
+    pre_c = ic - tc;
+    totw = lane_value(iw, 63);
+    totc = lane_value(ic, 63);
+  } else {
+    if (lane == 63) {
+      sh.wave_w[LEVEL - 1][wid] = iw;
+      sh.wave_c[LEVEL - 1][wid] = ic;
+    }
+    lds_barrier();
+    // every 16-lane row holds the wave totals; their inclusive prefix
+    double pw = sh.wave_w[LEVEL - 1][lane & 15];
+    int64_t pc = sh.wave_c[LEVEL - 1][lane & 15];
+    pw += dpp_move<0x111, 0xF>(pw); pc += dpp_move<0x111, 0xF>(pc);
+    pw += dpp_move<0x112, 0xF>(pw); pc += dpp_move<0x112, 0xF>(pc);
+    pw += dpp_move<0x114, 0xF>(pw); pc += dpp_move<0x114, 0xF>(pc);
+    pw += dpp_move<0x118, 0xF>(pw); pc += dpp_move<0x118, 0xF>(pc);
+    totw = lane_value(pw, kRowWaves - 1);
+    totc = lane_value(pc, kRowWaves - 1);
+    const double bw = wid ? lane_value(pw, wid - 1) : 0.0;
+    const int64_t bcn = wid ? lane_value(pc, wid - 1) : 0;
+    pre_w = bw + iw - tw;
+    pre_c = bcn + ic - tc;
+  }
   const int crit = st.crit;
   const double tmass = (LEVEL == 1) ? totw * a.top_p : st.target_mass;
   const double base_w = (LEVEL == 1) ? 0.0 : st.mass_above;
   const int64_t base_c = (LEVEL == 1) ? 0 : st.count_above;
   const int64_t tcount = st.target_count;
+  // this thread's crossings, if any
+  int my_bm = -1, my_bc = -1;
+  double my_bm_w = 0.0, my_bc_w = 0.0;
+  int64_t my_bm_c = 0, my_bc_c = 0;
   if (owns) {
     double cw = base_w + pre_w;
     int64_t cc = base_c + pre_c;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int bk = NB - 1 - (PER * tid + k);
-      const double nw = cw + (MASS ? s_w[bk] : 0.0);
-      const int64_t nc = cc + s_c[bk];
-      if ((crit & CRIT_MASS) && s_c[bk] && cw < tmass && nw >= tmass) {
-        fs.bm = bk; fs.bm_w = cw; fs.bm_c = cc;
-      }
-      if ((crit & CRIT_COUNT) && s_c[bk] && cc < tcount && nc >= tcount) {
-        fs.bc = bk; fs.bc_w = cw; fs.bc_c = cc;
-      }
+      const int bk = NB - 1 - (PER * owner + k);
+      const double nw = cw + (MASS ? w[k] : 0.0);
+      const int64_t nc = cc + c[k];
+      if ((crit & CRIT_MASS) && c[k] && cw < tmass && nw >= tmass) { my_bm = bk; my_bm_w = cw; my_bm_c = cc; }
+      if ((crit & CRIT_COUNT) && c[k] && cc < tcount && nc >= tcount) { my_bc = bk; my_bc_w = cw; my_bc_c = cc; }
       cw = nw;
       cc = nc;
     }
   }
-  __syncthreads();
-  if (tid == 0) {
-    if (LEVEL == 1) st.target_mass = tmass;
-    const bool m_on = (crit & CRIT_MASS) != 0, c_on = (crit & CRIT_COUNT) != 0;
-    int bm = fs.bm, bc = fs.bc;
-    double bm_w = fs.bm_w;
-    int64_t bm_c = fs.bm_c;
-    if (m_on && bm < 0 && LEVEL > 1) {
-      // The previous level placed the crossing inside this prefix; a
-      // last-place disagreement between the two levels' mass sums lands it on
-      // the first or last non-empty bucket (rare: a serial walk is fine).
-      int hi_b = -1, lo_b = -1;
-      for (int bk = NB - 1; bk >= 0; --bk)
-        if (s_c[bk]) { if (hi_b < 0) hi_b = bk; lo_b = bk; }
-      bm = (base_w >= tmass) ? hi_b : lo_b;
-      bm_w = base_w;
-      bm_c = base_c;
-      for (int bk = NB - 1; bk > bm && bm >= 0; --bk) { if (MASS) bm_w += s_w[bk]; bm_c += s_c[bk]; }
-    }
-    // the mass crossing decides unless the count crossing lies further down
-    // the order (a lower bucket); both stay live while they share a bucket
-    int bstar, ncrit;
-    if (m_on && c_on) {
-      const bool mass_wins = (bc < 0) || (bm >= 0 && bm < bc);
-      const bool count_wins = (bm >= 0) && (bc >= 0) && (bc < bm);
-      bstar = count_wins ? bc : bm;
-      ncrit = mass_wins ? CRIT_MASS : (count_wins ? CRIT_COUNT : (CRIT_MASS | CRIT_COUNT));
-    } else {
-      bstar = m_on ? bm : bc;
-      ncrit = crit;
-    }
-    if (bstar < 0) {                 // the target lies past the last token
-      st.all = 1;
-      st.m = a.n;
-    } else {
-      // everything above the chosen bucket, as accumulated by the scan
-      const bool from_mass = (bstar == bm) && m_on;
-      const double above_w = from_mass ? bm_w : fs.bc_w;
-      const int64_t above_c = from_mass ? bm_c : fs.bc_c;
-      const uint32_t prefix = (LEVEL == 1) ? (uint32_t)bstar : ((st.prefix << BITS) | (uint32_t)bstar);
-      st.mass_above = above_w;
-      st.count_above = above_c;
-      st.crit = ncrit;
-      st.prefix = prefix;
-      if (LEVEL == 3) {
-        const int64_t ties = s_c[bstar];
-        int64_t need = 1;
-        if (ncrit & CRIT_MASS) {
-          const double e = exp((double)key_to_float(prefix) - st.R);
-          const double c = ceil((tmass - above_w) / e);
-          need = (c >= (double)ties) ? ties : (c <= 1.0 ? 1 : (int64_t)c);
-        }
-        if (ncrit & CRIT_COUNT) {
-          const int64_t nc = tcount - above_c;
-          need = need > nc ? need : nc;
-        }
-        if (need > ties) need = ties;
-        if (need < 1) need = 1;
-        st.cut_key = prefix;
-        st.need = (int32_t)need;
-        st.m = (int32_t)(above_c + need);
-      }
-    }
+  int bm, bc;
+  double bm_w, bc_w;
+  int64_t bm_c, bc_c;
+  if constexpr (ONE_WAVE) {
+    const uint64_t fm = __ballot(my_bm >= 0), fc = __ballot(my_bc >= 0);
+    const int lm = fm ? __ffsll((unsigned long long)fm) - 1 : 0;
+    const int lc = fc ? __ffsll((unsigned long long)fc) - 1 : 0;
+    bm = fm ? lane_value(my_bm, lm) : -1;
+    bm_w = lane_value(my_bm_w, lm);
+    bm_c = lane_value(my_bm_c, lm);
+    bc = fc ? lane_value(my_bc, lc) : -1;
+    bc_w = lane_value(my_bc_w, lc);
+    bc_c = lane_value(my_bc_c, lc);
+  } else {
+    Cross& x = sh.x[LEVEL - 1];
+    if (my_bm >= 0) { x.bm = my_bm; x.bm_w = my_bm_w; x.bm_c = my_bm_c; }
+    if (my_bc >= 0) { x.bc = my_bc; x.bc_w = my_bc_w; x.bc_c = my_bc_c; }
+    lds_barrier();
+    bm = uniform(x.bm);
+    bm_w = uniform(x.bm_w);
+    bm_c = uniform(x.bm_c);
+    bc = uniform(x.bc);
+    bc_w = uniform(x.bc_w);
+    bc_c = uniform(x.bc_c);
   }
-  __syncthreads();
+  if (LEVEL == 1) st.target_mass = tmass;
+  const bool m_on = (crit & CRIT_MASS) != 0, c_on = (crit & CRIT_COUNT) != 0;
+  if (LEVEL > 1 && m_on && bm < 0) {
+    // The previous level placed the crossing inside this prefix; a last-place
+    // disagreement between the two levels' mass sums lands it on the first or
+    // last non-empty bucket (rare: a serial walk is fine).
+    int hi_b = -1, lo_b = -1;
+    for (int bk = NB - 1; bk >= 0; --bk)
+      if (hc[bk]) { if (hi_b < 0) hi_b = bk; lo_b = bk; }
+    bm = (base_w >= tmass) ? hi_b : lo_b;
+    bm_w = base_w;
+    bm_c = base_c;
+    for (int bk = NB - 1; bk > bm && bm >= 0; --bk) { if (MASS) bm_w += hw[bk]; bm_c += hc[bk]; }
+  }
+  // the mass crossing decides unless the count crossing lies further down the
+  // order (a lower bucket); both stay live while they share a bucket
+  int bstar, ncrit;
+  if (m_on && c_on) {
+    const bool mass_wins = (bc < 0) || (bm >= 0 && bm < bc);
+    const bool count_wins = (bm >= 0) && (bc >= 0) && (bc < bm);
+    bstar = count_wins ? bc : bm;
+    ncrit = mass_wins ? CRIT_MASS : (count_wins ? CRIT_COUNT : (CRIT_MASS | CRIT_COUNT));
+  } else {
+    bstar = m_on ? bm : bc;
+    ncrit = crit;
+  }
+  if (bstar < 0) {                   // the target lies past the last token
+    st.all = 1;
+    st.m = a.n;
+    return;
+  }
+  const bool from_mass = (bstar == bm) && m_on;
+  const double above_w = from_mass ? bm_w : bc_w;
+  const int64_t above_c = from_mass ? bm_c : bc_c;
+  const uint32_t prefix = (LEVEL == 1) ? (uint32_t)bstar : ((st.prefix << BITS) | (uint32_t)bstar);
+  st.mass_above = above_w;
+  st.count_above = above_c;
+  st.crit = ncrit;
+  st.prefix = prefix;
+  if (LEVEL == 3) {
+    const int64_t ties = hc[bstar];
+    int64_t need = 1;
+    if (ncrit & CRIT_MASS) {
+      const double e = exp((double)key_to_float(prefix) - st.R);
+      const double cn = ceil((tmass - above_w) / e);
+      need = (cn >= (double)ties) ? ties : (cn <= 1.0 ? 1 : (int64_t)cn);
+    }
+    if (ncrit & CRIT_COUNT) {
+      const int64_t nc = tcount - above_c;
+      need = need > nc ? need : nc;
+    }
+    if (need > ties) need = ties;
+    if (need < 1) need = 1;
+    st.cut_key = prefix;
+    st.need = (int32_t)need;
+    st.m = (int32_t)(above_c + need);
+  }
 }
 
-constexpr int kRowU = 8;                              // float4 per thread per chunk
-constexpr int kRowChunk = kRowThreads * kRowU * 4;    // tokens per chunk (32 per thread)
-
 // Histogram of the next radix digit of the row's logits whose keys carry the
-// current prefix (level 2: bits 19..8, level 3: bits 7..0).  Each thread
-// issues its chunk's eight 16-byte loads before using any of them.
+// current prefix (level 2: bits 19..8, level 3: bits 7..0), streamed from the
+// workspace: the fallback when the cut bucket holds more than kCand logits.
 template <int LEVEL, bool MASS>
 __device__ void level_hist(const SelectArgs& a, const float* lg, const RowState& st, uint32_t* s_c,
                            double* s_w) {
@@ -274,81 +363,24 @@ __device__ void level_hist(const SelectArgs& a, const float* lg, const RowState&
   __syncthreads();
   const uint32_t prefix = st.prefix;
   const double R = st.R;
+  const int last = (int)a.row_stride - 4;
   for (int c0 = 0; c0 < a.n; c0 += kRowChunk) {
-    float4 v[kRowU];
+    sel_f32x4 v[kRowU];
 #pragma unroll
-    for (int k = 0; k < kRowU; ++k) {
-      const int j = c0 + 4 * (tid + k * kRowThreads);   // < row_stride: in bounds
-      v[k] = *reinterpret_cast<const float4*>(lg + j);
-    }
+    for (int k = 0; k < kRowU; ++k)
+      v[k] = *reinterpret_cast<const sel_f32x4*>(lg + min(c0 + 4 * (tid + k * kRowThreads), last));
 #pragma unroll
     for (int k = 0; k < kRowU; ++k) {
       const int j = c0 + 4 * (tid + k * kRowThreads);
-      const float vv[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t key = order_key(vv[i]);
+        const uint32_t key = order_key(v[k][i]);
         if (j + i < a.n && (key >> PSHIFT) == prefix) {
           const uint32_t bk = (key >> SHIFT) & (NB - 1);
           atomicAdd(&s_c[bk], 1u);
-          if (MASS) atomicAdd(&s_w[bk], exp((double)vv[i] - R));
+          if (MASS) atomicAdd(&s_w[bk], exp((double)v[k][i] - R));
         }
       }
-    }
-  }
-  __syncthreads();
-}
-
-constexpr int kCand = 8192;        // logits of the level-1 cut bucket kept in LDS
-
-// Collect the logits of the level-1 cut bucket into LDS (order is free).
-// Returns their number; more than kCand means they did not fit.
-__device__ int collect_candidates(const SelectArgs& a, const float* lg, uint32_t prefix, float* cand,
-                                  int* s_cnt) {
-  const int tid = threadIdx.x;
-  if (tid == 0) *s_cnt = 0;
-  __syncthreads();
-  for (int c0 = 0; c0 < a.n; c0 += kRowChunk) {
-    float4 v[kRowU];
-#pragma unroll
-    for (int k = 0; k < kRowU; ++k) v[k] = *reinterpret_cast<const float4*>(lg + c0 + 4 * (tid + k * kRowThreads));
-#pragma unroll
-    for (int k = 0; k < kRowU; ++k) {
-      const int j = c0 + 4 * (tid + k * kRowThreads);
-      const float vv[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if ((j + i < a.n) && ((order_key(vv[i]) >> 20) == prefix)) {
-          const int slot = atomicAdd(s_cnt, 1);
-          if (slot < kCand) cand[slot] = vv[i];
-        }
-      }
-    }
-  }
-  __syncthreads();
-  return *s_cnt;
-}
-
-// Histogram of the next digit over the candidates whose keys carry the
-// current prefix (level 2: bits 19..8 under the 12-bit prefix, level 3:
-// bits 7..0 under the 24-bit prefix).
-template <int LEVEL, bool MASS>
-__device__ void cand_hist(const float* cand, int nc, const RowState& st, uint32_t* s_c, double* s_w) {
-  constexpr int NB = (LEVEL == 2) ? 4096 : 256;
-  constexpr int SHIFT = (LEVEL == 2) ? 8 : 0;
-  constexpr int PSHIFT = (LEVEL == 2) ? 20 : 8;
-  const int tid = threadIdx.x;
-  for (int i = tid; i < NB; i += kRowThreads) { s_c[i] = 0; if (MASS) s_w[i] = 0.0; }
-  __syncthreads();
-  const uint32_t prefix = st.prefix;
-  const double R = st.R;
-  for (int i = tid; i < nc; i += kRowThreads) {
-    const float l = cand[i];
-    const uint32_t key = order_key(l);
-    if ((key >> PSHIFT) == prefix) {
-      const uint32_t bk = (key >> SHIFT) & (NB - 1);
-      atomicAdd(&s_c[bk], 1u);
-      if (MASS) atomicAdd(&s_w[bk], exp((double)l - R));
     }
   }
   __syncthreads();
@@ -356,55 +388,200 @@ __device__ void cand_hist(const float* cand, int nc, const RowState& st, uint32_
 
 // One workgroup per row: every radix level after the scan's, leaving the
 // row's cut (key, ties to keep, count) in the workspace for the compaction.
+// Every thread holds the row state; the barriers order LDS only, so the first
+// chunk of logits, requested at the start, stays in flight through level 1.
 template <bool MASS>
 __global__ __launch_bounds__(kRowThreads) void select_row_kernel(SelectArgs a) {
-  __shared__ uint32_t s_c[4096];
+  __shared__ uint32_t s_c[4096];                 // level-2 histogram
   __shared__ double s_w[MASS ? 4096 : 1];
-  __shared__ FindScratch fs;
-  __shared__ RowState st;
+  __shared__ uint32_t s_c3[256];                 // level-3 histogram
+  __shared__ double s_w3[MASS ? 256 : 1];
   __shared__ float s_cand[kCand];
-  __shared__ int s_ncand;
-  const int row = blockIdx.x, tid = threadIdx.x;
-  if (tid == 0) {
-    RowState init{};
-    init.target_count = a.target_count;
-    init.crit = (MASS ? CRIT_MASS : 0) | (a.target_count > 0 ? CRIT_COUNT : 0);
-    st = init;
-  }
-  // level 1: the row's histogram as merged by the scan, zeroed after use
+  __shared__ RowShared sh;
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+
+  // level 1: this thread's four buckets of the histogram merged by the scan
+  // (returned to zero here), and the row's largest key
   uint32_t* gc = a.cnt1 + (int64_t)row * 4096;
   double* gw = a.mass1 + (int64_t)row * 4096;
-  uint32_t cv[4];
-  double wv[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    cv[k] = gc[tid + k * kRowThreads];
-    wv[k] = MASS ? gw[tid + k * kRowThreads] : 0.0;
+  const int b0 = 4092 - 4 * tid;                 // buckets b0 .. b0 + 3
+  const sel_u32x4 c4 = *reinterpret_cast<const sel_u32x4*>(gc + b0);
+  sel_f64x2 w4[2] = {{0.0, 0.0}, {0.0, 0.0}};
+  if (MASS) {
+    w4[0] = *reinterpret_cast<const sel_f64x2*>(gw + b0);
+    w4[1] = *reinterpret_cast<const sel_f64x2*>(gw + b0 + 2);
   }
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    s_c[tid + k * kRowThreads] = cv[k];
-    if (MASS) s_w[tid + k * kRowThreads] = wv[k];
-    gc[tid + k * kRowThreads] = 0;
-    if (MASS) gw[tid + k * kRowThreads] = 0.0;
-  }
-  __syncthreads();
-  find_cut<1, MASS>(a, s_c, s_w, st, fs);
+  const uint32_t mk = a.maxkey[row];
+  // first chunk of the row's logits (addresses clamped into the row)
   const float* lg = a.logits + (int64_t)row * a.row_stride;
-  // levels 2 and 3 over the cut bucket's logits, gathered into LDS once (a
-  // streaming pass per level when they do not fit)
+  const int last = (int)a.row_stride - 4;
+  sel_f32x4 v[kRowU];
+#pragma unroll
+  for (int k = 0; k < kRowU; ++k)
+    v[k] = *reinterpret_cast<const sel_f32x4*>(lg + min(4 * (tid + k * kRowThreads), last));
+  *reinterpret_cast<sel_u32x4*>(gc + b0) = sel_u32x4{0u, 0u, 0u, 0u};
+  if (MASS) {
+    *reinterpret_cast<sel_f64x2*>(gw + b0) = sel_f64x2{0.0, 0.0};
+    *reinterpret_cast<sel_f64x2*>(gw + b0 + 2) = sel_f64x2{0.0, 0.0};
+  }
+  for (int i = tid; i < 4096; i += kRowThreads) { s_c[i] = 0; if (MASS) s_w[i] = 0.0; }
+  if (tid < 256) { s_c3[tid] = 0; if (MASS) s_w3[tid] = 0.0; }
+  if (tid < 3) { sh.x[tid].bm = -1; sh.x[tid].bc = -1; }
+
+  RowState st{};
+  st.target_count = a.target_count;
+  st.crit = (MASS ? CRIT_MASS : 0) | (a.target_count > 0 ? CRIT_COUNT : 0);
+  // masses arrive relative to each bucket's upper bound; rescale them to the
+  // top bucket's bound R
+  const double R = bucket_hi(mk >> 20, 20);
+  if (MASS) st.R = R;
+  uint32_t c1[4];
+  double w1[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int e = 3 - k;                           // bucket 4095 - 4 tid - k
+    c1[k] = c4[e];
+    const double wr = w4[e >> 1][e & 1];
+    w1[k] = (MASS && c1[k]) ? wr * exp(bucket_hi((uint32_t)(b0 + e), 20) - R) : 0.0;
+  }
+  cut_level<1, MASS, 4, 4096, false>(a, c1, w1, true, st, sh, nullptr, nullptr);
+  if (tid == 0) a.maxkey[row] = 0;                // every thread has used it
+
+  // the logits of the level-1 cut bucket, gathered into LDS (ascending
+  // positions per chunk; a block prefix of per-thread counts gives the slots)
   int nc = 0;
-  if (!st.all) nc = collect_candidates(a, lg, st.prefix, s_cand, &s_ncand);
+  if (!st.all) {
+    const uint32_t pf = st.prefix;
+    uint32_t total = 0;
+    int it = 0;
+    for (int c0 = 0; c0 < a.n; c0 += kRowChunk, ++it) {
+      if (c0 > 0) {
+#pragma unroll
+        for (int k = 0; k < kRowU; ++k)
+          v[k] = *reinterpret_cast<const sel_f32x4*>(lg + min(c0 + 4 * (tid + k * kRowThreads), last));
+      }
+      // bit 4k+i: value i of load k lies in the cut bucket (keys compared
+      // branch-free; positions past the row's end are masked off after)
+      const uint32_t kb = pf << 20;
+      uint32_t mask = 0;
+#pragma unroll
+      for (int k = 0; k < kRowU; ++k) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t u = __float_as_uint(v[k][i]);
+          const uint32_t key = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+          mask |= (uint32_t)((key - kb) < 0x100000u) << (4 * k + i);
+        }
+      }
+      const int rem = a.n - c0;
+      if (rem < kRowChunk) {
+        uint32_t valid = 0;
+#pragma unroll
+        for (int k = 0; k < kRowU; ++k) {
+          const int nv = min(max(rem - 4 * (tid + k * kRowThreads), 0), 4);
+          valid |= ((1u << nv) - 1u) << (4 * k);
+        }
+        mask &= valid;
+      }
+      const uint32_t cnt = __popc(mask);
+      const uint32_t incl = wave_inclusive_scan(cnt);
+      if (lane == 63) sh.cand_w[it & 1][wid] = incl;
+      lds_barrier();
+      uint32_t base = 0, tot = 0;
+#pragma unroll
+      for (int w = 0; w < kRowWaves; ++w) {
+        const uint32_t sc = sh.cand_w[it & 1][w];
+        if (w < wid) base += sc;
+        tot += sc;
+      }
+      if (mask) {
+        uint32_t slot = total + base + incl - cnt;
+#pragma unroll
+        for (int k = 0; k < kRowU; ++k)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if ((mask >> (4 * k + i)) & 1u) {
+              if (slot < (uint32_t)kCand) s_cand[slot] = v[k][i];
+              ++slot;
+            }
+      }
+      total += tot;
+    }
+    lds_barrier();
+    nc = (int)total;
+  }
   const bool fits = nc <= kCand;
+
+  // level 2: bits 19..8 under the 12-bit prefix
   if (!st.all) {
-    if (fits) cand_hist<2, MASS>(s_cand, nc, st, s_c, s_w); else level_hist<2, MASS>(a, lg, st, s_c, s_w);
-    find_cut<2, MASS>(a, s_c, s_w, st, fs);
+    if (fits) {
+      for (int i = tid; i < nc; i += kRowThreads) {
+        const float l = s_cand[i];
+        const uint32_t key = order_key(l);
+        if ((key >> 20) == st.prefix) {
+          const uint32_t bk = (key >> 8) & 4095u;
+          atomicAdd(&s_c[bk], 1u);
+          if (MASS) atomicAdd(&s_w[bk], exp((double)l - st.R));
+        }
+      }
+      lds_barrier();
+    } else {
+      level_hist<2, MASS>(a, lg, st, s_c, s_w);
+    }
+    const sel_u32x4 cc = *reinterpret_cast<const sel_u32x4*>(s_c + b0);
+    sel_f64x2 ww[2] = {{0.0, 0.0}, {0.0, 0.0}};
+    if (MASS) {
+      ww[0] = *reinterpret_cast<const sel_f64x2*>(s_w + b0);
+      ww[1] = *reinterpret_cast<const sel_f64x2*>(s_w + b0 + 2);
+    }
+    uint32_t c2[4];
+    double w2[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = 3 - k;
+      c2[k] = cc[e];
+      w2[k] = MASS ? ww[e >> 1][e & 1] : 0.0;
+    }
+    cut_level<2, MASS, 4, 4096, false>(a, c2, w2, true, st, sh, s_c, s_w);
   }
+
+  // level 3: bits 7..0 under the 24-bit prefix; the histogram by every
+  // wave, the cut by wave 0 alone (lane l owns buckets 255-4l ... 252-4l)
   if (!st.all) {
-    if (fits) cand_hist<3, MASS>(s_cand, nc, st, s_c, s_w); else level_hist<3, MASS>(a, lg, st, s_c, s_w);
-    find_cut<3, MASS>(a, s_c, s_w, st, fs);
+    if (fits) {
+      for (int i = tid; i < nc; i += kRowThreads) {
+        const float l = s_cand[i];
+        const uint32_t key = order_key(l);
+        if ((key >> 8) == st.prefix) {
+          atomicAdd(&s_c3[key & 255u], 1u);
+          if (MASS) atomicAdd(&s_w3[key & 255u], exp((double)l - st.R));
+        }
+      }
+      lds_barrier();
+    } else {
+      level_hist<3, MASS>(a, lg, st, s_c3, s_w3);
+    }
   }
-  if (tid == 0) a.state[row] = st;
+  if (wid != 0) return;
+  if (!st.all) {
+    const int b3 = 252 - 4 * lane;
+    const sel_u32x4 cc = *reinterpret_cast<const sel_u32x4*>(s_c3 + b3);
+    sel_f64x2 ww[2] = {{0.0, 0.0}, {0.0, 0.0}};
+    if (MASS) {
+      ww[0] = *reinterpret_cast<const sel_f64x2*>(s_w3 + b3);
+      ww[1] = *reinterpret_cast<const sel_f64x2*>(s_w3 + b3 + 2);
+    }
+    uint32_t c3[4];
+    double w3[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = 3 - k;
+      c3[k] = cc[e];
+      w3[k] = MASS ? ww[e >> 1][e & 1] : 0.0;
+    }
+    cut_level<3, MASS, 4, 256, true>(a, c3, w3, true, st, sh, s_c3, s_w3);
+  }
+  if (lane == 0) a.state[row] = st;
 }
 
 // ------------------------------------------------------------------ compact

@@ -352,3 +352,38 @@ def test_workspace_reuse_across_calls():
         run.decode()
         torch.cuda.synchronize()
         assert torch.equal(run.t["out"], first)
+
+
+def test_select_workspace_reuse_changing_data_and_shape():
+    """One selector workspace across calls whose data, context length (its
+    tile count) and batch change: every call's sets equal the oracle's."""
+    base = workloads.LLAMA_32K.with_(batch=2, n_ctx=5000, top_p=0.95, min_tokens=64)
+    steps = [(base, 0), (base, 1), (base.with_(n_ctx=6100), 2), (base.with_(n_ctx=2100), 3),
+             (base.with_(batch=1, n_ctx=6100), 4), (base, 5)]
+    ws = None
+    for cfg, s in steps:
+        log("select reuse", cfg.batch, cfg.n_ctx, s)
+
+        def accept(inp, cfg=cfg):
+            k, q = np64(inp["k_idx"]), np64(inp["q_idx"])
+            return all(oracle.topp_margin(_oracle_logits(cfg, k, q, b, g), cfg.top_p) >= 1e-7
+                       for b in range(cfg.batch) for g in _ret_groups(cfg))
+
+        _, inp = _robust_seed(cfg, lambda t, cfg=cfg: workloads.lattice_index_inputs(
+            cfg, 500 + 10 * s + t, k_amp=24, q_amp=12), accept)
+        run = DecodeRun(cfg, {}, n_cap=cfg.n_ctx)
+        if ws is not None:
+            run.ws_sel = ws
+        ws = run.ws_sel
+        run.t["k_idx"].copy_(to_dev(inp["k_idx"], cfg.dtype))
+        run.t["q_idx"].copy_(inp["q_idx"].to(DEV))
+        run.select()
+        torch.cuda.synchronize()
+        idx, cnt = run.sets()
+        k, q = np64(inp["k_idx"]), np64(inp["q_idx"])
+        for b in range(cfg.batch):
+            for g in _ret_groups(cfg):
+                ref, m = oracle.select_topp(_oracle_logits(cfg, k, q, b, g), cfg.top_p,
+                                            cfg.min_tokens)
+                assert cnt[b, g] == m, (s, b, g, cnt[b, g], m)
+                assert np.array_equal(idx[b, g, :m], ref), (s, b, g)
