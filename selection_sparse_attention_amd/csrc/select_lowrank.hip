@@ -68,6 +68,41 @@ __device__ __forceinline__ void merge_hist(const uint32_t* lc, const double* lw,
 }
 
 // ------------------------------------------------------------------ scan
+// Raw 32-byte index rows of one token, requested before any is used.
+template <typename T> struct IdxRow;
+template <> struct IdxRow<bf16_t> {
+  vl_u32x4 w[2];
+  __device__ void load(const void* base, int64_t row) {
+    const vl_u32x4* p = reinterpret_cast<const vl_u32x4*>(reinterpret_cast<const uint16_t*>(base) + row * 16);
+    w[0] = __builtin_nontemporal_load(p);
+    w[1] = __builtin_nontemporal_load(p + 1);
+  }
+  __device__ float dot(const float (&q)[16]) const {
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t x = w[e >> 2][e & 3];
+      acc = fmaf(q[2 * e], bf16_lo(x), acc);
+      acc = fmaf(q[2 * e + 1], bf16_hi(x), acc);
+    }
+    return acc;
+  }
+};
+template <> struct IdxRow<float> {
+  vl_f32x4 w[4];
+  __device__ void load(const void* base, int64_t row) {
+    const vl_f32x4* p = reinterpret_cast<const vl_f32x4*>(reinterpret_cast<const float*>(base) + row * 16);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) w[c] = __builtin_nontemporal_load(p + c);
+  }
+  __device__ float dot(const float (&q)[16]) const {
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc = fmaf(q[e], w[e >> 2][e & 3], acc);
+    return acc;
+  }
+};
+
 template <typename T, bool MASS>
 __global__ __launch_bounds__(kThreads) void select_scan_kernel(SelectArgs a) {
   __shared__ uint32_t lc[4096];
@@ -76,6 +111,13 @@ __global__ __launch_bounds__(kThreads) void select_scan_kernel(SelectArgs a) {
   const int row = blockIdx.y, tile = blockIdx.x, tid = threadIdx.x;
   int b, g;
   row_coords(a, row, b, g);
+  // the tile's index rows first (tokens past the end re-read the last one),
+  // so their latency overlaps everything up to the first use
+  const int64_t krow = ((int64_t)b * a.Hkv + g) * a.n_cap;
+  IdxRow<T> kr[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) kr[i].load(a.k_idx, krow + min(tile * kTile + i * kThreads + tid, a.n - 1));
+
   for (int i = tid; i < 4096; i += kThreads) { lc[i] = 0; if (MASS) lw[i] = 0.0; }
   // the compaction's look-back words of this call start empty
   if (tid == 0) a.lookback[(int64_t)row * a.tiles + tile] = 0;
@@ -93,25 +135,15 @@ __global__ __launch_bounds__(kThreads) void select_scan_kernel(SelectArgs a) {
   const float invG = 1.0f / (float)a.G;
 #pragma unroll
   for (int c = 0; c < 16; ++c) qb[c] *= invG;
-  __syncthreads();
+  lds_barrier();
 
-  const int64_t krow = ((int64_t)b * a.Hkv + g) * a.n_cap;
   float* lg = a.logits + (int64_t)row * a.row_stride;
-  float kv[kPer][16];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {                 // all loads in flight first
-    const int j = tile * kTile + i * kThreads + tid;
-    if (j < a.n) VecLoad<T, 16, true>::run(a.k_idx, (krow + j) * 16, kv[i]);
-  }
   uint32_t kmax = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int j = tile * kTile + i * kThreads + tid;
     if (j < a.n) {
-      float acc = 0.f;
-#pragma unroll
-      for (int c = 0; c < 16; ++c) acc = fmaf(qb[c], kv[i][c], acc);
-      float l = acc * 0.25f;
+      float l = kr[i].dot(qb) * 0.25f;
       if (l == 0.f) l = 0.f;                       // fold -0 into +0
       lg[j] = l;
       const uint32_t key = order_key(l);
@@ -317,8 +349,10 @@ __device__ __forceinline__ void cut_level(const SelectArgs& a, const uint32_t (&
     ncrit = crit;
   }
   if (bstar < 0) {                   // the target lies past the last token
-    st.all = 1;
+    st.all = 1;                      // every key lies above cut_key 0
     st.m = a.n;
+    st.cut_key = 0;
+    st.need = 0;
     return;
   }
   const bool from_mass = (bstar == bm) && m_on;
@@ -601,8 +635,10 @@ __global__ __launch_bounds__(kThreads) void select_compact_kernel(SelectArgs a) 
   row_coords(a, row, b, g);
   const int64_t orow = ((int64_t)b * a.Hkv + g) * a.n_cap;
   const int j0 = tile * kTile + tid * kPer;   // this thread's 4 consecutive tokens
-  const bool all = a.select_all || a.state[row].all;
-  if (all) {                                   // every token: position j goes to slot j
+  // their logits, requested first (in bounds: rows are whole tiles long)
+  const float* lg = a.logits + (int64_t)row * a.row_stride;
+  const vl_f32x4 lv = *reinterpret_cast<const vl_f32x4*>(lg + j0);
+  if (a.select_all) {                          // every token: position j goes to slot j
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
       if (j0 + i < a.n) a.sel_idx[orow + j0 + i] = j0 + i;
@@ -610,13 +646,12 @@ __global__ __launch_bounds__(kThreads) void select_compact_kernel(SelectArgs a) 
     return;
   }
   const RowState st = a.state[row];
-  const float* lg = a.logits + (int64_t)row * a.row_stride;
   uint32_t strict_f = 0, tie_f = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int j = j0 + i;
     if (j >= a.n) continue;
-    const uint32_t key = order_key(lg[j]);
+    const uint32_t key = order_key(lv[i]);
     if (key > st.cut_key) strict_f |= 1u << i;
     else if (key == st.cut_key) tie_f |= 1u << i;
   }
