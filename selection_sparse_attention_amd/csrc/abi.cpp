@@ -371,10 +371,12 @@ int32_t sparse_attn_decode(const sa_params* p, const sa_buffers* b, void* ws, si
   int tps = kDecodeTps, max_splits, target_items = 0;
   size_t n_partial;
   if (p->dtype == SA_BF16) {
-    // work items: the step's visible tokens spread over about two
-    // workgroups per compute unit; the plan itself is made on the device
+    // work items: the step's visible tokens spread over one item per
+    // workgroup slot (two per compute unit, one for 8-head groups, whose
+    // workgroups use a whole unit's registers); the plan itself is made on
+    // the device
     const int groups = p->batch * p->n_kv_heads;
-    target_items = std::max(64, 2 * compute_units() - groups);
+    target_items = (G > 4 ? 1 : 2) * compute_units();
     max_splits = target_items + groups;        // bound on the item count
     if (max_splits > kMaxDecodeItems) return SA_ERR_UNSUPPORTED;
     n_partial = (size_t)max_splits * G * (p->head_dim + 2);

@@ -9,12 +9,15 @@
 //   o_h = sum_{j in T_g} softmax_j(q_h . k_j / sqrt(d)) v_j .
 //
 // Work plan: the visible tokens of all (sequence, KV group) pairs are cut into
-// items of `chunk` consecutive list entries, with chunk = total / target
-// (rounded up to 64), so that the items of the whole step - however the
-// selected counts are distributed - fill the chip about once.  Every
-// workgroup derives the same plan from the counts (a block reduction and a
-// scan over the groups, no extra launch) and takes item blockIdx.x; the
-// combine launch re-derives it to find each head's items.
+// items of about `chunk` list entries, with chunk searched so that the items
+// of the whole step - however the selected counts are distributed - give
+// every workgroup slot of the launch one item.  Every wave derives the same
+// plan from the counts (wave reductions, no LDS, no extra launch); workgroup
+// b takes item b, and its four waves take the group's 16-token tiles in turn
+// with the waves of the group's other items (wave q of W takes tiles q,
+// q + W, ...), so that all waves of a group carry the same number of tiles
+// and stream through the list together.  Workgroup 0 records each group's
+// items for the combine launch.
 //
 // Layout per wave, one 16-token tile at a time:
 //   * lane l gathers token (l % 16): at k-step s the four lanes of a token
@@ -74,42 +77,100 @@ __device__ __forceinline__ int group_count(const DecodeArgs& a, int bg) {
   return min(max(a.sel_count[bg], 0), a.n);
 }
 
-// The item size: all visible tokens over target_items items, rounded up to
-// 64 entries, at least min_chunk.  Identical in every workgroup.
-__device__ int plan_chunk(const DecodeArgs& a, int64_t* s_scan) {
-  int64_t t = 0;
-  for (int bg = threadIdx.x; bg < a.B * a.Hkv; bg += kMfmaThreads) t += group_count(a, bg);
-  int64_t tot;
-  (void)block_exclusive_scan<int64_t, kMfmaThreads>(t, s_scan, &tot);
-  int64_t c = (tot + a.target_items - 1) / a.target_items;
-  c = (c + 63) / 64 * 64;
-  return (int)(c > a.min_chunk ? c : a.min_chunk);
+// Wave-wide sum of an int (DPP row reductions, then the four rows).
+__device__ __forceinline__ int wave_sum_i(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);   // row_ror 8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false);   // row_ror 4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x122, 0xF, 0xF, false);   // row_ror 2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x121, 0xF, 0xF, false);   // row_ror 1
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
 }
 
-// Number the items group by group (ceil(count / chunk) each).  Leaves in
-// s_out: [0] the group of item `item` (-1 when the plan has fewer items),
-// [1] its split within the group, [2] the first item of group `want`, [3]
-// that group's item count; with `table`, also writes (first item, item
-// count) of every group there.
-__device__ void plan_walk(const DecodeArgs& a, int chunk, int item, int want, int* s_scan,
-                          int* s_out, int2* table) {
-  if (threadIdx.x == 0) { s_out[0] = -1; s_out[1] = 0; s_out[2] = 0; s_out[3] = 0; }
-  __syncthreads();
+constexpr int kPlanPasses = 8;      // groups held in registers: 64 per pass
+
+// The work plan, made by every wave on its own (no LDS, no barrier): lane i
+// holds the visible-token counts of groups i, i + 64, ...; the item size is
+// the smallest multiple of 16 (at least min_chunk) for which the groups'
+// items (group_items each) number at most target_items, so that every
+// workgroup slot of the launch gets one item of about the same size.
+// Returns the group and split of item `item` (group -1: no such item) and
+// the group's item count; with `table`, also writes every group's (first
+// item, item count) there.
+struct PlanItem { int bg, split, chunk, ns; };
+
+// Items of a group with `count` visible tokens for item size c: the nearest
+// whole number of items (at least one), so that every item of every group
+// holds about c tokens (a group of 1.03 c is one item, not one plus a sliver).
+__device__ __forceinline__ int group_items(int count, int c) {
+  return count > 0 ? max(1, (count + c / 2) / c) : 0;
+}
+
+__device__ PlanItem plan_item(const DecodeArgs& a, int item, int2* table) {
+  const int lane = threadIdx.x & 63;
   const int ng = a.B * a.Hkv;
-  int carry = 0;
-  for (int base = 0; base < ng; base += kMfmaThreads) {
-    const int bg = base + threadIdx.x;
-    const int ns = (bg < ng) ? (group_count(a, bg) + chunk - 1) / chunk : 0;
-    int tot;
-    const int first = carry + block_exclusive_scan<int, kMfmaThreads>(ns, s_scan, &tot);
-    if (bg < ng) {
-      if (item >= first && item < first + ns) { s_out[0] = bg; s_out[1] = item - first; }
-      if (bg == want) { s_out[2] = first; s_out[3] = ns; }
-      if (table) table[bg] = make_int2(first, ns);
-    }
-    carry += tot;
+  const int passes = (ng + 63) / 64;
+  int cnt[kPlanPasses];
+  int64_t tot = 0;
+#pragma unroll
+  for (int p = 0; p < kPlanPasses; ++p) {
+    const int bg = p * 64 + lane;
+    cnt[p] = (p < passes && bg < ng) ? group_count(a, bg) : 0;
   }
-  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < kPlanPasses; ++p)
+    if (p < passes) tot += wave_sum_i(cnt[p]);
+  // items for a chunk size c (groups beyond the registers: one pass each)
+  auto items = [&](int c) __attribute__((always_inline)) -> int64_t {
+    int64_t n = 0;
+#pragma unroll
+    for (int p = 0; p < kPlanPasses; ++p)
+      if (p < passes) n += wave_sum_i(group_items(cnt[p], c));
+    for (int p = kPlanPasses; p < passes; ++p) {
+      const int bg = p * 64 + lane;
+      n += wave_sum_i(bg < ng ? group_items(group_count(a, bg), c) : 0);
+    }
+    return n;
+  };
+  const int64_t target = a.target_items;
+  auto up16 = [](int64_t x) -> int64_t { return (x + 15) / 16 * 16; };
+  int64_t lo = up16(max((int64_t)a.min_chunk, (tot + target - 1) / target));
+  int64_t hi = lo;
+  if (items((int)lo) > target) {
+    // at 2 n every non-empty group is one item: the fewest there can be
+    hi = up16(max((int64_t)a.min_chunk, 2 * (int64_t)a.n));
+    while (lo < hi) {                          // multiples of 16; items(hi) <= target
+      const int64_t mid = lo + (hi - lo) / 32 * 16;
+      if (items((int)mid) <= target) hi = mid; else lo = mid + 16;
+    }
+  }
+  const int chunk = (int)hi;
+  // number the items group by group and find `item`
+  PlanItem r{-1, 0, chunk, 0};
+  int carry = 0;
+  auto number = [&](int p, int c) __attribute__((always_inline)) {
+    const int bg = p * 64 + lane;
+    const int ns = (bg < ng) ? group_items(c, chunk) : 0;
+    const int incl = wave_inclusive_scan(ns);
+    const int first = carry + incl - ns;
+    if (table && bg < ng) table[bg] = make_int2(first, ns);
+    const uint64_t hit = __ballot(bg < ng && item >= first && item < first + ns);
+    if (hit) {
+      const int l = __ffsll((unsigned long long)hit) - 1;
+      r.bg = p * 64 + l;
+      r.split = item - __builtin_amdgcn_readlane(first, l);
+      r.ns = __builtin_amdgcn_readlane(ns, l);
+    }
+    carry += __builtin_amdgcn_readlane(incl, 63);
+  };
+#pragma unroll
+  for (int p = 0; p < kPlanPasses; ++p)
+    if (p < passes) number(p, cnt[p]);
+  for (int p = kPlanPasses; p < passes; ++p) {
+    const int bg = p * 64 + lane;
+    number(p, bg < ng ? group_count(a, bg) : 0);
+  }
+  return r;
 }
 
 template <int D>
@@ -124,9 +185,6 @@ struct Tile {
 
 template <int D, int G>
 struct DecodeShared {
-  int64_t scan64[kMfmaThreads / 64];
-  int scan32[kMfmaThreads / 64];
-  int plan[4];
   float p[4][16][8];                           // per wave: p[token][head]
   float m[4][8], l[4][8];
   float acc[4][8][D];
@@ -134,7 +192,7 @@ struct DecodeShared {
 
 template <int D, int G, bool LOCAL>
 __device__ __forceinline__ void decode_item(const DecodeArgs& a, DecodeShared<D, G>& sh, int item,
-                                            int bg, int split, int chunk) {
+                                            int bg, int split, int nsg) {
   using TL = Tile<D>;
   constexpr int KS = TL::KS, NCLS = TL::NCLS, VT = TL::VT;
   static_assert(G <= 8, "at most 8 query heads per KV group");
@@ -149,8 +207,6 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, DecodeShared<D,
   } else {
     count = min(max(a.sel_count[bg], 0), n);
   }
-  const int start = split * chunk;
-  const int len = min(chunk, count - start);
   const int64_t row0 = (int64_t)bg * a.n_cap;
 
   // query fragment: head (lane % 16), this lane's slice of the k mapping
@@ -170,9 +226,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, DecodeShared<D,
   }
 
   // this wave's contiguous share of the item, in whole 16-token tiles
-  const int per_wave = (((len + 3) / 4) + 15) & ~15;
-  const int w0 = start + wid * per_wave, w1 = min(start + len, w0 + per_wave);
-  const int ntiles = (w1 > w0) ? (w1 - w0 + 15) / 16 : 0;
+  // the group's waves take its tiles in turn (tile q, q + W, ...)
+  const int Wg = 4 * nsg, qw = 4 * split + wid;
+  const int Tg = (count + 15) / 16;
+  const int ntiles = (Tg > qw) ? (Tg - qw + Wg - 1) / Wg : 0;
 
   const int kt = lane & 15, jg = lane >> 4;            // K role
   const int vd = 2 * (lane % (D / 2)), vc = lane / (D / 2);   // V role
@@ -183,14 +240,14 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, DecodeShared<D,
   // raw list entry of this lane's token in a tile (a load for listed groups,
   // in bounds even past the end; checked when it is used)
   auto raw_id = [&](int tile) __attribute__((always_inline)) -> int {
-    const int e = w0 + tile * 16 + kt;
+    const int e = (qw + tile * Wg) * 16 + kt;
     if (LOCAL) return (e < s_eff) ? e : wst + (e - s_eff);
-    return a.sel_idx[row0 + min(e, w1 - 1)];
+    return a.sel_idx[row0 + min(e, count - 1)];
   };
   // issue a tile's K and V loads
   auto issue = [&](int tile, TL& t, int raw) __attribute__((always_inline)) {
-    const int e = w0 + tile * 16 + kt;
-    const int tok = (e < w1 && (unsigned)raw < (unsigned)n) ? raw : -1;
+    const int e = (qw + tile * Wg) * 16 + kt;
+    const int tok = (e < count && (unsigned)raw < (unsigned)n) ? raw : -1;
     t.tok = tok;
     const uint16_t* kp = kbase + (int64_t)max(tok, 0) * D;
 #pragma unroll
@@ -338,13 +395,13 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, DecodeShared<D,
 template <int D, int G>
 __global__ __launch_bounds__(kMfmaThreads, (G > 4 ? 1 : 2)) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ DecodeShared<D, G> sh;
-  const int chunk = plan_chunk(a, sh.scan64);
-  // workgroup 0 also records every group's items for the combine launch
-  plan_walk(a, chunk, blockIdx.x, -1, sh.scan32, sh.plan, blockIdx.x == 0 ? a.plan : nullptr);
-  const int bg = sh.plan[0], split = sh.plan[1];
+  // every wave makes the same plan; wave 0 of workgroup 0 also records every
+  // group's items for the combine launch
+  const PlanItem pl = plan_item(a, blockIdx.x, (blockIdx.x == 0 && threadIdx.x < 64) ? a.plan : nullptr);
+  const int bg = pl.bg, split = pl.split, nsg = pl.ns;
   if (bg < 0) return;
-  if ((a.local_mask >> (bg % a.Hkv)) & 1ull) decode_item<D, G, true>(a, sh, blockIdx.x, bg, split, chunk);
-  else decode_item<D, G, false>(a, sh, blockIdx.x, bg, split, chunk);
+  if ((a.local_mask >> (bg % a.Hkv)) & 1ull) decode_item<D, G, true>(a, sh, blockIdx.x, bg, split, nsg);
+  else decode_item<D, G, false>(a, sh, blockIdx.x, bg, split, nsg);
 }
 
 // Merge the items of one (sequence, query head).  Thread (e, part) owns
