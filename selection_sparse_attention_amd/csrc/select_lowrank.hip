@@ -12,7 +12,7 @@
 // histogram-based threshold): logits are mapped to order-preserving 32-bit
 // keys and resolved by three radix levels (12 + 12 + 8 bits).
 //
-//   scan (tiles x rows)  logits to the workspace (4 B/token) + level-1
+//   scan (2K-token tiles x rows)  logits to the workspace (4 B/token) + level-1
 //                        histogram of counts and fp64 masses, merged into the
 //                        row's histogram with atomics
 //   row  (rows)          one 1024-thread workgroup per row: the level-1 cut
@@ -36,9 +36,11 @@
 
 namespace sa {
 
-constexpr int kTile = 1024;        // tokens per workgroup
+constexpr int kTile = 1024;        // tokens per compaction workgroup
+constexpr int kScanTile = 2048;    // tokens per scan workgroup (two compaction tiles)
 constexpr int kThreads = 256;
 constexpr int kPer = kTile / kThreads;
+constexpr int kScanPer = kScanTile / kThreads;
 constexpr int kSpinLimit = 1 << 24;
 
 enum : int { CRIT_MASS = 1, CRIT_COUNT = 2 };
@@ -114,13 +116,15 @@ __global__ __launch_bounds__(kThreads) void select_scan_kernel(SelectArgs a) {
   // the tile's index rows first (tokens past the end re-read the last one),
   // so their latency overlaps everything up to the first use
   const int64_t krow = ((int64_t)b * a.Hkv + g) * a.n_cap;
-  IdxRow<T> kr[kPer];
+  IdxRow<T> kr[kScanPer];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) kr[i].load(a.k_idx, krow + min(tile * kTile + i * kThreads + tid, a.n - 1));
+  for (int i = 0; i < kScanPer; ++i)
+    kr[i].load(a.k_idx, krow + min(tile * kScanTile + i * kThreads + tid, a.n - 1));
 
   for (int i = tid; i < 4096; i += kThreads) { lc[i] = 0; if (MASS) lw[i] = 0.0; }
   // the compaction's look-back words of this call start empty
-  if (tid == 0) a.lookback[(int64_t)row * a.tiles + tile] = 0;
+  if (tid < kScanTile / kTile && tile * (kScanTile / kTile) + tid < a.tiles)
+    a.lookback[(int64_t)row * a.tiles + tile * (kScanTile / kTile) + tid] = 0;
 
   // qbar: mean of the group's index queries (exact for power-of-two G on
   // lattice inputs)
@@ -140,8 +144,8 @@ __global__ __launch_bounds__(kThreads) void select_scan_kernel(SelectArgs a) {
   float* lg = a.logits + (int64_t)row * a.row_stride;
   uint32_t kmax = 0;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int j = tile * kTile + i * kThreads + tid;
+  for (int i = 0; i < kScanPer; ++i) {
+    const int j = tile * kScanTile + i * kThreads + tid;
     if (j < a.n) {
       float l = kr[i].dot(qb) * 0.25f;
       if (l == 0.f) l = 0.f;                       // fold -0 into +0
@@ -723,7 +727,7 @@ hipError_t launch_select_lowrank(const SelectArgs& a, int dtype, hipStream_t s) 
   const int rows = a.B * a.groups.n;
   if (rows == 0) return hipSuccess;
   if (!a.select_all) {
-    dim3 grid(a.tiles, rows);
+    dim3 grid((a.n + kScanTile - 1) / kScanTile, rows);
     if (dtype == 0) {
       if (a.use_mass) hipLaunchKernelGGL((select_scan_kernel<bf16_t, true>), grid, dim3(kThreads), 0, s, a);
       else hipLaunchKernelGGL((select_scan_kernel<bf16_t, false>), grid, dim3(kThreads), 0, s, a);
