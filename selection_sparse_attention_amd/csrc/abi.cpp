@@ -266,13 +266,27 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
     PyrGeom pg;
     if ((st = pyramid_geom(p, &pg))) return st;
     if (p->q_block < 1 || p->q_block % pg.top_span || p->block_top_k < 1) return SA_ERR_INVALID_ARG;
+    // intervals of S blocks whose candidates (about K + S x the entries one
+    // block adds) fit the kPsCap slots; none when K leaves too little room
+    int64_t per_block = 0;
+    for (int l = 0, w = 1; l < p->levels; ++l, w *= p->factor) per_block += p->q_block / w;
+    const int64_t room = (int64_t)sa::kPsCap - p->block_top_k - 512;
+    const int S = (per_block > 0 && room > 0) ? (int)std::min<int64_t>(room / per_block, 64) : 0;
+    const int n_int = (S >= 2) ? (pg.nblk + S - 1) / S : 0;
+    const size_t bh = (size_t)p->batch * p->n_q_heads;
     Carver c(ws);
-    uint2* prefix = c.take<uint2>((size_t)p->batch * p->n_q_heads);
+    uint2* prefix = c.take<uint2>(bh);
+    uint32_t* tau = c.take<uint32_t>(bh * n_int);
+    int32_t* cand_len = c.take<int32_t>(bh * n_int);
+    uint2* cand = c.take<uint2>(bh * n_int * sa::kPsCap);
     const size_t need = c.size();
     if ((st = workspace_gate(ws, ws_bytes, need))) return st < 0 ? st : SA_OK;
     if (!b->pyr_scores || !b->blk_idx || !b->blk_count) return SA_ERR_INVALID_ARG;
     sa::PyrSelectArgs a{};
     a.prefix = prefix;
+    a.S = n_int > 0 ? S : 0;
+    a.n_int = n_int;
+    a.tau = tau; a.cand_len = cand_len; a.cand = cand;
     a.scores = b->pyr_scores; a.blk_idx = b->blk_idx; a.blk_count = b->blk_count;
     a.B = p->batch; a.H = p->n_q_heads; a.N = p->n_ctx; a.levels = p->levels; a.factor = p->factor;
     a.q_block = p->q_block; a.K = p->block_top_k; a.nblk = pg.nblk; a.Nt = pg.Nt;

@@ -107,7 +107,14 @@ struct PyrSelectArgs {
   int32_t len[8];        // entries of each level
   int64_t soff[8];       // flat id of each level's first entry
   uint2* prefix;         // workspace [B*H]: (AND, OR) of the head's score keys
+  // intervals of S consecutive blocks (n_int per head; 0 = not used)
+  int32_t S, n_int;
+  uint32_t* tau;         // [B*H, n_int]: cut key of the interval's first block
+  int32_t* cand_len;     // [B*H, n_int]: candidates kept (-1: more than kPsCap)
+  uint2* cand;           // [B*H, n_int, kPsCap]: (key, flat id), ascending flat id
 };
+
+constexpr int kPsCap = 7680;   // candidate slots per interval (and LDS entries per block)
 
 // ---------------------------------------------------------------- attention
 struct DecodeArgs {

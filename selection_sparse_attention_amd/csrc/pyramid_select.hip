@@ -9,13 +9,23 @@
 // lower index - which is the order of the flat entry ids off_l + j.  When at
 // most K entries are visible, all are kept.
 //
-// One 256-thread workgroup per (block, sequence-head).  The K-th largest score
-// key is resolved by radix levels of up to 12 bits over LDS histograms of the
-// visible prefixes, with no sort; the digits start below the leading bits all
-// keys of the head share (an AND/OR reduction over the head, one small launch
-// first), so the buckets are well spread.  A final pass writes the kept flat
-// ids in ascending order (strictly larger keys, then the first ties by flat
-// id).
+// The K-th largest score key (the cut) is resolved by radix levels of up to
+// 12 bits over LDS histograms, with no sort; the digits start below the
+// leading bits all keys of the head share (an AND/OR reduction over the head,
+// one small launch first), so the buckets are well spread.  The kept flat ids
+// are written in ascending order (strictly larger keys, then the first ties by
+// flat id).
+//
+// Visibility only grows with the block index, so the cut never decreases
+// along a head's blocks.  Blocks are grouped into intervals of S: one
+// workgroup per interval resolves the cut of the interval's first block over
+// its visible prefixes - a lower bound of every later block's cut - and
+// stores, in ascending flat id, the entries the interval's last block sees
+// whose key reaches that bound (the kept entries of every block in the
+// interval are among them; about K + S x (entries a block adds)).  Each block
+// then selects from its visible candidates in LDS instead of passing over all
+// its visible scores.  An interval with more than kPsCap candidates (many
+// equal scores) leaves its blocks to the full passes.
 #include "args.hpp"
 #include "common.hpp"
 
@@ -139,12 +149,156 @@ __device__ int vis_find(const uint32_t* hist, int64_t target, int64_t* above, in
   return b;
 }
 
+struct PsShared {
+  uint32_t hist[4096];
+  int64_t scan[kPsThreads / 64];
+  uint32_t scan32[kPsThreads / 64];
+  int b;
+  int64_t above;
+  uint32_t kand[kPsThreads / 64], kor[kPsThreads / 64];
+};
+
+// The cut over the visible prefixes v of one head: the key of the K-th
+// largest visible score; *above receives how many visible keys exceed it.
+__device__ uint32_t visible_cut(const PyrSelectArgs& a, const VisRanges& v, const float* sc, int bh,
+                                PsShared& sh, int64_t* above_out) {
+  const uint2 pf = a.prefix[bh];
+  const uint32_t diff = pf.x ^ pf.y;
+  const int common = diff ? __clz(diff) : 32;
+  int64_t above = 0;
+  uint32_t cut = pf.x;                              // when every key is equal
+  if (common < 32) {
+    int pos = 32 - common;                          // bits still to resolve
+    uint32_t prefix = pf.x >> pos;
+    while (pos > 0) {                               // digits of at most 12 bits
+      const int bits = pos < 12 ? pos : 12;
+      const int shift = pos - bits;
+      for (int i = threadIdx.x; i < 4096; i += kPsThreads) sh.hist[i] = 0;
+      __syncthreads();
+      vis_hist(sc, v, prefix, pos, shift, bits, sh.hist);
+      __syncthreads();
+      const int bk = vis_find<4096>(sh.hist, a.K, &above, sh.scan, &sh.b, &sh.above);
+      prefix = (prefix << bits) | (uint32_t)bk;
+      pos = shift;
+    }
+    cut = prefix;
+  }
+  *above_out = above;
+  return cut;
+}
+
+// Ordered compaction over n entries produced by get(i) -> (key, id): the
+// entries with keep(key) go to emit(slot, key, id) with slots in entry order.
+// Thread t takes kPsU consecutive entries of every chunk.  Returns the count.
+template <typename Get, typename Keep, typename Emit>
+__device__ uint32_t ordered_compact(int n, Get get, Keep keep, Emit emit, uint32_t* s_scan32) {
+  uint32_t run = 0;
+  for (int j0 = 0; j0 < n; j0 += kPsU * kPsThreads) {
+    const int jt = j0 + kPsU * threadIdx.x;
+    uint32_t key[kPsU];
+    int32_t id[kPsU];
+#pragma unroll
+    for (int u = 0; u < kPsU; ++u) get(min(jt + u, n - 1), key[u], id[u]);
+    uint32_t f = 0;
+#pragma unroll
+    for (int u = 0; u < kPsU; ++u)
+      if (jt + u < n && keep(key[u], id[u])) f |= 1u << u;
+    uint32_t tot;
+    uint32_t o = run + block_exclusive_scan<uint32_t, kPsThreads>(__popc(f), s_scan32, &tot);
+#pragma unroll
+    for (int u = 0; u < kPsU; ++u)
+      if (f & (1u << u)) emit(o++, key[u], id[u]);
+    run += tot;
+  }
+  return run;
+}
+
+// One workgroup per (interval, sequence-head): the cut of the interval's first
+// block, then the candidates of the interval (entries its last block sees with
+// a key at least that cut).
+__global__ __launch_bounds__(kPsThreads) void pyr_interval_kernel(PyrSelectArgs a) {
+  __shared__ PsShared sh;
+  const int iv = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int b0 = iv * a.S, b1 = min(b0 + a.S, a.nblk) - 1;
+  const int64_t slot = (int64_t)bh * a.n_int + iv;
+  const VisRanges v1 = visible(a, b1);
+  if (v1.total <= a.K) {                    // every block of the interval keeps all it sees
+    if (tid == 0) { a.tau[slot] = 0; a.cand_len[slot] = 0; }
+    return;
+  }
+  const float* sc = a.scores + (int64_t)bh * a.Nt;
+  const VisRanges v0 = visible(a, b0);
+  uint32_t tau = 0;
+  if (v0.total > a.K) {
+    int64_t above;
+    tau = visible_cut(a, v0, sc, bh, sh, &above);
+  }
+  uint2* out = a.cand + slot * kPsCap;
+  uint32_t total = 0;
+  for (int l = 0; l < v1.nl; ++l) {
+    const float* p = sc + v1.off[l];
+    const int base = (int)v1.off[l];
+    const uint32_t room = total < (uint32_t)kPsCap ? (uint32_t)kPsCap - total : 0u;
+    uint2* o = out + min(total, (uint32_t)kPsCap);
+    total += ordered_compact(
+        v1.cnt[l],
+        [&](int j, uint32_t& key, int32_t& id) { key = order_key(p[j]); id = base + j; },
+        [&](uint32_t key, int32_t) { return key >= tau; },
+        [&](uint32_t k, uint32_t key, int32_t id) { if (k < room) o[k] = make_uint2(key, (uint32_t)id); },
+        sh.scan32);
+  }
+  if (tid == 0) {
+    a.tau[slot] = tau;
+    a.cand_len[slot] = total <= (uint32_t)kPsCap ? (int32_t)total : -1;
+  }
+}
+
+// The cut over n keys held in LDS, as visible_cut does over global prefixes.
+__device__ uint32_t lds_cut(const uint32_t* keys, int n, int64_t K, PsShared& sh, int64_t* above_out) {
+  const int tid = threadIdx.x;
+  uint32_t kand = 0xFFFFFFFFu, kor = 0u;
+  for (int i = tid; i < n; i += kPsThreads) { kand &= keys[i]; kor |= keys[i]; }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    kand &= (uint32_t)__shfl_xor((int)kand, m);
+    kor |= (uint32_t)__shfl_xor((int)kor, m);
+  }
+  if ((tid & 63) == 0) { sh.kand[tid >> 6] = kand; sh.kor[tid >> 6] = kor; }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kPsThreads / 64; ++w) { kand &= sh.kand[w]; kor |= sh.kor[w]; }
+  const uint32_t diff = kand ^ kor;
+  const int common = diff ? __clz(diff) : 32;
+  int64_t above = 0;
+  uint32_t cut = kand;
+  if (common < 32) {
+    int pos = 32 - common;
+    uint32_t prefix = kand >> pos;
+    while (pos > 0) {
+      const int bits = pos < 12 ? pos : 12;
+      const int shift = pos - bits;
+      const uint32_t mask = (1u << bits) - 1u;
+      for (int i = tid; i < 4096; i += kPsThreads) sh.hist[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < n; i += kPsThreads) {
+        const uint32_t key = keys[i];
+        if ((key >> pos) == prefix) atomicAdd(&sh.hist[(key >> shift) & mask], 1u);
+      }
+      __syncthreads();
+      const int bk = vis_find<4096>(sh.hist, K, &above, sh.scan, &sh.b, &sh.above);
+      prefix = (prefix << bits) | (uint32_t)bk;
+      pos = shift;
+    }
+    cut = prefix;
+  }
+  *above_out = above;
+  return cut;
+}
+
 __global__ __launch_bounds__(kPsThreads) void pyr_select_kernel(PyrSelectArgs a) {
-  __shared__ uint32_t hist[4096];
-  __shared__ int64_t s_scan[kPsThreads / 64];
-  __shared__ uint32_t s_scan32[kPsThreads / 64];
-  __shared__ int s_b;
-  __shared__ int64_t s_above;
+  __shared__ PsShared sh;
+  __shared__ uint32_t c_key[kPsCap];
+  __shared__ int32_t c_id[kPsCap];
   // late blocks see the most entries: dispatch them first
   const int blk = a.nblk - 1 - (int)blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const VisRanges v = visible(a, blk);
@@ -160,31 +314,62 @@ __global__ __launch_bounds__(kPsThreads) void pyr_select_kernel(PyrSelectArgs a)
     if (tid == 0) a.blk_count[(int64_t)bh * a.nblk + blk] = (int32_t)v.total;
     return;
   }
-  // The leading bits every key of the head shares carry no information: the
-  // radix digits start below them (scores share sign and most exponent bits,
-  // so a histogram of the top bits would pile everything into a few buckets).
-  const uint2 pf = a.prefix[bh];
-  const uint32_t diff = pf.x ^ pf.y;
-  const int common = diff ? __clz(diff) : 32;
-  int64_t above = 0;
-  uint32_t cut = pf.x;                              // when every key is equal
-  if (common < 32) {
-    int pos = 32 - common;                          // bits still to resolve
-    uint32_t prefix = pf.x >> pos;
-    // digits of at most 12 bits
-    while (pos > 0) {
-      const int bits = pos < 12 ? pos : 12;
-      const int shift = pos - bits;
-      for (int i = tid; i < 4096; i += kPsThreads) hist[i] = 0;
-      __syncthreads();
-      vis_hist(sc, v, prefix, pos, shift, bits, hist);
-      __syncthreads();
-      const int bk = vis_find<4096>(hist, K, &above, s_scan, &s_b, &s_above);
-      prefix = (prefix << bits) | (uint32_t)bk;
-      pos = shift;
+  const int64_t slot = (int64_t)bh * a.n_int + (a.S > 0 ? blk / a.S : 0);
+  const int ncand = (a.n_int > 0) ? a.cand_len[slot] : -1;
+  if (ncand >= 0) {
+    // the interval's candidates this block sees, in ascending flat id
+    const uint2* cp = a.cand + slot * kPsCap;
+    const int m = (int)ordered_compact(
+        ncand,
+        [&](int i, uint32_t& key, int32_t& id) { const uint2 e = cp[i]; key = e.x; id = (int32_t)e.y; },
+        [&](uint32_t, int32_t id) {
+          bool vis = false;
+#pragma unroll
+          for (int l = 0; l < 8; ++l)
+            if (l < v.nl && id >= v.off[l] && id < v.off[l] + a.len[l]) vis = (id - v.off[l]) < v.cnt[l];
+          return vis;
+        },
+        [&](uint32_t k, uint32_t key, int32_t id) { c_key[k] = key; c_id[k] = id; },
+        sh.scan32);
+    __syncthreads();
+    int64_t above;
+    const uint32_t cut = lds_cut(c_key, m, K, sh, &above);
+    const uint32_t need = (uint32_t)(K - above);    // ties kept, lowest flat ids first
+    uint32_t s_run = 0, t_run = 0;
+    for (int j0 = 0; j0 < m; j0 += kPsU * kPsThreads) {
+      const int jt = j0 + kPsU * tid;
+      uint32_t sf = 0, tf = 0;
+#pragma unroll
+      for (int u = 0; u < kPsU; ++u) {
+        if (jt + u < m) {
+          const uint32_t key = c_key[jt + u];
+          if (key > cut) sf |= 1u << u;
+          else if (key == cut) tf |= 1u << u;
+        }
+      }
+      uint32_t tot_s, tot_t;
+      const uint32_t ex_s = block_exclusive_scan<uint32_t, kPsThreads>(__popc(sf), sh.scan32, &tot_s);
+      const uint32_t ex_t = block_exclusive_scan<uint32_t, kPsThreads>(__popc(tf), sh.scan32, &tot_t);
+      uint32_t sb = s_run + ex_s, tb = t_run + ex_t;
+#pragma unroll
+      for (int u = 0; u < kPsU; ++u) {
+        if (sf & (1u << u)) {
+          out[sb + (tb < need ? tb : need)] = c_id[jt + u];
+          ++sb;
+        } else if (tf & (1u << u)) {
+          if (tb < need) out[sb + tb] = c_id[jt + u];
+          ++tb;
+        }
+      }
+      s_run += tot_s;
+      t_run += tot_t;
     }
-    cut = prefix;
+    if (tid == 0) a.blk_count[(int64_t)bh * a.nblk + blk] = (int32_t)K;
+    return;
   }
+  // full passes over the visible scores
+  int64_t above;
+  const uint32_t cut = visible_cut(a, v, sc, bh, sh, &above);
   const uint32_t need = (uint32_t)(K - above);        // ties kept, lowest flat ids first
 
   // ascending flat ids: strict (key > cut) and the first `need` ties; thread
@@ -208,8 +393,8 @@ __global__ __launch_bounds__(kPsThreads) void pyr_select_kernel(PyrSelectArgs a)
         }
       }
       uint32_t tot_s, tot_t;
-      const uint32_t ex_s = block_exclusive_scan<uint32_t, kPsThreads>(__popc(sf), s_scan32, &tot_s);
-      const uint32_t ex_t = block_exclusive_scan<uint32_t, kPsThreads>(__popc(tf), s_scan32, &tot_t);
+      const uint32_t ex_s = block_exclusive_scan<uint32_t, kPsThreads>(__popc(sf), sh.scan32, &tot_s);
+      const uint32_t ex_t = block_exclusive_scan<uint32_t, kPsThreads>(__popc(tf), sh.scan32, &tot_t);
       uint32_t sb = s_run + ex_s, tb = t_run + ex_t;
 #pragma unroll
       for (int u = 0; u < kPsU; ++u) {
@@ -231,6 +416,10 @@ __global__ __launch_bounds__(kPsThreads) void pyr_select_kernel(PyrSelectArgs a)
 hipError_t launch_pyramid_select(const PyrSelectArgs& a, hipStream_t s) {
   if (!a.prefix) return hipErrorInvalidValue;
   hipLaunchKernelGGL(pyr_prefix_kernel, dim3(a.B * a.H), dim3(1024), 0, s, a);
+  if (a.n_int > 0) {
+    if (a.S < 1 || !a.tau || !a.cand_len || !a.cand) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pyr_interval_kernel, dim3(a.n_int, a.B * a.H), dim3(kPsThreads), 0, s, a);
+  }
   dim3 grid(a.nblk, a.B * a.H);
   hipLaunchKernelGGL(pyr_select_kernel, grid, dim3(kPsThreads), 0, s, a);
   return hipGetLastError();

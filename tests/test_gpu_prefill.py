@@ -84,6 +84,7 @@ SELECT_CASES = [
     SMALL.with_(block_top_k=5000),                       # every visible entry
     SMALL.with_(n_ctx=2048 + 16 * 9, block_top_k=500),   # ragged last block
     SMALL.with_(levels=2, factor=2, n_ctx=1024, block_top_k=100),
+    SMALL.with_(n_ctx=8192, block_top_k=300),           # intervals past the first: bound > 0
 ]
 
 
@@ -213,3 +214,28 @@ def test_prefill_full_size_sampled():
         t = {k: run.t[k][:, heads] for k in ("out", "blk_idx", "blk_count")}
     worst = _check_prefill(sub, Sub, ni, {(0, i): blocks for i in range(2)})
     assert worst <= BF16_TOL
+
+
+def test_block_select_all_equal_scores():
+    """Every score equal (zero queries and keys): every visible entry ties, so
+    the later intervals hold more candidates than fit and their blocks take
+    the full passes; the kept entries are the lowest flat ids."""
+    cfg = SMALL.with_(n_ctx=8192, block_top_k=300)
+    inp = workloads.prefill_inputs(cfg, 3)
+    inp["q"] = torch.zeros_like(inp["q"])
+    inp["k"] = torch.zeros_like(inp["k"])
+    run = PrefillRun(cfg, inp)
+    run.pyramid()
+    run.select()
+    torch.cuda.synchronize()
+    idx = run.t["blk_idx"].cpu().numpy()
+    cnt = run.t["blk_count"].cpu().numpy()
+    ni = _np(inp)
+    for h in range(cfg.n_heads):
+        sc = oracle.pyramid_scores(ni["q"][0, h], ni["k"][0, h], cfg.levels, cfg.factor)
+        for blk in range(run.nblk):
+            ref = oracle.block_select(sc, blk, cfg.n_ctx, cfg.levels, cfg.factor, cfg.q_block,
+                                      cfg.block_top_k)
+            c = cnt[0, h, blk]
+            assert c == len(ref), (h, blk, c, len(ref))
+            assert np.array_equal(idx[0, h, blk, :c], np.sort(ref)), (h, blk)
