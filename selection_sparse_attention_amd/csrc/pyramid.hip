@@ -9,8 +9,9 @@
 // a coarse entry inherits the largest score among the entries it covers.
 //
 // One workgroup (d threads, one per dim) per span of p^(L-1) level-0 rows of
-// one (sequence, head): it streams the span once, emits every coarse entry of
-// every level inside it, and the span's scores.
+// one (sequence, head): it streams the span once, 16 rows' loads in flight at
+// a time, emits every coarse entry of every level inside it, and the span's
+// scores.
 #include "args.hpp"
 #include "common.hpp"
 
@@ -29,26 +30,46 @@ __global__ __launch_bounds__(D) void pyramid_kernel(PyramidArgs a) {
   double aq[8], ak[8], av[8];
 #pragma unroll
   for (int l = 0; l < 8; ++l) { aq[l] = 0.0; ak[l] = 0.0; av[l] = 0.0; }
-  for (int r = 0; r < P; ++r) {
-    const float xq = Elem<T>::load(a.q, (base + r) * D + e);
-    const float xk = Elem<T>::load(a.k, (base + r) * D + e);
-    const float xv = Elem<T>::load(a.v, (base + r) * D + e);
-    const float sq = wave_sum(xq * xq + xk * xk);
-    if (lane == 0) s_part[wid][r] = sq;
-    int width = 1;
+  // rows in batches of kRows: every load of a batch is issued before any is
+  // used (rows past the span re-read its last row and are skipped)
+  constexpr int kRows = 16;
+  for (int rb = 0; rb < P; rb += kRows) {
+    float xq[kRows], xk[kRows], xv[kRows];
 #pragma unroll
-    for (int l = 1; l < 8; ++l) {
-      if (l >= a.levels) break;
-      width *= a.factor;
-      aq[l] += xq; ak[l] += xk; av[l] += xv;
-      if ((r + 1) % width == 0) {
-        const int64_t j = (r0 + r + 1) / width - 1;     // entry index inside level l
-        const int64_t row = (int64_t)bh * a.Nc + a.coff[l] + j;
-        const double inv = 1.0 / (double)width;
-        Elem<T>::store_d(a.pq, row * D + e, aq[l] * inv);
-        Elem<T>::store_d(a.pk, row * D + e, ak[l] * inv);
-        Elem<T>::store_d(a.pv, row * D + e, av[l] * inv);
-        aq[l] = 0.0; ak[l] = 0.0; av[l] = 0.0;
+    for (int u = 0; u < kRows; ++u) {
+      const int64_t r = base + min(rb + u, P - 1);
+      xq[u] = Elem<T>::load(a.q, r * D + e);
+      xk[u] = Elem<T>::load(a.k, r * D + e);
+      xv[u] = Elem<T>::load(a.v, r * D + e);
+    }
+    float sq[kRows];
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) sq[u] = xq[u] * xq[u] + xk[u] * xk[u];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+#pragma unroll
+      for (int u = 0; u < kRows; ++u) sq[u] += __shfl_xor(sq[u], m);
+    }
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+      const int r = rb + u;
+      if (r >= P) break;
+      if (lane == 0) s_part[wid][r] = sq[u];
+      int width = 1;
+#pragma unroll
+      for (int l = 1; l < 8; ++l) {
+        if (l >= a.levels) break;
+        width *= a.factor;
+        aq[l] += xq[u]; ak[l] += xk[u]; av[l] += xv[u];
+        if ((r + 1) % width == 0) {
+          const int64_t j = (r0 + r + 1) / width - 1;     // entry index inside level l
+          const int64_t row = (int64_t)bh * a.Nc + a.coff[l] + j;
+          const double inv = 1.0 / (double)width;
+          Elem<T>::store_d(a.pq, row * D + e, aq[l] * inv);
+          Elem<T>::store_d(a.pk, row * D + e, ak[l] * inv);
+          Elem<T>::store_d(a.pv, row * D + e, av[l] * inv);
+          aq[l] = 0.0; ak[l] = 0.0; av[l] = 0.0;
+        }
       }
     }
   }
