@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   //      level-0 row 0 - never dereferenced out of bounds; its contribution
   //      is unspecified.
   {
-    const int n_stage = (ntiles + 2) * kKT;
+    const int n_stage = (ntiles + 3) * kKT;
     for (int e = tid; e < n_stage; e += kPfThreads) {
       uint32_t r = 0u;
       if (e < c_sel) {
@@ -136,23 +136,29 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     const uint16_t* base = (r & kCoarse) ? bc : b0;
     return base + (size_t)(r & ~kCoarse) * kD;
   };
-  struct Rows { u32x4p k0, k1, v0, v1; };         // one tile's loads for this thread
-  // issue the loads of one tile (unconditionally: past the end they read
-  // row 0, which is never used)
-  auto gather = [&](int tile, Rows& r) __attribute__((always_inline)) {
-    const int e0 = tile * kKT;
-    const uint32_t lk = s_seq[e0 + gk_key];
-    const uint2 lv = *reinterpret_cast<const uint2*>(&s_seq[e0 + 2 * gv_kp]);
+  // one set of loads for this thread: the K rows of tile x + 1 and the V rows
+  // of tile x (K runs a tile ahead: its product is issued a tile early)
+  struct Rows { u32x4p k0, k1, v0, v1; };
+  // issue set x (unconditionally: past the end the rows are row 0, never used)
+  auto gather = [&](int x, Rows& r) __attribute__((always_inline)) {
+    const uint32_t lk = s_seq[(x + 1) * kKT + gk_key];
+    const uint2 lv = *reinterpret_cast<const uint2*>(&s_seq[x * kKT + 2 * gv_kp]);
     const uint16_t* pk = row_ptr(lk, kb, pkb);
     r.k0 = *reinterpret_cast<const u32x4p*>(pk + 16 * gk_seg);
     r.k1 = *reinterpret_cast<const u32x4p*>(pk + 16 * gk_seg + 8);
     r.v0 = *reinterpret_cast<const u32x4p*>(row_ptr(lv.x, vb, pvb) + 8 * gv_seg);
     r.v1 = *reinterpret_cast<const u32x4p*>(row_ptr(lv.y, vb, pvb) + 8 * gv_seg);
   };
-  auto stash = [&](int buf, const Rows& r) __attribute__((always_inline)) {
+  auto stash_k = [&](int buf, const u32x4p& k0, const u32x4p& k1) __attribute__((always_inline)) {
     uint16_t* kdst = s_k[buf] + gk_key * kKRow + 16 * gk_seg;
-    *reinterpret_cast<u32x4p*>(kdst) = r.k0;
-    *reinterpret_cast<u32x4p*>(kdst + 8) = r.k1;
+    *reinterpret_cast<u32x4p*>(kdst) = k0;
+    *reinterpret_cast<u32x4p*>(kdst + 8) = k1;
+  };
+  // set x: K of tile x + 1 into K buffer (x + 1) & 1, V of tile x into V
+  // buffer x & 1
+  auto stash = [&](int x, const Rows& r) __attribute__((always_inline)) {
+    stash_k((x + 1) & 1, r.k0, r.k1);
+    const int buf = x & 1;
     // V^T: dims 8 gv_seg + i, keys 2 gv_kp and 2 gv_kp + 1 packed in one dword
     uint16_t* vdst = s_vt[buf] + (8 * gv_seg) * kVRow + 2 * gv_kp;
     auto put = [&](int i, uint32_t x0, uint32_t x1) __attribute__((always_inline)) {
@@ -174,16 +180,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     for (int nt = 0; nt < 2; ++nt) o[dt][nt] = (f32x4p){0.f, 0.f, 0.f, 0.f};
   const float sc = a.scale_log2;
 
-  // one tile of math: `mine` held this tile's rows and now takes those of
-  // tile + 2 (so a tile's rows have two tiles of math to arrive); `next`
-  // holds tile + 1, staged at the end
-  auto body = [&](const int tile, Rows& mine, const Rows& next) __attribute__((always_inline)) {
-    const int buf = tile & 1;
-    gather(tile + 2, mine);
-    const uint16_t* kt = s_k[buf];
-    const uint16_t* vt = s_vt[buf];
-    // S^T[key = 16 mt + 4 jg + i][q = 16 nt + l16]
-    f32x4p s[2][2];
+  // S^T[key = 16 mt + 4 jg + i][q = 16 nt + l16] of the tile in K buffer kbuf
+  auto qk = [&](int kbuf, f32x4p (&s)[2][2]) __attribute__((always_inline)) {
+    const uint16_t* kt = s_k[kbuf];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       bf16x8p kf[4];
@@ -199,6 +198,18 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
         s[mt][nt] = c;
       }
     }
+  };
+
+  // one tile of math.  The scores of tile + 1 are started first, so the
+  // matrix cores work on them while this tile's softmax runs on the vector
+  // units; then this tile's PV product.  `mine` held set `tile` (staged
+  // already) and now takes set tile + 2; `next` holds set tile + 1, staged at
+  // the end.
+  auto body = [&](const int tile, Rows& mine, const Rows& next, f32x4p (&s)[2][2],
+                  f32x4p (&sn)[2][2]) __attribute__((always_inline)) {
+    gather(tile + 2, mine);
+    if (tile + 1 < ntiles) qk((tile + 1) & 1, sn);
+    const uint16_t* vt = s_vt[tile & 1];
     // mask only on tiles that reach past the selection
     const int e0 = tile * kKT;
     if (e0 + kKT > c_sel) {
@@ -276,25 +287,34 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     }
     // unconditional (past the end it stages rows nobody reads), so that the
     // wait for this set's loads is the same on every path
-    stash(buf ^ 1, next);
+    stash(tile + 1, next);
     lds_barrier();
   };
 
-  // prologue: tiles 0 and 1 in flight, tile 0 staged
+  // prologue: K of tile 0 staged alone, sets 0 and 1 in flight, set 0 staged,
+  // the scores of tile 0 started
   lds_barrier();                                    // s_seq complete
+  {
+    const uint16_t* pk = row_ptr(s_seq[gk_key], kb, pkb);
+    const u32x4p k0 = *reinterpret_cast<const u32x4p*>(pk + 16 * gk_seg);
+    const u32x4p k1 = *reinterpret_cast<const u32x4p*>(pk + 16 * gk_seg + 8);
+    stash_k(0, k0, k1);
+  }
   Rows ra, rb;
   gather(0, ra);
   gather(1, rb);
   stash(0, ra);
   lds_barrier();
+  f32x4p sa_[2][2], sb_[2][2];
+  qk(0, sa_);
   // pairs of tiles, then an odd last one: every path back to the loop head
   // passes both bodies, so the loads in flight there are always set 1's
   int tile = 0;
   for (; tile + 1 < ntiles; tile += 2) {
-    body(tile, ra, rb);
-    body(tile + 1, rb, ra);
+    body(tile, ra, rb, sa_, sb_);
+    body(tile + 1, rb, ra, sb_, sa_);
   }
-  if (tile < ntiles) body(tile, ra, rb);
+  if (tile < ntiles) body(tile, ra, rb, sa_, sb_);
 
   // ---- normalise and write: lane holds d = 16 dt + 4 jg + 0..3 of query
   //      32w + 16 nt + l16
