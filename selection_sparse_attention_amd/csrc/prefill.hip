@@ -42,6 +42,7 @@ constexpr int kVRow = 36;               // V^T tile row stride (bf16 elements) =
 constexpr int kListMax = 8192;          // largest block_top_k the kernel stages in LDS
 constexpr int kSeqMax = kListMax + 128 + 4 * kKT;   // + own keys + tail the gathers run past
 constexpr uint32_t kCoarse = 0x80000000u;           // staged entry: coarse row flag
+constexpr float kLazy = 8.f;            // log2 headroom before the softmax reference moves
 
 typedef float f32x2p __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2p __attribute__((ext_vector_type(2)));
@@ -239,9 +240,13 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[mt][nt][i]);
       tmax = max_over_lane_groups(tmax);
-      const float mn = fmaxf(m[nt], tmax * sc);
+      // the reference moves only when the tile's max exceeds it by more than
+      // 2^8 (p stays <= 256, far from overflow), so the accumulators are
+      // rescaled rarely; the final normalisation divides the scale out
+      const float cand = tmax * sc;
+      const float mn = (cand > m[nt] + kLazy) ? cand : m[nt];
       const float msub = (mn == -INFINITY) ? 0.f : mn;   // a fully masked row stays at p = 0
-      alpha[nt] = __builtin_amdgcn_exp2f(m[nt] - msub);
+      alpha[nt] = (mn == m[nt]) ? 1.f : __builtin_amdgcn_exp2f(m[nt] - msub);
       m[nt] = mn;
       float p[8];
 #pragma unroll
