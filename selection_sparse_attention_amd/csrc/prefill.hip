@@ -54,15 +54,11 @@ __device__ __forceinline__ uint32_t pk_bf16(float x, float y) {
 }
 
 // max over the four lanes l16 + 16 jg (jg = 0..3) that hold one query's
-// scores: a swap of the wave's halves, then of neighbouring 16-lane rows
-// (both VALU, no LDS round trip)
+// scores: exchanges across the wave's halves and across neighbouring 16-lane
+// rows
 __device__ __forceinline__ float max_over_lane_groups(float v) {
-  const auto h = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
-                                                  __builtin_bit_cast(uint32_t, v), false, false);
-  v = fmaxf(__builtin_bit_cast(float, h[0]), __builtin_bit_cast(float, h[1]));
-  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
-                                                  __builtin_bit_cast(uint32_t, v), false, false);
-  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return fmaxf(v, __shfl_xor(v, 16));
 }
 
 __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {

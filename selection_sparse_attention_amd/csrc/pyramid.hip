@@ -17,6 +17,18 @@
 
 namespace sa {
 
+// Sum over the 64 lanes of a wave: DPP rotations inside each 16-lane row,
+// then two cross-row exchanges.
+__device__ __forceinline__ float wave_sum_rows(float v) {
+  v += dpp_move<0x128, 0xF>(v);     // row_ror:8
+  v += dpp_move<0x124, 0xF>(v);     // row_ror:4
+  v += dpp_move<0x122, 0xF>(v);     // row_ror:2
+  v += dpp_move<0x121, 0xF>(v);     // row_ror:1
+  v += __shfl_xor(v, 32);
+  v += __shfl_xor(v, 16);
+  return v;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(D) void pyramid_kernel(PyramidArgs a) {
   constexpr int NW = D / 64;
@@ -30,6 +42,22 @@ __global__ __launch_bounds__(D) void pyramid_kernel(PyramidArgs a) {
   double aq[8], ak[8], av[8];
 #pragma unroll
   for (int l = 0; l < 8; ++l) { aq[l] = 0.0; ak[l] = 0.0; av[l] = 0.0; }
+  // per level: rows per entry, rows still to add to the open entry, and the
+  // index of that entry inside the level (no division per row)
+  int ewidth[8], left[8];
+  int64_t jnext[8];
+  double inv[8];
+  {
+    int w = 1;
+#pragma unroll
+    for (int l = 1; l < 8; ++l) {
+      w = (l < a.levels) ? w * a.factor : w;
+      ewidth[l] = w;
+      left[l] = w;
+      jnext[l] = r0 / w;
+      inv[l] = 1.0 / (double)w;
+    }
+  }
   // rows in batches of kRows: every load of a batch is issued before any is
   // used (rows past the span re-read its last row and are skipped)
   constexpr int kRows = 16;
@@ -46,29 +74,24 @@ __global__ __launch_bounds__(D) void pyramid_kernel(PyramidArgs a) {
 #pragma unroll
     for (int u = 0; u < kRows; ++u) sq[u] = xq[u] * xq[u] + xk[u] * xk[u];
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-#pragma unroll
-      for (int u = 0; u < kRows; ++u) sq[u] += __shfl_xor(sq[u], m);
-    }
+    for (int u = 0; u < kRows; ++u) sq[u] = wave_sum_rows(sq[u]);
 #pragma unroll
     for (int u = 0; u < kRows; ++u) {
       const int r = rb + u;
       if (r >= P) break;
       if (lane == 0) s_part[wid][r] = sq[u];
-      int width = 1;
 #pragma unroll
       for (int l = 1; l < 8; ++l) {
         if (l >= a.levels) break;
-        width *= a.factor;
         aq[l] += xq[u]; ak[l] += xk[u]; av[l] += xv[u];
-        if ((r + 1) % width == 0) {
-          const int64_t j = (r0 + r + 1) / width - 1;     // entry index inside level l
-          const int64_t row = (int64_t)bh * a.Nc + a.coff[l] + j;
-          const double inv = 1.0 / (double)width;
-          Elem<T>::store_d(a.pq, row * D + e, aq[l] * inv);
-          Elem<T>::store_d(a.pk, row * D + e, ak[l] * inv);
-          Elem<T>::store_d(a.pv, row * D + e, av[l] * inv);
+        if (--left[l] == 0) {                           // entry jnext[l] of level l is complete
+          const int64_t row = (int64_t)bh * a.Nc + a.coff[l] + jnext[l];
+          Elem<T>::store_d(a.pq, row * D + e, aq[l] * inv[l]);
+          Elem<T>::store_d(a.pk, row * D + e, ak[l] * inv[l]);
+          Elem<T>::store_d(a.pv, row * D + e, av[l] * inv[l]);
           aq[l] = 0.0; ak[l] = 0.0; av[l] = 0.0;
+          left[l] = ewidth[l];
+          ++jnext[l];
         }
       }
     }

@@ -239,3 +239,21 @@ def test_block_select_all_equal_scores():
             c = cnt[0, h, blk]
             assert c == len(ref), (h, blk, c, len(ref))
             assert np.array_equal(idx[0, h, blk, :c], np.sort(ref)), (h, blk)
+
+
+def test_prefill_wide_score_range():
+    """A few keys scaled x32 (still exact in bf16): their scores exceed the
+    rest by thousands in the log2 domain, so the softmax reference must be the
+    true maximum over the whole tile, or the weights overflow."""
+    cfg = SMALL.with_(n_ctx=2048, block_top_k=300)
+    inp = workloads.prefill_inputs(cfg, 5)
+    g = torch.Generator().manual_seed(55)
+    rows = torch.randperm(cfg.n_ctx, generator=g)[:24]
+    inp["k"][:, :, rows] *= 32
+    run = PrefillRun(cfg, inp)
+    run.pyramid(); run.select(); run.prefill()
+    torch.cuda.synchronize()
+    assert torch.isfinite(run.t["out"]).all()
+    ni = _np(inp)
+    worst = _check_prefill(cfg, run, ni, {(0, h): range(run.nblk) for h in range(cfg.n_heads)})
+    assert worst <= BF16_TOL
