@@ -277,6 +277,7 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
     Carver c(ws);
     uint2* prefix = c.take<uint2>(bh);
     uint32_t* tau = c.take<uint32_t>(bh * n_int);
+    uint32_t* tau_hi = c.take<uint32_t>(bh * n_int);
     int32_t* cand_len = c.take<int32_t>(bh * n_int);
     uint2* cand = c.take<uint2>(bh * n_int * sa::kPsCap);
     const size_t need = c.size();
@@ -286,7 +287,7 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
     a.prefix = prefix;
     a.S = n_int > 0 ? S : 0;
     a.n_int = n_int;
-    a.tau = tau; a.cand_len = cand_len; a.cand = cand;
+    a.tau = tau; a.tau_hi = tau_hi; a.cand_len = cand_len; a.cand = cand;
     a.scores = b->pyr_scores; a.blk_idx = b->blk_idx; a.blk_count = b->blk_count;
     a.B = p->batch; a.H = p->n_q_heads; a.N = p->n_ctx; a.levels = p->levels; a.factor = p->factor;
     a.q_block = p->q_block; a.K = p->block_top_k; a.nblk = pg.nblk; a.Nt = pg.Nt;

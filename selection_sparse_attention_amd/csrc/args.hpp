@@ -110,6 +110,7 @@ struct PyrSelectArgs {
   // intervals of S consecutive blocks (n_int per head; 0 = not used)
   int32_t S, n_int;
   uint32_t* tau;         // [B*H, n_int]: cut key of the interval's first block
+  uint32_t* tau_hi;      // [B*H, n_int]: cut key of the interval's last block
   int32_t* cand_len;     // [B*H, n_int]: candidates kept (-1: more than kPsCap)
   uint2* cand;           // [B*H, n_int, kPsCap]: (key, flat id), ascending flat id
 };

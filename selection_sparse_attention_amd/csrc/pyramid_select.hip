@@ -59,6 +59,9 @@ __device__ __forceinline__ VisRanges visible(const PyrSelectArgs& a, int blk) {
 
 constexpr int kPsU = 16;                 // entries per thread in flight per pass step
 
+// key >> pos for pos in 0..32 (a 32-bit shift by 32 is not defined)
+__device__ __forceinline__ uint32_t key_hi(uint32_t key, int pos) { return pos >= 32 ? 0u : key >> pos; }
+
 // AND and OR of every score key of one (sequence, head): the leading bits
 // all its keys share.  One 1024-thread workgroup per head.
 __global__ __launch_bounds__(1024) void pyr_prefix_kernel(PyrSelectArgs a) {
@@ -113,7 +116,7 @@ __device__ void vis_hist(const float* sc, const VisRanges& v, uint32_t prefix, i
       for (int u = 0; u < kPsU; ++u) {
         const int j = j0 + u * kPsThreads + threadIdx.x;
         const uint32_t key = order_key(x[u]);
-        if (j < cnt && (pshift >= 32 || (key >> pshift) == prefix))
+        if (j < cnt && key_hi(key, pshift) == prefix)
           atomicAdd(&hist[(key >> shift) & mask], 1u);
       }
     }
@@ -169,7 +172,7 @@ __device__ uint32_t visible_cut(const PyrSelectArgs& a, const VisRanges& v, cons
   uint32_t cut = pf.x;                              // when every key is equal
   if (common < 32) {
     int pos = 32 - common;                          // bits still to resolve
-    uint32_t prefix = pf.x >> pos;
+    uint32_t prefix = key_hi(pf.x, pos);
     while (pos > 0) {                               // digits of at most 12 bits
       const int bits = pos < 12 ? pos : 12;
       const int shift = pos - bits;
@@ -213,17 +216,62 @@ __device__ uint32_t ordered_compact(int n, Get get, Keep keep, Emit emit, uint32
   return run;
 }
 
+// The cut over n keys held in LDS, as visible_cut does over global prefixes,
+// given that it lies in [lo, hi]: the keys above hi are counted (all above
+// the cut), and the radix digits run below the bits lo and hi share - the
+// keys in the window spread over the buckets even when a few keys far above
+// it (outliers) would otherwise crowd the bulk into one bucket.
+__device__ uint32_t lds_cut(const uint32_t* keys, int n, int64_t K, uint32_t lo, uint32_t hi,
+                            PsShared& sh, int64_t* above_out) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  uint32_t over = 0;
+  for (int i = tid; i < n; i += kPsThreads) over += keys[i] > hi ? 1u : 0u;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) over += (uint32_t)__shfl_xor((int)over, m);
+  if (lane == 0) sh.kand[tid >> 6] = over;
+  __syncthreads();
+  int64_t above = 0;
+#pragma unroll
+  for (int w = 0; w < kPsThreads / 64; ++w) above += sh.kand[w];
+  const uint32_t diff = lo ^ hi;
+  const int common = diff ? __clz(diff) : 32;
+  uint32_t cut = lo;                               // lo == hi: the window is one key
+  if (common < 32) {
+    int pos = 32 - common;
+    uint32_t prefix = key_hi(lo, pos);
+    while (pos > 0) {
+      const int bits = pos < 12 ? pos : 12;
+      const int shift = pos - bits;
+      const uint32_t mask = (1u << bits) - 1u;
+      for (int i = tid; i < 4096; i += kPsThreads) sh.hist[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < n; i += kPsThreads) {
+        const uint32_t key = keys[i];
+        if (key <= hi && key_hi(key, pos) == prefix) atomicAdd(&sh.hist[(key >> shift) & mask], 1u);
+      }
+      __syncthreads();
+      const int bk = vis_find<4096>(sh.hist, K, &above, sh.scan, &sh.b, &sh.above);
+      prefix = (prefix << bits) | (uint32_t)bk;
+      pos = shift;
+    }
+    cut = prefix;
+  }
+  *above_out = above;
+  return cut;
+}
+
 // One workgroup per (interval, sequence-head): the cut of the interval's first
 // block, then the candidates of the interval (entries its last block sees with
 // a key at least that cut).
 __global__ __launch_bounds__(kPsThreads) void pyr_interval_kernel(PyrSelectArgs a) {
   __shared__ PsShared sh;
+  __shared__ uint32_t c_key[kPsCap];
   const int iv = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int b0 = iv * a.S, b1 = min(b0 + a.S, a.nblk) - 1;
   const int64_t slot = (int64_t)bh * a.n_int + iv;
   const VisRanges v1 = visible(a, b1);
   if (v1.total <= a.K) {                    // every block of the interval keeps all it sees
-    if (tid == 0) { a.tau[slot] = 0; a.cand_len[slot] = 0; }
+    if (tid == 0) { a.tau[slot] = 0; a.tau_hi[slot] = 0; a.cand_len[slot] = 0; }
     return;
   }
   const float* sc = a.scores + (int64_t)bh * a.Nt;
@@ -244,55 +292,27 @@ __global__ __launch_bounds__(kPsThreads) void pyr_interval_kernel(PyrSelectArgs 
         v1.cnt[l],
         [&](int j, uint32_t& key, int32_t& id) { key = order_key(p[j]); id = base + j; },
         [&](uint32_t key, int32_t) { return key >= tau; },
-        [&](uint32_t k, uint32_t key, int32_t id) { if (k < room) o[k] = make_uint2(key, (uint32_t)id); },
+        [&](uint32_t k, uint32_t key, int32_t id) {
+          if (k < room) {
+            o[k] = make_uint2(key, (uint32_t)id);
+            c_key[(o - out) + k] = key;
+          }
+        },
         sh.scan32);
+  }
+  // the last block's cut, over the candidates (they hold every entry it
+  // keeps): an upper bound of the cut of every block in the interval
+  uint32_t tau_hi = 0xFFFFFFFFu;
+  if (total <= (uint32_t)kPsCap) {
+    __syncthreads();
+    int64_t above;
+    tau_hi = lds_cut(c_key, (int)total, a.K, tau, 0xFFFFFFFFu, sh, &above);
   }
   if (tid == 0) {
     a.tau[slot] = tau;
+    a.tau_hi[slot] = tau_hi;
     a.cand_len[slot] = total <= (uint32_t)kPsCap ? (int32_t)total : -1;
   }
-}
-
-// The cut over n keys held in LDS, as visible_cut does over global prefixes.
-__device__ uint32_t lds_cut(const uint32_t* keys, int n, int64_t K, PsShared& sh, int64_t* above_out) {
-  const int tid = threadIdx.x;
-  uint32_t kand = 0xFFFFFFFFu, kor = 0u;
-  for (int i = tid; i < n; i += kPsThreads) { kand &= keys[i]; kor |= keys[i]; }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    kand &= (uint32_t)__shfl_xor((int)kand, m);
-    kor |= (uint32_t)__shfl_xor((int)kor, m);
-  }
-  if ((tid & 63) == 0) { sh.kand[tid >> 6] = kand; sh.kor[tid >> 6] = kor; }
-  __syncthreads();
-#pragma unroll
-  for (int w = 0; w < kPsThreads / 64; ++w) { kand &= sh.kand[w]; kor |= sh.kor[w]; }
-  const uint32_t diff = kand ^ kor;
-  const int common = diff ? __clz(diff) : 32;
-  int64_t above = 0;
-  uint32_t cut = kand;
-  if (common < 32) {
-    int pos = 32 - common;
-    uint32_t prefix = kand >> pos;
-    while (pos > 0) {
-      const int bits = pos < 12 ? pos : 12;
-      const int shift = pos - bits;
-      const uint32_t mask = (1u << bits) - 1u;
-      for (int i = tid; i < 4096; i += kPsThreads) sh.hist[i] = 0;
-      __syncthreads();
-      for (int i = tid; i < n; i += kPsThreads) {
-        const uint32_t key = keys[i];
-        if ((key >> pos) == prefix) atomicAdd(&sh.hist[(key >> shift) & mask], 1u);
-      }
-      __syncthreads();
-      const int bk = vis_find<4096>(sh.hist, K, &above, sh.scan, &sh.b, &sh.above);
-      prefix = (prefix << bits) | (uint32_t)bk;
-      pos = shift;
-    }
-    cut = prefix;
-  }
-  *above_out = above;
-  return cut;
 }
 
 __global__ __launch_bounds__(kPsThreads) void pyr_select_kernel(PyrSelectArgs a) {
@@ -333,7 +353,7 @@ __global__ __launch_bounds__(kPsThreads) void pyr_select_kernel(PyrSelectArgs a)
         sh.scan32);
     __syncthreads();
     int64_t above;
-    const uint32_t cut = lds_cut(c_key, m, K, sh, &above);
+    const uint32_t cut = lds_cut(c_key, m, K, a.tau[slot], a.tau_hi[slot], sh, &above);
     const uint32_t need = (uint32_t)(K - above);    // ties kept, lowest flat ids first
     uint32_t s_run = 0, t_run = 0;
     for (int j0 = 0; j0 < m; j0 += kPsU * kPsThreads) {
