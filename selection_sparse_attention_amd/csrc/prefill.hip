@@ -53,12 +53,29 @@ __device__ __forceinline__ uint32_t pk_bf16(float x, float y) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2p){x, y}, bf16x2p));
 }
 
+// max of two scores by a compare and select: fmaxf would first quiet each
+// operand that the compiler cannot show to be canonical (a value that comes
+// back from a lane swap), one extra instruction per operand; scores are
+// never NaN
+__device__ __forceinline__ float max_raw(float a, float b) { return a > b ? a : b; }
+
 // max over the four lanes l16 + 16 jg (jg = 0..3) that hold one query's
-// scores: exchanges across the wave's halves and across neighbouring 16-lane
-// rows
+// scores: a lane-swap across the wave's halves, then one across neighbouring
+// 16-lane rows. Each swap exchanges half of its first operand with half of
+// its second, so with both operands holding v, every lane ends with its own
+// value in one result and its partner's in the other. The second operand is
+// an opaque copy of v: given the same value twice, the compiler takes the
+// two results as equal and keeps one of them.
 __device__ __forceinline__ float max_over_lane_groups(float v) {
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return fmaxf(v, __shfl_xor(v, 16));
+  uint32_t u = __float_as_uint(v), w = u;
+  asm volatile("" : "+v"(w));
+  auto r = __builtin_amdgcn_permlane32_swap(u, w, false, false);
+  v = max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  u = __float_as_uint(v);
+  w = u;
+  asm volatile("" : "+v"(w));
+  r = __builtin_amdgcn_permlane16_swap(u, w, false, false);
+  return max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
