@@ -34,14 +34,19 @@ from .numerics import round_store
 def pyramid_levels(X, levels, factor, store="bf16"):
     """[X_1, ..., X_{L-1}] for X [N, d]: X_l[j] = mean of p entries of X_{l-1}.
 
-    Means are taken in fp64 on the unrounded previous level and each level is
-    rounded once for storage."""
+    The p children's sums are added (the sum over the entry's p^l level-0
+    rows) and divided once by p^l, so the mean of means carries no rounding
+    of the unrounded intermediate levels; each level is rounded once for
+    storage."""
     cur = np.asarray(X, np.float64)
     out = []
+    width = 1
     for _ in range(1, levels):
         m = cur.shape[0] // factor
-        cur = cur[: m * factor].reshape(m, factor, -1).mean(axis=1)
-        out.append(round_store(cur, store) if store else cur.copy())
+        cur = cur[: m * factor].reshape(m, factor, -1).sum(axis=1)
+        width *= factor
+        mean = cur / width
+        out.append(round_store(mean, store) if store else mean)
     return out
 
 

@@ -424,6 +424,17 @@ def test_pyramid_levels_are_span_means():
         np.testing.assert_allclose(lv[0][j], X[4 * j:4 * j + 4].mean(0), atol=1e-13)
 
 
+def test_pyramid_levels_exact_for_factor_three():
+    """p = 3: an entry whose 9 rows sum to zero is exactly zero, though its
+    three children (k/3 each) are not representable."""
+    X = np.zeros((27, 2))
+    X[:9, 0] = np.array([-7, -4, -7, 0, 8, 5, 4, 4, -3]) / 8   # children sums -18, 13, 5 (x 1/8)
+    X[9:18, 1] = [0.125] * 9
+    lv = oracle.pyramid_levels(X, 3, 3, None)
+    assert lv[1][0, 0] == 0.0 and lv[1][1, 1] == 0.125
+    assert lv[0][0, 0] == -0.75 and lv[0][1, 0] == 13 / 24
+
+
 def test_pyramid_scores_inherit_span_max():
     rng = np.random.default_rng(19)
     Q, K = rng.standard_normal((256, 8)), rng.standard_normal((256, 8))
