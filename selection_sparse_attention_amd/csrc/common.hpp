@@ -61,6 +61,7 @@ template <> struct Elem<float> {
 
 typedef uint32_t vl_u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t vl_u32x4 __attribute__((ext_vector_type(4)));
+typedef float vl_f32x2 __attribute__((ext_vector_type(2)));
 typedef float vl_f32x4 __attribute__((ext_vector_type(4)));
 
 // A plain load, or a non-temporal one (streamed data read once: it does not

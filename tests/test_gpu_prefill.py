@@ -43,7 +43,12 @@ def _coarse(run, b, h, cfg, name):
     SMALL,
     SMALL.with_(levels=2, factor=2, n_ctx=1024 + 256),
     SMALL.with_(levels=4, factor=2, n_ctx=1024),
-])
+    SMALL.with_(levels=4, factor=3, n_ctx=27 * 40),           # spans of 27 rows: batches cross them
+    SMALL.with_(levels=1, n_ctx=1000),                       # level 0 only: scores
+    SMALL.with_(levels=2, factor=4, n_ctx=4096 + 64, batch=2),  # several runs per head, short last run
+    SMALL.with_(head_dim=64, dtype="fp32", n_ctx=1024 + 16),
+    SMALL.with_(head_dim=64, levels=5, factor=2, n_ctx=512),
+], ids=lambda c: f"N{c.n_ctx}-L{c.levels}-p{c.factor}-d{c.head_dim}-{c.dtype}-B{c.batch}")
 def test_pyramid_matches_oracle_exactly_on_lattice(cfg):
     """Lattice inputs: coarse means (accumulated exactly, rounded once) and
     squared-norm scores are exact on both sides."""
