@@ -315,12 +315,11 @@ __global__ __launch_bounds__(kPsThreads) void pyr_interval_kernel(PyrSelectArgs 
   }
 }
 
-__global__ __launch_bounds__(kPsThreads) void pyr_select_kernel(PyrSelectArgs a) {
-  __shared__ PsShared sh;
-  __shared__ uint32_t c_key[kPsCap];
-  __shared__ int32_t c_id[kPsCap];
-  // late blocks see the most entries: dispatch them first
-  const int blk = a.nblk - 1 - (int)blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+// One block's selection by whole-workgroup passes over its visible scores:
+// every visible entry when at most K are visible, else the cut and the kept
+// flat ids in ascending order (strict, then the first ties).
+__device__ __forceinline__ void full_select(const PyrSelectArgs& a, int blk, int bh, PsShared& sh) {
+  const int tid = threadIdx.x;
   const VisRanges v = visible(a, blk);
   const float* sc = a.scores + (int64_t)bh * a.Nt;
   int32_t* out = a.blk_idx + ((int64_t)bh * a.nblk + blk) * a.K;
@@ -334,60 +333,6 @@ __global__ __launch_bounds__(kPsThreads) void pyr_select_kernel(PyrSelectArgs a)
     if (tid == 0) a.blk_count[(int64_t)bh * a.nblk + blk] = (int32_t)v.total;
     return;
   }
-  const int64_t slot = (int64_t)bh * a.n_int + (a.S > 0 ? blk / a.S : 0);
-  const int ncand = (a.n_int > 0) ? a.cand_len[slot] : -1;
-  if (ncand >= 0) {
-    // the interval's candidates this block sees, in ascending flat id
-    const uint2* cp = a.cand + slot * kPsCap;
-    const int m = (int)ordered_compact(
-        ncand,
-        [&](int i, uint32_t& key, int32_t& id) { const uint2 e = cp[i]; key = e.x; id = (int32_t)e.y; },
-        [&](uint32_t, int32_t id) {
-          bool vis = false;
-#pragma unroll
-          for (int l = 0; l < 8; ++l)
-            if (l < v.nl && id >= v.off[l] && id < v.off[l] + a.len[l]) vis = (id - v.off[l]) < v.cnt[l];
-          return vis;
-        },
-        [&](uint32_t k, uint32_t key, int32_t id) { c_key[k] = key; c_id[k] = id; },
-        sh.scan32);
-    __syncthreads();
-    int64_t above;
-    const uint32_t cut = lds_cut(c_key, m, K, a.tau[slot], a.tau_hi[slot], sh, &above);
-    const uint32_t need = (uint32_t)(K - above);    // ties kept, lowest flat ids first
-    uint32_t s_run = 0, t_run = 0;
-    for (int j0 = 0; j0 < m; j0 += kPsU * kPsThreads) {
-      const int jt = j0 + kPsU * tid;
-      uint32_t sf = 0, tf = 0;
-#pragma unroll
-      for (int u = 0; u < kPsU; ++u) {
-        if (jt + u < m) {
-          const uint32_t key = c_key[jt + u];
-          if (key > cut) sf |= 1u << u;
-          else if (key == cut) tf |= 1u << u;
-        }
-      }
-      uint32_t tot_s, tot_t;
-      const uint32_t ex_s = block_exclusive_scan<uint32_t, kPsThreads>(__popc(sf), sh.scan32, &tot_s);
-      const uint32_t ex_t = block_exclusive_scan<uint32_t, kPsThreads>(__popc(tf), sh.scan32, &tot_t);
-      uint32_t sb = s_run + ex_s, tb = t_run + ex_t;
-#pragma unroll
-      for (int u = 0; u < kPsU; ++u) {
-        if (sf & (1u << u)) {
-          out[sb + (tb < need ? tb : need)] = c_id[jt + u];
-          ++sb;
-        } else if (tf & (1u << u)) {
-          if (tb < need) out[sb + tb] = c_id[jt + u];
-          ++tb;
-        }
-      }
-      s_run += tot_s;
-      t_run += tot_t;
-    }
-    if (tid == 0) a.blk_count[(int64_t)bh * a.nblk + blk] = (int32_t)K;
-    return;
-  }
-  // full passes over the visible scores
   int64_t above;
   const uint32_t cut = visible_cut(a, v, sc, bh, sh, &above);
   const uint32_t need = (uint32_t)(K - above);        // ties kept, lowest flat ids first
@@ -433,15 +378,217 @@ __global__ __launch_bounds__(kPsThreads) void pyr_select_kernel(PyrSelectArgs a)
   if (tid == 0) a.blk_count[(int64_t)bh * a.nblk + blk] = (int32_t)K;
 }
 
+// Without intervals: one workgroup per (block, sequence-head), late blocks
+// (the most visible entries) first.
+__global__ __launch_bounds__(kPsThreads) void pyr_select_kernel(PyrSelectArgs a) {
+  __shared__ PsShared sh;
+  full_select(a, a.nblk - 1 - (int)blockIdx.x, blockIdx.y, sh);
+}
+
+// ---------------------------------------------------------------- one wave per block
+// With intervals, one workgroup per (interval, sequence-head) stages the
+// interval's candidates in LDS once, and each wave selects for its own blocks
+// of the interval with no workgroup barrier:
+//  * the candidates are in ascending flat id and each level's visible entries
+//    are a prefix of the level, so a block's visible candidates are one range
+//    per level, found by a search;
+//  * the cut lies between the interval's two bounds: keys above the upper one
+//    are counted, and radix digits of 8 bits below the bits the bounds share
+//    go through a 256-bucket histogram of the wave's own;
+//  * the kept ids are written in ascending flat id, positions from ballots.
+// An interval with more candidates than fit runs the whole-workgroup passes
+// for each of its blocks.
+constexpr int kPwWaves = kPsThreads / 64;
+constexpr int kPwBuckets = 256;
+
+union PwShared {
+  struct {
+    uint32_t key[kPsCap];
+    int32_t id[kPsCap];
+    uint32_t hist[kPwWaves][kPwBuckets];
+  } w;
+  PsShared ps;
+};
+
+__device__ __forceinline__ uint64_t wave_ballot(bool p) { return __ballot(p); }
+
+// lanes below this one whose bit is set in m
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// First index i in ids[0, n) (ascending) with ids[i] >= x, by the whole wave:
+// 64 segments tested at their last element, then the one segment holding the
+// boundary element by element.
+__device__ int wave_lower_bound(const int32_t* ids, int n, int64_t x, int lane) {
+  if (n == 0) return 0;
+  const int seg = (n + 63) / 64;
+  const int last = min((lane + 1) * seg, n) - 1;
+  const bool below = lane * seg < n && ids[last] < x;
+  const int j = __popcll(wave_ballot(below));          // segments wholly below x
+  if (j * seg >= n) return n;
+  int cnt = 0;
+  for (int t0 = 0; t0 < seg; t0 += 64) {
+    const int i = j * seg + t0 + lane;
+    cnt += __popcll(wave_ballot(t0 + lane < seg && i < n && ids[i] < x));
+  }
+  return j * seg + cnt;
+}
+
+// A bucket of hist[0, 256) counted from the top: the one holding the
+// target-th key when `above` keys lie above the histogram. Returns it and
+// adds the count above it to *above.
+__device__ int wave_find256(const uint32_t* hist, uint32_t target, uint32_t* above, int lane) {
+  uint32_t c[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) c[k] = hist[kPwBuckets - 1 - 4 * lane - k];
+  const uint32_t sum = c[0] + c[1] + c[2] + c[3];
+  const uint32_t incl = wave_inclusive_scan(sum);
+  uint32_t base = *above + incl - sum;
+  const uint64_t m = wave_ballot(base < target && target <= base + sum);
+  const int src = m ? (int)__builtin_ctzll(m) : 0;            // m != 0 while target <= the total
+  int bk = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (bk == 0 && base + c[k] >= target) bk = kPwBuckets - 4 * lane - k;   // bucket + 1
+    else if (bk == 0) base += c[k];
+  }
+  const int b = __builtin_amdgcn_readlane(bk, src) - 1;
+  *above = (uint32_t)__builtin_amdgcn_readlane((int)base, src);
+  return b;
+}
+
+// wave-local ordering of LDS accesses (one wave's own histogram)
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+struct LevelRanges { int lo[8]; };
+
+__device__ __forceinline__ void wave_select(const PyrSelectArgs& a, const PwShared& s, uint32_t* hist,
+                                            int ncand, const LevelRanges lstart, int blk, int bh,
+                                            uint32_t lo, uint32_t hi, int lane) {
+  const VisRanges v = visible(a, blk);
+  int32_t* out = a.blk_idx + ((int64_t)bh * a.nblk + blk) * a.K;
+  const uint32_t K = (uint32_t)a.K;
+  if (v.total <= (int64_t)K) {
+    int64_t o = 0;
+#pragma unroll
+    for (int l = 0; l < 8; ++l) {
+      if (l < v.nl) {
+        for (int j = lane; j < v.cnt[l]; j += 64) out[o + j] = (int32_t)(v.off[l] + j);
+        o += v.cnt[l];
+      }
+    }
+    if (lane == 0) a.blk_count[(int64_t)bh * a.nblk + blk] = (int32_t)v.total;
+    return;
+  }
+  // the visible candidates: [lstart.lo[l], lend[l]) of each level (the
+  // level loops are unrolled so that the bounds stay in registers)
+  int lend[8];
+#pragma unroll
+  for (int l = 0; l < 8; ++l)
+    lend[l] = l < v.nl ? wave_lower_bound(s.w.id, ncand, v.off[l] + v.cnt[l], lane) : 0;
+  // keys above the upper bound: all kept
+  uint32_t over = 0;
+#pragma unroll
+  for (int l = 0; l < 8; ++l)
+    if (l < v.nl)
+      for (int i = lstart.lo[l] + lane; i < lend[l]; i += 64) over += s.w.key[i] > hi ? 1u : 0u;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) over += (uint32_t)__shfl_xor((int)over, m);
+  uint32_t above = over;
+  const uint32_t diff = lo ^ hi;
+  const int common = diff ? __clz(diff) : 32;
+  uint32_t cut = lo;                                   // lo == hi: the window is one key
+  if (common < 32) {
+    int pos = 32 - common;
+    uint32_t prefix = key_hi(lo, pos);
+    while (pos > 0) {
+      const int bits = pos < 8 ? pos : 8;
+      const int shift = pos - bits;
+      const uint32_t mask = (1u << bits) - 1u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) hist[4 * lane + k] = 0;
+      wave_lds_sync();
+#pragma unroll
+      for (int l = 0; l < 8; ++l)
+        if (l < v.nl)
+          for (int i = lstart.lo[l] + lane; i < lend[l]; i += 64) {
+            const uint32_t key = s.w.key[i];
+            if (key <= hi && key_hi(key, pos) == prefix) atomicAdd(&hist[(key >> shift) & mask], 1u);
+          }
+      wave_lds_sync();
+      const int bk = wave_find256(hist, K, &above, lane);
+      wave_lds_sync();
+      prefix = (prefix << bits) | (uint32_t)bk;
+      pos = shift;
+    }
+    cut = prefix;
+  }
+  const uint32_t need = K - above;                     // ties kept, lowest flat ids first
+  // every position is below K when `above` counts the keys over the cut;
+  // the test keeps a write inside the block's K slots regardless
+  uint32_t srun = 0, trun = 0;
+#pragma unroll
+  for (int l = 0; l < 8; ++l)
+    if (l < v.nl)
+      for (int i0 = lstart.lo[l]; i0 < lend[l]; i0 += 64) {
+        const int i = i0 + lane;
+        const bool ok = i < lend[l];
+        const uint32_t key = ok ? s.w.key[i] : 0u;
+        const bool st = ok && key > cut, ti = ok && key == cut;
+        const uint64_t ms = wave_ballot(st), mt = wave_ballot(ti);
+        const uint32_t sb = srun + lanes_below(ms), tb = trun + lanes_below(mt);
+        const uint32_t p = st ? sb + (tb < need ? tb : need) : sb + tb;
+        if ((st || (ti && tb < need)) && p < K) out[p] = s.w.id[i];
+        srun += (uint32_t)__popcll(ms);
+        trun += (uint32_t)__popcll(mt);
+      }
+  if (lane == 0) a.blk_count[(int64_t)bh * a.nblk + blk] = (int32_t)K;
+}
+
+__global__ __launch_bounds__(kPsThreads) void pyr_block_select_kernel(PyrSelectArgs a) {
+  __shared__ PwShared s;
+  const int iv = a.n_int - 1 - (int)blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t slot = (int64_t)bh * a.n_int + iv;
+  const int b0 = iv * a.S, b1 = min(b0 + a.S, a.nblk) - 1;
+  const int ncand = a.cand_len[slot];
+  if (ncand < 0) {                                     // too many candidates
+    for (int blk = b1; blk >= b0; --blk) {
+      full_select(a, blk, bh, s.ps);
+      __syncthreads();
+    }
+    return;
+  }
+  const uint2* cp = a.cand + slot * kPsCap;
+  for (int i = tid; i < ncand; i += kPsThreads) {
+    const uint2 e = cp[i];
+    s.w.key[i] = e.x;
+    s.w.id[i] = (int32_t)e.y;
+  }
+  __syncthreads();
+  LevelRanges lstart;
+#pragma unroll
+  for (int l = 0; l < 8; ++l) lstart.lo[l] = l < a.levels ? wave_lower_bound(s.w.id, ncand, a.soff[l], lane) : 0;
+  const uint32_t lo = a.tau[slot], hi = a.tau_hi[slot];
+  for (int blk = b1 - wid; blk >= b0; blk -= kPwWaves)
+    wave_select(a, s, s.w.hist[wid], ncand, lstart, blk, bh, lo, hi, lane);
+}
+
 hipError_t launch_pyramid_select(const PyrSelectArgs& a, hipStream_t s) {
   if (!a.prefix) return hipErrorInvalidValue;
   hipLaunchKernelGGL(pyr_prefix_kernel, dim3(a.B * a.H), dim3(1024), 0, s, a);
   if (a.n_int > 0) {
     if (a.S < 1 || !a.tau || !a.cand_len || !a.cand) return hipErrorInvalidValue;
     hipLaunchKernelGGL(pyr_interval_kernel, dim3(a.n_int, a.B * a.H), dim3(kPsThreads), 0, s, a);
+    hipLaunchKernelGGL(pyr_block_select_kernel, dim3(a.n_int, a.B * a.H), dim3(kPsThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(pyr_select_kernel, dim3(a.nblk, a.B * a.H), dim3(kPsThreads), 0, s, a);
   }
-  dim3 grid(a.nblk, a.B * a.H);
-  hipLaunchKernelGGL(pyr_select_kernel, grid, dim3(kPsThreads), 0, s, a);
   return hipGetLastError();
 }
 

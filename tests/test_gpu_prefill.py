@@ -90,6 +90,8 @@ SELECT_CASES = [
     SMALL.with_(n_ctx=2048 + 16 * 9, block_top_k=500),   # ragged last block
     SMALL.with_(levels=2, factor=2, n_ctx=1024, block_top_k=100),
     SMALL.with_(n_ctx=8192, block_top_k=300),           # intervals past the first: bound > 0
+    SMALL.with_(n_ctx=8192, block_top_k=7000),          # no room for intervals: full passes
+    SMALL.with_(levels=4, factor=3, n_ctx=27 * 200, q_block=54, block_top_k=700),
 ]
 
 
