@@ -180,13 +180,14 @@ __device__ __forceinline__ T wave_inclusive_scan(T v) {
 
 // Exclusive prefix sum over a block of NT threads (NT a multiple of 64),
 // using `scratch` (NT/64 entries of T in LDS).  Returns the exclusive value
-// and writes the block total to *total.
+// and writes the block total to *total.  Its barriers order LDS only, so the
+// callers' global loads and stores stay in flight across it.
 template <typename T, int NT>
 __device__ __forceinline__ T block_exclusive_scan(T v, T* scratch, T* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const T incl = wave_inclusive_scan(v);
   if (lane == 63) scratch[wid] = incl;
-  __syncthreads();
+  lds_barrier();
   T base = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < NT / 64; ++w) {
@@ -194,7 +195,7 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T* scratch, T* total) {
     if (w < wid) base += s;
     tot += s;
   }
-  __syncthreads();
+  lds_barrier();
   *total = tot;
   return base + incl - v;
 }

@@ -98,43 +98,55 @@ __global__ __launch_bounds__(1024) void pyr_prefix_kernel(PyrSelectArgs a) {
 
 // Histogram of the visible keys whose bits above `pshift` equal `prefix`,
 // bucket = (key >> shift) & (2^bits - 1).  Each thread keeps kPsU loads in
-// flight.
+// flight, and the next chunk's loads are issued before a chunk is counted.
+template <int NT>
 __device__ void vis_hist(const float* sc, const VisRanges& v, uint32_t prefix, int pshift, int shift,
                          int bits, uint32_t* hist) {
   const uint32_t mask = (1u << bits) - 1u;
   for (int l = 0; l < v.nl; ++l) {
     const float* p = sc + v.off[l];
     const int cnt = v.cnt[l];
-    for (int j0 = 0; j0 < cnt; j0 += kPsU * kPsThreads) {
-      float x[kPsU];
+    if (cnt <= 0) continue;
+    auto load = [&](float (&x)[kPsU], int j0) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < kPsU; ++u) {
-        const int j = j0 + u * kPsThreads + threadIdx.x;
+        const int j = j0 + u * NT + threadIdx.x;
         x[u] = p[j < cnt ? j : cnt - 1];
       }
+    };
+    auto count = [&](const float (&x)[kPsU], int j0) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < kPsU; ++u) {
-        const int j = j0 + u * kPsThreads + threadIdx.x;
+        const int j = j0 + u * NT + threadIdx.x;
         const uint32_t key = order_key(x[u]);
         if (j < cnt && key_hi(key, pshift) == prefix)
           atomicAdd(&hist[(key >> shift) & mask], 1u);
       }
+    };
+    float xa[kPsU], xb[kPsU];
+    load(xa, 0);
+    for (int j0 = 0; j0 < cnt; j0 += 2 * kPsU * NT) {
+      load(xb, j0 + kPsU * NT);
+      count(xa, j0);
+      if (j0 + kPsU * NT >= cnt) break;
+      load(xa, j0 + 2 * kPsU * NT);
+      count(xb, j0 + kPsU * NT);
     }
   }
 }
 
 // Scan a histogram of NB buckets from the top for the bucket holding the
 // `target`-th key; returns the bucket and adds the count above it to *above.
-template <int NB>
+template <int NB, int NT>
 __device__ int vis_find(const uint32_t* hist, int64_t target, int64_t* above, int64_t* s_scan,
                         int* s_b, int64_t* s_above) {
-  constexpr int PER = NB / kPsThreads;
+  constexpr int PER = NB / NT;
   const int tid = threadIdx.x;
   int64_t tc = 0;
 #pragma unroll
   for (int k = 0; k < PER; ++k) tc += hist[NB - 1 - (PER * tid + k)];
   int64_t tot;
-  const int64_t pre = block_exclusive_scan<int64_t, kPsThreads>(tc, s_scan, &tot);
+  const int64_t pre = block_exclusive_scan<int64_t, NT>(tc, s_scan, &tot);
   if (tid == 0) *s_b = -1;
   __syncthreads();
   int64_t cc = *above + pre;
@@ -154,15 +166,16 @@ __device__ int vis_find(const uint32_t* hist, int64_t target, int64_t* above, in
 
 struct PsShared {
   uint32_t hist[4096];
-  int64_t scan[kPsThreads / 64];
-  uint32_t scan32[kPsThreads / 64];
+  int64_t scan[16];                  // one entry per wave, up to 1024 threads
+  uint32_t scan32[16];
   int b;
   int64_t above;
-  uint32_t kand[kPsThreads / 64], kor[kPsThreads / 64];
+  uint32_t kand[16], kor[16];
 };
 
 // The cut over the visible prefixes v of one head: the key of the K-th
 // largest visible score; *above receives how many visible keys exceed it.
+template <int NT>
 __device__ uint32_t visible_cut(const PyrSelectArgs& a, const VisRanges& v, const float* sc, int bh,
                                 PsShared& sh, int64_t* above_out) {
   const uint2 pf = a.prefix[bh];
@@ -176,11 +189,11 @@ __device__ uint32_t visible_cut(const PyrSelectArgs& a, const VisRanges& v, cons
     while (pos > 0) {                               // digits of at most 12 bits
       const int bits = pos < 12 ? pos : 12;
       const int shift = pos - bits;
-      for (int i = threadIdx.x; i < 4096; i += kPsThreads) sh.hist[i] = 0;
+      for (int i = threadIdx.x; i < 4096; i += NT) sh.hist[i] = 0;
       __syncthreads();
-      vis_hist(sc, v, prefix, pos, shift, bits, sh.hist);
+      vis_hist<NT>(sc, v, prefix, pos, shift, bits, sh.hist);
       __syncthreads();
-      const int bk = vis_find<4096>(sh.hist, a.K, &above, sh.scan, &sh.b, &sh.above);
+      const int bk = vis_find<4096, NT>(sh.hist, a.K, &above, sh.scan, &sh.b, &sh.above);
       prefix = (prefix << bits) | (uint32_t)bk;
       pos = shift;
     }
@@ -190,28 +203,41 @@ __device__ uint32_t visible_cut(const PyrSelectArgs& a, const VisRanges& v, cons
   return cut;
 }
 
-// Ordered compaction over n entries produced by get(i) -> (key, id): the
-// entries with keep(key) go to emit(slot, key, id) with slots in entry order.
-// Thread t takes kPsU consecutive entries of every chunk.  Returns the count.
-template <typename Get, typename Keep, typename Emit>
-__device__ uint32_t ordered_compact(int n, Get get, Keep keep, Emit emit, uint32_t* s_scan32) {
+// Ordered compaction of the scores p[0, cnt) whose key is at least tau: each
+// goes to emit(slot, key, id = base + index), slots in index order. Thread t
+// takes kPsU consecutive entries of every chunk; the next chunk's loads are
+// issued before a chunk is scanned. Returns the count.
+template <int NT, typename Emit>
+__device__ uint32_t compact_scores(const float* p, int cnt, int base, uint32_t tau, Emit emit,
+                                   uint32_t* s_scan32) {
+  if (cnt <= 0) return 0;
   uint32_t run = 0;
-  for (int j0 = 0; j0 < n; j0 += kPsU * kPsThreads) {
-    const int jt = j0 + kPsU * threadIdx.x;
-    uint32_t key[kPsU];
-    int32_t id[kPsU];
+  auto load = [&](float (&x)[kPsU], int j0) __attribute__((always_inline)) {
+    const int jt = j0 + kPsU * (int)threadIdx.x;
 #pragma unroll
-    for (int u = 0; u < kPsU; ++u) get(min(jt + u, n - 1), key[u], id[u]);
+    for (int u = 0; u < kPsU; ++u) x[u] = p[min(jt + u, cnt - 1)];
+  };
+  auto step = [&](const float (&x)[kPsU], int j0) __attribute__((always_inline)) {
+    const int jt = j0 + kPsU * (int)threadIdx.x;
     uint32_t f = 0;
 #pragma unroll
     for (int u = 0; u < kPsU; ++u)
-      if (jt + u < n && keep(key[u], id[u])) f |= 1u << u;
+      if (jt + u < cnt && order_key(x[u]) >= tau) f |= 1u << u;
     uint32_t tot;
-    uint32_t o = run + block_exclusive_scan<uint32_t, kPsThreads>(__popc(f), s_scan32, &tot);
+    uint32_t o = run + block_exclusive_scan<uint32_t, NT>(__popc(f), s_scan32, &tot);
 #pragma unroll
     for (int u = 0; u < kPsU; ++u)
-      if (f & (1u << u)) emit(o++, key[u], id[u]);
+      if (f & (1u << u)) emit(o++, order_key(x[u]), base + jt + u);
     run += tot;
+  };
+  float xa[kPsU], xb[kPsU];
+  load(xa, 0);
+  for (int j0 = 0; j0 < cnt; j0 += 2 * kPsU * NT) {
+    load(xb, j0 + kPsU * NT);
+    step(xa, j0);
+    if (j0 + kPsU * NT >= cnt) break;
+    load(xa, j0 + 2 * kPsU * NT);
+    step(xb, j0 + kPsU * NT);
   }
   return run;
 }
@@ -221,18 +247,19 @@ __device__ uint32_t ordered_compact(int n, Get get, Keep keep, Emit emit, uint32
 // the cut), and the radix digits run below the bits lo and hi share - the
 // keys in the window spread over the buckets even when a few keys far above
 // it (outliers) would otherwise crowd the bulk into one bucket.
+template <int NT>
 __device__ uint32_t lds_cut(const uint32_t* keys, int n, int64_t K, uint32_t lo, uint32_t hi,
                             PsShared& sh, int64_t* above_out) {
   const int tid = threadIdx.x, lane = tid & 63;
   uint32_t over = 0;
-  for (int i = tid; i < n; i += kPsThreads) over += keys[i] > hi ? 1u : 0u;
+  for (int i = tid; i < n; i += NT) over += keys[i] > hi ? 1u : 0u;
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) over += (uint32_t)__shfl_xor((int)over, m);
   if (lane == 0) sh.kand[tid >> 6] = over;
   __syncthreads();
   int64_t above = 0;
 #pragma unroll
-  for (int w = 0; w < kPsThreads / 64; ++w) above += sh.kand[w];
+  for (int w = 0; w < NT / 64; ++w) above += sh.kand[w];
   const uint32_t diff = lo ^ hi;
   const int common = diff ? __clz(diff) : 32;
   uint32_t cut = lo;                               // lo == hi: the window is one key
@@ -243,14 +270,14 @@ __device__ uint32_t lds_cut(const uint32_t* keys, int n, int64_t K, uint32_t lo,
       const int bits = pos < 12 ? pos : 12;
       const int shift = pos - bits;
       const uint32_t mask = (1u << bits) - 1u;
-      for (int i = tid; i < 4096; i += kPsThreads) sh.hist[i] = 0;
+      for (int i = tid; i < 4096; i += NT) sh.hist[i] = 0;
       __syncthreads();
-      for (int i = tid; i < n; i += kPsThreads) {
+      for (int i = tid; i < n; i += NT) {
         const uint32_t key = keys[i];
         if (key <= hi && key_hi(key, pos) == prefix) atomicAdd(&sh.hist[(key >> shift) & mask], 1u);
       }
       __syncthreads();
-      const int bk = vis_find<4096>(sh.hist, K, &above, sh.scan, &sh.b, &sh.above);
+      const int bk = vis_find<4096, NT>(sh.hist, K, &above, sh.scan, &sh.b, &sh.above);
       prefix = (prefix << bits) | (uint32_t)bk;
       pos = shift;
     }
@@ -263,10 +290,27 @@ __device__ uint32_t lds_cut(const uint32_t* keys, int n, int64_t K, uint32_t lo,
 // One workgroup per (interval, sequence-head): the cut of the interval's first
 // block, then the candidates of the interval (entries its last block sees with
 // a key at least that cut).
-__global__ __launch_bounds__(kPsThreads) void pyr_interval_kernel(PyrSelectArgs a) {
+constexpr int kPiThreads = 256;
+
+// Workgroup ids are dealt to the 8 dies round-robin. The interval kernels
+// renumber them so that each die takes whole heads: the passes over a head's
+// scores then hit that die's own L2. Within a head, late intervals (they see
+// the most entries) come first.
+__device__ __forceinline__ void die_major(int n_int, int nbh, int* iv, int* bh) {
+  const int total = n_int * nbh;
+  const int L = (int)blockIdx.x, x = L & 7, j = L >> 3;
+  const int q = total >> 3, r = total & 7;
+  const int idx = x * q + min(x, r) + j;
+  *bh = idx / n_int;
+  *iv = n_int - 1 - (idx - *bh * n_int);
+}
+
+__global__ __launch_bounds__(kPiThreads) void pyr_interval_kernel(PyrSelectArgs a) {
   __shared__ PsShared sh;
   __shared__ uint32_t c_key[kPsCap];
-  const int iv = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  int iv, bh;
+  die_major(a.n_int, a.B * a.H, &iv, &bh);
+  const int tid = threadIdx.x;
   const int b0 = iv * a.S, b1 = min(b0 + a.S, a.nblk) - 1;
   const int64_t slot = (int64_t)bh * a.n_int + iv;
   const VisRanges v1 = visible(a, b1);
@@ -279,7 +323,7 @@ __global__ __launch_bounds__(kPsThreads) void pyr_interval_kernel(PyrSelectArgs 
   uint32_t tau = 0;
   if (v0.total > a.K) {
     int64_t above;
-    tau = visible_cut(a, v0, sc, bh, sh, &above);
+    tau = visible_cut<kPiThreads>(a, v0, sc, bh, sh, &above);
   }
   uint2* out = a.cand + slot * kPsCap;
   uint32_t total = 0;
@@ -288,10 +332,8 @@ __global__ __launch_bounds__(kPsThreads) void pyr_interval_kernel(PyrSelectArgs 
     const int base = (int)v1.off[l];
     const uint32_t room = total < (uint32_t)kPsCap ? (uint32_t)kPsCap - total : 0u;
     uint2* o = out + min(total, (uint32_t)kPsCap);
-    total += ordered_compact(
-        v1.cnt[l],
-        [&](int j, uint32_t& key, int32_t& id) { key = order_key(p[j]); id = base + j; },
-        [&](uint32_t key, int32_t) { return key >= tau; },
+    total += compact_scores<kPiThreads>(
+        p, v1.cnt[l], base, tau,
         [&](uint32_t k, uint32_t key, int32_t id) {
           if (k < room) {
             o[k] = make_uint2(key, (uint32_t)id);
@@ -306,7 +348,7 @@ __global__ __launch_bounds__(kPsThreads) void pyr_interval_kernel(PyrSelectArgs 
   if (total <= (uint32_t)kPsCap) {
     __syncthreads();
     int64_t above;
-    tau_hi = lds_cut(c_key, (int)total, a.K, tau, 0xFFFFFFFFu, sh, &above);
+    tau_hi = lds_cut<kPiThreads>(c_key, (int)total, a.K, tau, 0xFFFFFFFFu, sh, &above);
   }
   if (tid == 0) {
     a.tau[slot] = tau;
@@ -318,6 +360,7 @@ __global__ __launch_bounds__(kPsThreads) void pyr_interval_kernel(PyrSelectArgs 
 // One block's selection by whole-workgroup passes over its visible scores:
 // every visible entry when at most K are visible, else the cut and the kept
 // flat ids in ascending order (strict, then the first ties).
+template <int NT>
 __device__ __forceinline__ void full_select(const PyrSelectArgs& a, int blk, int bh, PsShared& sh) {
   const int tid = threadIdx.x;
   const VisRanges v = visible(a, blk);
@@ -327,14 +370,14 @@ __device__ __forceinline__ void full_select(const PyrSelectArgs& a, int blk, int
   if (v.total <= K) {                      // every visible entry
     int64_t o = 0;
     for (int l = 0; l < v.nl; ++l) {
-      for (int j = tid; j < v.cnt[l]; j += kPsThreads) out[o + j] = (int32_t)(v.off[l] + j);
+      for (int j = tid; j < v.cnt[l]; j += NT) out[o + j] = (int32_t)(v.off[l] + j);
       o += v.cnt[l];
     }
     if (tid == 0) a.blk_count[(int64_t)bh * a.nblk + blk] = (int32_t)v.total;
     return;
   }
   int64_t above;
-  const uint32_t cut = visible_cut(a, v, sc, bh, sh, &above);
+  const uint32_t cut = visible_cut<NT>(a, v, sc, bh, sh, &above);
   const uint32_t need = (uint32_t)(K - above);        // ties kept, lowest flat ids first
 
   // ascending flat ids: strict (key > cut) and the first `need` ties; thread
@@ -343,7 +386,7 @@ __device__ __forceinline__ void full_select(const PyrSelectArgs& a, int blk, int
   for (int l = 0; l < v.nl; ++l) {
     const float* p = sc + v.off[l];
     const int cnt = v.cnt[l];
-    for (int j0 = 0; j0 < cnt; j0 += kPsU * kPsThreads) {
+    for (int j0 = 0; j0 < cnt; j0 += kPsU * NT) {
       const int jt = j0 + kPsU * tid;
       float x[kPsU];
 #pragma unroll
@@ -358,8 +401,8 @@ __device__ __forceinline__ void full_select(const PyrSelectArgs& a, int blk, int
         }
       }
       uint32_t tot_s, tot_t;
-      const uint32_t ex_s = block_exclusive_scan<uint32_t, kPsThreads>(__popc(sf), sh.scan32, &tot_s);
-      const uint32_t ex_t = block_exclusive_scan<uint32_t, kPsThreads>(__popc(tf), sh.scan32, &tot_t);
+      const uint32_t ex_s = block_exclusive_scan<uint32_t, NT>(__popc(sf), sh.scan32, &tot_s);
+      const uint32_t ex_t = block_exclusive_scan<uint32_t, NT>(__popc(tf), sh.scan32, &tot_t);
       uint32_t sb = s_run + ex_s, tb = t_run + ex_t;
 #pragma unroll
       for (int u = 0; u < kPsU; ++u) {
@@ -382,7 +425,7 @@ __device__ __forceinline__ void full_select(const PyrSelectArgs& a, int blk, int
 // (the most visible entries) first.
 __global__ __launch_bounds__(kPsThreads) void pyr_select_kernel(PyrSelectArgs a) {
   __shared__ PsShared sh;
-  full_select(a, a.nblk - 1 - (int)blockIdx.x, blockIdx.y, sh);
+  full_select<kPsThreads>(a, a.nblk - 1 - (int)blockIdx.x, blockIdx.y, sh);
 }
 
 // ---------------------------------------------------------------- one wave per block
@@ -398,7 +441,8 @@ __global__ __launch_bounds__(kPsThreads) void pyr_select_kernel(PyrSelectArgs a)
 //  * the kept ids are written in ascending flat id, positions from ballots.
 // An interval with more candidates than fit runs the whole-workgroup passes
 // for each of its blocks.
-constexpr int kPwWaves = kPsThreads / 64;
+constexpr int kPwWaves = 8;
+constexpr int kPwThreads = kPwWaves * 64;
 constexpr int kPwBuckets = 256;
 
 union PwShared {
@@ -550,22 +594,24 @@ __device__ __forceinline__ void wave_select(const PyrSelectArgs& a, const PwShar
   if (lane == 0) a.blk_count[(int64_t)bh * a.nblk + blk] = (int32_t)K;
 }
 
-__global__ __launch_bounds__(kPsThreads) void pyr_block_select_kernel(PyrSelectArgs a) {
+__global__ __launch_bounds__(kPwThreads) void pyr_block_select_kernel(PyrSelectArgs a) {
   __shared__ PwShared s;
-  const int iv = a.n_int - 1 - (int)blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  int iv, bh;
+  die_major(a.n_int, a.B * a.H, &iv, &bh);
+  const int tid = threadIdx.x;
   const int lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t slot = (int64_t)bh * a.n_int + iv;
   const int b0 = iv * a.S, b1 = min(b0 + a.S, a.nblk) - 1;
   const int ncand = a.cand_len[slot];
   if (ncand < 0) {                                     // too many candidates
     for (int blk = b1; blk >= b0; --blk) {
-      full_select(a, blk, bh, s.ps);
+      full_select<kPwThreads>(a, blk, bh, s.ps);
       __syncthreads();
     }
     return;
   }
   const uint2* cp = a.cand + slot * kPsCap;
-  for (int i = tid; i < ncand; i += kPsThreads) {
+  for (int i = tid; i < ncand; i += kPwThreads) {
     const uint2 e = cp[i];
     s.w.key[i] = e.x;
     s.w.id[i] = (int32_t)e.y;
@@ -584,8 +630,8 @@ hipError_t launch_pyramid_select(const PyrSelectArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(pyr_prefix_kernel, dim3(a.B * a.H), dim3(1024), 0, s, a);
   if (a.n_int > 0) {
     if (a.S < 1 || !a.tau || !a.cand_len || !a.cand) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(pyr_interval_kernel, dim3(a.n_int, a.B * a.H), dim3(kPsThreads), 0, s, a);
-    hipLaunchKernelGGL(pyr_block_select_kernel, dim3(a.n_int, a.B * a.H), dim3(kPsThreads), 0, s, a);
+    hipLaunchKernelGGL(pyr_interval_kernel, dim3(a.n_int * a.B * a.H), dim3(kPiThreads), 0, s, a);
+    hipLaunchKernelGGL(pyr_block_select_kernel, dim3(a.n_int * a.B * a.H), dim3(kPwThreads), 0, s, a);
   } else {
     hipLaunchKernelGGL(pyr_select_kernel, dim3(a.nblk, a.B * a.H), dim3(kPsThreads), 0, s, a);
   }
