@@ -224,6 +224,25 @@ def run_decode(args, torch, sa, workloads, workload=None, steps=None, warmup=Non
     t_kernel = k0.elapsed_time(k1) / steps * 1e-3
     log(f"[bench] {cfg.name}: timed {steps} steps: {t_step * 1e6:.1f} us/step, "
         f"attention call {t_kernel * 1e6:.1f} us")
+    # the spread: one event pair per step and per attention call, in a pass
+    # of its own after the timed ones (the events add a little per step)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        x = insts[i % len(insts)]
+        ev[i][0].record(stream)
+        if use_graph:
+            x.g_sel.replay()
+        else:
+            x.index_and_select()
+        ev[i][1].record(stream)
+        if use_graph:
+            x.g_dec.replay()
+        else:
+            x.decode()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    per_step = [e[0].elapsed_time(e[2]) * 1e3 for e in ev]
+    per_call = [e[1].elapsed_time(e[2]) * 1e3 for e in ev]
     kinds = cfg.head_kind()
     attn_b, step_b = 0, 0
     sel_frac = []
@@ -257,6 +276,9 @@ def run_decode(args, torch, sa, workloads, workload=None, steps=None, warmup=Non
         "step_hbm_gbps": step_b / t_step / 1e9,
         "step_bytes": step_b,
         "selected_frac_mean": (sum(sel_frac) / len(sel_frac)) if sel_frac else None,
+        "spread_us": {"step": percentiles(per_step), "attention_call": percentiles(per_call),
+                      "note": "one event pair per step in a separate pass; rotated instances "
+                              "(cold in the 256 MB Infinity Cache)"},
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": traffic_record(kernel, cfg.name, sha),
@@ -268,6 +290,13 @@ def run_decode(args, torch, sa, workloads, workload=None, steps=None, warmup=Non
     del insts
     torch.cuda.empty_cache()
     return res
+
+
+def percentiles(xs):
+    """p10 / p50 / p90 of a list of times."""
+    ys = sorted(xs)
+    at = lambda q: ys[min(len(ys) - 1, int(round(q * (len(ys) - 1))))]
+    return {"p10": at(0.1), "p50": at(0.5), "p90": at(0.9)}
 
 
 def blas_threads():
