@@ -171,13 +171,14 @@ struct PsShared {
   int b;
   int64_t above;
   uint32_t kand[16], kor[16];
+  uint32_t n;
 };
 
 // The cut over the visible prefixes v of one head: the key of the K-th
 // largest visible score; *above receives how many visible keys exceed it.
 template <int NT>
 __device__ uint32_t visible_cut(const PyrSelectArgs& a, const VisRanges& v, const float* sc, int bh,
-                                PsShared& sh, int64_t* above_out) {
+                                PsShared& sh, int64_t* above_out, int64_t target) {
   const uint2 pf = a.prefix[bh];
   const uint32_t diff = pf.x ^ pf.y;
   const int common = diff ? __clz(diff) : 32;
@@ -193,7 +194,7 @@ __device__ uint32_t visible_cut(const PyrSelectArgs& a, const VisRanges& v, cons
       __syncthreads();
       vis_hist<NT>(sc, v, prefix, pos, shift, bits, sh.hist);
       __syncthreads();
-      const int bk = vis_find<4096, NT>(sh.hist, a.K, &above, sh.scan, &sh.b, &sh.above);
+      const int bk = vis_find<4096, NT>(sh.hist, target, &above, sh.scan, &sh.b, &sh.above);
       prefix = (prefix << bits) | (uint32_t)bk;
       pos = shift;
     }
@@ -201,6 +202,57 @@ __device__ uint32_t visible_cut(const PyrSelectArgs& a, const VisRanges& v, cons
   }
   *above_out = above;
   return cut;
+}
+
+// Every visible key at least lb, gathered into keys[0, cap) in no particular
+// order (one LDS atomic per wave and load step); returns how many there are
+// (all are counted, the first cap stored).
+template <int NT>
+__device__ uint32_t collect_at_least(const float* sc, const VisRanges& v, uint32_t lb, uint32_t* keys,
+                                     int cap, uint32_t* s_n) {
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x == 0) *s_n = 0;
+  __syncthreads();
+  for (int l = 0; l < v.nl; ++l) {
+    const float* p = sc + v.off[l];
+    const int cnt = v.cnt[l];
+    if (cnt <= 0) continue;
+    auto load = [&](float (&x)[kPsU], int j0) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < kPsU; ++u) {
+        const int j = j0 + u * NT + threadIdx.x;
+        x[u] = p[j < cnt ? j : cnt - 1];
+      }
+    };
+    auto put = [&](const float (&x)[kPsU], int j0) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < kPsU; ++u) {
+        const int j = j0 + u * NT + threadIdx.x;
+        const uint32_t key = order_key(x[u]);
+        const bool keep = j < cnt && key >= lb;
+        const uint64_t m = __ballot(keep);
+        if (m) {
+          uint32_t base = 0;
+          if (lane == 0) base = atomicAdd(s_n, (uint32_t)__popcll(m));
+          base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+          const uint32_t pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          if (keep && pos < (uint32_t)cap) keys[pos] = key;
+        }
+      }
+    };
+    float xa[kPsU], xb[kPsU];
+    load(xa, 0);
+    for (int j0 = 0; j0 < cnt; j0 += 2 * kPsU * NT) {
+      load(xb, j0 + kPsU * NT);
+      put(xa, j0);
+      if (j0 + kPsU * NT >= cnt) break;
+      load(xa, j0 + 2 * kPsU * NT);
+      put(xb, j0 + kPsU * NT);
+    }
+  }
+  __syncthreads();
+  return *s_n;
 }
 
 // Ordered compaction of the scores p[0, cnt) whose key is at least tau: each
@@ -322,8 +374,30 @@ __global__ __launch_bounds__(kPiThreads) void pyr_interval_kernel(PyrSelectArgs 
   const VisRanges v0 = visible(a, b0);
   uint32_t tau = 0;
   if (v0.total > a.K) {
+    // A lower bound first: a visible entry of the top level carries its
+    // score down a chain of one entry per level (the child holding its max),
+    // all visible and all with that score, so the ceil(K/L)-th largest
+    // visible top-level score has at least K visible entries at or above it.
+    // The keys reaching the bound are gathered in LDS and the exact cut taken
+    // there; with too many of them (or too few top-level entries) the radix
+    // passes run over every visible score.
     int64_t above;
-    tau = visible_cut<kPiThreads>(a, v0, sc, bh, sh, &above);
+    bool done = false;
+    const int L = v0.nl;
+    const int64_t tk = (a.K + L - 1) / L;
+    if (L > 1 && v0.cnt[L - 1] >= tk) {
+      VisRanges vt = v0;
+      for (int l = 0; l < L - 1; ++l) vt.cnt[l] = 0;
+      vt.total = v0.cnt[L - 1];
+      const uint32_t lb = visible_cut<kPiThreads>(a, vt, sc, bh, sh, &above, tk);
+      const uint32_t n = collect_at_least<kPiThreads>(sc, v0, lb, c_key, kPsCap, &sh.n);
+      if (n <= (uint32_t)kPsCap) {
+        tau = lds_cut<kPiThreads>(c_key, (int)n, a.K, lb, 0xFFFFFFFFu, sh, &above);
+        done = true;
+      }
+      __syncthreads();
+    }
+    if (!done) tau = visible_cut<kPiThreads>(a, v0, sc, bh, sh, &above, a.K);
   }
   uint2* out = a.cand + slot * kPsCap;
   uint32_t total = 0;
@@ -377,7 +451,7 @@ __device__ __forceinline__ void full_select(const PyrSelectArgs& a, int blk, int
     return;
   }
   int64_t above;
-  const uint32_t cut = visible_cut<NT>(a, v, sc, bh, sh, &above);
+  const uint32_t cut = visible_cut<NT>(a, v, sc, bh, sh, &above, a.K);
   const uint32_t need = (uint32_t)(K - above);        // ties kept, lowest flat ids first
 
   // ascending flat ids: strict (key > cut) and the first `need` ties; thread
