@@ -14,11 +14,13 @@
 // Scores are ranked on the raw dot product: dividing by sqrt(d) does not
 // change the order.
 //
-// One 256-thread workgroup per (KV group, sequence).  Rows are scored with 16
-// lanes each (d/16 elements per lane, a 16-lane DPP reduction, four rounds of
-// loads in flight), chunk scores stay in LDS, and the top chunks come from
-// per-wave arg-max rounds over (score key, inverted index) 64-bit keys
-// merged by one wave - no block barrier per extracted chunk.
+// One 1024-thread workgroup per (KV group, sequence): there are fewer of these
+// than compute units, so each takes a whole unit and keeps as many summary
+// rows in flight as it can.  Rows are scored with 16 lanes each (d/16
+// elements per lane, a 16-lane DPP reduction, eight rounds of loads in
+// flight), chunk scores stay in LDS, and the top chunks come from per-wave
+// arg-max rounds over (score key, inverted index) 64-bit keys merged by one
+// wave - no block barrier per extracted chunk.
 #include <algorithm>
 
 #include "args.hpp"
@@ -26,7 +28,7 @@
 
 namespace sa {
 
-constexpr int kRouteThreads = 256;
+constexpr int kRouteThreads = 1024;
 constexpr int kMaxRoutedGroups = 4096;     // top_chunks * top_groups
 
 template <int CTRL>
@@ -44,28 +46,29 @@ __device__ __forceinline__ float row16_sum_r(float v) {
 
 // Scores qbar . rows[r] for r in [0, nrows) into out[r]; rows are d wide.
 // A wave scores 4 rows per round (16 lanes per row) and keeps the loads of
-// 4 rounds in flight.
+// U rounds in flight.
 template <typename T, int D>
 __device__ void score_rows(const void* base, int64_t row_of0, int nrows, const float* s_q,
                            float* out, const int* row_map) {
   constexpr int EPL = D / 16;
-  constexpr int U = 4;
+  constexpr int U = 8;
+  constexpr int NW = kRouteThreads / 64;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int sub = lane & 15, rg = lane >> 4;
   float q[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) q[e] = s_q[sub * EPL + e];
-  for (int r0 = 0; r0 < nrows; r0 += 16 * U) {
+  for (int r0 = 0; r0 < nrows; r0 += 4 * NW * U) {
     float kv[U][EPL];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int r = min(r0 + u * 16 + wid * 4 + rg, nrows - 1);
+      const int r = min(r0 + u * 4 * NW + wid * 4 + rg, nrows - 1);
       const int64_t row = row_map ? (int64_t)row_map[r] : (row_of0 + r);
       VecLoad<T, EPL>::run(base, row * D + sub * EPL, kv[u]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int r = r0 + u * 16 + wid * 4 + rg;
+      const int r = r0 + u * 4 * NW + wid * 4 + rg;
       float p = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) p = fmaf(q[e], kv[u][e], p);
@@ -92,6 +95,24 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
   return ((uint64_t)hi << 32) | lo;
+}
+
+// Bitonic sort of one 64-bit key per lane across the wave, largest in lane 0.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v, int lane) {
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, j);
+      const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), j);
+      const uint64_t o = ((uint64_t)hi << 32) | lo;
+      // within blocks of k lanes (all descending at the last stage) the
+      // lower lane of a pair keeps the larger key
+      const bool keep_max = ((lane & k) == 0) == ((lane & j) == 0);
+      v = keep_max ? (o > v ? o : v) : (o < v ? o : v);
+    }
+  }
+  return v;
 }
 
 template <typename T, int D>
@@ -123,12 +144,30 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   if (nT > 0) {
     score_rows<T, D>(a.chunk_sum, bg * a.n_cs_cap + c_lo, ncand, s_q, dyn, nullptr);
     __syncthreads();
-    // level 1: every wave extracts the top nT of its candidates (i = tid +
-    // 256 k) by nT rounds of wave arg-max over (score key, inverted index)
-    // keys; wave 0 then takes the top nT of those 4 nT in order
-    {
+    if (nT <= 16 && ncand <= kRouteThreads) {
+      // level 1 with at most one candidate per thread: every wave sorts its
+      // 64 (score key, inverted index) keys, four waves sort the waves' top
+      // 16s four waves at a time, and one wave the four results
       const int lane = tid & 63, wid = tid >> 6;
-      uint64_t done_mask = 0;                        // bit k: candidate tid + 256 k taken
+      uint64_t k1 = tid < ncand ? score_key(dyn[tid], tid) : 0ull;     // keys are never 0
+      k1 = wave_sort_desc(k1, lane);
+      if (lane < 16) s_wtop[wid][lane] = k1;
+      __syncthreads();
+      uint64_t k2 = 0;
+      if (wid < 4) k2 = wave_sort_desc(s_wtop[4 * wid + (lane >> 4)][lane & 15], lane);
+      __syncthreads();
+      if (wid < 4 && lane < 16) s_wtop[wid][lane] = k2;
+      __syncthreads();
+      if (wid == 0) {
+        const uint64_t k3 = wave_sort_desc(s_wtop[lane >> 4][lane & 15], lane);
+        if (lane < nT) s_chunks[lane] = c_lo + (int)(0xFFFFFFFFu - (uint32_t)k3);
+      }
+    } else {
+    // level 1: every wave extracts the top nT of its candidates (i = tid +
+    // kRouteThreads k) by nT rounds of wave arg-max over (score key, inverted
+    // index) keys; wave 0 then takes the top nT of those in order
+      const int lane = tid & 63, wid = tid >> 6;
+      uint64_t done_mask = 0;                        // bit k: candidate tid + kRouteThreads k taken
       for (int r = 0; r < nT; ++r) {
         uint64_t best = 0;
         for (int k = 0, i = tid; i < ncand; ++k, i += kRouteThreads)
