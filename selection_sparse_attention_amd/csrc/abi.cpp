@@ -354,6 +354,8 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
     const bool has_cand = kappa - p->local_chunks > p->sink_chunks;
     if (!b->q || !b->sel_idx || !b->sel_count) return SA_ERR_INVALID_ARG;
     if (has_cand && (!b->chunk_sum || !b->group_sum)) return SA_ERR_INVALID_ARG;
+    if (!aligned16(b->q) || (has_cand && (!aligned16(b->chunk_sum) || !aligned16(b->group_sum))))
+      return SA_ERR_INVALID_ARG;
     sa::RouteArgs a{};
     a.q = b->q; a.chunk_sum = b->chunk_sum; a.group_sum = b->group_sum;
     a.sel_idx = b->sel_idx; a.sel_count = b->sel_count;

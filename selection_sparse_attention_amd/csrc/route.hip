@@ -44,20 +44,18 @@ __device__ __forceinline__ float row16_sum_r(float v) {
   return v;
 }
 
-// Scores qbar . rows[r] for r in [0, nrows) into out[r]; rows are d wide.
-// A wave scores 4 rows per round (16 lanes per row) and keeps the loads of
-// U rounds in flight.
+// Scores qbar . rows[r] for r in [0, nrows) into out[r]; rows are d wide,
+// and q holds this lane's d/16 elements of qbar (lane l: elements
+// (l % 16) d/16 ..). A wave scores 4 rows per round (16 lanes per row) and
+// keeps the loads of U rounds in flight.
 template <typename T, int D>
-__device__ void score_rows(const void* base, int64_t row_of0, int nrows, const float* s_q,
+__device__ void score_rows(const void* base, int64_t row_of0, int nrows, const float (&q)[D / 16],
                            float* out, const int* row_map) {
   constexpr int EPL = D / 16;
   constexpr int U = 8;
   constexpr int NW = kRouteThreads / 64;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int sub = lane & 15, rg = lane >> 4;
-  float q[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) q[e] = s_q[sub * EPL + e];
   for (int r0 = 0; r0 < nrows; r0 += 4 * NW * U) {
     float kv[U][EPL];
 #pragma unroll
@@ -118,7 +116,6 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v, int lane) {
 template <typename T, int D>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   extern __shared__ float dyn[];                 // chunk scores, then group scores
-  __shared__ float s_q[D];
   __shared__ int s_chunks[256], s_sorted[256];
   __shared__ uint64_t s_wtop[kRouteThreads / 64][64];
   __shared__ int s_groups[kMaxRoutedGroups];
@@ -133,16 +130,28 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   const int nT = min(a.top_chunks, ncand);
   const int TG = a.top_groups;
 
-  for (int e = tid; e < D; e += kRouteThreads) {
-    float s = 0.f;
-    for (int h = 0; h < a.G; ++h) s += Elem<T>::load(a.q, ((int64_t)b * a.Hq + g * a.G + h) * D + e);
-    s_q[e] = s * (1.0f / (float)a.G);
+  // this lane's share of qbar, in registers (its loads overlap the first
+  // summary rows' loads: no barrier in between)
+  constexpr int EPL = D / 16;
+  float qv[EPL];
+  {
+    const int sub = tid & 15;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qv[e] = 0.f;
+    for (int h = 0; h < a.G; ++h) {
+      float x[EPL];
+      VecLoad<T, EPL>::run(a.q, ((int64_t)b * a.Hq + g * a.G + h) * D + sub * EPL, x);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qv[e] += x[e];
+    }
+    const float invG = 1.0f / (float)a.G;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qv[e] *= invG;
   }
-  __syncthreads();
 
   const int64_t bg = (int64_t)b * a.Hkv + g;
   if (nT > 0) {
-    score_rows<T, D>(a.chunk_sum, bg * a.n_cs_cap + c_lo, ncand, s_q, dyn, nullptr);
+    score_rows<T, D>(a.chunk_sum, bg * a.n_cs_cap + c_lo, ncand, qv, dyn, nullptr);
     __syncthreads();
     if (nT <= 16 && ncand <= kRouteThreads) {
       // level 1 with at most one candidate per thread: every wave sorts its
@@ -211,7 +220,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     for (int i = tid; i < nT * gpc; i += kRouteThreads)
       s_rowmap[i] = (int)(bg * a.n_gs_cap + (int64_t)s_sorted[i / gpc] * gpc + (i % gpc));
     __syncthreads();
-    score_rows<T, D>(a.group_sum, 0, nT * gpc, s_q, dyn, s_rowmap);
+    score_rows<T, D>(a.group_sum, 0, nT * gpc, qv, dyn, s_rowmap);
     __syncthreads();
     if (tid < nT) {
       // top TG of this chunk's gpc groups, then ascending
