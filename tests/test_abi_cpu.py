@@ -125,6 +125,13 @@ def test_select_topk_and_route_validation():
     assert _select(_decode_params(top_chunks=0, **routed), _full_bufs(),
                    sa.SEL_ROUTE2)[0] == sa.SA_ERR_INVALID_ARG
     assert _select(_decode_params(), _full_bufs(), 17)[0] == sa.SA_ERR_INVALID_ARG
+    # the routed select's vector loads need 16-byte aligned query and summaries
+    p = _decode_params(**routed)
+    _, need = _select(p, _full_bufs(), sa.SEL_ROUTE2)
+    for name in ("q", "chunk_sum", "group_sum"):
+        b = _full_bufs()
+        setattr(b, name, FAKE + 8)
+        assert _select(p, b, sa.SEL_ROUTE2, FAKE, need)[0] == sa.SA_ERR_INVALID_ARG, name
 
 
 def test_missing_buffers_are_rejected():
