@@ -142,8 +142,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     }
   }
 
-  // ---- gather roles: K (thread -> key t/8, 16 dims at 16*(t%8)),
-  //      V (thread -> keys 2(t%16), 2(t%16)+1, 8 dims at 8*(t/16)).
+  // ---- gather roles: K (thread -> key t/8, dims 8 (t%8) .. +8 and 64 + 8 (t%8)
+  //      .. +8: the eight threads of a key write 128 contiguous bytes per
+  //      store, which spreads them over all LDS banks), V (thread -> keys
+  //      2(t%16), 2(t%16)+1, 8 dims at 8*(t/16)).
   const int gk_key = tid >> 3, gk_seg = tid & 7;
   const int gv_kp = tid & 15, gv_seg = tid >> 4;
   auto row_ptr = [](uint32_t r, const uint16_t* b0, const uint16_t* bc) -> const uint16_t* {
@@ -158,15 +160,15 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     const uint32_t lk = s_seq[(x + 1) * kKT + gk_key];
     const uint2 lv = *reinterpret_cast<const uint2*>(&s_seq[x * kKT + 2 * gv_kp]);
     const uint16_t* pk = row_ptr(lk, kb, pkb);
-    r.k0 = *reinterpret_cast<const u32x4p*>(pk + 16 * gk_seg);
-    r.k1 = *reinterpret_cast<const u32x4p*>(pk + 16 * gk_seg + 8);
+    r.k0 = *reinterpret_cast<const u32x4p*>(pk + 8 * gk_seg);
+    r.k1 = *reinterpret_cast<const u32x4p*>(pk + 8 * gk_seg + 64);
     r.v0 = *reinterpret_cast<const u32x4p*>(row_ptr(lv.x, vb, pvb) + 8 * gv_seg);
     r.v1 = *reinterpret_cast<const u32x4p*>(row_ptr(lv.y, vb, pvb) + 8 * gv_seg);
   };
   auto stash_k = [&](int buf, const u32x4p& k0, const u32x4p& k1) __attribute__((always_inline)) {
-    uint16_t* kdst = s_k[buf] + gk_key * kKRow + 16 * gk_seg;
+    uint16_t* kdst = s_k[buf] + gk_key * kKRow + 8 * gk_seg;
     *reinterpret_cast<u32x4p*>(kdst) = k0;
-    *reinterpret_cast<u32x4p*>(kdst + 8) = k1;
+    *reinterpret_cast<u32x4p*>(kdst + 64) = k1;
   };
   // set x: K of tile x + 1 into K buffer (x + 1) & 1, V of tile x into V
   // buffer x & 1
@@ -314,8 +316,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   lds_barrier();                                    // s_seq complete
   {
     const uint16_t* pk = row_ptr(s_seq[gk_key], kb, pkb);
-    const u32x4p k0 = *reinterpret_cast<const u32x4p*>(pk + 16 * gk_seg);
-    const u32x4p k1 = *reinterpret_cast<const u32x4p*>(pk + 16 * gk_seg + 8);
+    const u32x4p k0 = *reinterpret_cast<const u32x4p*>(pk + 8 * gk_seg);
+    const u32x4p k1 = *reinterpret_cast<const u32x4p*>(pk + 8 * gk_seg + 64);
     stash_k(0, k0, k1);
   }
   Rows ra, rb;
