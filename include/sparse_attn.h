@@ -233,10 +233,11 @@ int32_t sparse_attn_decode(const sa_params* params, const sa_buffers* bufs,
  * v_cache for level 0, of pyr_k / pyr_v above) plus the block's own level-0
  * keys up to and including i, with scale 1/sqrt(d); the fp32 result is
  * written to out row i.  Requires n_q_heads == n_kv_heads, dtype bf16,
- * head_dim 128, q_block 128 and block_top_k <= 8192 (SA_ERR_UNSUPPORTED
- * otherwise).  blk_idx holds flat ids as SA_SEL_PYRAMID_TOPK writes them; an
- * id outside [0, n_ctx + coarse entries) is never dereferenced and acts as a
- * zero key and value row.  Needs a workspace.
+ * head_dim 128, q_block 128, block_top_k <= 8192 and n_ctx < 2^23
+ * (SA_ERR_UNSUPPORTED otherwise).  blk_idx holds flat ids as
+ * SA_SEL_PYRAMID_TOPK writes them; an id outside [0, n_ctx + coarse entries)
+ * is never dereferenced: level-0 row 0 is read in its place, so its
+ * contribution is unspecified.  Needs a workspace.
  */
 int32_t sparse_attn_prefill_chunked(const sa_params* params, const sa_buffers* bufs,
                                     void* workspace, size_t* workspace_bytes,

@@ -433,6 +433,7 @@ int32_t sparse_attn_prefill_chunked(const sa_params* p, const sa_buffers* b, voi
   if (p->dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
   if (p->head_dim != 128 || p->q_block != 128) return SA_ERR_UNSUPPORTED;
   if (p->block_top_k > 8192) return SA_ERR_UNSUPPORTED;   // the selection is staged in LDS
+  if (p->n_ctx >= (1 << 23)) return SA_ERR_UNSUPPORTED;   // rows are staged as 32-bit byte offsets
   Carver c(ws);
   c.take<uint32_t>(1);
   if ((st = workspace_gate(ws, ws_bytes, c.size()))) return st < 0 ? st : SA_OK;

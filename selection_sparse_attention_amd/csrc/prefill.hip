@@ -42,7 +42,12 @@ constexpr int kVRow = 36;               // V^T tile row stride (bf16 elements) =
 constexpr int kListMax = 8192;          // largest block_top_k the kernel stages in LDS
 constexpr int kSeqMax = kListMax + 128 + 4 * kKT;   // + own keys + tail the gathers run past
 constexpr uint32_t kCoarse = 0x80000000u;           // staged entry: coarse row flag
+constexpr int kRowBytes = kD * 2;                   // one bf16 row of K or V
+constexpr int kMaxRows = 1 << 23;                   // rows addressable by a staged byte offset
 constexpr float kLazy = 8.f;            // log2 headroom before the softmax reference moves
+// initial softmax reference: finite, so that a row with no visible key yet
+// gives 2^(-inf - m) = 0 rather than 2^(-inf + inf)
+constexpr float kMInit = -1e30f;
 
 typedef float f32x2p __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2p __attribute__((ext_vector_type(2)));
@@ -53,11 +58,20 @@ __device__ __forceinline__ uint32_t pk_bf16(float x, float y) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2p){x, y}, bf16x2p));
 }
 
-// max of two scores by a compare and select: fmaxf would first quiet each
-// operand that the compiler cannot show to be canonical (a value that comes
-// back from a lane swap), one extra instruction per operand; scores are
-// never NaN
-__device__ __forceinline__ float max_raw(float a, float b) { return a > b ? a : b; }
+// max of two or three scores as one instruction: fmaxf would first quiet
+// each operand that the compiler cannot show to be canonical (a matrix-core
+// result, a value that comes back from a lane swap), one extra instruction
+// per operand; scores are never NaN
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 
 // max over the four lanes l16 + 16 jg (jg = 0..3) that hold one query's
 // scores: a lane-swap across the wave's halves, then one across neighbouring
@@ -120,7 +134,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     }
   }
 
-  // ---- the block's key sequence, staged once in LDS as row references:
+  // ---- the block's key sequence, staged once in LDS as row byte offsets:
   //      selected entry e < c_sel (a flat id: level-0 row, or coarse row
   //      flagged kCoarse), then the block's own level-0 keys q0 .. q0+nq-1,
   //      then row 0 for the tail that the two-ahead gathers run past (masked
@@ -133,10 +147,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
       uint32_t r = 0u;
       if (e < c_sel) {
         const int f = list[e];
-        if ((unsigned)f < (unsigned)a.N) r = (uint32_t)f;
-        else if ((unsigned)(f - a.N) < (unsigned)a.Nc) r = (uint32_t)(f - a.N) | kCoarse;
+        if ((unsigned)f < (unsigned)a.N) r = (uint32_t)f * kRowBytes;
+        else if ((unsigned)(f - a.N) < (unsigned)a.Nc) r = (uint32_t)(f - a.N) * kRowBytes | kCoarse;
       } else if (e < T) {
-        r = (uint32_t)(q0 + e - c_sel);
+        r = (uint32_t)(q0 + e - c_sel) * kRowBytes;
       }
       s_seq[e] = r;
     }
@@ -148,9 +162,15 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   //      2(t%16), 2(t%16)+1, 8 dims at 8*(t/16)).
   const int gk_key = tid >> 3, gk_seg = tid & 7;
   const int gv_kp = tid & 15, gv_seg = tid >> 4;
-  auto row_ptr = [](uint32_t r, const uint16_t* b0, const uint16_t* bc) -> const uint16_t* {
-    const uint16_t* base = (r & kCoarse) ? bc : b0;
-    return base + (size_t)(r & ~kCoarse) * kD;
+  // a staged entry is a row's byte offset, the coarse flag in its top bit;
+  // the bases already point at this thread's dims
+  const char* k_seg = reinterpret_cast<const char*>(kb + 8 * gk_seg);
+  const char* pk_seg = reinterpret_cast<const char*>(pkb + 8 * gk_seg);
+  const char* v_seg = reinterpret_cast<const char*>(vb + 8 * gv_seg);
+  const char* pv_seg = reinterpret_cast<const char*>(pvb + 8 * gv_seg);
+  auto row_ptr = [](uint32_t r, const char* b0, const char* bc) -> const u32x4p* {
+    const char* base = ((int32_t)r < 0) ? bc : b0;
+    return reinterpret_cast<const u32x4p*>(base + (r & ~kCoarse));
   };
   // one set of loads for this thread: the K rows of tile x + 1 and the V rows
   // of tile x (K runs a tile ahead: its product is issued a tile early)
@@ -159,11 +179,11 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   auto gather = [&](int x, Rows& r) __attribute__((always_inline)) {
     const uint32_t lk = s_seq[(x + 1) * kKT + gk_key];
     const uint2 lv = *reinterpret_cast<const uint2*>(&s_seq[x * kKT + 2 * gv_kp]);
-    const uint16_t* pk = row_ptr(lk, kb, pkb);
-    r.k0 = *reinterpret_cast<const u32x4p*>(pk + 8 * gk_seg);
-    r.k1 = *reinterpret_cast<const u32x4p*>(pk + 8 * gk_seg + 64);
-    r.v0 = *reinterpret_cast<const u32x4p*>(row_ptr(lv.x, vb, pvb) + 8 * gv_seg);
-    r.v1 = *reinterpret_cast<const u32x4p*>(row_ptr(lv.y, vb, pvb) + 8 * gv_seg);
+    const u32x4p* pk = row_ptr(lk, k_seg, pk_seg);
+    r.k0 = pk[0];
+    r.k1 = pk[8];
+    r.v0 = *row_ptr(lv.x, v_seg, pv_seg);
+    r.v1 = *row_ptr(lv.y, v_seg, pv_seg);
   };
   auto stash_k = [&](int buf, const u32x4p& k0, const u32x4p& k1) __attribute__((always_inline)) {
     uint16_t* kdst = s_k[buf] + gk_key * kKRow + 8 * gk_seg;
@@ -188,13 +208,22 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   };
 
   // ---- running state for queries 32w + 16nt + l16
-  float m[2] = {-INFINITY, -INFINITY}, lpart[2] = {0.f, 0.f};
+  float m[2] = {kMInit, kMInit}, lpart[2] = {0.f, 0.f};
   f32x4p o[8][2];                                   // O^T[d = 16 dt + 4 jg + i][q]
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) o[dt][nt] = (f32x4p){0.f, 0.f, 0.f, 0.f};
   const float sc = a.scale_log2;
+  // packed bf16 pairs (-1, 0), (0, -1) and (1, 1) for the dot2 steps of the
+  // softmax, held in registers: as instruction constants the compiler may
+  // encode one as an inline float constant, which this instruction need not
+  // read as the same pair
+  uint32_t c_neg_lo = 0x0000BF80u, c_neg_hi = 0xBF800000u, c_ones = 0x3F803F80u;
+  asm volatile("" : "+v"(c_neg_lo), "+v"(c_neg_hi), "+v"(c_ones));
+  const bf16x2p neg_lo = __builtin_bit_cast(bf16x2p, c_neg_lo);
+  const bf16x2p neg_hi = __builtin_bit_cast(bf16x2p, c_neg_hi);
+  const bf16x2p ones = __builtin_bit_cast(bf16x2p, c_ones);
 
   // S^T[key = 16 mt + 4 jg + i][q = 16 nt + l16] of the tile in K buffer kbuf
   auto qk = [&](int kbuf, f32x4p (&s)[2][2]) __attribute__((always_inline)) {
@@ -242,54 +271,62 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
           }
       }
     }
-    // online softmax per query (log2 domain: p = 2^(s sc - m)); P^T
-    // fragments as a bf16 high part and a bf16 remainder (the weights keep
-    // ~16 bits through the second product)
-    uint4 ph[2], pl[2];
-    float alpha[2];
+    // online softmax per query (log2 domain: p = 2^(s sc - m)).  A query's
+    // reference m moves only when the tile's max exceeds it by more than 2^8
+    // (p stays <= 256, far from overflow), so the accumulators are rescaled
+    // rarely, on a path the whole wave skips otherwise; the final
+    // normalisation divides the scale out
+    float tmax[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      float tmax = s[0][nt][0];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[mt][nt][i]);
-      tmax = max_over_lane_groups(tmax);
-      // the reference moves only when the tile's max exceeds it by more than
-      // 2^8 (p stays <= 256, far from overflow), so the accumulators are
-      // rescaled rarely; the final normalisation divides the scale out
-      const float cand = tmax * sc;
-      const float mn = (cand > m[nt] + kLazy) ? cand : m[nt];
-      const float msub = (mn == -INFINITY) ? 0.f : mn;   // a fully masked row stays at p = 0
-      alpha[nt] = (mn == m[nt]) ? 1.f : __builtin_amdgcn_exp2f(m[nt] - msub);
-      m[nt] = mn;
-      float p[8];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[4 * mt + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][nt][i], sc, -msub));
-      float ps = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) ps += p[j];
-      lpart[nt] = lpart[nt] * alpha[nt] + ps;
-      uint32_t hw[4], lw[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t h = pk_bf16(p[2 * j], p[2 * j + 1]);
-        const float r0 = p[2 * j] - __builtin_bit_cast(float, h << 16);
-        const float r1 = p[2 * j + 1] - __builtin_bit_cast(float, h & 0xFFFF0000u);
-        hw[j] = h;
-        lw[j] = pk_bf16(r0, r1);
-      }
-      ph[nt] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      pl[nt] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      float t = max3_raw(s[0][nt][0], s[0][nt][1], s[0][nt][2]);
+      t = max3_raw(t, s[0][nt][3], s[1][nt][0]);
+      t = max3_raw(t, s[1][nt][1], s[1][nt][2]);
+      tmax[nt] = max_over_lane_groups(max_raw(t, s[1][nt][3]));
     }
-    // rescale the accumulators only when some query's running max moved
-    if (!__all(alpha[0] == 1.f && alpha[1] == 1.f)) {
+    const bool up0 = __builtin_fmaf(tmax[0], sc, -m[0]) > kLazy;
+    const bool up1 = __builtin_fmaf(tmax[1], sc, -m[1]) > kLazy;
+    if (__builtin_expect(__any(up0 || up1), 0)) {
+      float alpha[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float mn = (nt ? up1 : up0) ? tmax[nt] * sc : m[nt];
+        alpha[nt] = __builtin_amdgcn_exp2f(m[nt] - mn);   // 1 where m stays
+        m[nt] = mn;
+        lpart[nt] *= alpha[nt];
+      }
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) o[dt][nt] *= alpha[nt];
+    }
+    // P^T fragments as a bf16 high part and a bf16 remainder (the weights
+    // keep ~16 bits through the second product); the remainder p - hi(p) is
+    // exact in fp32 and comes from one dot2 of the packed pair with (-1, 0)
+    // or (0, -1).  The normaliser sums the two bf16 parts (dot2 with (1, 1)),
+    // exactly the weights the product uses
+    uint4 ph[2], pl[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float p[8];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[4 * mt + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][nt][i], sc, -m[nt]));
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t h = pk_bf16(p[2 * j], p[2 * j + 1]);
+        const bf16x2p hb = __builtin_bit_cast(bf16x2p, h);
+        const float r0 = __builtin_amdgcn_fdot2_f32_bf16(hb, neg_lo, p[2 * j], false);
+        const float r1 = __builtin_amdgcn_fdot2_f32_bf16(hb, neg_hi, p[2 * j + 1], false);
+        hw[j] = h;
+        lw[j] = pk_bf16(r0, r1);
+        lpart[nt] = __builtin_amdgcn_fdot2_f32_bf16(hb, ones, lpart[nt], false);
+        lpart[nt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2p, lw[j]), ones, lpart[nt], false);
+      }
+      ph[nt] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      pl[nt] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     }
     // O^T += V^T P^T over the tile's 32 keys: k-slot j of lane group jg is
     // key 4 jg + j (j < 4) or 16 + 4 jg + (j - 4)
@@ -315,10 +352,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   // the scores of tile 0 started
   lds_barrier();                                    // s_seq complete
   {
-    const uint16_t* pk = row_ptr(s_seq[gk_key], kb, pkb);
-    const u32x4p k0 = *reinterpret_cast<const u32x4p*>(pk + 8 * gk_seg);
-    const u32x4p k1 = *reinterpret_cast<const u32x4p*>(pk + 8 * gk_seg + 64);
-    stash_k(0, k0, k1);
+    const u32x4p* pk = row_ptr(s_seq[gk_key], k_seg, pk_seg);
+    stash_k(0, pk[0], pk[8]);
   }
   Rows ra, rb;
   gather(0, ra);
@@ -359,6 +394,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
 
 hipError_t launch_prefill(const PrefillArgs& a, int d, hipStream_t s) {
   if (d != kD || a.q_block != 128 || a.K > kListMax) return hipErrorInvalidValue;
+  if (a.N >= kMaxRows || a.Nc >= kMaxRows) return hipErrorInvalidValue;
   const int nh = a.B * a.H;
   const int hpx = (nh + 7) / 8;
   dim3 grid(8 * hpx * a.nblk);

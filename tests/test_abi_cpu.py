@@ -192,8 +192,9 @@ def test_pyramid_validation():
 
 
 def test_prefill_limits():
-    """The chunked prefill stages a block's selection in LDS: block_top_k
-    above 8192 is refused before anything is launched."""
+    """The chunked prefill stages a block's selection in LDS and its rows as
+    32-bit byte offsets: block_top_k above 8192 and n_ctx of 2^23 or more are
+    refused before anything is launched."""
     b = _full_bufs()
     ok = dict(batch=1, n_q_heads=4, n_kv_heads=4, head_dim=128, n_ctx=1024, levels=3, factor=4,
               q_block=128, block_top_k=8192)
@@ -205,5 +206,11 @@ def test_prefill_limits():
     assert sa.raw_call("prefill_chunked", ctypes.byref(pf), ctypes.byref(b), None,
                        ctypes.byref(n), None) == sa.SA_ERR_UNSUPPORTED
     pf = sa.make_params(**{**ok, "head_dim": 64})
+    assert sa.raw_call("prefill_chunked", ctypes.byref(pf), ctypes.byref(b), None,
+                       ctypes.byref(n), None) == sa.SA_ERR_UNSUPPORTED
+    pf = sa.make_params(**{**ok, "n_ctx": (1 << 23) - 256})
+    assert sa.raw_call("prefill_chunked", ctypes.byref(pf), ctypes.byref(b), None,
+                       ctypes.byref(n), None) == sa.SA_OK
+    pf = sa.make_params(**{**ok, "n_ctx": 1 << 23})
     assert sa.raw_call("prefill_chunked", ctypes.byref(pf), ctypes.byref(b), None,
                        ctypes.byref(n), None) == sa.SA_ERR_UNSUPPORTED

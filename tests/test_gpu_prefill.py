@@ -147,7 +147,13 @@ def test_prefill_end_to_end_small():
     torch.cuda.synchronize()
     ni = _np(inp)
     blocks = {(0, h): list(range(run.nblk)) for h in range(cfg.n_heads)}
-    assert _check_prefill(cfg, run, ni, blocks) <= BF16_TOL
+    worst = _check_prefill(cfg, run, ni, blocks)
+    assert worst <= BF16_TOL
+    # the probabilities reach the PV product as a bf16 high part plus a bf16
+    # remainder (~16 bits).  On these inputs that stays near 2e-5, where one
+    # bf16 probability would reach 1.1e-2 and one fp16 probability 1.2e-3
+    # (the same weights rounded in fp64, the rest exact)
+    assert worst <= 2e-4
 
 
 def test_prefill_over_given_selection():
