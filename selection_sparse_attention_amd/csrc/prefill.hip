@@ -25,6 +25,8 @@
 //   * blocks of a head run on one die: block ids are mapped so that each of
 //     the 8 dies (round-robin dispatch) serves two heads, heaviest blocks
 //     first, keeping the heads' selected rows hot in that die's L2.
+#include <type_traits>
+
 #include "args.hpp"
 #include "common.hpp"
 
@@ -137,12 +139,12 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   // ---- the block's key sequence, staged once in LDS as row byte offsets:
   //      selected entry e < c_sel (a flat id: level-0 row, or coarse row
   //      flagged kCoarse), then the block's own level-0 keys q0 .. q0+nq-1,
-  //      then row 0 for the tail that the two-ahead gathers run past (masked
+  //      then row 0 for the tail that the gathers ahead run past (masked
   //      out of the softmax).  A flat id outside the pyramid is clamped to
   //      level-0 row 0 - never dereferenced out of bounds; its contribution
   //      is unspecified.
   {
-    const int n_stage = (ntiles + 3) * kKT;
+    const int n_stage = (ntiles + 4) * kKT;
     for (int e = tid; e < n_stage; e += kPfThreads) {
       uint32_t r = 0u;
       if (e < c_sel) {
@@ -172,12 +174,13 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     const char* base = ((int32_t)r < 0) ? bc : b0;
     return reinterpret_cast<const u32x4p*>(base + (r & ~kCoarse));
   };
-  // one set of loads for this thread: the K rows of tile x + 1 and the V rows
-  // of tile x (K runs a tile ahead: its product is issued a tile early)
+  // one set of loads for this thread: the K rows of tile x + 2 and the V rows
+  // of tile x (K runs two tiles ahead: its scores are computed two tiles
+  // before their PV product)
   struct Rows { u32x4p k0, k1, v0, v1; };
   // issue set x (unconditionally: past the end the rows are row 0, never used)
   auto gather = [&](int x, Rows& r) __attribute__((always_inline)) {
-    const uint32_t lk = s_seq[(x + 1) * kKT + gk_key];
+    const uint32_t lk = s_seq[(x + 2) * kKT + gk_key];
     const uint2 lv = *reinterpret_cast<const uint2*>(&s_seq[x * kKT + 2 * gv_kp]);
     const u32x4p* pk = row_ptr(lk, k_seg, pk_seg);
     r.k0 = pk[0];
@@ -190,10 +193,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     *reinterpret_cast<u32x4p*>(kdst) = k0;
     *reinterpret_cast<u32x4p*>(kdst + 64) = k1;
   };
-  // set x: K of tile x + 1 into K buffer (x + 1) & 1, V of tile x into V
-  // buffer x & 1
+  // set x: K of tile x + 2 into K buffer x & 1, V of tile x into V buffer
+  // x & 1
   auto stash = [&](int x, const Rows& r) __attribute__((always_inline)) {
-    stash_k((x + 1) & 1, r.k0, r.k1);
+    stash_k(x & 1, r.k0, r.k1);
     const int buf = x & 1;
     // V^T: dims 8 gv_seg + i, keys 2 gv_kp and 2 gv_kp + 1 packed in one dword
     uint16_t* vdst = s_vt[buf] + (8 * gv_seg) * kVRow + 2 * gv_kp;
@@ -245,19 +248,22 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  // one tile of math.  The scores of tile + 1 are started first, so the
-  // matrix cores work on them while this tile's softmax runs on the vector
-  // units; then this tile's PV product.  `mine` held set `tile` (staged
-  // already) and now takes set tile + 2; `next` holds set tile + 1, staged at
-  // the end.
-  auto body = [&](const int tile, Rows& mine, const Rows& next, f32x4p (&s)[2][2],
-                  f32x4p (&sn)[2][2]) __attribute__((always_inline)) {
-    gather(tile + 2, mine);
-    if (tile + 1 < ntiles) qk((tile + 1) & 1, sn);
-    const uint16_t* vt = s_vt[tile & 1];
-    // mask only on tiles that reach past the selection
-    const int e0 = tile * kKT;
-    if (e0 + kKT > c_sel) {
+  // softmax of one tile's scores (log2 domain: p = 2^(s sc - m)) into its
+  // P^T fragments: a bf16 high part and a bf16 remainder per query tile nt.
+  // A query's reference m moves only when the tile's max exceeds it by more
+  // than 2^8 (p stays <= 256, far from overflow); the factor 2^(m_old -
+  // m_new) is returned in `alpha` (exactly 1 where m stays) and the caller
+  // rescales the accumulators before it adds this tile's product, on a path
+  // the whole wave skips when every factor is 1.  No branch in the common
+  // case, so the caller's products and this vector work form one
+  // scheduling region.  `mask` (a compile-time bool): the tile reaches past
+  // the selection (causal mask over the block's own keys, nothing past the
+  // end).
+  struct PFrag { uint4 h[2], l[2]; };
+  auto softmax = [&](auto mask, const int tile, f32x4p (&s)[2][2], PFrag& P,
+                     float (&alpha)[2]) __attribute__((always_inline)) {
+    if constexpr (decltype(mask)::value) {
+      const int e0 = tile * kKT;
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const int ql = 32 * wid + 16 * nt + l16;
@@ -267,45 +273,24 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
           for (int i = 0; i < 4; ++i) {
             const int e = e0 + 16 * mt + 4 * jg + i;
             const bool ok = (e < c_sel) || (e < T && (e - c_sel) <= ql);
-            if (!ok) s[mt][nt][i] = -INFINITY;
+            s[mt][nt][i] = ok ? s[mt][nt][i] : -INFINITY;
           }
       }
     }
-    // online softmax per query (log2 domain: p = 2^(s sc - m)).  A query's
-    // reference m moves only when the tile's max exceeds it by more than 2^8
-    // (p stays <= 256, far from overflow), so the accumulators are rescaled
-    // rarely, on a path the whole wave skips otherwise; the final
-    // normalisation divides the scale out
-    float tmax[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       float t = max3_raw(s[0][nt][0], s[0][nt][1], s[0][nt][2]);
       t = max3_raw(t, s[0][nt][3], s[1][nt][0]);
       t = max3_raw(t, s[1][nt][1], s[1][nt][2]);
-      tmax[nt] = max_over_lane_groups(max_raw(t, s[1][nt][3]));
+      const float mx = max_over_lane_groups(max_raw(t, s[1][nt][3])) * sc;
+      const float mn = (mx - m[nt] > kLazy) ? mx : m[nt];
+      alpha[nt] = __builtin_amdgcn_exp2f(m[nt] - mn);
+      m[nt] = mn;
+      lpart[nt] *= alpha[nt];
     }
-    const bool up0 = __builtin_fmaf(tmax[0], sc, -m[0]) > kLazy;
-    const bool up1 = __builtin_fmaf(tmax[1], sc, -m[1]) > kLazy;
-    if (__builtin_expect(__any(up0 || up1), 0)) {
-      float alpha[2];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const float mn = (nt ? up1 : up0) ? tmax[nt] * sc : m[nt];
-        alpha[nt] = __builtin_amdgcn_exp2f(m[nt] - mn);   // 1 where m stays
-        m[nt] = mn;
-        lpart[nt] *= alpha[nt];
-      }
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) o[dt][nt] *= alpha[nt];
-    }
-    // P^T fragments as a bf16 high part and a bf16 remainder (the weights
-    // keep ~16 bits through the second product); the remainder p - hi(p) is
-    // exact in fp32 and comes from one dot2 of the packed pair with (-1, 0)
-    // or (0, -1).  The normaliser sums the two bf16 parts (dot2 with (1, 1)),
-    // exactly the weights the product uses
-    uint4 ph[2], pl[2];
+    // the remainder p - hi(p) is exact in fp32 and comes from one dot2 of
+    // the packed pair with (-1, 0) or (0, -1); the normaliser sums the two
+    // bf16 parts (dot2 with (1, 1)), exactly the weights the product uses
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       float p[8];
@@ -325,11 +310,24 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
         lpart[nt] = __builtin_amdgcn_fdot2_f32_bf16(hb, ones, lpart[nt], false);
         lpart[nt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2p, lw[j]), ones, lpart[nt], false);
       }
-      ph[nt] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      pl[nt] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      P.h[nt] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      P.l[nt] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     }
-    // O^T += V^T P^T over the tile's 32 keys: k-slot j of lane group jg is
-    // key 4 jg + j (j < 4) or 16 + 4 jg + (j - 4)
+  };
+  // the rescale a softmax step asked for, before the next product
+  auto rescale = [&](const float (&alpha)[2]) __attribute__((always_inline)) {
+    if (__builtin_expect(!__all(alpha[0] == 1.f && alpha[1] == 1.f), 0)) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) o[dt][nt] *= alpha[nt];
+    }
+  };
+
+  // O^T += V^T P^T over one tile's 32 keys (V in buffer tile & 1): k-slot j
+  // of lane group jg is key 4 jg + j (j < 4) or 16 + 4 jg + (j - 4)
+  auto pv = [&](const int tile, const PFrag& P) __attribute__((always_inline)) {
+    const uint16_t* vt = s_vt[tile & 1];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const uint16_t* vrow = vt + (16 * dt + l16) * kVRow;
@@ -338,38 +336,74 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
       const bf16x8p vf = __builtin_bit_cast(bf16x8p, make_uint4(w0.x, w0.y, w1.x, w1.y));
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        o[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, __builtin_bit_cast(bf16x8p, ph[nt]), o[dt][nt], 0, 0, 0);
-        o[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, __builtin_bit_cast(bf16x8p, pl[nt]), o[dt][nt], 0, 0, 0);
+        o[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, __builtin_bit_cast(bf16x8p, P.h[nt]), o[dt][nt], 0, 0, 0);
+        o[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, __builtin_bit_cast(bf16x8p, P.l[nt]), o[dt][nt], 0, 0, 0);
       }
     }
-    // unconditional (past the end it stages rows nobody reads), so that the
-    // wait for this set's loads is the same on every path
-    stash(tile + 1, next);
+  };
+
+  // one step of the pipeline at tile t: the scores of tile t + 2 and the PV
+  // product of tile t go to the matrix cores while the vector units turn
+  // the scores of tile t + 1 into its probabilities - the three are
+  // independent, so one wave's vector work runs under its own products.
+  // `mine` held set t (staged already) and now takes set t + 2; `next`
+  // holds set t + 1, staged at the end.  s1 holds the scores of tile t + 1
+  // and s2 receives those of tile t + 2; P0 holds the probabilities of tile
+  // t and P1 receives those of tile t + 1.  Past the end the scores and
+  // probabilities are of rows nobody reads (fully masked), so every step
+  // runs the same instructions.
+  float alpha[2];
+  auto body = [&](auto mask, const int t, Rows& mine, const Rows& next, f32x4p (&s1)[2][2],
+                  f32x4p (&s2)[2][2], const PFrag& P0, PFrag& P1) __attribute__((always_inline)) {
+    rescale(alpha);
+    gather(t + 2, mine);
+    qk(t & 1, s2);
+    pv(t, P0);
+    softmax(mask, t + 1, s1, P1, alpha);
+    stash(t + 1, next);
     lds_barrier();
   };
 
-  // prologue: K of tile 0 staged alone, sets 0 and 1 in flight, set 0 staged,
-  // the scores of tile 0 started
+  // prologue: K of tiles 0 and 1 staged alone and their scores computed,
+  // sets 0 and 1 in flight, tile 0's probabilities, then set 0 staged (its
+  // K, of tile 2, over tile 0's once every wave has read those)
   lds_barrier();                                    // s_seq complete
   {
-    const u32x4p* pk = row_ptr(s_seq[gk_key], k_seg, pk_seg);
-    stash_k(0, pk[0], pk[8]);
+    const u32x4p* pk0 = row_ptr(s_seq[gk_key], k_seg, pk_seg);
+    const u32x4p* pk1 = row_ptr(s_seq[kKT + gk_key], k_seg, pk_seg);
+    stash_k(0, pk0[0], pk0[8]);
+    stash_k(1, pk1[0], pk1[8]);
   }
-  Rows ra, rb;
-  gather(0, ra);
-  gather(1, rb);
-  stash(0, ra);
   lds_barrier();
   f32x4p sa_[2][2], sb_[2][2];
   qk(0, sa_);
-  // pairs of tiles, then an odd last one: every path back to the loop head
-  // passes both bodies, so the loads in flight there are always set 1's
+  qk(1, sb_);
+  Rows ra, rb;
+  gather(0, ra);
+  gather(1, rb);
+  PFrag pa, pb;
+  const std::true_type masked;
+  const std::false_type unmasked;
+  softmax(masked, 0, sa_, pa, alpha);
+  lds_barrier();                                    // K buffer 0 read by every wave
+  stash(0, ra);
+  lds_barrier();
+  // pairs of tiles, then an odd last one: every path back to a loop head
+  // passes both bodies of a pair, so the loads in flight there are always
+  // set 1's.  Tiles from tile c_sel / 32 on reach past the selection: the
+  // steps that turn them into probabilities take the masked form.
+  const int mask_from = c_sel / kKT;
   int tile = 0;
-  for (; tile + 1 < ntiles; tile += 2) {
-    body(tile, ra, rb, sa_, sb_);
-    body(tile + 1, rb, ra, sb_, sa_);
+  for (; tile + 2 < mask_from; tile += 2) {
+    body(unmasked, tile, ra, rb, sb_, sa_, pa, pb);
+    body(unmasked, tile + 1, rb, ra, sa_, sb_, pb, pa);
   }
-  if (tile < ntiles) body(tile, ra, rb, sa_, sb_);
+  for (; tile + 1 < ntiles; tile += 2) {
+    body(masked, tile, ra, rb, sb_, sa_, pa, pb);
+    body(masked, tile + 1, rb, ra, sa_, sb_, pb, pa);
+  }
+  if (tile < ntiles) body(masked, tile, ra, rb, sb_, sa_, pa, pb);
+  rescale(alpha);
 
   // ---- normalise and write: lane holds d = 16 dt + 4 jg + 0..3 of query
   //      32w + 16 nt + l16
