@@ -156,6 +156,24 @@ def test_prefill_end_to_end_small():
     assert worst <= 2e-4
 
 
+def test_prefill_largest_selection():
+    """block_top_k at the largest list the attention kernel stages (8192): the
+    late blocks see more entries than that, so their key sequence - the
+    selection, the block's own keys and the tail the gathers ahead run past -
+    fills the staging area exactly; the last block is ragged (64 queries)."""
+    cfg = SMALL.with_(n_heads=1, n_ctx=8192 + 64, block_top_k=8192)
+    inp = workloads.prefill_inputs(cfg, 9)
+    run = PrefillRun(cfg, inp)
+    run.pyramid(); run.select(); run.prefill()
+    torch.cuda.synchronize()
+    ni = _np(inp)
+    cnt = run.t["blk_count"].cpu().numpy()
+    assert cnt[0, 0, run.nblk - 1] == 8192                  # the list is full there
+    blocks = [0, 1, 48, 49, 50, run.nblk - 2, run.nblk - 1]
+    worst = _check_prefill(cfg, run, ni, {(0, 0): blocks})
+    assert worst <= BF16_TOL
+
+
 def test_prefill_over_given_selection():
     """The attention stage alone: blk_idx filled with random visible entries
     drawn by the test's generator, unsorted."""
