@@ -10,11 +10,14 @@
 //
 // gfx950 design, one 256-thread workgroup per (block, head), wave w owning
 // queries 32w .. 32w+31:
-//   * keys are processed in tiles of 32; the 256 threads gather a tile's K
-//     and V rows by index straight from HBM into LDS (double-buffered, the
-//     next tile's loads in flight during the current tile's math).  K is kept
-//     row-major (rows padded to 272 B), V transposed (d rows of 32 keys,
-//     padded to 72 B) - the operand layouts the matrix cores want.
+//   * keys are processed in tiles of 32; the 256 threads gather K and V rows
+//     by index straight from HBM into double-buffered LDS tiles, the loads
+//     issued a step before they are staged.  K is kept row-major (rows padded
+//     to 272 B), V transposed (d rows of 32 keys, padded to 72 B) - the
+//     operand layouts the matrix cores want.
+//   * a three-stage pipeline per step t: the scores of tile t+2 and the PV
+//     product of tile t on the matrix cores, the softmax of tile t+1 on the
+//     vector units, all independent, in one scheduling region.
 //   * scores come out transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16 with
 //     the query block's fragments resident in registers), so every lane holds
 //     8 keys x 2 queries; a query's running max is a reduction over 8 values
