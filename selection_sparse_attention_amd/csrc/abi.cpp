@@ -142,7 +142,7 @@ SelectWs carve_select(void* ws, int rows, int n) {
 
 // ---------------------------------------------------------------- decode ws
 constexpr int kDecodeTps = 256;           // fp32 caches: list entries per split
-constexpr int kDecodeMinChunk = 128;      // bf16 caches: smallest work item (list entries)
+constexpr int kDecodeMinChunk = 64;       // bf16 caches: smallest work item (list entries)
 constexpr int kMaxDecodeItems = 8192;     // bf16 caches: work items one launch may hold
 constexpr int kMaxDecodeSplits = 8192;     // contexts up to 2M tokens
 
