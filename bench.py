@@ -323,12 +323,44 @@ def blas_threads():
         return 1
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline_decode(cfg, inst, budget_s, torch):
     """The fp64 oracle on whole (sequence, KV group) slices of the same step
-    until ``budget_s`` of CPU time is spent; scaled to tokens/s."""
+    until ``budget_s`` of CPU time is spent; scaled to tokens/s.  A second,
+    shorter sample runs with the BLAS pool held to one thread."""
+    blas = blas_threads()
+    done_heads, spent = _oracle_decode_sample(cfg, inst, budget_s, torch)
+    one = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            d1, s1 = _oracle_decode_sample(cfg, inst, budget_s / 3, torch)
+        one = d1 * cfg.n_ctx / s1
+    except ImportError:
+        pass
+    return {"value": done_heads * cfg.n_ctx / spent, "unit": "tokens/s",
+            "cores": int(blas), "kind": "oracle",
+            "sample": f"{done_heads // cfg.gqa} whole (sequence, KV group) slices of the "
+                      f"{cfg.name} step ({done_heads} query heads x {cfg.n_ctx} tokens), "
+                      f"index + selection + attention, fp64 numpy, {spent:.1f} s",
+            "value_1_thread": one,
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": cpu_model()}
+
+
+def _oracle_decode_sample(cfg, inst, budget_s, torch):
     import numpy as np
     import oracle
-    blas = blas_threads()
     G = cfg.gqa
     groups = [(b, g) for b in range(cfg.batch) for g in range(cfg.n_kv_heads)]
     t = inst.t
@@ -349,12 +381,7 @@ def cpu_baseline_decode(cfg, inst, budget_s, torch):
         oracle.decode_step(sub, ni)
         spent += time.perf_counter() - t0
         done_heads += G
-    return {"value": done_heads * cfg.n_ctx / spent, "unit": "tokens/s",
-            "cores": int(blas), "kind": "oracle",
-            "sample": f"{done_heads // G} whole (sequence, KV group) slices of the "
-                      f"{cfg.name} step ({done_heads} query heads x {cfg.n_ctx} tokens), "
-                      f"index + selection + attention, fp64 numpy, {spent:.1f} s",
-            "host_cpus": os.cpu_count()}
+    return done_heads, spent
 
 
 def compact(r):
