@@ -1,0 +1,37 @@
+"""Host-side checks of bench.py's contract (no GPU): it refuses more than one
+GPU before touching a device, and the counter-derived traffic it reports is
+taken only from a profile of the current kernel source."""
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_bench_refuses_several_gpus():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
+
+
+def test_traffic_record_follows_the_source():
+    with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+        recs = json.load(f)
+    key = "prefill_kernel:pyramid_prefill_128k"
+    rec = recs[key]
+    assert bench.traffic_record("prefill_kernel", "pyramid_prefill_128k",
+                                rec["source_sha"]) == rec["bytes_per_launch"]
+    assert bench.traffic_record("prefill_kernel", "pyramid_prefill_128k", "0" * 16) is None
+    assert bench.traffic_record("prefill_kernel", "no_such_workload", rec["source_sha"]) is None
+
+
+def test_source_sha_changes_with_the_text():
+    a = bench.source_sha(["prefill.hip", "common.hpp", "args.hpp"])
+    b = bench.source_sha(["prefill.hip", "common.hpp"])
+    assert len(a) == 16 and a != b
