@@ -288,6 +288,12 @@ def test_pipeline_llama_128k_topk_full_size_sampled():
     _pipeline_check(workloads.LLAMA_128K_TOPK, 2, require_exact_sets=False, sample=4)
 
 
+def test_pipeline_llama_128k_topp_full_size_sampled():
+    """The 128K top-p step at full size: tens of thousands of selected tokens
+    per group, so every work item spans many tiles."""
+    _pipeline_check(workloads.LLAMA_128K, 3, require_exact_sets=False, sample=4)
+
+
 # ------------------------------------------------------------------ edge cases
 @pytest.mark.parametrize("cfg", [
     workloads.TINY.with_(n_ctx=1, needles_per_head=0),
