@@ -220,7 +220,10 @@ int32_t sparse_attn_select(const sa_params* params, const sa_buffers* bufs,
  * sel_idx[b,g,0:sel_count[b,g]].  out[b,h,:] = sum_j pi_j v_j with
  * pi = softmax(q[b,h] . k_j / sqrt(d)) over that set, accumulated in fp32.
  * The GQA heads of a group share every gathered key/value row.  Reads q,
- * k_cache, v_cache, sel_idx, sel_count; writes out.  Needs a workspace.
+ * k_cache, v_cache, sel_idx, sel_count; writes out.  A selecting group whose
+ * sel_count is negative (a selection that reported failure) gets NaN in
+ * every output of its query heads.  Needs a workspace; no part of it has to
+ * start at zero.
  */
 int32_t sparse_attn_decode(const sa_params* params, const sa_buffers* bufs,
                            void* workspace, size_t* workspace_bytes,

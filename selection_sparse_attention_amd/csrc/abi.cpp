@@ -146,15 +146,12 @@ constexpr int kDecodeMinChunk = 64;       // bf16 caches: smallest work item (li
 constexpr int kMaxDecodeItems = 8192;     // bf16 caches: work items one launch may hold
 constexpr int kMaxDecodeSplits = 8192;     // contexts up to 2M tokens
 
-// Compute units of the current device (queried once per device).
+// Compute units of the current device (a runtime query on every call: the
+// library keeps no state between calls).
 int compute_units() {
-  static int cache[64] = {0};
-  int dev = 0;
+  int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64 && cache[dev] > 0) return cache[dev];
-  int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-  if (dev < 64) cache[dev] = n;
   return n;
 }
 

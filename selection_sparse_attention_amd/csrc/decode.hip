@@ -219,7 +219,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 #pragma unroll
     for (int q = 1; q < P; ++q) v += s_red[q * D + e];
     const float L = s_L;
-    a.out[(int64_t)bh * D + e] = (L > 0.f) ? v / L : 0.f;
+    // a failed selection (negative count) poisons the group's outputs
+    const bool failed = !((a.local_mask >> g) & 1ull) && a.sel_count[(int64_t)b * a.Hkv + g] < 0;
+    a.out[(int64_t)bh * D + e] = failed ? __builtin_nanf("") : ((L > 0.f) ? v / L : 0.f);
   }
 }
 

@@ -466,7 +466,9 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_item_combine_kernel(Decod
     float v = A;
 #pragma unroll
     for (int q = 1; q < P; ++q) v += s_a[q * D + e];
-    a.out[((int64_t)b * a.Hq + g * G + h) * D + e] = (L > 0.f) ? v / L : 0.f;
+    // a failed selection (negative count) poisons the group's outputs
+    const bool failed = !((a.local_mask >> g) & 1ull) && a.sel_count[bg] < 0;
+    a.out[((int64_t)b * a.Hq + g * G + h) * D + e] = failed ? __builtin_nanf("") : ((L > 0.f) ? v / L : 0.f);
   }
 }
 

@@ -31,8 +31,9 @@ __global__ __launch_bounds__(256) void index_lowrank_kernel(IndexLowrankArgs a) 
   if (q_side) {
     if (a.q_pre == nullptr) return;
     __syncthreads();
-    const int hh = tid / 16, c = tid % 16;
-    if (hh < a.G) {
+    // 16 heads per pass of the workgroup, as many passes as the group has heads
+    const int c = tid % 16;
+    for (int hh = tid / 16; hh < a.G; hh += 16) {
       const int h = g * a.G + hh;
       const int64_t base = ((int64_t)b * a.Hq + h) * D;
       float acc = 0.f;
