@@ -24,9 +24,11 @@
  *
  * Conventions common to every entry point
  *  - Ownership: the caller allocates every device buffer and the workspace;
- *    the library never allocates or frees memory, keeps no pointer after a
- *    call returns and holds no mutable global state.  Calls on different
- *    streams with disjoint output and workspace buffers may run concurrently.
+ *    the library never allocates or frees memory and keeps no pointer after a
+ *    call returns.  Its only global state is the device address of the
+ *    static scratch array of sparse_attn_decode_noalloc, looked up once per
+ *    device.  Calls on different streams with disjoint output and workspace
+ *    buffers may run concurrently.
  *  - Streams: all device work is enqueued on `hip_stream` (a hipStream_t; NULL
  *    means the default stream).  No call synchronises or copies device memory
  *    to the host; data-dependent sizes (selected counts) stay on the device.
@@ -63,7 +65,11 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_VERSION 1
+#define SPARSE_ATTN_VERSION 2
+
+/* Size of the static device scratch array behind sparse_attn_decode_noalloc
+ * (one per GPU the library runs on, held until the process ends). */
+#define SPARSE_ATTN_NOALLOC_SCRATCH_BYTES (8u << 20)
 
 typedef enum {
   SA_OK = 0,
@@ -228,6 +234,24 @@ int32_t sparse_attn_select(const sa_params* params, const sa_buffers* bufs,
 int32_t sparse_attn_decode(const sa_params* params, const sa_buffers* bufs,
                            void* workspace, size_t* workspace_bytes,
                            void* hip_stream);
+
+/*
+ * sparse_attn_decode_noalloc - sparse_attn_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, validation, kernels and
+ * results as sparse_attn_decode, without the workspace arguments: the
+ * workspace is carved from a static device array of
+ * SPARSE_ATTN_NOALLOC_SCRATCH_BYTES on the current device (the stream must
+ * belong to it).  The call allocates nothing; the first call on a device
+ * looks up that device's copy of the array.  Returns SA_ERR_WORKSPACE when
+ * the workspace sparse_attn_decode would need is larger than the array, and
+ * SA_ERR_HIP when the array's address cannot be obtained.  Every call on one
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other host threads) race and give undefined results.  The array
+ * keeps the last call's contents; nothing in it needs to start at zero.
+ */
+int32_t sparse_attn_decode_noalloc(const sa_params* params, const sa_buffers* bufs,
+                                   void* hip_stream);
 
 /*
  * sparse_attn_prefill_chunked - pyramid-selection prefill forward

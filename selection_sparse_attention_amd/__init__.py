@@ -32,8 +32,8 @@ IDX_LOWRANK, IDX_CHUNK_SUMMARY, IDX_PYRAMID = 0, 1, 2
 SEL_TOPP, SEL_TOPK, SEL_ROUTE2, SEL_PYRAMID_TOPK = 0, 1, 2, 3
 
 EXPORTED = ("sparse_attn_index_build", "sparse_attn_select", "sparse_attn_decode",
-            "sparse_attn_prefill_chunked", "sparse_attn_status_string",
-            "sparse_attn_version")
+            "sparse_attn_decode_noalloc", "sparse_attn_prefill_chunked",
+            "sparse_attn_status_string", "sparse_attn_version")
 
 
 class Params(ctypes.Structure):
@@ -78,6 +78,9 @@ for _name, _args in (
                                          ctypes.c_void_p])):
     getattr(_lib, _name).argtypes = _args
     getattr(_lib, _name).restype = ctypes.c_int32
+_lib.sparse_attn_decode_noalloc.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(Buffers),
+                                            ctypes.c_void_p]
+_lib.sparse_attn_decode_noalloc.restype = ctypes.c_int32
 _lib.sparse_attn_status_string.argtypes = [ctypes.c_int32]
 _lib.sparse_attn_status_string.restype = ctypes.c_char_p
 _lib.sparse_attn_version.restype = ctypes.c_int32
@@ -239,6 +242,13 @@ def decode(params: Params, bufs: Buffers, ws: Optional[Workspace] = None, stream
     n = ctypes.c_size_t(w.numel())
     _check(_lib.sparse_attn_decode(ctypes.byref(params), ctypes.byref(bufs), w.data_ptr(),
                                    ctypes.byref(n), _stream(stream)), "decode")
+
+
+def decode_noalloc(params: Params, bufs: Buffers, stream=None):
+    """decode() with the library's static scratch array as its workspace
+    (nothing is allocated; concurrent calls on one GPU race)."""
+    _check(_lib.sparse_attn_decode_noalloc(ctypes.byref(params), ctypes.byref(bufs),
+                                           _stream(stream)), "decode_noalloc")
 
 
 def prefill_chunked(params: Params, bufs: Buffers, ws: Optional[Workspace] = None,

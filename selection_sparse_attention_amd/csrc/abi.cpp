@@ -9,6 +9,7 @@
 #include <cstring>
 
 #include "../../include/sparse_attn.h"
+#include "abi_internal.hpp"
 #include "args.hpp"
 
 namespace {
@@ -171,6 +172,66 @@ int decode_max_count(const sa_params* p, const int8_t* kinds) {
 }
 
 }  // namespace
+
+namespace sa {
+
+// The decode entry point's work, shared with the entry point that takes its
+// workspace from the library's static scratch array.
+int32_t decode_entry(const sa_params* p, const sa_buffers* b, void* ws, size_t* ws_bytes,
+                     void* stream) {
+  int32_t st = check_common(p, b);
+  if (st) return st;
+  int8_t kinds[sa::kMaxGroups];
+  if ((st = group_kinds(p, kinds))) return st;
+  const int G = p->n_q_heads / p->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return SA_ERR_UNSUPPORTED;
+  bool any_local = false, any_list = false;
+  uint64_t local_mask = 0;
+  for (int g = 0; g < p->n_kv_heads; ++g) {
+    if (kinds[g] == SA_HEAD_LOCAL) { any_local = true; local_mask |= 1ull << g; }
+    else any_list = true;
+  }
+  if (any_local && (p->sinks < 0 || p->window < 0 || (int64_t)p->sinks + p->window < 1))
+    return SA_ERR_INVALID_ARG;
+  int tps = kDecodeTps, max_splits, target_items = 0;
+  size_t n_partial;
+  if (p->dtype == SA_BF16) {
+    // work items: the step's visible tokens spread over one item per
+    // workgroup slot (two per compute unit, one for 8-head groups, whose
+    // workgroups use a whole unit's registers); the plan itself is made on
+    // the device
+    const int groups = p->batch * p->n_kv_heads;
+    target_items = (G > 4 ? 1 : 2) * compute_units();
+    max_splits = target_items + groups;        // bound on the item count
+    if (max_splits > kMaxDecodeItems) return SA_ERR_UNSUPPORTED;
+    n_partial = (size_t)max_splits * G * (p->head_dim + 2);
+  } else {
+    const int max_count = decode_max_count(p, kinds);
+    max_splits = (max_count + tps - 1) / tps;
+    if (max_splits > kMaxDecodeSplits) return SA_ERR_UNSUPPORTED;
+    n_partial = (size_t)p->batch * p->n_q_heads * max_splits * (p->head_dim + 2);
+  }
+  Carver c(ws);
+  float* partial = c.take<float>(n_partial);
+  int2* plan = (p->dtype == SA_BF16) ? c.take<int2>((size_t)p->batch * p->n_kv_heads) : nullptr;
+  if ((st = workspace_gate(ws, ws_bytes, c.size()))) return st < 0 ? st : SA_OK;
+  if (!b->q || !b->k_cache || !b->v_cache || !b->out) return SA_ERR_INVALID_ARG;
+  if (any_list && (!b->sel_idx || !b->sel_count)) return SA_ERR_INVALID_ARG;
+  if (!aligned16(b->q) || !aligned16(b->k_cache) || !aligned16(b->v_cache)) return SA_ERR_INVALID_ARG;
+  sa::DecodeArgs a{};
+  a.q = b->q; a.k = b->k_cache; a.v = b->v_cache; a.sel_idx = b->sel_idx; a.sel_count = b->sel_count;
+  a.out = b->out; a.partial = partial;
+  a.B = p->batch; a.Hq = p->n_q_heads; a.Hkv = p->n_kv_heads; a.n = p->n_ctx; a.n_cap = p->n_cap;
+  a.G = G; a.sinks = p->sinks; a.window = p->window; a.tps = tps; a.max_splits = max_splits;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->head_dim));
+  a.local_mask = local_mask;
+  a.target_items = target_items;
+  a.min_chunk = kDecodeMinChunk;
+  a.plan = plan;
+  return hip_status(sa::launch_decode(a, p->dtype, p->head_dim, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace sa
 
 extern "C" {
 
@@ -368,56 +429,7 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
 
 int32_t sparse_attn_decode(const sa_params* p, const sa_buffers* b, void* ws, size_t* ws_bytes,
                            void* stream) {
-  int32_t st = check_common(p, b);
-  if (st) return st;
-  int8_t kinds[sa::kMaxGroups];
-  if ((st = group_kinds(p, kinds))) return st;
-  const int G = p->n_q_heads / p->n_kv_heads;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return SA_ERR_UNSUPPORTED;
-  bool any_local = false, any_list = false;
-  uint64_t local_mask = 0;
-  for (int g = 0; g < p->n_kv_heads; ++g) {
-    if (kinds[g] == SA_HEAD_LOCAL) { any_local = true; local_mask |= 1ull << g; }
-    else any_list = true;
-  }
-  if (any_local && (p->sinks < 0 || p->window < 0 || (int64_t)p->sinks + p->window < 1))
-    return SA_ERR_INVALID_ARG;
-  int tps = kDecodeTps, max_splits, target_items = 0;
-  size_t n_partial;
-  if (p->dtype == SA_BF16) {
-    // work items: the step's visible tokens spread over one item per
-    // workgroup slot (two per compute unit, one for 8-head groups, whose
-    // workgroups use a whole unit's registers); the plan itself is made on
-    // the device
-    const int groups = p->batch * p->n_kv_heads;
-    target_items = (G > 4 ? 1 : 2) * compute_units();
-    max_splits = target_items + groups;        // bound on the item count
-    if (max_splits > kMaxDecodeItems) return SA_ERR_UNSUPPORTED;
-    n_partial = (size_t)max_splits * G * (p->head_dim + 2);
-  } else {
-    const int max_count = decode_max_count(p, kinds);
-    max_splits = (max_count + tps - 1) / tps;
-    if (max_splits > kMaxDecodeSplits) return SA_ERR_UNSUPPORTED;
-    n_partial = (size_t)p->batch * p->n_q_heads * max_splits * (p->head_dim + 2);
-  }
-  Carver c(ws);
-  float* partial = c.take<float>(n_partial);
-  int2* plan = (p->dtype == SA_BF16) ? c.take<int2>((size_t)p->batch * p->n_kv_heads) : nullptr;
-  if ((st = workspace_gate(ws, ws_bytes, c.size()))) return st < 0 ? st : SA_OK;
-  if (!b->q || !b->k_cache || !b->v_cache || !b->out) return SA_ERR_INVALID_ARG;
-  if (any_list && (!b->sel_idx || !b->sel_count)) return SA_ERR_INVALID_ARG;
-  if (!aligned16(b->q) || !aligned16(b->k_cache) || !aligned16(b->v_cache)) return SA_ERR_INVALID_ARG;
-  sa::DecodeArgs a{};
-  a.q = b->q; a.k = b->k_cache; a.v = b->v_cache; a.sel_idx = b->sel_idx; a.sel_count = b->sel_count;
-  a.out = b->out; a.partial = partial;
-  a.B = p->batch; a.Hq = p->n_q_heads; a.Hkv = p->n_kv_heads; a.n = p->n_ctx; a.n_cap = p->n_cap;
-  a.G = G; a.sinks = p->sinks; a.window = p->window; a.tps = tps; a.max_splits = max_splits;
-  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->head_dim));
-  a.local_mask = local_mask;
-  a.target_items = target_items;
-  a.min_chunk = kDecodeMinChunk;
-  a.plan = plan;
-  return hip_status(sa::launch_decode(a, p->dtype, p->head_dim, static_cast<hipStream_t>(stream)));
+  return sa::decode_entry(p, b, ws, ws_bytes, stream);
 }
 
 int32_t sparse_attn_prefill_chunked(const sa_params* p, const sa_buffers* b, void* ws,

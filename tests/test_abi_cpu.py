@@ -214,3 +214,17 @@ def test_prefill_limits():
     pf = sa.make_params(**{**ok, "n_ctx": 1 << 23})
     assert sa.raw_call("prefill_chunked", ctypes.byref(pf), ctypes.byref(b), None,
                        ctypes.byref(n), None) == sa.SA_ERR_UNSUPPORTED
+
+
+def test_decode_noalloc_rejects_a_workspace_larger_than_its_array():
+    # fp32 decode of a long context: the split partials need more than the
+    # static array holds; the size check runs before any device call
+    p = _decode_params(dtype="fp32", batch=8, n_q_heads=32, n_kv_heads=32,
+                       head_kind=[1] * 32, n_ctx=200000)
+    b = _full_bufs()
+    n = ctypes.c_size_t(0)
+    assert sa.raw_call("decode", ctypes.byref(p), ctypes.byref(b), None, ctypes.byref(n),
+                       None) == sa.SA_OK
+    assert n.value > 8 << 20
+    st = sa.raw_call("decode_noalloc", ctypes.byref(p), ctypes.byref(b), None)
+    assert st == sa.SA_ERR_WORKSPACE
