@@ -79,14 +79,22 @@ def traffic_record(kernel, workload, sha):
 
 # ----------------------------------------------------------------- decode
 class DecodeInstance:
-    def __init__(self, cfg, seed, sa, torch, workloads):
+    def __init__(self, cfg, seed, sa, torch, workloads, alpha=1.0, like=None):
+        """One step's device buffers.  ``like``: copy another instance's
+        inputs (same values at new addresses, so the Infinity Cache holds
+        nothing of this one when the other has just run)."""
         B, Hq, Hkv, d, n = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_ctx
         self.cfg = cfg
-        inp = workloads.decode_inputs(cfg, seed, device="cuda")
         dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-        self.t = {k: inp[k].to(dt).contiguous() for k in ("q_pre", "q", "k_pre", "k_cache", "v_cache")}
-        del inp["k_pre"], inp["k_cache"], inp["v_cache"]
-        self.t["proj"] = inp["proj"].float().contiguous()
+        if like is None:
+            inp = workloads.decode_inputs(cfg, seed, device="cuda", alpha=alpha)
+            self.t = {k: inp[k].to(dt).contiguous()
+                      for k in ("q_pre", "q", "k_pre", "k_cache", "v_cache")}
+            del inp["k_pre"], inp["k_cache"], inp["v_cache"]
+            self.t["proj"] = inp["proj"].float().contiguous()
+        else:
+            self.t = {k: like.t[k].clone() for k in ("q_pre", "q", "k_pre", "k_cache", "v_cache",
+                                                    "proj")}
         self.t["k_idx"] = torch.zeros(B, Hkv, n, cfg.r, dtype=dt, device="cuda")
         self.t["q_idx"] = torch.zeros(B, Hq, cfg.r, dtype=torch.float32, device="cuda")
         self.t["sel_idx"] = torch.zeros(B, Hkv, n, dtype=torch.int32, device="cuda")
@@ -170,15 +178,34 @@ DECODE_CONFIGS = {
 }
 
 
+MIN_TOUCHED_BYTES = 1 << 30     # rotated instances touch at least this much per round
+
+
 def run_decode(args, torch, sa, workloads, workload=None, steps=None, warmup=None,
-               instances=None, cpu=True):
+               instances=None, cpu=True, alpha=1.0):
     workload = workload or args.workload
     steps = steps or args.steps
     warmup = args.warmup if warmup is None else warmup
     instances = instances or args.instances
     cfg = getattr(workloads, DECODE_CONFIGS[workload])
-    log(f"[bench] generating {instances} instance(s) of {cfg.name}")
-    insts = [DecodeInstance(cfg, 1000 + i, sa, torch, workloads) for i in range(instances)]
+    kinds = cfg.head_kind()
+    log(f"[bench] generating {instances} instance(s) of {cfg.name} (alpha {alpha})")
+    insts = [DecodeInstance(cfg, 1000 + i, sa, torch, workloads, alpha=alpha)
+             for i in range(instances)]
+    # one step of each, then copies until a round of the rotation touches
+    # >= 1 GiB (so no step finds its rows in the 256 MB Infinity Cache)
+    for x in insts:
+        x.index_and_select()
+    torch.cuda.synchronize()
+    per_step = sum(decode_bytes(cfg, x.t["sel_count"].cpu().tolist(), kinds)[1]
+                   for x in insts) / len(insts)
+    want = max(len(insts), -(-MIN_TOUCHED_BYTES // int(per_step)))
+    base = len(insts)
+    while len(insts) < want:
+        insts.append(DecodeInstance(cfg, 0, sa, torch, workloads, like=insts[len(insts) % base]))
+    if len(insts) > base:
+        log(f"[bench] {len(insts) - base} copies added: {len(insts)} instances, "
+            f"{len(insts) * per_step / 2**30:.2f} GiB touched per rotation")
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     for i in range(warmup):
@@ -256,7 +283,6 @@ def run_decode(args, torch, sa, workloads, workload=None, steps=None, warmup=Non
     w1.record(stream)
     torch.cuda.synchronize()
     t_warm = w0.elapsed_time(w1) / steps * 1e-3
-    kinds = cfg.head_kind()
     attn_b, step_b = 0, 0
     sel_frac = []
     for x in insts:
@@ -284,9 +310,16 @@ def run_decode(args, torch, sa, workloads, workload=None, steps=None, warmup=Non
                    "n_ctx": cfg.n_ctx, "top_p": cfg.top_p if not cfg.top_k else None,
                    "top_k": cfg.top_k or None, "min_tokens": cfg.min_tokens,
                    "sinks": cfg.sinks, "window": cfg.window, "routed": cfg.routed,
-                   "instances_rotated": len(insts),
+                   "instances_rotated": len(insts), "alpha": alpha,
+                   "touched_gib_per_rotation": len(insts) * step_b / 2**30,
                    "launch": "hip_graph" if args.graph else "eager"},
         "step_hbm_gbps": step_b / t_step / 1e9,
+        "step_roofline": {"bound": "hbm", "achieved": step_b / t_step / 1e9,
+                          "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                          "frac": step_b / t_step / 1e9 / PEAK_HBM_GBPS,
+                          "bytes_per_step": step_b,
+                          "note": "whole decode step (index append + selection + attention): "
+                                  "the figure the 128K >= 70% target applies to"},
         "step_bytes": step_b,
         "selected_frac_mean": (sum(sel_frac) / len(sel_frac)) if sel_frac else None,
         "spread_us": {"step": percentiles(per_step), "attention_call": percentiles(per_call),
@@ -385,8 +418,8 @@ def _oracle_decode_sample(cfg, inst, budget_s, torch):
 
 
 def compact(r):
-    keep = ("value", "unit", "ms_per_step", "step_hbm_gbps", "selected_frac_mean", "config",
-            "roofline", "step_tflops")
+    keep = ("value", "unit", "ms_per_step", "step_hbm_gbps", "step_roofline",
+            "selected_frac_mean", "config", "roofline", "step_tflops", "spread_us")
     return {k: r[k] for k in keep if k in r}
 
 
@@ -414,7 +447,12 @@ def main():
         other = {}
         for w in ("llama3_8b_decode_128k_topk", "llama3_8b_decode_128k", "hga_route_decode_64k"):
             other[w] = compact(run_decode(args, torch, sa, workloads, workload=w, steps=20,
-                                          warmup=3, instances=2, cpu=False))
+                                          warmup=3, instances=4, cpu=False))
+        # the 128K top-p step at other attention entropies (query norms x alpha)
+        for a in (0.5, 2.0):
+            other[f"llama3_8b_decode_128k_alpha{a:g}"] = compact(run_decode(
+                args, torch, sa, workloads, workload="llama3_8b_decode_128k", steps=20, warmup=3,
+                instances=4, cpu=False, alpha=a))
         other["pyramid_prefill_128k"] = compact(run_prefill(args, torch, sa, workloads, steps=5,
                                                             warmup=1, cpu=False))
         res["other_workloads"] = other

@@ -28,13 +28,14 @@ Parity pins: every public function here is checked in ``tests/`` against
 something other than itself (a library routine, a closed form, brute force on
 tiny inputs, or a hand-worked fixture).  The parts fixed only by a stated
 reading and not by the pages (the l2 score combination of q and k, the
-high/low frequency cutoff, the tie-break) are pinned to that reading alone:
-"parity unpinned" by the pages, pinned to the stated reading.
+high/low frequency cutoff, the index logit scale 1/sqrt(r), the tie-break)
+are pinned to that reading alone: "parity unpinned" by the pages, pinned to
+the stated reading.
 """
 from .numerics import round_bf16, round_fp32, round_store, bf16_ulp
 from .attention import attend, attend_heads, dense_causal
 from .rope import rope_rotate, rope_angles
-from .lowrank import (index_keys, index_query, index_logits, select_prefix,
+from .lowrank import (index_keys, index_query, index_logits, order, select_prefix,
                       select_topp, select_topk, topp_margin, cut_gap)
 from .local import local_set
 from .hga import (high_freq_pairs, chunk_summary, chunk_summaries, group_summaries,

@@ -51,8 +51,9 @@ def index_logits(q_idx_heads, k_idx, r=None):
     return (np.asarray(k_idx, np.float64) @ qbar) / np.sqrt(r)
 
 
-def _order(logits):
-    """Positions sorted by (logit desc, position asc)."""
+def order(logits):
+    """Positions sorted by (logit desc, position asc): the ranking both
+    selectors cut."""
     logits = np.asarray(logits, np.float64)
     pos = np.arange(logits.shape[0])
     return np.lexsort((pos, -logits))
@@ -60,7 +61,7 @@ def _order(logits):
 
 def select_prefix(logits, m):
     """The first m tokens of the (logit desc, position asc) order, ascending."""
-    return np.sort(_order(logits)[:m]).astype(np.int64)
+    return np.sort(order(logits)[:m]).astype(np.int64)
 
 
 def _topp_count(logits, p):
@@ -68,9 +69,9 @@ def _topp_count(logits, p):
     n = logits.shape[0]
     if p >= 1.0:
         return n
-    order = _order(logits)
+    ranked = order(logits)
     w = np.exp(logits - logits.max())
-    cs = np.cumsum(w[order] / w.sum())
+    cs = np.cumsum(w[ranked] / w.sum())
     hit = np.nonzero(cs >= p)[0]
     return int(hit[0]) + 1 if hit.size else n
 
@@ -93,9 +94,9 @@ def topp_margin(logits, p):
 
     Used to draw inputs whose cut cannot move under last-place rounding."""
     logits = np.asarray(logits, np.float64)
-    order = _order(logits)
+    ranked = order(logits)
     w = np.exp(logits - logits.max())
-    cs = np.cumsum(w[order] / w.sum())
+    cs = np.cumsum(w[ranked] / w.sum())
     m = _topp_count(logits, p)
     hi = cs[m - 1] - p
     lo = p - (cs[m - 2] if m >= 2 else 0.0)
@@ -107,5 +108,5 @@ def cut_gap(logits, m):
     logits = np.asarray(logits, np.float64)
     if m >= len(logits) or m <= 0:
         return np.inf
-    order = _order(logits)
-    return float(logits[order[m - 1]] - logits[order[m]])
+    ranked = order(logits)
+    return float(logits[ranked[m - 1]] - logits[ranked[m]])

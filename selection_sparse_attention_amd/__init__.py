@@ -244,6 +244,16 @@ def decode(params: Params, bufs: Buffers, ws: Optional[Workspace] = None, stream
                                    ctypes.byref(n), _stream(stream)), "decode")
 
 
+def check_selection(sel_count):
+    """Raise SparseAttnError when a selection reported failure: a negative
+    count among ``sel_count`` (a tensor on any device, holding the counts of
+    the rows a selection wrote - slice out groups it does not select for).
+    Reading the counts waits for the selection to finish."""
+    bad = int((sel_count < 0).sum().item())
+    if bad:
+        raise SparseAttnError(SA_ERR_HIP, f"select: {bad} row(s) reported a failed selection")
+
+
 def decode_noalloc(params: Params, bufs: Buffers, stream=None):
     """decode() with the library's static scratch array as its workspace
     (nothing is allocated; concurrent calls on one GPU race)."""

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 
 #include "../../include/sparse_attn.h"
@@ -115,30 +116,33 @@ int32_t pyramid_geom(const sa_params* p, PyrGeom* g) {
 }
 
 // ---------------------------------------------------------------- select ws
-constexpr int kSelTile = 1024;
-
 struct SelectWs {
-  float* logits; uint32_t* cnt1; double* mass1; uint32_t* maxkey; sa::RowState* state;
-  uint64_t* lookback;
-  int tiles; int64_t row_stride; size_t bytes;
+  uint32_t* hist_c; double* hist_m; uint32_t* ctl; uint64_t* slots; uint32_t* cand;
+  size_t bytes;
 };
 
-// The regions that must be zero when a call starts (the level-1 histogram and
-// the row maxima, returned to zero by every call) come first, so their
-// offsets depend on the number of rows only, not on n_ctx.
-SelectWs carve_select(void* ws, int rows, int n) {
+// The regions that must be zero when a call starts (histograms, control words,
+// compaction slots; returned to zero by every call) come first; every size
+// depends on the number of rows only, not on n_ctx.
+SelectWs carve_select(void* ws, int rows) {
   SelectWs s{};
-  s.tiles = (n + kSelTile - 1) / kSelTile;
-  s.row_stride = (int64_t)s.tiles * kSelTile;
   Carver c(ws);
-  s.cnt1 = c.take<uint32_t>((size_t)rows * 4096);
-  s.mass1 = c.take<double>((size_t)rows * 4096);
-  s.maxkey = c.take<uint32_t>((size_t)rows);
-  s.state = c.take<sa::RowState>((size_t)rows);
-  s.lookback = c.take<uint64_t>((size_t)rows * s.tiles);
-  s.logits = c.take<float>((size_t)rows * s.row_stride);
+  s.hist_c = c.take<uint32_t>((size_t)rows * 3 * 4096);
+  s.hist_m = c.take<double>((size_t)rows * 3 * 4096);
+  s.ctl = c.take<uint32_t>((size_t)rows * sa::kCtlWords);
+  s.slots = c.take<uint64_t>((size_t)rows * sa::kMaxSelW);
+  s.cand = c.take<uint32_t>((size_t)rows * sa::kCap);
   s.bytes = c.size();
   return s;
+}
+
+// Polls per cross-workgroup wait of the selector: about a second at the
+// default.  SPARSE_ATTN_SPIN_LIMIT overrides it (a negative value fails every
+// wait at once: a diagnostic for the failure path).
+int select_spin_limit() {
+  const char* e = std::getenv("SPARSE_ATTN_SPIN_LIMIT");
+  if (e && *e) return std::atoi(e);
+  return 1 << 20;
 }
 
 // ---------------------------------------------------------------- decode ws
@@ -368,17 +372,29 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
     if (mode == SA_SEL_TOPK && p->top_k < 1) return SA_ERR_INVALID_ARG;
     GroupList gl = groups_of_kind(p, kinds, SA_HEAD_RETRIEVAL);
     const int rows = p->batch * gl.n;
-    SelectWs sw = carve_select(nullptr, rows, p->n_ctx);
+    SelectWs sw = carve_select(nullptr, rows);
     if ((st = workspace_gate(ws, ws_bytes, sw.bytes))) return st < 0 ? st : SA_OK;
     if (gl.n == 0) return SA_OK;
     if (!b->q_idx || !b->k_idx || !b->sel_idx || !b->sel_count) return SA_ERR_INVALID_ARG;
     if (!aligned16(b->k_idx)) return SA_ERR_INVALID_ARG;
-    sw = carve_select(ws, rows, p->n_ctx);
+    const bool mass = mode == SA_SEL_TOPP;
+    // tokens per workgroup: the smallest tile giving at most two workgroups
+    // per compute unit over all rows.  The workgroups of a row wait for each
+    // other, so all of them must be resident together: W stays within the
+    // compute units (each holds at least one), which covers 1M tokens.
+    const int cus = compute_units();
+    const int wmax = std::min(cus, sa::kMaxSelW);
+    auto tiles = [&](int per) { return (p->n_ctx + 256 * per - 1) / (256 * per); };
+    int per = 4;
+    while (per < 16 && ((int64_t)rows * tiles(per) > 2 * cus || tiles(per) > wmax)) per *= 2;
+    const int W = tiles(per);
+    if (W > wmax) return SA_ERR_UNSUPPORTED;
+    sw = carve_select(ws, rows);
     sa::SelectArgs a{};
     a.q_idx = b->q_idx; a.k_idx = b->k_idx; a.sel_idx = b->sel_idx; a.sel_count = b->sel_count;
     a.B = p->batch; a.Hq = p->n_q_heads; a.Hkv = p->n_kv_heads; a.n = p->n_ctx; a.n_cap = p->n_cap;
     a.G = G;
-    if (mode == SA_SEL_TOPP) {
+    if (mass) {
       a.use_mass = 1;
       a.top_p = p->top_p;
       a.target_count = p->min_tokens;
@@ -388,11 +404,11 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
       a.target_count = p->top_k;
       a.select_all = (p->top_k >= p->n_ctx) ? 1 : 0;
     }
-    a.tiles = sw.tiles; a.row_stride = sw.row_stride;
-    a.logits = sw.logits; a.cnt1 = sw.cnt1; a.mass1 = sw.mass1; a.maxkey = sw.maxkey;
-    a.state = sw.state;
-    a.lookback = sw.lookback; a.groups = gl;
-    return hip_status(sa::launch_select_lowrank(a, p->dtype, s));
+    a.W = W;
+    a.spin_limit = select_spin_limit();
+    a.hist_c = sw.hist_c; a.hist_m = sw.hist_m; a.ctl = sw.ctl; a.slots = sw.slots; a.cand = sw.cand;
+    a.groups = gl;
+    return hip_status(sa::launch_select_lowrank(a, p->dtype, per, s));
   }
   if (mode == SA_SEL_ROUTE2) {
     if (p->chunk < 1 || p->group < 1 || p->chunk % p->group) return SA_ERR_INVALID_ARG;

@@ -50,21 +50,14 @@ struct PyramidArgs {
 };
 
 // ---------------------------------------------------------------- select
-// Per-row (sequence, retrieval group) state of the radix selector.
-struct RowState {
-  double R;             // reference logit: masses are exp(l - R)
-  double target_mass;   // p * total mass
-  double mass_above;    // mass of tokens above the current key prefix
-  int64_t count_above;  // tokens above the current key prefix
-  int32_t target_count; // min_tokens or k
-  uint32_t prefix;      // key bits fixed so far
-  int32_t crit;         // bit0: mass criterion live, bit1: count criterion live
-  int32_t all;          // 1: every token is selected
-  uint32_t cut_key;     // final key of the last selected token
-  int32_t need;         // tokens taken among those whose key == cut_key
-  int32_t m;            // selected count
-  int32_t err;
-};
+constexpr int kCap = 8192;         // candidate keys per row resolved in LDS
+constexpr int kMaxSelW = 512;      // workgroups per selector row
+// per-row control words of the selector workspace
+constexpr int kCtlArrive = 0;      // four arrival counters (three global rounds, candidates)
+constexpr int kCtlCand = 4;        // candidate count
+constexpr int kCtlErr = 5;         // a wait timed out
+constexpr int kCtlDepart = 6;      // workgroups that have left
+constexpr int kCtlWords = 16;
 
 struct SelectArgs {
   const float* q_idx;    // [B,Hq,16]
@@ -76,14 +69,14 @@ struct SelectArgs {
   int32_t select_all;    // every token is kept (no ranking needed)
   double top_p;
   int32_t target_count;  // top-k: k ; top-p: min_tokens (0 = none)
-  int32_t tiles;         // tiles per row
-  int64_t row_stride;    // logits stride per row (tiles * tile)
-  // workspace
-  float* logits;         // [rows, row_stride]
-  uint32_t* cnt1; double* mass1;   // [rows, 4096]: level-1 histogram, zero between calls
-  uint32_t* maxkey;      // [rows]: largest order key of the row's logits, zero between calls
-  RowState* state;       // [rows]: the cut found by the row kernel
-  uint64_t* lookback;    // [rows, tiles]: compaction prefix flags
+  int32_t W;             // workgroups per row
+  int32_t spin_limit;    // polls per cross-workgroup wait (< 0: every wait fails)
+  // workspace; everything but `cand` is zero between calls
+  uint32_t* hist_c;      // [rows, 3, 4096] counts of the three global digits
+  double* hist_m;        // [rows, 3, 4096] masses of the three global digits
+  uint32_t* ctl;         // [rows, kCtlWords]
+  uint64_t* slots;       // [rows, kMaxSelW] compaction counts
+  uint32_t* cand;        // [rows, kCap] candidate keys
   GroupList groups;
 };
 
@@ -149,7 +142,7 @@ struct PrefillArgs {
 hipError_t launch_index_lowrank(const IndexLowrankArgs& a, int dtype, int d, hipStream_t s);
 hipError_t launch_summary(const SummaryArgs& a, int dtype, int d, hipStream_t s);
 hipError_t launch_pyramid(const PyramidArgs& a, int dtype, int d, hipStream_t s);
-hipError_t launch_select_lowrank(const SelectArgs& a, int dtype, hipStream_t s);
+hipError_t launch_select_lowrank(const SelectArgs& a, int dtype, int per, hipStream_t s);
 hipError_t launch_route(const RouteArgs& a, int dtype, int d, hipStream_t s);
 hipError_t launch_pyramid_select(const PyrSelectArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, hipStream_t s);

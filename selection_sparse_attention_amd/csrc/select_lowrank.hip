@@ -9,39 +9,53 @@
 //          >= p (top-p; raised to min_tokens), or the first k (top-k).
 //
 // The cut is found without sorting (the summary describes a sort-free,
-// histogram-based threshold): logits are mapped to order-preserving 32-bit
-// keys and resolved by three radix levels (12 + 12 + 8 bits).
+// histogram-based threshold): logits map to order-preserving 32-bit keys and
+// the cut key is resolved digit by digit over histograms of counts and fp64
+// masses.  One launch does the whole selection.  A row is split over W
+// workgroups, each holding its tile of logits in registers from start to end
+// (the logits never go to memory):
 //
-//   scan (2K-token tiles x rows)  logits to the workspace (4 B/token) + level-1
-//                        histogram of counts and fp64 masses, merged into the
-//                        row's histogram with atomics
-//   row  (rows)          one 1024-thread workgroup per row: the level-1 cut
-//                        from the merged histogram held in registers, then
-//                        the logits of the cut bucket gathered into LDS and
-//                        levels 2 and 3 over them (LDS histograms): the exact
-//                        cut key and how many of its ties to keep
-//   compact (tiles x rows) ascending positions, via a decoupled look-back
+//   1. logits of the tile; LDS histogram of the top 12 key bits; merged into
+//      the row's histogram in the workspace with returning atomics; arrival.
+//   2. after every workgroup of the row has arrived, each reads the merged
+//      histogram and takes the same level-1 decision: the bucket holding the
+//      cut, with the count and mass above it.
+//   3. the keys of that bucket's tokens (normally a few thousand per row) are
+//      published to the row's candidate list; after a second arrival every
+//      workgroup loads them into LDS and resolves the remaining 20 bits there
+//      (two 10-bit digits): the exact cut key and how many of its ties to
+//      keep.  A bucket with more than kCap tokens takes one more global round
+//      (bits 19..8), then candidates or a last global round (bits 7..0).
+//   4. compaction: each workgroup publishes its (above-cut, tie) counts in a
+//      64-bit slot, sums its predecessors' slots and writes its selected
+//      positions in ascending order.
+//   5. the last workgroup of the row to leave writes sel_count (-1 when a
+//      wait timed out) and returns the row's histograms, counters and slots to
+//      zero, so a workspace that starts zero-filled stays reusable.
 //
-// Only the scan reads the 32 B/token index; the row kernel and the
-// compaction read the row's 4 B/token logits once each.  Level-1 masses are taken relative
-// to each bucket's upper bound - a data-independent reference, so tile
-// histograms add without knowing the maximum - and rescaled to the top
-// bucket's bound R when the row kernel reads them (the scan also records the
-// row's largest key); later levels use R directly.  The row kernel zeroes the
-// row's level-1 histogram and largest key after reading them, and the scan
-// clears the compaction's look-back words, so a workspace that starts
-// zero-filled stays reusable.
+// Everything that crosses workgroups goes through agent-scope atomics
+// (coherent across the dies' L2 caches): histogram adds and candidate writes
+// return values that are consumed before the arrival is signalled, so they
+// are performed by then, and every read of such data is an agent-coherent
+// (sc1) load.  No fence is used.  A workgroup waits only for workgroups of
+// its own row, and the host keeps W within what the device runs at once (see
+// the launcher), so every wait ends; each is bounded anyway by a spin limit.
+//
+// Level-1 masses are accumulated relative to each bucket's upper bound (a
+// data-independent reference, so tiles add without knowing the maximum) and
+// rescaled to R = the upper bound of the row's highest non-empty bucket when
+// the merged histogram is read; later digits use R directly.
 #include "args.hpp"
 #include "common.hpp"
 
 namespace sa {
 
-constexpr int kTile = 1024;        // tokens per compaction workgroup
-constexpr int kScanTile = 2048;    // tokens per scan workgroup (two compaction tiles)
 constexpr int kThreads = 256;
-constexpr int kPer = kTile / kThreads;
-constexpr int kScanPer = kScanTile / kThreads;
-constexpr int kSpinLimit = 1 << 24;
+constexpr int kWaves = kThreads / 64;
+constexpr int kNB1 = 4096;          // level-1 and level-2 buckets (12 bits)
+constexpr int kNB3 = 256;           // level-3 buckets (8 bits)
+constexpr int kNBL = 1024;          // local candidate digits (10 bits)
+constexpr uint64_t kSlotFlag = 1ull << 63;
 
 enum : int { CRIT_MASS = 1, CRIT_COUNT = 2 };
 
@@ -56,21 +70,20 @@ __device__ __forceinline__ double bucket_hi(uint32_t b, int shift) {
   return (double)key_to_float(top);
 }
 
-// Add a tile's LDS histogram into the row's histogram (non-empty buckets).
-template <int NB>
-__device__ __forceinline__ void merge_hist(const uint32_t* lc, const double* lw, uint32_t* gc,
-                                           double* gw, bool mass) {
-  for (int i = threadIdx.x; i < NB; i += kThreads) {
-    const uint32_t c = lc[i];
-    if (c) {
-      atomicAdd(gc + i, c);
-      if (mass) unsafeAtomicAdd(gw + i, lw[i]);
-    }
-  }
+// Agent-coherent loads through a buffer resource (sc1: not served from a
+// die's possibly stale cache lines).
+constexpr int kSc1 = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, 0x7FFFFFFF, 0x00020000);
+}
+__device__ __forceinline__ vl_u32x4 ld_sc1_u32x4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(vl_u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1));
 }
 
-// ------------------------------------------------------------------ scan
-// Raw 32-byte index rows of one token, requested before any is used.
+// Make the compiler wait for a value (a returned atomic) before going on.
+__device__ __forceinline__ void consume(uint32_t v) { asm volatile("" ::"v"(v)); }
+
+// ------------------------------------------------------------------ index rows
 template <typename T> struct IdxRow;
 template <> struct IdxRow<bf16_t> {
   vl_u32x4 w[2];
@@ -105,640 +118,609 @@ template <> struct IdxRow<float> {
   }
 };
 
-template <typename T, bool MASS>
-__global__ __launch_bounds__(kThreads) void select_scan_kernel(SelectArgs a) {
-  __shared__ uint32_t lc[4096];
-  __shared__ double lw[MASS ? 4096 : 1];
-  __shared__ uint32_t s_kmax[kThreads / 64];
-  const int row = blockIdx.y, tile = blockIdx.x, tid = threadIdx.x;
-  int b, g;
-  row_coords(a, row, b, g);
-  // the tile's index rows first (tokens past the end re-read the last one),
-  // so their latency overlaps everything up to the first use
-  const int64_t krow = ((int64_t)b * a.Hkv + g) * a.n_cap;
-  IdxRow<T> kr[kScanPer];
-#pragma unroll
-  for (int i = 0; i < kScanPer; ++i)
-    kr[i].load(a.k_idx, krow + min(tile * kScanTile + i * kThreads + tid, a.n - 1));
+// ------------------------------------------------------------------ shared state
+// The cut as it is resolved, held identically by every thread.
+struct Cut {
+  double R;             // reference logit: masses are exp(l - R)
+  double tmass;         // p * total mass
+  double above_w;       // mass of the tokens above the current prefix
+  int64_t above_c;      // tokens above the current prefix
+  int64_t tcount;       // count target (k, or min_tokens)
+  uint32_t prefix;      // the key's top `bits` bits
+  int bits;             // bits fixed so far
+  int crit;             // live criteria
+  int all;              // every token is selected
+  uint32_t in_count;    // tokens carrying the prefix
+  int32_t need;         // final: ties kept among keys == prefix (bits == 32)
+};
 
-  for (int i = tid; i < 4096; i += kThreads) { lc[i] = 0; if (MASS) lw[i] = 0.0; }
-  // the compaction's look-back words of this call start empty
-  if (tid < kScanTile / kTile && tile * (kScanTile / kTile) + tid < a.tiles)
-    a.lookback[(int64_t)row * a.tiles + tile * (kScanTile / kTile) + tid] = 0;
-
-  // qbar: mean of the group's index queries (exact for power-of-two G on
-  // lattice inputs)
-  float qb[16];
-#pragma unroll
-  for (int c = 0; c < 16; ++c) qb[c] = 0.f;
-  for (int hh = 0; hh < a.G; ++hh) {
-    const float* qp = a.q_idx + ((int64_t)b * a.Hq + g * a.G + hh) * 16;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) qb[c] += qp[c];
-  }
-  const float invG = 1.0f / (float)a.G;
-#pragma unroll
-  for (int c = 0; c < 16; ++c) qb[c] *= invG;
-  lds_barrier();
-
-  float* lg = a.logits + (int64_t)row * a.row_stride;
-  uint32_t kmax = 0;
-#pragma unroll
-  for (int i = 0; i < kScanPer; ++i) {
-    const int j = tile * kScanTile + i * kThreads + tid;
-    if (j < a.n) {
-      float l = kr[i].dot(qb) * 0.25f;
-      if (l == 0.f) l = 0.f;                       // fold -0 into +0
-      lg[j] = l;
-      const uint32_t key = order_key(l);
-      kmax = max(kmax, key);
-      const uint32_t bk = key >> 20;
-      atomicAdd(&lc[bk], 1u);
-      if (MASS) atomicAdd(&lw[bk], exp((double)l - bucket_hi(bk, 20)));
-    }
-  }
-  // the row's largest key (its top bucket's bound is the row kernel's
-  // reference for the masses): one atomic per workgroup
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, m));
-  if ((tid & 63) == 0) s_kmax[tid >> 6] = kmax;
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t km = s_kmax[0];
-#pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) km = max(km, s_kmax[w]);
-    if (km) atomicMax(a.maxkey + row, km);
-  }
-  merge_hist<4096>(lc, lw, a.cnt1 + (int64_t)row * 4096, a.mass1 + (int64_t)row * 4096, MASS);
-}
-
-// ------------------------------------------------------------------ row
-constexpr int kRowThreads = 1024;
-constexpr int kRowWaves = kRowThreads / 64;
-constexpr int kRowU = 8;                              // float4 per thread per chunk
-constexpr int kRowChunk = kRowThreads * kRowU * 4;    // tokens per chunk (32 per thread)
-constexpr int kCand = 8192;        // logits of the level-1 cut bucket kept in LDS
-
-typedef uint32_t sel_u32x4 __attribute__((ext_vector_type(4)));
-typedef double sel_f64x2 __attribute__((ext_vector_type(2)));
-typedef float sel_f32x4 __attribute__((ext_vector_type(4)));
-
-// Buckets of one level where the mass and the count targets are crossed, as
-// published by the threads that own them (-1: not crossed in this level).
+// Crossing of one criterion inside a level, as published by its owner.
 struct Cross {
-  int bm, bc;
-  double bm_w, bc_w;          // mass above the crossing bucket
-  int64_t bm_c, bc_c;         // count above the crossing bucket
+  int b;                // bucket, -1: none
+  double w;             // mass above it
+  int64_t c;            // count above it
 };
 
-struct RowShared {
-  double wave_w[3][kRowWaves];     // per level: inclusive wave totals
-  int64_t wave_c[3][kRowWaves];
-  uint32_t cand_w[2][kRowWaves];   // candidate counts, alternating per chunk
-  Cross x[3];
+template <bool MASS>
+struct SelShared {
+  union {
+    struct {            // level histograms (global rounds)
+      uint32_t c[kNB1];
+      double m[MASS ? kNB1 : 1];
+    } h;
+    struct {            // candidates and their local digits
+      uint32_t key[kCap];
+      uint32_t c[kNBL];
+      double m[MASS ? kNBL : 1];
+    } r;
+  } u;
+  double wave_w[kWaves];
+  int64_t wave_c[kWaves];
+  Cross xm, xc;
+  uint32_t top;         // highest non-empty bucket
+  uint32_t base;        // candidate slot base
+  uint32_t cnt_s[16][kWaves], cnt_t[16][kWaves];
+  uint64_t pre;         // (strict, tie) counts before this workgroup
+  int bad;              // a wait of this workgroup timed out
+  int last;             // this workgroup left the row last
 };
 
-// A 32- or 64-bit value of one lane (the lane index is wave-uniform), or of
-// the first active lane: the result lives in scalar registers.
-template <typename T>
-__device__ __forceinline__ T lane_value(T v, int src) {
-  if constexpr (sizeof(T) == 4) {
-    return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
-  } else {
-    const uint64_t u = __builtin_bit_cast(uint64_t, v);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, src);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), src);
-    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+// Wait until *ctr reaches `target` (one thread).  Returns false when the
+// spin limit runs out (a negative limit fails every wait at once).
+__device__ __forceinline__ bool wait_count(const uint32_t* ctr, uint32_t target, int limit) {
+  if (limit < 0) return false;
+  for (int s = 0; s <= limit; ++s) {
+    if (ld_agent(ctr) >= target) return true;
+    __builtin_amdgcn_s_sleep(1);
   }
-}
-template <typename T>
-__device__ __forceinline__ T uniform(T v) {
-  if constexpr (sizeof(T) == 4) {
-    return __builtin_bit_cast(T, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
-  } else {
-    const uint64_t u = __builtin_bit_cast(uint64_t, v);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
-    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
-  }
+  return false;
 }
 
-// One radix level.  Thread t owns the PER buckets NB-1-PER*t ... NB-PER*t
-// (descending key order), their counts c[] and masses w[] in registers.  The
-// prefix above each thread's buckets comes from wave scans and, across the
-// workgroup's waves, one barrier and a 16-lane scan of the wave totals (with
-// ONE_WAVE a single wave owns every bucket and no barrier is needed).  The
-// owners of the crossing buckets publish them and every thread takes the same
-// decision, in scalar registers, into its copy of the row state `st`.  The
-// histogram hc / hw in LDS is read only by the rare fallback below and, at
-// level 3, for the tie count.
-template <int LEVEL, bool MASS, int PER, int NB, bool ONE_WAVE>
-__device__ __forceinline__ void cut_level(const SelectArgs& a, const uint32_t (&c)[PER],
-                                          const double (&w)[PER], bool owns, RowState& st,
-                                          RowShared& sh, const uint32_t* hc, const double* hw) {
-  constexpr int BITS = (NB == 4096) ? 12 : 8;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int owner = ONE_WAVE ? lane : tid;
+// Block-wide inclusive prefix (thread order) of one double and one int64 with
+// their block totals; LDS-only barriers.
+template <bool MASS>
+__device__ __forceinline__ void block_scan2(double tw, int64_t tc, SelShared<MASS>& sh, double& pre_w,
+                                            int64_t& pre_c, double& tot_w, int64_t& tot_c) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const double iw = MASS ? wave_inclusive_scan(tw) : 0.0;
+  const int64_t ic = wave_inclusive_scan(tc);
+  if (lane == 63) { sh.wave_w[wid] = iw; sh.wave_c[wid] = ic; }
+  lds_barrier();
+  double bw = 0.0, aw = 0.0;
+  int64_t bc = 0, ac = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const double x = MASS ? sh.wave_w[w] : 0.0;
+    const int64_t y = sh.wave_c[w];
+    if (w < wid) { bw += x; bc += y; }
+    aw += x;
+    ac += y;
+  }
+  pre_w = bw + iw - tw;
+  pre_c = bc + ic - tc;
+  tot_w = aw;
+  tot_c = ac;
+}
+
+// One digit of the cut.  Thread t owns the PER buckets NB-1-PER*t ...
+// NB-PER*t (descending key order) with counts c[] and masses w[] (relative to
+// R).  `first` marks level 1, where the mass target is p times the total.
+// Every thread ends with the same updated cut.
+template <int NB, bool MASS>
+__device__ void cut_digit(const SelectArgs& a, const uint32_t (&c)[NB / kThreads],
+                          const double (&w)[NB / kThreads], bool first, Cut& ct,
+                          SelShared<MASS>& sh, int dbits, const uint32_t* hc, const double* hm) {
+  constexpr int PER = NB / kThreads;
+  const int tid = threadIdx.x;
   double tw = 0.0;
   int64_t tc = 0;
-  if (owns) {
+#pragma unroll
+  for (int k = 0; k < PER; ++k) { if (MASS) tw += w[k]; tc += c[k]; }
+  double pre_w, tot_w;
+  int64_t pre_c, tot_c;
+  block_scan2<MASS>(tw, tc, sh, pre_w, pre_c, tot_w, tot_c);
+  if (first && MASS) ct.tmass = tot_w * a.top_p;
+  const double tmass = ct.tmass;
+  const int64_t tcount = ct.tcount;
+  const int crit = ct.crit;
+  if (tid == 0) { sh.xm.b = -1; sh.xc.b = -1; }
+  lds_barrier();
+  {
+    double cw = ct.above_w + pre_w;
+    int64_t cc = ct.above_c + pre_c;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      if (MASS) tw += w[k];
-      tc += c[k];
-    }
-  }
-  const double iw = wave_inclusive_scan(tw);
-  const int64_t ic = wave_inclusive_scan(tc);
-  double pre_w, totw;
-  int64_t pre_c, totc;
-  if constexpr (ONE_WAVE) {
-    pre_w = iw - tw;
-    pre_c = ic - tc;
-    totw = lane_value(iw, 63);
-    totc = lane_value(ic, 63);
-  } else {
-    if (lane == 63) {
-      sh.wave_w[LEVEL - 1][wid] = iw;
-      sh.wave_c[LEVEL - 1][wid] = ic;
-    }
-    lds_barrier();
-    // every 16-lane row holds the wave totals; their inclusive prefix
-    double pw = sh.wave_w[LEVEL - 1][lane & 15];
-    int64_t pc = sh.wave_c[LEVEL - 1][lane & 15];
-    pw += dpp_move<0x111, 0xF>(pw); pc += dpp_move<0x111, 0xF>(pc);
-    pw += dpp_move<0x112, 0xF>(pw); pc += dpp_move<0x112, 0xF>(pc);
-    pw += dpp_move<0x114, 0xF>(pw); pc += dpp_move<0x114, 0xF>(pc);
-    pw += dpp_move<0x118, 0xF>(pw); pc += dpp_move<0x118, 0xF>(pc);
-    totw = lane_value(pw, kRowWaves - 1);
-    totc = lane_value(pc, kRowWaves - 1);
-    const double bw = wid ? lane_value(pw, wid - 1) : 0.0;
-    const int64_t bcn = wid ? lane_value(pc, wid - 1) : 0;
-    pre_w = bw + iw - tw;
-    pre_c = bcn + ic - tc;
-  }
-  const int crit = st.crit;
-  const double tmass = (LEVEL == 1) ? totw * a.top_p : st.target_mass;
-  const double base_w = (LEVEL == 1) ? 0.0 : st.mass_above;
-  const int64_t base_c = (LEVEL == 1) ? 0 : st.count_above;
-  const int64_t tcount = st.target_count;
-  // this thread's crossings, if any
-  int my_bm = -1, my_bc = -1;
-  double my_bm_w = 0.0, my_bc_w = 0.0;
-  int64_t my_bm_c = 0, my_bc_c = 0;
-  if (owns) {
-    double cw = base_w + pre_w;
-    int64_t cc = base_c + pre_c;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int bk = NB - 1 - (PER * owner + k);
+      const int bk = NB - 1 - (PER * tid + k);
       const double nw = cw + (MASS ? w[k] : 0.0);
       const int64_t nc = cc + c[k];
-      if ((crit & CRIT_MASS) && c[k] && cw < tmass && nw >= tmass) { my_bm = bk; my_bm_w = cw; my_bm_c = cc; }
-      if ((crit & CRIT_COUNT) && c[k] && cc < tcount && nc >= tcount) { my_bc = bk; my_bc_w = cw; my_bc_c = cc; }
+      if ((crit & CRIT_MASS) && c[k] && cw < tmass && nw >= tmass) { sh.xm.b = bk; sh.xm.w = cw; sh.xm.c = cc; }
+      if ((crit & CRIT_COUNT) && c[k] && cc < tcount && nc >= tcount) { sh.xc.b = bk; sh.xc.w = cw; sh.xc.c = cc; }
       cw = nw;
       cc = nc;
     }
   }
-  int bm, bc;
-  double bm_w, bc_w;
-  int64_t bm_c, bc_c;
-  if constexpr (ONE_WAVE) {
-    const uint64_t fm = __ballot(my_bm >= 0), fc = __ballot(my_bc >= 0);
-    const int lm = fm ? __ffsll((unsigned long long)fm) - 1 : 0;
-    const int lc = fc ? __ffsll((unsigned long long)fc) - 1 : 0;
-    bm = fm ? lane_value(my_bm, lm) : -1;
-    bm_w = lane_value(my_bm_w, lm);
-    bm_c = lane_value(my_bm_c, lm);
-    bc = fc ? lane_value(my_bc, lc) : -1;
-    bc_w = lane_value(my_bc_w, lc);
-    bc_c = lane_value(my_bc_c, lc);
-  } else {
-    Cross& x = sh.x[LEVEL - 1];
-    if (my_bm >= 0) { x.bm = my_bm; x.bm_w = my_bm_w; x.bm_c = my_bm_c; }
-    if (my_bc >= 0) { x.bc = my_bc; x.bc_w = my_bc_w; x.bc_c = my_bc_c; }
-    lds_barrier();
-    bm = uniform(x.bm);
-    bm_w = uniform(x.bm_w);
-    bm_c = uniform(x.bm_c);
-    bc = uniform(x.bc);
-    bc_w = uniform(x.bc_w);
-    bc_c = uniform(x.bc_c);
-  }
-  if (LEVEL == 1) st.target_mass = tmass;
+  lds_barrier();
+  Cross xm = sh.xm, xc = sh.xc;
   const bool m_on = (crit & CRIT_MASS) != 0, c_on = (crit & CRIT_COUNT) != 0;
-  if (LEVEL > 1 && m_on && bm < 0) {
-    // The previous level placed the crossing inside this prefix; a last-place
-    // disagreement between the two levels' mass sums lands it on the first or
-    // last non-empty bucket (rare: a serial walk is fine).
+  if (!first && m_on && xm.b < 0) {
+    // the previous digit placed the mass crossing inside this prefix; a
+    // last-place disagreement between the two digits' sums puts it on the
+    // first or last non-empty bucket here (rare: a serial walk is fine)
+    // (hc / hm: this digit's histogram in LDS, bucket i at index i)
+    const bool above = ct.above_w >= tmass;
     int hi_b = -1, lo_b = -1;
     for (int bk = NB - 1; bk >= 0; --bk)
       if (hc[bk]) { if (hi_b < 0) hi_b = bk; lo_b = bk; }
-    bm = (base_w >= tmass) ? hi_b : lo_b;
-    bm_w = base_w;
-    bm_c = base_c;
-    for (int bk = NB - 1; bk > bm && bm >= 0; --bk) { if (MASS) bm_w += hw[bk]; bm_c += hc[bk]; }
+    xm.b = above ? hi_b : lo_b;
+    xm.w = ct.above_w;
+    xm.c = ct.above_c;
+    for (int bk = NB - 1; bk > xm.b && xm.b >= 0; --bk) { if (MASS) xm.w += hm[bk]; xm.c += hc[bk]; }
   }
-  // the mass crossing decides unless the count crossing lies further down the
-  // order (a lower bucket); both stay live while they share a bucket
+  // the mass crossing decides unless the count crossing lies further down
+  // the order (a lower bucket); both stay live while they share a bucket
   int bstar, ncrit;
   if (m_on && c_on) {
-    const bool mass_wins = (bc < 0) || (bm >= 0 && bm < bc);
-    const bool count_wins = (bm >= 0) && (bc >= 0) && (bc < bm);
-    bstar = count_wins ? bc : bm;
+    const bool mass_wins = (xc.b < 0) || (xm.b >= 0 && xm.b < xc.b);
+    const bool count_wins = (xm.b >= 0) && (xc.b >= 0) && (xc.b < xm.b);
+    bstar = count_wins ? xc.b : xm.b;
     ncrit = mass_wins ? CRIT_MASS : (count_wins ? CRIT_COUNT : (CRIT_MASS | CRIT_COUNT));
   } else {
-    bstar = m_on ? bm : bc;
+    bstar = m_on ? xm.b : xc.b;
     ncrit = crit;
   }
-  if (bstar < 0) {                   // the target lies past the last token
-    st.all = 1;                      // every key lies above cut_key 0
-    st.m = a.n;
-    st.cut_key = 0;
-    st.need = 0;
+  if (bstar < 0) {             // the target lies past the last token
+    ct.all = 1;
     return;
   }
-  const bool from_mass = (bstar == bm) && m_on;
-  const double above_w = from_mass ? bm_w : bc_w;
-  const int64_t above_c = from_mass ? bm_c : bc_c;
-  const uint32_t prefix = (LEVEL == 1) ? (uint32_t)bstar : ((st.prefix << BITS) | (uint32_t)bstar);
-  st.mass_above = above_w;
-  st.count_above = above_c;
-  st.crit = ncrit;
-  st.prefix = prefix;
-  if (LEVEL == 3) {
-    const int64_t ties = hc[bstar];
+  const bool from_mass = (bstar == xm.b) && m_on;
+  ct.above_w = from_mass ? xm.w : xc.w;
+  ct.above_c = from_mass ? xm.c : xc.c;
+  ct.crit = ncrit;
+  ct.prefix = (ct.bits == 0) ? (uint32_t)bstar : ((ct.prefix << dbits) | (uint32_t)bstar);
+  ct.bits += dbits;
+  // the chosen bucket's count: its owner's c[] entry, through LDS
+  const int owner = (NB - 1 - bstar) / PER, k = (NB - 1 - bstar) % PER;
+  if (tid == owner) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) if (q == k) v = c[q];
+    sh.top = v;
+  }
+  lds_barrier();
+  ct.in_count = sh.top;
+  lds_barrier();
+  if (ct.bits == 32) {
+    // every token left carries the same key: how many of them to keep
+    const int64_t ties = ct.in_count;
     int64_t need = 1;
     if (ncrit & CRIT_MASS) {
-      const double e = exp((double)key_to_float(prefix) - st.R);
-      const double cn = ceil((tmass - above_w) / e);
+      const double e = exp((double)key_to_float(ct.prefix) - ct.R);
+      const double cn = ceil((tmass - ct.above_w) / e);
       need = (cn >= (double)ties) ? ties : (cn <= 1.0 ? 1 : (int64_t)cn);
     }
     if (ncrit & CRIT_COUNT) {
-      const int64_t nc = tcount - above_c;
+      const int64_t nc = tcount - ct.above_c;
       need = need > nc ? need : nc;
     }
     if (need > ties) need = ties;
     if (need < 1) need = 1;
-    st.cut_key = prefix;
-    st.need = (int32_t)need;
-    st.m = (int32_t)(above_c + need);
+    ct.need = (int32_t)need;
   }
 }
 
-// Histogram of the next radix digit of the row's logits whose keys carry the
-// current prefix (level 2: bits 19..8, level 3: bits 7..0), streamed from the
-// workspace: the fallback when the cut bucket holds more than kCand logits.
-template <int LEVEL, bool MASS>
-__device__ void level_hist(const SelectArgs& a, const float* lg, const RowState& st, uint32_t* s_c,
-                           double* s_w) {
-  constexpr int NB = (LEVEL == 2) ? 4096 : 256;
-  constexpr int SHIFT = (LEVEL == 2) ? 8 : 0;
-  constexpr int PSHIFT = (LEVEL == 2) ? 20 : 8;
-  const int tid = threadIdx.x;
-  for (int i = tid; i < NB; i += kRowThreads) { s_c[i] = 0; if (MASS) s_w[i] = 0.0; }
-  __syncthreads();
-  const uint32_t prefix = st.prefix;
-  const double R = st.R;
-  const int last = (int)a.row_stride - 4;
-  for (int c0 = 0; c0 < a.n; c0 += kRowChunk) {
-    sel_f32x4 v[kRowU];
-#pragma unroll
-    for (int k = 0; k < kRowU; ++k)
-      v[k] = *reinterpret_cast<const sel_f32x4*>(lg + min(c0 + 4 * (tid + k * kRowThreads), last));
-#pragma unroll
-    for (int k = 0; k < kRowU; ++k) {
-      const int j = c0 + 4 * (tid + k * kRowThreads);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t key = order_key(v[k][i]);
-        if (j + i < a.n && (key >> PSHIFT) == prefix) {
-          const uint32_t bk = (key >> SHIFT) & (NB - 1);
-          atomicAdd(&s_c[bk], 1u);
-          if (MASS) atomicAdd(&s_w[bk], exp((double)v[k][i] - R));
-        }
-      }
-    }
-  }
-  __syncthreads();
-}
-
-// One workgroup per row: every radix level after the scan's, leaving the
-// row's cut (key, ties to keep, count) in the workspace for the compaction.
-// Every thread holds the row state; the barriers order LDS only, so the first
-// chunk of logits, requested at the start, stays in flight through level 1.
-template <bool MASS>
-__global__ __launch_bounds__(kRowThreads) void select_row_kernel(SelectArgs a) {
-  __shared__ uint32_t s_c[4096];                 // level-2 histogram
-  __shared__ double s_w[MASS ? 4096 : 1];
-  __shared__ uint32_t s_c3[256];                 // level-3 histogram
-  __shared__ double s_w3[MASS ? 256 : 1];
-  __shared__ float s_cand[kCand];
-  __shared__ RowShared sh;
-  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-
-  // level 1: this thread's four buckets of the histogram merged by the scan
-  // (returned to zero here), and the row's largest key
-  uint32_t* gc = a.cnt1 + (int64_t)row * 4096;
-  double* gw = a.mass1 + (int64_t)row * 4096;
-  const int b0 = 4092 - 4 * tid;                 // buckets b0 .. b0 + 3
-  const sel_u32x4 c4 = *reinterpret_cast<const sel_u32x4*>(gc + b0);
-  sel_f64x2 w4[2] = {{0.0, 0.0}, {0.0, 0.0}};
-  if (MASS) {
-    w4[0] = *reinterpret_cast<const sel_f64x2*>(gw + b0);
-    w4[1] = *reinterpret_cast<const sel_f64x2*>(gw + b0 + 2);
-  }
-  const uint32_t mk = a.maxkey[row];
-  // first chunk of the row's logits (addresses clamped into the row)
-  const float* lg = a.logits + (int64_t)row * a.row_stride;
-  const int last = (int)a.row_stride - 4;
-  sel_f32x4 v[kRowU];
-#pragma unroll
-  for (int k = 0; k < kRowU; ++k)
-    v[k] = *reinterpret_cast<const sel_f32x4*>(lg + min(4 * (tid + k * kRowThreads), last));
-  *reinterpret_cast<sel_u32x4*>(gc + b0) = sel_u32x4{0u, 0u, 0u, 0u};
-  if (MASS) {
-    *reinterpret_cast<sel_f64x2*>(gw + b0) = sel_f64x2{0.0, 0.0};
-    *reinterpret_cast<sel_f64x2*>(gw + b0 + 2) = sel_f64x2{0.0, 0.0};
-  }
-  for (int i = tid; i < 4096; i += kRowThreads) { s_c[i] = 0; if (MASS) s_w[i] = 0.0; }
-  if (tid < 256) { s_c3[tid] = 0; if (MASS) s_w3[tid] = 0.0; }
-  if (tid < 3) { sh.x[tid].bm = -1; sh.x[tid].bc = -1; }
-
-  RowState st{};
-  st.target_count = a.target_count;
-  st.crit = (MASS ? CRIT_MASS : 0) | (a.target_count > 0 ? CRIT_COUNT : 0);
-  // masses arrive relative to each bucket's upper bound; rescale them to the
-  // top bucket's bound R
-  const double R = bucket_hi(mk >> 20, 20);
-  if (MASS) st.R = R;
-  uint32_t c1[4];
-  double w1[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int e = 3 - k;                           // bucket 4095 - 4 tid - k
-    c1[k] = c4[e];
-    const double wr = w4[e >> 1][e & 1];
-    w1[k] = (MASS && c1[k]) ? wr * exp(bucket_hi((uint32_t)(b0 + e), 20) - R) : 0.0;
-  }
-  cut_level<1, MASS, 4, 4096, false>(a, c1, w1, true, st, sh, nullptr, nullptr);
-  if (tid == 0) a.maxkey[row] = 0;                // every thread has used it
-
-  // the logits of the level-1 cut bucket, gathered into LDS (ascending
-  // positions per chunk; a block prefix of per-thread counts gives the slots)
-  int nc = 0;
-  if (!st.all) {
-    const uint32_t pf = st.prefix;
-    uint32_t total = 0;
-    int it = 0;
-    for (int c0 = 0; c0 < a.n; c0 += kRowChunk, ++it) {
-      if (c0 > 0) {
-#pragma unroll
-        for (int k = 0; k < kRowU; ++k)
-          v[k] = *reinterpret_cast<const sel_f32x4*>(lg + min(c0 + 4 * (tid + k * kRowThreads), last));
-      }
-      // bit 4k+i: value i of load k lies in the cut bucket (keys compared
-      // branch-free; positions past the row's end are masked off after)
-      const uint32_t kb = pf << 20;
-      uint32_t mask = 0;
-#pragma unroll
-      for (int k = 0; k < kRowU; ++k) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t u = __float_as_uint(v[k][i]);
-          const uint32_t key = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
-          mask |= (uint32_t)((key - kb) < 0x100000u) << (4 * k + i);
-        }
-      }
-      const int rem = a.n - c0;
-      if (rem < kRowChunk) {
-        uint32_t valid = 0;
-#pragma unroll
-        for (int k = 0; k < kRowU; ++k) {
-          const int nv = min(max(rem - 4 * (tid + k * kRowThreads), 0), 4);
-          valid |= ((1u << nv) - 1u) << (4 * k);
-        }
-        mask &= valid;
-      }
-      const uint32_t cnt = __popc(mask);
-      const uint32_t incl = wave_inclusive_scan(cnt);
-      if (lane == 63) sh.cand_w[it & 1][wid] = incl;
-      lds_barrier();
-      uint32_t base = 0, tot = 0;
-#pragma unroll
-      for (int w = 0; w < kRowWaves; ++w) {
-        const uint32_t sc = sh.cand_w[it & 1][w];
-        if (w < wid) base += sc;
-        tot += sc;
-      }
-      if (mask) {
-        uint32_t slot = total + base + incl - cnt;
-#pragma unroll
-        for (int k = 0; k < kRowU; ++k)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if ((mask >> (4 * k + i)) & 1u) {
-              if (slot < (uint32_t)kCand) s_cand[slot] = v[k][i];
-              ++slot;
-            }
-      }
-      total += tot;
-    }
-    lds_barrier();
-    nc = (int)total;
-  }
-  const bool fits = nc <= kCand;
-
-  // level 2: bits 19..8 under the 12-bit prefix
-  if (!st.all) {
-    if (fits) {
-      for (int i = tid; i < nc; i += kRowThreads) {
-        const float l = s_cand[i];
-        const uint32_t key = order_key(l);
-        if ((key >> 20) == st.prefix) {
-          const uint32_t bk = (key >> 8) & 4095u;
-          atomicAdd(&s_c[bk], 1u);
-          if (MASS) atomicAdd(&s_w[bk], exp((double)l - st.R));
-        }
-      }
-      lds_barrier();
-    } else {
-      level_hist<2, MASS>(a, lg, st, s_c, s_w);
-    }
-    const sel_u32x4 cc = *reinterpret_cast<const sel_u32x4*>(s_c + b0);
-    sel_f64x2 ww[2] = {{0.0, 0.0}, {0.0, 0.0}};
-    if (MASS) {
-      ww[0] = *reinterpret_cast<const sel_f64x2*>(s_w + b0);
-      ww[1] = *reinterpret_cast<const sel_f64x2*>(s_w + b0 + 2);
-    }
-    uint32_t c2[4];
-    double w2[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int e = 3 - k;
-      c2[k] = cc[e];
-      w2[k] = MASS ? ww[e >> 1][e & 1] : 0.0;
-    }
-    cut_level<2, MASS, 4, 4096, false>(a, c2, w2, true, st, sh, s_c, s_w);
-  }
-
-  // level 3: bits 7..0 under the 24-bit prefix; the histogram by every
-  // wave, the cut by wave 0 alone (lane l owns buckets 255-4l ... 252-4l)
-  if (!st.all) {
-    if (fits) {
-      for (int i = tid; i < nc; i += kRowThreads) {
-        const float l = s_cand[i];
-        const uint32_t key = order_key(l);
-        if ((key >> 8) == st.prefix) {
-          atomicAdd(&s_c3[key & 255u], 1u);
-          if (MASS) atomicAdd(&s_w3[key & 255u], exp((double)l - st.R));
-        }
-      }
-      lds_barrier();
-    } else {
-      level_hist<3, MASS>(a, lg, st, s_c3, s_w3);
-    }
-  }
-  if (wid != 0) return;
-  if (!st.all) {
-    const int b3 = 252 - 4 * lane;
-    const sel_u32x4 cc = *reinterpret_cast<const sel_u32x4*>(s_c3 + b3);
-    sel_f64x2 ww[2] = {{0.0, 0.0}, {0.0, 0.0}};
-    if (MASS) {
-      ww[0] = *reinterpret_cast<const sel_f64x2*>(s_w3 + b3);
-      ww[1] = *reinterpret_cast<const sel_f64x2*>(s_w3 + b3 + 2);
-    }
-    uint32_t c3[4];
-    double w3[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int e = 3 - k;
-      c3[k] = cc[e];
-      w3[k] = MASS ? ww[e >> 1][e & 1] : 0.0;
-    }
-    cut_level<3, MASS, 4, 256, true>(a, c3, w3, true, st, sh, s_c3, s_w3);
-  }
-  if (lane == 0) a.state[row] = st;
-}
-
-// ------------------------------------------------------------------ compact
-// Writes the selected positions of a row in ascending order.  Tiles publish
-// (strict, tie) counts and look back over earlier tiles for their prefix; the
-// counts travel inside the 64-bit flag words, so relaxed atomics suffice.
-constexpr uint64_t kFlagAgg = 1ull << 62, kFlagIncl = 2ull << 62;
-__device__ __forceinline__ uint64_t pack_counts(uint64_t flag, uint32_t s, uint32_t t) {
-  return flag | ((uint64_t)s << 31) | (uint64_t)t;
-}
-
-__global__ __launch_bounds__(kThreads) void select_compact_kernel(SelectArgs a) {
-  __shared__ uint32_t s_scan[kThreads / 64];
-  __shared__ uint32_t s_pre_s, s_pre_t;
-  const int row = blockIdx.y, tile = blockIdx.x, tid = threadIdx.x;
+// ------------------------------------------------------------------ the kernel
+template <typename T, bool MASS, int PER>
+__global__ __launch_bounds__(kThreads) void select_fused_kernel(SelectArgs a) {
+  __shared__ SelShared<MASS> sh;
+  const int row = blockIdx.y, wg = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
   int b, g;
   row_coords(a, row, b, g);
+  const int W = a.W;
+  constexpr int TILE = kThreads * PER;
+  const int j0 = wg * TILE;
   const int64_t orow = ((int64_t)b * a.Hkv + g) * a.n_cap;
-  const int j0 = tile * kTile + tid * kPer;   // this thread's 4 consecutive tokens
-  // their logits, requested first (in bounds: rows are whole tiles long)
-  const float* lg = a.logits + (int64_t)row * a.row_stride;
-  const vl_f32x4 lv = *reinterpret_cast<const vl_f32x4*>(lg + j0);
-  if (a.select_all) {                          // every token: position j goes to slot j
-#pragma unroll
-    for (int i = 0; i < kPer; ++i)
-      if (j0 + i < a.n) a.sel_idx[orow + j0 + i] = j0 + i;
-    if (tile == 0 && tid == 0) a.sel_count[(int64_t)b * a.Hkv + g] = a.n;
-    return;
-  }
-  const RowState st = a.state[row];
-  uint32_t strict_f = 0, tie_f = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int j = j0 + i;
-    if (j >= a.n) continue;
-    const uint32_t key = order_key(lv[i]);
-    if (key > st.cut_key) strict_f |= 1u << i;
-    else if (key == st.cut_key) tie_f |= 1u << i;
-  }
-  uint32_t tot_s, tot_t;
-  const uint32_t ex_s = block_exclusive_scan<uint32_t, kThreads>(__popc(strict_f), s_scan, &tot_s);
-  const uint32_t ex_t = block_exclusive_scan<uint32_t, kThreads>(__popc(tie_f), s_scan, &tot_t);
+  uint32_t* ctl = a.ctl + (int64_t)row * kCtlWords;
+  int bad = 0;
+  uint32_t sink = 0;          // returned atomic values, consumed before arrivals
 
-  if (tid < 64) {
-    // wave 0 looks back over up to 64 predecessors at once: lane i reads tile
-    // (base - i); the window is consumed up to the nearest inclusive prefix
-    uint64_t* lb = a.lookback + (int64_t)row * a.tiles;
-    const int lane = tid;
-    uint32_t ps = 0, pt = 0;
-    if (tile == 0) {
-      if (lane == 0) st_agent(lb, pack_counts(kFlagIncl, tot_s, tot_t));
-    } else {
-      if (lane == 0) st_agent(lb + tile, pack_counts(kFlagAgg, tot_s, tot_t));
-      int base = tile - 1;
-      int spins = 0;
-      while (base >= 0) {
-        const int p = base - lane;
-        uint64_t w = (p >= 0) ? ld_agent(lb + p) : kFlagIncl;   // before tile 0: an empty prefix
-        const uint64_t f = w & (3ull << 62);
-        // all lanes up to the first inclusive one must have published
-        const uint64_t incl_mask = __ballot(f == kFlagIncl);
-        const int first_incl = incl_mask ? __ffsll((unsigned long long)incl_mask) - 1 : 64;
-        const uint64_t ready = __ballot(f != 0);
-        const int need_lanes = (first_incl < 64) ? first_incl + 1 : 64;
-        const uint64_t want = (need_lanes == 64) ? ~0ull : ((1ull << need_lanes) - 1);
-        if ((ready & want) != want) {
-          if (++spins > kSpinLimit) { if (lane == 0) a.state[row].err = 1; break; }
-          continue;
-        }
-        uint32_t vs = (lane < need_lanes && p >= 0) ? (uint32_t)((w >> 31) & 0x7FFFFFFFu) : 0u;
-        uint32_t vt = (lane < need_lanes && p >= 0) ? (uint32_t)(w & 0x7FFFFFFFu) : 0u;
+  // ---- 1. logits in registers (token j0 + i * 256 + tid)
+  float lg[PER];
+  uint32_t key[PER];
+  {
+    float qb[16];
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) { vs += __shfl_xor(vs, o); vt += __shfl_xor(vt, o); }
-        ps += vs;
-        pt += vt;
-        if (first_incl < 64) break;
-        base -= 64;
+    for (int c = 0; c < 16; ++c) qb[c] = 0.f;
+    const int64_t krow = ((int64_t)b * a.Hkv + g) * a.n_cap;
+    constexpr int BATCH = PER < 8 ? PER : 8;
+#pragma unroll
+    for (int i0 = 0; i0 < PER; i0 += BATCH) {
+      IdxRow<T> kr[BATCH];
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i)
+        kr[i].load(a.k_idx, krow + min(j0 + (i0 + i) * kThreads + tid, a.n - 1));
+      if (i0 == 0) {
+        for (int hh = 0; hh < a.G; ++hh) {
+          const float* qp = a.q_idx + ((int64_t)b * a.Hq + g * a.G + hh) * 16;
+#pragma unroll
+          for (int c = 0; c < 16; ++c) qb[c] += qp[c];
+        }
+        const float invG = 1.0f / (float)a.G;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) qb[c] *= invG;
       }
-      if (lane == 0) st_agent(lb + tile, pack_counts(kFlagIncl, ps + tot_s, pt + tot_t));
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        float l = kr[i].dot(qb) * 0.25f;
+        if (l == 0.f) l = 0.f;                  // fold -0 into +0
+        lg[i0 + i] = l;
+      }
     }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const bool valid = j0 + i * kThreads + tid < a.n;
+      key[i] = valid ? order_key(lg[i]) : 0u;   // key 0: no token (below every real key)
+    }
+  }
+  auto valid = [&](int i) __attribute__((always_inline)) { return j0 + i * kThreads + tid < a.n; };
+
+  Cut ct{};
+  ct.tcount = a.target_count;
+  ct.crit = (MASS ? CRIT_MASS : 0) | (a.target_count > 0 ? CRIT_COUNT : 0);
+  ct.all = a.select_all;
+  int rounds = 0;             // global histogram rounds taken (1..3)
+  bool used_cand = false;
+
+  // One global round: histogram of the digit under the current prefix of the
+  // tokens carrying it, merged, waited for and cut.
+  auto global_round = [&](int level) __attribute__((always_inline)) {
+    const int NB = (level == 3) ? kNB3 : kNB1;
+    const int shift = (level == 1) ? 20 : (level == 2 ? 8 : 0);
+    const int pbits = ct.bits;
+    const uint32_t prefix = ct.prefix;
+    for (int i = tid; i < NB; i += kThreads) { sh.u.h.c[i] = 0; if (MASS) sh.u.h.m[i] = 0.0; }
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const uint32_t k = key[i];
+      const bool in = valid(i) && (pbits == 0 || (k >> (32 - pbits)) == prefix);
+      if (in) {
+        const uint32_t bk = (k >> shift) & (uint32_t)(NB - 1);
+        atomicAdd(&sh.u.h.c[bk], 1u);
+        if (MASS) {
+          const double ref = (level == 1) ? bucket_hi(bk, 20) : ct.R;
+          atomicAdd(&sh.u.h.m[bk], exp((double)lg[i] - ref));
+        }
+      }
+    }
+    lds_barrier();
+    uint32_t* gc = a.hist_c + ((int64_t)row * 3 + (level - 1)) * kNB1;
+    double* gm = a.hist_m + ((int64_t)row * 3 + (level - 1)) * kNB1;
+    for (int i = tid; i < NB; i += kThreads) {
+      const uint32_t cv = sh.u.h.c[i];
+      if (cv) {
+        sink ^= atomicAdd(gc + i, cv);
+        if (MASS) sink ^= (uint32_t)__double_as_longlong(atomicAdd(gm + i, sh.u.h.m[i]));
+      }
+    }
+    consume(sink);
+    __syncthreads();
+    if (tid == 0) {
+      atomicAdd(ctl + kCtlArrive + level - 1, 1u);
+      if (!wait_count(ctl + kCtlArrive + level - 1, (uint32_t)W, a.spin_limit)) sh.bad = 1;
+    }
+    __syncthreads();
+    // the merged histogram: thread t reads buckets NB-1-PER*t ... NB-PER*t
+    if (NB == kNB1) {
+      constexpr int P1 = kNB1 / kThreads;     // 16
+      uint32_t c[P1];
+      double w[P1];
+      const int lo = kNB1 - P1 * (tid + 1);   // lowest bucket of this thread
+      const __amdgpu_buffer_rsrc_t rc = rsrc_of(gc), rm = rsrc_of(gm);
+      vl_u32x4 cv[P1 / 4];
+#pragma unroll
+      for (int q = 0; q < P1 / 4; ++q) cv[q] = ld_sc1_u32x4(rc, (lo + 4 * q) * 4);
+      vl_u32x4 mv[MASS ? P1 / 2 : 1];
+      if (MASS) {
+#pragma unroll
+        for (int q = 0; q < P1 / 2; ++q) mv[q] = ld_sc1_u32x4(rm, (lo + 2 * q) * 8);
+      }
+#pragma unroll
+      for (int k = 0; k < P1; ++k) {
+        const int e = P1 - 1 - k;             // bucket lo + e, descending in k
+        c[k] = cv[e >> 2][e & 3];
+        if (MASS) {
+          const vl_u32x4 m2 = mv[e >> 1];
+          const uint64_t u = (e & 1) ? (((uint64_t)m2[3] << 32) | m2[2]) : (((uint64_t)m2[1] << 32) | m2[0]);
+          w[k] = __longlong_as_double(u);
+        } else {
+          w[k] = 0.0;
+        }
+      }
+      if (level == 1) {
+        // R: the upper bound of the highest non-empty bucket
+        int top = -1;
+#pragma unroll
+        for (int k = P1 - 1; k >= 0; --k) if (c[k]) top = kNB1 - 1 - (P1 * tid + k);
+        if (tid == 0) sh.top = 0;
+        lds_barrier();
+        if (top >= 0) atomicMax(&sh.top, (uint32_t)top + 1u);
+        lds_barrier();
+        const uint32_t tb = sh.top;
+        ct.R = tb ? bucket_hi(tb - 1, 20) : 0.0;
+        if (MASS) {
+#pragma unroll
+          for (int k = 0; k < P1; ++k) {
+            const int bk = kNB1 - 1 - (P1 * tid + k);
+            w[k] = c[k] ? w[k] * exp(bucket_hi((uint32_t)bk, 20) - ct.R) : 0.0;
+          }
+        }
+      } else {
+        // the merged histogram in LDS, for the rare fallback walk
+        lds_barrier();
+#pragma unroll
+        for (int k = 0; k < P1; ++k) {
+          const int bk = kNB1 - 1 - (P1 * tid + k);
+          sh.u.h.c[bk] = c[k];
+          if (MASS) sh.u.h.m[bk] = w[k];
+        }
+        lds_barrier();
+      }
+      cut_digit<kNB1, MASS>(a, c, w, level == 1, ct, sh, 12, sh.u.h.c, sh.u.h.m);
+    } else {
+      uint32_t c[1];
+      double w[1];
+      const int bk = kNB3 - 1 - tid;
+      c[0] = ld_agent(gc + bk);
+      w[0] = MASS ? ld_agent(gm + bk) : 0.0;
+      lds_barrier();
+      sh.u.h.c[bk] = c[0];
+      if (MASS) sh.u.h.m[bk] = w[0];
+      lds_barrier();
+      cut_digit<kNB3, MASS>(a, c, w, false, ct, sh, 8, sh.u.h.c, sh.u.h.m);
+    }
+    rounds = level;
+  };
+
+  // Candidates: the keys of every token carrying the current prefix, gathered
+  // from the whole row into LDS; the remaining bits are cut there.
+  auto candidates = [&]() __attribute__((always_inline)) {
+    used_cand = true;
+    const int pbits = ct.bits;
+    const uint32_t prefix = ct.prefix;
+    uint32_t mine = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (valid(i) && (key[i] >> (32 - pbits)) == prefix) ++mine;
+    uint32_t total;
+    const uint32_t ex = block_exclusive_scan<uint32_t, kThreads>(mine, &sh.cnt_s[0][0], &total);
+    if (tid == 0) sh.base = total ? atomicAdd(ctl + kCtlCand, total) : 0u;
+    __syncthreads();
+    uint32_t slot = sh.base + ex;
+    uint32_t* cand = a.cand + (int64_t)row * kCap;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (valid(i) && (key[i] >> (32 - pbits)) == prefix) {
+        if (slot < (uint32_t)kCap)
+          sink ^= __hip_atomic_exchange(cand + slot, key[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ++slot;
+      }
+    }
+    consume(sink);
+    __syncthreads();
+    if (tid == 0) {
+      atomicAdd(ctl + kCtlArrive + 3, 1u);
+      if (!wait_count(ctl + kCtlArrive + 3, (uint32_t)W, a.spin_limit)) sh.bad = 1;
+    }
+    __syncthreads();
+    const uint32_t got = ld_agent(ctl + kCtlCand);
+    if (got != ct.in_count && tid == 0) sh.bad = 1;        // the lists disagree
+    const int C = (int)min(got, (uint32_t)kCap);
+    {
+      const __amdgpu_buffer_rsrc_t rc = rsrc_of(cand);
+      for (int i = 4 * tid; i < C; i += 4 * kThreads) {
+        const vl_u32x4 v = ld_sc1_u32x4(rc, i * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) if (i + e < C) sh.u.r.key[i + e] = v[e];
+      }
+    }
+    // remaining bits: 10 + 10 after 12, or 8 after 24
+    while (ct.bits < 32 && !ct.all) {
+      const int rem = 32 - ct.bits;
+      const int dbits = rem > 10 ? 10 : rem;
+      const int shift = rem - dbits;
+      const int NBd = 1 << dbits;
+      const int pb = ct.bits;
+      const uint32_t pf = ct.prefix;
+      for (int i = tid; i < kNBL; i += kThreads) { sh.u.r.c[i] = 0; if (MASS) sh.u.r.m[i] = 0.0; }
+      lds_barrier();
+      for (int i = tid; i < C; i += kThreads) {
+        const uint32_t k = sh.u.r.key[i];
+        if ((k >> (32 - pb)) == pf) {
+          const uint32_t bk = (k >> shift) & (uint32_t)(NBd - 1);
+          atomicAdd(&sh.u.r.c[bk], 1u);
+          if (MASS) atomicAdd(&sh.u.r.m[bk], exp((double)key_to_float(k) - ct.R));
+        }
+      }
+      lds_barrier();
+      if (NBd == kNBL) {
+        constexpr int P = kNBL / kThreads;
+        uint32_t c[P];
+        double w[P];
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+          const int bk = kNBL - 1 - (P * tid + k);
+          c[k] = sh.u.r.c[bk];
+          w[k] = MASS ? sh.u.r.m[bk] : 0.0;
+        }
+        cut_digit<kNBL, MASS>(a, c, w, false, ct, sh, 10, sh.u.r.c, sh.u.r.m);
+      } else {
+        // 2^dbits buckets (dbits <= 8) fill the top of a 256-bucket digit
+        uint32_t c[1];
+        double w[1];
+        const int bk = kNB3 - 1 - tid;
+        c[0] = bk < NBd ? sh.u.r.c[bk] : 0u;
+        w[0] = (MASS && bk < NBd) ? sh.u.r.m[bk] : 0.0;
+        cut_digit<kNB3, MASS>(a, c, w, false, ct, sh, dbits, sh.u.r.c, sh.u.r.m);
+      }
+    }
+  };
+
+  if (tid == 0) { sh.bad = 0; sh.last = 0; }
+  __syncthreads();
+  if (!ct.all) {
+    global_round(1);
+    if (!ct.all) {
+      if (ct.in_count <= (uint32_t)kCap) {
+        candidates();
+      } else {
+        global_round(2);
+        if (!ct.all) {
+          if (ct.in_count <= (uint32_t)kCap) candidates();
+          else global_round(3);
+        }
+      }
+    }
+  }
+  bad = sh.bad;
+
+  // ---- 4. compaction
+  const uint32_t cut = ct.prefix;
+  const int64_t need = ct.all ? 0 : ct.need;
+  const int64_t m = ct.all ? (int64_t)a.n : ct.above_c + need;
+  uint32_t fs = 0, ft = 0;       // bit i: token i above the cut / a tie
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (!valid(i)) continue;
+    if (ct.all || key[i] > cut) fs |= 1u << i;
+    else if (key[i] == cut) ft |= 1u << i;
+  }
+  uint64_t bs[PER], bt[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    bs[i] = __ballot((fs >> i) & 1u);
+    bt[i] = __ballot((ft >> i) & 1u);
+    if (lane == 0) { sh.cnt_s[i][wid] = __popcll(bs[i]); sh.cnt_t[i][wid] = __popcll(bt[i]); }
+  }
+  __syncthreads();
+  uint32_t tot_s = 0, tot_t = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) { tot_s += sh.cnt_s[i][w]; tot_t += sh.cnt_t[i][w]; }
+  uint64_t* slots = a.slots + (int64_t)row * kMaxSelW;
+  if (tid < 64) {
+    if (lane == 0)
+      __hip_atomic_store(slots + wg, kSlotFlag | ((uint64_t)tot_s << 31) | (uint64_t)tot_t,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the (above-cut, tie) counts of every earlier workgroup of the row
+    uint32_t ps = 0, pt = 0;
+    bool ok = true;
+    for (int c0 = 0; c0 < wg; c0 += 64) {
+      const int p = c0 + lane;
+      uint64_t v = kSlotFlag;
+      int spins = 0;
+      if (p < wg) {
+        v = ld_agent(slots + p);
+        while (!(v & kSlotFlag)) {
+          if (a.spin_limit < 0 || ++spins > a.spin_limit) { ok = false; break; }
+          __builtin_amdgcn_s_sleep(1);
+          v = ld_agent(slots + p);
+        }
+      }
+      uint32_t vs = (p < wg && ok) ? (uint32_t)((v >> 31) & 0xFFFFFFFFu) : 0u;
+      uint32_t vt = (p < wg && ok) ? (uint32_t)(v & 0x7FFFFFFFu) : 0u;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) { vs += __shfl_xor(vs, o); vt += __shfl_xor(vt, o); }
+      ps += vs;
+      pt += vt;
+    }
+    const uint64_t okm = __ballot(!ok);
     if (lane == 0) {
-      s_pre_s = ps;
-      s_pre_t = pt;
-      if (tile == a.tiles - 1) a.sel_count[(int64_t)b * a.Hkv + g] = st.m;
+      sh.pre = ((uint64_t)ps << 32) | pt;
+      if (okm) sh.bad = 1;
     }
   }
   __syncthreads();
-  const uint32_t need = (uint32_t)st.need;
-  uint32_t s_before = s_pre_s + ex_s, t_before = s_pre_t + ex_t;
+  bad = sh.bad;
+  if (!bad) {
+    const uint32_t ps = (uint32_t)(sh.pre >> 32), pt = (uint32_t)sh.pre;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint32_t run_s = ps, run_t = pt;       // counts before token group i
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int j = j0 + i;
-    if (strict_f & (1u << i)) {
-      const uint32_t o = s_before + (t_before < need ? t_before : need);
-      a.sel_idx[orow + o] = j;
-      ++s_before;
-    } else if (tie_f & (1u << i)) {
-      if (t_before < need) a.sel_idx[orow + s_before + t_before] = j;
-      ++t_before;
+    for (int i = 0; i < PER; ++i) {
+      uint32_t ws = 0, wt = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        if (w < wid) { ws += sh.cnt_s[i][w]; wt += sh.cnt_t[i][w]; }
+      }
+      const uint32_t sb = run_s + ws + __popcll(bs[i] & lt);
+      const uint32_t tb = run_t + wt + __popcll(bt[i] & lt);
+      const int j = j0 + i * kThreads + tid;
+      int64_t o = -1;
+      if ((fs >> i) & 1u) o = (int64_t)sb + ((int64_t)tb < need ? tb : need);
+      else if (((ft >> i) & 1u) && (int64_t)tb < need) o = (int64_t)sb + tb;
+      if (o >= 0 && o < m && o < a.n_cap) a.sel_idx[orow + o] = j;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) { run_s += sh.cnt_s[i][w]; run_t += sh.cnt_t[i][w]; }
     }
   }
+
+  // ---- 5. leave; the last workgroup of the row cleans up
+  if (tid == 0) {
+    if (bad) sink ^= atomicOr(ctl + kCtlErr, 1u);
+    consume(sink);
+    const uint32_t old = atomicAdd(ctl + kCtlDepart, 1u);
+    sh.last = (old == (uint32_t)W - 1);
+  }
+  __syncthreads();
+  if (!sh.last) return;
+  if (tid == 0) {
+    const uint32_t err = ld_agent(ctl + kCtlErr);
+    a.sel_count[(int64_t)b * a.Hkv + g] = err ? -1 : (int32_t)m;
+    sh.bad = err ? 1 : 0;
+  }
+  __syncthreads();
+  // histograms of the rounds taken (every round after a failed wait, as the
+  // row's workgroups may then have taken different ones), counters and slots
+  // back to zero
+  const int clear_rounds = sh.bad ? 3 : rounds;
+  for (int lvl = 0; lvl < clear_rounds; ++lvl) {
+    const int NB = (lvl == 2) ? kNB3 : kNB1;
+    uint32_t* gc = a.hist_c + ((int64_t)row * 3 + lvl) * kNB1;
+    double* gm = a.hist_m + ((int64_t)row * 3 + lvl) * kNB1;
+    for (int i = 4 * tid; i < NB; i += 4 * kThreads) {
+      *reinterpret_cast<vl_u32x4*>(gc + i) = vl_u32x4{0u, 0u, 0u, 0u};
+      if (MASS) {
+        *reinterpret_cast<vl_u32x4*>(gm + i) = vl_u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<vl_u32x4*>(gm + i + 2) = vl_u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+  for (int i = tid; i < W; i += kThreads) slots[i] = 0ull;
+  if (tid < kCtlWords) ctl[tid] = 0u;
+  (void)used_cand;
 }
 
-hipError_t launch_select_lowrank(const SelectArgs& a, int dtype, hipStream_t s) {
+hipError_t launch_select_lowrank(const SelectArgs& a, int dtype, int per, hipStream_t s) {
   const int rows = a.B * a.groups.n;
   if (rows == 0) return hipSuccess;
-  if (!a.select_all) {
-    dim3 grid((a.n + kScanTile - 1) / kScanTile, rows);
-    if (dtype == 0) {
-      if (a.use_mass) hipLaunchKernelGGL((select_scan_kernel<bf16_t, true>), grid, dim3(kThreads), 0, s, a);
-      else hipLaunchKernelGGL((select_scan_kernel<bf16_t, false>), grid, dim3(kThreads), 0, s, a);
-    } else {
-      if (a.use_mass) hipLaunchKernelGGL((select_scan_kernel<float, true>), grid, dim3(kThreads), 0, s, a);
-      else hipLaunchKernelGGL((select_scan_kernel<float, false>), grid, dim3(kThreads), 0, s, a);
-    }
-    if (a.use_mass) hipLaunchKernelGGL((select_row_kernel<true>), dim3(rows), dim3(kRowThreads), 0, s, a);
-    else hipLaunchKernelGGL((select_row_kernel<false>), dim3(rows), dim3(kRowThreads), 0, s, a);
+  dim3 grid(a.W, rows), block(kThreads);
+#define SA_SEL(T_, M_, P_) hipLaunchKernelGGL((select_fused_kernel<T_, M_, P_>), grid, block, 0, s, a)
+#define SA_SEL_P(T_, M_)                      \
+  switch (per) {                              \
+    case 4: SA_SEL(T_, M_, 4); break;         \
+    case 8: SA_SEL(T_, M_, 8); break;         \
+    case 16: SA_SEL(T_, M_, 16); break;       \
+    default: return hipErrorInvalidValue;     \
   }
-  hipLaunchKernelGGL(select_compact_kernel, dim3(a.tiles, rows), dim3(kThreads), 0, s, a);
+  if (dtype == 0) {
+    if (a.use_mass) { SA_SEL_P(bf16_t, true) } else { SA_SEL_P(bf16_t, false) }
+  } else {
+    if (a.use_mass) { SA_SEL_P(float, true) } else { SA_SEL_P(float, false) }
+  }
+#undef SA_SEL_P
+#undef SA_SEL
   return hipGetLastError();
 }
 

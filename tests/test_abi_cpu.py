@@ -228,3 +228,10 @@ def test_decode_noalloc_rejects_a_workspace_larger_than_its_array():
     assert n.value > 8 << 20
     st = sa.raw_call("decode_noalloc", ctypes.byref(p), ctypes.byref(b), None)
     assert st == sa.SA_ERR_WORKSPACE
+
+
+def test_check_selection_flags_negative_counts():
+    import torch
+    sa.check_selection(torch.tensor([[5, 0], [7, 100]], dtype=torch.int32))
+    with pytest.raises(sa.SparseAttnError):
+        sa.check_selection(torch.tensor([[5, -1], [7, 100]], dtype=torch.int32))

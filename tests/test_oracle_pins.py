@@ -497,3 +497,46 @@ def test_prefill_block_matches_sdpa_on_gathered_rows():
         Kt = np.concatenate([Ks, K[80:i + 1]])
         Vt = np.concatenate([Vs, V[80:i + 1]])
         np.testing.assert_allclose(out[i], sdpa64(Q[i], Kt, Vt)[0], atol=1e-12)
+
+
+# ---------------------------------------------------------------- three-level pyramid, by hand
+def _hand_value(v):
+    """Numbers of the hand fixtures: plain, a fraction "a/b", or 2 sqrt(2) ln 2."""
+    if isinstance(v, str):
+        if v == "2sqrt2ln2":
+            return 2.0 * np.sqrt(2.0) * np.log(2.0)
+        a, b = v.split("/")
+        return float(a) / float(b)
+    return float(v)
+
+
+def test_pyramid_three_levels_hand_fixture():
+    """Lighthouse Attention summary, 2A-2C, on a 16-token three-level pyramid
+    worked by hand (tests/golden/pyramid_three_levels_hand.json): the level
+    scores with max inheritance, the joint top-K with the level tie-break,
+    the rows of level-0, level-1 and level-2 entries, and the outputs (exact
+    rationals) of queries in both blocks."""
+    fx = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                      "pyramid_three_levels_hand.json")))
+    N, d, L, p, qb = fx["N"], fx["d"], fx["levels"], fx["factor"], fx["q_block"]
+    rows = {}
+    for name in ("Q", "K", "V"):
+        X = np.zeros((N, d))
+        for i, r in fx.get(f"{name}_rows", {}).items():
+            X[int(i)] = [_hand_value(v) for v in r]
+        rows[name] = X
+    Q, K, V = rows["Q"], rows["K"], rows["V"]
+    sc = oracle.pyramid_scores(Q, K, L, p)
+    for lvl, want in enumerate(("level0", "level1", "level2")):
+        exp = fx["expect_scores_before_8"][want]
+        np.testing.assert_allclose(sc[lvl][:len(exp)], exp, atol=1e-12)
+    kc = oracle.pyramid_levels(K, L, p, None)
+    vc = oracle.pyramid_levels(V, L, p, None)
+    for case in fx["cases"]:
+        sel = oracle.block_select(sc, 1, N, L, p, qb, case["top_k"])
+        assert sel.tolist() == case["block1_ids"]
+        np.testing.assert_allclose(LH.entry_rows(sel, K, kc, N, L, p), case["block1_K"], atol=1e-12)
+        np.testing.assert_allclose(LH.entry_rows(sel, V, vc, N, L, p), case["block1_V"], atol=1e-12)
+        out, _, _, _ = oracle.prefill(Q, K, V, L, p, qb, case["top_k"], store=None)
+        for i, want in case["out"].items():
+            np.testing.assert_allclose(out[int(i)], [_hand_value(v) for v in want], atol=1e-12)

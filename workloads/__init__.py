@@ -240,6 +240,34 @@ def lattice_index_inputs(cfg: DecodeConfig, seed: int, k_amp: int = 8,
                 head_kind=torch.tensor(cfg.head_kind(), dtype=torch.int8))
 
 
+def clustered_index_inputs(cfg: DecodeConfig, seed: int, spread: bool = True,
+                           device="cpu") -> dict:
+    """Exact-arithmetic index inputs whose logits crowd together.
+
+    With ``spread``: every query head of a group has index-query component 0
+    equal to 1, the group's first head also has component 1 equal to 1/4 (the
+    others 0), and every index key has component 0 equal to 4 and component 1
+    uniform in {0, 1/8, ..., 63/8}; all other components are 0.  For a group
+    of G heads every logit is then 1 + k_1 / (16 G): 64 distinct values in
+    the range [1, 1.125), each shared by about n/64 tokens.  Without
+    ``spread`` every index key is zero, so every logit is 0 (one n-way tie).
+    Values are exact in bf16 and fp32.
+    """
+    B, Hq, Hkv, n = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.n_ctx
+    G = cfg.gqa
+    g = _gen(seed, device, 13)
+    k_idx = torch.zeros(B, Hkv, n, cfg.r, dtype=torch.float32, device=device)
+    q_idx = torch.zeros(B, Hq, cfg.r, dtype=torch.float32, device=device)
+    if spread:
+        k_idx[..., 0] = 4.0
+        k_idx[..., 1] = torch.randint(0, 64, (B, Hkv, n), generator=g,
+                                      device=device).to(torch.float32) / 8.0
+        q_idx[..., 0] = 1.0
+        q_idx[:, ::G, 1] = 0.25
+    return dict(k_idx=k_idx, q_idx=q_idx, n_cap=n,
+                head_kind=torch.tensor(cfg.head_kind(), dtype=torch.int8))
+
+
 def lattice_summary_inputs(cfg: DecodeConfig, seed: int, amp: int = 16,
                            q_amp: int = 8, device="cpu") -> dict:
     """Exact-arithmetic routing inputs: chunk/group summaries in (1/8)Z and a
