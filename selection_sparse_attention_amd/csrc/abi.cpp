@@ -117,21 +117,23 @@ int32_t pyramid_geom(const sa_params* p, PyrGeom* g) {
 
 // ---------------------------------------------------------------- select ws
 struct SelectWs {
-  uint32_t* hist_c; double* hist_m; uint32_t* ctl; uint64_t* slots; uint32_t* cand;
-  size_t bytes;
+  uint32_t* hist_c; double* hist_m; uint32_t* ctl; uint32_t* slot_a; uint64_t* slot_b;
+  uint32_t* cand; size_t bytes;
 };
 
-// The regions that must be zero when a call starts (histograms, control words,
-// compaction slots; returned to zero by every call) come first; every size
-// depends on the number of rows only, not on n_ctx.
-SelectWs carve_select(void* ws, int rows) {
+// The regions that must be zero when a call starts (histograms, control
+// words, flags; returned to zero by every call) come first, and their sizes
+// depend on the number of rows only; the candidate regions (a tile of keys
+// per workgroup, written before they are read) come last.
+SelectWs carve_select(void* ws, int rows, int64_t cand_stride) {
   SelectWs s{};
   Carver c(ws);
   s.hist_c = c.take<uint32_t>((size_t)rows * 3 * 4096);
   s.hist_m = c.take<double>((size_t)rows * 3 * 4096);
   s.ctl = c.take<uint32_t>((size_t)rows * sa::kCtlWords);
-  s.slots = c.take<uint64_t>((size_t)rows * sa::kMaxSelW);
-  s.cand = c.take<uint32_t>((size_t)rows * sa::kCap);
+  s.slot_a = c.take<uint32_t>((size_t)rows * sa::kMaxSelW);
+  s.slot_b = c.take<uint64_t>((size_t)rows * sa::kMaxSelW);
+  s.cand = c.take<uint32_t>((size_t)rows * cand_stride);
   s.bytes = c.size();
   return s;
 }
@@ -372,12 +374,6 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
     if (mode == SA_SEL_TOPK && p->top_k < 1) return SA_ERR_INVALID_ARG;
     GroupList gl = groups_of_kind(p, kinds, SA_HEAD_RETRIEVAL);
     const int rows = p->batch * gl.n;
-    SelectWs sw = carve_select(nullptr, rows);
-    if ((st = workspace_gate(ws, ws_bytes, sw.bytes))) return st < 0 ? st : SA_OK;
-    if (gl.n == 0) return SA_OK;
-    if (!b->q_idx || !b->k_idx || !b->sel_idx || !b->sel_count) return SA_ERR_INVALID_ARG;
-    if (!aligned16(b->k_idx)) return SA_ERR_INVALID_ARG;
-    const bool mass = mode == SA_SEL_TOPP;
     // tokens per workgroup: the smallest tile giving at most two workgroups
     // per compute unit over all rows.  The workgroups of a row wait for each
     // other, so all of them must be resident together: W stays within the
@@ -388,8 +384,15 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
     int per = 4;
     while (per < 16 && ((int64_t)rows * tiles(per) > 2 * cus || tiles(per) > wmax)) per *= 2;
     const int W = tiles(per);
+    const int64_t cand_stride = (int64_t)W * 256 * per;
+    SelectWs sw = carve_select(nullptr, rows, cand_stride);
+    if ((st = workspace_gate(ws, ws_bytes, sw.bytes))) return st < 0 ? st : SA_OK;
+    if (gl.n == 0) return SA_OK;
+    if (!b->q_idx || !b->k_idx || !b->sel_idx || !b->sel_count) return SA_ERR_INVALID_ARG;
+    if (!aligned16(b->k_idx)) return SA_ERR_INVALID_ARG;
     if (W > wmax) return SA_ERR_UNSUPPORTED;
-    sw = carve_select(ws, rows);
+    const bool mass = mode == SA_SEL_TOPP;
+    sw = carve_select(ws, rows, cand_stride);
     sa::SelectArgs a{};
     a.q_idx = b->q_idx; a.k_idx = b->k_idx; a.sel_idx = b->sel_idx; a.sel_count = b->sel_count;
     a.B = p->batch; a.Hq = p->n_q_heads; a.Hkv = p->n_kv_heads; a.n = p->n_ctx; a.n_cap = p->n_cap;
@@ -406,7 +409,8 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
     }
     a.W = W;
     a.spin_limit = select_spin_limit();
-    a.hist_c = sw.hist_c; a.hist_m = sw.hist_m; a.ctl = sw.ctl; a.slots = sw.slots; a.cand = sw.cand;
+    a.hist_c = sw.hist_c; a.hist_m = sw.hist_m; a.ctl = sw.ctl; a.slot_a = sw.slot_a; a.slot_b = sw.slot_b;
+    a.cand = sw.cand; a.cand_stride = cand_stride;
     a.groups = gl;
     return hip_status(sa::launch_select_lowrank(a, p->dtype, per, s));
   }

@@ -53,10 +53,8 @@ struct PyramidArgs {
 constexpr int kCap = 8192;         // candidate keys per row resolved in LDS
 constexpr int kMaxSelW = 512;      // workgroups per selector row
 // per-row control words of the selector workspace
-constexpr int kCtlArrive = 0;      // four arrival counters (three global rounds, candidates)
-constexpr int kCtlCand = 4;        // candidate count
-constexpr int kCtlErr = 5;         // a wait timed out
-constexpr int kCtlDepart = 6;      // workgroups that have left
+constexpr int kCtlErr = 0;         // a wait timed out
+constexpr int kCtlDepart = 1;      // workgroups that have left
 constexpr int kCtlWords = 16;
 
 struct SelectArgs {
@@ -75,8 +73,10 @@ struct SelectArgs {
   uint32_t* hist_c;      // [rows, 3, 4096] counts of the three global digits
   double* hist_m;        // [rows, 3, 4096] masses of the three global digits
   uint32_t* ctl;         // [rows, kCtlWords]
-  uint64_t* slots;       // [rows, kMaxSelW] compaction counts
-  uint32_t* cand;        // [rows, kCap] candidate keys
+  uint32_t* slot_a;      // [rows, kMaxSelW] last global digit each workgroup has merged
+  uint64_t* slot_b;      // [rows, kMaxSelW] each workgroup's exchange counts (flagged)
+  uint32_t* cand;        // [rows, cand_stride] candidate keys, one region of a tile per workgroup
+  int64_t cand_stride;
   GroupList groups;
 };
 

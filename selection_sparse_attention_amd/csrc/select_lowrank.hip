@@ -134,7 +134,7 @@ struct Cut {
   int32_t need;         // final: ties kept among keys == prefix (bits == 32)
 };
 
-// Crossing of one criterion inside a level, as published by its owner.
+// Crossing of one criterion inside a digit, as published by its owner.
 struct Cross {
   int b;                // bucket, -1: none
   double w;             // mass above it
@@ -144,36 +144,82 @@ struct Cross {
 template <bool MASS>
 struct SelShared {
   union {
-    struct {            // level histograms (global rounds)
+    struct {            // histogram of a global digit
       uint32_t c[kNB1];
       double m[MASS ? kNB1 : 1];
     } h;
-    struct {            // candidates and their local digits
+    struct {            // the exchange: every workgroup's counts, the candidates, local digits
       uint32_t key[kCap];
       uint32_t c[kNBL];
       double m[MASS ? kNBL : 1];
+      uint32_t strict[kMaxSelW];   // above-prefix tokens of each workgroup
+      uint32_t base[kMaxSelW + 1]; // exclusive prefix of the candidate counts
     } r;
   } u;
   double wave_w[kWaves];
   int64_t wave_c[kWaves];
   Cross xm, xc;
-  uint32_t top;         // highest non-empty bucket
-  uint32_t base;        // candidate slot base
+  uint32_t top;
   uint32_t cnt_s[16][kWaves], cnt_t[16][kWaves];
-  uint64_t pre;         // (strict, tie) counts before this workgroup
+  uint32_t red[2][kWaves];
   int bad;              // a wait of this workgroup timed out
+  int err_any;          // some workgroup of the row reported a timed-out wait
   int last;             // this workgroup left the row last
 };
 
-// Wait until *ctr reaches `target` (one thread).  Returns false when the
-// spin limit runs out (a negative limit fails every wait at once).
-__device__ __forceinline__ bool wait_count(const uint32_t* ctr, uint32_t target, int limit) {
-  if (limit < 0) return false;
-  for (int s = 0; s <= limit; ++s) {
-    if (ld_agent(ctr) >= target) return true;
-    __builtin_amdgcn_s_sleep(1);
+// Wave 0: wait until each of the row's W words reaches `atleast` (returns
+// false when a poll runs past the spin limit; a negative limit fails at once).
+__device__ bool wait_round(const uint32_t* slots, int W, uint32_t atleast, int limit) {
+  const int lane = threadIdx.x & 63;
+  bool ok = limit >= 0;
+  for (int base = 0; base < W && ok; base += 64) {
+    const int i = base + lane;
+    if (i < W) {
+      int spins = 0;
+      while (ld_agent(slots + i) < atleast) {
+        if (++spins > limit) { ok = false; break; }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    ok = __ballot(!ok) == 0;
   }
-  return false;
+  return ok;
+}
+
+// Position-order ranks (token j0 + i * 256 + tid) of the flagged tokens of a
+// workgroup, for two flag sets at once (one pair of barriers): ra[i] / rb[i]
+// for this thread's token i, and the workgroup's totals ta / tb.
+template <int PER>
+__device__ __forceinline__ void wg_ranks2(uint32_t fa, uint32_t fb, uint32_t (&ra)[PER],
+                                          uint32_t (&rb)[PER], uint32_t& ta, uint32_t& tb,
+                                          uint32_t (*ca)[kWaves], uint32_t (*cb)[kWaves]) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint64_t ba[PER], bb[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    ba[i] = __ballot((fa >> i) & 1u);
+    bb[i] = __ballot((fb >> i) & 1u);
+    if (lane == 0) { ca[i][wid] = (uint32_t)__popcll(ba[i]); cb[i][wid] = (uint32_t)__popcll(bb[i]); }
+  }
+  __syncthreads();
+  uint32_t runa = 0, runb = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    uint32_t bfa = 0, bfb = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const uint32_t x = ca[i][w], y = cb[i][w];
+      if (w < wid) { bfa += x; bfb += y; }
+    }
+    ra[i] = runa + bfa + (uint32_t)__popcll(ba[i] & lt);
+    rb[i] = runb + bfb + (uint32_t)__popcll(bb[i] & lt);
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) { runa += ca[i][w]; runb += cb[i][w]; }
+  }
+  __syncthreads();
+  ta = runa;
+  tb = runb;
 }
 
 // Block-wide inclusive prefix (thread order) of one double and one int64 with
@@ -204,12 +250,17 @@ __device__ __forceinline__ void block_scan2(double tw, int64_t tc, SelShared<MAS
 
 // One digit of the cut.  Thread t owns the PER buckets NB-1-PER*t ...
 // NB-PER*t (descending key order) with counts c[] and masses w[] (relative to
-// R).  `first` marks level 1, where the mass target is p times the total.
-// Every thread ends with the same updated cut.
+// R); hc / hm hold the same digit's histogram in LDS (bucket i at index i),
+// read only by the rare fallback below.  `first` marks level 1, where the
+// mass target is p times the total.  Every thread ends with the same cut.
+// (The state goes in and out by value: written through a reference, two of
+// its fields set on different paths got merged into one store through a
+// pointer, which kept the whole state in scratch memory.)
 template <int NB, bool MASS>
-__device__ void cut_digit(const SelectArgs& a, const uint32_t (&c)[NB / kThreads],
-                          const double (&w)[NB / kThreads], bool first, Cut& ct,
-                          SelShared<MASS>& sh, int dbits, const uint32_t* hc, const double* hm) {
+__device__ __forceinline__ Cut cut_digit(const SelectArgs& a, const uint32_t (&c)[NB / kThreads],
+                                         const double (&w)[NB / kThreads], bool first, Cut ct,
+                                         SelShared<MASS>& sh, int dbits, const uint32_t* hc,
+                                         const double* hm) {
   constexpr int PER = NB / kThreads;
   const int tid = threadIdx.x;
   double tw = 0.0;
@@ -246,7 +297,6 @@ __device__ void cut_digit(const SelectArgs& a, const uint32_t (&c)[NB / kThreads
     // the previous digit placed the mass crossing inside this prefix; a
     // last-place disagreement between the two digits' sums puts it on the
     // first or last non-empty bucket here (rare: a serial walk is fine)
-    // (hc / hm: this digit's histogram in LDS, bucket i at index i)
     const bool above = ct.above_w >= tmass;
     int hi_b = -1, lo_b = -1;
     for (int bk = NB - 1; bk >= 0; --bk)
@@ -270,7 +320,7 @@ __device__ void cut_digit(const SelectArgs& a, const uint32_t (&c)[NB / kThreads
   }
   if (bstar < 0) {             // the target lies past the last token
     ct.all = 1;
-    return;
+    return ct;
   }
   const bool from_mass = (bstar == xm.b) && m_on;
   ct.above_w = from_mass ? xm.w : xc.w;
@@ -306,6 +356,7 @@ __device__ void cut_digit(const SelectArgs& a, const uint32_t (&c)[NB / kThreads
     if (need < 1) need = 1;
     ct.need = (int32_t)need;
   }
+  return ct;
 }
 
 // ------------------------------------------------------------------ the kernel
@@ -321,11 +372,13 @@ __global__ __launch_bounds__(kThreads) void select_fused_kernel(SelectArgs a) {
   const int j0 = wg * TILE;
   const int64_t orow = ((int64_t)b * a.Hkv + g) * a.n_cap;
   uint32_t* ctl = a.ctl + (int64_t)row * kCtlWords;
-  int bad = 0;
-  uint32_t sink = 0;          // returned atomic values, consumed before arrivals
+  uint32_t* slot_a = a.slot_a + (int64_t)row * kMaxSelW;
+  uint64_t* slot_b = a.slot_b + (int64_t)row * kMaxSelW;
+  uint32_t* cand_row = a.cand + (int64_t)row * a.cand_stride;
+  uint32_t sink = 0;          // returned atomic values, consumed before a flag is raised
 
-  // ---- 1. logits in registers (token j0 + i * 256 + tid)
-  float lg[PER];
+  // ---- 1. logits in registers, as order keys (token j0 + i * 256 + tid; a
+  // key maps back to its logit exactly)
   uint32_t key[PER];
   {
     float qb[16];
@@ -353,13 +406,9 @@ __global__ __launch_bounds__(kThreads) void select_fused_kernel(SelectArgs a) {
       for (int i = 0; i < BATCH; ++i) {
         float l = kr[i].dot(qb) * 0.25f;
         if (l == 0.f) l = 0.f;                  // fold -0 into +0
-        lg[i0 + i] = l;
+        const bool valid = j0 + (i0 + i) * kThreads + tid < a.n;
+        key[i0 + i] = valid ? order_key(l) : 0u;   // key 0: no token (below every real key)
       }
-    }
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const bool valid = j0 + i * kThreads + tid < a.n;
-      key[i] = valid ? order_key(lg[i]) : 0u;   // key 0: no token (below every real key)
     }
   }
   auto valid = [&](int i) __attribute__((always_inline)) { return j0 + i * kThreads + tid < a.n; };
@@ -368,11 +417,12 @@ __global__ __launch_bounds__(kThreads) void select_fused_kernel(SelectArgs a) {
   ct.tcount = a.target_count;
   ct.crit = (MASS ? CRIT_MASS : 0) | (a.target_count > 0 ? CRIT_COUNT : 0);
   ct.all = a.select_all;
-  int rounds = 0;             // global histogram rounds taken (1..3)
-  bool used_cand = false;
+  int rounds = 0;             // global digits taken (1..3)
+  if (tid == 0) { sh.bad = 0; sh.err_any = 0; sh.last = 0; }
+  __syncthreads();
 
-  // One global round: histogram of the digit under the current prefix of the
-  // tokens carrying it, merged, waited for and cut.
+  // ---- 2. one global digit: histogram of the tokens under the current
+  // prefix, merged, flagged, waited for, read back and cut
   auto global_round = [&](int level) __attribute__((always_inline)) {
     const int NB = (level == 3) ? kNB3 : kNB1;
     const int shift = (level == 1) ? 20 : (level == 2 ? 8 : 0);
@@ -389,7 +439,7 @@ __global__ __launch_bounds__(kThreads) void select_fused_kernel(SelectArgs a) {
         atomicAdd(&sh.u.h.c[bk], 1u);
         if (MASS) {
           const double ref = (level == 1) ? bucket_hi(bk, 20) : ct.R;
-          atomicAdd(&sh.u.h.m[bk], exp((double)lg[i] - ref));
+          atomicAdd(&sh.u.h.m[bk], exp((double)key_to_float(k) - ref));
         }
       }
     }
@@ -405,38 +455,30 @@ __global__ __launch_bounds__(kThreads) void select_fused_kernel(SelectArgs a) {
     }
     consume(sink);
     __syncthreads();
-    if (tid == 0) {
-      atomicAdd(ctl + kCtlArrive + level - 1, 1u);
-      if (!wait_count(ctl + kCtlArrive + level - 1, (uint32_t)W, a.spin_limit)) sh.bad = 1;
+    if (tid == 0) __hip_atomic_store(slot_a + wg, (uint32_t)level, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < 64) {
+      const bool ok = wait_round(slot_a, W, (uint32_t)level, a.spin_limit);
+      if (!ok && lane == 0) sh.bad = 1;
     }
     __syncthreads();
-    // the merged histogram: thread t reads buckets NB-1-PER*t ... NB-PER*t
+    // the merged histogram: thread t reads buckets NB-1-PER*t ... NB-PER*t,
+    // the masses of its non-empty buckets only
     if (NB == kNB1) {
       constexpr int P1 = kNB1 / kThreads;     // 16
       uint32_t c[P1];
       double w[P1];
       const int lo = kNB1 - P1 * (tid + 1);   // lowest bucket of this thread
-      const __amdgpu_buffer_rsrc_t rc = rsrc_of(gc), rm = rsrc_of(gm);
+      const __amdgpu_buffer_rsrc_t rc = rsrc_of(gc);
       vl_u32x4 cv[P1 / 4];
 #pragma unroll
       for (int q = 0; q < P1 / 4; ++q) cv[q] = ld_sc1_u32x4(rc, (lo + 4 * q) * 4);
-      vl_u32x4 mv[MASS ? P1 / 2 : 1];
-      if (MASS) {
-#pragma unroll
-        for (int q = 0; q < P1 / 2; ++q) mv[q] = ld_sc1_u32x4(rm, (lo + 2 * q) * 8);
-      }
 #pragma unroll
       for (int k = 0; k < P1; ++k) {
         const int e = P1 - 1 - k;             // bucket lo + e, descending in k
         c[k] = cv[e >> 2][e & 3];
-        if (MASS) {
-          const vl_u32x4 m2 = mv[e >> 1];
-          const uint64_t u = (e & 1) ? (((uint64_t)m2[3] << 32) | m2[2]) : (((uint64_t)m2[1] << 32) | m2[0]);
-          w[k] = __longlong_as_double(u);
-        } else {
-          w[k] = 0.0;
-        }
       }
+#pragma unroll
+      for (int k = 0; k < P1; ++k) w[k] = (MASS && c[k]) ? ld_agent(gm + lo + P1 - 1 - k) : 0.0;
       if (level == 1) {
         // R: the upper bound of the highest non-empty bucket
         int top = -1;
@@ -449,11 +491,33 @@ __global__ __launch_bounds__(kThreads) void select_fused_kernel(SelectArgs a) {
         const uint32_t tb = sh.top;
         ct.R = tb ? bucket_hi(tb - 1, 20) : 0.0;
         if (MASS) {
+          // rescale factors exp(hi(b) - R) of the non-empty buckets: listed in
+          // LDS and computed a few per thread (the non-empty buckets bunch up
+          // in a few threads' ranges), then read back by their owners
+          uint32_t ne = 0;
 #pragma unroll
-          for (int k = 0; k < P1; ++k) {
-            const int bk = kNB1 - 1 - (P1 * tid + k);
-            w[k] = c[k] ? w[k] * exp(bucket_hi((uint32_t)bk, 20) - ct.R) : 0.0;
+          for (int k = 0; k < P1; ++k) ne |= (c[k] ? 1u : 0u) << k;
+          uint32_t total;
+          const uint32_t first_i = block_exclusive_scan<uint32_t, kThreads>(
+              (uint32_t)__popc(ne), &sh.cnt_s[0][0], &total);
+          uint32_t* list = sh.u.h.c;            // free: the tile's level-1 counts are merged
+          double* fac = sh.u.h.m;
+          {
+            uint32_t i = first_i;
+#pragma unroll
+            for (int k = 0; k < P1; ++k)
+              if ((ne >> k) & 1u) list[i++] = (uint32_t)(kNB1 - 1 - (P1 * tid + k));
           }
+          lds_barrier();
+          for (uint32_t i = tid; i < total; i += kThreads) fac[i] = exp(bucket_hi(list[i], 20) - ct.R);
+          lds_barrier();
+          {
+            uint32_t i = first_i;
+#pragma unroll
+            for (int k = 0; k < P1; ++k)
+              if ((ne >> k) & 1u) w[k] *= fac[i++];
+          }
+          lds_barrier();
         }
       } else {
         // the merged histogram in LDS, for the rare fallback walk
@@ -466,207 +530,250 @@ __global__ __launch_bounds__(kThreads) void select_fused_kernel(SelectArgs a) {
         }
         lds_barrier();
       }
-      cut_digit<kNB1, MASS>(a, c, w, level == 1, ct, sh, 12, sh.u.h.c, sh.u.h.m);
+      ct = cut_digit<kNB1, MASS>(a, c, w, level == 1, ct, sh, 12, sh.u.h.c, sh.u.h.m);
     } else {
       uint32_t c[1];
       double w[1];
       const int bk = kNB3 - 1 - tid;
       c[0] = ld_agent(gc + bk);
-      w[0] = MASS ? ld_agent(gm + bk) : 0.0;
+      w[0] = (MASS && c[0]) ? ld_agent(gm + bk) : 0.0;
       lds_barrier();
       sh.u.h.c[bk] = c[0];
       if (MASS) sh.u.h.m[bk] = w[0];
       lds_barrier();
-      cut_digit<kNB3, MASS>(a, c, w, false, ct, sh, 8, sh.u.h.c, sh.u.h.m);
+      ct = cut_digit<kNB3, MASS>(a, c, w, false, ct, sh, 8, sh.u.h.c, sh.u.h.m);
     }
     rounds = level;
   };
 
-  // Candidates: the keys of every token carrying the current prefix, gathered
-  // from the whole row into LDS; the remaining bits are cut there.
-  auto candidates = [&]() __attribute__((always_inline)) {
-    used_cand = true;
-    const int pbits = ct.bits;
-    const uint32_t prefix = ct.prefix;
-    uint32_t mine = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (valid(i) && (key[i] >> (32 - pbits)) == prefix) ++mine;
-    uint32_t total;
-    const uint32_t ex = block_exclusive_scan<uint32_t, kThreads>(mine, &sh.cnt_s[0][0], &total);
-    if (tid == 0) sh.base = total ? atomicAdd(ctl + kCtlCand, total) : 0u;
-    __syncthreads();
-    uint32_t slot = sh.base + ex;
-    uint32_t* cand = a.cand + (int64_t)row * kCap;
+  if (!ct.all) {
+    global_round(1);
+    while (!ct.all && ct.in_count > (uint32_t)kCap && ct.bits < 32) global_round(ct.bits == 12 ? 2 : 3);
+  }
+
+  // ---- 3. the exchange: every workgroup publishes how many of its tokens lie
+  // above the prefix and, in position order, the keys of those that carry it
+  // (none when all 32 bits are fixed: they are ties); after it, every
+  // workgroup resolves the cut and knows what precedes its tiles
+  uint32_t s_before = 0, a_before = 0, t_before = 0;
+  if (rounds > 0) {
+    const int pb = ct.bits;
+    const uint32_t pf = ct.prefix;
+    const bool keys = !ct.all && pb < 32;
+    uint32_t fa = 0, fc = 0;                  // bit i: token i above / carrying the prefix
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      if (valid(i) && (key[i] >> (32 - pbits)) == prefix) {
-        if (slot < (uint32_t)kCap)
-          sink ^= __hip_atomic_exchange(cand + slot, key[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ++slot;
-      }
+      if (!valid(i)) continue;
+      if (ct.all) { fa |= 1u << i; continue; }
+      const uint32_t kp = key[i] >> (32 - pb);
+      if (kp > pf) fa |= 1u << i;
+      else if (kp == pf) fc |= 1u << i;
+    }
+    uint32_t ra[PER], rk[PER], n_above, n_cand;
+    wg_ranks2<PER>(fa, fc, ra, rk, n_above, n_cand, sh.cnt_s, sh.cnt_t);
+    if (keys) {
+      uint32_t* region = cand_row + (int64_t)wg * TILE;
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if ((fc >> i) & 1u)
+          sink ^= __hip_atomic_exchange(region + rk[i], key[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     consume(sink);
     __syncthreads();
-    if (tid == 0) {
-      atomicAdd(ctl + kCtlArrive + 3, 1u);
-      if (!wait_count(ctl + kCtlArrive + 3, (uint32_t)W, a.spin_limit)) sh.bad = 1;
+    if (tid == 0)
+      __hip_atomic_store(slot_b + wg, kSlotFlag | ((uint64_t)sh.bad << 62) | ((uint64_t)n_above << 31) | n_cand,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // every workgroup's counts, into LDS (wave 0)
+    if (tid < 64) {
+      bool ok = a.spin_limit >= 0;
+      int err = 0;
+      for (int base = 0; base < W; base += 64) {
+        const int i = base + lane;
+        uint64_t v = kSlotFlag;
+        if (i < W && ok) {
+          int spins = 0;
+          v = ld_agent(slot_b + i);
+          while (!(v & kSlotFlag)) {
+            if (++spins > a.spin_limit) { ok = false; break; }
+            __builtin_amdgcn_s_sleep(1);
+            v = ld_agent(slot_b + i);
+          }
+        }
+        if (i < W) {
+          sh.u.r.strict[i] = ok ? (uint32_t)((v >> 31) & 0x7FFFFFFFu) : 0u;
+          sh.u.r.base[i] = ok ? (uint32_t)(v & 0x7FFFFFFFu) : 0u;
+          err |= (int)((v >> 62) & 1u);
+        }
+        ok = __ballot(!ok) == 0;
+      }
+      const bool any_err = __ballot(err != 0) != 0;
+      if (lane == 0) {
+        if (!ok) sh.bad = 1;
+        if (any_err || !ok) sh.err_any = 1;
+      }
     }
     __syncthreads();
-    const uint32_t got = ld_agent(ctl + kCtlCand);
-    if (got != ct.in_count && tid == 0) sh.bad = 1;        // the lists disagree
-    const int C = (int)min(got, (uint32_t)kCap);
-    {
-      const __amdgpu_buffer_rsrc_t rc = rsrc_of(cand);
-      for (int i = 4 * tid; i < C; i += 4 * kThreads) {
-        const vl_u32x4 v = ld_sc1_u32x4(rc, i * 4);
+    // exclusive prefixes of the candidate counts (wave 0, 64 at a time) and
+    // the above-prefix tokens before this workgroup
+    if (tid < 64) {
+      uint32_t carry = 0, sb = 0;
+      for (int base = 0; base < W; base += 64) {
+        const int i = base + lane;
+        const uint32_t cnt = i < W ? sh.u.r.base[i] : 0u;
+        const uint32_t st = (i < wg) ? sh.u.r.strict[i] : 0u;
+        const uint32_t inc = wave_inclusive_scan(cnt);
+        if (i < W) sh.u.r.base[i] = carry + inc - cnt;
+        carry += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+        uint32_t s2 = st;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) if (i + e < C) sh.u.r.key[i + e] = v[e];
+        for (int o = 32; o >= 1; o >>= 1) s2 += __shfl_xor(s2, o);
+        sb += s2;
       }
+      if (lane == 0) { sh.u.r.base[W] = carry; sh.red[0][0] = sb; }
     }
-    // remaining bits: 10 + 10 after 12, or 8 after 24
-    while (ct.bits < 32 && !ct.all) {
-      const int rem = 32 - ct.bits;
-      const int dbits = rem > 10 ? 10 : rem;
-      const int shift = rem - dbits;
-      const int NBd = 1 << dbits;
-      const int pb = ct.bits;
-      const uint32_t pf = ct.prefix;
-      for (int i = tid; i < kNBL; i += kThreads) { sh.u.r.c[i] = 0; if (MASS) sh.u.r.m[i] = 0.0; }
-      lds_barrier();
-      for (int i = tid; i < C; i += kThreads) {
+    __syncthreads();
+    s_before = sh.red[0][0];
+    const uint32_t C_all = sh.u.r.base[W];
+    if (!ct.all && C_all != ct.in_count && tid == 0) sh.err_any = 1;   // the lists disagree
+    if (keys) {
+      // every candidate, region by region: position order
+      // (wave w loads regions w, w + 4, ..., 64 keys per load, every load
+      // issued before the first is used)
+      const int C = (int)min(C_all, (uint32_t)kCap);
+      {
+        constexpr int kBatch = 8;
+        for (int r0 = wid; r0 < W; r0 += kWaves * kBatch) {
+          uint32_t v[kBatch];
+          int dst[kBatch];
+#pragma unroll
+          for (int q = 0; q < kBatch; ++q) {
+            const int r = r0 + q * kWaves;
+            dst[q] = -1;
+            v[q] = 0u;
+            if (r < W) {
+              const int lo = (int)sh.u.r.base[r], cnt = (int)sh.u.r.base[r + 1] - lo;
+              for (int e = lane; e < cnt && lo + e < C; e += 64) {
+                if (e >= 64) {                  // more than 64 keys in the region: rare
+                  sh.u.r.key[lo + e] = ld_agent(cand_row + (int64_t)r * TILE + e);
+                  continue;
+                }
+                v[q] = ld_agent(cand_row + (int64_t)r * TILE + e);
+                dst[q] = lo + e;
+              }
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < kBatch; ++q)
+            if (dst[q] >= 0) sh.u.r.key[dst[q]] = v[q];
+        }
+      }
+      __syncthreads();
+      // the remaining bits: 10 + 10 after 12, or 8 after 24
+      while (ct.bits < 32 && !ct.all) {
+        const int rem = 32 - ct.bits;
+        const int dbits = rem > 10 ? 10 : rem;
+        const int shift = rem - dbits;
+        const int NBd = 1 << dbits;
+        const int pbd = ct.bits;
+        const uint32_t pfd = ct.prefix;
+        for (int i = tid; i < kNBL; i += kThreads) { sh.u.r.c[i] = 0; if (MASS) sh.u.r.m[i] = 0.0; }
+        lds_barrier();
+        for (int i = tid; i < C; i += kThreads) {
+          const uint32_t k = sh.u.r.key[i];
+          if ((k >> (32 - pbd)) == pfd) {
+            const uint32_t bk = (k >> shift) & (uint32_t)(NBd - 1);
+            atomicAdd(&sh.u.r.c[bk], 1u);
+            if (MASS) atomicAdd(&sh.u.r.m[bk], exp((double)key_to_float(k) - ct.R));
+          }
+        }
+        lds_barrier();
+        if (NBd == kNBL) {
+          constexpr int P = kNBL / kThreads;
+          uint32_t c[P];
+          double w[P];
+#pragma unroll
+          for (int k = 0; k < P; ++k) {
+            const int bk = kNBL - 1 - (P * tid + k);
+            c[k] = sh.u.r.c[bk];
+            w[k] = MASS ? sh.u.r.m[bk] : 0.0;
+          }
+          ct = cut_digit<kNBL, MASS>(a, c, w, false, ct, sh, 10, sh.u.r.c, sh.u.r.m);
+        } else {
+          // 2^dbits buckets (dbits <= 8) fill the top of a 256-bucket digit
+          uint32_t c[1];
+          double w[1];
+          const int bk = kNB3 - 1 - tid;
+          c[0] = bk < NBd ? sh.u.r.c[bk] : 0u;
+          w[0] = (MASS && bk < NBd) ? sh.u.r.m[bk] : 0.0;
+          ct = cut_digit<kNB3, MASS>(a, c, w, false, ct, sh, dbits, sh.u.r.c, sh.u.r.m);
+        }
+      }
+      // candidates of earlier workgroups above the cut, and ties among them
+      const uint32_t cut = ct.prefix;
+      const int mine = (int)min(sh.u.r.base[wg], (uint32_t)C);
+      uint32_t na = 0, nt = 0;
+      for (int i = tid; i < mine; i += kThreads) {
         const uint32_t k = sh.u.r.key[i];
-        if ((k >> (32 - pb)) == pf) {
-          const uint32_t bk = (k >> shift) & (uint32_t)(NBd - 1);
-          atomicAdd(&sh.u.r.c[bk], 1u);
-          if (MASS) atomicAdd(&sh.u.r.m[bk], exp((double)key_to_float(k) - ct.R));
-        }
+        na += k > cut;
+        nt += k == cut;
       }
-      lds_barrier();
-      if (NBd == kNBL) {
-        constexpr int P = kNBL / kThreads;
-        uint32_t c[P];
-        double w[P];
 #pragma unroll
-        for (int k = 0; k < P; ++k) {
-          const int bk = kNBL - 1 - (P * tid + k);
-          c[k] = sh.u.r.c[bk];
-          w[k] = MASS ? sh.u.r.m[bk] : 0.0;
-        }
-        cut_digit<kNBL, MASS>(a, c, w, false, ct, sh, 10, sh.u.r.c, sh.u.r.m);
-      } else {
-        // 2^dbits buckets (dbits <= 8) fill the top of a 256-bucket digit
-        uint32_t c[1];
-        double w[1];
-        const int bk = kNB3 - 1 - tid;
-        c[0] = bk < NBd ? sh.u.r.c[bk] : 0u;
-        w[0] = (MASS && bk < NBd) ? sh.u.r.m[bk] : 0.0;
-        cut_digit<kNB3, MASS>(a, c, w, false, ct, sh, dbits, sh.u.r.c, sh.u.r.m);
-      }
-    }
-  };
-
-  if (tid == 0) { sh.bad = 0; sh.last = 0; }
-  __syncthreads();
-  if (!ct.all) {
-    global_round(1);
-    if (!ct.all) {
-      if (ct.in_count <= (uint32_t)kCap) {
-        candidates();
-      } else {
-        global_round(2);
-        if (!ct.all) {
-          if (ct.in_count <= (uint32_t)kCap) candidates();
-          else global_round(3);
-        }
-      }
+      for (int o = 32; o >= 1; o >>= 1) { na += __shfl_xor(na, o); nt += __shfl_xor(nt, o); }
+      if (lane == 0) { sh.red[0][wid] = na; sh.red[1][wid] = nt; }
+      __syncthreads();
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) { a_before += sh.red[0][w]; t_before += sh.red[1][w]; }
+    } else if (!ct.all) {
+      t_before = sh.u.r.base[wg];              // every candidate is a tie
     }
   }
-  bad = sh.bad;
 
-  // ---- 4. compaction
+  // ---- 4. compaction: this workgroup's selected positions, ascending
   const uint32_t cut = ct.prefix;
   const int64_t need = ct.all ? 0 : ct.need;
   const int64_t m = ct.all ? (int64_t)a.n : ct.above_c + need;
-  uint32_t fs = 0, ft = 0;       // bit i: token i above the cut / a tie
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    if (!valid(i)) continue;
-    if (ct.all || key[i] > cut) fs |= 1u << i;
-    else if (key[i] == cut) ft |= 1u << i;
-  }
-  uint64_t bs[PER], bt[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    bs[i] = __ballot((fs >> i) & 1u);
-    bt[i] = __ballot((ft >> i) & 1u);
-    if (lane == 0) { sh.cnt_s[i][wid] = __popcll(bs[i]); sh.cnt_t[i][wid] = __popcll(bt[i]); }
-  }
-  __syncthreads();
-  uint32_t tot_s = 0, tot_t = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i)
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) { tot_s += sh.cnt_s[i][w]; tot_t += sh.cnt_t[i][w]; }
-  uint64_t* slots = a.slots + (int64_t)row * kMaxSelW;
-  if (tid < 64) {
-    if (lane == 0)
-      __hip_atomic_store(slots + wg, kSlotFlag | ((uint64_t)tot_s << 31) | (uint64_t)tot_t,
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // the (above-cut, tie) counts of every earlier workgroup of the row
-    uint32_t ps = 0, pt = 0;
-    bool ok = true;
-    for (int c0 = 0; c0 < wg; c0 += 64) {
-      const int p = c0 + lane;
-      uint64_t v = kSlotFlag;
-      int spins = 0;
-      if (p < wg) {
-        v = ld_agent(slots + p);
-        while (!(v & kSlotFlag)) {
-          if (a.spin_limit < 0 || ++spins > a.spin_limit) { ok = false; break; }
-          __builtin_amdgcn_s_sleep(1);
-          v = ld_agent(slots + p);
-        }
-      }
-      uint32_t vs = (p < wg && ok) ? (uint32_t)((v >> 31) & 0xFFFFFFFFu) : 0u;
-      uint32_t vt = (p < wg && ok) ? (uint32_t)(v & 0x7FFFFFFFu) : 0u;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) { vs += __shfl_xor(vs, o); vt += __shfl_xor(vt, o); }
-      ps += vs;
-      pt += vt;
-    }
-    const uint64_t okm = __ballot(!ok);
-    if (lane == 0) {
-      sh.pre = ((uint64_t)ps << 32) | pt;
-      if (okm) sh.bad = 1;
-    }
-  }
-  __syncthreads();
-  bad = sh.bad;
-  if (!bad) {
-    const uint32_t ps = (uint32_t)(sh.pre >> 32), pt = (uint32_t)sh.pre;
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    uint32_t run_s = ps, run_t = pt;       // counts before token group i
+  int bad = 0;
+  {
+    uint32_t fs = 0, ft = 0;                  // bit i: token i above the cut / a tie
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      uint32_t ws = 0, wt = 0;
+      if (!valid(i)) continue;
+      if (ct.all || key[i] > cut) fs |= 1u << i;
+      else if (key[i] == cut) ft |= 1u << i;
+    }
+    uint32_t rs[PER], rt[PER], ns, nt;
+    wg_ranks2<PER>(fs, ft, rs, rt, ns, nt, sh.cnt_s, sh.cnt_t);   // (its barriers also publish sh.bad / sh.err_any)
+    bad = sh.bad | sh.err_any;
+    if (!bad) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        if (w < wid) { ws += sh.cnt_s[i][w]; wt += sh.cnt_t[i][w]; }
+      for (int i = 0; i < PER; ++i) {
+        const int j = j0 + i * kThreads + tid;
+        const int64_t sb = (int64_t)s_before + a_before + rs[i];
+        const int64_t tb = (int64_t)t_before + rt[i];
+        int64_t o = -1;
+        if (ct.all) o = j;
+        else if ((fs >> i) & 1u) o = sb + (tb < need ? tb : need);
+        else if (((ft >> i) & 1u) && tb < need) o = sb + tb;
+        if (o >= 0 && o < m && o < a.n_cap) a.sel_idx[orow + o] = j;
       }
-      const uint32_t sb = run_s + ws + __popcll(bs[i] & lt);
-      const uint32_t tb = run_t + wt + __popcll(bt[i] & lt);
-      const int j = j0 + i * kThreads + tid;
-      int64_t o = -1;
-      if ((fs >> i) & 1u) o = (int64_t)sb + ((int64_t)tb < need ? tb : need);
-      else if (((ft >> i) & 1u) && (int64_t)tb < need) o = (int64_t)sb + tb;
-      if (o >= 0 && o < m && o < a.n_cap) a.sel_idx[orow + o] = j;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) { run_s += sh.cnt_s[i][w]; run_t += sh.cnt_t[i][w]; }
     }
   }
 
-  // ---- 5. leave; the last workgroup of the row cleans up
+  // ---- 5. this workgroup's share of the histograms back to zero (every
+  // workgroup has read them: all have published in the exchange), then leave;
+  // the last workgroup of the row out writes sel_count and clears the flags
+  if (rounds > 0) {
+    const int levels = bad ? 3 : rounds;
+    for (int lvl = 0; lvl < levels; ++lvl) {
+      const int NB = (lvl == 2) ? kNB3 : kNB1;
+      uint32_t* gc = a.hist_c + ((int64_t)row * 3 + lvl) * kNB1;
+      double* gm = a.hist_m + ((int64_t)row * 3 + lvl) * kNB1;
+      for (int i = wg + tid * W; i < NB; i += kThreads * W) {
+        gc[i] = 0u;
+        if (MASS) gm[i] = 0.0;
+      }
+    }
+  }
   if (tid == 0) {
     if (bad) sink ^= atomicOr(ctl + kCtlErr, 1u);
     consume(sink);
@@ -678,28 +785,10 @@ __global__ __launch_bounds__(kThreads) void select_fused_kernel(SelectArgs a) {
   if (tid == 0) {
     const uint32_t err = ld_agent(ctl + kCtlErr);
     a.sel_count[(int64_t)b * a.Hkv + g] = err ? -1 : (int32_t)m;
-    sh.bad = err ? 1 : 0;
   }
   __syncthreads();
-  // histograms of the rounds taken (every round after a failed wait, as the
-  // row's workgroups may then have taken different ones), counters and slots
-  // back to zero
-  const int clear_rounds = sh.bad ? 3 : rounds;
-  for (int lvl = 0; lvl < clear_rounds; ++lvl) {
-    const int NB = (lvl == 2) ? kNB3 : kNB1;
-    uint32_t* gc = a.hist_c + ((int64_t)row * 3 + lvl) * kNB1;
-    double* gm = a.hist_m + ((int64_t)row * 3 + lvl) * kNB1;
-    for (int i = 4 * tid; i < NB; i += 4 * kThreads) {
-      *reinterpret_cast<vl_u32x4*>(gc + i) = vl_u32x4{0u, 0u, 0u, 0u};
-      if (MASS) {
-        *reinterpret_cast<vl_u32x4*>(gm + i) = vl_u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<vl_u32x4*>(gm + i + 2) = vl_u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  }
-  for (int i = tid; i < W; i += kThreads) slots[i] = 0ull;
+  for (int i = tid; i < W; i += kThreads) { slot_a[i] = 0u; slot_b[i] = 0ull; }
   if (tid < kCtlWords) ctl[tid] = 0u;
-  (void)used_cand;
 }
 
 hipError_t launch_select_lowrank(const SelectArgs& a, int dtype, int per, hipStream_t s) {

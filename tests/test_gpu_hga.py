@@ -175,41 +175,54 @@ def test_hga_end_to_end_small():
 
 def test_hga_full_size_sampled():
     """The 64K routed workload at full size (16 x 8 groups), inputs drawn on
-    the GPU; sampled groups checked against the oracle.  A group whose oracle
-    cut gaps are under 1e-3 may legitimately route differently (bf16 summary
-    rounding); its set is then only checked for validity of shape."""
+    the GPU.  Eight sampled groups are checked exactly, stage by stage: the
+    oracle routes over the GPU's own bf16 summaries, and a sampled group whose
+    17 routing cuts (top chunks, then the groups of each) are not all at
+    least 1e-3 apart has the non-needle dims of its queries re-drawn until
+    they are; its set must then equal the oracle's, and its outputs the
+    oracle's attention over that set."""
     cfg = workloads.HGA_64K
-    inp = workloads.decode_inputs(cfg, 5, device=DEV)
+    seed = 5
+    inp = workloads.decode_inputs(cfg, seed, device=DEV)
     run = DecodeRun(cfg, inp)
     run.summaries()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    pairs = [(b, g) for b in range(cfg.batch) for g in range(cfg.n_kv_heads)]
+    groups = [pairs[i] for i in sorted(rng.choice(len(pairs), 8, replace=False))]
+    G = cfg.gqa
+    q_pre = inp["q_pre"].to(DEV)
+    q = run.t["q"].float()
+    expect = {}
+    redraws = 0
+    for b, g in groups:
+        cs = np64(run.t["chunk_sum"][b, g])
+        gs = np64(run.t["group_sum"][b, g])
+        for rnd in range(1, 40):
+            qg = np64(q[b, g * G:(g + 1) * G])
+            T, info = oracle.route_token_list(qg, cs, gs, cfg.n_ctx, cfg.chunk, cfg.group,
+                                              cfg.top_chunks, cfg.top_groups, cfg.sink_chunks,
+                                              cfg.local_chunks)
+            if info["chunk_gap"] >= 1e-3 and min(info["group_gaps"]) >= 1e-3:
+                break
+            q_pre, q = workloads.redraw_query_dims(cfg, q_pre, seed, [(b, h) for h in
+                                                   range(g * G, (g + 1) * G)], rnd)
+            redraws += 1
+        else:
+            raise AssertionError(f"no robust redraw for group {(b, g)}")
+        expect[(b, g)] = (T, qg)
+    log("full-size routed groups redrawn", redraws, "times over", len(groups), "groups")
+    run.t["q"].copy_(q.to(run.t["q"].dtype))
     run.select()
     run.decode()
     torch.cuda.synchronize()
     idx, cnt = run.sets()
     out = np64(run.t["out"])
-    rng = np.random.default_rng(0)
-    groups = [(int(b), int(g)) for b, g in zip(rng.integers(0, cfg.batch, 5),
-                                               rng.integers(0, cfg.n_kv_heads, 5))]
-    G = cfg.gqa
-    checked = 0
-    for b, g in groups:
-        sl = {k: inp[k][b:b + 1, g:g + 1] for k in ("k_pre", "k_cache", "v_cache")}
-        sl["q"] = inp["q"][b:b + 1, g * G:(g + 1) * G]
-        ni = {k: np64(v) for k, v in sl.items()}
-        cs, gs = _oracle_summaries(cfg, ni["k_pre"][0, 0], cfg.dtype)
-        T, info = oracle.route_token_list(ni["q"][0], cs, gs, cfg.n_ctx, cfg.chunk, cfg.group,
-                                          cfg.top_chunks, cfg.top_groups, cfg.sink_chunks,
-                                          cfg.local_chunks)
+    for (b, g), (T, qg) in expect.items():
         got = idx[b, g, :cnt[b, g]]
-        assert cnt[b, g] == len(T) and np.all(np.diff(got) > 0)
-        robust = info["chunk_gap"] >= 1e-3 and min(info["group_gaps"]) >= 1e-3
-        if robust:
-            assert np.array_equal(got, T), (b, g)
-            K = ni["k_cache"][0, 0][T]
-            V = ni["v_cache"][0, 0][T]
-            for hh in range(G):
-                o = oracle.attend(ni["q"][0, hh], K, V)
-                assert max_err(out[b, g * G + hh], o) <= 2e-3
-            checked += 1
-    log("full-size groups checked exactly:", checked, "of", len(groups))
-    assert checked >= 1
+        assert cnt[b, g] == len(T) and np.array_equal(got, T), (b, g)
+        K = np64(run.t["k_cache"][b, g])[T]
+        V = np64(run.t["v_cache"][b, g])[T]
+        for hh in range(G):
+            o = oracle.attend(qg[hh], K, V)
+            assert max_err(out[b, g * G + hh], o) <= 2e-3

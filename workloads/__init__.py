@@ -219,6 +219,27 @@ def decode_inputs(cfg: DecodeConfig, seed: int, device="cpu", alpha: float = 1.0
                 needles=needles, n_cap=cap)
 
 
+def redraw_query_dims(cfg: DecodeConfig, q_pre: torch.Tensor, seed: int, heads, round_: int,
+                      alpha: float = 1.0):
+    """Re-draw the dims of ``q_pre`` outside the low-frequency pairs (pairs
+    i < d/4 and their partners) for the query heads ``heads`` [(b, h), ...],
+    from generators tagged with ``round_``; the low-frequency dims, which the
+    needle keys copy, are left as they are.  Returns new (q_pre, q), q being
+    the post-RoPE query at t = n - 1, both rounded to the workload dtype."""
+    d = cfg.head_dim
+    dev = q_pre.device
+    lf = set(low_freq_dims(d).tolist())
+    hf = torch.tensor([i for i in range(d) if i not in lf], device=dev)
+    q_pre = q_pre.clone()
+    for b, h in heads:
+        g = _gen(seed, dev, 5, b, h, round_)
+        x = torch.randn(len(hf), generator=g, dtype=torch.float32, device=dev) * alpha
+        q_pre[b, h, hf] = _quant(x, cfg.dtype)
+    t = cfg.n_ctx - 1
+    q = _quant(apply_rope(q_pre, torch.full((1,), t, device=dev)[0], cfg.rope_base), cfg.dtype)
+    return q_pre, q
+
+
 def lattice_index_inputs(cfg: DecodeConfig, seed: int, k_amp: int = 8,
                          q_amp: int = 4, device="cpu", n_cap: Optional[int] = None) -> dict:
     """Exact-arithmetic index inputs for set-exact selector tests.
