@@ -374,14 +374,17 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
     if (mode == SA_SEL_TOPK && p->top_k < 1) return SA_ERR_INVALID_ARG;
     GroupList gl = groups_of_kind(p, kinds, SA_HEAD_RETRIEVAL);
     const int rows = p->batch * gl.n;
-    // tokens per workgroup: the smallest tile giving at most two workgroups
-    // per compute unit over all rows.  The workgroups of a row wait for each
-    // other, so all of them must be resident together: W stays within the
-    // compute units (each holds at least one), which covers 1M tokens.
+    // tokens per workgroup: 2048 (8 per thread), or a larger tile while the
+    // rows would need more than two workgroups per compute unit (measured:
+    // 1024-token tiles are no faster at 32K and, at more workgroups than the
+    // device holds, run the rows in batches).  The workgroups of a row wait
+    // for each other, so all of them must be resident together: W stays
+    // within the compute units (each holds at least one), which covers 1M
+    // tokens.
     const int cus = compute_units();
     const int wmax = std::min(cus, sa::kMaxSelW);
     auto tiles = [&](int per) { return (p->n_ctx + 256 * per - 1) / (256 * per); };
-    int per = 4;
+    int per = 8;
     while (per < 16 && ((int64_t)rows * tiles(per) > 2 * cus || tiles(per) > wmax)) per *= 2;
     const int W = tiles(per);
     const int64_t cand_stride = (int64_t)W * 256 * per;

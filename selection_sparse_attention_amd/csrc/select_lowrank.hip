@@ -162,6 +162,9 @@ struct SelShared {
   uint32_t top;
   uint32_t cnt_s[16][kWaves], cnt_t[16][kWaves];
   uint32_t red[2][kWaves];
+  uint32_t small[64];   // the last few candidates, for the single-wave cut
+  uint32_t n_small;
+  Cut fin;              // the single-wave cut, for every thread
   int bad;              // a wait of this workgroup timed out
   int err_any;          // some workgroup of the row reported a timed-out wait
   int last;             // this workgroup left the row last
@@ -357,6 +360,92 @@ __device__ __forceinline__ Cut cut_digit(const SelectArgs& a, const uint32_t (&c
     ct.need = (int32_t)need;
   }
   return ct;
+}
+
+// A double held by one lane (the lane index is wave-uniform).
+__device__ __forceinline__ double lane_f64(double v, int src) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, src);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), src);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// The remaining digits of the cut when at most 64 of the C candidate keys in
+// LDS carry the current prefix: wave 0 sorts them (descending, a bitonic
+// network over the lanes) and walks them in order with the rules of
+// cut_digit: the lower of the live crossings decides, and at its key the
+// tie count follows from the mass of one tie or from the count target.
+template <bool MASS>
+__device__ Cut cut_small(const SelectArgs& a, Cut ct, SelShared<MASS>& sh, int C) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int pb = ct.bits;
+  const uint32_t pf = ct.prefix;
+  if (tid == 0) sh.n_small = 0;
+  lds_barrier();
+  for (int i = tid; i < C; i += kThreads) {
+    const uint32_t k = sh.u.r.key[i];
+    if ((k >> (32 - pb)) == pf) {
+      const uint32_t slot = atomicAdd(&sh.n_small, 1u);
+      if (slot < 64u) sh.small[slot] = k;
+    }
+  }
+  lds_barrier();
+  if (tid < 64) {
+    const int n = (int)min(sh.n_small, 64u);
+    uint32_t k = lane < n ? sh.small[lane] : 0u;          // 0: no key (below every real one)
+#pragma unroll
+    for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)k, stride);
+        const bool desc = (lane & size) == 0 || size == 64;
+        const bool low = (lane & stride) == 0;
+        k = (low == desc) ? max(k, o) : min(k, o);
+      }
+    }
+    const bool valid = lane < n;
+    const double e = (MASS && valid) ? exp((double)key_to_float(k) - ct.R) : 0.0;
+    const double incl_w = MASS ? wave_inclusive_scan(e) : 0.0;
+    const double before_w = ct.above_w + incl_w - e;
+    const int64_t before_c = ct.above_c + lane;
+    const bool m_on = (ct.crit & CRIT_MASS) != 0, c_on = (ct.crit & CRIT_COUNT) != 0;
+    const uint64_t mx = __ballot(MASS && m_on && valid && before_w < ct.tmass && before_w + e >= ct.tmass);
+    const uint64_t cx = __ballot(c_on && valid && before_c < ct.tcount && before_c + 1 >= ct.tcount);
+    int lm = -1, lc = -1;
+    if (m_on) lm = mx ? __ffsll((unsigned long long)mx) - 1 : (ct.above_w >= ct.tmass ? 0 : n - 1);
+    if (c_on) lc = cx ? __ffsll((unsigned long long)cx) - 1 : (n - 1);
+    const int ls = max(lm, lc);
+    const uint32_t ks = (uint32_t)__builtin_amdgcn_readlane((int)k, max(ls, 0));
+    const bool mass_live = m_on && lm >= 0 && (uint32_t)__builtin_amdgcn_readlane((int)k, lm) == ks;
+    const bool count_live = c_on && lc >= 0 && (uint32_t)__builtin_amdgcn_readlane((int)k, lc) == ks;
+    const uint64_t tie = __ballot(valid && k == ks);
+    const int f = tie ? __ffsll((unsigned long long)tie) - 1 : 0;
+    const int64_t ties = __popcll(tie);
+    Cut r = ct;
+    r.above_c = ct.above_c + f;
+    r.above_w = MASS ? lane_f64(before_w, f) : 0.0;
+    r.prefix = ks;
+    r.bits = 32;
+    r.in_count = (uint32_t)ties;
+    r.crit = (mass_live ? CRIT_MASS : 0) | (count_live ? CRIT_COUNT : 0);
+    int64_t need = 1;
+    if (mass_live) {
+      const double et = exp((double)key_to_float(ks) - ct.R);
+      const double cn = ceil((ct.tmass - r.above_w) / et);
+      need = (cn >= (double)ties) ? ties : (cn <= 1.0 ? 1 : (int64_t)cn);
+    }
+    if (count_live) {
+      const int64_t nc = ct.tcount - r.above_c;
+      need = need > nc ? need : nc;
+    }
+    if (need > ties) need = ties;
+    if (need < 1) need = 1;
+    r.need = (int32_t)need;
+    if (ls < 0) r.all = 1;                               // no live criterion (cannot happen)
+    if (lane == 0) sh.fin = r;
+  }
+  lds_barrier();
+  return sh.fin;
 }
 
 // ------------------------------------------------------------------ the kernel
@@ -668,8 +757,13 @@ __global__ __launch_bounds__(kThreads) void select_fused_kernel(SelectArgs a) {
         }
       }
       __syncthreads();
-      // the remaining bits: 10 + 10 after 12, or 8 after 24
+      // the remaining bits: 10 + 10 after 12, or 8 after 24, by LDS
+      // histograms until at most 64 candidates are left, then by one wave
       while (ct.bits < 32 && !ct.all) {
+        if (ct.in_count <= 64u) {
+          ct = cut_small<MASS>(a, ct, sh, C);
+          break;
+        }
         const int rem = 32 - ct.bits;
         const int dbits = rem > 10 ? 10 : rem;
         const int shift = rem - dbits;
@@ -798,7 +892,6 @@ hipError_t launch_select_lowrank(const SelectArgs& a, int dtype, int per, hipStr
 #define SA_SEL(T_, M_, P_) hipLaunchKernelGGL((select_fused_kernel<T_, M_, P_>), grid, block, 0, s, a)
 #define SA_SEL_P(T_, M_)                      \
   switch (per) {                              \
-    case 4: SA_SEL(T_, M_, 4); break;         \
     case 8: SA_SEL(T_, M_, 8); break;         \
     case 16: SA_SEL(T_, M_, 16); break;       \
     default: return hipErrorInvalidValue;     \
