@@ -293,6 +293,7 @@ int32_t sparse_attn_index_build(const sa_params* p, const sa_buffers* b, int32_t
     a.k_idx = b->k_idx; a.q_idx = b->q_idx;
     a.B = p->batch; a.Hq = p->n_q_heads; a.Hkv = p->n_kv_heads; a.n_cap = p->n_cap; a.G = G;
     a.t0 = t_begin; a.t1 = t_end; a.groups = gl;
+    a.tokens_per_wg = 2048;      // a whole number of the kernel's steps for every shape
     return hip_status(sa::launch_index_lowrank(a, p->dtype, p->head_dim, s));
   }
   if (mode == SA_IDX_CHUNK_SUMMARY) {

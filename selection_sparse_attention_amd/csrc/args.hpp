@@ -25,6 +25,7 @@ struct IndexLowrankArgs {
   void* k_idx;           // [B,Hkv,n_cap,16]
   float* q_idx;          // [B,Hq,16]
   int32_t B, Hq, Hkv, n_cap, G, t0, t1;
+  int32_t tokens_per_wg; // key rows per workgroup
   GroupList groups;
 };
 

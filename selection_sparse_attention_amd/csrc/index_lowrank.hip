@@ -5,69 +5,288 @@
 // k_idx[b,g,j,c] = sum_e P_k[g,c,e] * k_pre[b,g,j,e]   (fp32, rounded once)
 // q_idx[b,h,c]   = sum_e P_q[g,c,e] * q_pre[b,h,e]     (fp32)
 //
-// One workgroup projects 16 tokens of one (sequence, retrieval group): the
-// group's projector (16 x d fp32) and the 16 key rows are staged in LDS and
-// each of the 256 threads produces one (token, component) output.  The last
-// x-block of the grid projects the group's query heads instead.  This is an
-// HBM-bound pass over k_pre (d * e bytes per token in, 16 * e out).
+// Key side: an HBM-bound stream over k_pre (d * e bytes in, 16 * e out per
+// token).  L = d / (16 bytes / e) lanes share a token: each loads 16
+// contiguous bytes of its row (so one wave instruction reads 64 / L whole
+// rows) and multiplies them with its slice of the projector, which it holds
+// in registers for the whole launch (16 outputs x 16 bytes of dims).  A
+// recursive-halving exchange across the token's lanes then sums the 16
+// partial outputs, leaving output c on lane c of the token (outputs 2c and
+// 2c + 1 on lane c when L = 8; output c on lanes 2c and 2c + 1 when L = 32),
+// so a token's 16 outputs are stored contiguously.  Every token goes
+// through the same order of operations, so appending rows one at a time
+// gives the same bits as a full build.  Query side: the last workgroup of each
+// (sequence, group) projects the group's query heads the same way (they are
+// consecutive rows of q_pre).
 #include "args.hpp"
 #include "common.hpp"
 
 namespace sa {
 
+constexpr int kIdxThreads = 256;
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void index_lowrank_kernel(IndexLowrankArgs a) {
-  __shared__ float sP[16][D + 1];
-  __shared__ float sK[16][D + 1];
-  const int tid = threadIdx.x;
+struct IdxGeom {
+  static constexpr int E = 16 / (int)sizeof(T);    // dims per lane (one 16-byte load)
+  static constexpr int L = D / E;                  // lanes per token
+  static constexpr int TPW = 64 / L;               // tokens per wave step
+};
+
+// One 16-byte slice of a key row, widened to fp32.
+template <typename T> struct Slice;
+template <> struct Slice<bf16_t> {
+  static constexpr int E = 8;
+  vl_u32x4 w;
+  __device__ void load(const void* base, int64_t elem) {
+    w = __builtin_nontemporal_load(reinterpret_cast<const vl_u32x4*>(reinterpret_cast<const uint16_t*>(base) + elem));
+  }
+  __device__ float get(int i) const { return (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]); }
+};
+template <> struct Slice<float> {
+  static constexpr int E = 4;
+  vl_f32x4 w;
+  __device__ void load(const void* base, int64_t elem) {
+    w = __builtin_nontemporal_load(reinterpret_cast<const vl_f32x4*>(reinterpret_cast<const float*>(base) + elem));
+  }
+  __device__ float get(int i) const { return w[i]; }
+};
+
+// Sum the 16 per-lane partial outputs over the L lanes of a token (lanes
+// l0 .. l0 + L - 1, l0 a multiple of L): recursive halving, each step keeps
+// the half of the outputs selected by one bit of the lane index.  Returns
+// with acc[0 .. 16/L) holding outputs  (lane % L) * (16/L) + i; for L = 32
+// the last step adds two lanes that hold the same output, so lanes 2c and
+// 2c + 1 of a token both end with output c.
+// A value from lane (lane ^ S).  Inside a 16-lane row by DPP (VALU moves):
+// quad permutes for S = 1, 2; a rotate by 8 for S = 8; for S = 4 the lanes
+// with bit 2 set take the rotate by 4 (from lane - 4) and the others the
+// rotate by 12 (from lane + 4).  S = 16 and 32 go through ds_bpermute.
+template <int CTRL>
+__device__ __forceinline__ float dpp_xf(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int S>
+__device__ __forceinline__ float xor_lane(float v, int lane) {
+  if constexpr (S == 1) return dpp_xf<0xB1>(v);         // quad_perm [1,0,3,2]
+  else if constexpr (S == 2) return dpp_xf<0x4E>(v);    // quad_perm [2,3,0,1]
+  else if constexpr (S == 4) {
+    const float from_below = dpp_xf<0x124>(v), from_above = dpp_xf<0x12C>(v);   // row_ror 4 / 12
+    return (lane & 4) ? from_below : from_above;
+  } else if constexpr (S == 8) return dpp_xf<0x128>(v);  // row_ror 8
+  else return __shfl_xor(v, S);
+}
+
+// One halving step over lane bit S with N outputs still held (compile-time
+// sizes, so every register index is static).
+template <int S, int N>
+__device__ __forceinline__ void rs_step(float (&acc)[16], int lane) {
+  if constexpr (S >= 1) {
+    if constexpr (N > 1) {
+      constexpr int H = N / 2;
+      // lanes with bit S set keep the upper half (and send the lower)
+      const bool upper = (lane & S) != 0;
+#pragma unroll
+      for (int i = 0; i < H; ++i) {
+        const float keep = upper ? acc[H + i] : acc[i];
+        const float give = upper ? acc[i] : acc[H + i];
+        acc[i] = keep + xor_lane<S>(give, lane);
+      }
+      rs_step<S / 2, H>(acc, lane);
+    } else {
+      acc[0] += xor_lane<S>(acc[0], lane);
+      rs_step<S / 2, 1>(acc, lane);
+    }
+  }
+}
+
+template <int L>
+__device__ __forceinline__ void reduce_scatter16(float (&acc)[16]) {
+  rs_step<L / 2, 16>(acc, threadIdx.x & 63);
+}
+
+// Project rows [first, last) of src (row r at element (row0 + r) * D) with
+// the projector P (16 x D fp32): dst[(row0 + r) * 16 + c], in the element
+// type of OutT.  The workgroup's waves take TPW rows per step each, U steps
+// of loads in flight (16 for builds: with two waves per SIMD the stream needs
+// that many rows in flight; 1 for appends, where only latency counts).
+template <typename T, int D, typename OutT, int U>
+__device__ __forceinline__ void project_rows(const void* src, const float* Pg, void* dst, int64_t row0,
+                                             int first, int last) {
+  using GM = IdxGeom<T, D>;
+  constexpr int E = GM::E, L = GM::L, TPW = GM::TPW;
+  constexpr int OUTS = (16 / L) > 0 ? (16 / L) : 1;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  // this lane's slice of the projector: dims e0 .. e0 + E of every output
+  const int sl = lane % L;
+  const int e0 = sl * E;
+  float P[16][E];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+#pragma unroll
+    for (int q = 0; q < E; q += 4) {
+      const vl_f32x4 v = *reinterpret_cast<const vl_f32x4*>(Pg + c * D + e0 + q);
+      P[c][q] = v[0]; P[c][q + 1] = v[1]; P[c][q + 2] = v[2]; P[c][q + 3] = v[3];
+    }
+  }
+  const int tw = lane / L;                         // this lane's row within a wave step
+  constexpr int STEP = TPW * (kIdxThreads / 64);   // rows per workgroup step
+  for (int base = first; base < last; base += STEP * U) {
+    Slice<T> s[U];
+    int row[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      row[u] = base + (u * (kIdxThreads / 64) + wid) * TPW + tw;
+      s[u].load(src, (row0 + min(row[u], last - 1)) * D + e0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float acc[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        float x = 0.f;
+#pragma unroll
+        for (int q = 0; q < E; ++q) x = fmaf(P[c][q], s[u].get(q), x);
+        acc[c] = x;
+      }
+      reduce_scatter16<L>(acc);
+      if (row[u] < last) {
+        if (L <= 16) {
+#pragma unroll
+          for (int i = 0; i < OUTS; ++i) Elem<OutT>::store(dst, (row0 + row[u]) * 16 + sl * OUTS + i, acc[i]);
+        } else if ((sl & 1) == 0) {
+          Elem<OutT>::store(dst, (row0 + row[u]) * 16 + (sl >> 1), acc[0]);
+        }
+      }
+    }
+  }
+}
+
+// bf16 rows on the matrix cores: for a tile of 16 rows, out[row][c] =
+// sum_e row[e] P[c][e] is one v_mfma_f32_16x16x32_bf16 per 32 dims, with the
+// rows as the A operand (lane l: row l % 16, dims 32 s + 8 (l / 16) .. +8, 64
+// contiguous bytes of every row per load) and the projector as the B operand
+// (lane l: output l % 16, the same dims).  The fp32 projector is split into
+// three bf16 parts (p = hi + mid + lo up to 2^-24 |p|), each multiplied in, so
+// the sum keeps fp32's precision; the accumulation is fp32.  The result
+// leaves rows 4 (l / 16) .. +4 of output l % 16 on lane l.
+typedef __bf16 ix_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float ix_f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint16_t ix_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+template <int D, typename OutT, int U>
+__device__ __forceinline__ void project_rows_mfma(const void* src, const float* Pg, void* dst, int64_t row0,
+                                                  int first, int last) {
+  constexpr int KS = D / 32;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int col = lane & 15, kb = lane >> 4;
+  ix_bf16x8 ph[KS], pm[KS], pl[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const float* pr = Pg + col * D + 32 * s + 8 * kb;
+    const vl_f32x4 x0 = *reinterpret_cast<const vl_f32x4*>(pr);
+    const vl_f32x4 x1 = *reinterpret_cast<const vl_f32x4*>(pr + 4);
+    uint16_t h[8], m[8], l[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = i < 4 ? x0[i] : x1[i - 4];
+      h[i] = ix_bf16_rne(p);
+      const float r1 = p - __uint_as_float((uint32_t)h[i] << 16);
+      m[i] = ix_bf16_rne(r1);
+      const float r2 = r1 - __uint_as_float((uint32_t)m[i] << 16);
+      l[i] = ix_bf16_rne(r2);
+    }
+    vl_u32x4 wh, wm, wl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wh[i] = (uint32_t)h[2 * i] | ((uint32_t)h[2 * i + 1] << 16);
+      wm[i] = (uint32_t)m[2 * i] | ((uint32_t)m[2 * i + 1] << 16);
+      wl[i] = (uint32_t)l[2 * i] | ((uint32_t)l[2 * i + 1] << 16);
+    }
+    ph[s] = __builtin_bit_cast(ix_bf16x8, wh);
+    pm[s] = __builtin_bit_cast(ix_bf16x8, wm);
+    pl[s] = __builtin_bit_cast(ix_bf16x8, wl);
+  }
+  const uint16_t* sp = reinterpret_cast<const uint16_t*>(src);
+  constexpr int STEP = 16 * U * (kIdxThreads / 64);   // rows per workgroup step
+  for (int base = first + wid * 16 * U; base < last; base += STEP) {
+    vl_u32x4 av[U][KS];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = min(base + 16 * u + col, last - 1);
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        av[u][s] = __builtin_nontemporal_load(
+            reinterpret_cast<const vl_u32x4*>(sp + (row0 + r) * D + 32 * s + 8 * kb));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      ix_f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const ix_bf16x8 av8 = __builtin_bit_cast(ix_bf16x8, av[u][s]);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av8, pl[s], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av8, pm[s], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av8, ph[s], c, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = base + 16 * u + 4 * kb + i;
+        if (r < last) Elem<OutT>::store(dst, (row0 + r) * 16 + col, c[i]);
+      }
+    }
+  }
+}
+
+template <typename T, int D, int U>
+__global__ __launch_bounds__(kIdxThreads) void index_lowrank_kernel(IndexLowrankArgs a) {
   const int gi = blockIdx.y, b = blockIdx.z;
   const int g = a.groups.ids[gi];
-  const int ntiles = (a.t1 - a.t0 + 15) / 16;
-  const bool q_side = (int)blockIdx.x == ntiles;
-  const float* P = (q_side ? a.proj_q : a.proj_k) + (int64_t)g * 16 * D;
-
-  for (int i = tid; i < 16 * D; i += 256) sP[i / D][i % D] = P[i];
-
-  if (q_side) {
+  const int n_tok = a.t1 - a.t0;
+  const int per_wg = (int)a.tokens_per_wg;
+  const int kblocks = (n_tok + per_wg - 1) / per_wg;
+  constexpr bool kMfma = sizeof(T) == 2;
+  if ((int)blockIdx.x == kblocks) {
+    // query side: the group's G query heads are G consecutive rows of q_pre
     if (a.q_pre == nullptr) return;
-    __syncthreads();
-    // 16 heads per pass of the workgroup, as many passes as the group has heads
-    const int c = tid % 16;
-    for (int hh = tid / 16; hh < a.G; hh += 16) {
-      const int h = g * a.G + hh;
-      const int64_t base = ((int64_t)b * a.Hq + h) * D;
-      float acc = 0.f;
-      for (int e = 0; e < D; ++e) acc = fmaf(sP[c][e], Elem<T>::load(a.q_pre, base + e), acc);
-      a.q_idx[((int64_t)b * a.Hq + h) * 16 + c] = acc;
-    }
+    if constexpr (kMfma)
+      project_rows_mfma<D, float, 1>(a.q_pre, a.proj_q + (int64_t)g * 16 * D, a.q_idx,
+                                     (int64_t)b * a.Hq + (int64_t)g * a.G, 0, a.G);
+    else
+      project_rows<T, D, float, 1>(a.q_pre, a.proj_q + (int64_t)g * 16 * D, a.q_idx,
+                                   (int64_t)b * a.Hq + (int64_t)g * a.G, 0, a.G);
     return;
   }
-
-  const int j0 = a.t0 + 16 * blockIdx.x;
-  const int64_t row0 = ((int64_t)b * a.Hkv + g) * a.n_cap;
-  for (int i = tid; i < 16 * D; i += 256) {
-    const int jj = i / D, e = i % D;
-    const int j = j0 + jj;
-    sK[jj][e] = (j < a.t1) ? Elem<T>::load(a.k_pre, (row0 + j) * D + e) : 0.f;
-  }
-  __syncthreads();
-  const int jj = tid / 16, c = tid % 16;
-  const int j = j0 + jj;
-  if (j >= a.t1) return;
-  float acc = 0.f;
-#pragma unroll 8
-  for (int e = 0; e < D; ++e) acc = fmaf(sP[c][e], sK[jj][e], acc);
-  Elem<T>::store(a.k_idx, (row0 + j) * 16 + c, acc);
+  const int first = a.t0 + (int)blockIdx.x * per_wg;
+  if constexpr (kMfma)
+    project_rows_mfma<D, T, U>(a.k_pre, a.proj_k + (int64_t)g * 16 * D, a.k_idx,
+                                            ((int64_t)b * a.Hkv + g) * a.n_cap, first,
+                                            min(first + per_wg, a.t1));
+  else
+    project_rows<T, D, T, U>(a.k_pre, a.proj_k + (int64_t)g * 16 * D, a.k_idx,
+                             ((int64_t)b * a.Hkv + g) * a.n_cap, first, min(first + per_wg, a.t1));
 }
 
 hipError_t launch_index_lowrank(const IndexLowrankArgs& a, int dtype, int d, hipStream_t s) {
-  const int ntiles = (a.t1 - a.t0 + 15) / 16;
-  dim3 grid(ntiles + 1, a.groups.n, a.B);
-  if (dtype == 0 && d == 128) hipLaunchKernelGGL((index_lowrank_kernel<bf16_t, 128>), grid, dim3(256), 0, s, a);
-  else if (dtype == 0 && d == 64) hipLaunchKernelGGL((index_lowrank_kernel<bf16_t, 64>), grid, dim3(256), 0, s, a);
-  else if (dtype == 1 && d == 128) hipLaunchKernelGGL((index_lowrank_kernel<float, 128>), grid, dim3(256), 0, s, a);
-  else if (dtype == 1 && d == 64) hipLaunchKernelGGL((index_lowrank_kernel<float, 64>), grid, dim3(256), 0, s, a);
+  const int n_tok = a.t1 - a.t0;
+  const int kblocks = (n_tok + a.tokens_per_wg - 1) / a.tokens_per_wg;
+  dim3 grid(kblocks + 1, a.groups.n, a.B), block(kIdxThreads);
+  const bool build = n_tok > 64;
+#define SA_IDX(T_, D_)                                                                       \
+  do {                                                                                       \
+    if (build) hipLaunchKernelGGL((index_lowrank_kernel<T_, D_, 8>), grid, block, 0, s, a); \
+    else hipLaunchKernelGGL((index_lowrank_kernel<T_, D_, 1>), grid, block, 0, s, a);        \
+  } while (0)
+  if (dtype == 0 && d == 128) SA_IDX(bf16_t, 128);
+  else if (dtype == 0 && d == 64) SA_IDX(bf16_t, 64);
+  else if (dtype == 1 && d == 128) SA_IDX(float, 128);
+  else if (dtype == 1 && d == 64) SA_IDX(float, 64);
   else return hipErrorInvalidValue;
+#undef SA_IDX
   return hipGetLastError();
 }
 
