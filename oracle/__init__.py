@@ -20,6 +20,9 @@ Sources (web summaries of five papers; cited by page title and section):
   dense attention on the gathered subsequence and scatter back.
 * "Autonomia de Cabecas (AoH)" summary - Methodology item 4: head scores are
   averaged to the GQA group; sinks plus a recent window for streaming heads.
+* Head-split prefill (RTPurbo, Methodology item 1): local heads window their
+  prefill, retrieval heads attend densely; per-query-head selection as the
+  group rule applied to a group of one head.
 
 Readings of points the pages leave open are listed, one per line, in the
 design notes next to this package and are restated where each is used.
@@ -42,6 +45,7 @@ from .hga import (high_freq_pairs, chunk_summary, chunk_summaries, group_summari
                   route_token_list, route_scores)
 from .lighthouse import (pyramid_levels, pyramid_scores, visible_entries,
                          block_select, prefill_block, prefill)
-from .decode import decode_step, decode_token_sets
+from .decode import decode_step, decode_token_sets, decode_token_sets_per_head
+from .prefill_heads import prefill_visible, head_prefill_rows, visible_pairs
 
 __all__ = [n for n in dir() if not n.startswith("_")]

@@ -540,3 +540,138 @@ def test_pyramid_three_levels_hand_fixture():
         out, _, _, _ = oracle.prefill(Q, K, V, L, p, qb, case["top_k"], store=None)
         for i, want in case["out"].items():
             np.testing.assert_allclose(out[int(i)], [_hand_value(v) for v in want], atol=1e-12)
+
+
+# --------------------------------------------------------------- per-head selection
+def _split_groups(cfg, inp):
+    """The same step with every query head given a KV group of its own (the
+    group's keys, values, pre-RoPE keys and projector repeated G times)."""
+    G = cfg.gqa
+    inp2 = dict(inp)
+    for k in ("k_pre", "k_cache", "v_cache", "proj"):
+        inp2[k] = np.repeat(inp[k], G, axis=1 if k != "proj" else 0)
+    return cfg.with_(n_kv_heads=cfg.n_q_heads), inp2
+
+
+@pytest.mark.parametrize("which", ["topp", "topk", "routed"])
+def test_per_head_sets_equal_groups_of_one(which):
+    # per-query-head mode under GQA (G = 4) against the group rule on a
+    # layout where each query head owns a copy of its KV group: sets and
+    # outputs must agree head by head
+    base = workloads.TINY.with_(n_q_heads=8, n_kv_heads=2, n_ctx=1500, n_ret_q_heads=4,
+                                needles_per_head=8)
+    cfg = {"topp": base, "topk": base.with_(top_k=100),
+           "routed": workloads.HGA_64K.with_(batch=1, n_q_heads=8, n_kv_heads=2, head_dim=64,
+                                             n_ctx=64 * 30 + 9, top_chunks=5,
+                                             needles_per_head=4)}[which]
+    inp = _np_inputs(cfg, 11)
+    cfg2, inp2 = _split_groups(cfg, inp)
+    per_head = oracle.decode_token_sets_per_head(cfg, inp)
+    groups = oracle.decode_token_sets(cfg2, inp2)
+    assert per_head.keys() == groups.keys()
+    differs = 0
+    for key in per_head:
+        assert per_head[key].tolist() == groups[key].tolist()
+    G = cfg.gqa
+    for h in range(cfg.n_q_heads):        # heads of one group pick different sets
+        differs += per_head[(0, h)].tolist() != per_head[(0, (h // G) * G)].tolist()
+    assert differs > 0
+    o1 = oracle.decode_step(cfg, inp, per_head=True)
+    o2 = oracle.decode_step(cfg2, inp2)
+    for key in o1:
+        np.testing.assert_allclose(o1[key], o2[key], atol=1e-12)
+
+
+def test_per_head_equals_group_mode_without_gqa():
+    cfg = workloads.TINY
+    inp = _np_inputs(cfg, 12)
+    a = oracle.decode_token_sets_per_head(cfg, inp)
+    b = oracle.decode_token_sets(cfg, inp)
+    assert {k: v.tolist() for k, v in a.items()} == {k: v.tolist() for k, v in b.items()}
+
+
+def test_per_head_topk_brute_force():
+    # each retrieval head's own top-k by brute force over its own logits
+    cfg = workloads.TINY.with_(n_q_heads=4, n_kv_heads=1, n_ret_q_heads=4, n_ctx=300, top_k=7,
+                               r=16)
+    li = workloads.lattice_index_inputs(cfg, 5)
+    inp = {"head_kind": li["head_kind"].numpy()}
+    k_idx = li["k_idx"].numpy().astype(np.float64)
+    q_idx = li["q_idx"].numpy().astype(np.float64)
+    sets = oracle.decode_token_sets_per_head(cfg, inp, k_idx=k_idx, q_idx=q_idx)
+    for h in range(4):
+        lg = [float(np.dot(q_idx[0, h], k_idx[0, 0, j])) / 4.0 for j in range(300)]
+        best = sorted(range(300), key=lambda j: (-lg[j], j))[:7]
+        assert sets[(0, h)].tolist() == sorted(best)
+
+
+# --------------------------------------------------------------- head-split prefill
+def _qkv(seed, N=260, d=16):
+    rng = np.random.default_rng(seed)
+    return tuple(rng.standard_normal((N, d)) for _ in range(3))
+
+
+@pytest.mark.parametrize("kind,sinks,window", [(0, 4, 260), (0, 0, 1000), (0, 260, 0),
+                                               (0, 300, 5), (1, 4, 16), (2, 0, 0)])
+def test_head_prefill_reduces_to_dense_causal(kind, sinks, window):
+    # window >= n (or sinks covering everything) on a local head, and every
+    # retrieval or routed head: torch's causal attention
+    Q, K, V = _qkv(20)
+    o = oracle.head_prefill_rows(Q, K, V, kind, sinks, window, np.arange(260))
+    np.testing.assert_allclose(o, sdpa64(Q, K, V, causal=True), atol=1e-12)
+
+
+def test_head_prefill_window_one_is_own_value():
+    Q, K, V = _qkv(21)
+    o = oracle.head_prefill_rows(Q, K, V, 0, 0, 1, np.arange(260))
+    np.testing.assert_allclose(o, V, atol=1e-15)
+
+
+def test_head_prefill_one_sink_one_window_closed_form():
+    # query i >= 1 sees keys 0 and i: a two-term softmax
+    Q, K, V = _qkv(22)
+    rows = np.arange(260)
+    o = oracle.head_prefill_rows(Q, K, V, 0, 1, 1, rows)
+    np.testing.assert_allclose(o[0], V[0], atol=1e-15)
+    for i in rows[1:]:
+        a0, ai = Q[i] @ K[0] / 4.0, Q[i] @ K[i] / 4.0
+        w0 = 1.0 / (1.0 + math.exp(ai - a0))
+        np.testing.assert_allclose(o[i], w0 * V[0] + (1 - w0) * V[i], atol=1e-13)
+
+
+@pytest.mark.parametrize("window", [1, 7, 64])
+def test_head_prefill_pure_window_is_sdpa_on_slice(window):
+    Q, K, V = _qkv(23)
+    o = oracle.head_prefill_rows(Q, K, V, 0, 0, window, np.arange(260))
+    for i in range(260):
+        lo = max(0, i - window + 1)
+        np.testing.assert_allclose(o[i], sdpa64(Q[i], K[lo:i + 1], V[lo:i + 1])[0], atol=1e-12)
+
+
+@pytest.mark.parametrize("sinks,window", [(4, 32), (3, 1), (40, 17)])
+def test_head_prefill_sinks_and_window_masked_sdpa(sinks, window):
+    # torch's attention with a boolean mask written from key distances
+    Q, K, V = _qkv(24)
+    N = 260
+    mask = torch.zeros(N, N, dtype=torch.bool)
+    for i in range(N):
+        for j in range(i + 1):
+            mask[i, j] = j < sinks or (i - j) < window
+    qt, kt, vt = (torch.as_tensor(x)[None, None] for x in (Q, K, V))
+    ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask[None, None])[0, 0].numpy()
+    o = oracle.head_prefill_rows(Q, K, V, 0, sinks, window, np.arange(N))
+    np.testing.assert_allclose(o, ref, atol=1e-12)
+
+
+@pytest.mark.parametrize("N,sinks,window", [(10, 2, 3), (300, 4, 64), (50, 60, 0), (77, 0, 5)])
+def test_visible_pairs_closed_form(N, sinks, window):
+    # |[0, min(s, i+1))| + |[max(0, i-w+1), i]| - their overlap, summed
+    total = 0
+    for i in range(N):
+        a = min(sinks, i + 1)
+        lo = max(0, i - window + 1)
+        wcount = (i + 1 - lo) if window > 0 else 0
+        over = max(0, a - lo) if window > 0 else 0
+        total += a + wcount - over
+    assert oracle.visible_pairs(N, 0, sinks, window) == total
+    assert oracle.visible_pairs(N, 1, sinks, window) == N * (N + 1) // 2
