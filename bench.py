@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--workload", default="llama3_8b_decode_32k",
                     choices=["llama3_8b_decode_32k", "llama3_8b_decode_128k",
                              "llama3_8b_decode_128k_topk", "hga_route_decode_64k",
-                             "pyramid_prefill_128k"])
+                             "pyramid_prefill_128k", "llama3_8b_head_split_prefill_32k"])
     ap.add_argument("--instances", type=int, default=4,
                     help="independent input sets rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -419,7 +419,8 @@ def _oracle_decode_sample(cfg, inst, budget_s, torch):
 
 def compact(r):
     keep = ("value", "unit", "ms_per_step", "step_hbm_gbps", "step_roofline",
-            "selected_frac_mean", "config", "roofline", "step_tflops", "spread_us")
+            "selected_frac_mean", "config", "roofline", "step_tflops", "spread_us",
+            "all_dense_ms", "speedup_vs_all_dense")
     return {k: r[k] for k in keep if k in r}
 
 
@@ -441,6 +442,8 @@ def main():
         return
     if args.workload == "pyramid_prefill_128k":
         res = run_prefill(args, torch, sa, workloads)
+    elif args.workload == "llama3_8b_head_split_prefill_32k":
+        res = run_prefill_heads(args, torch, sa, workloads)
     else:
         res = run_decode(args, torch, sa, workloads)
     if not args.no_extras and args.workload == "llama3_8b_decode_32k":
@@ -455,6 +458,8 @@ def main():
                 instances=4, cpu=False, alpha=a))
         other["pyramid_prefill_128k"] = compact(run_prefill(args, torch, sa, workloads, steps=5,
                                                             warmup=1, cpu=False))
+        other["llama3_8b_head_split_prefill_32k"] = compact(run_prefill_heads(
+            args, torch, sa, workloads, steps=5, warmup=1, cpu=False))
         res["other_workloads"] = other
     print(json.dumps(res), flush=True)
 
@@ -560,6 +565,125 @@ def run_prefill(args, torch, sa, workloads, steps=None, warmup=None, cpu=True):
     del t
     torch.cuda.empty_cache()
     return res
+
+
+def head_split_pairs(n, local, sinks, window):
+    """(query, key) pairs one head attends over in a head-split prefill of n
+    tokens: every i sees [0, i] (dense) or [0, min(s, i + 1)) and
+    [max(0, i - w + 1), i] (local, a union)."""
+    import numpy as np
+    if not local:
+        return n * (n + 1) // 2
+    i = np.arange(n, dtype=np.int64)
+    a = np.minimum(sinks, i + 1)
+    lo = np.maximum(0, i - window + 1)
+    w = (i + 1 - lo) if window > 0 else np.zeros_like(i)
+    over = np.maximum(0, a - lo) if window > 0 else np.zeros_like(i)
+    return int((a + w - over).sum())
+
+
+def run_prefill_heads(args, torch, sa, workloads, steps=None, warmup=None, cpu=True):
+    """Head-split prefill of the 32K decode layer's heads (one sequence):
+    the retrieval heads dense causal, the local heads over sinks + window.
+    Also times the same call with every head dense (the full-attention
+    prefill this method replaces) for the speed-up."""
+    cfg = workloads.LLAMA_PREFILL_32K
+    steps = steps or max(3, min(args.steps, 10))
+    warmup = 1 if warmup is None else warmup
+    B, Hq, N, d = cfg.batch, cfg.n_q_heads, cfg.n_ctx, cfg.head_dim
+    log(f"[bench] generating {cfg.name}")
+    inp = workloads.head_prefill_inputs(cfg, 2100, device="cuda")
+    t = {k: inp[k].to(torch.bfloat16).contiguous() for k in ("q", "k_cache", "v_cache")}
+    del inp
+    t["out"] = torch.zeros(B, Hq, N, d, dtype=torch.float32, device="cuda")
+    bufs = sa.make_buffers(q=t["q"], k_cache=t["k_cache"], v_cache=t["v_cache"], out=t["out"])
+    p = sa.params_from_config(cfg)
+    p_dense = sa.params_from_config(cfg.with_(n_ret_q_heads=Hq))
+    stream = torch.cuda.current_stream()
+
+    def timed(params, n):
+        for _ in range(warmup):
+            sa.prefill_heads(params, bufs)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for a, b in ev:
+            a.record(stream)
+            sa.prefill_heads(params, bufs)
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / n * 1e-3
+
+    t_kernel = timed(p, steps)
+    t_dense = timed(p_dense, max(2, steps // 2))
+    timed(p, 1)                                   # leave the head-split result in out
+    kinds = cfg.head_kind()
+    pairs = B * sum(head_split_pairs(N, k == workloads.HEAD_LOCAL, cfg.sinks, cfg.window)
+                    for k in kinds)
+    flops = 4 * d * pairs
+    achieved = flops / t_kernel / 1e12
+    log(f"[bench] {cfg.name}: prefill kernel {t_kernel * 1e3:.3f} ms, {achieved:.1f} TFLOP/s; "
+        f"all heads dense {t_dense * 1e3:.3f} ms ({t_dense / t_kernel:.2f}x)")
+    sha = source_sha(["prefill.hip", "common.hpp", "args.hpp"])
+    res = {
+        "metric": "head-split prefill tokens/s + achieved bf16 MFMA TFLOP/s vs peak",
+        "value": B * Hq * N / t_kernel, "unit": "tokens/s (B x heads x N per call)",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": t_kernel * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": B, "n_q_heads": Hq, "n_kv_heads": cfg.n_kv_heads,
+                   "head_dim": d, "n_ctx": N, "dense_heads": Hq - kinds.count(workloads.HEAD_LOCAL),
+                   "sinks": cfg.sinks, "window": cfg.window},
+        "all_dense_ms": t_dense * 1e3, "speedup_vs_all_dense": t_dense / t_kernel,
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel<true>", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic_record("prefill_kernel<true>", cfg.name, sha),
+                     "flops_per_launch": flops, "launch_us": t_kernel * 1e6, "source_sha": sha},
+    }
+    if cpu and not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill_heads(cfg, t, args.cpu_seconds, torch)
+    del t
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline_prefill_heads(cfg, t, budget_s, torch):
+    """The fp64 oracle on query rows of the first dense head and the first
+    local head, alternating, at positions spread over the sequence (a stride
+    of 97 from the end), until ``budget_s`` is spent; the rate is scaled to
+    the whole call's rows."""
+    import numpy as np
+    import oracle
+    kinds = cfg.head_kind()
+    hd = next(h for h, k in enumerate(kinds) if k != 0)      # a dense head
+    hl = kinds.index(0)                                      # a local head
+    G = cfg.gqa
+    side = {h: (t["q"][0, h].to("cpu", torch.float64).numpy(),
+                t["k_cache"][0, h // G, :cfg.n_ctx].to("cpu", torch.float64).numpy(),
+                t["v_cache"][0, h // G, :cfg.n_ctx].to("cpu", torch.float64).numpy())
+            for h in {hd, hl}}
+    t0 = time.perf_counter()
+    done = {hd: 0, hl: 0}
+    spent_by = {hd: 0.0, hl: 0.0}
+    k = 0
+    while time.perf_counter() - t0 < budget_s or min(done.values()) == 0:
+        h = hd if k % 2 == 0 else hl
+        Q, K, V = side[h]
+        i = cfg.n_ctx - 1 - (k // 2) * 97 % cfg.n_ctx
+        s0 = time.perf_counter()
+        oracle.head_prefill_rows(Q, K, V, kinds[h], cfg.sinks, cfg.window, np.array([i]))
+        spent_by[h] += time.perf_counter() - s0
+        done[h] += 1
+        k += 1
+    spent = time.perf_counter() - t0
+    # seconds per row of each kind, weighted by the call's rows of each kind
+    n_loc = kinds.count(0)
+    per_row = (spent_by[hd] / done[hd]) * (len(kinds) - n_loc) + (spent_by[hl] / done[hl]) * n_loc
+    return {"value": len(kinds) / per_row, "unit": "tokens/s (B x heads x N)",
+            "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{done[hd]} query rows of dense head {hd} and {done[hl]} of local head "
+                      f"{hl} of {cfg.name} (positions a stride of 97 apart from the end), fp64 "
+                      f"numpy, {spent:.1f} s; per-row times weighted by the call's heads"}
 
 
 def cpu_baseline_prefill(cfg, t, budget_s, torch):

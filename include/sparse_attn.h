@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_VERSION 2
+#define SPARSE_ATTN_VERSION 3
 
 /* Size of the static device scratch array behind sparse_attn_decode_noalloc
  * (one per GPU the library runs on, held until the process ends). */
@@ -129,7 +129,22 @@ typedef struct sa_params {
   int32_t factor;       /* pyramid: p >= 2                                     */
   int32_t q_block;      /* pyramid: queries per block; % p^(L-1) == 0          */
   int32_t block_top_k;  /* pyramid: K entries per block                        */
+  int32_t per_head_sets;/* 0: one set per KV group, shared by its G query heads;
+                         * 1: one set per query head (see below)               */
 } sa_params;
+
+/*
+ * Per-query-head sets (per_head_sets = 1; the "Full Attention Strikes Back"
+ * summary speaks of per-head sparse attention, read here as every query head
+ * selecting for itself).  SA_SEL_TOPP / SA_SEL_TOPK and SA_SEL_ROUTE2 then
+ * treat each query head as a group of one: a retrieval head ranks tokens with
+ * its own q_idx row, a routed head routes with its own query, against the
+ * index keys or summaries of its KV group h / G.  sel_idx is [B,Hq,n_cap] and
+ * sel_count [B,Hq], and sparse_attn_decode reads them per query head (the
+ * heads of a KV group then share no gathered rows).  Labels must still be
+ * equal inside a GQA group, and n_q_heads <= 64.  The index build is the same
+ * in both modes.
+ */
 
 /* Device pointers owned by the caller; NULL where a call does not use them. */
 typedef struct sa_buffers {
@@ -149,7 +164,8 @@ typedef struct sa_buffers {
   void* pyr_v;
   float* pyr_scores;    /* [B,H,Nt] fp32, Nt = sum_{l>=0} N/p^l, level 0 first */
   int32_t* sel_idx;     /* [B,Hkv,n_cap] selected positions, ascending         */
-  int32_t* sel_count;   /* [B,Hkv] number of valid entries in sel_idx          */
+                        /* ([B,Hq,n_cap] with per_head_sets)                   */
+  int32_t* sel_count;   /* [B,Hkv] number of valid entries in sel_idx ([B,Hq]) */
   int32_t* blk_idx;     /* [B,H,ceil(N/q_block),K] flat entry ids per block    */
   int32_t* blk_count;   /* [B,H,ceil(N/q_block)]                               */
   float* out;           /* [B,Hq,d] decode | [B,H,N,d] prefill, fp32           */
@@ -225,7 +241,9 @@ int32_t sparse_attn_select(const sa_params* params, const sa_buffers* bufs,
  * [n_ctx - window, n_ctx) (a union); retrieval and routed groups see
  * sel_idx[b,g,0:sel_count[b,g]].  out[b,h,:] = sum_j pi_j v_j with
  * pi = softmax(q[b,h] . k_j / sqrt(d)) over that set, accumulated in fp32.
- * The GQA heads of a group share every gathered key/value row.  Reads q,
+ * The GQA heads of a group share every gathered key/value row.  With
+ * per_head_sets, head h sees sel_idx[b,h,0:sel_count[b,h]] (local heads as
+ * above) over the rows of KV group h / G.  Reads q,
  * k_cache, v_cache, sel_idx, sel_count; writes out.  A selecting group whose
  * sel_count is negative (a selection that reported failure) gets NaN in
  * every output of its query heads.  Needs a workspace; no part of it has to
@@ -269,6 +287,24 @@ int32_t sparse_attn_decode_noalloc(const sa_params* params, const sa_buffers* bu
 int32_t sparse_attn_prefill_chunked(const sa_params* params, const sa_buffers* bufs,
                                     void* workspace, size_t* workspace_bytes,
                                     void* hip_stream);
+
+/*
+ * sparse_attn_prefill_heads - head-split prefill forward ("Full Attention
+ * Strikes Back" summary, Methodology item 1 and Results: local heads window
+ * their prefill, retrieval heads keep the whole cache; AoH summary,
+ * Methodology item 4).  Every query position i = 0 .. n_ctx - 1 of query head
+ * h attends, with scale 1/sqrt(d), over the keys of KV group h / G that its
+ * label allows: a local head sees positions [0, sinks) and [i - window + 1,
+ * i] (a union, clipped to [0, i]) - what a decode query would see with a
+ * cache of i + 1 keys; a retrieval or routed head sees [0, i] (dense causal).
+ * q is [B,Hq,n_ctx,d] (post-RoPE), k_cache / v_cache [B,Hkv,n_cap,d] with
+ * keys 0 .. n_ctx - 1 filled, out [B,Hq,n_ctx,d] fp32.  Requires dtype bf16,
+ * head_dim 128, n_q_heads <= 128 and n_ctx < 2^23 (SA_ERR_UNSUPPORTED
+ * otherwise); sinks >= 0, window >= 0 and sinks + window >= 1 when some head
+ * is local.  No workspace; q_block and the selection fields are not used.
+ */
+int32_t sparse_attn_prefill_heads(const sa_params* params, const sa_buffers* bufs,
+                                  void* hip_stream);
 
 /* Human-readable name of a status code (static string). */
 const char* sparse_attn_status_string(int32_t status);

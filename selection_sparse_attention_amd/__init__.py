@@ -33,6 +33,7 @@ SEL_TOPP, SEL_TOPK, SEL_ROUTE2, SEL_PYRAMID_TOPK = 0, 1, 2, 3
 
 EXPORTED = ("sparse_attn_index_build", "sparse_attn_select", "sparse_attn_decode",
             "sparse_attn_decode_noalloc", "sparse_attn_prefill_chunked",
+            "sparse_attn_prefill_heads",
             "sparse_attn_status_string", "sparse_attn_version")
 
 
@@ -50,7 +51,7 @@ class Params(ctypes.Structure):
         ("top_groups", ctypes.c_int32), ("sink_chunks", ctypes.c_int32),
         ("local_chunks", ctypes.c_int32), ("levels", ctypes.c_int32),
         ("factor", ctypes.c_int32), ("q_block", ctypes.c_int32),
-        ("block_top_k", ctypes.c_int32),
+        ("block_top_k", ctypes.c_int32), ("per_head_sets", ctypes.c_int32),
     ]
 
 
@@ -81,6 +82,9 @@ for _name, _args in (
 _lib.sparse_attn_decode_noalloc.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(Buffers),
                                             ctypes.c_void_p]
 _lib.sparse_attn_decode_noalloc.restype = ctypes.c_int32
+_lib.sparse_attn_prefill_heads.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(Buffers),
+                                           ctypes.c_void_p]
+_lib.sparse_attn_prefill_heads.restype = ctypes.c_int32
 _lib.sparse_attn_status_string.argtypes = [ctypes.c_int32]
 _lib.sparse_attn_status_string.restype = ctypes.c_char_p
 _lib.sparse_attn_version.restype = ctypes.c_int32
@@ -104,7 +108,7 @@ def make_params(*, batch, n_q_heads, n_kv_heads, head_dim, n_ctx, n_cap=None, dt
                 head_kind=None, rope_base=10000.0, r=16, top_p=1.0, top_k=0, min_tokens=0,
                 sinks=0, window=0, chunk=64, group=16, top_chunks=16, top_groups=2,
                 sink_chunks=4, local_chunks=8, levels=1, factor=4, q_block=128,
-                block_top_k=0) -> Params:
+                block_top_k=0, per_head_sets=False) -> Params:
     """Fill a Params struct.  ``head_kind`` is a per-query-head sequence."""
     p = Params()
     p.batch, p.n_q_heads, p.n_kv_heads, p.head_dim = batch, n_q_heads, n_kv_heads, head_dim
@@ -120,6 +124,7 @@ def make_params(*, batch, n_q_heads, n_kv_heads, head_dim, n_ctx, n_cap=None, dt
     p.chunk, p.group, p.top_chunks, p.top_groups = chunk, group, top_chunks, top_groups
     p.sink_chunks, p.local_chunks = sink_chunks, local_chunks
     p.levels, p.factor, p.q_block, p.block_top_k = levels, factor, q_block, block_top_k
+    p.per_head_sets = int(per_head_sets)
     return p
 
 
@@ -269,6 +274,13 @@ def prefill_chunked(params: Params, bufs: Buffers, ws: Optional[Workspace] = Non
     _check(_lib.sparse_attn_prefill_chunked(ctypes.byref(params), ctypes.byref(bufs),
                                             w.data_ptr(), ctypes.byref(n), _stream(stream)),
            "prefill_chunked")
+
+
+def prefill_heads(params: Params, bufs: Buffers, stream=None):
+    """Head-split prefill: local heads over sinks + window, the others
+    dense causal (no workspace)."""
+    _check(_lib.sparse_attn_prefill_heads(ctypes.byref(params), ctypes.byref(bufs),
+                                          _stream(stream)), "prefill_heads")
 
 
 def raw_call(fn: str, params, bufs, *args):

@@ -61,6 +61,41 @@ GroupList groups_of_kind(const sa_params* p, const int8_t* kinds, int kind) {
   return gl;
 }
 
+// The units that select and attend together: the KV groups (their G query
+// heads share one set), or, with per-head sets, every query head alone (a
+// group of one head; kv_div of them per KV group).
+struct SelGroups {
+  int n;                        // units per sequence
+  int G;                        // query heads per unit
+  int kv_div;                   // units per KV group
+  int8_t kind[sa::kMaxGroups];  // label of each unit
+};
+
+int32_t sel_groups(const sa_params* p, SelGroups* u) {
+  int8_t kinds[sa::kMaxGroups];
+  int32_t st = group_kinds(p, kinds);
+  if (st) return st;
+  const int G = p->n_q_heads / p->n_kv_heads;
+  if (p->per_head_sets != 0 && p->per_head_sets != 1) return SA_ERR_INVALID_ARG;
+  if (!p->per_head_sets) {
+    u->n = p->n_kv_heads; u->G = G; u->kv_div = 1;
+    for (int g = 0; g < p->n_kv_heads; ++g) u->kind[g] = kinds[g];
+    return SA_OK;
+  }
+  if (p->n_q_heads > sa::kMaxGroups) return SA_ERR_UNSUPPORTED;
+  u->n = p->n_q_heads; u->G = 1; u->kv_div = G;
+  for (int h = 0; h < p->n_q_heads; ++h) u->kind[h] = kinds[h / G];
+  return SA_OK;
+}
+
+GroupList units_of_kind(const SelGroups& u, int kind) {
+  GroupList gl{};
+  gl.n = 0;
+  for (int g = 0; g < u.n; ++g)
+    if (u.kind[g] == kind) gl.ids[gl.n++] = g;
+  return gl;
+}
+
 // Checks shared by every entry point.
 int32_t check_common(const sa_params* p, const sa_buffers* b) {
   if (!p || !b) return SA_ERR_INVALID_ARG;
@@ -162,9 +197,10 @@ int compute_units() {
   return n;
 }
 
-int decode_max_count(const sa_params* p, const int8_t* kinds) {
+int decode_max_count(const sa_params* p, const SelGroups& u) {
+  const int8_t* kinds = u.kind;
   int mc = 0;
-  for (int g = 0; g < p->n_kv_heads; ++g) {
+  for (int g = 0; g < u.n; ++g) {
     int c;
     if (kinds[g] == SA_HEAD_LOCAL) {
       const int64_t sw = (int64_t)p->sinks + p->window;
@@ -187,14 +223,14 @@ int32_t decode_entry(const sa_params* p, const sa_buffers* b, void* ws, size_t* 
                      void* stream) {
   int32_t st = check_common(p, b);
   if (st) return st;
-  int8_t kinds[sa::kMaxGroups];
-  if ((st = group_kinds(p, kinds))) return st;
-  const int G = p->n_q_heads / p->n_kv_heads;
+  SelGroups u;
+  if ((st = sel_groups(p, &u))) return st;
+  const int G = u.G;
   if (G != 1 && G != 2 && G != 4 && G != 8) return SA_ERR_UNSUPPORTED;
   bool any_local = false, any_list = false;
   uint64_t local_mask = 0;
-  for (int g = 0; g < p->n_kv_heads; ++g) {
-    if (kinds[g] == SA_HEAD_LOCAL) { any_local = true; local_mask |= 1ull << g; }
+  for (int g = 0; g < u.n; ++g) {
+    if (u.kind[g] == SA_HEAD_LOCAL) { any_local = true; local_mask |= 1ull << g; }
     else any_list = true;
   }
   if (any_local && (p->sinks < 0 || p->window < 0 || (int64_t)p->sinks + p->window < 1))
@@ -206,20 +242,20 @@ int32_t decode_entry(const sa_params* p, const sa_buffers* b, void* ws, size_t* 
     // workgroup slot (two per compute unit, one for 8-head groups, whose
     // workgroups use a whole unit's registers); the plan itself is made on
     // the device
-    const int groups = p->batch * p->n_kv_heads;
+    const int groups = p->batch * u.n;
     target_items = (G > 4 ? 1 : 2) * compute_units();
     max_splits = target_items + groups;        // bound on the item count
     if (max_splits > kMaxDecodeItems) return SA_ERR_UNSUPPORTED;
     n_partial = (size_t)max_splits * G * (p->head_dim + 2);
   } else {
-    const int max_count = decode_max_count(p, kinds);
+    const int max_count = decode_max_count(p, u);
     max_splits = (max_count + tps - 1) / tps;
     if (max_splits > kMaxDecodeSplits) return SA_ERR_UNSUPPORTED;
     n_partial = (size_t)p->batch * p->n_q_heads * max_splits * (p->head_dim + 2);
   }
   Carver c(ws);
   float* partial = c.take<float>(n_partial);
-  int2* plan = (p->dtype == SA_BF16) ? c.take<int2>((size_t)p->batch * p->n_kv_heads) : nullptr;
+  int2* plan = (p->dtype == SA_BF16) ? c.take<int2>((size_t)p->batch * u.n) : nullptr;
   if ((st = workspace_gate(ws, ws_bytes, c.size()))) return st < 0 ? st : SA_OK;
   if (!b->q || !b->k_cache || !b->v_cache || !b->out) return SA_ERR_INVALID_ARG;
   if (any_list && (!b->sel_idx || !b->sel_count)) return SA_ERR_INVALID_ARG;
@@ -227,8 +263,9 @@ int32_t decode_entry(const sa_params* p, const sa_buffers* b, void* ws, size_t* 
   sa::DecodeArgs a{};
   a.q = b->q; a.k = b->k_cache; a.v = b->v_cache; a.sel_idx = b->sel_idx; a.sel_count = b->sel_count;
   a.out = b->out; a.partial = partial;
-  a.B = p->batch; a.Hq = p->n_q_heads; a.Hkv = p->n_kv_heads; a.n = p->n_ctx; a.n_cap = p->n_cap;
-  a.G = G; a.sinks = p->sinks; a.window = p->window; a.tps = tps; a.max_splits = max_splits;
+  a.B = p->batch; a.Hq = p->n_q_heads; a.Hkv = u.n; a.n = p->n_ctx; a.n_cap = p->n_cap;
+  a.G = G; a.kv_div = u.kv_div;
+  a.sinks = p->sinks; a.window = p->window; a.tps = tps; a.max_splits = max_splits;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->head_dim));
   a.local_mask = local_mask;
   a.target_items = target_items;
@@ -326,7 +363,6 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
   int32_t st = check_common(p, b);
   if (st) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int G = p->n_q_heads / p->n_kv_heads;
   if (mode == SA_SEL_PYRAMID_TOPK) {
     PyrGeom pg;
     if ((st = pyramid_geom(p, &pg))) return st;
@@ -366,14 +402,14 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
     }
     return hip_status(sa::launch_pyramid_select(a, s));
   }
-  int8_t kinds[sa::kMaxGroups];
-  if ((st = group_kinds(p, kinds))) return st;
+  SelGroups u;
+  if ((st = sel_groups(p, &u))) return st;
   if (mode == SA_SEL_TOPP || mode == SA_SEL_TOPK) {
     if (p->r != 16) return SA_ERR_UNSUPPORTED;
     if (mode == SA_SEL_TOPP && (!(p->top_p > 0.f) || std::isnan(p->top_p) || p->min_tokens < 0))
       return SA_ERR_INVALID_ARG;
     if (mode == SA_SEL_TOPK && p->top_k < 1) return SA_ERR_INVALID_ARG;
-    GroupList gl = groups_of_kind(p, kinds, SA_HEAD_RETRIEVAL);
+    GroupList gl = units_of_kind(u, SA_HEAD_RETRIEVAL);
     const int rows = p->batch * gl.n;
     // tokens per workgroup: 2048 (8 per thread), or a larger tile while the
     // rows would need more than two workgroups per compute unit (measured:
@@ -399,8 +435,8 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
     sw = carve_select(ws, rows, cand_stride);
     sa::SelectArgs a{};
     a.q_idx = b->q_idx; a.k_idx = b->k_idx; a.sel_idx = b->sel_idx; a.sel_count = b->sel_count;
-    a.B = p->batch; a.Hq = p->n_q_heads; a.Hkv = p->n_kv_heads; a.n = p->n_ctx; a.n_cap = p->n_cap;
-    a.G = G;
+    a.B = p->batch; a.Hq = p->n_q_heads; a.Hkv = u.n; a.n = p->n_ctx; a.n_cap = p->n_cap;
+    a.G = u.G; a.kv_div = u.kv_div;
     if (mass) {
       a.use_mass = 1;
       a.top_p = p->top_p;
@@ -426,7 +462,7 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
     if (p->top_chunks > 64 || gpc > 64 || p->top_chunks * p->top_groups > 4096)
       return SA_ERR_UNSUPPORTED;
     if (p->n_ctx / p->chunk > 16384) return SA_ERR_UNSUPPORTED;
-    GroupList gl = groups_of_kind(p, kinds, SA_HEAD_ROUTED);
+    GroupList gl = units_of_kind(u, SA_HEAD_ROUTED);
     Carver c(ws);
     c.take<uint32_t>(1);
     if ((st = workspace_gate(ws, ws_bytes, c.size()))) return st < 0 ? st : SA_OK;
@@ -441,8 +477,8 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
     sa::RouteArgs a{};
     a.q = b->q; a.chunk_sum = b->chunk_sum; a.group_sum = b->group_sum;
     a.sel_idx = b->sel_idx; a.sel_count = b->sel_count;
-    a.B = p->batch; a.Hq = p->n_q_heads; a.Hkv = p->n_kv_heads; a.n = p->n_ctx; a.n_cap = p->n_cap;
-    a.G = G; a.chunk = p->chunk; a.group = p->group; a.top_chunks = p->top_chunks;
+    a.B = p->batch; a.Hq = p->n_q_heads; a.Hkv = u.n; a.n = p->n_ctx; a.n_cap = p->n_cap;
+    a.G = u.G; a.kv_div = u.kv_div; a.chunk = p->chunk; a.group = p->group; a.top_chunks = p->top_chunks;
     a.top_groups = p->top_groups; a.sink_chunks = p->sink_chunks; a.local_chunks = p->local_chunks;
     a.n_cs_cap = p->n_cap / p->chunk; a.n_gs_cap = p->n_cap / p->group;
     a.groups = gl;
@@ -480,6 +516,38 @@ int32_t sparse_attn_prefill_chunked(const sa_params* p, const sa_buffers* b, voi
   a.K = p->block_top_k; a.q_block = p->q_block;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->head_dim));
   return hip_status(sa::launch_prefill(a, p->head_dim, static_cast<hipStream_t>(stream)));
+}
+
+int32_t sparse_attn_prefill_heads(const sa_params* p, const sa_buffers* b, void* stream) {
+  int32_t st = check_common(p, b);
+  if (st) return st;
+  int8_t kinds[sa::kMaxGroups];
+  if ((st = group_kinds(p, kinds))) return st;
+  if (p->dtype != SA_BF16 || p->head_dim != 128) return SA_ERR_UNSUPPORTED;
+  if (p->n_q_heads > sa::kMaxPrefillHeads) return SA_ERR_UNSUPPORTED;
+  if (p->n_ctx >= (1 << 23)) return SA_ERR_UNSUPPORTED;   // rows are addressed as 32-bit byte offsets
+  const int G = p->n_q_heads / p->n_kv_heads;
+  sa::PrefillArgs a{};
+  for (int h = 0; h < p->n_q_heads; ++h) {
+    const int c = kinds[h / G] == SA_HEAD_LOCAL ? 1 : 0;
+    a.cls_heads[c][a.n_cls[c]++] = (uint8_t)h;
+  }
+  if (a.n_cls[1] > 0 && (p->sinks < 0 || p->window < 0 || (int64_t)p->sinks + p->window < 1))
+    return SA_ERR_INVALID_ARG;
+  if (!b->q || !b->k_cache || !b->v_cache || !b->out) return SA_ERR_INVALID_ARG;
+  if (!aligned16(b->q) || !aligned16(b->k_cache) || !aligned16(b->v_cache) || !aligned16(b->out))
+    return SA_ERR_INVALID_ARG;
+  a.q = b->q; a.k = b->k_cache; a.v = b->v_cache; a.pk = b->k_cache; a.pv = b->v_cache;
+  a.out = b->out;
+  a.B = p->batch; a.H = p->n_q_heads; a.N = p->n_ctx; a.Nc = 0;
+  a.q_block = 128;                       // queries per workgroup
+  a.nblk = (p->n_ctx + a.q_block - 1) / a.q_block;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->head_dim));
+  a.Hkv = p->n_kv_heads; a.G = G; a.kv_stride = p->n_cap;
+  a.sinks = a.n_cls[1] > 0 ? p->sinks : 0;
+  a.window = a.n_cls[1] > 0 ? p->window : 0;
+  a.units0 = 8 * ((a.B * a.n_cls[0] + 7) / 8) * a.nblk;
+  return hip_status(sa::launch_prefill_heads(a, p->head_dim, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

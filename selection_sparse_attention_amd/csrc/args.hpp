@@ -69,6 +69,7 @@ struct SelectArgs {
   double top_p;
   int32_t target_count;  // top-k: k ; top-p: min_tokens (0 = none)
   int32_t W;             // workgroups per row
+  int32_t kv_div;        // rows per KV group of k_idx (G with per-head sets, else 1)
   int32_t spin_limit;    // polls per cross-workgroup wait (< 0: every wait fails)
   // workspace; everything but `cand` is zero between calls
   uint32_t* hist_c;      // [rows, 3, 4096] counts of the three global digits
@@ -89,6 +90,7 @@ struct RouteArgs {
   int32_t B, Hq, Hkv, n, n_cap, G, chunk, group, top_chunks, top_groups,
       sink_chunks, local_chunks;
   int32_t n_cs_cap, n_gs_cap;   // rows per (b,g) in chunk_sum / group_sum
+  int32_t kv_div;               // selection rows per KV group (G with per-head sets, else 1)
   float* scratch;               // [rows, n_cs_cap] chunk scores
   GroupList groups;
 };
@@ -120,7 +122,10 @@ struct DecodeArgs {
   const int32_t* sel_count;
   float* out;             // [B,Hq,d]
   float* partial;         // [B,Hq,max_splits,d+2]
+  // Hkv / G count selection groups: KV groups, or single query heads with
+  // per-head sets (Hkv = Hq, G = 1); K/V rows belong to group index / kv_div
   int32_t B, Hq, Hkv, n, n_cap, G, sinks, window;
+  int32_t kv_div;
   int32_t tps;            // tokens per split (fp32 path)
   int32_t max_splits;     // fp32 path: splits per group; bf16 path: work items
   float scale_log2;       // log2(e) / sqrt(d)
@@ -130,13 +135,22 @@ struct DecodeArgs {
   int2* plan;             // bf16 path: per group (first item, item count) [B*Hkv]
 };
 
+constexpr int kMaxPrefillHeads = 128;
+
 struct PrefillArgs {
-  const void* q; const void* k; const void* v;   // [B,H,N,d]
+  const void* q; const void* k; const void* v;   // q [B,H,N,d]; k, v [B,Hkv,kv_stride,d]
   const void* pk; const void* pv;                // [B,H,Nc,d]
   const int32_t* blk_idx; const int32_t* blk_count;
   float* out;                                    // [B,H,N,d]
   int32_t B, H, N, Nc, nblk, K, q_block;
   float scale_log2;
+  // head-split mode: the visible keys follow from each head's class - class
+  // 0 dense causal, class 1 sinks + sliding window; query head h reads KV
+  // head h / G
+  int32_t Hkv, G, kv_stride, sinks, window;
+  int32_t n_cls[2];                              // heads in each class
+  int32_t units0;                                // workgroups of class 0
+  uint8_t cls_heads[2][kMaxPrefillHeads];        // the heads of each class
 };
 
 // ---------------------------------------------------------------- launchers
@@ -149,5 +163,6 @@ hipError_t launch_pyramid_select(const PyrSelectArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int d, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int d, hipStream_t s);
+hipError_t launch_prefill_heads(const PrefillArgs& a, int d, hipStream_t s);
 
 }  // namespace sa

@@ -66,6 +66,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a)
   }
   const int64_t row0 = ((int64_t)b * a.Hkv + g) * a.n_cap;
   const int32_t* list = a.sel_idx + row0;
+  const int64_t kv0 = (((int64_t)b * a.Hkv + g) / a.kv_div) * a.n_cap;
   const float sc = a.scale_log2;
 
   for (int base = start; base < end; base += 16 * U) {
@@ -79,8 +80,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeArgs a)
       if (valid[u]) tok = local ? (i < s_eff ? i : ws + (i - s_eff)) : list[i];
       valid[u] = valid[u] && (unsigned)tok < (unsigned)n;   // ignore malformed entries
       if (valid[u]) {
-        VecLoad<T, EPL>::run(a.k, (row0 + tok) * D + sub * EPL, kk[u]);
-        VecLoad<T, EPL>::run(a.v, (row0 + tok) * D + sub * EPL, vv[u]);
+        VecLoad<T, EPL>::run(a.k, (kv0 + tok) * D + sub * EPL, kk[u]);
+        VecLoad<T, EPL>::run(a.v, (kv0 + tok) * D + sub * EPL, vv[u]);
       } else {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) { kk[u][e] = 0.f; vv[u][e] = 0.f; }

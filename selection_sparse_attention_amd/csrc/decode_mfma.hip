@@ -207,7 +207,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, DecodeShared<D,
   } else {
     count = min(max(a.sel_count[bg], 0), n);
   }
-  const int64_t row0 = (int64_t)bg * a.n_cap;
+  const int64_t row0 = (int64_t)bg * a.n_cap;          // the group's list
+  const int64_t kv0 = (int64_t)(bg / a.kv_div) * a.n_cap;   // its K/V rows
 
   // query fragment: head (lane % 16), this lane's slice of the k mapping
   bf16x8 qf[KS];
@@ -233,9 +234,9 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, DecodeShared<D,
 
   const int kt = lane & 15, jg = lane >> 4;            // K role
   const int vd = 2 * (lane % (D / 2)), vc = lane / (D / 2);   // V role
-  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + row0 * D + 8 * jg;
+  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + kv0 * D + 8 * jg;
   // V rows: a wave-uniform row address (scalar) plus this lane's dims
-  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v) + row0 * D;
+  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v) + kv0 * D;
 
   // raw list entry of this lane's token in a tile (a load for listed groups,
   // in bounds even past the end; checked when it is used)

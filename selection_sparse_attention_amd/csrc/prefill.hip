@@ -97,33 +97,82 @@ __device__ __forceinline__ float max_over_lane_groups(float v) {
   return max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// HEADS = false: pyramid selection (each block's entry list from blk_idx,
+// then the block's own keys).  HEADS = true: head-split prefill, no list:
+// a block's key sequence is implicit - positions [0, A) (the sinks, A =
+// min(sinks, end of block)) then [lo, end of block) (the window reaching
+// back from the block's first query; everything for dense heads) - and each
+// (query i, key j) pair is kept iff j <= i and (j < sinks or j > i - window).
+template <bool HEADS>
 __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kKT * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kD * kVRow];
-  __shared__ __attribute__((aligned(16))) uint32_t s_seq[kSeqMax];
+  __shared__ __attribute__((aligned(16))) uint32_t s_seq[HEADS ? 4 : kSeqMax];
 
-  // ---- which (head, block): die-major, two heads per die, heavy first
-  const int nh = a.B * a.H;
-  const int hpx = (nh + 7) / 8;
-  const int L = blockIdx.x;
-  const int xcd = L % 8, slot = L / 8;
-  const int bh = xcd + 8 * (slot % hpx);
-  const int blk = a.nblk - 1 - slot / hpx;
-  if (bh >= nh || blk < 0) return;
+  int bh, kvh, blk;
+  int S = 0, W = 0;                      // head-split: sinks and window of the head's class
+  if constexpr (HEADS) {
+    // ---- which (class, head, block): class 0 (the heavy dense heads) first;
+    //      within a class die-major with a die's heads contiguous (the query
+    //      heads of one KV head share a die's L2), heavy blocks first
+    int L = blockIdx.x, cls = 0;
+    if (L >= a.units0) { L -= a.units0; cls = 1; }
+    const int nc = a.n_cls[cls];
+    const int nbh = a.B * nc;
+    const int hpx = (nbh + 7) / 8;
+    const int xcd = L % 8, slot = L / 8;
+    const int bi = xcd * hpx + slot % hpx;
+    blk = a.nblk - 1 - slot / hpx;
+    if (bi >= nbh || blk < 0) return;
+    const int b = bi / nc, h = a.cls_heads[cls][bi - b * nc];
+    bh = b * a.H + h;
+    kvh = b * a.Hkv + h / a.G;
+    if (cls == 0) { S = 0; W = a.N + 1; } else { S = a.sinks; W = a.window; }
+  } else {
+    // ---- which (head, block): die-major, two heads per die, heavy first
+    const int nh = a.B * a.H;
+    const int hpx = (nh + 7) / 8;
+    const int L = blockIdx.x;
+    const int xcd = L % 8, slot = L / 8;
+    bh = xcd + 8 * (slot % hpx);
+    blk = a.nblk - 1 - slot / hpx;
+    if (bh >= nh || blk < 0) return;
+    kvh = bh;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int l16 = lane & 15, jg = lane >> 4;
   const int q0 = blk * a.q_block;
   const int nq = min(a.q_block, a.N - q0);
-  const int c_sel = min(max(a.blk_count[(int64_t)bh * a.nblk + blk], 0), min(a.K, kListMax));
-  const int32_t* list = a.blk_idx + ((int64_t)bh * a.nblk + blk) * a.K;
-  const int T = c_sel + nq;
+  const int q1 = q0 + nq;
+  int c_sel, T;
+  int A = 0, lo = 0;                     // head-split: sink entries, first window position
+  const int32_t* list = nullptr;
+  if constexpr (HEADS) {
+    A = min(S, q1);
+    lo = (W > 0) ? max(A, q0 - W + 1) : q1;
+    T = A + (q1 - lo);
+    c_sel = 0;
+  } else {
+    c_sel = min(max(a.blk_count[(int64_t)bh * a.nblk + blk], 0), min(a.K, kListMax));
+    list = a.blk_idx + ((int64_t)bh * a.nblk + blk) * a.K;
+    T = c_sel + nq;
+  }
   const int ntiles = (T + kKT - 1) / kKT;
+  const int64_t kv_rows = HEADS ? (int64_t)a.kv_stride : (int64_t)a.N;
   const uint16_t* qb = reinterpret_cast<const uint16_t*>(a.q) + (int64_t)bh * a.N * kD;
-  const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k) + (int64_t)bh * a.N * kD;
-  const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.v) + (int64_t)bh * a.N * kD;
-  const uint16_t* pkb = reinterpret_cast<const uint16_t*>(a.pk) + (int64_t)bh * a.Nc * kD;
-  const uint16_t* pvb = reinterpret_cast<const uint16_t*>(a.pv) + (int64_t)bh * a.Nc * kD;
+  const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k) + (int64_t)kvh * kv_rows * kD;
+  const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.v) + (int64_t)kvh * kv_rows * kD;
+  const uint16_t* pkb = HEADS ? kb : reinterpret_cast<const uint16_t*>(a.pk) + (int64_t)bh * a.Nc * kD;
+  const uint16_t* pvb = HEADS ? vb : reinterpret_cast<const uint16_t*>(a.pv) + (int64_t)bh * a.Nc * kD;
+  // head-split: position of sequence entry e (e < T)
+  auto pos = [&](int e) __attribute__((always_inline)) -> int { return e < A ? e : lo + (e - A); };
+  // the row byte offset of sequence entry e: staged in LDS, or (head-split)
+  // computed; past the end, row 0
+  auto seq = [&](int e) __attribute__((always_inline)) -> uint32_t {
+    if constexpr (HEADS) return (e < T) ? (uint32_t)pos(e) * kRowBytes : 0u;
+    else return s_seq[e];
+  };
 
   // ---- query fragments (B operand of S^T = K Q^T): query 32w + 16nt + l16,
   //      dims 32 jg + 8 s .. +8
@@ -146,7 +195,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   //      out of the softmax).  A flat id outside the pyramid is clamped to
   //      level-0 row 0 - never dereferenced out of bounds; its contribution
   //      is unspecified.
-  {
+  if constexpr (!HEADS) {
     const int n_stage = (ntiles + 4) * kKT;
     for (int e = tid; e < n_stage; e += kPfThreads) {
       uint32_t r = 0u;
@@ -183,8 +232,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   struct Rows { u32x4p k0, k1, v0, v1; };
   // issue set x (unconditionally: past the end the rows are row 0, never used)
   auto gather = [&](int x, Rows& r) __attribute__((always_inline)) {
-    const uint32_t lk = s_seq[(x + 2) * kKT + gk_key];
-    const uint2 lv = *reinterpret_cast<const uint2*>(&s_seq[x * kKT + 2 * gv_kp]);
+    const uint32_t lk = seq((x + 2) * kKT + gk_key);
+    uint2 lv;
+    if constexpr (HEADS) lv = make_uint2(seq(x * kKT + 2 * gv_kp), seq(x * kKT + 2 * gv_kp + 1));
+    else lv = *reinterpret_cast<const uint2*>(&s_seq[x * kKT + 2 * gv_kp]);
     const u32x4p* pk = row_ptr(lk, k_seg, pk_seg);
     r.k0 = pk[0];
     r.k1 = pk[8];
@@ -275,7 +326,13 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int e = e0 + 16 * mt + 4 * jg + i;
-            const bool ok = (e < c_sel) || (e < T && (e - c_sel) <= ql);
+            bool ok;
+            if constexpr (HEADS) {
+              const int j = pos(e), qi = q0 + ql;
+              ok = e < T && j <= qi && (j < S || j > qi - W);
+            } else {
+              ok = (e < c_sel) || (e < T && (e - c_sel) <= ql);
+            }
             s[mt][nt][i] = ok ? s[mt][nt][i] : -INFINITY;
           }
       }
@@ -372,8 +429,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   // K, of tile 2, over tile 0's once every wave has read those)
   lds_barrier();                                    // s_seq complete
   {
-    const u32x4p* pk0 = row_ptr(s_seq[gk_key], k_seg, pk_seg);
-    const u32x4p* pk1 = row_ptr(s_seq[kKT + gk_key], k_seg, pk_seg);
+    const u32x4p* pk0 = row_ptr(seq(gk_key), k_seg, pk_seg);
+    const u32x4p* pk1 = row_ptr(seq(kKT + gk_key), k_seg, pk_seg);
     stash_k(0, pk0[0], pk0[8]);
     stash_k(1, pk1[0], pk1[8]);
   }
@@ -395,15 +452,35 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   // passes both bodies of a pair, so the loads in flight there are always
   // set 1's.  Tiles from tile c_sel / 32 on reach past the selection: the
   // steps that turn them into probabilities take the masked form.
-  const int mask_from = c_sel / kKT;
   int tile = 0;
-  for (; tile + 2 < mask_from; tile += 2) {
-    body(unmasked, tile, ra, rb, sb_, sa_, pa, pb);
-    body(unmasked, tile + 1, rb, ra, sa_, sb_, pb, pa);
-  }
-  for (; tile + 1 < ntiles; tile += 2) {
-    body(masked, tile, ra, rb, sb_, sa_, pa, pb);
-    body(masked, tile + 1, rb, ra, sa_, sb_, pb, pa);
+  if constexpr (HEADS) {
+    // a tile needs the mask unless all of its entries are in the sequence,
+    // at or before the block's first query, and each a sink or inside the
+    // window of the block's last query (entries ascend in position)
+    auto needs_mask = [&](int t) __attribute__((always_inline)) -> bool {
+      const int e0 = t * kKT, e1 = e0 + kKT;
+      if (e1 > T || pos(e1 - 1) > q0) return true;
+      return e1 > A && lo + (max(e0, A) - A) <= q1 - 1 - W;
+    };
+    for (; tile + 1 < ntiles; tile += 2) {
+      if (needs_mask(tile + 1) || needs_mask(tile + 2)) {
+        body(masked, tile, ra, rb, sb_, sa_, pa, pb);
+        body(masked, tile + 1, rb, ra, sa_, sb_, pb, pa);
+      } else {
+        body(unmasked, tile, ra, rb, sb_, sa_, pa, pb);
+        body(unmasked, tile + 1, rb, ra, sa_, sb_, pb, pa);
+      }
+    }
+  } else {
+    const int mask_from = c_sel / kKT;
+    for (; tile + 2 < mask_from; tile += 2) {
+      body(unmasked, tile, ra, rb, sb_, sa_, pa, pb);
+      body(unmasked, tile + 1, rb, ra, sa_, sb_, pb, pa);
+    }
+    for (; tile + 1 < ntiles; tile += 2) {
+      body(masked, tile, ra, rb, sb_, sa_, pa, pb);
+      body(masked, tile + 1, rb, ra, sa_, sb_, pb, pa);
+    }
   }
   if (tile < ntiles) body(masked, tile, ra, rb, sb_, sa_, pa, pb);
   rescale(alpha);
@@ -435,7 +512,24 @@ hipError_t launch_prefill(const PrefillArgs& a, int d, hipStream_t s) {
   const int nh = a.B * a.H;
   const int hpx = (nh + 7) / 8;
   dim3 grid(8 * hpx * a.nblk);
-  hipLaunchKernelGGL(prefill_kernel, grid, dim3(kPfThreads), 0, s, a);
+  hipLaunchKernelGGL(prefill_kernel<false>, grid, dim3(kPfThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_heads(const PrefillArgs& a, int d, hipStream_t s) {
+  if (d != kD || a.q_block != 128 || a.G < 1 || a.H != a.Hkv * a.G) return hipErrorInvalidValue;
+  if (a.N >= kMaxRows || a.kv_stride < a.N) return hipErrorInvalidValue;
+  int units = 0;
+  for (int c = 0; c < 2; ++c) {
+    if (a.n_cls[c] < 0 || a.n_cls[c] > kMaxPrefillHeads) return hipErrorInvalidValue;
+    for (int i = 0; i < a.n_cls[c]; ++i)
+      if (a.cls_heads[c][i] >= a.H) return hipErrorInvalidValue;
+    const int u = 8 * ((a.B * a.n_cls[c] + 7) / 8) * a.nblk;
+    if (c == 0 && u != a.units0) return hipErrorInvalidValue;
+    units += u;
+  }
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL(prefill_kernel<true>, dim3(units), dim3(kPfThreads), 0, s, a);
   return hipGetLastError();
 }
 

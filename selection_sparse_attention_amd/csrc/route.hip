@@ -150,8 +150,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   }
 
   const int64_t bg = (int64_t)b * a.Hkv + g;
+  const int64_t kvg = bg / a.kv_div;        // the summaries' KV group
   if (nT > 0) {
-    score_rows<T, D>(a.chunk_sum, bg * a.n_cs_cap + c_lo, ncand, qv, dyn, nullptr);
+    score_rows<T, D>(a.chunk_sum, kvg * a.n_cs_cap + c_lo, ncand, qv, dyn, nullptr);
     __syncthreads();
     if (nT <= 16 && ncand <= kRouteThreads) {
       // level 1 with at most one candidate per thread: every wave sorts its
@@ -218,7 +219,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     __syncthreads();
     // level 2: score every group of every chosen chunk
     for (int i = tid; i < nT * gpc; i += kRouteThreads)
-      s_rowmap[i] = (int)(bg * a.n_gs_cap + (int64_t)s_sorted[i / gpc] * gpc + (i % gpc));
+      s_rowmap[i] = (int)(kvg * a.n_gs_cap + (int64_t)s_sorted[i / gpc] * gpc + (i % gpc));
     __syncthreads();
     score_rows<T, D>(a.group_sum, 0, nT * gpc, qv, dyn, s_rowmap);
     __syncthreads();

@@ -473,7 +473,7 @@ __global__ __launch_bounds__(kThreads) void select_fused_kernel(SelectArgs a) {
     float qb[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) qb[c] = 0.f;
-    const int64_t krow = ((int64_t)b * a.Hkv + g) * a.n_cap;
+    const int64_t krow = (((int64_t)b * a.Hkv + g) / a.kv_div) * a.n_cap;
     constexpr int BATCH = PER < 8 ? PER : 8;
 #pragma unroll
     for (int i0 = 0; i0 < PER; i0 += BATCH) {

@@ -31,8 +31,9 @@ def to_dev(x, dtype):
 class DecodeRun:
     """Device buffers of one decode step and the calls that fill them."""
 
-    def __init__(self, cfg, inp, n_cap=None):
+    def __init__(self, cfg, inp, n_cap=None, per_head=False):
         self.cfg = cfg
+        self.per_head = per_head
         B, Hq, Hkv, d, n = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_ctx
         cap = inp.get("n_cap", n) if n_cap is None else n_cap
         self.n_cap = cap
@@ -49,13 +50,15 @@ class DecodeRun:
             self.t["proj"] = inp["proj"].to(DEV, torch.float32).contiguous()
         self.t["k_idx"] = torch.zeros(B, Hkv, cap, cfg.r, dtype=dt, device=DEV)
         self.t["q_idx"] = torch.zeros(B, Hq, cfg.r, dtype=torch.float32, device=DEV)
-        self.t["sel_idx"] = torch.full((B, Hkv, cap), -1, dtype=torch.int32, device=DEV)
-        self.t["sel_count"] = torch.full((B, Hkv), -1, dtype=torch.int32, device=DEV)
+        ns = Hq if per_head else Hkv               # selection rows per sequence
+        self.t["sel_idx"] = torch.full((B, ns, cap), -1, dtype=torch.int32, device=DEV)
+        self.t["sel_count"] = torch.full((B, ns), -1, dtype=torch.int32, device=DEV)
         self.t["out"] = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device=DEV)
         if cfg.routed:
             self.t["chunk_sum"] = torch.zeros(B, Hkv, cap // cfg.chunk, d, dtype=dt, device=DEV)
             self.t["group_sum"] = torch.zeros(B, Hkv, cap // cfg.group, d, dtype=dt, device=DEV)
         self.params = sa.params_from_config(cfg, n_cap=cap)
+        self.params.per_head_sets = int(per_head)
         self.ws_sel = sa.Workspace(DEV)
         self.ws_dec = sa.Workspace(DEV)
 

@@ -235,3 +235,52 @@ def test_check_selection_flags_negative_counts():
     sa.check_selection(torch.tensor([[5, 0], [7, 100]], dtype=torch.int32))
     with pytest.raises(sa.SparseAttnError):
         sa.check_selection(torch.tensor([[5, -1], [7, 100]], dtype=torch.int32))
+
+
+def test_per_head_sets_validation_and_sizes():
+    # the flag is 0 or 1; per-head units need n_q_heads <= 64; a per-head
+    # selection has G times the rows (a larger zero-carrying workspace)
+    b = _full_bufs()
+    st, group_bytes = _select(_decode_params(), b, sa.SEL_TOPP)
+    assert st == sa.SA_OK
+    st, head_bytes = _select(_decode_params(per_head_sets=True), b, sa.SEL_TOPP)
+    assert st == sa.SA_OK and head_bytes > group_bytes
+    p = _decode_params()
+    p.per_head_sets = 2
+    assert _select(p, b, sa.SEL_TOPP)[0] == sa.SA_ERR_INVALID_ARG
+    assert _decode(p, b)[0] == sa.SA_ERR_INVALID_ARG
+    many = _decode_params(n_q_heads=72, n_kv_heads=8, head_kind=[1] * 72, per_head_sets=True)
+    assert _select(many, b, sa.SEL_TOPP)[0] == sa.SA_ERR_UNSUPPORTED
+    assert _decode(many, b)[0] == sa.SA_ERR_UNSUPPORTED
+    # GQA groups of 3 heads are fine per head (each head is its own unit)
+    odd = _decode_params(n_q_heads=6, n_kv_heads=2, head_kind=[1] * 3 + [0] * 3)
+    assert _decode(odd, b)[0] == sa.SA_ERR_UNSUPPORTED
+    odd.per_head_sets = 1
+    assert _decode(odd, b)[0] == sa.SA_OK
+
+
+def _prefill_heads(p, b):
+    return sa.raw_call("prefill_heads", ctypes.byref(p), ctypes.byref(b), None)
+
+
+def test_prefill_heads_validation():
+    b = _full_bufs()
+    ok = dict(n_ctx=4096, sinks=4, window=1024)
+    assert _prefill_heads(_decode_params(**ok, dtype="fp32"), b) == sa.SA_ERR_UNSUPPORTED
+    assert _prefill_heads(_decode_params(**ok, head_dim=64), b) == sa.SA_ERR_UNSUPPORTED
+    assert _prefill_heads(_decode_params(n_ctx=1 << 23, sinks=4, window=8), b) == \
+        sa.SA_ERR_UNSUPPORTED
+    assert _prefill_heads(_decode_params(n_ctx=4096, sinks=0, window=0), b) == \
+        sa.SA_ERR_INVALID_ARG
+    assert _prefill_heads(_decode_params(n_ctx=4096, sinks=-1, window=8), b) == \
+        sa.SA_ERR_INVALID_ARG
+    # labels must agree inside a GQA group
+    mixed = _decode_params(**ok, head_kind=[1, 0, 1, 1, 0, 0, 0, 0])
+    assert _prefill_heads(mixed, b) == sa.SA_ERR_INVALID_ARG
+    # a missing or misaligned buffer
+    nb = _full_bufs()
+    nb.out = None
+    assert _prefill_heads(_decode_params(**ok), nb) == sa.SA_ERR_INVALID_ARG
+    mb = _full_bufs()
+    mb.q = FAKE + 8
+    assert _prefill_heads(_decode_params(**ok), mb) == sa.SA_ERR_INVALID_ARG

@@ -35,3 +35,12 @@ def test_source_sha_changes_with_the_text():
     a = bench.source_sha(["prefill.hip", "common.hpp", "args.hpp"])
     b = bench.source_sha(["prefill.hip", "common.hpp"])
     assert len(a) == 16 and a != b
+
+
+def test_head_split_flop_count_matches_the_oracle_pairs():
+    # the bench's closed-form pair count (its FLOP numerator) against the
+    # oracle's count of each query's visible set
+    import oracle
+    for n, s, w in ((1, 4, 8), (300, 4, 64), (513, 0, 1), (200, 250, 0), (1000, 4, 1024)):
+        assert bench.head_split_pairs(n, True, s, w) == oracle.visible_pairs(n, 0, s, w)
+        assert bench.head_split_pairs(n, False, s, w) == oracle.visible_pairs(n, 1, s, w)

@@ -121,6 +121,11 @@ HGA_64K = DecodeConfig(
     needles_per_head=64, chunk=64, group=16, top_chunks=16, top_groups=2,
     sink_chunks=4, local_chunks=8)
 
+# head-split prefill of the 32K decode layer's heads (one sequence): the 8
+# retrieval heads attend densely, the 24 local heads over 4 sinks + 1024
+LLAMA_PREFILL_32K = LLAMA_32K.with_(name="llama3_8b_head_split_prefill_32k", batch=1,
+                                    needles_per_head=0)
+
 PYRAMID_128K = PrefillConfig(
     name="pyramid_prefill_128k", batch=1, n_heads=16, head_dim=128,
     n_ctx=131072)
@@ -324,6 +329,35 @@ def prefill_inputs(cfg: PrefillConfig, seed: int, device="cpu") -> dict:
         out[name] = t
     out["heavy"] = heavy.cpu()
     return out
+
+
+def head_prefill_inputs(cfg: DecodeConfig, seed: int, device="cpu",
+                        n_cap: Optional[int] = None) -> dict:
+    """Inputs of a head-split prefill over n = cfg.n_ctx tokens: q_pre
+    [B,Hq,n,d] and k_pre, v [B,Hkv,n_cap,d] ~ N(0,1) rounded to the workload
+    dtype (keys and values past n are zero), and the post-RoPE q and k at
+    positions 0 .. n - 1 (rounded again)."""
+    B, Hq, Hkv, d, n = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_ctx
+    cap = n if n_cap is None else n_cap
+    f32 = dict(dtype=torch.float32, device=device)
+    q_pre = torch.empty(B, Hq, n, d, **f32)
+    k_pre = torch.zeros(B, Hkv, cap, d, **f32)
+    v = torch.zeros(B, Hkv, cap, d, **f32)
+    for b in range(B):
+        for h in range(Hq):
+            q_pre[b, h] = _quant(torch.randn(n, d, generator=_gen(seed, device, 31, b, h), **f32),
+                                 cfg.dtype)
+        for g in range(Hkv):
+            gk = _gen(seed, device, 32, b, g)
+            k_pre[b, g, :n] = _quant(torch.randn(n, d, generator=gk, **f32), cfg.dtype)
+            v[b, g, :n] = _quant(torch.randn(n, d, generator=gk, **f32), cfg.dtype)
+    pos = torch.arange(n, device=device)
+    q = _quant(apply_rope(q_pre, pos, cfg.rope_base), cfg.dtype)
+    k = _quant(apply_rope(k_pre[:, :, :n], pos, cfg.rope_base), cfg.dtype)
+    k_cache = torch.zeros_like(k_pre)
+    k_cache[:, :, :n] = k
+    return dict(q=q, k_cache=k_cache, v_cache=v, n_cap=cap,
+                head_kind=torch.tensor(cfg.head_kind(), dtype=torch.int8))
 
 
 def to_device_dtype(x: torch.Tensor, dtype: str, device) -> torch.Tensor:
