@@ -6,7 +6,9 @@
 // q_idx[b,h,c]   = sum_e P_q[g,c,e] * q_pre[b,h,e]     (fp32)
 //
 // Key side: an HBM-bound stream over k_pre (d * e bytes in, 16 * e out per
-// token).  L = d / (16 bytes / e) lanes share a token: each loads 16
+// token).  bf16 rows go through the matrix cores (project_rows_mfma below:
+// 16-row tiles, the fp32 projector split into three bf16 parts).  fp32 rows
+// take a vector path: L = d / (16 bytes / e) lanes share a token: each loads 16
 // contiguous bytes of its row (so one wave instruction reads 64 / L whole
 // rows) and multiplies them with its slice of the projector, which it holds
 // in registers for the whole launch (16 outputs x 16 bytes of dims).  A

@@ -454,22 +454,25 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   // steps that turn them into probabilities take the masked form.
   int tile = 0;
   if constexpr (HEADS) {
-    // a tile needs the mask unless all of its entries are in the sequence,
-    // at or before the block's first query, and each a sink or inside the
-    // window of the block's last query (entries ascend in position)
-    auto needs_mask = [&](int t) __attribute__((always_inline)) -> bool {
-      const int e0 = t * kKT, e1 = e0 + kKT;
-      if (e1 > T || pos(e1 - 1) > q0) return true;
-      return e1 > A && lo + (max(e0, A) - A) <= q1 - 1 - W;
-    };
+    // tiles [0, u0) hold window entries that the block's last query does
+    // not see (pos <= q1 - 1 - W), tiles from u1 on entries past the block's
+    // first query (pos > q0) or past the sequence: both need the mask, the
+    // tiles between do not (entries ascend in position)
+    const int e_w = A + max(0, q1 - W - lo + 1);
+    const int e_c = (q0 + 1 < A) ? q0 + 1 : A + max(0, q0 + 1 - lo);
+    const int u0 = (min(e_w, T) + kKT - 1) / kKT;
+    const int u1 = min(e_c, T) / kKT;
+    for (; tile + 1 < ntiles && tile + 1 < u0; tile += 2) {
+      body(masked, tile, ra, rb, sb_, sa_, pa, pb);
+      body(masked, tile + 1, rb, ra, sa_, sb_, pb, pa);
+    }
+    for (; tile + 2 < u1; tile += 2) {
+      body(unmasked, tile, ra, rb, sb_, sa_, pa, pb);
+      body(unmasked, tile + 1, rb, ra, sa_, sb_, pb, pa);
+    }
     for (; tile + 1 < ntiles; tile += 2) {
-      if (needs_mask(tile + 1) || needs_mask(tile + 2)) {
-        body(masked, tile, ra, rb, sb_, sa_, pa, pb);
-        body(masked, tile + 1, rb, ra, sa_, sb_, pb, pa);
-      } else {
-        body(unmasked, tile, ra, rb, sb_, sa_, pa, pb);
-        body(unmasked, tile + 1, rb, ra, sa_, sb_, pb, pa);
-      }
+      body(masked, tile, ra, rb, sb_, sa_, pa, pb);
+      body(masked, tile + 1, rb, ra, sa_, sb_, pb, pa);
     }
   } else {
     const int mask_from = c_sel / kKT;
