@@ -174,49 +174,15 @@ __device__ __forceinline__ void project_rows(const void* src, const float* Pg, v
 typedef __bf16 ix_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float ix_f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ uint16_t ix_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
-
 template <int D, typename OutT, int U>
 __device__ __forceinline__ void project_rows_mfma(const void* src, const float* Pg, void* dst, int64_t row0,
                                                   int first, int last) {
   constexpr int KS = D / 32;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int col = lane & 15, kb = lane >> 4;
-  ix_bf16x8 ph[KS], pm[KS], pl[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const float* pr = Pg + col * D + 32 * s + 8 * kb;
-    const vl_f32x4 x0 = *reinterpret_cast<const vl_f32x4*>(pr);
-    const vl_f32x4 x1 = *reinterpret_cast<const vl_f32x4*>(pr + 4);
-    uint16_t h[8], m[8], l[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = i < 4 ? x0[i] : x1[i - 4];
-      h[i] = ix_bf16_rne(p);
-      const float r1 = p - __uint_as_float((uint32_t)h[i] << 16);
-      m[i] = ix_bf16_rne(r1);
-      const float r2 = r1 - __uint_as_float((uint32_t)m[i] << 16);
-      l[i] = ix_bf16_rne(r2);
-    }
-    vl_u32x4 wh, wm, wl;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      wh[i] = (uint32_t)h[2 * i] | ((uint32_t)h[2 * i + 1] << 16);
-      wm[i] = (uint32_t)m[2 * i] | ((uint32_t)m[2 * i + 1] << 16);
-      wl[i] = (uint32_t)l[2 * i] | ((uint32_t)l[2 * i + 1] << 16);
-    }
-    ph[s] = __builtin_bit_cast(ix_bf16x8, wh);
-    pm[s] = __builtin_bit_cast(ix_bf16x8, wm);
-    pl[s] = __builtin_bit_cast(ix_bf16x8, wl);
-  }
   const uint16_t* sp = reinterpret_cast<const uint16_t*>(src);
   constexpr int STEP = 16 * U * (kIdxThreads / 64);   // rows per workgroup step
-  for (int base = first + wid * 16 * U; base < last; base += STEP) {
-    vl_u32x4 av[U][KS];
+  auto load_rows = [&](int base, vl_u32x4 (&av)[U][KS]) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int r = min(base + 16 * u + col, last - 1);
@@ -225,6 +191,39 @@ __device__ __forceinline__ void project_rows_mfma(const void* src, const float* 
         av[u][s] = __builtin_nontemporal_load(
             reinterpret_cast<const vl_u32x4*>(sp + (row0 + r) * D + 32 * s + 8 * kb));
     }
+  };
+  // the first step's rows are requested before the projector is loaded and
+  // split, so the two memory latencies overlap (an append is one step)
+  int base = first + wid * 16 * U;
+  vl_u32x4 av[U][KS];
+  if (base < last) load_rows(base, av);
+  ix_bf16x8 ph[KS], pm[KS], pl[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const float* pr = Pg + col * D + 32 * s + 8 * kb;
+    const vl_f32x4 x0 = *reinterpret_cast<const vl_f32x4*>(pr);
+    const vl_f32x4 x1 = *reinterpret_cast<const vl_f32x4*>(pr + 4);
+    float p[8], r1[8], r2[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = i < 4 ? x0[i] : x1[i - 4];
+    // p = hi + mid + lo, each part the nearest bf16 of what is left
+    // (v_cvt_pk_bf16_f32 rounds to nearest even)
+    ix_bf16x8 h, m, l;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = (__bf16)p[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r1[i] = p[i] - (float)h[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m[i] = (__bf16)r1[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r2[i] = r1[i] - (float)m[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) l[i] = (__bf16)r2[i];
+    ph[s] = h;
+    pm[s] = m;
+    pl[s] = l;
+  }
+  for (; base < last; base += STEP) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       ix_f32x4 c = {0.f, 0.f, 0.f, 0.f};
@@ -241,6 +240,7 @@ __device__ __forceinline__ void project_rows_mfma(const void* src, const float* 
         if (r < last) Elem<OutT>::store(dst, (row0 + r) * 16 + col, c[i]);
       }
     }
+    if (base + STEP < last) load_rows(base + STEP, av);
   }
 }
 
