@@ -42,7 +42,7 @@ from .lowrank import (index_keys, index_query, index_logits, order, select_prefi
                       select_topp, select_topk, topp_margin, cut_gap)
 from .local import local_set
 from .hga import (high_freq_pairs, chunk_summary, chunk_summaries, group_summaries,
-                  route_token_list, route_scores)
+                  route_token_list, route_scores, route_prefill_block, route_prefill_rows)
 from .lighthouse import (pyramid_levels, pyramid_scores, visible_entries,
                          block_select, prefill_block, prefill)
 from .decode import decode_step, decode_token_sets, decode_token_sets_per_head

@@ -1,4 +1,4 @@
-"""Hierarchical chunk/group routing (HGA) for decode.
+"""Hierarchical chunk/group routing (HGA) for decode and chunked prefill.
 
 "Atencao Global Hierarquica (HGA)" summary, Core mechanism:
   1. the sequence is cut into fixed chunks (e.g. C = 64 tokens), each split
@@ -121,3 +121,42 @@ def route_token_list(q_heads, chunk_sum, group_sum, n, chunk=64, group=16,
     info = dict(chunks=np.sort(chosen_chunks), groups=np.sort(np.asarray(chosen_groups, np.int64)),
                 chunk_gap=chunk_gap, group_gaps=group_gaps, kappa=kappa)
     return tokens, info
+
+
+# ------------------------------------------------------------ chunked prefill
+# HGA summary, Core mechanism item 2: the current chunk routes against the
+# summaries of earlier chunks; the page reports the routed prefill's speed-up,
+# so routing also runs during (chunked) prefill.  Readings:
+#   * a query block is one chunk (its C queries route together); its
+#     chunk-level query is the mean of the block's post-RoPE query rows over
+#     the KV group's heads (G x C rows, fewer in a last partial block);
+#   * the block routes as the decode rule does at its last position t, so
+#     kappa is the block itself, candidates are the complete chunks in
+#     [sink_chunks, kappa - local_chunks), and sink and local chunks are
+#     always visible;
+#   * query i of the block sees that list (all of it lies before the block)
+#     plus the block's own keys kappa*C .. i (causal).
+
+
+def route_prefill_block(q_rows, chunk_sum, group_sum, block, n, chunk, group, top_chunks,
+                        top_groups, sink_chunks, local_chunks):
+    """Routed list (ascending positions before the block) of prefill query
+    block ``block`` and the routing details.  q_rows: the block's query rows
+    of the group's heads, [rows, d]."""
+    t = min(n, (block + 1) * chunk) - 1
+    toks, info = route_token_list(q_rows, chunk_sum, group_sum, t + 1, chunk, group,
+                                  top_chunks, top_groups, sink_chunks, local_chunks)
+    return toks[toks < block * chunk], info
+
+
+def route_prefill_rows(q, K, V, lst, block, chunk, rows, scale=None):
+    """Outputs [len(rows), d] of one query head for positions ``rows`` of
+    block ``block``: each attends over the block's routed list ``lst`` and the
+    block's keys block*chunk .. i.  q [n, d] of the head; K, V [n, d] of its
+    KV group."""
+    from .attention import attend
+    out = np.empty((len(rows), np.asarray(q).shape[-1]))
+    for r, i in enumerate(rows):
+        T = np.concatenate([np.asarray(lst, np.int64), np.arange(block * chunk, i + 1)])
+        out[r] = attend(q[i], K[T], V[T], scale)
+    return out

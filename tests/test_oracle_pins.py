@@ -675,3 +675,75 @@ def test_visible_pairs_closed_form(N, sinks, window):
         total += a + wcount - over
     assert oracle.visible_pairs(N, 0, sinks, window) == total
     assert oracle.visible_pairs(N, 1, sinks, window) == N * (N + 1) // 2
+
+
+# --------------------------------------------------------------- HGA chunked prefill
+def _hga_prefill_case(seed, n=16 * 13 + 5, d=16, G=2, chunk=16, group=4):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((G, n, d))
+    K = rng.standard_normal((n, d))
+    V = rng.standard_normal((n, d))
+    cs = rng.standard_normal((n // chunk, d))
+    gs = rng.standard_normal((n // group, d))
+    return q, K, V, cs, gs
+
+
+def _hga_prefill_all(q, K, V, cs, gs, n, chunk, group, **kw):
+    out = np.empty((q.shape[0], n, q.shape[2]))
+    for blk in range((n + chunk - 1) // chunk):
+        rows = np.arange(blk * chunk, min(n, (blk + 1) * chunk))
+        lst, _ = oracle.route_prefill_block(q[:, rows].reshape(-1, q.shape[2]), cs, gs, blk, n,
+                                            chunk, group, **kw)
+        for h in range(q.shape[0]):
+            out[h, rows] = oracle.route_prefill_rows(q[h], K, V, lst, blk, chunk, rows)
+    return out
+
+
+@pytest.mark.parametrize("kw", [
+    dict(top_chunks=100, top_groups=4, sink_chunks=2, local_chunks=1),   # everything routed
+    dict(top_chunks=1, top_groups=1, sink_chunks=0, local_chunks=100),   # everything local
+    dict(top_chunks=1, top_groups=1, sink_chunks=100, local_chunks=0),   # everything a sink
+])
+def test_hga_prefill_keeping_everything_is_dense_causal(kw):
+    n, chunk, group = 16 * 13 + 5, 16, 4
+    q, K, V, cs, gs = _hga_prefill_case(30)
+    out = _hga_prefill_all(q, K, V, cs, gs, n, chunk, group, **kw)
+    for h in range(q.shape[0]):
+        np.testing.assert_allclose(out[h], sdpa64(q[h], K, V, causal=True), atol=1e-12)
+
+
+def test_hga_prefill_lists_brute_force():
+    # the block's chunk-level query is the mean of its rows over the group's
+    # heads; candidates are the complete chunks in [sinks, block - local);
+    # top chunks, then top groups, by sorting (score desc, index asc)
+    n, chunk, group = 16 * 13 + 5, 16, 4
+    gpc = chunk // group
+    q, K, V, cs, gs = _hga_prefill_case(31)
+    kw = dict(top_chunks=3, top_groups=2, sink_chunks=1, local_chunks=2)
+    for blk in range((n + chunk - 1) // chunk):
+        rows = np.arange(blk * chunk, min(n, (blk + 1) * chunk))
+        qr = q[:, rows].reshape(-1, q.shape[2])
+        lst, _ = oracle.route_prefill_block(qr, cs, gs, blk, n, chunk, group, **kw)
+        qbar = qr.sum(axis=0) / len(qr)
+        cand = list(range(1, max(1, blk - 2)))
+        top = sorted(cand, key=lambda c: (-float(qbar @ cs[c]), c))[:3]
+        expect = set(range(0, min(1, blk) * chunk))
+        expect |= set(range(max(1, blk - 2) * chunk, blk * chunk))
+        for c in top:
+            grp = sorted(range(c * gpc, (c + 1) * gpc), key=lambda gi: (-float(qbar @ gs[gi]), gi))[:2]
+            for gi in grp:
+                expect |= set(range(gi * group, (gi + 1) * group))
+        assert lst.tolist() == sorted(expect), blk
+
+
+def test_hga_prefill_rows_are_attention_over_list_and_causal_block():
+    n, chunk, group = 16 * 13 + 5, 16, 4
+    q, K, V, cs, gs = _hga_prefill_case(32)
+    blk = 11
+    rows = np.arange(blk * chunk, (blk + 1) * chunk)
+    lst, _ = oracle.route_prefill_block(q[:, rows].reshape(-1, 16), cs, gs, blk, n, chunk, group,
+                                        top_chunks=2, top_groups=1, sink_chunks=1, local_chunks=1)
+    out = oracle.route_prefill_rows(q[0], K, V, lst, blk, chunk, rows)
+    for r, i in enumerate(rows):
+        T = np.r_[lst, blk * chunk:i + 1]
+        np.testing.assert_allclose(out[r], sdpa64(q[0, i], K[T], V[T])[0], atol=1e-12)
