@@ -40,7 +40,8 @@ def parse():
     ap.add_argument("--workload", default="llama3_8b_decode_32k",
                     choices=["llama3_8b_decode_32k", "llama3_8b_decode_128k",
                              "llama3_8b_decode_128k_topk", "hga_route_decode_64k",
-                             "pyramid_prefill_128k", "llama3_8b_head_split_prefill_32k"])
+                             "pyramid_prefill_128k", "llama3_8b_head_split_prefill_32k",
+                             "hga_route_prefill_64k"])
     ap.add_argument("--instances", type=int, default=4,
                     help="independent input sets rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -79,12 +80,15 @@ def traffic_record(kernel, workload, sha):
 
 # ----------------------------------------------------------------- decode
 class DecodeInstance:
-    def __init__(self, cfg, seed, sa, torch, workloads, alpha=1.0, like=None):
+    def __init__(self, cfg, seed, sa, torch, workloads, alpha=1.0, like=None, per_head=False):
         """One step's device buffers.  ``like``: copy another instance's
         inputs (same values at new addresses, so the Infinity Cache holds
-        nothing of this one when the other has just run)."""
+        nothing of this one when the other has just run).  ``per_head``:
+        every query head selects its own set."""
         B, Hq, Hkv, d, n = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_ctx
         self.cfg = cfg
+        self.per_head = per_head
+        ns = Hq if per_head else Hkv
         dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
         if like is None:
             inp = workloads.decode_inputs(cfg, seed, device="cuda", alpha=alpha)
@@ -97,14 +101,15 @@ class DecodeInstance:
                                                     "proj")}
         self.t["k_idx"] = torch.zeros(B, Hkv, n, cfg.r, dtype=dt, device="cuda")
         self.t["q_idx"] = torch.zeros(B, Hq, cfg.r, dtype=torch.float32, device="cuda")
-        self.t["sel_idx"] = torch.zeros(B, Hkv, n, dtype=torch.int32, device="cuda")
-        self.t["sel_count"] = torch.zeros(B, Hkv, dtype=torch.int32, device="cuda")
+        self.t["sel_idx"] = torch.zeros(B, ns, n, dtype=torch.int32, device="cuda")
+        self.t["sel_count"] = torch.zeros(B, ns, dtype=torch.int32, device="cuda")
         self.t["out"] = torch.zeros(B, Hq, d, dtype=torch.float32, device="cuda")
         if cfg.routed:
             self.t["chunk_sum"] = torch.zeros(B, Hkv, n // cfg.chunk, d, dtype=dt, device="cuda")
             self.t["group_sum"] = torch.zeros(B, Hkv, n // cfg.group, d, dtype=dt, device="cuda")
         t = self.t
         self.params = sa.params_from_config(cfg)
+        self.params.per_head_sets = int(per_head)
         self.bufs = sa.make_buffers(
             q_pre=t["q_pre"], k_pre=t["k_pre"], q=t["q"], k_cache=t["k_cache"],
             v_cache=t["v_cache"], proj_q=t["proj"], proj_k=t["proj"], q_idx=t["q_idx"],
@@ -135,6 +140,29 @@ class DecodeInstance:
     def decode(self):
         self.sa.decode(self.params, self.bufs, self.ws_dec)
 
+    def counts(self, torch):
+        """Selected counts per (b, KV group) as the step's bytes count them:
+        with per-head sets, the size of the union of the group's heads' sets
+        (the rows the group's heads read between them), plus the per-head
+        counts (the list entries)."""
+        cnt = self.t["sel_count"].cpu()
+        if not self.per_head:
+            return cnt.tolist(), None
+        cfg = self.cfg
+        G, n = cfg.gqa, cfg.n_ctx
+        union = []
+        for b in range(cfg.batch):
+            row = []
+            for g in range(cfg.n_kv_heads):
+                seen = torch.zeros(n, dtype=torch.bool, device="cuda")
+                for h in range(g * G, (g + 1) * G):
+                    c = int(cnt[b, h])
+                    if c > 0:
+                        seen[self.t["sel_idx"][b, h, :c].long()] = True
+                row.append(int(seen.sum()))
+            union.append(row)
+        return union, cnt.tolist()
+
     def capture(self, torch):
         """Record the step's two halves into HIP graphs (after a warm-up)."""
         self.g_sel, self.g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
@@ -144,8 +172,11 @@ class DecodeInstance:
             self.decode()
 
 
-def decode_bytes(cfg, counts, kinds):
-    """Algorithmic bytes of one decode step and of its attention kernel."""
+def decode_bytes(cfg, counts, kinds, head_counts=None):
+    """Algorithmic bytes of one decode step and of its attention kernel.
+    ``counts``: visible tokens per (b, KV group) (with per-head sets, the
+    union over the group's heads); ``head_counts``: per-head list lengths
+    when the sets are per head."""
     e = 2 if cfg.dtype == "bf16" else 4
     B, Hq, Hkv, d, n, G = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_ctx, cfg.gqa
     kv = 0
@@ -157,7 +188,10 @@ def decode_bytes(cfg, counts, kinds):
                 c = min(n, cfg.sinks + cfg.window)
             else:
                 c = int(counts[b][g])
-                lists += 4 * c
+                if head_counts is None:
+                    lists += 4 * c
+                else:
+                    lists += 4 * sum(int(head_counts[b][h]) for h in range(g * G, (g + 1) * G))
             kv += c * 2 * d * e
     qo = B * Hq * d * (e + 4)
     attn = kv + lists + qo
@@ -182,27 +216,32 @@ MIN_TOUCHED_BYTES = 1 << 30     # rotated instances touch at least this much per
 
 
 def run_decode(args, torch, sa, workloads, workload=None, steps=None, warmup=None,
-               instances=None, cpu=True, alpha=1.0):
+               instances=None, cpu=True, alpha=1.0, per_head=False):
     workload = workload or args.workload
     steps = steps or args.steps
     warmup = args.warmup if warmup is None else warmup
     instances = instances or args.instances
     cfg = getattr(workloads, DECODE_CONFIGS[workload])
     kinds = cfg.head_kind()
-    log(f"[bench] generating {instances} instance(s) of {cfg.name} (alpha {alpha})")
-    insts = [DecodeInstance(cfg, 1000 + i, sa, torch, workloads, alpha=alpha)
+    log(f"[bench] generating {instances} instance(s) of {cfg.name} (alpha {alpha}"
+        f"{', per-head sets' if per_head else ''})")
+    insts = [DecodeInstance(cfg, 1000 + i, sa, torch, workloads, alpha=alpha, per_head=per_head)
              for i in range(instances)]
     # one step of each, then copies until a round of the rotation touches
     # >= 1 GiB (so no step finds its rows in the 256 MB Infinity Cache)
     for x in insts:
         x.index_and_select()
     torch.cuda.synchronize()
-    per_step = sum(decode_bytes(cfg, x.t["sel_count"].cpu().tolist(), kinds)[1]
-                   for x in insts) / len(insts)
+    per_step = 0
+    for x in insts:
+        c, hc = x.counts(torch)
+        per_step += decode_bytes(cfg, c, kinds, hc)[1]
+    per_step /= len(insts)
     want = max(len(insts), -(-MIN_TOUCHED_BYTES // int(per_step)))
     base = len(insts)
     while len(insts) < want:
-        insts.append(DecodeInstance(cfg, 0, sa, torch, workloads, like=insts[len(insts) % base]))
+        insts.append(DecodeInstance(cfg, 0, sa, torch, workloads, like=insts[len(insts) % base],
+                                    per_head=per_head))
     if len(insts) > base:
         log(f"[bench] {len(insts) - base} copies added: {len(insts)} instances, "
             f"{len(insts) * per_step / 2**30:.2f} GiB touched per rotation")
@@ -286,14 +325,16 @@ def run_decode(args, torch, sa, workloads, workload=None, steps=None, warmup=Non
     attn_b, step_b = 0, 0
     sel_frac = []
     for x in insts:
-        c = x.t["sel_count"].cpu().tolist()
-        a, s_ = decode_bytes(cfg, c, kinds)
+        c, hc = x.counts(torch)
+        a, s_ = decode_bytes(cfg, c, kinds, hc)
         attn_b += a
         step_b += s_
         for b in range(cfg.batch):
-            for g in range(cfg.n_kv_heads):
-                if kinds[g * cfg.gqa] != 0:
-                    sel_frac.append(c[b][g] / cfg.n_ctx)
+            if hc is None:
+                sel_frac += [c[b][g] / cfg.n_ctx for g in range(cfg.n_kv_heads)
+                             if kinds[g * cfg.gqa] != 0]
+            else:
+                sel_frac += [hc[b][h] / cfg.n_ctx for h in range(cfg.n_q_heads) if kinds[h] != 0]
     attn_b /= len(insts)
     step_b /= len(insts)
     tokens = cfg.batch * cfg.n_q_heads * cfg.n_ctx
@@ -311,6 +352,7 @@ def run_decode(args, torch, sa, workloads, workload=None, steps=None, warmup=Non
                    "top_k": cfg.top_k or None, "min_tokens": cfg.min_tokens,
                    "sinks": cfg.sinks, "window": cfg.window, "routed": cfg.routed,
                    "instances_rotated": len(insts), "alpha": alpha,
+                   "per_head_sets": per_head,
                    "touched_gib_per_rotation": len(insts) * step_b / 2**30,
                    "launch": "hip_graph" if args.graph else "eager"},
         "step_hbm_gbps": step_b / t_step / 1e9,
@@ -444,6 +486,8 @@ def main():
         res = run_prefill(args, torch, sa, workloads)
     elif args.workload == "llama3_8b_head_split_prefill_32k":
         res = run_prefill_heads(args, torch, sa, workloads)
+    elif args.workload == "hga_route_prefill_64k":
+        res = run_prefill_routed(args, torch, sa, workloads)
     else:
         res = run_decode(args, torch, sa, workloads)
     if not args.no_extras and args.workload == "llama3_8b_decode_32k":
@@ -451,6 +495,10 @@ def main():
         for w in ("llama3_8b_decode_128k_topk", "llama3_8b_decode_128k", "hga_route_decode_64k"):
             other[w] = compact(run_decode(args, torch, sa, workloads, workload=w, steps=20,
                                           warmup=3, instances=4, cpu=False))
+        # the 32K step with one set per query head (no GQA sharing of sets)
+        other["llama3_8b_decode_32k_per_head"] = compact(run_decode(
+            args, torch, sa, workloads, workload="llama3_8b_decode_32k", steps=20, warmup=3,
+            instances=4, cpu=False, per_head=True))
         # the 128K top-p step at other attention entropies (query norms x alpha)
         for a in (0.5, 2.0):
             other[f"llama3_8b_decode_128k_alpha{a:g}"] = compact(run_decode(
@@ -459,6 +507,8 @@ def main():
         other["pyramid_prefill_128k"] = compact(run_prefill(args, torch, sa, workloads, steps=5,
                                                             warmup=1, cpu=False))
         other["llama3_8b_head_split_prefill_32k"] = compact(run_prefill_heads(
+            args, torch, sa, workloads, steps=5, warmup=1, cpu=False))
+        other["hga_route_prefill_64k"] = compact(run_prefill_routed(
             args, torch, sa, workloads, steps=5, warmup=1, cpu=False))
         res["other_workloads"] = other
     print(json.dumps(res), flush=True)
@@ -645,6 +695,125 @@ def run_prefill_heads(args, torch, sa, workloads, steps=None, warmup=None, cpu=T
     del t
     torch.cuda.empty_cache()
     return res
+
+
+def run_prefill_routed(args, torch, sa, workloads, steps=None, warmup=None, cpu=True):
+    """Routed chunked prefill of the 64K routed layer's heads (one
+    sequence): chunk/group summaries of the whole prefix, every query block's
+    routing, then attention over each block's list plus its causal keys."""
+    cfg = workloads.HGA_PREFILL_64K
+    steps = steps or max(3, min(args.steps, 10))
+    warmup = 1 if warmup is None else warmup
+    B, Hq, Hkv, N, d = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.n_ctx, cfg.head_dim
+    C, G = cfg.chunk, cfg.gqa
+    nblk = (N + C - 1) // C
+    K = (cfg.sink_chunks + cfg.local_chunks) * C + cfg.top_chunks * cfg.top_groups * cfg.group
+    log(f"[bench] generating {cfg.name}")
+    inp = workloads.head_prefill_inputs(cfg.with_(n_ret_q_heads=Hq), 2200, device="cuda")
+    t = {k: inp[k].to(torch.bfloat16).contiguous() for k in ("q", "k_pre", "k_cache", "v_cache")}
+    del inp
+    t["chunk_sum"] = torch.zeros(B, Hkv, N // C, d, dtype=torch.bfloat16, device="cuda")
+    t["group_sum"] = torch.zeros(B, Hkv, N // cfg.group, d, dtype=torch.bfloat16, device="cuda")
+    t["blk_idx"] = torch.zeros(B, Hkv, nblk, K, dtype=torch.int32, device="cuda")
+    t["blk_count"] = torch.zeros(B, Hkv, nblk, dtype=torch.int32, device="cuda")
+    t["out"] = torch.zeros(B, Hq, N, d, dtype=torch.float32, device="cuda")
+    p = sa.make_params(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, n_ctx=N, dtype="bf16",
+                       head_kind=[workloads.HEAD_ROUTED] * Hq, rope_base=cfg.rope_base, chunk=C,
+                       group=cfg.group, top_chunks=cfg.top_chunks, top_groups=cfg.top_groups,
+                       sink_chunks=cfg.sink_chunks, local_chunks=cfg.local_chunks, levels=1,
+                       factor=4, q_block=C, block_top_k=K)
+    bufs = sa.make_buffers(q=t["q"], k_pre=t["k_pre"], k_cache=t["k_cache"], v_cache=t["v_cache"],
+                           chunk_sum=t["chunk_sum"], group_sum=t["group_sum"],
+                           blk_idx=t["blk_idx"], blk_count=t["blk_count"], out=t["out"])
+    ws_s, ws_p = sa.Workspace("cuda"), sa.Workspace("cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        sa.index_build(p, bufs, sa.IDX_CHUNK_SUMMARY, 0, N)
+        sa.select(p, bufs, sa.SEL_ROUTE2_PREFILL, ws_s)
+        if ev:
+            ev[0].record(stream)
+        sa.prefill_chunked(p, bufs, ws_p)
+        if ev:
+            ev[1].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        step(ev[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_step = start.elapsed_time(end) / steps * 1e-3
+    t_kernel = sum(a.elapsed_time(b) for a, b in ev) / steps * 1e-3
+    counts = t["blk_count"].cpu()
+    pairs = 0
+    for blk in range(nblk):
+        nq = min(C, N - blk * C)
+        pairs += G * (int(counts[:, :, blk].sum()) * nq + B * Hkv * nq * (nq + 1) // 2)
+    flops = 4 * d * pairs
+    achieved = flops / t_kernel / 1e12
+    vis_frac = pairs / (B * Hq * N * (N + 1) / 2)
+    log(f"[bench] {cfg.name}: {t_step * 1e3:.3f} ms/step, prefill kernel {t_kernel * 1e3:.3f} ms, "
+        f"{achieved:.1f} TFLOP/s, {100 * vis_frac:.2f} % of the causal pairs")
+    sha = source_sha(["prefill.hip", "common.hpp", "args.hpp"])
+    res = {
+        "metric": "routed chunked prefill tokens/s + achieved bf16 MFMA TFLOP/s vs peak",
+        "value": B * Hq * N / t_step, "unit": "tokens/s (B x heads x N per step)",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": t_step * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv,
+                   "head_dim": d, "n_ctx": N, "chunk": C, "group": cfg.group,
+                   "top_chunks": cfg.top_chunks, "top_groups": cfg.top_groups,
+                   "sink_chunks": cfg.sink_chunks, "local_chunks": cfg.local_chunks,
+                   "visible_pair_frac": vis_frac},
+        "step_tflops": flops / t_step / 1e12,
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel<false>", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic_record("prefill_kernel<false>", cfg.name, sha),
+                     "flops_per_launch": flops, "launch_us": t_kernel * 1e6, "source_sha": sha},
+    }
+    if cpu and not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill_routed(cfg, t, args.cpu_seconds, torch)
+    del t
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline_prefill_routed(cfg, t, budget_s, torch):
+    """The fp64 oracle on whole query blocks of KV group 0 (routing over the
+    GPU's summaries, then attention for the group's query heads), last blocks
+    first, until ``budget_s`` is spent."""
+    import numpy as np
+    import oracle
+    G, C, N = cfg.gqa, cfg.chunk, cfg.n_ctx
+    q = t["q"][0, :G].to("cpu", torch.float64).numpy()
+    K = t["k_cache"][0, 0].to("cpu", torch.float64).numpy()
+    V = t["v_cache"][0, 0].to("cpu", torch.float64).numpy()
+    cs = t["chunk_sum"][0, 0].to("cpu", torch.float64).numpy()
+    gs = t["group_sum"][0, 0].to("cpu", torch.float64).numpy()
+    nblk = (N + C - 1) // C
+    t0 = time.perf_counter()
+    done = 0
+    while time.perf_counter() - t0 < budget_s or done == 0:
+        blk = nblk - 1 - (done * 37) % nblk
+        rows = np.arange(blk * C, min(N, (blk + 1) * C))
+        lst, _ = oracle.route_prefill_block(q[:, rows].reshape(-1, q.shape[-1]), cs, gs, blk, N, C,
+                                            cfg.group, cfg.top_chunks, cfg.top_groups,
+                                            cfg.sink_chunks, cfg.local_chunks)
+        for h in range(G):
+            oracle.route_prefill_rows(q[h], K, V, lst, blk, C, rows)
+        done += 1
+    spent = time.perf_counter() - t0
+    return {"value": done * C * G / spent, "unit": "tokens/s (B x heads x N)",
+            "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{done} query blocks of KV group 0 ({G} query heads) of {cfg.name}: routing "
+                      f"over the GPU's summaries and attention, fp64 numpy, {spent:.1f} s"}
 
 
 def cpu_baseline_prefill_heads(cfg, t, budget_s, torch):

@@ -99,7 +99,8 @@ typedef enum {
   SA_SEL_TOPP = 0,          /* retrieval groups: top-p mass, min_tokens floor */
   SA_SEL_TOPK = 1,          /* retrieval groups: fixed top_k                  */
   SA_SEL_ROUTE2 = 2,        /* routed groups: chunk then group routing        */
-  SA_SEL_PYRAMID_TOPK = 3   /* per query block: joint top-K over levels       */
+  SA_SEL_PYRAMID_TOPK = 3,  /* per query block: joint top-K over levels       */
+  SA_SEL_ROUTE2_PREFILL = 4 /* routed groups, prefill: per query block (chunk) */
 } sa_select_mode;
 
 /* Host struct, read only during the call. */
@@ -220,6 +221,19 @@ int32_t sparse_attn_index_build(const sa_params* params, const sa_buffers* bufs,
  *   is the union of sink chunks, local chunks, tokens kappa*chunk .. t, and
  *   the routed groups, ascending.  Needs n_cap >= the list length;
  *   top_chunks <= 64 and chunk / group <= 64 (SA_ERR_UNSUPPORTED otherwise).
+ * SA_SEL_ROUTE2_PREFILL (HGA summary, Core mechanism items 1-2, routing
+ *   while prefilling): for each routed group and every query block of
+ *   chunk = 128 queries (block beta holds positions 128 beta .. t, t its last
+ *   position), qbar = mean of the block's post-RoPE query rows q[b,h,i] over
+ *   the group's heads; the block then routes as SA_SEL_ROUTE2 does at
+ *   position t (kappa = beta), and its list - sink chunks, local chunks and
+ *   routed groups, all before the block - is written ascending to
+ *   blk_idx[b,g,beta,:] with its length in blk_count[b,g,beta];
+ *   sparse_attn_prefill_chunked with levels = 1 then adds each query's own
+ *   causal part of the block.  q is [B,Hq,n_ctx,d]; blk_idx is
+ *   [B,Hkv,ceil(n_ctx/128),block_top_k].  Needs chunk == 128 and
+ *   per_head_sets == 0 (SA_ERR_UNSUPPORTED) and block_top_k >= (sink_chunks +
+ *   local_chunks) * chunk + top_chunks * top_groups * group (SA_ERR_CAPACITY).
  * SA_SEL_PYRAMID_TOPK (Lighthouse summary, 2B-2C): for every block of q_block
  *   queries, among entries (l, j) with (j + 1) p^l <= q_block * block, keeps
  *   the block_top_k largest pyr_scores (ties: lower level, then lower j) as
@@ -277,7 +291,11 @@ int32_t sparse_attn_decode_noalloc(const sa_params* params, const sa_buffers* bu
  * each query i attends to the block's selected entries (rows of k_cache /
  * v_cache for level 0, of pyr_k / pyr_v above) plus the block's own level-0
  * keys up to and including i, with scale 1/sqrt(d); the fp32 result is
- * written to out row i.  Requires n_q_heads == n_kv_heads, dtype bf16,
+ * written to out row i.  With levels = 1 the heads may be grouped (GQA):
+ * blk_idx / blk_count then belong to the KV heads ([B,Hkv,...]) and the G
+ * query heads of a group share its lists and rows (the layout
+ * SA_SEL_ROUTE2_PREFILL writes); otherwise n_q_heads == n_kv_heads.
+ * Requires dtype bf16,
  * head_dim 128, q_block 128, block_top_k <= 8192 and n_ctx < 2^23
  * (SA_ERR_UNSUPPORTED otherwise).  blk_idx holds flat ids as
  * SA_SEL_PYRAMID_TOPK writes them; an id outside [0, n_ctx + coarse entries)

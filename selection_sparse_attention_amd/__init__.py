@@ -29,7 +29,7 @@ SA_ERR_WORKSPACE, SA_ERR_CAPACITY, SA_ERR_HIP = -3, -4, -5
 SA_BF16, SA_FP32 = 0, 1
 HEAD_LOCAL, HEAD_RETRIEVAL, HEAD_ROUTED = 0, 1, 2
 IDX_LOWRANK, IDX_CHUNK_SUMMARY, IDX_PYRAMID = 0, 1, 2
-SEL_TOPP, SEL_TOPK, SEL_ROUTE2, SEL_PYRAMID_TOPK = 0, 1, 2, 3
+SEL_TOPP, SEL_TOPK, SEL_ROUTE2, SEL_PYRAMID_TOPK, SEL_ROUTE2_PREFILL = 0, 1, 2, 3, 4
 
 EXPORTED = ("sparse_attn_index_build", "sparse_attn_select", "sparse_attn_decode",
             "sparse_attn_decode_noalloc", "sparse_attn_prefill_chunked",

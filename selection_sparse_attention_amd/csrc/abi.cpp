@@ -130,9 +130,10 @@ struct PyrGeom {
   int off[16];   // flat offsets of each level
 };
 
-int32_t pyramid_geom(const sa_params* p, PyrGeom* g) {
+// allow_gqa: one level (no pyramid), the lists belonging to the KV heads
+int32_t pyramid_geom(const sa_params* p, PyrGeom* g, bool allow_gqa = false) {
   if (p->levels < 1 || p->levels > 8 || p->factor < 2) return SA_ERR_INVALID_ARG;
-  if (p->n_q_heads != p->n_kv_heads) return SA_ERR_INVALID_ARG;
+  if (p->n_q_heads != p->n_kv_heads && !(allow_gqa && p->levels == 1)) return SA_ERR_INVALID_ARG;
   const int64_t span = [&] { int64_t s = 1; for (int i = 1; i < p->levels; ++i) s *= p->factor; return s; }();
   if (span > 256) return SA_ERR_UNSUPPORTED;
   if (p->n_ctx % span) return SA_ERR_INVALID_ARG;
@@ -454,6 +455,42 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
     a.groups = gl;
     return hip_status(sa::launch_select_lowrank(a, p->dtype, per, s));
   }
+  if (mode == SA_SEL_ROUTE2_PREFILL) {
+    if (p->chunk < 1 || p->group < 1 || p->chunk % p->group) return SA_ERR_INVALID_ARG;
+    const int gpc = p->chunk / p->group;
+    if (p->top_chunks < 1 || p->top_groups < 1 || p->top_groups > gpc) return SA_ERR_INVALID_ARG;
+    if (p->sink_chunks < 0 || p->local_chunks < 0) return SA_ERR_INVALID_ARG;
+    if (p->chunk != 128 || p->per_head_sets) return SA_ERR_UNSUPPORTED;   // a query block is one chunk
+    if (p->top_chunks > 64 || gpc > 64 || p->top_chunks * p->top_groups > 4096 || p->head_dim > 128)
+      return SA_ERR_UNSUPPORTED;
+    if (p->n_ctx / p->chunk > 16384) return SA_ERR_UNSUPPORTED;
+    // the longest list: sink and local chunks plus the routed groups
+    const int64_t longest = ((int64_t)p->sink_chunks + p->local_chunks) * p->chunk +
+                            (int64_t)p->top_chunks * p->top_groups * p->group;
+    if (p->block_top_k < 1) return SA_ERR_INVALID_ARG;
+    if (longest > p->block_top_k) return SA_ERR_CAPACITY;
+    GroupList gl = units_of_kind(u, SA_HEAD_ROUTED);
+    Carver c(ws);
+    c.take<uint32_t>(1);
+    if ((st = workspace_gate(ws, ws_bytes, c.size()))) return st < 0 ? st : SA_OK;
+    if (gl.n == 0) return SA_OK;
+    const int nblk = (p->n_ctx + p->chunk - 1) / p->chunk;
+    const bool has_cand = nblk - 1 - p->local_chunks > p->sink_chunks;
+    if (!b->q || !b->blk_idx || !b->blk_count) return SA_ERR_INVALID_ARG;
+    if (has_cand && (!b->chunk_sum || !b->group_sum)) return SA_ERR_INVALID_ARG;
+    if (!aligned16(b->q) || (has_cand && (!aligned16(b->chunk_sum) || !aligned16(b->group_sum))))
+      return SA_ERR_INVALID_ARG;
+    sa::RouteArgs a{};
+    a.q = b->q; a.chunk_sum = b->chunk_sum; a.group_sum = b->group_sum;
+    a.B = p->batch; a.Hq = p->n_q_heads; a.Hkv = u.n; a.n = p->n_ctx; a.n_cap = p->n_cap;
+    a.G = u.G; a.kv_div = 1; a.chunk = p->chunk; a.group = p->group; a.top_chunks = p->top_chunks;
+    a.top_groups = p->top_groups; a.sink_chunks = p->sink_chunks; a.local_chunks = p->local_chunks;
+    a.n_cs_cap = p->n_cap / p->chunk; a.n_gs_cap = p->n_cap / p->group;
+    a.groups = gl;
+    a.prefill = 1; a.nblk = nblk; a.K = p->block_top_k;
+    a.blk_idx = b->blk_idx; a.blk_count = b->blk_count;
+    return hip_status(sa::launch_route(a, p->dtype, p->head_dim, s));
+  }
   if (mode == SA_SEL_ROUTE2) {
     if (p->chunk < 1 || p->group < 1 || p->chunk % p->group) return SA_ERR_INVALID_ARG;
     const int gpc = p->chunk / p->group;
@@ -497,7 +534,7 @@ int32_t sparse_attn_prefill_chunked(const sa_params* p, const sa_buffers* b, voi
   int32_t st = check_common(p, b);
   if (st) return st;
   PyrGeom pg;
-  if ((st = pyramid_geom(p, &pg))) return st;
+  if ((st = pyramid_geom(p, &pg, true))) return st;
   if (p->q_block < 1 || p->q_block % pg.top_span || p->block_top_k < 1) return SA_ERR_INVALID_ARG;
   if (p->dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
   if (p->head_dim != 128 || p->q_block != 128) return SA_ERR_UNSUPPORTED;
@@ -514,6 +551,7 @@ int32_t sparse_attn_prefill_chunked(const sa_params* p, const sa_buffers* b, voi
   a.blk_idx = b->blk_idx; a.blk_count = b->blk_count; a.out = b->out;
   a.B = p->batch; a.H = p->n_q_heads; a.N = p->n_ctx; a.Nc = pg.Nc; a.nblk = pg.nblk;
   a.K = p->block_top_k; a.q_block = p->q_block;
+  a.Hkv = p->n_kv_heads; a.G = p->n_q_heads / p->n_kv_heads; a.kv_stride = p->n_ctx;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->head_dim));
   return hip_status(sa::launch_prefill(a, p->head_dim, static_cast<hipStream_t>(stream)));
 }

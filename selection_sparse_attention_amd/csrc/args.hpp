@@ -93,6 +93,12 @@ struct RouteArgs {
   int32_t kv_div;               // selection rows per KV group (G with per-head sets, else 1)
   float* scratch;               // [rows, n_cs_cap] chunk scores
   GroupList groups;
+  // chunked prefill: every query block of `chunk` queries routes (q is then
+  // [B,Hq,n,d]); lists go to blk_idx [B,Hkv,nblk,K] / blk_count [B,Hkv,nblk]
+  int32_t prefill;
+  int32_t nblk, K;
+  int32_t* blk_idx;
+  int32_t* blk_count;
 };
 
 struct PyrSelectArgs {

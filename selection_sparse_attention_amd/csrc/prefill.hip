@@ -5,7 +5,9 @@
 //
 // For query block beta of one (sequence, head), query i = 128 beta + u sees
 // the block's selected entries (rows of K/V for level 0, of the coarse K/V
-// levels above) and the block's own level-0 keys 128 beta .. i:
+// levels above) and the block's own level-0 keys 128 beta .. i (the lists
+// and K/V belong to the head's KV head: GQA heads share both; a pyramid has
+// one query head per KV head):
 //   out[i] = sum_j softmax_j(q_i . k_j / sqrt(d)) v_j      (fp32)
 //
 // gfx950 design, one 256-thread workgroup per (block, head), wave w owning
@@ -129,15 +131,17 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     kvh = b * a.Hkv + h / a.G;
     if (cls == 0) { S = 0; W = a.N + 1; } else { S = a.sinks; W = a.window; }
   } else {
-    // ---- which (head, block): die-major, two heads per die, heavy first
+    // ---- which (head, block): die-major, heavy first; heads sharing a KV
+    //      head (and its lists) on one die, otherwise two heads per die
+    //      taken eight apart
     const int nh = a.B * a.H;
     const int hpx = (nh + 7) / 8;
     const int L = blockIdx.x;
     const int xcd = L % 8, slot = L / 8;
-    bh = xcd + 8 * (slot % hpx);
+    bh = (a.G > 1) ? xcd * hpx + slot % hpx : xcd + 8 * (slot % hpx);
     blk = a.nblk - 1 - slot / hpx;
     if (bh >= nh || blk < 0) return;
-    kvh = bh;
+    kvh = bh / a.G;
   }
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -154,8 +158,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     T = A + (q1 - lo);
     c_sel = 0;
   } else {
-    c_sel = min(max(a.blk_count[(int64_t)bh * a.nblk + blk], 0), min(a.K, kListMax));
-    list = a.blk_idx + ((int64_t)bh * a.nblk + blk) * a.K;
+    c_sel = min(max(a.blk_count[(int64_t)kvh * a.nblk + blk], 0), min(a.K, kListMax));
+    list = a.blk_idx + ((int64_t)kvh * a.nblk + blk) * a.K;
     T = c_sel + nq;
   }
   const int ntiles = (T + kKT - 1) / kKT;
@@ -163,8 +167,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   const uint16_t* qb = reinterpret_cast<const uint16_t*>(a.q) + (int64_t)bh * a.N * kD;
   const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k) + (int64_t)kvh * kv_rows * kD;
   const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.v) + (int64_t)kvh * kv_rows * kD;
-  const uint16_t* pkb = HEADS ? kb : reinterpret_cast<const uint16_t*>(a.pk) + (int64_t)bh * a.Nc * kD;
-  const uint16_t* pvb = HEADS ? vb : reinterpret_cast<const uint16_t*>(a.pv) + (int64_t)bh * a.Nc * kD;
+  const uint16_t* pkb = HEADS ? kb : reinterpret_cast<const uint16_t*>(a.pk) + (int64_t)kvh * a.Nc * kD;
+  const uint16_t* pvb = HEADS ? vb : reinterpret_cast<const uint16_t*>(a.pv) + (int64_t)kvh * a.Nc * kD;
   // head-split: position of sequence entry e (e < T)
   auto pos = [&](int e) __attribute__((always_inline)) -> int { return e < A ? e : lo + (e - A); };
   // the row byte offset of sequence entry e: staged in LDS, or (head-split)
@@ -511,6 +515,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
 
 hipError_t launch_prefill(const PrefillArgs& a, int d, hipStream_t s) {
   if (d != kD || a.q_block != 128 || a.K > kListMax) return hipErrorInvalidValue;
+  if (a.G < 1 || a.H != a.Hkv * a.G || (a.G > 1 && a.Nc > 0)) return hipErrorInvalidValue;
   if (a.N >= kMaxRows || a.Nc >= kMaxRows) return hipErrorInvalidValue;
   const int nh = a.B * a.H;
   const int hpx = (nh + 7) / 8;

@@ -120,10 +120,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   __shared__ uint64_t s_wtop[kRouteThreads / 64][64];
   __shared__ int s_groups[kMaxRoutedGroups];
   __shared__ int s_rowmap[kMaxRoutedGroups];
-  const int gi = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  // decode: one row per (group, sequence); prefill: one per (query block,
+  // group, sequence), the block's last position taking the query's place
+  const int blk = blockIdx.x, gi = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int g = a.groups.ids[gi];
   const int n = a.n, C = a.chunk, GR = a.group, gpc = C / GR;
-  const int t = n - 1, kappa = t / C;
+  const int t = a.prefill ? min(n, (blk + 1) * C) - 1 : n - 1;
+  const int kappa = t / C;
   const int c_lo = a.sink_chunks;
   const int c_hi = max(c_lo, kappa - a.local_chunks);
   const int ncand = c_hi - c_lo;
@@ -134,7 +137,42 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   // summary rows' loads: no barrier in between)
   constexpr int EPL = D / 16;
   float qv[EPL];
-  {
+  if (a.prefill) {
+    // the block's chunk-level query: the sum of its G x nq query rows
+    // (ranking by a positive multiple of the mean is ranking by the mean);
+    // thread (row slot tid / 16, sub) sums every 64th row, the four row
+    // slots of a wave are added by lane swaps, the 16 waves through LDS
+    const int sub = tid & 15, slot = tid >> 4;
+    const int q0 = blk * C, nq = t + 1 - q0, rows = a.G * nq;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qv[e] = 0.f;
+    for (int r = slot; r < rows; r += kRouteThreads / 16) {
+      const int h = r / nq, i = r - h * nq;
+      float x[EPL];
+      VecLoad<T, EPL>::run(a.q, (((int64_t)b * a.Hq + g * a.G + h) * a.n + q0 + i) * D + sub * EPL, x);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qv[e] += x[e];
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      qv[e] += __shfl_xor(qv[e], 16);
+      qv[e] += __shfl_xor(qv[e], 32);
+    }
+    float (*part)[D] = reinterpret_cast<float (*)[D]>(&s_wtop[0][0]);   // [16][D]: 8 KB at D = 128
+    const int lane = tid & 63, wid = tid >> 6;
+    if (lane < 16) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) part[wid][sub * EPL + e] = qv[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float x = 0.f;
+      for (int w = 0; w < kRouteThreads / 64; ++w) x += part[w][sub * EPL + e];
+      qv[e] = x;
+    }
+    __syncthreads();
+  } else {
     const int sub = tid & 15;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qv[e] = 0.f;
@@ -250,13 +288,18 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   const int n_local = max(0, kappa - loc_lo) * C;
   const int cur0 = kappa * C;
   const int o_routed = sinks_end, o_local = o_routed + n_routed, o_cur = o_local + n_local;
-  const int total = o_cur + (n - cur0);
-  int32_t* out = a.sel_idx + bg * a.n_cap;
+  // prefill lists stop before the block: its queries add their own keys
+  const int n_cur = a.prefill ? 0 : (n - cur0);
+  const int total = o_cur + n_cur;
+  int32_t* out = a.prefill ? a.blk_idx + ((int64_t)bg * a.nblk + blk) * a.K : a.sel_idx + bg * a.n_cap;
   for (int i = tid; i < sinks_end; i += kRouteThreads) out[i] = i;
   for (int i = tid; i < n_routed; i += kRouteThreads) out[o_routed + i] = s_groups[i / GR] * GR + (i % GR);
   for (int i = tid; i < n_local; i += kRouteThreads) out[o_local + i] = loc_lo * C + i;
-  for (int i = tid; i < n - cur0; i += kRouteThreads) out[o_cur + i] = cur0 + i;
-  if (tid == 0) a.sel_count[bg] = total;
+  for (int i = tid; i < n_cur; i += kRouteThreads) out[o_cur + i] = cur0 + i;
+  if (tid == 0) {
+    if (a.prefill) a.blk_count[bg * a.nblk + blk] = total;
+    else a.sel_count[bg] = total;
+  }
 }
 
 hipError_t launch_route(const RouteArgs& a, int dtype, int d, hipStream_t s) {
@@ -267,7 +310,8 @@ hipError_t launch_route(const RouteArgs& a, int dtype, int d, hipStream_t s) {
   const int ncand_max = a.n / a.chunk + 1;
   if (ncand_max > 16384) return hipErrorInvalidValue;
   const size_t dyn = 4 * (size_t)std::max(ncand_max, a.top_chunks * gpc);
-  dim3 grid(a.groups.n, a.B), block(kRouteThreads);
+  if (a.prefill && (d > 128 || a.nblk < 1)) return hipErrorInvalidValue;
+  dim3 grid(a.prefill ? a.nblk : 1, a.groups.n, a.B), block(kRouteThreads);
   if (dtype == 0 && d == 128) hipLaunchKernelGGL((route_kernel<bf16_t, 128>), grid, block, dyn, s, a);
   else if (dtype == 0 && d == 64) hipLaunchKernelGGL((route_kernel<bf16_t, 64>), grid, block, dyn, s, a);
   else if (dtype == 1 && d == 128) hipLaunchKernelGGL((route_kernel<float, 128>), grid, block, dyn, s, a);

@@ -284,3 +284,27 @@ def test_prefill_heads_validation():
     mb = _full_bufs()
     mb.q = FAKE + 8
     assert _prefill_heads(_decode_params(**ok), mb) == sa.SA_ERR_INVALID_ARG
+
+
+def test_route_prefill_validation():
+    b = _full_bufs()
+    base = dict(n_ctx=128 * 40, head_kind=[2] * 8, chunk=128, group=32, top_chunks=4,
+                top_groups=2, sink_chunks=2, local_chunks=3, levels=1, q_block=128)
+    need = (2 + 3) * 128 + 4 * 2 * 32
+    st, _ = _select(_decode_params(**base, block_top_k=need), b, sa.SEL_ROUTE2_PREFILL)
+    assert st == sa.SA_OK
+    assert _select(_decode_params(**base, block_top_k=need - 1), b,
+                   sa.SEL_ROUTE2_PREFILL)[0] == sa.SA_ERR_CAPACITY
+    bad_chunk = dict(base, chunk=64, group=16)
+    assert _select(_decode_params(**bad_chunk, block_top_k=need), b,
+                   sa.SEL_ROUTE2_PREFILL)[0] == sa.SA_ERR_UNSUPPORTED
+    assert _select(_decode_params(**base, block_top_k=need, per_head_sets=True), b,
+                   sa.SEL_ROUTE2_PREFILL)[0] == sa.SA_ERR_UNSUPPORTED
+    # a GQA prefill over lists is allowed with one level only
+    n = ctypes.c_size_t(0)
+    p1 = _decode_params(**base, block_top_k=need)
+    assert sa.raw_call("prefill_chunked", ctypes.byref(p1), ctypes.byref(b), None,
+                       ctypes.byref(n), None) == sa.SA_OK
+    p3 = _decode_params(**dict(base, levels=3, factor=4), block_top_k=need)
+    assert sa.raw_call("prefill_chunked", ctypes.byref(p3), ctypes.byref(b), None,
+                       ctypes.byref(n), None) == sa.SA_ERR_INVALID_ARG

@@ -126,6 +126,12 @@ HGA_64K = DecodeConfig(
 LLAMA_PREFILL_32K = LLAMA_32K.with_(name="llama3_8b_head_split_prefill_32k", batch=1,
                                     needles_per_head=0)
 
+# routed chunked prefill of the 64K routed layer's heads (one sequence): a
+# query block is one chunk of 128 tokens (4 groups of 32), the routing
+# budget as in the routed decode workload
+HGA_PREFILL_64K = HGA_64K.with_(name="hga_route_prefill_64k", batch=1, chunk=128, group=32,
+                                needles_per_head=0)
+
 PYRAMID_128K = PrefillConfig(
     name="pyramid_prefill_128k", batch=1, n_heads=16, head_dim=128,
     n_ctx=131072)
@@ -356,8 +362,22 @@ def head_prefill_inputs(cfg: DecodeConfig, seed: int, device="cpu",
     k = _quant(apply_rope(k_pre[:, :, :n], pos, cfg.rope_base), cfg.dtype)
     k_cache = torch.zeros_like(k_pre)
     k_cache[:, :, :n] = k
-    return dict(q=q, k_cache=k_cache, v_cache=v, n_cap=cap,
+    return dict(q=q, k_pre=k_pre, k_cache=k_cache, v_cache=v, n_cap=cap,
                 head_kind=torch.tensor(cfg.head_kind(), dtype=torch.int8))
+
+
+def lattice_prefill_route_inputs(cfg: DecodeConfig, seed: int, amp: int = 16, q_amp: int = 4,
+                                 device="cpu") -> dict:
+    """Exact-arithmetic inputs for routing during prefill: chunk/group
+    summaries in (1/8)Z with |x| <= amp/8 and prefill queries q [B,Hq,n,d] in
+    (1/8)Z with |x| <= q_amp/8, written straight into the buffers."""
+    B, Hq, Hkv, d, n = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_ctx
+    g = _gen(seed, device, 14)
+    nc, ng = n // cfg.chunk, n // cfg.group
+    cs = torch.randint(-amp, amp + 1, (B, Hkv, nc, d), generator=g, device=device).float() / 8
+    gs = torch.randint(-amp, amp + 1, (B, Hkv, ng, d), generator=g, device=device).float() / 8
+    q = torch.randint(-q_amp, q_amp + 1, (B, Hq, n, d), generator=g, device=device).float() / 8
+    return dict(chunk_sum=cs, group_sum=gs, q=q)
 
 
 def to_device_dtype(x: torch.Tensor, dtype: str, device) -> torch.Tensor:
