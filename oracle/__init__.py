@@ -20,6 +20,9 @@ Sources (web summaries of five papers; cited by page title and section):
   dense attention on the gathered subsequence and scatter back.
 * "Autonomia de Cabecas (AoH)" summary - Methodology item 4: head scores are
   averaged to the GQA group; sinks plus a recent window for streaming heads.
+* "S2O" summary - Methodology 2-3: candidates visited in descending
+  estimated importance after a dense first pass, stopping on the marginal
+  gain of attention mass (monotone-gain early stop).
 * Head-split prefill (RTPurbo, Methodology item 1): local heads window their
   prefill, retrieval heads attend densely; per-query-head selection as the
   group rule applied to a group of one head.
@@ -47,5 +50,6 @@ from .lighthouse import (pyramid_levels, pyramid_scores, visible_entries,
                          block_select, prefill_block, prefill)
 from .decode import decode_step, decode_token_sets, decode_token_sets_per_head
 from .prefill_heads import prefill_visible, head_prefill_rows, visible_pairs
+from .s2o import s2o_order, s2o_head
 
 __all__ = [n for n in dir() if not n.startswith("_")]

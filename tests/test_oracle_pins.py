@@ -747,3 +747,65 @@ def test_hga_prefill_rows_are_attention_over_list_and_causal_block():
     for r, i in enumerate(rows):
         T = np.r_[lst, blk * chunk:i + 1]
         np.testing.assert_allclose(out[r], sdpa64(q[0, i], K[T], V[T])[0], atol=1e-12)
+
+
+# --------------------------------------------------------------- S2O early stop
+def test_s2o_order_brute_force():
+    rng = np.random.default_rng(40)
+    lg = rng.integers(-3, 4, 50).astype(np.float64)       # many ties
+    cand = rng.choice(50, 30, replace=False)
+    got = oracle.s2o_order(lg, cand)
+    assert got.tolist() == sorted(cand.tolist(), key=lambda j: (-lg[j], j))
+
+
+def _s2o_case(seed, n=700, d=16):
+    rng = np.random.default_rng(seed)
+    q, K, V = rng.standard_normal(d), rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    init = np.r_[0:4, n - 32:n]
+    order = rng.permutation(n - 36) + 4                     # every non-init token, shuffled
+    return q, K, V, init, order
+
+
+def test_s2o_tau_zero_keeps_everything():
+    q, K, V, init, order = _s2o_case(41)
+    o, nb = oracle.s2o_head(q, K, V, init, order, 0.0)
+    assert nb == -(-len(order) // 64)
+    ref = sdpa64(q, K, V)[0]                                 # init + all candidates = every token
+    np.testing.assert_allclose(o, ref, atol=1e-12)
+
+
+def test_s2o_huge_tau_keeps_one_block():
+    q, K, V, init, order = _s2o_case(42)
+    o, nb = oracle.s2o_head(q, K, V, init, order, 1e30)
+    assert nb == 1
+    T = np.r_[init, order[:64]]
+    np.testing.assert_allclose(o, sdpa64(q, K[T], V[T])[0], atol=1e-12)
+
+
+def test_s2o_stop_hand_case():
+    # scale 1, q = e0, scores set on dim 0: the first pass is one token of
+    # score 0 (mass 1); blocks of 64 equal scores x_i add 64 e^{x_i}:
+    #   block 0: x = 0              -> gain 64 / 1          = 64   (go on, mass 65)
+    #   block 1: x = ln(65/128)     -> gain 32.5 / 65       = 0.5  (go on, mass 97.5)
+    #   block 2: x = ln(97.5/320)   -> gain 19.5 / 97.5     = 0.2  (< 0.3: stop, kept)
+    #   block 3: never visited
+    d = 4
+    xs = [0.0, math.log(65 / 128), math.log(97.5 / 320), 5.0]
+    K = np.zeros((1 + 64 * 4, d))
+    V = np.zeros((1 + 64 * 4, d))
+    for i, x in enumerate(xs):
+        K[1 + 64 * i:1 + 64 * (i + 1), 0] = x
+        V[1 + 64 * i:1 + 64 * (i + 1), 1] = i + 1
+    q = np.eye(d)[0]
+    order = np.arange(1, 1 + 64 * 4)
+    o, nb = oracle.s2o_head(q, K, V, np.array([0]), order, 0.3, scale=1.0)
+    assert nb == 3
+    # weights: init 1, block masses 64, 32.5, 19.5 (total 117)
+    expect = (64 * 1 + 32.5 * 2 + 19.5 * 3) / 117.0
+    np.testing.assert_allclose(o, [0.0, expect, 0.0, 0.0], atol=1e-12)
+
+
+def test_s2o_blocks_shrink_as_tau_grows():
+    q, K, V, init, order = _s2o_case(43)
+    nbs = [oracle.s2o_head(q, K, V, init, order, tau)[1] for tau in (0.0, 1e-4, 1e-3, 1e-2, 0.1, 1.0)]
+    assert all(a >= b for a, b in zip(nbs, nbs[1:])) and nbs[0] > nbs[-1]
