@@ -40,6 +40,7 @@ def parse():
     ap.add_argument("--workload", default="llama3_8b_decode_32k",
                     choices=["llama3_8b_decode_32k", "llama3_8b_decode_128k",
                              "llama3_8b_decode_128k_topk", "hga_route_decode_64k",
+                             "llama3_8b_decode_32k_s2o",
                              "pyramid_prefill_128k", "llama3_8b_head_split_prefill_32k",
                              "hga_route_prefill_64k"])
     ap.add_argument("--instances", type=int, default=4,
@@ -124,7 +125,8 @@ class DecodeInstance:
         else:
             sa.index_build(self.params, self.bufs, sa.IDX_LOWRANK, 0, n)
         self.sel_mode = (sa.SEL_ROUTE2 if cfg.routed else
-                         (sa.SEL_TOPK if cfg.top_k > 0 else sa.SEL_TOPP))
+                         (sa.SEL_TOPK_BY_SCORE if cfg.s2o_tau > 0 else
+                          (sa.SEL_TOPK if cfg.top_k > 0 else sa.SEL_TOPP)))
 
     def index_and_select(self):
         sa, cfg = self.sa, self.cfg
@@ -209,6 +211,7 @@ DECODE_CONFIGS = {
     "llama3_8b_decode_128k": "LLAMA_128K",
     "llama3_8b_decode_128k_topk": "LLAMA_128K_TOPK",
     "hga_route_decode_64k": "HGA_64K",
+    "llama3_8b_decode_32k_s2o": "LLAMA_32K_S2O",
 }
 
 
@@ -352,7 +355,7 @@ def run_decode(args, torch, sa, workloads, workload=None, steps=None, warmup=Non
                    "top_k": cfg.top_k or None, "min_tokens": cfg.min_tokens,
                    "sinks": cfg.sinks, "window": cfg.window, "routed": cfg.routed,
                    "instances_rotated": len(insts), "alpha": alpha,
-                   "per_head_sets": per_head,
+                   "per_head_sets": per_head, "s2o_tau": cfg.s2o_tau or None,
                    "touched_gib_per_rotation": len(insts) * step_b / 2**30,
                    "launch": "hip_graph" if args.graph else "eager"},
         "step_hbm_gbps": step_b / t_step / 1e9,
@@ -375,6 +378,13 @@ def run_decode(args, torch, sa, workloads, workload=None, steps=None, warmup=Non
                      "bytes_per_launch": attn_b, "launch_us": t_kernel * 1e6,
                      "source_sha": sha},
     }
+    if cfg.s2o_tau > 0:
+        # the early stop reads a data-dependent share of each group's
+        # candidates (the kernel does not report how many): no byte count
+        for k in ("roofline", "step_roofline", "step_hbm_gbps", "step_bytes"):
+            res.pop(k, None)
+        res["note"] = ("retrieval groups: top-k candidates in index-score order, early stop at "
+                       f"tau {cfg.s2o_tau}; bytes read depend on the stop and are not reported")
     if cpu and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_decode(cfg, insts[0], args.cpu_seconds, torch)
     del insts
@@ -462,7 +472,7 @@ def _oracle_decode_sample(cfg, inst, budget_s, torch):
 def compact(r):
     keep = ("value", "unit", "ms_per_step", "step_hbm_gbps", "step_roofline",
             "selected_frac_mean", "config", "roofline", "step_tflops", "spread_us",
-            "all_dense_ms", "speedup_vs_all_dense")
+            "all_dense_ms", "speedup_vs_all_dense", "note")
     return {k: r[k] for k in keep if k in r}
 
 
@@ -495,6 +505,10 @@ def main():
         for w in ("llama3_8b_decode_128k_topk", "llama3_8b_decode_128k", "hga_route_decode_64k"):
             other[w] = compact(run_decode(args, torch, sa, workloads, workload=w, steps=20,
                                           warmup=3, instances=4, cpu=False))
+        # the 32K step with the early stop over the top-2048 candidates
+        other["llama3_8b_decode_32k_s2o"] = compact(run_decode(
+            args, torch, sa, workloads, workload="llama3_8b_decode_32k_s2o", steps=20, warmup=3,
+            instances=4, cpu=False))
         # the 32K step with one set per query head (no GQA sharing of sets)
         other["llama3_8b_decode_32k_per_head"] = compact(run_decode(
             args, torch, sa, workloads, workload="llama3_8b_decode_32k", steps=20, warmup=3,

@@ -100,7 +100,8 @@ typedef enum {
   SA_SEL_TOPK = 1,          /* retrieval groups: fixed top_k                  */
   SA_SEL_ROUTE2 = 2,        /* routed groups: chunk then group routing        */
   SA_SEL_PYRAMID_TOPK = 3,  /* per query block: joint top-K over levels       */
-  SA_SEL_ROUTE2_PREFILL = 4 /* routed groups, prefill: per query block (chunk) */
+  SA_SEL_ROUTE2_PREFILL = 4,/* routed groups, prefill: per query block (chunk) */
+  SA_SEL_TOPK_BY_SCORE = 5  /* retrieval groups: top_k, listed by index score   */
 } sa_select_mode;
 
 /* Host struct, read only during the call. */
@@ -132,6 +133,8 @@ typedef struct sa_params {
   int32_t block_top_k;  /* pyramid: K entries per block                        */
   int32_t per_head_sets;/* 0: one set per KV group, shared by its G query heads;
                          * 1: one set per query head (see below)               */
+  float s2o_tau;        /* decode: > 0 turns on the monotone-gain early stop of
+                         * retrieval groups (see sparse_attn_decode); 0: off   */
 } sa_params;
 
 /*
@@ -221,6 +224,11 @@ int32_t sparse_attn_index_build(const sa_params* params, const sa_buffers* bufs,
  *   is the union of sink chunks, local chunks, tokens kappa*chunk .. t, and
  *   the routed groups, ascending.  Needs n_cap >= the list length;
  *   top_chunks <= 64 and chunk / group <= 64 (SA_ERR_UNSUPPORTED otherwise).
+ * SA_SEL_TOPK_BY_SCORE ("S2O" summary, Methodology 1-2: candidates visited in
+ *   descending estimated importance): the SA_SEL_TOPK set, written to sel_idx
+ *   in (logit desc, position asc) order instead of ascending - the visit
+ *   order of the early-stop decode.  Needs top_k <= 8192
+ *   (SA_ERR_UNSUPPORTED).
  * SA_SEL_ROUTE2_PREFILL (HGA summary, Core mechanism items 1-2, routing
  *   while prefilling): for each routed group and every query block of
  *   chunk = 128 queries (block beta holds positions 128 beta .. t, t its last
@@ -257,7 +265,15 @@ int32_t sparse_attn_select(const sa_params* params, const sa_buffers* bufs,
  * pi = softmax(q[b,h] . k_j / sqrt(d)) over that set, accumulated in fp32.
  * The GQA heads of a group share every gathered key/value row.  With
  * per_head_sets, head h sees sel_idx[b,h,0:sel_count[b,h]] (local heads as
- * above) over the rows of KV group h / G.  Reads q,
+ * above) over the rows of KV group h / G.
+ * With s2o_tau > 0 ("S2O" summary, Methodology 2-3: monotone-gain early
+ * stop), retrieval groups instead read sel_idx as candidates in visit order
+ * (SA_SEL_TOPK_BY_SCORE; at most 8192 are read): each head attends first
+ * over the local rule's tokens (sinks + window), then over the candidates
+ * outside them in blocks of 64 in list order, and after each block stops
+ * when the block's attention mass falls below s2o_tau times the mass
+ * attended before it (that block is kept).  Needs dtype bf16 and sinks +
+ * window >= 1.  Reads q,
  * k_cache, v_cache, sel_idx, sel_count; writes out.  A selecting group whose
  * sel_count is negative (a selection that reported failure) gets NaN in
  * every output of its query heads.  Needs a workspace; no part of it has to

@@ -32,11 +32,13 @@ def s2o_order(logits, candidates):
     return candidates[np.lexsort((candidates, -lg))]
 
 
-def s2o_head(q, K, V, init, ordered, tau, block=BLOCK, scale=None):
+def s2o_head(q, K, V, init, ordered, tau, block=BLOCK, scale=None, gains=None):
     """One query head: output [d] and the number of candidate blocks kept.
 
     init: positions of the first pass; ordered: the visit order of the
-    candidates (those in init are skipped)."""
+    candidates (those in init are skipped).  ``gains``: a list that receives
+    each visited block's S_block / S_before (the quantity compared with tau),
+    so that tests can keep clear of the threshold."""
     q = np.asarray(q, np.float64)
     K = np.asarray(K, np.float64)
     V = np.asarray(V, np.float64)
@@ -56,6 +58,8 @@ def s2o_head(q, K, V, init, ordered, tau, block=BLOCK, scale=None):
         S_blk = np.sum(np.exp((K[blk] @ q) * scale - ref))
         kept.append(blk)
         nb += 1
+        if gains is not None:
+            gains.append(S_blk / S_before)
         if S_before > 0 and S_blk / S_before < tau:
             break
         S_before += S_blk

@@ -29,7 +29,7 @@ SA_ERR_WORKSPACE, SA_ERR_CAPACITY, SA_ERR_HIP = -3, -4, -5
 SA_BF16, SA_FP32 = 0, 1
 HEAD_LOCAL, HEAD_RETRIEVAL, HEAD_ROUTED = 0, 1, 2
 IDX_LOWRANK, IDX_CHUNK_SUMMARY, IDX_PYRAMID = 0, 1, 2
-SEL_TOPP, SEL_TOPK, SEL_ROUTE2, SEL_PYRAMID_TOPK, SEL_ROUTE2_PREFILL = 0, 1, 2, 3, 4
+SEL_TOPP, SEL_TOPK, SEL_ROUTE2, SEL_PYRAMID_TOPK, SEL_ROUTE2_PREFILL, SEL_TOPK_BY_SCORE = 0, 1, 2, 3, 4, 5
 
 EXPORTED = ("sparse_attn_index_build", "sparse_attn_select", "sparse_attn_decode",
             "sparse_attn_decode_noalloc", "sparse_attn_prefill_chunked",
@@ -52,6 +52,7 @@ class Params(ctypes.Structure):
         ("local_chunks", ctypes.c_int32), ("levels", ctypes.c_int32),
         ("factor", ctypes.c_int32), ("q_block", ctypes.c_int32),
         ("block_top_k", ctypes.c_int32), ("per_head_sets", ctypes.c_int32),
+        ("s2o_tau", ctypes.c_float),
     ]
 
 
@@ -108,7 +109,7 @@ def make_params(*, batch, n_q_heads, n_kv_heads, head_dim, n_ctx, n_cap=None, dt
                 head_kind=None, rope_base=10000.0, r=16, top_p=1.0, top_k=0, min_tokens=0,
                 sinks=0, window=0, chunk=64, group=16, top_chunks=16, top_groups=2,
                 sink_chunks=4, local_chunks=8, levels=1, factor=4, q_block=128,
-                block_top_k=0, per_head_sets=False) -> Params:
+                block_top_k=0, per_head_sets=False, s2o_tau=0.0) -> Params:
     """Fill a Params struct.  ``head_kind`` is a per-query-head sequence."""
     p = Params()
     p.batch, p.n_q_heads, p.n_kv_heads, p.head_dim = batch, n_q_heads, n_kv_heads, head_dim
@@ -125,6 +126,7 @@ def make_params(*, batch, n_q_heads, n_kv_heads, head_dim, n_ctx, n_cap=None, dt
     p.sink_chunks, p.local_chunks = sink_chunks, local_chunks
     p.levels, p.factor, p.q_block, p.block_top_k = levels, factor, q_block, block_top_k
     p.per_head_sets = int(per_head_sets)
+    p.s2o_tau = float(s2o_tau)
     return p
 
 
@@ -142,7 +144,8 @@ def params_from_config(cfg, n_cap=None) -> Params:
                        top_p=cfg.top_p, top_k=cfg.top_k, min_tokens=cfg.min_tokens,
                        sinks=cfg.sinks, window=cfg.window, chunk=cfg.chunk, group=cfg.group,
                        top_chunks=cfg.top_chunks, top_groups=cfg.top_groups,
-                       sink_chunks=cfg.sink_chunks, local_chunks=cfg.local_chunks)
+                       sink_chunks=cfg.sink_chunks, local_chunks=cfg.local_chunks,
+                       s2o_tau=getattr(cfg, "s2o_tau", 0.0))
 
 
 def make_buffers(**tensors) -> Buffers:

@@ -229,13 +229,18 @@ int32_t decode_entry(const sa_params* p, const sa_buffers* b, void* ws, size_t* 
   const int G = u.G;
   if (G != 1 && G != 2 && G != 4 && G != 8) return SA_ERR_UNSUPPORTED;
   bool any_local = false, any_list = false;
-  uint64_t local_mask = 0;
+  uint64_t local_mask = 0, s2o_mask = 0;
+  const bool s2o = p->s2o_tau > 0.f;
+  if (std::isnan(p->s2o_tau) || p->s2o_tau < 0.f) return SA_ERR_INVALID_ARG;
+  GroupList s2o_units{};
   for (int g = 0; g < u.n; ++g) {
     if (u.kind[g] == SA_HEAD_LOCAL) { any_local = true; local_mask |= 1ull << g; }
     else any_list = true;
+    if (s2o && u.kind[g] == SA_HEAD_RETRIEVAL) { s2o_mask |= 1ull << g; s2o_units.ids[s2o_units.n++] = g; }
   }
-  if (any_local && (p->sinks < 0 || p->window < 0 || (int64_t)p->sinks + p->window < 1))
+  if ((any_local || s2o_mask) && (p->sinks < 0 || p->window < 0 || (int64_t)p->sinks + p->window < 1))
     return SA_ERR_INVALID_ARG;
+  if (s2o_mask && p->dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
   int tps = kDecodeTps, max_splits, target_items = 0;
   size_t n_partial;
   if (p->dtype == SA_BF16) {
@@ -272,7 +277,13 @@ int32_t decode_entry(const sa_params* p, const sa_buffers* b, void* ws, size_t* 
   a.target_items = target_items;
   a.min_chunk = kDecodeMinChunk;
   a.plan = plan;
-  return hip_status(sa::launch_decode(a, p->dtype, p->head_dim, static_cast<hipStream_t>(stream)));
+  a.skip_mask = s2o_mask;
+  a.s2o_tau = p->s2o_tau;
+  a.s2o = s2o_units;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = hip_status(sa::launch_decode(a, p->dtype, p->head_dim, hs)))) return st;
+  if (!s2o_mask) return SA_OK;
+  return hip_status(sa::launch_decode_s2o(a, p->head_dim, hs));
 }
 
 }  // namespace sa
@@ -405,8 +416,11 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
   }
   SelGroups u;
   if ((st = sel_groups(p, &u))) return st;
-  if (mode == SA_SEL_TOPP || mode == SA_SEL_TOPK) {
+  if (mode == SA_SEL_TOPP || mode == SA_SEL_TOPK || mode == SA_SEL_TOPK_BY_SCORE) {
+    const bool by_score = mode == SA_SEL_TOPK_BY_SCORE;
+    if (by_score) mode = SA_SEL_TOPK;
     if (p->r != 16) return SA_ERR_UNSUPPORTED;
+    if (by_score && p->top_k > sa::kS2oMax) return SA_ERR_UNSUPPORTED;
     if (mode == SA_SEL_TOPP && (!(p->top_p > 0.f) || std::isnan(p->top_p) || p->min_tokens < 0))
       return SA_ERR_INVALID_ARG;
     if (mode == SA_SEL_TOPK && p->top_k < 1) return SA_ERR_INVALID_ARG;
@@ -453,7 +467,9 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
     a.hist_c = sw.hist_c; a.hist_m = sw.hist_m; a.ctl = sw.ctl; a.slot_a = sw.slot_a; a.slot_b = sw.slot_b;
     a.cand = sw.cand; a.cand_stride = cand_stride;
     a.groups = gl;
-    return hip_status(sa::launch_select_lowrank(a, p->dtype, per, s));
+    if ((st = hip_status(sa::launch_select_lowrank(a, p->dtype, per, s)))) return st;
+    if (!by_score) return SA_OK;
+    return hip_status(sa::launch_select_order(a, p->dtype, s));
   }
   if (mode == SA_SEL_ROUTE2_PREFILL) {
     if (p->chunk < 1 || p->group < 1 || p->chunk % p->group) return SA_ERR_INVALID_ARG;

@@ -139,7 +139,15 @@ struct DecodeArgs {
   int32_t target_items;   // bf16 path: work items the visible tokens are spread over
   int32_t min_chunk;      // bf16 path: smallest item (list entries)
   int2* plan;             // bf16 path: per group (first item, item count) [B*Hkv]
+  // monotone-gain early stop: the groups in `s2o` read their lists in visit
+  // order and are left to the early-stop kernel (bit g of skip_mask set: the
+  // split kernels give group g no work and write none of its outputs)
+  uint64_t skip_mask;
+  float s2o_tau;
+  GroupList s2o;
 };
+
+constexpr int kS2oMax = 8192;     // candidates per group the early-stop kernel stages
 
 constexpr int kMaxPrefillHeads = 128;
 
@@ -168,6 +176,8 @@ hipError_t launch_route(const RouteArgs& a, int dtype, int d, hipStream_t s);
 hipError_t launch_pyramid_select(const PyrSelectArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int d, hipStream_t s);
+hipError_t launch_decode_s2o(const DecodeArgs& a, int d, hipStream_t s);
+hipError_t launch_select_order(const SelectArgs& a, int dtype, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int d, hipStream_t s);
 hipError_t launch_prefill_heads(const PrefillArgs& a, int d, hipStream_t s);
 

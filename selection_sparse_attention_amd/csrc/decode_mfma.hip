@@ -70,6 +70,7 @@ __device__ __forceinline__ float row16_sum(float v) {
 // ---------------------------------------------------------------- work plan
 __device__ __forceinline__ int group_count(const DecodeArgs& a, int bg) {
   const int g = bg % a.Hkv;
+  if ((a.skip_mask >> g) & 1ull) return 0;
   if ((a.local_mask >> g) & 1ull) {
     const int s = min(a.sinks, a.n);
     return s + (a.n - max(s, a.n - a.window));
@@ -421,6 +422,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_item_combine_kernel(Decod
   const int bgh = blockIdx.x;
   const int bg = bgh / G, h = bgh - bg * G;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  if ((a.skip_mask >> g) & 1ull) return;       // written by the early-stop kernel
   const int2 fr = a.plan[bg];
   const int first = fr.x, ns = fr.y;
   const int tid = threadIdx.x, e = tid % D, part = tid / D;
@@ -513,6 +515,293 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int d, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
 #undef SA_CMB
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- early stop
+// Monotone-gain early stop ("S2O" summary, Methodology 2-3) for the groups in
+// a.s2o, whose lists hold their top-k candidates in visit order (index logit
+// descending).  One workgroup per (group, sequence), the group's G heads in
+// one MFMA tile as above:
+//   * first pass: the local rule's tokens (sinks + window), in blocks of 64;
+//   * the candidates outside the first pass, staged in LDS in visit order
+//     (each wave compacts a quarter of the list with ballots), in blocks of
+//     64 = one 16-token tile per wave;
+//   * after each candidate block, per head: the block's mass S_blk and the
+//     mass attended before it S_before, both from the four waves' (max, sum)
+//     pairs exchanged through LDS (double-buffered: one barrier per block);
+//     the head stops when S_blk < tau * S_before (the block is kept);
+//     stopped heads take no more tokens, and the group ends when every head
+//     has stopped;
+//   * the next block's rows are requested before the current block is
+//     scored, so a stop costs one block of loads.
+// Outputs go straight to `out` (the whole group is one workgroup).
+template <int D, int G>
+__global__ __launch_bounds__(kMfmaThreads) void decode_s2o_kernel(DecodeArgs a) {
+  using TL = Tile<D>;
+  constexpr int KS = TL::KS, NCLS = TL::NCLS, VT = TL::VT;
+  static_assert(G <= 8, "at most 8 query heads per KV group");
+  __shared__ DecodeShared<D, G> sh;
+  __shared__ int s_visit[kS2oMax];
+  __shared__ float s_tm[2][4][8], s_ts[2][4][8], s_m[2][4][8], s_l[2][4][8];
+  __shared__ int s_cnt[4];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int b = blockIdx.y, g = a.s2o.ids[blockIdx.x];
+  const int bg = b * a.Hkv + g;
+  const int n = a.n;
+  const int s_eff = min(a.sinks, n), wst = max(s_eff, n - a.window);
+  const int c0 = s_eff + (n - wst);                         // first-pass tokens
+  const int raw_count = a.sel_count[bg];
+  const int count = min(max(raw_count, 0), min(n, kS2oMax));
+  const int64_t row0 = (int64_t)bg * a.n_cap;
+  const int64_t kv0 = (int64_t)(bg / a.kv_div) * a.n_cap;
+
+  // ---- the visit list: candidates outside the first pass, in list order
+  {
+    const int Q = (count + 3) / 4;
+    const int lo = min(count, wid * Q), hi = min(count, lo + Q);
+    int kept = 0;
+    for (int base = lo; base < hi; base += 64) {
+      const int e = base + lane;
+      const int j = (e < hi) ? a.sel_idx[row0 + e] : -1;
+      const bool keep = e < hi && (unsigned)j < (unsigned)n && !(j < s_eff || j >= wst);
+      kept += __popcll(__ballot(keep));
+    }
+    if (lane == 0) s_cnt[wid] = kept;
+    __syncthreads();
+    int run = 0;
+    for (int w = 0; w < wid; ++w) run += s_cnt[w];
+    for (int base = lo; base < hi; base += 64) {
+      const int e = base + lane;
+      const int j = (e < hi) ? a.sel_idx[row0 + e] : -1;
+      const bool keep = e < hi && (unsigned)j < (unsigned)n && !(j < s_eff || j >= wst);
+      const uint64_t bal = __ballot(keep);
+      if (keep) s_visit[run + __popcll(bal & ((1ull << lane) - 1ull))] = j;
+      run += __popcll(bal);
+    }
+  }
+  __syncthreads();
+  const int nv = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+  const int nb0 = (c0 + 63) / 64, nbt = nb0 + (nv + 63) / 64;
+
+  // query fragment: head (lane % 16), this lane's slice of the k mapping
+  bf16x8 qf[KS];
+  {
+    const int h = lane & 15, jq = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (h < G) {
+        const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                             ((int64_t)b * a.Hq + g * G + h) * D + 32 * s + 8 * jq;
+        w = *reinterpret_cast<const u32x4*>(qp);
+      }
+      qf[s] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  const int kt = lane & 15, jg = lane >> 4;
+  const int vd = 2 * (lane % (D / 2)), vc = lane / (D / 2);
+  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + kv0 * D + 8 * jg;
+  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v) + kv0 * D;
+  // token of this lane in block blk (this wave's tile of it), -1 if none
+  auto token = [&](int blk) __attribute__((always_inline)) -> int {
+    const int e = 64 * blk + 16 * wid + kt;
+    if (blk < nb0) return (e < c0) ? ((e < s_eff) ? e : wst + (e - s_eff)) : -1;
+    const int ev = e - 64 * nb0;
+    return (ev < nv) ? s_visit[ev] : -1;
+  };
+  auto issue = [&](int blk, TL& t) __attribute__((always_inline)) {
+    const int tok = (blk < nbt) ? token(blk) : -1;
+    t.tok = tok;
+    const uint16_t* kp = kbase + (int64_t)max(tok, 0) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      t.k[s] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 32 * s)));
+#pragma unroll
+    for (int r = 0; r < VT; ++r) {
+      int tv = __builtin_amdgcn_readlane(tok, r * NCLS);
+      if (NCLS == 2) {
+        const int tv1 = __builtin_amdgcn_readlane(tok, r * NCLS + 1);
+        tv = vc ? tv1 : tv;
+      }
+      const uint16_t* vrow = vbase + (int64_t)max(tv, 0) * D;
+      t.v[r] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vrow + vd));
+    }
+  };
+
+  float m[G], lsum[4], acc[G][2];
+  bool active[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) { m[h] = -INFINITY; acc[h][0] = 0.f; acc[h][1] = 0.f; active[h] = true; }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lsum[i] = 0.f;
+  const float sc = a.scale_log2;
+  const float tau = a.s2o_tau;
+
+  auto block_step = [&](int blk, const TL& t) __attribute__((always_inline)) -> bool {
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[s], t.k[s], c, 0, 0, 0);
+    const bool valid = t.tok >= 0;
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = valid ? c[i] * sc : -INFINITY;
+    bool stop[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) stop[h] = false;
+    if (blk >= nb0) {
+      // this wave's (max, sum) of its tile and of what it attended before
+      const int par = blk & 1;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const int grp = h >> 2, r = h & 3;
+        const float tm = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, row16_max(sv[r])), 16 * grp));
+        const float e = (tm == -INFINITY || sv[r] == -INFINITY) ? 0.f : exp2f(sv[r] - tm);
+        const float ts = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, row16_sum(e)), 16 * grp));
+        const float lw = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, row16_sum(lsum[r])), 16 * grp));
+        if (lane == 0) {
+          s_tm[par][wid][h] = tm;
+          s_ts[par][wid][h] = ts;
+          s_m[par][wid][h] = m[h];
+          s_l[par][wid][h] = lw;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float mb = -INFINITY, mp = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) { mb = fmaxf(mb, s_tm[par][w][h]); mp = fmaxf(mp, s_m[par][w][h]); }
+        float sb = 0.f, sp = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          if (s_ts[par][w][h] > 0.f) sb += s_ts[par][w][h] * exp2f(s_tm[par][w][h] - mb);
+          if (s_l[par][w][h] > 0.f) sp += s_l[par][w][h] * exp2f(s_m[par][w][h] - mp);
+        }
+        const float ref = fmaxf(mb, mp);
+        const float gain = (sb > 0.f) ? sb * exp2f(mb - ref) : 0.f;
+        const float before = (sp > 0.f) ? sp * exp2f(mp - ref) : 0.f;
+        stop[h] = active[h] && before > 0.f && gain < tau * before;
+      }
+    }
+    // merge the tile into this wave's state, for the heads still active
+    float alpha[G];
+    bool moved = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const int grp = h >> 2, r = h & 3;
+      const float tmx = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, row16_max(sv[r])), 16 * grp));
+      const float mn = active[h] ? fmaxf(m[h], tmx) : m[h];
+      alpha[h] = (m[h] == mn) ? 1.f : exp2f(m[h] - mn);
+      moved |= (m[h] != mn);
+      m[h] = mn;
+      if (jg == grp) {
+        const float p = (!active[h] || sv[r] == -INFINITY) ? 0.f : exp2f(sv[r] - mn);
+        lsum[r] = lsum[r] * alpha[h] + p;
+        sh.p[wid][kt][h] = p;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (moved) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) { acc[h][0] *= alpha[h]; acc[h][1] *= alpha[h]; }
+    }
+#pragma unroll
+    for (int r = 0; r < VT; ++r) {
+      const int tt = r * NCLS + vc;
+      const float v0 = bf16_lo(t.v[r]), v1 = bf16_hi(t.v[r]);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = sh.p[wid][tt][h];
+        acc[h][0] = fmaf(p, v0, acc[h][0]);
+        acc[h][1] = fmaf(p, v1, acc[h][1]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    bool any = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) { active[h] = active[h] && !stop[h]; any |= active[h]; }
+    return any;
+  };
+
+  if (raw_count >= 0) {
+    TL ta, tb;
+    issue(0, ta);
+    for (int blk = 0; blk < nbt; blk += 2) {
+      issue(blk + 1, tb);
+      if (!block_step(blk, ta)) break;
+      if (blk + 1 >= nbt) break;
+      issue(blk + 2, ta);
+      if (!block_step(blk + 1, tb)) break;
+    }
+  }
+
+  // merge the four waves and write the group's outputs
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    if (NCLS == 2) {
+      acc[h][0] += __shfl_xor(acc[h][0], 32);
+      acc[h][1] += __shfl_xor(acc[h][1], 32);
+    }
+  }
+  float lw[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const int grp = h >> 2, r = h & 3;
+    const float ls = row16_sum(lsum[r]);
+    lw[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ls), 16 * grp));
+  }
+  __syncthreads();
+  if (lane < D / 2) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      sh.acc[wid][h][vd] = acc[h][0];
+      sh.acc[wid][h][vd + 1] = acc[h][1];
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) { sh.m[wid][h] = m[h]; sh.l[wid][h] = lw[h]; }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += kMfmaThreads) {
+    const int h = idx / D, e = idx % D;
+    float M = sh.m[0][h];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, sh.m[w][h]);
+    float av = 0.f, lv = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = sh.m[w][h];
+      const float wt = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+      av += wt * sh.acc[w][h][e];
+      lv += wt * sh.l[w][h];
+    }
+    a.out[((int64_t)b * a.Hq + g * G + h) * D + e] =
+        (raw_count < 0) ? __builtin_nanf("") : ((lv > 0.f) ? av / lv : 0.f);
+  }
+}
+
+hipError_t launch_decode_s2o(const DecodeArgs& a, int d, hipStream_t s) {
+  if (a.s2o.n == 0) return hipSuccess;
+  dim3 grid(a.s2o.n, a.B), block(kMfmaThreads);
+#define SA_S2O(D_, G_) hipLaunchKernelGGL((decode_s2o_kernel<D_, G_>), grid, block, 0, s, a)
+  switch (a.G * 1000 + d) {
+    case 1128: SA_S2O(128, 1); break;
+    case 2128: SA_S2O(128, 2); break;
+    case 4128: SA_S2O(128, 4); break;
+    case 8128: SA_S2O(128, 8); break;
+    case 1064: SA_S2O(64, 1); break;
+    case 2064: SA_S2O(64, 2); break;
+    case 4064: SA_S2O(64, 4); break;
+    case 8064: SA_S2O(64, 8); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef SA_S2O
   return hipGetLastError();
 }
 

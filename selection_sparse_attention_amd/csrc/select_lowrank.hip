@@ -906,4 +906,76 @@ hipError_t launch_select_lowrank(const SelectArgs& a, int dtype, int per, hipStr
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ visit order
+// Rewrites each row's selected positions (sel_count[row] of them, at most
+// kS2oMax) in visit order for the early-stop decode: index logit descending,
+// then position ascending - the ranking the cut used, with every logit
+// recomputed by the same arithmetic (so equal keys stay equal).  One
+// workgroup per row: the (key, position) pairs are bitonic-sorted in LDS.
+constexpr int kOrderThreads = 1024;
+
+template <typename T>
+__global__ __launch_bounds__(kOrderThreads) void select_order_kernel(SelectArgs a) {
+  __shared__ uint64_t s_key[kS2oMax];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  int b, g;
+  row_coords(a, row, b, g);
+  const int64_t orow = ((int64_t)b * a.Hkv + g) * a.n_cap;
+  const int cnt = a.sel_count[(int64_t)b * a.Hkv + g];
+  if (cnt <= 1) return;                        // failed (negative), empty or one token
+  const int m = min(cnt, kS2oMax);
+  int P = 2;
+  while (P < m) P <<= 1;
+  float qb[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) qb[c] = 0.f;
+  for (int hh = 0; hh < a.G; ++hh) {
+    const float* qp = a.q_idx + ((int64_t)b * a.Hq + g * a.G + hh) * 16;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) qb[c] += qp[c];
+  }
+  const float invG = 1.0f / (float)a.G;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) qb[c] *= invG;
+  const int64_t krow = (((int64_t)b * a.Hkv + g) / a.kv_div) * a.n_cap;
+  // sorted ascending on the complement: keys descending, then positions
+  // ascending; padding (all ones) goes last
+  for (int i = tid; i < P; i += kOrderThreads) {
+    uint64_t v = ~0ull;
+    if (i < m) {
+      const int j = a.sel_idx[orow + i];
+      IdxRow<T> r;
+      r.load(a.k_idx, krow + min(max(j, 0), a.n - 1));
+      float l = r.dot(qb) * 0.25f;
+      if (l == 0.f) l = 0.f;
+      v = ~(((uint64_t)order_key(l) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j));
+    }
+    s_key[i] = v;
+  }
+  __syncthreads();
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < P; i += kOrderThreads) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const uint64_t x = s_key[i], y = s_key[ixj];
+          const bool up = (i & k) == 0;
+          if ((x > y) == up) { s_key[i] = y; s_key[ixj] = x; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < m; i += kOrderThreads)
+    a.sel_idx[orow + i] = (int32_t)(0xFFFFFFFFu - (uint32_t)(~s_key[i]));
+}
+
+hipError_t launch_select_order(const SelectArgs& a, int dtype, hipStream_t s) {
+  const int rows = a.B * a.groups.n;
+  if (rows == 0) return hipSuccess;
+  if (dtype == 0) hipLaunchKernelGGL((select_order_kernel<bf16_t>), dim3(rows), dim3(kOrderThreads), 0, s, a);
+  else hipLaunchKernelGGL((select_order_kernel<float>), dim3(rows), dim3(kOrderThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace sa

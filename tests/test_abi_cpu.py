@@ -308,3 +308,17 @@ def test_route_prefill_validation():
     p3 = _decode_params(**dict(base, levels=3, factor=4), block_top_k=need)
     assert sa.raw_call("prefill_chunked", ctypes.byref(p3), ctypes.byref(b), None,
                        ctypes.byref(n), None) == sa.SA_ERR_INVALID_ARG
+
+
+def test_s2o_validation():
+    b = _full_bufs()
+    topk = dict(top_k=4096)
+    assert _select(_decode_params(**topk), b, sa.SEL_TOPK_BY_SCORE)[0] == sa.SA_OK
+    assert _select(_decode_params(top_k=8193), b, sa.SEL_TOPK_BY_SCORE)[0] == sa.SA_ERR_UNSUPPORTED
+    assert _decode(_decode_params(s2o_tau=0.01), b)[0] == sa.SA_OK
+    assert _decode(_decode_params(s2o_tau=-1.0), b)[0] == sa.SA_ERR_INVALID_ARG
+    assert _decode(_decode_params(s2o_tau=float("nan")), b)[0] == sa.SA_ERR_INVALID_ARG
+    assert _decode(_decode_params(s2o_tau=0.01, dtype="fp32"), b)[0] == sa.SA_ERR_UNSUPPORTED
+    # the first pass needs sinks or a window
+    assert _decode(_decode_params(s2o_tau=0.01, sinks=0, window=0, head_kind=[1] * 8), b)[0] == \
+        sa.SA_ERR_INVALID_ARG

@@ -62,6 +62,8 @@ class DecodeConfig:
     top_groups: int = 2
     sink_chunks: int = 4
     local_chunks: int = 8
+    # monotone-gain early stop over the top-k candidates (0: off)
+    s2o_tau: float = 0.0
 
     @property
     def gqa(self) -> int:
@@ -114,6 +116,11 @@ LLAMA_128K = LLAMA_32K.with_(name="llama3_8b_decode_128k", batch=4,
                              n_ctx=131072)
 LLAMA_128K_TOPK = LLAMA_128K.with_(name="llama3_8b_decode_128k_topk",
                                    top_p=1.0, top_k=2048)
+
+# the 32K layer with the early stop: its retrieval heads visit their top 2048
+# candidates by index score after sinks + window, stopping at a gain of 1 %
+LLAMA_32K_S2O = LLAMA_32K.with_(name="llama3_8b_decode_32k_s2o", top_p=1.0, top_k=2048,
+                                s2o_tau=0.01)
 
 HGA_64K = DecodeConfig(
     name="hga_route_decode_64k", batch=16, n_q_heads=32, n_kv_heads=8,
