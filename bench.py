@@ -619,9 +619,9 @@ def run_prefill(args, torch, sa, workloads, steps=None, warmup=None, cpu=True):
                    "levels": cfg.levels, "factor": cfg.factor, "q_block": cfg.q_block,
                    "block_top_k": cfg.block_top_k},
         "step_tflops": flops / t_step / 1e12,
-        "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": achieved,
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel<false>", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic_record("prefill_kernel", cfg.name, sha),
+                     "traffic": traffic_record("prefill_kernel<false>", cfg.name, sha),
                      "flops_per_launch": flops, "launch_us": t_kernel * 1e6, "source_sha": sha},
     }
     if cpu and not args.no_cpu_baseline:

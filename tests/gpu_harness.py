@@ -82,6 +82,8 @@ class DecodeRun:
     def select(self):
         if self.cfg.routed:
             mode = sa.SEL_ROUTE2
+        elif self.cfg.s2o_tau > 0:
+            mode = sa.SEL_TOPK_BY_SCORE
         else:
             mode = sa.SEL_TOPK if self.cfg.top_k > 0 else sa.SEL_TOPP
         sa.select(self.params, self.bufs(), mode, self.ws_sel)

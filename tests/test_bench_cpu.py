@@ -23,12 +23,12 @@ def test_bench_refuses_several_gpus():
 def test_traffic_record_follows_the_source():
     with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
         recs = json.load(f)
-    key = "prefill_kernel:pyramid_prefill_128k"
+    key = next(iter(recs))
+    kernel, workload = key.rsplit(":", 1)
     rec = recs[key]
-    assert bench.traffic_record("prefill_kernel", "pyramid_prefill_128k",
-                                rec["source_sha"]) == rec["bytes_per_launch"]
-    assert bench.traffic_record("prefill_kernel", "pyramid_prefill_128k", "0" * 16) is None
-    assert bench.traffic_record("prefill_kernel", "no_such_workload", rec["source_sha"]) is None
+    assert bench.traffic_record(kernel, workload, rec["source_sha"]) == rec["bytes_per_launch"]
+    assert bench.traffic_record(kernel, workload, "0" * 16) is None
+    assert bench.traffic_record(kernel, "no_such_workload", rec["source_sha"]) is None
 
 
 def test_source_sha_changes_with_the_text():

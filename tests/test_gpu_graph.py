@@ -35,7 +35,8 @@ def _same(a, b, groups=None):
     workloads.LLAMA_32K.with_(batch=2, n_ctx=8192 + 77),
     workloads.LLAMA_32K.with_(batch=2, n_ctx=4096, top_p=1.0, top_k=300),
     workloads.HGA_64K.with_(batch=2, n_ctx=8192),
-], ids=["topp", "topk", "routed"])
+    workloads.LLAMA_32K.with_(batch=2, n_ctx=4096, top_p=1.0, top_k=300, s2o_tau=0.01),
+], ids=["topp", "topk", "routed", "early-stop"])
 def test_decode_step_graph_replays_match_eager(cfg):
     inp = workloads.decode_inputs(cfg, 21, device=DEV)
     run = DecodeRun(cfg, inp)
