@@ -527,14 +527,15 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int d, hipStream_t s) {
 //   * the candidates outside the first pass, staged in LDS in visit order
 //     (each wave compacts a quarter of the list with ballots), in blocks of
 //     64 = one 16-token tile per wave;
-//   * after each candidate block, per head: the block's mass S_blk and the
-//     mass attended before it S_before, both from the four waves' (max, sum)
-//     pairs exchanged through LDS (double-buffered: one barrier per block);
-//     the head stops when S_blk < tau * S_before (the block is kept);
-//     stopped heads take no more tokens, and the group ends when every head
-//     has stopped;
-//   * the next block's rows are requested before the current block is
-//     scored, so a stop costs one block of loads.
+//   * blocks go in rounds of four: after scoring a round, per head and per
+//     block in order, the block's mass S_blk and the mass attended before it
+//     S_before come from the four waves' (max, sum) pairs exchanged through
+//     LDS (double-buffered: one barrier per round); the head stops at the
+//     first block with S_blk < tau * S_before (that block is kept), exactly
+//     as block-by-block decisions would; stopped heads take no more tokens,
+//     and the group ends when every head has stopped;
+//   * a round's rows are all requested before any is scored, so a stop
+//     within a round costs at most three blocks of loads.
 // Outputs go straight to `out` (the whole group is one workgroup).
 template <int D, int G>
 __global__ __launch_bounds__(kMfmaThreads) void decode_s2o_kernel(DecodeArgs a) {
@@ -543,7 +544,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_s2o_kernel(DecodeArgs a) 
   static_assert(G <= 8, "at most 8 query heads per KV group");
   __shared__ DecodeShared<D, G> sh;
   __shared__ int s_visit[kS2oMax];
-  __shared__ float s_tm[2][4][8], s_ts[2][4][8], s_m[2][4][8], s_l[2][4][8];
+  __shared__ float s_tm[2][4][4][8], s_ts[2][4][4][8], s_m[2][4][8], s_l[2][4][8];   // [parity][block][wave][head]
   __shared__ int s_cnt[4];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int b = blockIdx.y, g = a.s2o.ids[blockIdx.x];
@@ -638,105 +639,141 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_s2o_kernel(DecodeArgs a) 
   const float sc = a.scale_log2;
   const float tau = a.s2o_tau;
 
-  auto block_step = [&](int blk, const TL& t) __attribute__((always_inline)) -> bool {
-    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+  // One round: blocks blk0 .. blk0 + nr - 1 (nr <= kRound, never mixing the
+  // first pass with candidates), one 16-token tile of each per wave.  Every
+  // wave scores its tiles; for candidate blocks the waves exchange, per head,
+  // each tile's (max, sum) and their state before the round, and every wave
+  // then takes the same decisions block by block in order: a head keeps
+  // blocks up to and including the first whose mass is below tau times the
+  // mass before it - the decisions one block at a time would take.  Then each
+  // wave merges its tiles, each head up to its last kept block.
+  constexpr int kRound = 4;
+  auto round_step = [&](int blk0, int nr, const TL (&t)[kRound]) __attribute__((always_inline)) -> bool {
+    const bool cand = blk0 >= nb0;
+    float sv[kRound][4];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[s], t.k[s], c, 0, 0, 0);
-    const bool valid = t.tok >= 0;
-    float sv[4];
+    for (int r = 0; r < kRound; ++r) {
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sv[i] = valid ? c[i] * sc : -INFINITY;
-    bool stop[G];
+      for (int s = 0; s < KS; ++s) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[s], t[r].k[s], c, 0, 0, 0);
+      const bool valid = r < nr && t[r].tok >= 0;
 #pragma unroll
-    for (int h = 0; h < G; ++h) stop[h] = false;
-    if (blk >= nb0) {
-      // this wave's (max, sum) of its tile and of what it attended before
-      const int par = blk & 1;
+      for (int i = 0; i < 4; ++i) sv[r][i] = valid ? c[i] * sc : -INFINITY;
+    }
+    int keep[G];                                   // last block of the round each head keeps
+#pragma unroll
+    for (int h = 0; h < G; ++h) keep[h] = active[h] ? kRound - 1 : -1;
+    if (cand) {
+      const int par = (blk0 / kRound) & 1;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const int grp = h >> 2, r = h & 3;
-        const float tm = __builtin_bit_cast(
-            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, row16_max(sv[r])), 16 * grp));
-        const float e = (tm == -INFINITY || sv[r] == -INFINITY) ? 0.f : exp2f(sv[r] - tm);
-        const float ts = __builtin_bit_cast(
-            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, row16_sum(e)), 16 * grp));
-        const float lw = __builtin_bit_cast(
-            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, row16_sum(lsum[r])), 16 * grp));
-        if (lane == 0) {
-          s_tm[par][wid][h] = tm;
-          s_ts[par][wid][h] = ts;
-          s_m[par][wid][h] = m[h];
-          s_l[par][wid][h] = lw;
+        const int grp = h >> 2, ri = h & 3;
+#pragma unroll
+        for (int r = 0; r < kRound; ++r) {
+          const float tm = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, row16_max(sv[r][ri])), 16 * grp));
+          const float e = (tm == -INFINITY || sv[r][ri] == -INFINITY) ? 0.f : exp2f(sv[r][ri] - tm);
+          const float ts = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, row16_sum(e)), 16 * grp));
+          if (lane == 0) { s_tm[par][r][wid][h] = tm; s_ts[par][r][wid][h] = ts; }
         }
+        const float lw = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, row16_sum(lsum[ri])), 16 * grp));
+        if (lane == 0) { s_m[par][wid][h] = m[h]; s_l[par][wid][h] = lw; }
       }
       __syncthreads();
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float mb = -INFINITY, mp = -INFINITY;
+        // mass before the round, (mp, sp): sp relative to mp
+        float mp = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) { mb = fmaxf(mb, s_tm[par][w][h]); mp = fmaxf(mp, s_m[par][w][h]); }
-        float sb = 0.f, sp = 0.f;
+        for (int w = 0; w < 4; ++w) mp = fmaxf(mp, s_m[par][w][h]);
+        float sp = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          if (s_ts[par][w][h] > 0.f) sb += s_ts[par][w][h] * exp2f(s_tm[par][w][h] - mb);
+        for (int w = 0; w < 4; ++w)
           if (s_l[par][w][h] > 0.f) sp += s_l[par][w][h] * exp2f(s_m[par][w][h] - mp);
+        bool act = active[h];
+        int kp = act ? nr - 1 : -1;
+        for (int r = 0; r < nr; ++r) {
+          if (!act) break;
+          float mb = -INFINITY;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) mb = fmaxf(mb, s_tm[par][r][w][h]);
+          float sb = 0.f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            if (s_ts[par][r][w][h] > 0.f) sb += s_ts[par][r][w][h] * exp2f(s_tm[par][r][w][h] - mb);
+          const float ref = fmaxf(mb, mp);
+          const float gain = (sb > 0.f) ? sb * exp2f(mb - ref) : 0.f;
+          const float before = (sp > 0.f) ? sp * exp2f(mp - ref) : 0.f;
+          if (before > 0.f && gain < tau * before) { kp = r; act = false; break; }
+          // the block joins the mass before the next one
+          sp = before + gain;
+          mp = ref;
         }
-        const float ref = fmaxf(mb, mp);
-        const float gain = (sb > 0.f) ? sb * exp2f(mb - ref) : 0.f;
-        const float before = (sp > 0.f) ? sp * exp2f(mp - ref) : 0.f;
-        stop[h] = active[h] && before > 0.f && gain < tau * before;
+        keep[h] = kp;
+        active[h] = act;
       }
     }
-    // merge the tile into this wave's state, for the heads still active
-    float alpha[G];
-    bool moved = false;
+    // merge this wave's tiles, head h up to block keep[h]
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const int grp = h >> 2, r = h & 3;
-      const float tmx = __builtin_bit_cast(
-          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, row16_max(sv[r])), 16 * grp));
-      const float mn = active[h] ? fmaxf(m[h], tmx) : m[h];
-      alpha[h] = (m[h] == mn) ? 1.f : exp2f(m[h] - mn);
-      moved |= (m[h] != mn);
-      m[h] = mn;
-      if (jg == grp) {
-        const float p = (!active[h] || sv[r] == -INFINITY) ? 0.f : exp2f(sv[r] - mn);
-        lsum[r] = lsum[r] * alpha[h] + p;
-        sh.p[wid][kt][h] = p;
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    if (moved) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) { acc[h][0] *= alpha[h]; acc[h][1] *= alpha[h]; }
-    }
-#pragma unroll
-    for (int r = 0; r < VT; ++r) {
-      const int tt = r * NCLS + vc;
-      const float v0 = bf16_lo(t.v[r]), v1 = bf16_hi(t.v[r]);
+    for (int r = 0; r < kRound; ++r) {
+      if (r >= nr) break;
+      float alpha[G];
+      bool moved = false;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float p = sh.p[wid][tt][h];
-        acc[h][0] = fmaf(p, v0, acc[h][0]);
-        acc[h][1] = fmaf(p, v1, acc[h][1]);
+        const int grp = h >> 2, ri = h & 3;
+        const bool take = r <= keep[h];
+        const float tmx = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, row16_max(sv[r][ri])), 16 * grp));
+        const float mn = take ? fmaxf(m[h], tmx) : m[h];
+        alpha[h] = (m[h] == mn) ? 1.f : exp2f(m[h] - mn);
+        moved |= (m[h] != mn);
+        m[h] = mn;
+        if (jg == grp) {
+          const float p = (!take || sv[r][ri] == -INFINITY) ? 0.f : exp2f(sv[r][ri] - mn);
+          lsum[ri] = lsum[ri] * alpha[h] + p;
+          sh.p[wid][kt][h] = p;
+        }
       }
+      __builtin_amdgcn_wave_barrier();
+      if (moved) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) { acc[h][0] *= alpha[h]; acc[h][1] *= alpha[h]; }
+      }
+#pragma unroll
+      for (int q = 0; q < VT; ++q) {
+        const int tt = q * NCLS + vc;
+        const float v0 = bf16_lo(t[r].v[q]), v1 = bf16_hi(t[r].v[q]);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float p = sh.p[wid][tt][h];
+          acc[h][0] = fmaf(p, v0, acc[h][0]);
+          acc[h][1] = fmaf(p, v1, acc[h][1]);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
     }
-    __builtin_amdgcn_wave_barrier();
     bool any = false;
 #pragma unroll
-    for (int h = 0; h < G; ++h) { active[h] = active[h] && !stop[h]; any |= active[h]; }
+    for (int h = 0; h < G; ++h) any |= active[h];
     return any;
   };
 
   if (raw_count >= 0) {
-    TL ta, tb;
-    issue(0, ta);
-    for (int blk = 0; blk < nbt; blk += 2) {
-      issue(blk + 1, tb);
-      if (!block_step(blk, ta)) break;
-      if (blk + 1 >= nbt) break;
-      issue(blk + 2, ta);
-      if (!block_step(blk + 1, tb)) break;
+    // rounds of up to kRound blocks: the first pass, then the candidates
+    // (a round never mixes the two); a round's rows are all requested
+    // before any of them is scored
+    TL t[kRound];
+    int blk = 0;
+    while (blk < nbt) {
+      const int stop_at = (blk < nb0) ? nb0 : nbt;
+      const int nr = min(kRound, stop_at - blk);
+#pragma unroll
+      for (int r = 0; r < kRound; ++r) issue(r < nr ? blk + r : nbt, t[r]);
+      if (!round_step(blk, nr, t)) break;
+      blk += nr;
     }
   }
 
