@@ -521,32 +521,46 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int d, hipStream_t s) {
 // ---------------------------------------------------------------- early stop
 // Monotone-gain early stop ("S2O" summary, Methodology 2-3) for the groups in
 // a.s2o, whose lists hold their top-k candidates in visit order (index logit
-// descending).  One workgroup per (group, sequence), the group's G heads in
-// one MFMA tile as above:
-//   * first pass: the local rule's tokens (sinks + window), in blocks of 64;
+// descending).  One 512-thread workgroup per (group, sequence), the group's
+// G heads in one MFMA tile as above; blocks of 64 tokens go in rounds of
+// two, wave w taking tile w % 4 of block w / 4 of the round:
+//   * first pass: the local rule's tokens (sinks + window);
 //   * the candidates outside the first pass, staged in LDS in visit order
-//     (each wave compacts a quarter of the list with ballots), in blocks of
-//     64 = one 16-token tile per wave;
-//   * blocks go in rounds of four: after scoring a round, per head and per
-//     block in order, the block's mass S_blk and the mass attended before it
-//     S_before come from the four waves' (max, sum) pairs exchanged through
-//     LDS (double-buffered: one barrier per round); the head stops at the
-//     first block with S_blk < tau * S_before (that block is kept), exactly
-//     as block-by-block decisions would; stopped heads take no more tokens,
-//     and the group ends when every head has stopped;
-//   * a round's rows are all requested before any is scored, so a stop
-//     within a round costs at most three blocks of loads.
+//     (each wave compacts an eighth of the list with ballots);
+//   * after scoring a round of candidate blocks, the waves exchange through
+//     LDS, per head, each tile's (max, sum) and their state before the round
+//     (double-buffered: one barrier per round); every wave then takes the
+//     same decisions block by block in order: S_blk, the block's mass, and
+//     S_before, the mass attended before it; the head stops at the first
+//     block with S_blk < tau * S_before (that block is kept) - exactly the
+//     block-by-block rule; stopped heads take no more tokens, and the group
+//     ends when every head has stopped;
+//   * the next round's rows are requested before the current round is
+//     scored.
 // Outputs go straight to `out` (the whole group is one workgroup).
+constexpr int kS2oThreads = 512;
+constexpr int kS2oWaves = kS2oThreads / 64;
+constexpr int kRound = kS2oWaves / 4;            // blocks per round
+
+template <int D>
+struct S2oShared {
+  float p[kS2oWaves][16][8];                     // per wave: p[token][head]
+  float m[kS2oWaves][8], l[kS2oWaves][8];
+  float acc[kS2oWaves][8][D];
+  int visit[kS2oMax];
+  float tm[2][kRound][4][8], ts[2][kRound][4][8];   // [parity][block][tile][head]
+  float sm[2][kS2oWaves][8], sl[2][kS2oWaves][8];  // [parity][wave][head]
+  int cnt[kS2oWaves];
+};
+
 template <int D, int G>
-__global__ __launch_bounds__(kMfmaThreads) void decode_s2o_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kS2oThreads) void decode_s2o_kernel(DecodeArgs a) {
   using TL = Tile<D>;
   constexpr int KS = TL::KS, NCLS = TL::NCLS, VT = TL::VT;
   static_assert(G <= 8, "at most 8 query heads per KV group");
-  __shared__ DecodeShared<D, G> sh;
-  __shared__ int s_visit[kS2oMax];
-  __shared__ float s_tm[2][4][4][8], s_ts[2][4][4][8], s_m[2][4][8], s_l[2][4][8];   // [parity][block][wave][head]
-  __shared__ int s_cnt[4];
+  __shared__ S2oShared<D> sh;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int br = wid >> 2, tw = wid & 3;          // this wave's block of a round, and tile of it
   const int b = blockIdx.y, g = a.s2o.ids[blockIdx.x];
   const int bg = b * a.Hkv + g;
   const int n = a.n;
@@ -559,7 +573,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_s2o_kernel(DecodeArgs a) 
 
   // ---- the visit list: candidates outside the first pass, in list order
   {
-    const int Q = (count + 3) / 4;
+    const int Q = (count + kS2oWaves - 1) / kS2oWaves;
     const int lo = min(count, wid * Q), hi = min(count, lo + Q);
     int kept = 0;
     for (int base = lo; base < hi; base += 64) {
@@ -568,21 +582,22 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_s2o_kernel(DecodeArgs a) 
       const bool keep = e < hi && (unsigned)j < (unsigned)n && !(j < s_eff || j >= wst);
       kept += __popcll(__ballot(keep));
     }
-    if (lane == 0) s_cnt[wid] = kept;
+    if (lane == 0) sh.cnt[wid] = kept;
     __syncthreads();
     int run = 0;
-    for (int w = 0; w < wid; ++w) run += s_cnt[w];
+    for (int w = 0; w < wid; ++w) run += sh.cnt[w];
     for (int base = lo; base < hi; base += 64) {
       const int e = base + lane;
       const int j = (e < hi) ? a.sel_idx[row0 + e] : -1;
       const bool keep = e < hi && (unsigned)j < (unsigned)n && !(j < s_eff || j >= wst);
       const uint64_t bal = __ballot(keep);
-      if (keep) s_visit[run + __popcll(bal & ((1ull << lane) - 1ull))] = j;
+      if (keep) sh.visit[run + __popcll(bal & ((1ull << lane) - 1ull))] = j;
       run += __popcll(bal);
     }
   }
   __syncthreads();
-  const int nv = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+  int nv = 0;
+  for (int w = 0; w < kS2oWaves; ++w) nv += sh.cnt[w];
   const int nb0 = (c0 + 63) / 64, nbt = nb0 + (nv + 63) / 64;
 
   // query fragment: head (lane % 16), this lane's slice of the k mapping
@@ -604,15 +619,16 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_s2o_kernel(DecodeArgs a) 
   const int vd = 2 * (lane % (D / 2)), vc = lane / (D / 2);
   const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + kv0 * D + 8 * jg;
   const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v) + kv0 * D;
-  // token of this lane in block blk (this wave's tile of it), -1 if none
+  // this lane's token of block blk (this wave's tile of it), -1 if none
   auto token = [&](int blk) __attribute__((always_inline)) -> int {
-    const int e = 64 * blk + 16 * wid + kt;
+    if (blk >= nbt) return -1;
+    const int e = 64 * blk + 16 * tw + kt;
     if (blk < nb0) return (e < c0) ? ((e < s_eff) ? e : wst + (e - s_eff)) : -1;
     const int ev = e - 64 * nb0;
-    return (ev < nv) ? s_visit[ev] : -1;
+    return (ev < nv) ? sh.visit[ev] : -1;
   };
   auto issue = [&](int blk, TL& t) __attribute__((always_inline)) {
-    const int tok = (blk < nbt) ? token(blk) : -1;
+    const int tok = token(blk);
     t.tok = tok;
     const uint16_t* kp = kbase + (int64_t)max(tok, 0) * D;
 #pragma unroll
@@ -639,122 +655,107 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_s2o_kernel(DecodeArgs a) 
   const float sc = a.scale_log2;
   const float tau = a.s2o_tau;
 
-  // One round: blocks blk0 .. blk0 + nr - 1 (nr <= kRound, never mixing the
-  // first pass with candidates), one 16-token tile of each per wave.  Every
-  // wave scores its tiles; for candidate blocks the waves exchange, per head,
-  // each tile's (max, sum) and their state before the round, and every wave
-  // then takes the same decisions block by block in order: a head keeps
-  // blocks up to and including the first whose mass is below tau times the
-  // mass before it - the decisions one block at a time would take.  Then each
-  // wave merges its tiles, each head up to its last kept block.
-  constexpr int kRound = 4;
-  auto round_step = [&](int blk0, int nr, const TL (&t)[kRound]) __attribute__((always_inline)) -> bool {
+  // one round: blocks blk0 .. blk0 + nr - 1 (never mixing the first pass with
+  // candidates); this wave holds tile tw of block blk0 + br
+  auto round_step = [&](int blk0, int nr, int rnd, const TL& t) __attribute__((always_inline)) -> bool {
     const bool cand = blk0 >= nb0;
-    float sv[kRound][4];
-#pragma unroll
-    for (int r = 0; r < kRound; ++r) {
+    float sv[4];
+    {
       f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[s], t[r].k[s], c, 0, 0, 0);
-      const bool valid = r < nr && t[r].tok >= 0;
+      for (int s = 0; s < KS; ++s) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[s], t.k[s], c, 0, 0, 0);
+      const bool valid = br < nr && t.tok >= 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sv[r][i] = valid ? c[i] * sc : -INFINITY;
+      for (int i = 0; i < 4; ++i) sv[i] = valid ? c[i] * sc : -INFINITY;
     }
     int keep[G];                                   // last block of the round each head keeps
 #pragma unroll
     for (int h = 0; h < G; ++h) keep[h] = active[h] ? kRound - 1 : -1;
     if (cand) {
-      const int par = (blk0 / kRound) & 1;
+      const int par = rnd & 1;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const int grp = h >> 2, ri = h & 3;
-#pragma unroll
-        for (int r = 0; r < kRound; ++r) {
-          const float tm = __builtin_bit_cast(
-              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, row16_max(sv[r][ri])), 16 * grp));
-          const float e = (tm == -INFINITY || sv[r][ri] == -INFINITY) ? 0.f : exp2f(sv[r][ri] - tm);
-          const float ts = __builtin_bit_cast(
-              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, row16_sum(e)), 16 * grp));
-          if (lane == 0) { s_tm[par][r][wid][h] = tm; s_ts[par][r][wid][h] = ts; }
-        }
+        const float tm = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, row16_max(sv[ri])), 16 * grp));
+        const float e = (tm == -INFINITY || sv[ri] == -INFINITY) ? 0.f : exp2f(sv[ri] - tm);
+        const float ts = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, row16_sum(e)), 16 * grp));
         const float lw = __builtin_bit_cast(
             float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, row16_sum(lsum[ri])), 16 * grp));
-        if (lane == 0) { s_m[par][wid][h] = m[h]; s_l[par][wid][h] = lw; }
+        if (lane == 0) {
+          sh.tm[par][br][tw][h] = tm;
+          sh.ts[par][br][tw][h] = ts;
+          sh.sm[par][wid][h] = m[h];
+          sh.sl[par][wid][h] = lw;
+        }
       }
       __syncthreads();
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         // mass before the round, (mp, sp): sp relative to mp
         float mp = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) mp = fmaxf(mp, s_m[par][w][h]);
+        for (int w = 0; w < kS2oWaves; ++w) mp = fmaxf(mp, sh.sm[par][w][h]);
         float sp = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-          if (s_l[par][w][h] > 0.f) sp += s_l[par][w][h] * exp2f(s_m[par][w][h] - mp);
+        for (int w = 0; w < kS2oWaves; ++w)
+          if (sh.sl[par][w][h] > 0.f) sp += sh.sl[par][w][h] * exp2f(sh.sm[par][w][h] - mp);
         bool act = active[h];
         int kp = act ? nr - 1 : -1;
-        for (int r = 0; r < nr; ++r) {
-          if (!act) break;
+        for (int r = 0; r < nr && act; ++r) {
           float mb = -INFINITY;
 #pragma unroll
-          for (int w = 0; w < 4; ++w) mb = fmaxf(mb, s_tm[par][r][w][h]);
+          for (int q = 0; q < 4; ++q) mb = fmaxf(mb, sh.tm[par][r][q][h]);
           float sb = 0.f;
 #pragma unroll
-          for (int w = 0; w < 4; ++w)
-            if (s_ts[par][r][w][h] > 0.f) sb += s_ts[par][r][w][h] * exp2f(s_tm[par][r][w][h] - mb);
+          for (int q = 0; q < 4; ++q)
+            if (sh.ts[par][r][q][h] > 0.f) sb += sh.ts[par][r][q][h] * exp2f(sh.tm[par][r][q][h] - mb);
           const float ref = fmaxf(mb, mp);
           const float gain = (sb > 0.f) ? sb * exp2f(mb - ref) : 0.f;
           const float before = (sp > 0.f) ? sp * exp2f(mp - ref) : 0.f;
           if (before > 0.f && gain < tau * before) { kp = r; act = false; break; }
-          // the block joins the mass before the next one
-          sp = before + gain;
+          sp = before + gain;                      // the block joins the mass before the next
           mp = ref;
         }
         keep[h] = kp;
         active[h] = act;
       }
     }
-    // merge this wave's tiles, head h up to block keep[h]
+    // merge this wave's tile, head h if its block is kept
+    float alpha[G];
+    bool moved = false;
 #pragma unroll
-    for (int r = 0; r < kRound; ++r) {
-      if (r >= nr) break;
-      float alpha[G];
-      bool moved = false;
+    for (int h = 0; h < G; ++h) {
+      const int grp = h >> 2, ri = h & 3;
+      const bool take = br < nr && br <= keep[h];
+      const float tmx = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, row16_max(sv[ri])), 16 * grp));
+      const float mn = take ? fmaxf(m[h], tmx) : m[h];
+      alpha[h] = (m[h] == mn) ? 1.f : exp2f(m[h] - mn);
+      moved |= (m[h] != mn);
+      m[h] = mn;
+      if (jg == grp) {
+        const float p = (!take || sv[ri] == -INFINITY) ? 0.f : exp2f(sv[ri] - mn);
+        lsum[ri] = lsum[ri] * alpha[h] + p;
+        sh.p[wid][kt][h] = p;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (moved) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) { acc[h][0] *= alpha[h]; acc[h][1] *= alpha[h]; }
+    }
+#pragma unroll
+    for (int q = 0; q < VT; ++q) {
+      const int tt = q * NCLS + vc;
+      const float v0 = bf16_lo(t.v[q]), v1 = bf16_hi(t.v[q]);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const int grp = h >> 2, ri = h & 3;
-        const bool take = r <= keep[h];
-        const float tmx = __builtin_bit_cast(
-            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, row16_max(sv[r][ri])), 16 * grp));
-        const float mn = take ? fmaxf(m[h], tmx) : m[h];
-        alpha[h] = (m[h] == mn) ? 1.f : exp2f(m[h] - mn);
-        moved |= (m[h] != mn);
-        m[h] = mn;
-        if (jg == grp) {
-          const float p = (!take || sv[r][ri] == -INFINITY) ? 0.f : exp2f(sv[r][ri] - mn);
-          lsum[ri] = lsum[ri] * alpha[h] + p;
-          sh.p[wid][kt][h] = p;
-        }
+        const float p = sh.p[wid][tt][h];
+        acc[h][0] = fmaf(p, v0, acc[h][0]);
+        acc[h][1] = fmaf(p, v1, acc[h][1]);
       }
-      __builtin_amdgcn_wave_barrier();
-      if (moved) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) { acc[h][0] *= alpha[h]; acc[h][1] *= alpha[h]; }
-      }
-#pragma unroll
-      for (int q = 0; q < VT; ++q) {
-        const int tt = q * NCLS + vc;
-        const float v0 = bf16_lo(t[r].v[q]), v1 = bf16_hi(t[r].v[q]);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float p = sh.p[wid][tt][h];
-          acc[h][0] = fmaf(p, v0, acc[h][0]);
-          acc[h][1] = fmaf(p, v1, acc[h][1]);
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
     }
+    __builtin_amdgcn_wave_barrier();
     bool any = false;
 #pragma unroll
     for (int h = 0; h < G; ++h) any |= active[h];
@@ -762,22 +763,30 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_s2o_kernel(DecodeArgs a) 
   };
 
   if (raw_count >= 0) {
-    // rounds of up to kRound blocks: the first pass, then the candidates
-    // (a round never mixes the two); a round's rows are all requested
-    // before any of them is scored
-    TL t[kRound];
-    int blk = 0;
+    // rounds of up to kRound blocks: the first pass, then the candidates (a
+    // round never mixes the two); the next round's rows are requested
+    // before the current one is scored
+    auto round_len = [&](int blk) __attribute__((always_inline)) {
+      return min(kRound, ((blk < nb0) ? nb0 : nbt) - blk);
+    };
+    TL ta, tb;
+    int blk = 0, rnd = 0;
+    int nr = round_len(0);
+    issue(br < nr ? br : nbt, ta);
     while (blk < nbt) {
-      const int stop_at = (blk < nb0) ? nb0 : nbt;
-      const int nr = min(kRound, stop_at - blk);
-#pragma unroll
-      for (int r = 0; r < kRound; ++r) issue(r < nr ? blk + r : nbt, t[r]);
-      if (!round_step(blk, nr, t)) break;
-      blk += nr;
+      const int nblk = blk + nr, nnr = (nblk < nbt) ? round_len(nblk) : 0;
+      issue(br < nnr ? nblk + br : nbt, tb);
+      if (!round_step(blk, nr, rnd, ta)) break;
+      blk = nblk; nr = nnr; ++rnd;
+      if (blk >= nbt) break;
+      const int nblk2 = blk + nr, nnr2 = (nblk2 < nbt) ? round_len(nblk2) : 0;
+      issue(br < nnr2 ? nblk2 + br : nbt, ta);
+      if (!round_step(blk, nr, rnd, tb)) break;
+      blk = nblk2; nr = nnr2; ++rnd;
     }
   }
 
-  // merge the four waves and write the group's outputs
+  // merge the waves and write the group's outputs
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     if (NCLS == 2) {
@@ -788,8 +797,8 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_s2o_kernel(DecodeArgs a) 
   float lw[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const int grp = h >> 2, r = h & 3;
-    const float ls = row16_sum(lsum[r]);
+    const int grp = h >> 2, ri = h & 3;
+    const float ls = row16_sum(lsum[ri]);
     lw[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ls), 16 * grp));
   }
   __syncthreads();
@@ -805,14 +814,12 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_s2o_kernel(DecodeArgs a) 
     for (int h = 0; h < G; ++h) { sh.m[wid][h] = m[h]; sh.l[wid][h] = lw[h]; }
   }
   __syncthreads();
-  for (int idx = tid; idx < G * D; idx += kMfmaThreads) {
+  for (int idx = tid; idx < G * D; idx += kS2oThreads) {
     const int h = idx / D, e = idx % D;
     float M = sh.m[0][h];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, sh.m[w][h]);
+    for (int w = 1; w < kS2oWaves; ++w) M = fmaxf(M, sh.m[w][h]);
     float av = 0.f, lv = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kS2oWaves; ++w) {
       const float mw = sh.m[w][h];
       const float wt = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
       av += wt * sh.acc[w][h][e];
@@ -825,7 +832,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_s2o_kernel(DecodeArgs a) 
 
 hipError_t launch_decode_s2o(const DecodeArgs& a, int d, hipStream_t s) {
   if (a.s2o.n == 0) return hipSuccess;
-  dim3 grid(a.s2o.n, a.B), block(kMfmaThreads);
+  dim3 grid(a.s2o.n, a.B), block(kS2oThreads);
 #define SA_S2O(D_, G_) hipLaunchKernelGGL((decode_s2o_kernel<D_, G_>), grid, block, 0, s, a)
   switch (a.G * 1000 + d) {
     case 1128: SA_S2O(128, 1); break;
