@@ -238,6 +238,8 @@ int32_t decode_entry(const sa_params* p, const sa_buffers* b, void* ws, size_t* 
     else any_list = true;
     if (s2o && u.kind[g] == SA_HEAD_RETRIEVAL) { s2o_mask |= 1ull << g; s2o_units.ids[s2o_units.n++] = g; }
   }
+  // an early-stop group's first pass is the local rule, run by the split kernels
+  local_mask |= s2o_mask;
   if ((any_local || s2o_mask) && (p->sinks < 0 || p->window < 0 || (int64_t)p->sinks + p->window < 1))
     return SA_ERR_INVALID_ARG;
   if (s2o_mask && p->dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
@@ -262,6 +264,7 @@ int32_t decode_entry(const sa_params* p, const sa_buffers* b, void* ws, size_t* 
   Carver c(ws);
   float* partial = c.take<float>(n_partial);
   int2* plan = (p->dtype == SA_BF16) ? c.take<int2>((size_t)p->batch * u.n) : nullptr;
+  float* s2o_state = s2o_mask ? c.take<float>((size_t)p->batch * u.n * G * (p->head_dim + 2)) : nullptr;
   if ((st = workspace_gate(ws, ws_bytes, c.size()))) return st < 0 ? st : SA_OK;
   if (!b->q || !b->k_cache || !b->v_cache || !b->out) return SA_ERR_INVALID_ARG;
   if (any_list && (!b->sel_idx || !b->sel_count)) return SA_ERR_INVALID_ARG;
@@ -277,7 +280,8 @@ int32_t decode_entry(const sa_params* p, const sa_buffers* b, void* ws, size_t* 
   a.target_items = target_items;
   a.min_chunk = kDecodeMinChunk;
   a.plan = plan;
-  a.skip_mask = s2o_mask;
+  a.s2o_mask = s2o_mask;
+  a.s2o_state = s2o_state;
   a.s2o_tau = p->s2o_tau;
   a.s2o = s2o_units;
   hipStream_t hs = static_cast<hipStream_t>(stream);

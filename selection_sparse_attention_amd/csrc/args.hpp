@@ -139,11 +139,14 @@ struct DecodeArgs {
   int32_t target_items;   // bf16 path: work items the visible tokens are spread over
   int32_t min_chunk;      // bf16 path: smallest item (list entries)
   int2* plan;             // bf16 path: per group (first item, item count) [B*Hkv]
-  // monotone-gain early stop: the groups in `s2o` read their lists in visit
-  // order and are left to the early-stop kernel (bit g of skip_mask set: the
-  // split kernels give group g no work and write none of its outputs)
-  uint64_t skip_mask;
+  // monotone-gain early stop for the groups in `s2o` (bit g of s2o_mask
+  // set): the split kernels run their first pass (the local rule) and the
+  // combine caches each head's unnormalised state (m, l, acc[d]) in
+  // s2o_state [B*Hkv*G, d+2] instead of writing outputs; the early-stop
+  // kernel resumes from it over the candidates
+  uint64_t s2o_mask;
   float s2o_tau;
+  float* s2o_state;
   GroupList s2o;
 };
 

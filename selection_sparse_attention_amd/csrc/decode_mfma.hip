@@ -70,7 +70,6 @@ __device__ __forceinline__ float row16_sum(float v) {
 // ---------------------------------------------------------------- work plan
 __device__ __forceinline__ int group_count(const DecodeArgs& a, int bg) {
   const int g = bg % a.Hkv;
-  if ((a.skip_mask >> g) & 1ull) return 0;
   if ((a.local_mask >> g) & 1ull) {
     const int s = min(a.sinks, a.n);
     return s + (a.n - max(s, a.n - a.window));
@@ -422,7 +421,6 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_item_combine_kernel(Decod
   const int bgh = blockIdx.x;
   const int bg = bgh / G, h = bgh - bg * G;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
-  if ((a.skip_mask >> g) & 1ull) return;       // written by the early-stop kernel
   const int2 fr = a.plan[bg];
   const int first = fr.x, ns = fr.y;
   const int tid = threadIdx.x, e = tid % D, part = tid / D;
@@ -469,6 +467,13 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_item_combine_kernel(Decod
     float v = A;
 #pragma unroll
     for (int q = 1; q < P; ++q) v += s_a[q * D + e];
+    if ((a.s2o_mask >> g) & 1ull) {
+      // an early-stop group's first pass: its state, for the early-stop kernel
+      float* st = a.s2o_state + (bg * G + h) * (D + 2);
+      st[e] = v;
+      if (e == 0) { st[D] = M; st[D + 1] = L; }
+      return;
+    }
     // a failed selection (negative count) poisons the group's outputs
     const bool failed = !((a.local_mask >> g) & 1ull) && a.sel_count[bg] < 0;
     a.out[((int64_t)b * a.Hq + g * G + h) * D + e] = failed ? __builtin_nanf("") : ((L > 0.f) ? v / L : 0.f);
@@ -524,7 +529,9 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int d, hipStream_t s) {
 // descending).  One 512-thread workgroup per (group, sequence), the group's
 // G heads in one MFMA tile as above; blocks of 64 tokens go in rounds of
 // two, wave w taking tile w % 4 of block w / 4 of the round:
-//   * first pass: the local rule's tokens (sinks + window);
+//   * first pass: the local rule's tokens (sinks + window), computed by the
+//     split kernels (all groups at once) and resumed here from the cached
+//     (m, l, acc) of each head - the page's two-pass structure;
 //   * the candidates outside the first pass, staged in LDS in visit order
 //     (each wave compacts an eighth of the list with ballots);
 //   * after scoring a round of candidate blocks, the waves exchange through
@@ -598,7 +605,8 @@ __global__ __launch_bounds__(kS2oThreads) void decode_s2o_kernel(DecodeArgs a) {
   __syncthreads();
   int nv = 0;
   for (int w = 0; w < kS2oWaves; ++w) nv += sh.cnt[w];
-  const int nb0 = (c0 + 63) / 64, nbt = nb0 + (nv + 63) / 64;
+  (void)c0;
+  const int nb0 = 0, nbt = (nv + 63) / 64;       // the first pass is resumed, not recomputed
 
   // query fragment: head (lane % 16), this lane's slice of the k mapping
   bf16x8 qf[KS];
@@ -652,6 +660,17 @@ __global__ __launch_bounds__(kS2oThreads) void decode_s2o_kernel(DecodeArgs a) {
   for (int h = 0; h < G; ++h) { m[h] = -INFINITY; acc[h][0] = 0.f; acc[h][1] = 0.f; active[h] = true; }
 #pragma unroll
   for (int i = 0; i < 4; ++i) lsum[i] = 0.f;
+  if (wid == 0) {
+    // wave 0 starts from the first pass: m everywhere, l on the first lane of
+    // the head's lane group, acc on the lanes that own the dims
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float* st = a.s2o_state + ((int64_t)bg * G + h) * (D + 2);
+      m[h] = st[D];
+      if (jg == (h >> 2) && kt == 0) lsum[h & 3] = st[D + 1];
+      if (vc == 0) { acc[h][0] = st[vd]; acc[h][1] = st[vd + 1]; }
+    }
+  }
   const float sc = a.scale_log2;
   const float tau = a.s2o_tau;
 
