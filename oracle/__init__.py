@@ -17,7 +17,9 @@ Sources (web summaries of five papers; cited by page title and section):
   local and current chunks, RoPE-aware mixed summaries, exact token attention.
 * "Lighthouse Attention" summary - Methodology 2A-2C: symmetric mean pyramid,
   parameter-free l2 scoring with max inheritance, joint top-K across levels,
-  dense attention on the gathered subsequence and scatter back.
+  dense attention on the gathered subsequence and scatter back; the backward
+  pass through the gather, the attention and the scatter (2B: the selection
+  itself gets no gradient).
 * "Autonomia de Cabecas (AoH)" summary - Methodology item 4: head scores are
   averaged to the GQA group; sinks plus a recent window for streaming heads.
 * "S2O" summary - Methodology 2-3: candidates visited in descending
@@ -48,6 +50,7 @@ from .hga import (high_freq_pairs, chunk_summary, chunk_summaries, group_summari
                   route_token_list, route_scores, route_prefill_block, route_prefill_rows)
 from .lighthouse import (pyramid_levels, pyramid_scores, visible_entries,
                          block_select, prefill_block, prefill)
+from .lighthouse_bwd import block_grads, pyramid_backward, prefill_grads, n_entries
 from .decode import decode_step, decode_token_sets, decode_token_sets_per_head
 from .prefill_heads import prefill_visible, head_prefill_rows, visible_pairs
 from .s2o import s2o_order, s2o_head

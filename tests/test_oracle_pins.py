@@ -809,3 +809,117 @@ def test_s2o_blocks_shrink_as_tau_grows():
     q, K, V, init, order = _s2o_case(43)
     nbs = [oracle.s2o_head(q, K, V, init, order, tau)[1] for tau in (0.0, 1e-4, 1e-3, 1e-2, 0.1, 1.0)]
     assert all(a >= b for a, b in zip(nbs, nbs[1:])) and nbs[0] > nbs[-1]
+
+
+# ---------------------------------------------------------------- pyramid prefill backward
+def _autograd_grads(Q, K, V, dO, sels, L, p, qb):
+    """Gradients of sum(O * dO) by torch autograd (fp64, CPU) through a
+    dense masked restatement of the forward: the coarse levels as means of
+    level-0 rows, each block's gathered rows by index, a -inf mask, softmax."""
+    N, d = Q.shape
+    tQ, tK, tV = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (Q, K, V))
+
+    def flat(X):
+        parts = [X]
+        for lvl in range(1, L):
+            span = p ** lvl
+            m = N // span
+            parts.append(X[: m * span].reshape(m, span, d).mean(dim=1))
+        return torch.cat(parts)
+
+    Kf, Vf = flat(tK), flat(tV)
+    outs = []
+    for b in range((N + qb - 1) // qb):
+        lo, hi = qb * b, min(N, qb * b + qb)
+        idx = torch.tensor(np.asarray(sels[b], np.int64), dtype=torch.long)
+        Kt = torch.cat([Kf[idx], tK[lo:hi]])
+        Vt = torch.cat([Vf[idx], tV[lo:hi]])
+        a = (tQ[lo:hi] @ Kt.T) / math.sqrt(d)
+        n = len(idx)
+        mask = torch.zeros_like(a, dtype=torch.bool)
+        mask[:, n:] = torch.triu(torch.ones(hi - lo, hi - lo, dtype=torch.bool), diagonal=1)
+        a = a.masked_fill(mask, float("-inf"))
+        outs.append(torch.softmax(a, dim=1) @ Vt)
+    O = torch.cat(outs)
+    (O * torch.tensor(dO)).sum().backward()
+    return tQ.grad.numpy(), tK.grad.numpy(), tV.grad.numpy()
+
+
+@pytest.mark.parametrize("shape", [(64, 8, 3, 2, 8, 5), (96, 16, 2, 4, 16, 9),
+                                   (80, 8, 3, 2, 16, 40), (48, 4, 1, 4, 16, 48)])
+def test_pyramid_backward_matches_autograd(shape):
+    """Lighthouse Attention summary, 2B-2C: gradients flow through the
+    gather, the attention and the scatter only.  The oracle's hand-written
+    backward against torch autograd of the same forward (selection held
+    fixed, coarse levels unrounded), ragged last block included."""
+    N, d, L, p, qb, K_ = shape
+    rng = np.random.default_rng(N + L)
+    Q, K, V, dO = (rng.standard_normal((N, d)) for _ in range(4))
+    _, _, _, sels = oracle.prefill(Q, K, V, L, p, qb, K_, store=None)
+    got = oracle.prefill_grads(Q, K, V, dO, L, p, qb, K_, store=None, sels=sels)
+    ref = _autograd_grads(Q, K, V, dO, sels, L, p, qb)
+    for g, r in zip(got, ref):
+        np.testing.assert_allclose(g, r, atol=1e-11, rtol=1e-10)
+
+
+def test_pyramid_backward_finite_differences():
+    """Central differences of sum(O * dO) over single coordinates of Q, K
+    and V (selection fixed, unrounded levels) against the oracle's
+    gradients: brute force on a tiny pyramid."""
+    N, d, L, p, qb, K_ = 16, 3, 3, 2, 4, 3
+    rng = np.random.default_rng(5)
+    Q, K, V, dO = (rng.standard_normal((N, d)) for _ in range(4))
+    _, _, _, sels = oracle.prefill(Q, K, V, L, p, qb, K_, store=None)
+    gQ, gK, gV = oracle.prefill_grads(Q, K, V, dO, L, p, qb, K_, store=None, sels=sels)
+
+    def loss(Q_, K_, V_):
+        kc = oracle.pyramid_levels(K_, L, p, None)
+        vc = oracle.pyramid_levels(V_, L, p, None)
+        tot = 0.0
+        for b in range(N // qb):
+            o = oracle.prefill_block(Q_, K_, V_, kc, vc, sels[b], b, qb, L, p)
+            tot += float((o * dO[qb * b:qb * b + qb]).sum())
+        return tot
+
+    h = 1e-6
+    for which, G in ((0, gQ), (1, gK), (2, gV)):
+        for i in range(N):
+            for c in range(d):
+                args = [Q.copy(), K.copy(), V.copy()]
+                args[which][i, c] += h
+                up = loss(*args)
+                args[which][i, c] -= 2 * h
+                dn = loss(*args)
+                assert abs((up - dn) / (2 * h) - G[i, c]) < 1e-7, (which, i, c)
+
+
+def test_pyramid_backward_invariants():
+    """Every query's softmax weights sum to one, so its score gradients sum
+    to zero: the key gradients of a head sum to zero and its value
+    gradients sum to the sum of dO (the coarse means pass both sums on
+    unchanged)."""
+    N, d, L, p, qb, K_ = 256, 16, 3, 4, 32, 24
+    rng = np.random.default_rng(8)
+    Q, K, V, dO = (rng.standard_normal((N, d)) for _ in range(4))
+    _, gK, gV = oracle.prefill_grads(Q, K, V, dO, L, p, qb, K_, store="bf16")
+    np.testing.assert_allclose(gK.sum(axis=0), 0.0, atol=1e-10)
+    np.testing.assert_allclose(gV.sum(axis=0), dO.sum(axis=0), atol=1e-10)
+
+
+def test_pyramid_backward_single_key_and_scatter():
+    """One token: its only key is itself, so dV = dO and dQ = dK = 0.  And
+    the scatter of a coarse gradient by hand: an entry at level 2 of a
+    factor-2 pyramid spreads its gradient over 4 rows as quarters."""
+    rng = np.random.default_rng(3)
+    Q, K, V, dO = (rng.standard_normal((1, 4)) for _ in range(4))
+    gQ, gK, gV = oracle.prefill_grads(Q, K, V, dO, 1, 2, 1, 0, store=None)
+    np.testing.assert_allclose(gV, dO, atol=1e-15)
+    np.testing.assert_allclose(gQ, 0.0, atol=1e-15)
+    np.testing.assert_allclose(gK, 0.0, atol=1e-15)
+    # flat ids for N = 8, L = 3, p = 2: level 0 -> 0..7, level 1 -> 8..11, level 2 -> 12..13
+    g = np.zeros((14, 1))
+    g[13] = 8.0           # level-2 entry 1: rows 4..7
+    g[9] = 2.0            # level-1 entry 1: rows 2..3
+    g[0] = 1.0
+    np.testing.assert_allclose(oracle.pyramid_backward(g, 8, 3, 2)[:, 0],
+                               [1, 0, 1, 1, 2, 2, 2, 2])
