@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_VERSION 3
+#define SPARSE_ATTN_VERSION 4
 
 /* Size of the static device scratch array behind sparse_attn_decode_noalloc
  * (one per GPU the library runs on, held until the process ends). */
@@ -173,6 +173,12 @@ typedef struct sa_buffers {
   int32_t* blk_idx;     /* [B,H,ceil(N/q_block),K] flat entry ids per block    */
   int32_t* blk_count;   /* [B,H,ceil(N/q_block)]                               */
   float* out;           /* [B,Hq,d] decode | [B,H,N,d] prefill, fp32           */
+  /* pyramid prefill training pass (sparse_attn_prefill_backward)              */
+  const float* grad_out; /* [B,H,N,d] fp32   gradient of the loss w.r.t. out    */
+  float* lse;           /* [B,H,N] fp32      per query: log sum_j exp(q.k_j/sqrt d) */
+  float* grad_q;        /* [B,H,N,d] fp32    gradient w.r.t. level-0 Q           */
+  float* grad_k;        /* [B,H,N,d] fp32    gradient w.r.t. level-0 K           */
+  float* grad_v;        /* [B,H,N,d] fp32    gradient w.r.t. level-0 V           */
 } sa_buffers;
 
 /*
@@ -316,11 +322,46 @@ int32_t sparse_attn_decode_noalloc(const sa_params* params, const sa_buffers* bu
  * (SA_ERR_UNSUPPORTED otherwise).  blk_idx holds flat ids as
  * SA_SEL_PYRAMID_TOPK writes them; an id outside [0, n_ctx + coarse entries)
  * is never dereferenced: level-0 row 0 is read in its place, so its
- * contribution is unspecified.  Needs a workspace.
+ * contribution is unspecified.  When lse is not NULL it also receives, per
+ * query, the natural log of the softmax denominator sum_j exp(q.k_j /
+ * sqrt(d)) (what sparse_attn_prefill_backward reads).  Needs a workspace.
  */
 int32_t sparse_attn_prefill_chunked(const sa_params* params, const sa_buffers* bufs,
                                     void* workspace, size_t* workspace_bytes,
                                     void* hip_stream);
+
+/*
+ * sparse_attn_prefill_backward - gradients of the pyramid-selection prefill
+ * (Lighthouse summary, 2B-2C: the selection is discrete and receives no
+ * gradient; gradients pass through the gather, the attention and the scatter
+ * back; 2A: a level-l entry is the mean of the p^l level-0 rows it covers).
+ *
+ * For a loss L with dL/d(out) = grad_out, writes dL/dQ, dL/dK and dL/dV of the
+ * level-0 Q, K and V of sparse_attn_prefill_chunked, its selection (blk_idx,
+ * blk_count) held fixed: per block, with P the softmax weights and a = q.k /
+ * sqrt(d), dV_j += P_ij dO_i, dA_ij = P_ij (dO_i.v_j - dO_i.o_i), dQ_i = sum_j
+ * dA_ij k_j / sqrt(d), dK_j += dA_ij q_i / sqrt(d); the gradient of a coarse
+ * entry at level l goes to each level-0 row it covers divided by p^l (the
+ * stored rounding of a level counts as the identity).  Only level-0 queries
+ * attend, so the coarse Q levels get no gradient.
+ *
+ * Reads q, k_cache, v_cache, pyr_k, pyr_v (levels > 1), blk_idx, blk_count,
+ * out and lse as sparse_attn_prefill_chunked wrote them (pass lse to the
+ * forward call), and grad_out; writes grad_q, grad_k, grad_v.  Same
+ * requirements as the forward plus n_q_heads == n_kv_heads
+ * (SA_ERR_UNSUPPORTED).  The lists may come in any order, but they must have
+ * the shape the pyramid selection gives them: distinct visible ids, each
+ * entry chosen from the first block that sees it through a last block and by
+ * none after.  A head whose lists break this (or hold a negative count or an
+ * id outside the pyramid) gets NaN in every gradient row.  Deterministic:
+ * every sum is taken in a fixed order.  Needs a workspace of about
+ * B * H * (N + ceil(N/128) * block_top_k) * d * 8 bytes (per-block partial
+ * gradients of the chosen entries, reduced per entry in block order); no
+ * part of it has to start at zero.
+ */
+int32_t sparse_attn_prefill_backward(const sa_params* params, const sa_buffers* bufs,
+                                     void* workspace, size_t* workspace_bytes,
+                                     void* hip_stream);
 
 /*
  * sparse_attn_prefill_heads - head-split prefill forward ("Full Attention

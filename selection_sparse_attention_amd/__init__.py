@@ -33,7 +33,7 @@ SEL_TOPP, SEL_TOPK, SEL_ROUTE2, SEL_PYRAMID_TOPK, SEL_ROUTE2_PREFILL, SEL_TOPK_B
 
 EXPORTED = ("sparse_attn_index_build", "sparse_attn_select", "sparse_attn_decode",
             "sparse_attn_decode_noalloc", "sparse_attn_prefill_chunked",
-            "sparse_attn_prefill_heads",
+            "sparse_attn_prefill_heads", "sparse_attn_prefill_backward",
             "sparse_attn_status_string", "sparse_attn_version")
 
 
@@ -58,7 +58,8 @@ class Params(ctypes.Structure):
 
 _BUF_FIELDS = ["q_pre", "k_pre", "q", "k_cache", "v_cache", "proj_q", "proj_k", "q_idx",
                "k_idx", "chunk_sum", "group_sum", "pyr_q", "pyr_k", "pyr_v", "pyr_scores",
-               "sel_idx", "sel_count", "blk_idx", "blk_count", "out"]
+               "sel_idx", "sel_count", "blk_idx", "blk_count", "out",
+               "grad_out", "lse", "grad_q", "grad_k", "grad_v"]
 
 
 class Buffers(ctypes.Structure):
@@ -77,7 +78,10 @@ for _name, _args in (
                                 ctypes.c_void_p]),
         ("sparse_attn_prefill_chunked", [ctypes.POINTER(Params), ctypes.POINTER(Buffers),
                                          ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t),
-                                         ctypes.c_void_p])):
+                                         ctypes.c_void_p]),
+        ("sparse_attn_prefill_backward", [ctypes.POINTER(Params), ctypes.POINTER(Buffers),
+                                          ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t),
+                                          ctypes.c_void_p])):
     getattr(_lib, _name).argtypes = _args
     getattr(_lib, _name).restype = ctypes.c_int32
 _lib.sparse_attn_decode_noalloc.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(Buffers),
@@ -223,6 +227,9 @@ def workspace_size(fn: str, params: Params, bufs: Buffers, mode: int = 0) -> int
     elif fn == "prefill":
         st = _lib.sparse_attn_prefill_chunked(ctypes.byref(params), ctypes.byref(bufs), None,
                                               ctypes.byref(n), None)
+    elif fn == "prefill_backward":
+        st = _lib.sparse_attn_prefill_backward(ctypes.byref(params), ctypes.byref(bufs), None,
+                                               ctypes.byref(n), None)
     else:
         raise ValueError(fn)
     _check(st, f"{fn} (workspace query)")
@@ -277,6 +284,18 @@ def prefill_chunked(params: Params, bufs: Buffers, ws: Optional[Workspace] = Non
     _check(_lib.sparse_attn_prefill_chunked(ctypes.byref(params), ctypes.byref(bufs),
                                             w.data_ptr(), ctypes.byref(n), _stream(stream)),
            "prefill_chunked")
+
+
+def prefill_backward(params: Params, bufs: Buffers, ws: Optional[Workspace] = None,
+                     stream=None):
+    """Gradients of the pyramid prefill (grad_q, grad_k, grad_v) from
+    grad_out, the forward's out and lse, and its lists."""
+    need = workspace_size("prefill_backward", params, bufs)
+    w = _workspace(ws, "prefill_backward").get(need)
+    n = ctypes.c_size_t(w.numel())
+    _check(_lib.sparse_attn_prefill_backward(ctypes.byref(params), ctypes.byref(bufs),
+                                             w.data_ptr(), ctypes.byref(n), _stream(stream)),
+           "prefill_backward")
 
 
 def prefill_heads(params: Params, bufs: Buffers, stream=None):

@@ -568,12 +568,65 @@ int32_t sparse_attn_prefill_chunked(const sa_params* p, const sa_buffers* b, voi
   if (p->levels > 1 && (!b->pyr_k || !b->pyr_v)) return SA_ERR_INVALID_ARG;
   sa::PrefillArgs a{};
   a.q = b->q; a.k = b->k_cache; a.v = b->v_cache; a.pk = b->pyr_k; a.pv = b->pyr_v;
-  a.blk_idx = b->blk_idx; a.blk_count = b->blk_count; a.out = b->out;
+  a.blk_idx = b->blk_idx; a.blk_count = b->blk_count; a.out = b->out; a.lse = b->lse;
   a.B = p->batch; a.H = p->n_q_heads; a.N = p->n_ctx; a.Nc = pg.Nc; a.nblk = pg.nblk;
   a.K = p->block_top_k; a.q_block = p->q_block;
   a.Hkv = p->n_kv_heads; a.G = p->n_q_heads / p->n_kv_heads; a.kv_stride = p->n_ctx;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->head_dim));
   return hip_status(sa::launch_prefill(a, p->head_dim, static_cast<hipStream_t>(stream)));
+}
+
+int32_t sparse_attn_prefill_backward(const sa_params* p, const sa_buffers* b, void* ws,
+                                     size_t* ws_bytes, void* stream) {
+  int32_t st = check_common(p, b);
+  if (st) return st;
+  if (p->n_q_heads != p->n_kv_heads) return SA_ERR_UNSUPPORTED;
+  PyrGeom pg;
+  if ((st = pyramid_geom(p, &pg, false))) return st;
+  if (p->q_block < 1 || p->q_block % pg.top_span || p->block_top_k < 1) return SA_ERR_INVALID_ARG;
+  if (p->dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+  if (p->head_dim != 128 || p->q_block != 128) return SA_ERR_UNSUPPORTED;
+  if (p->block_top_k > 8192) return SA_ERR_UNSUPPORTED;
+  if (p->n_ctx >= (1 << 23)) return SA_ERR_UNSUPPORTED;
+  const int64_t bh = (int64_t)p->batch * p->n_q_heads;
+  const int64_t E = pg.Nt;
+  const int64_t R = (int64_t)p->n_ctx + (int64_t)pg.nblk * p->block_top_k;
+  if (R >= (1ll << 31)) return SA_ERR_UNSUPPORTED;
+  Carver c(ws);
+  float* delta = c.take<float>(bh * p->n_ctx);
+  int32_t* last = c.take<int32_t>(bh * E);
+  int32_t* base = c.take<int32_t>(bh * (E + 1));
+  uint32_t* err = c.take<uint32_t>(bh);
+  float* coarse_k = c.take<float>(bh * pg.Nc * p->head_dim);
+  float* coarse_v = c.take<float>(bh * pg.Nc * p->head_dim);
+  uint16_t* part_k = c.take<uint16_t>(bh * R * p->head_dim);
+  uint16_t* part_v = c.take<uint16_t>(bh * R * p->head_dim);
+  if ((st = workspace_gate(ws, ws_bytes, c.size()))) return st < 0 ? st : SA_OK;
+  if (!b->q || !b->k_cache || !b->v_cache || !b->blk_idx || !b->blk_count || !b->out ||
+      !b->lse || !b->grad_out || !b->grad_q || !b->grad_k || !b->grad_v)
+    return SA_ERR_INVALID_ARG;
+  if (p->levels > 1 && (!b->pyr_k || !b->pyr_v)) return SA_ERR_INVALID_ARG;
+  sa::BwdArgs a{};
+  a.q = b->q; a.k = b->k_cache; a.v = b->v_cache; a.pk = b->pyr_k; a.pv = b->pyr_v;
+  a.blk_idx = b->blk_idx; a.blk_count = b->blk_count;
+  a.out = b->out; a.lse = b->lse; a.dout = b->grad_out;
+  a.dq = b->grad_q; a.dk = b->grad_k; a.dv = b->grad_v;
+  a.delta = delta; a.last = last; a.base = base; a.err = err;
+  a.part_k = part_k; a.part_v = part_v;
+  a.coarse_k = coarse_k; a.coarse_v = coarse_v;
+  a.R = R;
+  a.B = p->batch; a.H = p->n_q_heads; a.N = p->n_ctx; a.Nc = pg.Nc; a.E = (int32_t)E;
+  a.nblk = pg.nblk; a.K = p->block_top_k; a.q_block = p->q_block; a.levels = p->levels;
+  int span = 1, m = p->n_ctx;
+  for (int l = 0; l < 8; ++l) {
+    a.off[l] = l < p->levels ? pg.off[l] : 0;
+    a.span[l] = span;
+    a.cnt[l] = l < p->levels ? m : 0;
+    if (l + 1 < p->levels) { span *= p->factor; m /= p->factor; }
+  }
+  a.scale = (float)(1.0 / std::sqrt((double)p->head_dim));
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->head_dim));
+  return hip_status(sa::launch_prefill_backward(a, p->head_dim, static_cast<hipStream_t>(stream)));
 }
 
 int32_t sparse_attn_prefill_heads(const sa_params* p, const sa_buffers* b, void* stream) {

@@ -159,6 +159,7 @@ struct PrefillArgs {
   const void* pk; const void* pv;                // [B,H,Nc,d]
   const int32_t* blk_idx; const int32_t* blk_count;
   float* out;                                    // [B,H,N,d]
+  float* lse;                                    // [B,H,N] or null: log of each row's softmax denominator
   int32_t B, H, N, Nc, nblk, K, q_block;
   float scale_log2;
   // head-split mode: the visible keys follow from each head's class - class
@@ -168,6 +169,29 @@ struct PrefillArgs {
   int32_t n_cls[2];                              // heads in each class
   int32_t units0;                                // workgroups of class 0
   uint8_t cls_heads[2][kMaxPrefillHeads];        // the heads of each class
+};
+
+// Backward pass of the pyramid prefill: inputs as the forward's, the
+// forward's outputs, the upstream gradient, the gradients, and workspace
+// regions (per query delta = dO.O; per flat entry its last choosing block and
+// the first row of its partial gradients; per head an error word; per-block
+// partial gradients of the chosen entries; the coarse entries' sums).
+struct BwdArgs {
+  const void* q; const void* k; const void* v;   // [B,H,N,d] bf16
+  const void* pk; const void* pv;                // [B,H,Nc,d] bf16
+  const int32_t* blk_idx; const int32_t* blk_count;
+  const float* out; const float* lse; const float* dout;
+  float* dq; float* dk; float* dv;               // [B,H,N,d]
+  float* delta;                                  // [B,H,N]
+  int32_t* last;                                 // [B,H,E]
+  int32_t* base;                                 // [B,H,E+1]
+  uint32_t* err;                                 // [B,H]
+  uint16_t* part_k; uint16_t* part_v;            // [B,H,R,d] bf16
+  float* coarse_k; float* coarse_v;              // [B,H,Nc,d]
+  int64_t R;                                     // partial rows per head
+  int32_t B, H, N, Nc, E, nblk, K, q_block, levels;
+  int32_t off[8], span[8], cnt[8];               // per level: flat offset, rows covered, entries
+  float scale, scale_log2;
 };
 
 // ---------------------------------------------------------------- launchers
@@ -183,5 +207,6 @@ hipError_t launch_decode_s2o(const DecodeArgs& a, int d, hipStream_t s);
 hipError_t launch_select_order(const SelectArgs& a, int dtype, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int d, hipStream_t s);
 hipError_t launch_prefill_heads(const PrefillArgs& a, int d, hipStream_t s);
+hipError_t launch_prefill_backward(const BwdArgs& a, int d, hipStream_t s);
 
 }  // namespace sa

@@ -502,6 +502,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     lt += __shfl_xor(lt, 32);
     const int ql = 32 * wid + 16 * nt + l16;
     if (ql < nq) {
+      // the row's log-sum-exp (natural log) for the backward pass: the
+      // weights were 2^(s sc - m), so the denominator is 2^m lt
+      if (a.lse != nullptr && jg == 0)
+        a.lse[(int64_t)bh * a.N + q0 + ql] = (m[nt] + log2f(lt)) * 0.6931471805599453f;
       const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
       float* orow = ob + (int64_t)(q0 + ql) * kD;
 #pragma unroll

@@ -344,6 +344,14 @@ def prefill_inputs(cfg: PrefillConfig, seed: int, device="cpu") -> dict:
     return out
 
 
+def prefill_grad_inputs(cfg: PrefillConfig, seed: int, device="cpu") -> torch.Tensor:
+    """An upstream gradient dL/d(out) for a pyramid prefill: [B,H,N,d] fp32
+    drawn N(0,1)."""
+    g = _gen(seed, device, 23)
+    return torch.randn(cfg.batch, cfg.n_heads, cfg.n_ctx, cfg.head_dim, generator=g,
+                       dtype=torch.float32, device=device)
+
+
 def head_prefill_inputs(cfg: DecodeConfig, seed: int, device="cpu",
                         n_cap: Optional[int] = None) -> dict:
     """Inputs of a head-split prefill over n = cfg.n_ctx tokens: q_pre
