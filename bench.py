@@ -41,8 +41,8 @@ def parse():
                     choices=["llama3_8b_decode_32k", "llama3_8b_decode_128k",
                              "llama3_8b_decode_128k_topk", "hga_route_decode_64k",
                              "llama3_8b_decode_32k_s2o",
-                             "pyramid_prefill_128k", "llama3_8b_head_split_prefill_32k",
-                             "hga_route_prefill_64k"])
+                             "pyramid_prefill_128k", "pyramid_prefill_backward_128k",
+                             "llama3_8b_head_split_prefill_32k", "hga_route_prefill_64k"])
     ap.add_argument("--instances", type=int, default=4,
                     help="independent input sets rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -472,7 +472,7 @@ def _oracle_decode_sample(cfg, inst, budget_s, torch):
 def compact(r):
     keep = ("value", "unit", "ms_per_step", "step_hbm_gbps", "step_roofline",
             "selected_frac_mean", "config", "roofline", "step_tflops", "spread_us",
-            "all_dense_ms", "speedup_vs_all_dense", "note")
+            "all_dense_ms", "speedup_vs_all_dense", "note", "forward_ms", "backward_ms")
     return {k: r[k] for k in keep if k in r}
 
 
@@ -494,6 +494,8 @@ def main():
         return
     if args.workload == "pyramid_prefill_128k":
         res = run_prefill(args, torch, sa, workloads)
+    elif args.workload == "pyramid_prefill_backward_128k":
+        res = run_prefill(args, torch, sa, workloads, backward=True)
     elif args.workload == "llama3_8b_head_split_prefill_32k":
         res = run_prefill_heads(args, torch, sa, workloads)
     elif args.workload == "hga_route_prefill_64k":
@@ -520,6 +522,8 @@ def main():
                 instances=4, cpu=False, alpha=a))
         other["pyramid_prefill_128k"] = compact(run_prefill(args, torch, sa, workloads, steps=5,
                                                             warmup=1, cpu=False))
+        other["pyramid_prefill_backward_128k"] = compact(run_prefill(
+            args, torch, sa, workloads, steps=3, warmup=1, cpu=False, backward=True))
         other["llama3_8b_head_split_prefill_32k"] = compact(run_prefill_heads(
             args, torch, sa, workloads, steps=5, warmup=1, cpu=False))
         other["hga_route_prefill_64k"] = compact(run_prefill_routed(
@@ -553,7 +557,10 @@ def prefill_flops(cfg, counts):
     return 4 * cfg.head_dim * pairs
 
 
-def run_prefill(args, torch, sa, workloads, steps=None, warmup=None, cpu=True):
+def run_prefill(args, torch, sa, workloads, steps=None, warmup=None, cpu=True, backward=False):
+    """The pyramid prefill step (pyramid, selection, attention); with
+    ``backward`` a training step: the forward keeps each row's log-sum-exp
+    and the backward pass follows with a synthetic upstream gradient."""
     cfg = workloads.PYRAMID_128K
     steps = steps or max(3, min(args.steps, 10))
     warmup = 1 if warmup is None else warmup
@@ -574,11 +581,17 @@ def run_prefill(args, torch, sa, workloads, steps=None, warmup=None, cpu=True):
     t["blk_idx"] = torch.zeros(B, H, nblk, cfg.block_top_k, dtype=torch.int32, device="cuda")
     t["blk_count"] = torch.zeros(B, H, nblk, dtype=torch.int32, device="cuda")
     t["out"] = torch.zeros(B, H, N, d, dtype=torch.float32, device="cuda")
+    grads = {}
+    if backward:
+        grads = dict(lse=torch.zeros(B, H, N, dtype=torch.float32, device="cuda"),
+                     grad_out=workloads.prefill_grad_inputs(cfg, 2001, device="cuda"),
+                     **{k: torch.zeros(B, H, N, d, dtype=torch.float32, device="cuda")
+                        for k in ("grad_q", "grad_k", "grad_v")})
     p = sa.params_from_config(cfg)
     bufs = sa.make_buffers(q=t["q"], k_cache=t["k"], v_cache=t["v"], pyr_q=t["pq"],
                            pyr_k=t["pk"], pyr_v=t["pv"], pyr_scores=t["scores"],
-                           blk_idx=t["blk_idx"], blk_count=t["blk_count"], out=t["out"])
-    ws_s, ws_p = sa.Workspace("cuda"), sa.Workspace("cuda")
+                           blk_idx=t["blk_idx"], blk_count=t["blk_count"], out=t["out"], **grads)
+    ws_s, ws_p, ws_b = sa.Workspace("cuda"), sa.Workspace("cuda"), sa.Workspace("cuda")
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -589,12 +602,15 @@ def run_prefill(args, torch, sa, workloads, steps=None, warmup=None, cpu=True):
         sa.prefill_chunked(p, bufs, ws_p)
         if ev:
             ev[1].record(stream)
+        if backward:
+            sa.prefill_backward(p, bufs, ws_b)
+            if ev:
+                ev[2].record(stream)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(steps):
@@ -602,11 +618,19 @@ def run_prefill(args, torch, sa, workloads, steps=None, warmup=None, cpu=True):
     end.record(stream)
     torch.cuda.synchronize()
     t_step = start.elapsed_time(end) / steps * 1e-3
-    t_kernel = sum(a.elapsed_time(b) for a, b in ev) / steps * 1e-3
+    t_kernel = sum(e[0].elapsed_time(e[1]) for e in ev) / steps * 1e-3
+    t_bwd = sum(e[1].elapsed_time(e[2]) for e in ev) / steps * 1e-3 if backward else 0.0
     counts = t["blk_count"].reshape(B * H, nblk).cpu().tolist()
     flops = prefill_flops(cfg, counts)
     log(f"[bench] {cfg.name}: {t_step * 1e3:.3f} ms/step, prefill kernel {t_kernel * 1e3:.3f} ms, "
-        f"{flops / t_kernel / 1e12:.1f} TFLOP/s")
+        f"{flops / t_kernel / 1e12:.1f} TFLOP/s" +
+        (f", backward {t_bwd * 1e3:.3f} ms ({2 * flops / t_bwd / 1e12:.1f} TFLOP/s)" if backward else ""))
+    if backward:
+        res = prefill_backward_result(args, cfg, t, steps, warmup, t_step, t_kernel, t_bwd, flops,
+                                      cpu, torch)
+        del t, grads, ws_b
+        torch.cuda.empty_cache()
+        return res
     sha = source_sha(["prefill.hip", "common.hpp", "args.hpp"])
     achieved = flops / t_kernel / 1e12
     res = {
@@ -628,6 +652,37 @@ def run_prefill(args, torch, sa, workloads, steps=None, warmup=None, cpu=True):
         res["cpu_baseline"] = cpu_baseline_prefill(cfg, t, args.cpu_seconds, torch)
     del t
     torch.cuda.empty_cache()
+    return res
+
+
+def prefill_backward_result(args, cfg, t, steps, warmup, t_step, t_kernel, t_bwd, flops, cpu, torch):
+    """The bench line of the pyramid prefill training step.  The backward's
+    algorithmic work is 8 d FLOP per (query, visible key) pair - dV = P^T dO,
+    dP = dO V^T, dQ = dS K, dK = dS^T Q - twice the forward's 4 d (the
+    recomputed scores are not counted)."""
+    B, H, N, d = cfg.batch, cfg.n_heads, cfg.n_ctx, cfg.head_dim
+    bflops = 2 * flops
+    achieved = bflops / t_bwd / 1e12
+    sha = source_sha(["prefill_bwd.hip", "common.hpp", "args.hpp"])
+    label = "sparse_attn_prefill_backward (all kernels of the call)"
+    res = {
+        "metric": "pyramid-selection prefill training step (forward + backward) tokens/s + "
+                  "backward bf16 MFMA TFLOP/s vs peak",
+        "value": B * H * N / t_step, "unit": "tokens/s (B x heads x N per step)",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": t_step * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name + "_forward_backward", "batch": B, "n_heads": H,
+                   "head_dim": d, "n_ctx": N, "levels": cfg.levels, "factor": cfg.factor,
+                   "q_block": cfg.q_block, "block_top_k": cfg.block_top_k},
+        "forward_ms": t_kernel * 1e3, "backward_ms": t_bwd * 1e3,
+        "roofline": {"bound": "mfma", "kernel": label, "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic_record(label, cfg.name, sha),
+                     "flops_per_launch": bflops, "launch_us": t_bwd * 1e6, "source_sha": sha},
+    }
+    if cpu and not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill_backward(cfg, t, args.cpu_seconds, torch)
     return res
 
 
@@ -893,6 +948,36 @@ def cpu_baseline_prefill(cfg, t, budget_s, torch):
             "sample": f"{done} query blocks of one head of {cfg.name} (pyramid and scores of "
                       f"the head once, then selection + attention per block), fp64 numpy, "
                       f"{spent:.1f} s"}
+
+
+def cpu_baseline_prefill_backward(cfg, t, budget_s, torch):
+    """The fp64 oracle's training step on whole query blocks of head 0
+    (pyramid and scores once, then per block: selection, attention and its
+    gradients) with a seeded upstream gradient, until ``budget_s`` is spent."""
+    import numpy as np
+    import oracle
+    from oracle import lighthouse as LH
+    Q, K, V = (t[k][0, 0].to("cpu", torch.float64).numpy() for k in ("q", "k", "v"))
+    dO = np.random.default_rng(0).standard_normal(Q.shape)
+    t0 = time.perf_counter()
+    kc = oracle.pyramid_levels(K, cfg.levels, cfg.factor, cfg.dtype)
+    vc = oracle.pyramid_levels(V, cfg.levels, cfg.factor, cfg.dtype)
+    sc = oracle.pyramid_scores(Q, K, cfg.levels, cfg.factor)
+    nblk = cfg.n_ctx // cfg.q_block
+    done = 0
+    while time.perf_counter() - t0 < budget_s or done == 0:
+        blk = nblk - 1 - (done * 37) % nblk
+        sel = oracle.block_select(sc, blk, cfg.n_ctx, cfg.levels, cfg.factor, cfg.q_block,
+                                  cfg.block_top_k)
+        LH.prefill_block(Q, K, V, kc, vc, sel, blk, cfg.q_block, cfg.levels, cfg.factor)
+        oracle.block_grads(Q, K, V, kc, vc, sel, blk, cfg.q_block, cfg.levels, cfg.factor, dO)
+        done += 1
+    spent = time.perf_counter() - t0
+    return {"value": done * cfg.q_block / spent, "unit": "tokens/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"{done} query blocks of one head of {cfg.name} (pyramid and scores of "
+                      f"the head once, then selection + attention + its gradients per block; "
+                      f"the scatter of the gradients is not included), fp64 numpy, {spent:.1f} s"}
 
 
 if __name__ == "__main__":

@@ -119,7 +119,7 @@ __global__ __launch_bounds__(256) void bwd_init_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- 2. interval
-constexpr int kIvThreads = 1024;
+constexpr int kIvThreads = 256;
 
 __device__ __forceinline__ bool in_sorted(const int32_t* x, int n, int32_t v) {
   int lo = 0, hi = n;
@@ -130,9 +130,12 @@ __device__ __forceinline__ bool in_sorted(const int32_t* x, int n, int32_t v) {
   return lo < n && x[lo] == v;
 }
 
-__global__ __launch_bounds__(kIvThreads) void bwd_interval_kernel(BwdArgs a) {
-  __shared__ int32_t s_l[3][kListMaxB];          // lists of blocks blk - 1, blk, blk + 1
-  __shared__ int s_bad;
+// Dynamic LDS: the lists of blocks blk - 1, blk and blk + 1, P ids each (P a
+// power of two >= block_top_k).  The pyramid selection writes its lists in
+// ascending order; lists in another order are sorted here first.
+__global__ __launch_bounds__(kIvThreads) void bwd_interval_kernel(BwdArgs a, int P) {
+  extern __shared__ int32_t s_dyn[];
+  int32_t* s_l[3] = {s_dyn, s_dyn + P, s_dyn + 2 * P};
   const int blk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int32_t* cnts = a.blk_count + (int64_t)bh * a.nblk;
   int n[3];
@@ -148,30 +151,33 @@ __global__ __launch_bounds__(kIvThreads) void bwd_interval_kernel(BwdArgs a) {
     }
     n[r] = c;
   }
-  int P = 2;
-  while (P < max(n[0], max(n[1], n[2]))) P <<= 1;
-  if (tid == 0) s_bad = 0;
+  int unsorted = 0;
 #pragma unroll
   for (int r = 0; r < 3; ++r) {
     const int32_t* lst = a.blk_idx + ((int64_t)bh * a.nblk + (blk - 1 + r)) * a.K;
-    for (int i = tid; i < P; i += kIvThreads) s_l[r][i] = (i < n[r]) ? lst[i] : INT32_MAX;
+    for (int i = tid; i < P; i += kIvThreads) {
+      const int32_t v = (i < n[r]) ? lst[i] : INT32_MAX;
+      s_l[r][i] = v;
+      if (i + 1 < n[r] && v >= lst[i + 1]) unsorted = 1;
+    }
   }
-  __syncthreads();
-  // ascending bitonic sort of the three lists together
-  for (int k = 2; k <= P; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < P; i += kIvThreads) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const bool up = (i & k) == 0;
+  if (__syncthreads_or(unsorted)) {
+    // ascending bitonic sort of the three lists together
+    for (int k = 2; k <= P; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < P; i += kIvThreads) {
+          const int ixj = i ^ j;
+          if (ixj > i) {
+            const bool up = (i & k) == 0;
 #pragma unroll
-          for (int r = 0; r < 3; ++r) {
-            const int32_t u = s_l[r][i], w = s_l[r][ixj];
-            if ((u > w) == up) { s_l[r][i] = w; s_l[r][ixj] = u; }
+            for (int r = 0; r < 3; ++r) {
+              const int32_t u = s_l[r][i], w = s_l[r][ixj];
+              if ((u > w) == up) { s_l[r][i] = w; s_l[r][ixj] = u; }
+            }
           }
         }
+        __syncthreads();
       }
-      __syncthreads();
     }
   }
   int32_t* last = a.last + (int64_t)bh * a.E;
@@ -188,9 +194,7 @@ __global__ __launch_bounds__(kIvThreads) void bwd_interval_kernel(BwdArgs a) {
     }
     if (!ok) bad = true;
   }
-  if (bad) s_bad = 1;
-  __syncthreads();
-  if (tid == 0 && s_bad) atomicOr(a.err + bh, 1u);
+  if (__syncthreads_or(bad) && tid == 0) atomicOr(a.err + bh, 1u);
 }
 
 // ---------------------------------------------------------------- 3. prefix
@@ -602,53 +606,83 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- 6. reduce
-// One wave per entry: lane holds dims 2 lane, 2 lane + 1.
-template <bool COARSE>
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
-  const int bh = blockIdx.y, lane = threadIdx.x & 63;
-  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int n = COARSE ? a.Nc : a.N;
-  if (w >= n) return;
-  const int32_t f = COARSE ? a.N + w : w;
+// Lane holds dims 2 lane, 2 lane + 1 of a row.  Sum of partial rows r0 + w,
+// r0 + w + stride, ... < r1 of one entry (bf16 pairs, eight rows in flight).
+__device__ __forceinline__ void sum_rows(const uint32_t* pk, const uint32_t* pv, int64_t r0,
+                                         int64_t r1, int stride, float2& sk, float2& sv) {
+  constexpr int U = 8;
+  int64_t r = r0;
+  for (; r + (int64_t)(U - 1) * stride < r1; r += (int64_t)U * stride) {
+    uint32_t xk[U], xv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      xk[u] = pk[(r + (int64_t)u * stride) * (kD / 2)];
+      xv[u] = pv[(r + (int64_t)u * stride) * (kD / 2)];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      sk.x += __uint_as_float(xk[u] << 16);
+      sk.y += __uint_as_float(xk[u] & 0xFFFF0000u);
+      sv.x += __uint_as_float(xv[u] << 16);
+      sv.y += __uint_as_float(xv[u] & 0xFFFF0000u);
+    }
+  }
+  for (; r < r1; r += stride) {
+    const uint32_t xk = pk[r * (kD / 2)], xv = pv[r * (kD / 2)];
+    sk.x += __uint_as_float(xk << 16);
+    sk.y += __uint_as_float(xk & 0xFFFF0000u);
+    sv.x += __uint_as_float(xv << 16);
+    sv.y += __uint_as_float(xv & 0xFFFF0000u);
+  }
+}
+
+// Coarse entries (chosen by many blocks): one 256-thread workgroup per
+// entry, wave w summing rows w, w + 4, ...; the four sums are added in wave
+// order.
+__global__ __launch_bounds__(256) void bwd_reduce_coarse_kernel(BwdArgs a) {
+  __shared__ float2 s_k[4][64], s_v[4][64];
+  const int bh = blockIdx.y, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int w = blockIdx.x;
+  const int32_t f = a.N + w;
   const bool bad = a.err[bh] != 0;
   float2 sk = make_float2(0.f, 0.f), sv = sk;
   if (!bad) {
     const int32_t* base = a.base + (int64_t)bh * (a.E + 1);
-    const int64_t r0 = base[f], r1 = base[f + 1];
     const uint32_t* pk = reinterpret_cast<const uint32_t*>(a.part_k) + (int64_t)bh * a.R * (kD / 2) + lane;
     const uint32_t* pv = reinterpret_cast<const uint32_t*>(a.part_v) + (int64_t)bh * a.R * (kD / 2) + lane;
-    int64_t r = r0;
-    constexpr int U = 8;
-    for (; r + U <= r1; r += U) {
-      uint32_t xk[U], xv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        xk[u] = pk[(r + u) * (kD / 2)];
-        xv[u] = pv[(r + u) * (kD / 2)];
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        sk.x += __uint_as_float(xk[u] << 16);
-        sk.y += __uint_as_float(xk[u] & 0xFFFF0000u);
-        sv.x += __uint_as_float(xv[u] << 16);
-        sv.y += __uint_as_float(xv[u] & 0xFFFF0000u);
-      }
-    }
-    for (; r < r1; ++r) {
-      const uint32_t xk = pk[r * (kD / 2)], xv = pv[r * (kD / 2)];
-      sk.x += __uint_as_float(xk << 16);
-      sk.y += __uint_as_float(xk & 0xFFFF0000u);
-      sv.x += __uint_as_float(xv << 16);
-      sv.y += __uint_as_float(xv & 0xFFFF0000u);
-    }
+    sum_rows(pk, pv, (int64_t)base[f] + wv, base[f + 1], 4, sk, sv);
   }
-  if constexpr (COARSE) {
+  s_k[wv][lane] = sk;
+  s_v[wv][lane] = sv;
+  __syncthreads();
+  if (wv == 0) {
+#pragma unroll
+    for (int u = 1; u < 4; ++u) {
+      sk.x += s_k[u][lane].x;
+      sk.y += s_k[u][lane].y;
+      sv.x += s_v[u][lane].x;
+      sv.y += s_v[u][lane].y;
+    }
     const int64_t o = ((int64_t)bh * a.Nc + w) * kD;
     reinterpret_cast<float2*>(a.coarse_k + o)[lane] = sk;
     reinterpret_cast<float2*>(a.coarse_v + o)[lane] = sv;
-  } else {
-    // each coarse ancestor's sum, divided by the rows it covers
-    for (int l = 1; l < a.levels && !bad; ++l) {
+  }
+}
+
+// Level-0 rows: one wave per row, its own partial rows, then each coarse
+// ancestor's sum divided by the rows it covers.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
+  const int bh = blockIdx.y, lane = threadIdx.x & 63;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= a.N) return;
+  const bool bad = a.err[bh] != 0;
+  float2 sk = make_float2(0.f, 0.f), sv = sk;
+  if (!bad) {
+    const int32_t* base = a.base + (int64_t)bh * (a.E + 1);
+    const uint32_t* pk = reinterpret_cast<const uint32_t*>(a.part_k) + (int64_t)bh * a.R * (kD / 2) + lane;
+    const uint32_t* pv = reinterpret_cast<const uint32_t*>(a.part_v) + (int64_t)bh * a.R * (kD / 2) + lane;
+    sum_rows(pk, pv, base[w], base[w + 1], 1, sk, sv);
+    for (int l = 1; l < a.levels; ++l) {
       const int j = w / a.span[l];
       if (j >= a.cnt[l]) continue;
       const int64_t o = ((int64_t)bh * a.Nc + (a.off[l] - a.N) + j) * kD;
@@ -660,16 +694,16 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
       sv.x += cv.x * inv;
       sv.y += cv.y * inv;
     }
-    const int64_t o = ((int64_t)bh * a.N + w) * kD;
-    if (bad) {
-      const float2 nan2 = make_float2(NAN, NAN);
-      sk = nan2;
-      sv = nan2;
-      reinterpret_cast<float2*>(a.dq + o)[lane] = nan2;
-    }
-    reinterpret_cast<float2*>(a.dk + o)[lane] = sk;
-    reinterpret_cast<float2*>(a.dv + o)[lane] = sv;
   }
+  const int64_t o = ((int64_t)bh * a.N + w) * kD;
+  if (bad) {
+    const float2 nan2 = make_float2(NAN, NAN);
+    sk = nan2;
+    sv = nan2;
+    reinterpret_cast<float2*>(a.dq + o)[lane] = nan2;
+  }
+  reinterpret_cast<float2*>(a.dk + o)[lane] = sk;
+  reinterpret_cast<float2*>(a.dv + o)[lane] = sv;
 }
 
 hipError_t launch_prefill_backward(const BwdArgs& a, int d, hipStream_t s) {
@@ -682,15 +716,22 @@ hipError_t launch_prefill_backward(const BwdArgs& a, int d, hipStream_t s) {
   const int64_t rows = (int64_t)nh * a.N;
   const int init_blocks = (int)std::min<int64_t>(8192, (rows * 64 + 255) / 256);
   hipLaunchKernelGGL(bwd_init_kernel, dim3(init_blocks), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(bwd_interval_kernel, dim3(a.nblk, nh), dim3(kIvThreads), 0, s, a);
+  int P = 2;
+  while (P < a.K) P <<= 1;
+  const size_t iv_lds = 3 * (size_t)P * sizeof(int32_t);
+  if (iv_lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_interval_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)iv_lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(bwd_interval_kernel, dim3(a.nblk, nh), dim3(kIvThreads), iv_lds, s, a, P);
   hipLaunchKernelGGL(bwd_prefix_kernel, dim3(nh), dim3(kPxThreads), 0, s, a);
   const int hpx = (nh + 7) / 8;
   const dim3 units(8 * hpx * a.nblk);
   hipLaunchKernelGGL(bwd_dq_kernel, units, dim3(kDqThreads), 0, s, a);
   hipLaunchKernelGGL(bwd_dkv_kernel, units, dim3(kKvThreads), 0, s, a);
-  if (a.Nc > 0)
-    hipLaunchKernelGGL(bwd_reduce_kernel<true>, dim3((a.Nc + 3) / 4, nh), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(bwd_reduce_kernel<false>, dim3((a.N + 3) / 4, nh), dim3(256), 0, s, a);
+  if (a.Nc > 0) hipLaunchKernelGGL(bwd_reduce_coarse_kernel, dim3(a.Nc, nh), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((a.N + 3) / 4, nh), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

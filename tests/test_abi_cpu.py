@@ -322,3 +322,38 @@ def test_s2o_validation():
     # the first pass needs sinks or a window
     assert _decode(_decode_params(s2o_tau=0.01, sinks=0, window=0, head_kind=[1] * 8), b)[0] == \
         sa.SA_ERR_INVALID_ARG
+
+
+def test_prefill_backward_validation_and_size():
+    """The backward pass: its workspace holds, per head, the per-entry
+    tables and one bf16 partial row of dK and of dV per (block, chosen
+    entry) and per level-0 key; grouped heads, fp32, d = 64 and a missing
+    gradient buffer are refused before anything is launched."""
+    b = _full_bufs()
+    for name in ("grad_out", "lse", "grad_q", "grad_k", "grad_v"):
+        setattr(b, name, FAKE)
+    ok = dict(batch=2, n_q_heads=4, n_kv_heads=4, head_dim=128, n_ctx=1024, levels=3, factor=4,
+              q_block=128, block_top_k=300)
+    n = ctypes.c_size_t(0)
+    pf = sa.make_params(**ok)
+    assert sa.raw_call("prefill_backward", ctypes.byref(pf), ctypes.byref(b), None,
+                       ctypes.byref(n), None) == sa.SA_OK
+    bh, N, E, nblk = 2 * 4, 1024, 1024 + 256 + 64, 8
+    R = N + nblk * 300
+    assert n.value >= bh * R * 128 * 2 * 2 + bh * (256 + 64) * 128 * 4 * 2
+    assert n.value <= bh * R * 128 * 2 * 2 + bh * (256 + 64) * 128 * 4 * 2 + bh * (N + 2 * E + 2) * 4 + 64 * 1024
+    for kw, code in ((dict(n_kv_heads=2), sa.SA_ERR_UNSUPPORTED),
+                     (dict(dtype="fp32"), sa.SA_ERR_UNSUPPORTED),
+                     (dict(head_dim=64), sa.SA_ERR_UNSUPPORTED),
+                     (dict(block_top_k=8193), sa.SA_ERR_UNSUPPORTED),
+                     (dict(n_ctx=1000), sa.SA_ERR_INVALID_ARG)):       # not a multiple of p^(L-1)
+        pf = sa.make_params(**{**ok, **kw})
+        assert sa.raw_call("prefill_backward", ctypes.byref(pf), ctypes.byref(b), None,
+                           ctypes.byref(n), None) == code, kw
+    pf = sa.make_params(**ok)
+    n = ctypes.c_size_t(1 << 40)
+    for name in ("grad_out", "lse", "grad_q", "grad_k", "grad_v"):
+        setattr(b, name, None)
+        assert sa.raw_call("prefill_backward", ctypes.byref(pf), ctypes.byref(b), FAKE,
+                           ctypes.byref(n), None) == sa.SA_ERR_INVALID_ARG, name
+        setattr(b, name, FAKE)

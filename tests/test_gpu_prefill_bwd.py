@@ -235,3 +235,29 @@ def test_prefill_backward_full_size_sampled():
     for k in ("dq", "dk", "dv"):
         assert torch.isfinite(run.t[k]).all(), k
     log("full-size backward worst error / bound", worst)
+
+
+def test_prefill_backward_lists_in_any_order():
+    """The same selection with every list of head 1 shuffled: the backward
+    sorts them itself.  dK and dV come out bit-identical (each key's partial
+    row does not depend on its slot); dQ sums its keys in list order, so it
+    only agrees to fp32 rounding."""
+    cfg = SMALL.with_(n_ctx=2048)
+    inp = workloads.prefill_inputs(cfg, 19)
+    run = BwdRun(cfg, inp, workloads.prefill_grad_inputs(cfg, 20))
+    run.forward_backward()
+    torch.cuda.synchronize()
+    ref = {k: run.t[k].clone() for k in ("dq", "dk", "dv")}
+    gen = torch.Generator().manual_seed(21)
+    cnt = run.t["blk_count"][0, 1].cpu()
+    for blk in range(run.nblk):
+        c = int(cnt[blk])
+        if c > 1:
+            perm = torch.randperm(c, generator=gen).to(DEV)
+            run.t["blk_idx"][0, 1, blk, :c] = run.t["blk_idx"][0, 1, blk, :c][perm]
+    run.backward()
+    torch.cuda.synchronize()
+    assert torch.equal(run.t["dk"], ref["dk"]) and torch.equal(run.t["dv"], ref["dv"])
+    assert torch.equal(run.t["dq"][0, 0], ref["dq"][0, 0])
+    scale = ref["dq"][0, 1].abs().max().item()
+    assert (run.t["dq"][0, 1] - ref["dq"][0, 1]).abs().max().item() <= 1e-5 * scale
