@@ -278,11 +278,15 @@ __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     dl[nt] = valid ? a.delta[(int64_t)bh * a.N + q0 + ql] : 0.f;
   }
 
-  // key sequence entry e -> row byte offset (past the end: row 0, masked)
-  auto seq_row = [&](int e) __attribute__((always_inline)) -> uint32_t {
-    if (e < c_sel) return row_of(a, list[e]);
+  // key sequence entry e with list entry f -> row byte offset (past the
+  // end: row 0, masked)
+  auto seq_row = [&](int e, int32_t f) __attribute__((always_inline)) -> uint32_t {
+    if (e < c_sel) return row_of(a, f);
     if (e < T) return (uint32_t)(q0 + e - c_sel) * kRowB;
     return 0u;
+  };
+  auto list_at = [&](int e) __attribute__((always_inline)) -> int32_t {
+    return (e < c_sel) ? list[e] : 0;
   };
   auto rptr = [](uint32_t r, const char* b0, const char* bc) __attribute__((always_inline)) {
     return reinterpret_cast<const u32x4b*>((((int32_t)r < 0) ? bc : b0) + (r & ~kCoarseB));
@@ -292,15 +296,20 @@ __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int gk_key = tid >> 3, gk_seg = tid & 7;
   const int gt_kp = tid & 15, gt_seg = tid >> 4;
   struct Rows { u32x4b k0, k1, v0, v1, t0, t1; };
-  auto gather = [&](int x, Rows& r) __attribute__((always_inline)) {
-    const uint32_t ra = seq_row(x * kKT + gk_key);
+  // the list entries of this thread's three rows of tile x
+  struct Ids { int32_t a, b0, b1; };
+  auto ids_of = [&](int x) __attribute__((always_inline)) -> Ids {
+    return Ids{list_at(x * kKT + gk_key), list_at(x * kKT + 2 * gt_kp), list_at(x * kKT + 2 * gt_kp + 1)};
+  };
+  auto gather = [&](int x, const Ids& id, Rows& r) __attribute__((always_inline)) {
+    const uint32_t ra = seq_row(x * kKT + gk_key, id.a);
     const u32x4b* pk = rptr(ra, kb + 16 * gk_seg, pkb + 16 * gk_seg);
     const u32x4b* pv = rptr(ra, vb + 16 * gk_seg, pvb + 16 * gk_seg);
     r.k0 = pk[0];
     r.k1 = pk[8];
     r.v0 = pv[0];
     r.v1 = pv[8];
-    const uint32_t rb0 = seq_row(x * kKT + 2 * gt_kp), rb1 = seq_row(x * kKT + 2 * gt_kp + 1);
+    const uint32_t rb0 = seq_row(x * kKT + 2 * gt_kp, id.b0), rb1 = seq_row(x * kKT + 2 * gt_kp + 1, id.b1);
     r.t0 = *rptr(rb0, kb + 16 * gt_seg, pkb + 16 * gt_seg);
     r.t1 = *rptr(rb1, kb + 16 * gt_seg, pkb + 16 * gt_seg);
   };
@@ -347,14 +356,19 @@ __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const float sc = a.scale_log2;
 
   Rows cur;
-  gather(0, cur);
+  gather(0, ids_of(0), cur);
   stash(0, cur);
+  Ids id_next = ids_of(1);
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     Rows nxt;
     const bool more = t + 1 < ntiles;
-    if (more) gather(t + 1, nxt);
+    Ids id_after{0, 0, 0};
+    if (more) {
+      gather(t + 1, id_next, nxt);
+      id_after = ids_of(t + 2);
+    }
     f32x4b s[2][2], dp[2][2];
     rows_x_frags(s_k[buf], qf, s);
     rows_x_frags(s_v[buf], df, dp);
@@ -388,6 +402,7 @@ __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, __builtin_bit_cast(bf16x8b, dsp[nt]), acc[dt][nt], 0, 0, 0);
     }
     if (more) stash(buf ^ 1, nxt);
+    id_next = id_after;
     __syncthreads();
   }
 
@@ -409,13 +424,15 @@ __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- 5. dK / dV partials
 constexpr int kKvThreads = 512;
-constexpr int kQRow = kD + 8;           // staged tile stride (bf16 elements)
+constexpr int kQRow = kD + 8;           // row-major staged tile stride (bf16 elements)
+constexpr int kQtRow = kD + 4;          // transposed staged tile stride: 66 dwords, so the
+                                        // 8-byte reads of 16 lanes (16 rows) hit distinct banks
 
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_q[128 * kQRow];    // Q[q][d]
-  __shared__ __attribute__((aligned(16))) uint16_t s_qt[128 * kQRow];   // Q^T[d][q]
+  __shared__ __attribute__((aligned(16))) uint16_t s_qt[128 * kQtRow];  // Q^T[d][q]
   __shared__ __attribute__((aligned(16))) uint16_t s_do[128 * kQRow];   // dO[q][d]
-  __shared__ __attribute__((aligned(16))) uint16_t s_dot[128 * kQRow];  // dO^T[d][q]
+  __shared__ __attribute__((aligned(16))) uint16_t s_dot[128 * kQtRow]; // dO^T[d][q]
   __shared__ __attribute__((aligned(16))) float s_lse[128];
   __shared__ __attribute__((aligned(16))) float s_dl[128];
   int bh, blk;
@@ -463,8 +480,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
     for (int m = 0; m < 32; ++m) {
       const int sh = (m & 1) * 16;
-      s_qt[(c0 + m) * kQRow + row] = (uint16_t)(qw[m >> 1] >> sh);
-      s_dot[(c0 + m) * kQRow + row] = (uint16_t)(gw[m >> 1] >> sh);
+      s_qt[(c0 + m) * kQtRow + row] = (uint16_t)(qw[m >> 1] >> sh);
+      s_dot[(c0 + m) * kQtRow + row] = (uint16_t)(gw[m >> 1] >> sh);
     }
     if (tid < 128) {
       const bool v = tid < nq;
@@ -479,13 +496,17 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
   uint16_t* pkd = a.part_k + (int64_t)bh * a.R * kD;
   uint16_t* pvd = a.part_v + (int64_t)bh * a.R * kD;
 
-  // this lane's key of a step: sequence entry e = step + 16 w + l16 ->
-  // (row byte offset, partial row); partial row -1: nothing to write
-  auto key_of = [&](int e, uint32_t& r, int64_t& pr) __attribute__((always_inline)) {
+  // the list entry of sequence entry e (read a step before its rows)
+  auto list_at = [&](int e) __attribute__((always_inline)) -> int32_t {
+    return (e < c_sel) ? list[e] : 0;
+  };
+  // this lane's key of a step: sequence entry e = step + 16 w + l16 with
+  // list entry f -> (row byte offset, partial row); partial row -1: nothing
+  // to write
+  auto key_of = [&](int e, int32_t f, uint32_t& r, int64_t& pr) __attribute__((always_inline)) {
     r = 0u;
     pr = -1;
     if (e < c_sel) {
-      const int32_t f = list[e];
       r = row_of(a, f);
       if ((unsigned)f < (unsigned)a.E)
         pr = (int64_t)base[f] + (f < a.N ? 1 : 0) + (blk - first_block(a, f));
@@ -510,27 +531,31 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
   int e = 16 * wid + l16;
   uint32_t r;
   int64_t pr;
-  key_of(e, r, pr);
+  key_of(e, list_at(e), r, pr);
   bf16x8b kf[4], vf[4];
   load_frags(r, kf, vf);
+  int32_t f_next = list_at(e + 128);
   for (int step = 0; step < T; step += 128) {
-    // the next step's key and rows, in flight under this step's products
+    // the next step's key and rows, in flight under this step's products,
+    // and the list entry of the step after it
     const int en = e + 128;
     uint32_t rn;
     int64_t prn;
     bf16x8b kn[4], vn[4];
     const bool more = step + 128 < T;
+    int32_t f_after = 0;
     if (more) {
-      key_of(en, rn, prn);
+      key_of(en, f_next, rn, prn);
       load_frags(rn, kn, vn);
+      f_after = list_at(en + 128);
     }
-    // S[q][e] = Q K^T and dP[q][e] = dO V^T over all 128 queries:
-    // qt-th tile rows q = 16 qt + 4 jg + i, column e = l16
+    // S[q][e] = Q K^T and dP[q][e] = dO V^T over all 128 queries, 32 at a
+    // time (query group c: tiles qt = 2c, 2c + 1, rows q = 16 qt + 4 jg + i,
+    // column e = l16).  Software-pipelined: group c + 1's products are issued
+    // before group c's softmax work, so the two overlap within the wave.
     uint4 pb[4], db[4];
     const bool ev = e < T;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      f32x4b s2[2], d2[2];
+    auto products = [&](int c, f32x4b (&s2)[2], f32x4b (&d2)[2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int qt = 2 * c + h;
@@ -545,8 +570,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
         s2[h] = cs;
         d2[h] = cd;
       }
-      // P and dS, packed as B operands over queries 32 c .. 32 c + 31:
-      // k-slot 8 jg + j is query 32 c + 4 jg + j (j < 4) or 32 c + 16 + 4 jg + (j - 4)
+    };
+    // P and dS of group c, packed as B operands over queries 32 c .. 32 c + 31:
+    // k-slot 8 jg + j is query 32 c + 4 jg + j (j < 4) or 32 c + 16 + 4 jg + (j - 4)
+    auto softmax_grad = [&](int c, const f32x4b (&s2)[2], const f32x4b (&d2)[2]) __attribute__((always_inline)) {
       float p[8], ds[8];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -565,17 +592,31 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
       }
       pb[c] = make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7]));
       db[c] = make_uint4(pack_bf16(ds[0], ds[1]), pack_bf16(ds[2], ds[3]), pack_bf16(ds[4], ds[5]), pack_bf16(ds[6], ds[7]));
-      // keep the next query group's operand reads from being hoisted here
-      // (all of them at once would not fit in registers)
+    };
+    {
+      f32x4b sa[2], da[2], sb[2], db2[2];
+      products(0, sa, da);
+      __builtin_amdgcn_sched_barrier(0);
+      products(1, sb, db2);
+      softmax_grad(0, sa, da);
+      __builtin_amdgcn_sched_barrier(0);
+      products(2, sa, da);
+      softmax_grad(1, sb, db2);
+      __builtin_amdgcn_sched_barrier(0);
+      products(3, sb, db2);
+      softmax_grad(2, sa, da);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax_grad(3, sb, db2);
       __builtin_amdgcn_sched_barrier(0);
     }
     // dV^T[d][e] = sum_q dO^T[d][q] P[q][e], dK^T[d][e] = sum_q Q^T[d][q] dS[q][e]:
-    // rows d = 16 dt + 4 jg + i, column e = l16
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      f32x4b cv = {0.f, 0.f, 0.f, 0.f}, ck = cv;
-      const uint16_t* vrow = s_dot + (16 * dt + l16) * kQRow;
-      const uint16_t* krow = s_qt + (16 * dt + l16) * kQRow;
+    // rows d = 16 dt + 4 jg + i, column e = l16; tile dt + 1's products are
+    // issued before tile dt's results are packed and stored
+    auto dvdk = [&](int dt, f32x4b& cv, f32x4b& ck) __attribute__((always_inline)) {
+      cv = (f32x4b){0.f, 0.f, 0.f, 0.f};
+      ck = cv;
+      const uint16_t* vrow = s_dot + (16 * dt + l16) * kQtRow;
+      const uint16_t* krow = s_qt + (16 * dt + l16) * kQtRow;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const uint2 v0 = *reinterpret_cast<const uint2*>(vrow + 32 * c + 4 * jg);
@@ -587,11 +628,26 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
         ck = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8b, make_uint4(k0.x, k0.y, k1.x, k1.y)),
                                                      __builtin_bit_cast(bf16x8b, db[c]), ck, 0, 0, 0);
       }
+    };
+    auto store = [&](int dt, f32x4b cv, f32x4b ck) __attribute__((always_inline)) {
       if (pr >= 0) {
         const int64_t o = pr * kD + 16 * dt + 4 * jg;
         *reinterpret_cast<uint2*>(pvd + o) = make_uint2(pack_bf16(cv[0], cv[1]), pack_bf16(cv[2], cv[3]));
         ck *= a.scale;
         *reinterpret_cast<uint2*>(pkd + o) = make_uint2(pack_bf16(ck[0], ck[1]), pack_bf16(ck[2], ck[3]));
+      }
+    };
+    {
+      f32x4b va, ka, vb, kb2;
+      dvdk(0, va, ka);
+#pragma unroll
+      for (int dt = 0; dt < 8; dt += 2) {
+        __builtin_amdgcn_sched_barrier(0);
+        dvdk(dt + 1, vb, kb2);
+        store(dt, va, ka);
+        __builtin_amdgcn_sched_barrier(0);
+        if (dt + 2 < 8) dvdk(dt + 2, va, ka);
+        store(dt + 1, vb, kb2);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -599,6 +655,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
       e = en;
       r = rn;
       pr = prn;
+      f_next = f_after;
 #pragma unroll
       for (int st = 0; st < 4; ++st) { kf[st] = kn[st]; vf[st] = vn[st]; }
     }
