@@ -43,6 +43,8 @@ def parse():
                              "llama3_8b_decode_32k_s2o",
                              "pyramid_prefill_128k", "pyramid_prefill_backward_128k",
                              "llama3_8b_head_split_prefill_32k", "hga_route_prefill_64k"])
+    ap.add_argument("--per-head", action="store_true",
+                    help="decode workloads: one set per query head (per_head_sets)")
     ap.add_argument("--instances", type=int, default=4,
                     help="independent input sets rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -501,7 +503,7 @@ def main():
     elif args.workload == "hga_route_prefill_64k":
         res = run_prefill_routed(args, torch, sa, workloads)
     else:
-        res = run_decode(args, torch, sa, workloads)
+        res = run_decode(args, torch, sa, workloads, per_head=args.per_head)
     if not args.no_extras and args.workload == "llama3_8b_decode_32k":
         other = {}
         for w in ("llama3_8b_decode_128k_topk", "llama3_8b_decode_128k", "hga_route_decode_64k"):

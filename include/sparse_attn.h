@@ -144,10 +144,13 @@ typedef struct sa_params {
  * treat each query head as a group of one: a retrieval head ranks tokens with
  * its own q_idx row, a routed head routes with its own query, against the
  * index keys or summaries of its KV group h / G.  sel_idx is [B,Hq,n_cap] and
- * sel_count [B,Hq], and sparse_attn_decode reads them per query head (the
- * heads of a KV group then share no gathered rows).  Labels must still be
- * equal inside a GQA group, and n_q_heads <= 64.  The index build is the same
- * in both modes.
+ * sel_count [B,Hq], and sparse_attn_decode reads them per query head.  With
+ * bf16 caches, n_ctx <= 147456 and no early stop, the decode still gathers
+ * each row once per KV group: it merges the group's heads' lists into one
+ * (ascending, each position tagged with the heads that chose it) in its
+ * workspace and masks every head to its own set; otherwise each head is
+ * decoded alone.  Labels must still be equal inside a GQA group, and
+ * n_q_heads <= 64.  The index build is the same in both modes.
  */
 
 /* Device pointers owned by the caller; NULL where a call does not use them. */
@@ -282,7 +285,8 @@ int32_t sparse_attn_select(const sa_params* params, const sa_buffers* bufs,
  * window >= 1.  Reads q,
  * k_cache, v_cache, sel_idx, sel_count; writes out.  A selecting group whose
  * sel_count is negative (a selection that reported failure) gets NaN in
- * every output of its query heads.  Needs a workspace; no part of it has to
+ * every output of its query heads (with per_head_sets: a head whose count
+ * is negative gets NaN in its own outputs).  Needs a workspace; no part of it has to
  * start at zero.
  */
 int32_t sparse_attn_decode(const sa_params* params, const sa_buffers* bufs,

@@ -261,10 +261,32 @@ int32_t decode_entry(const sa_params* p, const sa_buffers* b, void* ws, size_t* 
     if (max_splits > kMaxDecodeSplits) return SA_ERR_UNSUPPORTED;
     n_partial = (size_t)p->batch * p->n_q_heads * max_splits * (p->head_dim + 2);
   }
+  // per-head sets on the matrix-core path: each KV group's heads share one
+  // union list with head bits, so every row is gathered once for the group
+  // (decoded as KV groups of G heads with per-head masks)
+  const int Gkv = p->n_q_heads / p->n_kv_heads;
+  const bool head_union = p->per_head_sets && p->dtype == SA_BF16 && !s2o_mask && Gkv > 1 &&
+                          any_list && p->n_ctx <= sa::kUnionMaxN;
+  SelGroups ug = u;
+  if (head_union) {
+    ug.n = p->n_kv_heads; ug.G = Gkv; ug.kv_div = 1;
+    for (int g = 0; g < p->n_kv_heads; ++g) ug.kind[g] = u.kind[g * Gkv];
+    local_mask = 0;
+    for (int g = 0; g < ug.n; ++g)
+      if (ug.kind[g] == SA_HEAD_LOCAL) local_mask |= 1ull << g;
+    const int groups = p->batch * ug.n;
+    target_items = (Gkv > 4 ? 1 : 2) * compute_units();
+    max_splits = target_items + groups;
+    if (max_splits > kMaxDecodeItems) return SA_ERR_UNSUPPORTED;
+    n_partial = (size_t)max_splits * Gkv * (p->head_dim + 2);
+  }
   Carver c(ws);
   float* partial = c.take<float>(n_partial);
-  int2* plan = (p->dtype == SA_BF16) ? c.take<int2>((size_t)p->batch * u.n) : nullptr;
+  int2* plan = (p->dtype == SA_BF16) ? c.take<int2>((size_t)p->batch * ug.n) : nullptr;
   float* s2o_state = s2o_mask ? c.take<float>((size_t)p->batch * u.n * G * (p->head_dim + 2)) : nullptr;
+  int32_t* union_idx = head_union ? c.take<int32_t>((size_t)p->batch * p->n_kv_heads * p->n_cap) : nullptr;
+  int32_t* union_count = head_union ? c.take<int32_t>((size_t)p->batch * p->n_kv_heads) : nullptr;
+
   if ((st = workspace_gate(ws, ws_bytes, c.size()))) return st < 0 ? st : SA_OK;
   if (!b->q || !b->k_cache || !b->v_cache || !b->out) return SA_ERR_INVALID_ARG;
   if (any_list && (!b->sel_idx || !b->sel_count)) return SA_ERR_INVALID_ARG;
@@ -285,6 +307,20 @@ int32_t decode_entry(const sa_params* p, const sa_buffers* b, void* ws, size_t* 
   a.s2o_tau = p->s2o_tau;
   a.s2o = s2o_units;
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (head_union) {
+    sa::HeadUnionArgs ua{};
+    ua.sel_idx = b->sel_idx; ua.sel_count = b->sel_count;
+    ua.union_idx = union_idx; ua.union_count = union_count;
+    ua.B = p->batch; ua.Hq = p->n_q_heads; ua.Hkv = p->n_kv_heads; ua.G = Gkv;
+    ua.n = p->n_ctx; ua.n_cap = p->n_cap;
+    ua.groups.n = 0;
+    for (int g = 0; g < ug.n; ++g)
+      if (ug.kind[g] != SA_HEAD_LOCAL) ua.groups.ids[ua.groups.n++] = g;
+    if ((st = hip_status(sa::launch_head_union(ua, hs)))) return st;
+    a.sel_idx = union_idx; a.sel_count = union_count;
+    a.Hkv = ug.n; a.G = Gkv; a.kv_div = 1;
+    a.head_masks = 1; a.head_count = b->sel_count;
+  }
   if ((st = hip_status(sa::launch_decode(a, p->dtype, p->head_dim, hs)))) return st;
   if (!s2o_mask) return SA_OK;
   return hip_status(sa::launch_decode_s2o(a, p->head_dim, hs));

@@ -148,7 +148,25 @@ struct DecodeArgs {
   float s2o_tau;
   float* s2o_state;
   GroupList s2o;
+  // per-head sets decoded per KV group: sel_idx / sel_count hold each
+  // group's union of its heads' sets, an entry being (head mask << 24 |
+  // position); head_count [B,Hq] are the heads' own counts (a negative one
+  // poisons that head's output)
+  int32_t head_masks;
+  const int32_t* head_count;
 };
+
+// The union of the per-head sets of each selecting KV group.
+struct HeadUnionArgs {
+  const int32_t* sel_idx;     // [B,Hq,n_cap] each head's positions
+  const int32_t* sel_count;   // [B,Hq]
+  int32_t* union_idx;         // [B,Hkv,n_cap] (head mask << 24 | position), ascending
+  int32_t* union_count;       // [B,Hkv]
+  int32_t B, Hq, Hkv, G, n, n_cap;
+  GroupList groups;           // the selecting KV groups
+};
+
+constexpr int kUnionMaxN = 144 * 1024;   // positions whose masks fit in LDS (one byte each)
 
 constexpr int kS2oMax = 8192;     // candidates per group the early-stop kernel stages
 
@@ -204,6 +222,7 @@ hipError_t launch_pyramid_select(const PyrSelectArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int d, hipStream_t s);
 hipError_t launch_decode_s2o(const DecodeArgs& a, int d, hipStream_t s);
+hipError_t launch_head_union(const HeadUnionArgs& a, hipStream_t s);
 hipError_t launch_select_order(const SelectArgs& a, int dtype, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int d, hipStream_t s);
 hipError_t launch_prefill_heads(const PrefillArgs& a, int d, hipStream_t s);

@@ -35,6 +35,8 @@
 //     ahead (three register sets in rotation); every load is unconditional
 //     (rows past the end read the group's row 0 and are masked), so each wait
 //     is a partial one and two tiles of loads stay in flight.
+#include <algorithm>
+
 #include "args.hpp"
 #include "common.hpp"
 
@@ -180,7 +182,9 @@ struct Tile {
   static constexpr int VT = 16 / NCLS;         // V rows per lane per tile
   bf16x8 k[KS];
   uint32_t v[VT];
-  int tok;                                     // this lane's K-role token, -1 if none
+  // this lane's K-role token, -1 if none; with head-mask lists the bits
+  // 24 + i say whether head 4 (lane / 16) + i of the group has it in its set
+  int tok;
 };
 
 template <int D, int G>
@@ -190,7 +194,7 @@ struct DecodeShared {
   float acc[4][8][D];
 };
 
-template <int D, int G, bool LOCAL>
+template <int D, int G, bool LOCAL, bool HM>
 __device__ __forceinline__ void decode_item(const DecodeArgs& a, DecodeShared<D, G>& sh, int item,
                                             int bg, int split, int nsg) {
   using TL = Tile<D>;
@@ -248,9 +252,13 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, DecodeShared<D,
   // issue a tile's K and V loads
   auto issue = [&](int tile, TL& t, int raw) __attribute__((always_inline)) {
     const int e = (qw + tile * Wg) * 16 + kt;
-    const int tok = (e < count && (unsigned)raw < (unsigned)n) ? raw : -1;
+    // head-mask lists: the position is the low 24 bits, the heads the top 8
+    const int pos = HM ? (raw & 0xFFFFFF) : raw;
+    const int tok = (e < count && (unsigned)pos < (unsigned)n)
+                        ? (HM ? pos | (int)((((uint32_t)raw >> 24 >> (4 * jg)) & 0xFu) << 24) : pos)
+                        : -1;
     t.tok = tok;
-    const uint16_t* kp = kbase + (int64_t)max(tok, 0) * D;
+    const uint16_t* kp = kbase + (int64_t)(HM ? max(tok, 0) & 0xFFFFFF : max(tok, 0)) * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
       t.k[s] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 32 * s)));
@@ -261,7 +269,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, DecodeShared<D,
         const int tv1 = __builtin_amdgcn_readlane(tok, r * NCLS + 1);
         tv = vc ? tv1 : tv;
       }
-      const uint16_t* vrow = vbase + (int64_t)max(tv, 0) * D;
+      const uint16_t* vrow = vbase + (int64_t)(HM ? max(tv, 0) & 0xFFFFFF : max(tv, 0)) * D;
       t.v[r] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vrow + vd));
     }
   };
@@ -280,7 +288,11 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, DecodeShared<D,
     const bool valid = t.tok >= 0;
     float sv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sv[i] = valid ? c[i] * sc : -INFINITY;
+    for (int i = 0; i < 4; ++i) {
+      // lane group jg holds heads 4 jg .. 4 jg + 3 of its token
+      const bool mine = !HM || ((t.tok >> (24 + i)) & 1);
+      sv[i] = (valid && mine) ? c[i] * sc : -INFINITY;
+    }
     float alpha[G];
     bool moved = false;
 #pragma unroll
@@ -393,7 +405,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, DecodeShared<D,
   }
 }
 
-template <int D, int G>
+template <int D, int G, bool HM>
 __global__ __launch_bounds__(kMfmaThreads, (G > 4 ? 1 : 2)) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ DecodeShared<D, G> sh;
   // every wave makes the same plan; wave 0 of workgroup 0 also records every
@@ -401,8 +413,8 @@ __global__ __launch_bounds__(kMfmaThreads, (G > 4 ? 1 : 2)) void decode_mfma_ker
   const PlanItem pl = plan_item(a, blockIdx.x, (blockIdx.x == 0 && threadIdx.x < 64) ? a.plan : nullptr);
   const int bg = pl.bg, split = pl.split, nsg = pl.ns;
   if (bg < 0) return;
-  if ((a.local_mask >> (bg % a.Hkv)) & 1ull) decode_item<D, G, true>(a, sh, blockIdx.x, bg, split, nsg);
-  else decode_item<D, G, false>(a, sh, blockIdx.x, bg, split, nsg);
+  if ((a.local_mask >> (bg % a.Hkv)) & 1ull) decode_item<D, G, true, false>(a, sh, blockIdx.x, bg, split, nsg);
+  else decode_item<D, G, false, HM>(a, sh, blockIdx.x, bg, split, nsg);
 }
 
 // Merge the items of one (sequence, query head).  Thread (e, part) owns
@@ -474,8 +486,10 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_item_combine_kernel(Decod
       if (e == 0) { st[D] = M; st[D + 1] = L; }
       return;
     }
-    // a failed selection (negative count) poisons the group's outputs
-    const bool failed = !((a.local_mask >> g) & 1ull) && a.sel_count[bg] < 0;
+    // a failed selection (negative count) poisons the group's outputs (the
+    // head's own, with head-mask lists)
+    const bool failed = !((a.local_mask >> g) & 1ull) &&
+                        (a.head_masks ? a.head_count[(int64_t)b * a.Hq + g * G + h] < 0 : a.sel_count[bg] < 0);
     a.out[((int64_t)b * a.Hq + g * G + h) * D + e] = failed ? __builtin_nanf("") : ((L > 0.f) ? v / L : 0.f);
   }
 }
@@ -483,7 +497,11 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_item_combine_kernel(Decod
 hipError_t launch_decode_mfma(const DecodeArgs& a, int d, hipStream_t s) {
   if (a.max_splits < 1 || a.target_items < 1 || !a.plan) return hipErrorInvalidValue;
   dim3 grid(a.max_splits), block(kMfmaThreads);
-#define SA_DEC(D_, G_) hipLaunchKernelGGL((decode_mfma_kernel<D_, G_>), grid, block, 0, s, a)
+#define SA_DEC(D_, G_)                                                                         \
+  do {                                                                                         \
+    if (a.head_masks) hipLaunchKernelGGL((decode_mfma_kernel<D_, G_, true>), grid, block, 0, s, a); \
+    else hipLaunchKernelGGL((decode_mfma_kernel<D_, G_, false>), grid, block, 0, s, a);        \
+  } while (0)
   if (d == 128) {
     switch (a.G) {
       case 1: SA_DEC(128, 1); break;
@@ -520,6 +538,80 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int d, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
 #undef SA_CMB
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- head union
+// Per-head sets decoded per KV group: the union of the G heads' sets of one
+// (sequence, selecting group), each position tagged with the heads that
+// chose it, so that the decode gathers every row once for all G heads and
+// masks each head's scores to its own set.  One 1024-thread workgroup per
+// (group, sequence): one byte of head bits per position in LDS, ORed in from
+// the heads' lists one head after another, then an ordered compaction (each
+// thread a contiguous run of positions, offsets from one block scan).  Contexts whose masks do not fit in LDS
+// decode each head alone instead.
+constexpr int kUnionThreads = 1024;
+
+__global__ __launch_bounds__(kUnionThreads) void head_union_kernel(HeadUnionArgs a) {
+  extern __shared__ uint32_t s_hm[];          // ceil(n / 4) words: 8 head bits per position
+  __shared__ int32_t s_scan[kUnionThreads / 64];
+  const int g = a.groups.ids[blockIdx.x], b = blockIdx.y, tid = threadIdx.x;
+  const int n = a.n, nw = (n + 3) / 4;
+  for (int i = tid; i < nw; i += kUnionThreads) s_hm[i] = 0u;
+  __syncthreads();
+  // eight list entries per thread in flight, then their head bits ORed in
+  constexpr int U = 8;
+  for (int h = 0; h < a.G; ++h) {
+    const int64_t row = (int64_t)b * a.Hq + g * a.G + h;
+    const int cnt = min(max(a.sel_count[row], 0), n);
+    const int32_t* lst = a.sel_idx + row * a.n_cap;
+    const uint32_t bit = 1u << h;
+    for (int i0 = 0; i0 < cnt; i0 += U * kUnionThreads) {
+      int pos[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * kUnionThreads + tid;
+        pos[u] = (i < cnt) ? lst[i] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if ((unsigned)pos[u] < (unsigned)n) atomicOr(&s_hm[pos[u] >> 2], bit << (8 * (pos[u] & 3)));
+    }
+    __syncthreads();
+  }
+  // ordered compaction: thread t takes a contiguous run of words (one block
+  // scan for the whole group)
+  const int per = (nw + kUnionThreads - 1) / kUnionThreads;
+  const int w0 = min(nw, tid * per), w1 = min(nw, w0 + per);
+  int32_t c = 0;
+  for (int w = w0; w < w1; ++w) {
+    const uint32_t x = s_hm[w];
+    c += ((x & 0xFFu) != 0) + ((x & 0xFF00u) != 0) + ((x & 0xFF0000u) != 0) + ((x >> 24) != 0);
+  }
+  int32_t total;
+  int32_t o = block_exclusive_scan<int32_t, kUnionThreads>(c, s_scan, &total);
+  int32_t* out = a.union_idx + ((int64_t)b * a.Hkv + g) * a.n_cap;
+  for (int w = w0; w < w1; ++w) {
+    const uint32_t x = s_hm[w];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t m = (x >> (8 * k)) & 0xFFu;
+      if (m) out[o++] = (int32_t)((m << 24) | (uint32_t)(4 * w + k));
+    }
+  }
+  if (tid == 0) a.union_count[(int64_t)b * a.Hkv + g] = total;
+}
+
+hipError_t launch_head_union(const HeadUnionArgs& a, hipStream_t s) {
+  if (a.G < 1 || a.G > 8 || a.n < 1 || a.n > kUnionMaxN || a.n_cap < a.n) return hipErrorInvalidValue;
+  if (a.groups.n == 0 || a.B == 0) return hipSuccess;
+  const size_t lds = (size_t)((a.n + 3) / 4) * sizeof(uint32_t);
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&head_union_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(head_union_kernel, dim3(a.groups.n, a.B), dim3(kUnionThreads), lds, s, a);
   return hipGetLastError();
 }
 

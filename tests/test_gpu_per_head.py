@@ -109,10 +109,16 @@ def test_per_head_route_lattice_exact(cfg):
 @pytest.mark.parametrize("cfg", [
     workloads.TINY.with_(n_ctx=3000, n_q_heads=8, n_kv_heads=4, n_ret_q_heads=4),
     workloads.LLAMA_32K.with_(batch=2, n_ctx=4099),
-])
+    workloads.LLAMA_32K.with_(batch=2, n_ctx=4099, n_q_heads=16, n_kv_heads=2, n_ret_q_heads=8),
+    workloads.LLAMA_32K.with_(batch=2, n_ctx=4099, n_q_heads=8, n_kv_heads=4, n_ret_q_heads=4),
+    workloads.LLAMA_32K.with_(batch=1, n_ctx=150000, n_q_heads=8, n_kv_heads=2, n_ret_q_heads=4),
+], ids=lambda c: f"{c.name}-{c.n_ctx}-{c.n_q_heads}-{c.n_kv_heads}")
 def test_per_head_decode_over_given_lists(cfg):
     """The attention stage alone over random per-head lists (and sinks +
-    window for local heads, each head on its own)."""
+    window for local heads, each head on its own).  With bf16 caches the
+    heads of a KV group are decoded together over the union of their sets,
+    each masked to its own (GQA 4, 8 and 2 here); past the union's limit of
+    147456 positions each head is decoded alone (the 150000 case)."""
     log("per-head decode lists", cfg.name, cfg.n_ctx)
     inp = workloads.decode_inputs(cfg, 12)
     run = DecodeRun(cfg, inp, n_cap=cfg.n_ctx + 3, per_head=True)
@@ -122,7 +128,7 @@ def test_per_head_decode_over_given_lists(cfg):
     for b in range(cfg.batch):
         for h in range(cfg.n_q_heads):
             if h in ret:
-                m = int(torch.randint(1, cfg.n_ctx + 1, (1,), generator=gen))
+                m = int(torch.randint(1, min(cfg.n_ctx, 20000) + 1, (1,), generator=gen))
                 T = torch.sort(torch.randperm(cfg.n_ctx, generator=gen)[:m]).values
                 run.t["sel_idx"][b, h, :m] = T.to(DEV, torch.int32)
                 run.t["sel_count"][b, h] = m
@@ -231,3 +237,32 @@ def test_per_head_pipeline_32k_full_size():
     """The 32K decode layer with per-head sets: all 64 retrieval heads
     checked, 8 sampled local heads."""
     _per_head_pipeline(workloads.LLAMA_32K, 1, exact=False, sample_local=8)
+
+
+def test_per_head_failed_head_poisons_only_itself():
+    """A negative count for one head of a retrieval group (a selection that
+    reported failure): that head's output is NaN, the other heads of its
+    group (decoded over the group's union) stay exact."""
+    cfg = workloads.LLAMA_32K.with_(batch=2, n_ctx=3001)
+    inp = workloads.decode_inputs(cfg, 13)
+    run = DecodeRun(cfg, inp, per_head=True)
+    gen = torch.Generator().manual_seed(5)
+    ret = _heads(cfg, workloads.HEAD_RETRIEVAL)
+    sets = {}
+    for b in range(cfg.batch):
+        for h in ret:
+            m = int(torch.randint(1, cfg.n_ctx + 1, (1,), generator=gen))
+            T = torch.sort(torch.randperm(cfg.n_ctx, generator=gen)[:m]).values
+            run.t["sel_idx"][b, h, :m] = T.to(DEV, torch.int32)
+            run.t["sel_count"][b, h] = m
+            sets[(b, h)] = T.numpy()
+    bad = (1, ret[1])
+    run.t["sel_count"][bad] = -1
+    run.decode()
+    torch.cuda.synchronize()
+    out = np64(run.t["out"])
+    assert np.isnan(out[bad]).all()
+    del sets[bad]
+    ref = oracle.decode_step(cfg, np_inputs(inp), sets=sets, per_head=True)
+    err = max(max_err(out[b, h], ref[(b, h)]) for (b, h) in sets)
+    assert err <= BF16_TOL
