@@ -14,7 +14,8 @@ Sources (web summaries of five papers; cited by page title and section):
   top-p selector, sort-free histogram thresholding, sparse decode.
 * "Atencao Global Hierarquica (HGA)" summary - Core mechanism items 1-4:
   64-token chunks split into groups, two-level routing, always-visible sink,
-  local and current chunks, RoPE-aware mixed summaries, exact token attention.
+  local and current chunks, RoPE-aware mixed summaries, exact token attention;
+  Memory architecture: hot / warm (LRU) / cold (host RAM) K/V tiers.
 * "Lighthouse Attention" summary - Methodology 2A-2C: symmetric mean pyramid,
   parameter-free l2 scoring with max inheritance, joint top-K across levels,
   dense attention on the gathered subsequence and scatter back; the backward
@@ -54,5 +55,6 @@ from .lighthouse_bwd import block_grads, pyramid_backward, prefill_grads, n_entr
 from .decode import decode_step, decode_token_sets, decode_token_sets_per_head
 from .prefill_heads import prefill_visible, head_prefill_rows, visible_pairs
 from .s2o import s2o_order, s2o_head
+from .tier import WarmCache, split_positions, tier_rows, needed_groups
 
 __all__ = [n for n in dir() if not n.startswith("_")]

@@ -923,3 +923,71 @@ def test_pyramid_backward_single_key_and_scatter():
     g[0] = 1.0
     np.testing.assert_allclose(oracle.pyramid_backward(g, 8, 3, 2)[:, 0],
                                [1, 0, 1, 1, 2, 2, 2, 2])
+
+
+# ---------------------------------------------------------------- tiered K/V (HGA memory architecture)
+def test_warm_cache_one_group_per_step_is_plain_lru():
+    """With one group per step the warm tier is an ordinary LRU cache:
+    against an OrderedDict LRU on a random access sequence, the same hits
+    and misses and the same resident groups after every step."""
+    from collections import OrderedDict
+    rng = np.random.default_rng(1)
+    cache = oracle.WarmCache(5)
+    ref = OrderedDict()
+    for step, g in enumerate(rng.integers(0, 12, 400).tolist(), start=1):
+        hits, misses, place = cache.step([g], step)
+        if g in ref:
+            ref.move_to_end(g)
+            want = (1, 0)
+        else:
+            if len(ref) == 5:
+                ref.popitem(last=False)
+            ref[g] = True
+            want = (0, 1)
+        assert (hits, misses) == want, step
+        assert sorted(x for x in cache.group if x >= 0) == sorted(ref), step
+
+
+def test_warm_cache_hand_case():
+    """Two slots.  Step 1 needs {5}: slot 0.  Step 2 needs {7}: the empty
+    slot 1.  Step 3 needs {5, 9}: 5 hits in slot 0; 9 evicts 7 (slot 1, the
+    only slot step 3 does not need).  Step 4 needs {7, 9}: 9 hits; 7 takes
+    the least recently used other slot, slot 0 (last used at step 3, same as
+    slot 1, which step 4 needs)."""
+    c = oracle.WarmCache(2)
+    assert c.step([5], 1) == (0, 1, {5: 0})
+    assert c.step([7], 2) == (0, 1, {7: 1})
+    assert c.step([5, 9], 3) == (1, 1, {5: 0, 9: 1})
+    assert c.step([7, 9], 4) == (1, 1, {9: 1, 7: 0})
+    assert c.group == [7, 9] and c.stamp == [4, 4]
+    with pytest.raises(ValueError):
+        c.step([1, 2, 3], 5)
+
+
+def test_tier_rows_round_trip():
+    """Brute force on a small routed list: build the device tier the way the
+    rows say (sink rows, the ring of the last chunks, warm slots filled from
+    the cold store) and read every listed position back from its row."""
+    n, C, grp, sc, lc = 64 * 20 + 17, 64, 16, 2, 3
+    rng = np.random.default_rng(2)
+    K = rng.standard_normal((n, 4))
+    kappa = (n - 1) // C
+    routed = sorted(rng.choice(np.arange(sc * C // grp, (kappa - lc) * C // grp), 6, replace=False))
+    pos = np.concatenate([np.arange(sc * C)] + [np.arange(g * grp, (g + 1) * grp) for g in routed]
+                         + [np.arange((kappa - lc) * C, n)])
+    hot, rt = oracle.split_positions(pos, n, C, grp, sc, lc)
+    assert hot.sum() == sc * C + n - (kappa - lc) * C and rt.sum() == 6 * grp
+    need = oracle.needed_groups(pos, n, C, grp, sc, lc)
+    assert need == [int(g) for g in routed]
+    cache = oracle.WarmCache(8)
+    _, _, place = cache.step(need, 1)
+    rows = oracle.tier_rows(pos, n, C, grp, sc, lc, place)
+    assert len(set(rows.tolist())) == len(rows)               # one row per position
+    ring = (lc + 1) * C
+    tier = np.full((sc * C + ring + 8 * grp, 4), np.nan)
+    tier[:sc * C] = K[:sc * C]
+    for p in range((kappa - lc) * C, n):
+        tier[sc * C + p % ring] = K[p]
+    for g, s in place.items():
+        tier[sc * C + ring + s * grp: sc * C + ring + (s + 1) * grp] = K[g * grp:(g + 1) * grp]
+    np.testing.assert_array_equal(tier[rows], K[pos])
