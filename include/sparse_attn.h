@@ -385,6 +385,56 @@ int32_t sparse_attn_prefill_backward(const sa_params* params, const sa_buffers* 
 int32_t sparse_attn_prefill_heads(const sa_params* params, const sa_buffers* bufs,
                                   void* hip_stream);
 
+/*
+ * Tiered K/V store of the routed decode (HGA summary, Memory architecture:
+ * the whole K/V history in host RAM - cold -, a bounded LRU cache of
+ * recently routed blocks in device memory - warm -, the summaries and the
+ * always-visible windows in device memory - hot; Core mechanism item 4: the
+ * routed groups' token-level K/V rows are brought from host RAM).
+ *
+ * The device tier of each (sequence, KV group) holds dev_rows = hot_rows +
+ * warm_slots * group rows of K (and of V), hot_rows = (sink_chunks +
+ * local_chunks + 1) * chunk: rows [0, sink_chunks * chunk) are the sink
+ * positions themselves, the next (local_chunks + 1) * chunk rows a ring of
+ * the last chunks (position p at row sink_chunks * chunk + p mod that ring),
+ * and warm slot s the rows of one routing group.  The caller keeps the cold
+ * store (every cached token) and the hot rows up to date; the library keeps
+ * the warm slots.
+ */
+typedef struct sa_tier {
+  const void* cold_k;    /* pinned host memory [B,Hkv,n_cap,d]: every cached token's K */
+  const void* cold_v;    /* (allocated with hipHostMalloc, e.g. torch pin_memory)      */
+  void* dev_k;           /* device [B,Hkv,dev_rows,d]                                  */
+  void* dev_v;
+  int32_t warm_slots;    /* slots per (b, KV group); >= top_chunks * top_groups, <= 4096 */
+  int32_t step;          /* this call's stamp: larger than every earlier call's        */
+  int32_t* slot_group;   /* device [B,Hkv,warm_slots] group held, -1 empty (start: -1) */
+  int32_t* slot_stamp;   /* device [B,Hkv,warm_slots] step of last use (start: 0)      */
+  int32_t* stats;        /* device [B,Hkv,2] or NULL: this call's hits and misses      */
+  int32_t* rows;         /* device [B,Hkv,dev_rows]: the lists as rows of the device tier */
+} sa_tier;
+
+/*
+ * sparse_attn_tier_fetch - serve the routed lists of one decode step from
+ * the tiers.  For every routed KV group, after SA_SEL_ROUTE2 wrote its list
+ * (ascending positions) to sel_idx / sel_count: the distinct routing groups
+ * of the list's routed part (positions in [sink_chunks * chunk, (kappa -
+ * local_chunks) * chunk), kappa = (n_ctx - 1) / chunk) that no warm slot
+ * holds are copied from the cold store into slots - empty slots first, then
+ * the least recently used slot the step does not need (ties: lower slot),
+ * missing groups in ascending order - and every slot the step uses takes
+ * the stamp `step`; then the list is written to `rows` (same counts) as rows
+ * of the device tier.  sparse_attn_decode with k_cache / v_cache = dev_k /
+ * dev_v, sel_idx = rows and n_ctx = n_cap = dev_rows then computes the same
+ * outputs as over the whole cache.  Needs
+ * every head routed, per_head_sets == 0, chunk a multiple of group, and
+ * lists of at most 8192 entries (SA_ERR_UNSUPPORTED otherwise); cold
+ * pointers the device cannot reach give SA_ERR_INVALID_ARG.  Calls that
+ * share tables must not overlap.  No workspace.
+ */
+int32_t sparse_attn_tier_fetch(const sa_params* params, const sa_buffers* bufs,
+                               const sa_tier* tier, void* hip_stream);
+
 /* Human-readable name of a status code (static string). */
 const char* sparse_attn_status_string(int32_t status);
 

@@ -34,6 +34,7 @@ SEL_TOPP, SEL_TOPK, SEL_ROUTE2, SEL_PYRAMID_TOPK, SEL_ROUTE2_PREFILL, SEL_TOPK_B
 EXPORTED = ("sparse_attn_index_build", "sparse_attn_select", "sparse_attn_decode",
             "sparse_attn_decode_noalloc", "sparse_attn_prefill_chunked",
             "sparse_attn_prefill_heads", "sparse_attn_prefill_backward",
+            "sparse_attn_tier_fetch",
             "sparse_attn_status_string", "sparse_attn_version")
 
 
@@ -66,6 +67,16 @@ class Buffers(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in _BUF_FIELDS]
 
 
+class Tier(ctypes.Structure):
+    """sa_tier: the cold store (pinned host tensors), the device tier and the
+    warm slots' tables."""
+    _fields_ = [("cold_k", ctypes.c_void_p), ("cold_v", ctypes.c_void_p),
+                ("dev_k", ctypes.c_void_p), ("dev_v", ctypes.c_void_p),
+                ("warm_slots", ctypes.c_int32), ("step", ctypes.c_int32),
+                ("slot_group", ctypes.c_void_p), ("slot_stamp", ctypes.c_void_p),
+                ("stats", ctypes.c_void_p), ("rows", ctypes.c_void_p)]
+
+
 for _name, _args in (
         ("sparse_attn_index_build", [ctypes.POINTER(Params), ctypes.POINTER(Buffers),
                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -89,6 +100,9 @@ _lib.sparse_attn_decode_noalloc.argtypes = [ctypes.POINTER(Params), ctypes.POINT
 _lib.sparse_attn_decode_noalloc.restype = ctypes.c_int32
 _lib.sparse_attn_prefill_heads.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(Buffers),
                                            ctypes.c_void_p]
+_lib.sparse_attn_tier_fetch.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(Buffers),
+                                        ctypes.POINTER(Tier), ctypes.c_void_p]
+_lib.sparse_attn_tier_fetch.restype = ctypes.c_int32
 _lib.sparse_attn_prefill_heads.restype = ctypes.c_int32
 _lib.sparse_attn_status_string.argtypes = [ctypes.c_int32]
 _lib.sparse_attn_status_string.restype = ctypes.c_char_p
@@ -296,6 +310,27 @@ def prefill_backward(params: Params, bufs: Buffers, ws: Optional[Workspace] = No
     _check(_lib.sparse_attn_prefill_backward(ctypes.byref(params), ctypes.byref(bufs),
                                              w.data_ptr(), ctypes.byref(n), _stream(stream)),
            "prefill_backward")
+
+
+def make_tier(*, cold_k, cold_v, dev_k, dev_v, slot_group, slot_stamp, rows, step,
+              stats=None) -> Tier:
+    """Tier struct from tensors (cold_k / cold_v pinned host tensors)."""
+    t = Tier()
+    t.cold_k, t.cold_v = cold_k.data_ptr(), cold_v.data_ptr()
+    t.dev_k, t.dev_v = dev_k.data_ptr(), dev_v.data_ptr()
+    t.warm_slots = int(slot_group.shape[-1])
+    t.step = int(step)
+    t.slot_group, t.slot_stamp = slot_group.data_ptr(), slot_stamp.data_ptr()
+    t.stats = stats.data_ptr() if stats is not None else None
+    t.rows = rows.data_ptr()
+    return t
+
+
+def tier_fetch(params: Params, bufs: Buffers, tier: Tier, stream=None):
+    """Bring the routed groups of this step's lists into the warm slots and
+    write the lists as rows of the device tier (tier.rows)."""
+    _check(_lib.sparse_attn_tier_fetch(ctypes.byref(params), ctypes.byref(bufs), ctypes.byref(tier),
+                                       _stream(stream)), "tier_fetch")
 
 
 def prefill_heads(params: Params, bufs: Buffers, stream=None):

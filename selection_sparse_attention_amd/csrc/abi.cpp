@@ -612,6 +612,52 @@ int32_t sparse_attn_prefill_chunked(const sa_params* p, const sa_buffers* b, voi
   return hip_status(sa::launch_prefill(a, p->head_dim, static_cast<hipStream_t>(stream)));
 }
 
+int32_t sparse_attn_tier_fetch(const sa_params* p, const sa_buffers* b, const sa_tier* t,
+                               void* stream) {
+  int32_t st = check_common(p, b);
+  if (st) return st;
+  if (!t) return SA_ERR_INVALID_ARG;
+  if (p->per_head_sets) return SA_ERR_UNSUPPORTED;
+  SelGroups u;
+  if ((st = sel_groups(p, &u))) return st;
+  for (int g = 0; g < u.n; ++g)
+    if (u.kind[g] != SA_HEAD_ROUTED) return SA_ERR_UNSUPPORTED;
+  if (p->chunk < 1 || p->group < 1 || p->chunk % p->group) return SA_ERR_UNSUPPORTED;
+  if (p->sink_chunks < 0 || p->local_chunks < 0 || p->top_chunks < 1 || p->top_groups < 1)
+    return SA_ERR_INVALID_ARG;
+  const int64_t hot_rows = (int64_t)(p->sink_chunks + p->local_chunks + 1) * p->chunk;
+  const int64_t max_list = hot_rows + (int64_t)p->top_chunks * p->top_groups * p->group;
+  if (max_list > sa::kTierListMax || (int64_t)p->top_chunks * p->top_groups > sa::kTierNeedMax)
+    return SA_ERR_UNSUPPORTED;
+  if (t->warm_slots < (int64_t)p->top_chunks * p->top_groups || t->warm_slots > sa::kTierSlotsMax)
+    return SA_ERR_INVALID_ARG;
+  if (!t->cold_k || !t->cold_v || !t->dev_k || !t->dev_v || !t->slot_group || !t->slot_stamp ||
+      !t->rows || !b->sel_idx || !b->sel_count)
+    return SA_ERR_INVALID_ARG;
+  const int64_t dev_rows = hot_rows + (int64_t)t->warm_slots * p->group;
+  const int elem = p->dtype == SA_BF16 ? 2 : 4;
+  if ((int64_t)p->batch * p->n_kv_heads * p->n_cap * p->head_dim * elem >= (1ll << 62)) return SA_ERR_UNSUPPORTED;
+  // the device addresses of the cold store (pinned host memory)
+  void* ck = nullptr;
+  void* cv = nullptr;
+  if (hipHostGetDevicePointer(&ck, const_cast<void*>(t->cold_k), 0) != hipSuccess || !ck ||
+      hipHostGetDevicePointer(&cv, const_cast<void*>(t->cold_v), 0) != hipSuccess || !cv) {
+    (void)hipGetLastError();
+    return SA_ERR_INVALID_ARG;
+  }
+  sa::TierArgs a{};
+  a.sel_idx = b->sel_idx; a.rows = t->rows; a.sel_count = b->sel_count;
+  a.cold_k = static_cast<const char*>(ck); a.cold_v = static_cast<const char*>(cv);
+  a.dev_k = static_cast<char*>(t->dev_k); a.dev_v = static_cast<char*>(t->dev_v);
+  a.slot_group = t->slot_group; a.slot_stamp = t->slot_stamp; a.stats = t->stats;
+  a.B = p->batch; a.Hkv = p->n_kv_heads; a.n = p->n_ctx; a.n_cap = p->n_cap;
+  a.row_bytes = p->head_dim * elem; a.chunk = p->chunk; a.group = p->group;
+  a.sink_chunks = p->sink_chunks; a.local_chunks = p->local_chunks;
+  a.warm_slots = t->warm_slots; a.dev_rows = (int32_t)dev_rows; a.step = t->step;
+  a.groups = units_of_kind(u, SA_HEAD_ROUTED);
+  return hip_status(sa::launch_tier_fetch(a, static_cast<hipStream_t>(stream)));
+}
+
 int32_t sparse_attn_prefill_backward(const sa_params* p, const sa_buffers* b, void* ws,
                                      size_t* ws_bytes, void* stream) {
   int32_t st = check_common(p, b);

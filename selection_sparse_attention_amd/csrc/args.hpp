@@ -212,6 +212,27 @@ struct BwdArgs {
   float scale, scale_log2;
 };
 
+// Tiered K/V of the routed decode: the routed lists are served from a cold
+// host store through warm device slots (one routing group each, LRU) and
+// rewritten as rows of the device tier (hot rows, then the warm slots).
+struct TierArgs {
+  const int32_t* sel_idx;        // [B,Hkv,n_cap] routed positions
+  int32_t* rows;                 // [B,Hkv,dev_rows] the lists as rows of the device tier
+  const int32_t* sel_count;      // [B,Hkv]
+  const char* cold_k; const char* cold_v;   // device-visible host memory [B,Hkv,n_cap,row_bytes]
+  char* dev_k; char* dev_v;      // [B,Hkv,dev_rows,row_bytes]
+  int32_t* slot_group;           // [B,Hkv,warm_slots]
+  int32_t* slot_stamp;           // [B,Hkv,warm_slots]
+  int32_t* stats;                // [B,Hkv,2] or null
+  int32_t B, Hkv, n, n_cap, row_bytes, chunk, group, sink_chunks, local_chunks;
+  int32_t warm_slots, dev_rows, step;
+  GroupList groups;              // the routed KV groups
+};
+
+constexpr int kTierListMax = 8192;       // longest routed list a fetch stages
+constexpr int kTierSlotsMax = 4096;      // warm slots per (sequence, KV group)
+constexpr int kTierNeedMax = 256;        // routed groups per list
+
 // ---------------------------------------------------------------- launchers
 hipError_t launch_index_lowrank(const IndexLowrankArgs& a, int dtype, int d, hipStream_t s);
 hipError_t launch_summary(const SummaryArgs& a, int dtype, int d, hipStream_t s);
@@ -223,6 +244,7 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int d, hipStream_t s);
 hipError_t launch_decode_s2o(const DecodeArgs& a, int d, hipStream_t s);
 hipError_t launch_head_union(const HeadUnionArgs& a, hipStream_t s);
+hipError_t launch_tier_fetch(const TierArgs& a, hipStream_t s);
 hipError_t launch_select_order(const SelectArgs& a, int dtype, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int d, hipStream_t s);
 hipError_t launch_prefill_heads(const PrefillArgs& a, int d, hipStream_t s);

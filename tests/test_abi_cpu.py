@@ -357,3 +357,37 @@ def test_prefill_backward_validation_and_size():
         assert sa.raw_call("prefill_backward", ctypes.byref(pf), ctypes.byref(b), FAKE,
                            ctypes.byref(n), None) == sa.SA_ERR_INVALID_ARG, name
         setattr(b, name, FAKE)
+
+
+def test_tier_fetch_validation():
+    """The tier fetch refuses, before anything runs: heads that are not all
+    routed, per-head sets, a chunk that groups do not divide, fewer warm
+    slots than one step routes (or more than 4096), lists longer than 8192,
+    and missing tables or stores."""
+    b = _full_bufs()
+    ok = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_ctx=4096,
+              head_kind=[sa.HEAD_ROUTED] * 8, chunk=64, group=16, top_chunks=4, top_groups=2,
+              sink_chunks=2, local_chunks=3)
+
+    def tier(**kw):
+        t = sa.Tier()
+        t.cold_k = t.cold_v = t.dev_k = t.dev_v = FAKE
+        t.slot_group = t.slot_stamp = t.rows = FAKE
+        t.warm_slots, t.step = 8, 1
+        for k, v in kw.items():
+            setattr(t, k, v)
+        return t
+
+    def call(pkw, **tkw):
+        p = sa.make_params(**{**ok, **pkw})
+        return sa.raw_call("tier_fetch", ctypes.byref(p), ctypes.byref(b), ctypes.byref(tier(**tkw)), None)
+
+    assert call({"head_kind": [sa.HEAD_ROUTED] * 4 + [sa.HEAD_LOCAL] * 4}) == sa.SA_ERR_UNSUPPORTED
+    assert call({"per_head_sets": True}) == sa.SA_ERR_UNSUPPORTED
+    assert call({"chunk": 64, "group": 24}) == sa.SA_ERR_UNSUPPORTED
+    assert call({}, warm_slots=7) == sa.SA_ERR_INVALID_ARG
+    assert call({}, warm_slots=4097) == sa.SA_ERR_INVALID_ARG
+    assert call({"top_chunks": 64, "top_groups": 4, "sink_chunks": 64}) == sa.SA_ERR_UNSUPPORTED
+    assert call({}, slot_group=None) == sa.SA_ERR_INVALID_ARG
+    assert call({}, cold_v=None) == sa.SA_ERR_INVALID_ARG
+    assert call({}, rows=None) == sa.SA_ERR_INVALID_ARG
