@@ -41,6 +41,7 @@ def parse():
                     choices=["llama3_8b_decode_32k", "llama3_8b_decode_128k",
                              "llama3_8b_decode_128k_topk", "hga_route_decode_64k",
                              "llama3_8b_decode_32k_s2o",
+                             "hga_route_decode_64k_tiered",
                              "pyramid_prefill_128k", "pyramid_prefill_backward_128k",
                              "llama3_8b_head_split_prefill_32k", "hga_route_prefill_64k"])
     ap.add_argument("--per-head", action="store_true",
@@ -394,6 +395,102 @@ def run_decode(args, torch, sa, workloads, workload=None, steps=None, warmup=Non
     return res
 
 
+def run_tier(args, torch, sa, workloads, steps=20, warmup=3):
+    """The routed 64K decode step with the K/V history in pinned host memory
+    (cold tier) and only the hot rows (sinks, a ring of the last chunks) and
+    warm slots of routing groups in device memory; the device copy of the
+    whole cache is freed.  Two regimes: 'warm' - the routing repeats, every
+    routed group is already in a slot after the first step; 'cold' - the
+    slot tables are emptied before every step, so every routed group comes
+    over the host link."""
+    cfg = workloads.HGA_64K
+    log(f"[bench] generating {cfg.name} (tiered: history in host memory)")
+    inst = DecodeInstance(cfg, 1000, sa, torch, workloads)
+    B, Hkv, d, n = cfg.batch, cfg.n_kv_heads, cfg.head_dim, cfg.n_ctx
+    C, grp, sc, lc = cfg.chunk, cfg.group, cfg.sink_chunks, cfg.local_chunks
+    slots = 4 * cfg.top_chunks * cfg.top_groups
+    sink_rows, ring = sc * C, (lc + 1) * C
+    dev_rows = sink_rows + ring + slots * grp
+    dt = inst.t["k_cache"].dtype
+    cold = {k: inst.t[k].cpu().pin_memory() for k in ("k_cache", "v_cache")}
+    dev = {k: torch.zeros(B, Hkv, dev_rows, d, dtype=dt, device="cuda") for k in ("k", "v")}
+    kappa = (n - 1) // C
+    win = torch.arange(max((kappa - lc) * C, sink_rows), n, device="cuda")
+    for src, dst in ((inst.t["k_cache"], dev["k"]), (inst.t["v_cache"], dev["v"])):
+        dst[:, :, :sink_rows] = src[:, :, :sink_rows]
+        dst[:, :, sink_rows + win % ring] = src[:, :, win]
+    # the device no longer holds the history
+    del inst.t["k_cache"], inst.t["v_cache"]
+    torch.cuda.empty_cache()
+    slot_group = torch.full((B, Hkv, slots), -1, dtype=torch.int32, device="cuda")
+    slot_stamp = torch.zeros(B, Hkv, slots, dtype=torch.int32, device="cuda")
+    stats = torch.zeros(B, Hkv, 2, dtype=torch.int32, device="cuda")
+    rows = torch.zeros(B, Hkv, dev_rows, dtype=torch.int32, device="cuda")
+    pt = sa.params_from_config(cfg, n_cap=dev_rows)
+    pt.n_ctx = dev_rows
+    bt = sa.make_buffers(q=inst.t["q"], k_cache=dev["k"], v_cache=dev["v"], sel_idx=rows,
+                         sel_count=inst.t["sel_count"], out=inst.t["out"])
+    ws = sa.Workspace("cuda")
+    stream = torch.cuda.current_stream()
+    counter = [0]
+
+    def step(cold_regime, ev=None):
+        inst.index_and_select()
+        if cold_regime:
+            slot_group.fill_(-1)
+            slot_stamp.zero_()
+        counter[0] += 1
+        tier = sa.make_tier(cold_k=cold["k_cache"], cold_v=cold["v_cache"], dev_k=dev["k"],
+                            dev_v=dev["v"], slot_group=slot_group, slot_stamp=slot_stamp, rows=rows,
+                            step=counter[0], stats=stats)
+        if ev:
+            ev[0].record(stream)
+        sa.tier_fetch(inst.params, inst.bufs, tier)
+        if ev:
+            ev[1].record(stream)
+        sa.decode(pt, bt, ws)
+
+    res = {}
+    for regime in ("warm", "cold"):
+        for _ in range(warmup):
+            step(regime == "cold")
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for i in range(steps):
+            step(regime == "cold", ev[i])
+        end.record(stream)
+        torch.cuda.synchronize()
+        t_step = start.elapsed_time(end) / steps * 1e-3
+        t_fetch = sum(a.elapsed_time(b) for a, b in ev) / steps * 1e-3
+        st = stats.cpu()
+        hits, misses = int(st[..., 0].sum()), int(st[..., 1].sum())
+        fetched = misses * grp * d * (2 if cfg.dtype == "bf16" else 4) * 2
+        res[regime] = {"ms_per_step": t_step * 1e3, "fetch_us": t_fetch * 1e6,
+                       "hits_last_step": hits, "misses_last_step": misses,
+                       "fetched_mb_per_step": fetched / 1e6,
+                       "fetch_gbps": fetched / t_fetch / 1e9 if fetched else 0.0}
+        log(f"[bench] {cfg.name} tiered, {regime}: {t_step * 1e6:.1f} us/step, fetch "
+            f"{t_fetch * 1e6:.1f} us, {hits} hits / {misses} misses, "
+            f"{fetched / 1e6:.1f} MB from host")
+    dev_mb = sum(x.numel() * x.element_size() for x in dev.values()) / 1e6
+    cold_mb = sum(x.numel() * x.element_size() for x in cold.values()) / 1e6
+    out = {"value": B * cfg.n_q_heads * n / (res["warm"]["ms_per_step"] * 1e-3),
+           "unit": "tokens/s (B x heads x ctx per step, warm regime)",
+           "ms_per_step": res["warm"]["ms_per_step"],
+           "config": {"workload": cfg.name + "_tiered", "batch": B, "n_ctx": n,
+                      "warm_slots": slots, "device_kv_mb": dev_mb, "host_kv_mb": cold_mb},
+           "regimes": res,
+           "note": "history in pinned host memory (cold tier), read by the fetch kernel over the "
+                   "host link; hot rows and warm slots in device memory; cold = every routed "
+                   "group fetched each step"}
+    del inst, cold, dev
+    torch.cuda.empty_cache()
+    return out
+
+
 def percentiles(xs):
     """p10 / p50 / p90 of a list of times."""
     ys = sorted(xs)
@@ -496,6 +593,8 @@ def main():
         return
     if args.workload == "pyramid_prefill_128k":
         res = run_prefill(args, torch, sa, workloads)
+    elif args.workload == "hga_route_decode_64k_tiered":
+        res = run_tier(args, torch, sa, workloads, steps=min(args.steps, 20), warmup=3)
     elif args.workload == "pyramid_prefill_backward_128k":
         res = run_prefill(args, torch, sa, workloads, backward=True)
     elif args.workload == "llama3_8b_head_split_prefill_32k":
@@ -522,6 +621,7 @@ def main():
             other[f"llama3_8b_decode_128k_alpha{a:g}"] = compact(run_decode(
                 args, torch, sa, workloads, workload="llama3_8b_decode_128k", steps=20, warmup=3,
                 instances=4, cpu=False, alpha=a))
+        other["hga_route_decode_64k_tiered"] = run_tier(args, torch, sa, workloads)
         other["pyramid_prefill_128k"] = compact(run_prefill(args, torch, sa, workloads, steps=5,
                                                             warmup=1, cpu=False))
         other["pyramid_prefill_backward_128k"] = compact(run_prefill(

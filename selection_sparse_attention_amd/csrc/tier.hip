@@ -102,8 +102,11 @@ __global__ __launch_bounds__(kTierThreads) void tier_fetch_kernel(TierArgs a) {
   }
   __syncthreads();
 
-  // ---- 3. rank the candidate slots (ascending keys)
-  for (int k = 2; k <= P; k <<= 1) {
+  // ---- 3. rank the candidate slots (ascending keys), when a group misses
+  int nmiss_local = 0;
+  for (int k = tid; k < nneed; k += kTierThreads) nmiss_local += !s_hit[k];
+  const bool any_miss = __syncthreads_or(nmiss_local) != 0;
+  for (int k = 2; k <= P && any_miss; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       for (int i = tid; i < P; i += kTierThreads) {
         const int ixj = i ^ j;
@@ -116,7 +119,9 @@ __global__ __launch_bounds__(kTierThreads) void tier_fetch_kernel(TierArgs a) {
     }
   }
   // the missing groups take the first candidates in order
-  if (tid < 64) {
+  if (tid < 64 && !any_miss) {
+    if (tid == 0) s_nmiss = 0;
+  } else if (tid < 64) {
     int base = 0;
     for (int k0 = 0; k0 < nneed; k0 += 64) {
       const int k = k0 + tid;
