@@ -145,7 +145,7 @@ typedef struct sa_params {
  * its own q_idx row, a routed head routes with its own query, against the
  * index keys or summaries of its KV group h / G.  sel_idx is [B,Hq,n_cap] and
  * sel_count [B,Hq], and sparse_attn_decode reads them per query head.  With
- * bf16 caches, n_ctx <= 147456 and no early stop, the decode still gathers
+ * bf16 caches, n_ctx < 2^24 and no early stop, the decode still gathers
  * each row once per KV group: it merges the group's heads' lists into one
  * (ascending, each position tagged with the heads that chose it) in its
  * workspace and masks every head to its own set; otherwise each head is

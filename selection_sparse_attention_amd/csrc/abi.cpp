@@ -286,6 +286,10 @@ int32_t decode_entry(const sa_params* p, const sa_buffers* b, void* ws, size_t* 
   float* s2o_state = s2o_mask ? c.take<float>((size_t)p->batch * u.n * G * (p->head_dim + 2)) : nullptr;
   int32_t* union_idx = head_union ? c.take<int32_t>((size_t)p->batch * p->n_kv_heads * p->n_cap) : nullptr;
   int32_t* union_count = head_union ? c.take<int32_t>((size_t)p->batch * p->n_kv_heads) : nullptr;
+  const int mask_words = (p->n_ctx + 3) / 4;
+  const int n_slices = (p->n_ctx + sa::kUnionSlice - 1) / sa::kUnionSlice;
+  uint32_t* union_masks = head_union ? c.take<uint32_t>((size_t)p->batch * p->n_kv_heads * mask_words) : nullptr;
+  int32_t* slice_count = head_union ? c.take<int32_t>((size_t)p->batch * p->n_kv_heads * n_slices) : nullptr;
 
   if ((st = workspace_gate(ws, ws_bytes, c.size()))) return st < 0 ? st : SA_OK;
   if (!b->q || !b->k_cache || !b->v_cache || !b->out) return SA_ERR_INVALID_ARG;
@@ -313,6 +317,8 @@ int32_t decode_entry(const sa_params* p, const sa_buffers* b, void* ws, size_t* 
     ua.union_idx = union_idx; ua.union_count = union_count;
     ua.B = p->batch; ua.Hq = p->n_q_heads; ua.Hkv = p->n_kv_heads; ua.G = Gkv;
     ua.n = p->n_ctx; ua.n_cap = p->n_cap;
+    ua.masks = union_masks; ua.slice_count = slice_count;
+    ua.mask_words = mask_words; ua.n_slices = n_slices;
     ua.groups.n = 0;
     for (int g = 0; g < ug.n; ++g)
       if (ug.kind[g] != SA_HEAD_LOCAL) ua.groups.ids[ua.groups.n++] = g;

@@ -162,11 +162,14 @@ struct HeadUnionArgs {
   const int32_t* sel_count;   // [B,Hq]
   int32_t* union_idx;         // [B,Hkv,n_cap] (head mask << 24 | position), ascending
   int32_t* union_count;       // [B,Hkv]
-  int32_t B, Hq, Hkv, G, n, n_cap;
+  uint32_t* masks;            // [B,Hkv,mask_words] head bits, one byte per position
+  int32_t* slice_count;       // [B,Hkv,n_slices] tagged positions per slice
+  int32_t B, Hq, Hkv, G, n, n_cap, mask_words, n_slices;
   GroupList groups;           // the selecting KV groups
 };
 
-constexpr int kUnionMaxN = 144 * 1024;   // positions whose masks fit in LDS (one byte each)
+constexpr int kUnionMaxN = (1 << 24) - 1;  // positions an entry's 24 position bits hold
+constexpr int kUnionSlice = 2048;          // positions per slice of the union
 
 constexpr int kS2oMax = 8192;     // candidates per group the early-stop kernel stages
 

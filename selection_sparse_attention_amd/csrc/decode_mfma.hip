@@ -545,73 +545,128 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int d, hipStream_t s) {
 // Per-head sets decoded per KV group: the union of the G heads' sets of one
 // (sequence, selecting group), each position tagged with the heads that
 // chose it, so that the decode gathers every row once for all G heads and
-// masks each head's scores to its own set.  One 1024-thread workgroup per
-// (group, sequence): one byte of head bits per position in LDS, ORed in from
-// the heads' lists one head after another, then an ordered compaction (each
-// thread a contiguous run of positions, offsets from one block scan).  Contexts whose masks do not fit in LDS
-// decode each head alone instead.
-constexpr int kUnionThreads = 1024;
+// masks each head's scores to its own set.  The positions are cut into
+// slices of kUnionSlice; two launches spread over the whole chip:
+//   1. per (slice, group, sequence): each head's entries inside the slice
+//      (its list is ascending: one wave per head finds the slice's first
+//      and last entries with 64-way searches, three dependent loads for a
+//      32K list) set their head bits in an LDS byte per position; the
+//      slice's bytes and its count of tagged positions go to the workspace;
+//   2. per (slice, group, sequence): the slice's entries (head bits << 24 |
+//      position) written in order at the sum of the earlier slices' counts.
+constexpr int kUnionThreads = 256;
 
-__global__ __launch_bounds__(kUnionThreads) void head_union_kernel(HeadUnionArgs a) {
-  extern __shared__ uint32_t s_hm[];          // ceil(n / 4) words: 8 head bits per position
-  __shared__ int32_t s_scan[kUnionThreads / 64];
-  const int g = a.groups.ids[blockIdx.x], b = blockIdx.y, tid = threadIdx.x;
-  const int n = a.n, nw = (n + 3) / 4;
-  for (int i = tid; i < nw; i += kUnionThreads) s_hm[i] = 0u;
-  __syncthreads();
-  // eight list entries per thread in flight, then their head bits ORed in
-  constexpr int U = 8;
-  for (int h = 0; h < a.G; ++h) {
-    const int64_t row = (int64_t)b * a.Hq + g * a.G + h;
-    const int cnt = min(max(a.sel_count[row], 0), n);
-    const int32_t* lst = a.sel_idx + row * a.n_cap;
-    const uint32_t bit = 1u << h;
-    for (int i0 = 0; i0 < cnt; i0 += U * kUnionThreads) {
-      int pos[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * kUnionThreads + tid;
-        pos[u] = (i < cnt) ? lst[i] : -1;
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if ((unsigned)pos[u] < (unsigned)n) atomicOr(&s_hm[pos[u] >> 2], bit << (8 * (pos[u] & 3)));
-    }
-    __syncthreads();
+// First index i in [lo, hi) of the ascending list with x[i] >= v (hi if
+// none); one wave, every lane returns it.  64-way: each round reads 64
+// evenly spaced entries and keeps the sub-range where the bound lies.
+__device__ __forceinline__ int wave_lower_bound(const int32_t* x, int lo, int hi, int v) {
+  const int lane = threadIdx.x & 63;
+  while (hi - lo > 64) {
+    const int64_t span = hi - lo;
+    const int probe = lo + (int)((span * lane) / 64);          // lane 0 probes lo
+    const bool below = x[probe] < v;
+    const uint64_t m = __ballot(below);
+    const int k = __popcll(m);                                  // probes below v (a prefix)
+    const int nlo = (k == 0) ? lo : lo + (int)((span * (k - 1)) / 64);
+    const int nhi = (k == 64) ? hi : lo + (int)((span * k) / 64) + 1;
+    lo = nlo;
+    hi = min(hi, nhi);
   }
-  // ordered compaction: thread t takes a contiguous run of words (one block
-  // scan for the whole group)
-  const int per = (nw + kUnionThreads - 1) / kUnionThreads;
-  const int w0 = min(nw, tid * per), w1 = min(nw, w0 + per);
-  int32_t c = 0;
-  for (int w = w0; w < w1; ++w) {
+  const int i = lo + lane;
+  const bool below = i < hi && x[i] < v;
+  return lo + __popcll(__ballot(below));
+}
+
+// grid (slice, group, sequence)
+__global__ __launch_bounds__(kUnionThreads) void head_union_mark_kernel(HeadUnionArgs a) {
+  __shared__ uint32_t s_hm[kUnionSlice / 4];
+  __shared__ int s_lo[8], s_hi[8];
+  __shared__ int32_t s_red[kUnionThreads / 64];
+  const int g = a.groups.ids[blockIdx.y], b = blockIdx.z, tid = threadIdx.x;
+  const int wid = tid >> 6, lane = tid & 63;
+  const int p0 = blockIdx.x * kUnionSlice, p1 = min(a.n, p0 + kUnionSlice);
+  for (int i = tid; i < kUnionSlice / 4; i += kUnionThreads) s_hm[i] = 0u;
+  // each head's entries inside [p0, p1)
+  for (int h = wid; h < a.G; h += kUnionThreads / 64) {
+    const int64_t row = (int64_t)b * a.Hq + g * a.G + h;
+    const int cnt = min(max(a.sel_count[row], 0), a.n);
+    const int32_t* lst = a.sel_idx + row * a.n_cap;
+    const int lo = wave_lower_bound(lst, 0, cnt, p0);
+    const int hi = wave_lower_bound(lst, lo, cnt, p1);
+    if (lane == 0) { s_lo[h] = lo; s_hi[h] = hi; }
+  }
+  __syncthreads();
+  for (int h = 0; h < a.G; ++h) {
+    const int32_t* lst = a.sel_idx + ((int64_t)b * a.Hq + g * a.G + h) * a.n_cap;
+    const int lo = s_lo[h], hi = s_hi[h];
+    for (int i = lo + tid; i < hi; i += kUnionThreads) {
+      const int q = lst[i] - p0;
+      if ((unsigned)q < (unsigned)(p1 - p0)) atomicOr(&s_hm[q >> 2], (1u << h) << (8 * (q & 3)));
+    }
+  }
+  __syncthreads();
+  uint32_t* out = a.masks + ((int64_t)b * a.Hkv + g) * a.mask_words + p0 / 4;
+  int c = 0;
+  for (int w = tid; w < (p1 - p0 + 3) / 4; w += kUnionThreads) {
     const uint32_t x = s_hm[w];
+    out[w] = x;
     c += ((x & 0xFFu) != 0) + ((x & 0xFF00u) != 0) + ((x & 0xFF0000u) != 0) + ((x >> 24) != 0);
   }
-  int32_t total;
-  int32_t o = block_exclusive_scan<int32_t, kUnionThreads>(c, s_scan, &total);
-  int32_t* out = a.union_idx + ((int64_t)b * a.Hkv + g) * a.n_cap;
-  for (int w = w0; w < w1; ++w) {
-    const uint32_t x = s_hm[w];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t m = (x >> (8 * k)) & 0xFFu;
-      if (m) out[o++] = (int32_t)((m << 24) | (uint32_t)(4 * w + k));
+  for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
+  if (lane == 0) s_red[wid] = c;
+  __syncthreads();
+  if (tid == 0) {
+    int t = 0;
+    for (int w = 0; w < kUnionThreads / 64; ++w) t += s_red[w];
+    a.slice_count[((int64_t)b * a.Hkv + g) * a.n_slices + blockIdx.x] = t;
+  }
+}
+
+// grid (slice, group, sequence)
+__global__ __launch_bounds__(kUnionThreads) void head_union_compact_kernel(HeadUnionArgs a) {
+  __shared__ int32_t s_scan[kUnionThreads / 64];
+  const int g = a.groups.ids[blockIdx.y], b = blockIdx.z, tid = threadIdx.x;
+  const int64_t bg = (int64_t)b * a.Hkv + g;
+  const int p0 = blockIdx.x * kUnionSlice, p1 = min(a.n, p0 + kUnionSlice);
+  const int32_t* cnts = a.slice_count + bg * a.n_slices;
+  int before = 0;
+  for (int s = 0; s < blockIdx.x; ++s) before += cnts[s];
+  // thread t: 2 consecutive words (8 positions) of the slice
+  constexpr int PW = kUnionSlice / 4 / kUnionThreads;
+  const uint32_t* m = a.masks + bg * a.mask_words + p0 / 4;
+  const int nw = (p1 - p0 + 3) / 4;
+  uint32_t x[PW];
+  int mine = 0;
+#pragma unroll
+  for (int k = 0; k < PW; ++k) {
+    const int w = tid * PW + k;
+    x[k] = (w < nw) ? m[w] : 0u;
+    mine += ((x[k] & 0xFFu) != 0) + ((x[k] & 0xFF00u) != 0) + ((x[k] & 0xFF0000u) != 0) + ((x[k] >> 24) != 0);
+  }
+  int32_t total;
+  int32_t o = before + block_exclusive_scan<int32_t, kUnionThreads>(mine, s_scan, &total);
+  int32_t* out = a.union_idx + bg * a.n_cap;
+#pragma unroll
+  for (int k = 0; k < PW; ++k) {
+    const int w = tid * PW + k;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t hm = (x[k] >> (8 * q)) & 0xFFu;
+      if (hm) out[o++] = (int32_t)((hm << 24) | (uint32_t)(p0 + 4 * w + q));
     }
   }
-  if (tid == 0) a.union_count[(int64_t)b * a.Hkv + g] = total;
+  if (tid == 0 && blockIdx.x == a.n_slices - 1) a.union_count[bg] = before + total;
 }
 
 hipError_t launch_head_union(const HeadUnionArgs& a, hipStream_t s) {
   if (a.G < 1 || a.G > 8 || a.n < 1 || a.n > kUnionMaxN || a.n_cap < a.n) return hipErrorInvalidValue;
+  if (a.mask_words != (a.n + 3) / 4 || a.n_slices != (a.n + kUnionSlice - 1) / kUnionSlice)
+    return hipErrorInvalidValue;
   if (a.groups.n == 0 || a.B == 0) return hipSuccess;
-  const size_t lds = (size_t)((a.n + 3) / 4) * sizeof(uint32_t);
-  if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&head_union_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(head_union_kernel, dim3(a.groups.n, a.B), dim3(kUnionThreads), lds, s, a);
+  const dim3 grid(a.n_slices, a.groups.n, a.B);
+  hipLaunchKernelGGL(head_union_mark_kernel, grid, dim3(kUnionThreads), 0, s, a);
+  hipLaunchKernelGGL(head_union_compact_kernel, grid, dim3(kUnionThreads), 0, s, a);
   return hipGetLastError();
 }
 

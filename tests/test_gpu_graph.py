@@ -31,15 +31,16 @@ def _same(a, b, groups=None):
             assert torch.equal(a[k], b[k]), k
 
 
-@pytest.mark.parametrize("cfg", [
-    workloads.LLAMA_32K.with_(batch=2, n_ctx=8192 + 77),
-    workloads.LLAMA_32K.with_(batch=2, n_ctx=4096, top_p=1.0, top_k=300),
-    workloads.HGA_64K.with_(batch=2, n_ctx=8192),
-    workloads.LLAMA_32K.with_(batch=2, n_ctx=4096, top_p=1.0, top_k=300, s2o_tau=0.01),
-], ids=["topp", "topk", "routed", "early-stop"])
-def test_decode_step_graph_replays_match_eager(cfg):
+@pytest.mark.parametrize("cfg,per_head", [
+    (workloads.LLAMA_32K.with_(batch=2, n_ctx=8192 + 77), False),
+    (workloads.LLAMA_32K.with_(batch=2, n_ctx=4096, top_p=1.0, top_k=300), False),
+    (workloads.HGA_64K.with_(batch=2, n_ctx=8192), False),
+    (workloads.LLAMA_32K.with_(batch=2, n_ctx=4096, top_p=1.0, top_k=300, s2o_tau=0.01), False),
+    (workloads.LLAMA_32K.with_(batch=2, n_ctx=8192 + 77), True),
+], ids=["topp", "topk", "routed", "early-stop", "per-head"])
+def test_decode_step_graph_replays_match_eager(cfg, per_head):
     inp = workloads.decode_inputs(cfg, 21, device=DEV)
-    run = DecodeRun(cfg, inp)
+    run = DecodeRun(cfg, inp, per_head=per_head)
     n = cfg.n_ctx
     if cfg.routed:
         run.summaries(0, n)
@@ -57,7 +58,10 @@ def test_decode_step_graph_replays_match_eager(cfg):
 
     keys = ["sel_idx", "sel_count", "out"]
     kinds = cfg.head_kind()
-    groups = [g for g in range(cfg.n_kv_heads) if kinds[g * cfg.gqa] != workloads.HEAD_LOCAL]
+    if per_head:
+        groups = [h for h in range(cfg.n_q_heads) if kinds[h] != workloads.HEAD_LOCAL]
+    else:
+        groups = [g for g in range(cfg.n_kv_heads) if kinds[g * cfg.gqa] != workloads.HEAD_LOCAL]
     step()
     torch.cuda.synchronize()
     eager = _snapshot(run, keys)

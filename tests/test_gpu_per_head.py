@@ -117,8 +117,8 @@ def test_per_head_decode_over_given_lists(cfg):
     """The attention stage alone over random per-head lists (and sinks +
     window for local heads, each head on its own).  With bf16 caches the
     heads of a KV group are decoded together over the union of their sets,
-    each masked to its own (GQA 4, 8 and 2 here); past the union's limit of
-    147456 positions each head is decoded alone (the 150000 case)."""
+    each masked to its own (GQA 4, 8 and 2 here, and a context of 150000
+    whose union spans 74 slices of 2048 positions)."""
     log("per-head decode lists", cfg.name, cfg.n_ctx)
     inp = workloads.decode_inputs(cfg, 12)
     run = DecodeRun(cfg, inp, n_cap=cfg.n_ctx + 3, per_head=True)
