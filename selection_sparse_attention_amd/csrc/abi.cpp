@@ -678,7 +678,8 @@ int32_t sparse_attn_prefill_backward(const sa_params* p, const sa_buffers* b, vo
   if (p->n_ctx >= (1 << 23)) return SA_ERR_UNSUPPORTED;
   const int64_t bh = (int64_t)p->batch * p->n_q_heads;
   const int64_t E = pg.Nt;
-  const int64_t R = (int64_t)p->n_ctx + (int64_t)pg.nblk * p->block_top_k;
+  // partial rows: one per key, one per (block, chosen entry), and a spare
+  const int64_t R = (int64_t)p->n_ctx + (int64_t)pg.nblk * p->block_top_k + 1;
   if (R >= (1ll << 31)) return SA_ERR_UNSUPPORTED;
   Carver c(ws);
   float* delta = c.take<float>(bh * p->n_ctx);

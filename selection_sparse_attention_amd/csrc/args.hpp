@@ -209,7 +209,7 @@ struct BwdArgs {
   uint32_t* err;                                 // [B,H]
   uint16_t* part_k; uint16_t* part_v;            // [B,H,R,d] bf16
   float* coarse_k; float* coarse_v;              // [B,H,Nc,d]
-  int64_t R;                                     // partial rows per head
+  int64_t R;                                     // partial rows per head (the last is a spare)
   int32_t B, H, N, Nc, E, nblk, K, q_block, levels;
   int32_t off[8], span[8], cnt[8];               // per level: flat offset, rows covered, entries
   float scale, scale_log2;

@@ -64,19 +64,23 @@ __device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2b){x, y}, bf16x2b));
 }
 
-__device__ __forceinline__ int level_of(const BwdArgs& a, int32_t f) {
-  int l = 0;
-  for (int m = 1; m < a.levels; ++m)
-    if (f >= a.off[m]) l = m;
-  return l;
+// The per-level tables are read with constant indices only: a lane-dependent
+// index into the argument block would become a vector load, and its wait
+// would also wait for every store the wave still has in flight.
+
+// one past the last position that flat entry f covers
+__device__ __forceinline__ int64_t span_end(const BwdArgs& a, int32_t f) {
+  int o = a.off[0], sp = a.span[0];
+#pragma unroll
+  for (int m = 1; m < 8; ++m)
+    if (m < a.levels && f >= a.off[m]) { o = a.off[m]; sp = a.span[m]; }
+  return (int64_t)(f - o + 1) * sp;
 }
 
 // first block that sees flat entry f: its span must end at or before the
 // block's first query
 __device__ __forceinline__ int first_block(const BwdArgs& a, int32_t f) {
-  const int l = level_of(a, f);
-  const int64_t end = (int64_t)(f - a.off[l] + 1) * a.span[l];
-  return (int)((end + a.q_block - 1) / a.q_block);
+  return (int)((span_end(a, f) + a.q_block - 1) / a.q_block);
 }
 
 // byte offset of flat entry f's K/V row (level 0 in k/v, coarse in pk/pv
@@ -185,8 +189,7 @@ __global__ __launch_bounds__(kIvThreads) void bwd_interval_kernel(BwdArgs a, int
     const int32_t f = s_l[1][s];
     bool ok = f >= 0 && f < a.E && (s == 0 || s_l[1][s - 1] != f);
     if (ok) {
-      const int l = level_of(a, f);
-      const int64_t end = (int64_t)(f - a.off[l] + 1) * a.span[l];
+      const int64_t end = span_end(a, f);
       const int b0 = (int)((end + a.q_block - 1) / a.q_block);
       ok = end <= (int64_t)a.q_block * blk;               // visible to this block
       if (ok && blk > b0) ok = in_sorted(s_l[0], n[0], f); // chosen without a gap since b0
@@ -359,6 +362,9 @@ __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   gather(0, ids_of(0), cur);
   stash(0, cur);
   Ids id_next = ids_of(1);
+  // nothing in flight on entry: loads pending into registers that the loop
+  // reuses would otherwise put a full wait before every tile's first product
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
@@ -496,26 +502,38 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
   uint16_t* pkd = a.part_k + (int64_t)bh * a.R * kD;
   uint16_t* pvd = a.part_v + (int64_t)bh * a.R * kD;
 
-  // the list entry of sequence entry e (read a step before its rows)
+  // Partial rows past the last real one go to the head's spare row, R - 1:
+  // every lane stores every step, so the loop has no branch around its
+  // stores and the waits for its prefetches count them exactly.
+  const int64_t spare = a.R - 1;
+  // the list entry of sequence entry e (read a step before its rows; the
+  // read itself is always in bounds, K >= 1)
   auto list_at = [&](int e) __attribute__((always_inline)) -> int32_t {
-    return (e < c_sel) ? list[e] : 0;
+    const int32_t v = list[min(e, a.K - 1)];
+    return (e < c_sel) ? v : 0;
   };
   // this lane's key of a step: sequence entry e = step + 16 w + l16 with
-  // list entry f -> (row byte offset, partial row); partial row -1: nothing
-  // to write
-  auto key_of = [&](int e, int32_t f, uint32_t& r, int64_t& pr) __attribute__((always_inline)) {
+  // list entry f -> row byte offset r, and the partial row as base[bi] + adj
+  // (bi = -1: nothing to write); entries past the end read row 0
+  auto key_of = [&](int e, int32_t f, uint32_t& r, int32_t& bi, int32_t& adj) __attribute__((always_inline)) {
     r = 0u;
-    pr = -1;
+    bi = -1;
+    adj = 0;
     if (e < c_sel) {
       r = row_of(a, f);
-      if ((unsigned)f < (unsigned)a.E)
-        pr = (int64_t)base[f] + (f < a.N ? 1 : 0) + (blk - first_block(a, f));
+      if ((unsigned)f < (unsigned)a.E) {
+        bi = f;
+        adj = (f < a.N ? 1 : 0) + (blk - first_block(a, f));
+      }
     } else if (e < T) {
-      const int32_t f = q0 + e - c_sel;
-      r = (uint32_t)f * kRowB;
-      pr = base[f];
+      const int32_t qf = q0 + e - c_sel;
+      r = (uint32_t)qf * kRowB;
+      bi = qf;
     }
-    if (pr >= a.R) pr = -1;
+  };
+  auto part_row = [&](int32_t bi, int32_t bv, int32_t adj) __attribute__((always_inline)) -> int64_t {
+    const int64_t pr = (int64_t)bv + adj;
+    return (bi >= 0 && pr >= 0 && pr < spare) ? pr : spare;
   };
   auto load_frags = [&](uint32_t r, bf16x8b (&kf)[4], bf16x8b (&vf)[4]) __attribute__((always_inline)) {
     const bool coarse = (int32_t)r < 0;
@@ -531,24 +549,30 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
   int e = 16 * wid + l16;
   uint32_t r;
   int64_t pr;
-  key_of(e, list_at(e), r, pr);
+  {
+    int32_t bi, adj;
+    key_of(e, list_at(e), r, bi, adj);
+    pr = part_row(bi, base[max(bi, 0)], adj);
+  }
   bf16x8b kf[4], vf[4];
   load_frags(r, kf, vf);
   int32_t f_next = list_at(e + 128);
+  // the first step's rows land before the loop: with loads still in flight
+  // into kf/vf on entry, every step would wait for the next step's rows
+  // before its first product
+  __builtin_amdgcn_s_waitcnt(0);
   for (int step = 0; step < T; step += 128) {
-    // the next step's key and rows, in flight under this step's products,
-    // and the list entry of the step after it
+    // the next step's key, base entry and rows, in flight under this step's
+    // products, and the list entry of the step after it (issued also on the
+    // last step, where they read in-bounds rows that nothing uses)
     const int en = e + 128;
     uint32_t rn;
-    int64_t prn;
+    int32_t bin, adjn;
     bf16x8b kn[4], vn[4];
-    const bool more = step + 128 < T;
-    int32_t f_after = 0;
-    if (more) {
-      key_of(en, f_next, rn, prn);
-      load_frags(rn, kn, vn);
-      f_after = list_at(en + 128);
-    }
+    key_of(en, f_next, rn, bin, adjn);
+    const int32_t bvn = base[max(bin, 0)];
+    load_frags(rn, kn, vn);
+    const int32_t f_after = list_at(en + 128);
     // S[q][e] = Q K^T and dP[q][e] = dO V^T over all 128 queries, 32 at a
     // time (query group c: tiles qt = 2c, 2c + 1, rows q = 16 qt + 4 jg + i,
     // column e = l16).  Software-pipelined: group c + 1's products are issued
@@ -630,12 +654,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
       }
     };
     auto store = [&](int dt, f32x4b cv, f32x4b ck) __attribute__((always_inline)) {
-      if (pr >= 0) {
-        const int64_t o = pr * kD + 16 * dt + 4 * jg;
-        *reinterpret_cast<uint2*>(pvd + o) = make_uint2(pack_bf16(cv[0], cv[1]), pack_bf16(cv[2], cv[3]));
-        ck *= a.scale;
-        *reinterpret_cast<uint2*>(pkd + o) = make_uint2(pack_bf16(ck[0], ck[1]), pack_bf16(ck[2], ck[3]));
-      }
+      const int64_t o = pr * kD + 16 * dt + 4 * jg;
+      *reinterpret_cast<uint2*>(pvd + o) = make_uint2(pack_bf16(cv[0], cv[1]), pack_bf16(cv[2], cv[3]));
+      ck *= a.scale;
+      *reinterpret_cast<uint2*>(pkd + o) = make_uint2(pack_bf16(ck[0], ck[1]), pack_bf16(ck[2], ck[3]));
     };
     {
       f32x4b va, ka, vb, kb2;
@@ -651,14 +673,12 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkv_kernel(BwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) {
-      e = en;
-      r = rn;
-      pr = prn;
-      f_next = f_after;
+    e = en;
+    r = rn;
+    pr = part_row(bin, bvn, adjn);
+    f_next = f_after;
 #pragma unroll
-      for (int st = 0; st < 4; ++st) { kf[st] = kn[st]; vf[st] = vn[st]; }
-    }
+    for (int st = 0; st < 4; ++st) { kf[st] = kn[st]; vf[st] = vn[st]; }
   }
 }
 
@@ -767,7 +787,7 @@ hipError_t launch_prefill_backward(const BwdArgs& a, int d, hipStream_t s) {
   if (d != kD || a.q_block != 128 || a.K > kListMaxB || a.K < 1) return hipErrorInvalidValue;
   if (a.levels < 1 || a.levels > 8 || a.N < 1 || a.nblk != (a.N + 127) / 128) return hipErrorInvalidValue;
   if ((int64_t)a.N * kRowB >= (1ll << 31) || (int64_t)a.Nc * kRowB >= (1ll << 31)) return hipErrorInvalidValue;
-  if (a.R < (int64_t)a.N + (int64_t)a.nblk * a.K || a.R >= (1ll << 31)) return hipErrorInvalidValue;
+  if (a.R < (int64_t)a.N + (int64_t)a.nblk * a.K + 1 || a.R >= (1ll << 31)) return hipErrorInvalidValue;
   const int nh = a.B * a.H;
   if (nh == 0) return hipSuccess;
   const int64_t rows = (int64_t)nh * a.N;
