@@ -345,6 +345,9 @@ def run_decode(args, torch, sa, workloads, workload=None, steps=None, warmup=Non
     step_b /= len(insts)
     tokens = cfg.batch * cfg.n_q_heads * cfg.n_ctx
     kernel = "sparse_attn_decode (decode_mfma_kernel + decode_item_combine_kernel)"
+    if per_head:
+        kernel = ("sparse_attn_decode, per-head sets (head_union_mark_kernel + "
+                  "head_union_compact_kernel + decode_mfma_kernel + decode_item_combine_kernel)")
     sha = source_sha(["decode.hip", "decode_mfma.hip", "common.hpp", "args.hpp"])
     achieved = attn_b / t_kernel / 1e9
     res = {
