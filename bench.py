@@ -380,7 +380,8 @@ def run_decode(args, torch, sa, workloads, workload=None, steps=None, warmup=Non
                               "repeated"},
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": traffic_record(kernel, cfg.name, sha),
+                     # the counters were taken on the workload's own inputs (alpha 1)
+                     "traffic": traffic_record(kernel, cfg.name, sha) if alpha == 1.0 else None,
                      "bytes_per_launch": attn_b, "launch_us": t_kernel * 1e6,
                      "source_sha": sha},
     }
