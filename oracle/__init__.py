@@ -18,7 +18,8 @@ Sources (web summaries of five papers; cited by page title and section):
   Memory architecture: hot / warm (LRU) / cold (host RAM) K/V tiers.
 * "Lighthouse Attention" summary - Methodology 2A-2C: symmetric mean pyramid,
   parameter-free l2 scoring with max inheritance, joint top-K across levels,
-  dense attention on the gathered subsequence and scatter back; the backward
+  dense attention on the gathered subsequence and scatter back (coarse query
+  entries attend too, their outputs returned to their own slots); the backward
   pass through the gather, the attention and the scatter (2B: the selection
   itself gets no gradient).
 * "Autonomia de Cabecas (AoH)" summary - Methodology item 4: head scores are
@@ -50,7 +51,7 @@ from .local import local_set
 from .hga import (high_freq_pairs, chunk_summary, chunk_summaries, group_summaries,
                   route_token_list, route_scores, route_prefill_block, route_prefill_rows)
 from .lighthouse import (pyramid_levels, pyramid_scores, visible_entries,
-                         block_select, prefill_block, prefill)
+                         block_select, prefill_block, prefill, coarse_block, prefill_coarse)
 from .lighthouse_bwd import block_grads, pyramid_backward, prefill_grads, n_entries
 from .decode import decode_step, decode_token_sets, decode_token_sets_per_head
 from .prefill_heads import prefill_visible, head_prefill_rows, visible_pairs

@@ -20,8 +20,13 @@ Readings (the summary leaves these open):
     descending, then level ascending, then index ascending; at most K are
     taken (all when fewer are visible);
   * each query of block b also attends, causally, to the block's own level-0
-    keys; only level-0 queries produce outputs (the coarse Q levels are built
-    as part of the pyramid), and a query's output is written to its own row;
+    keys, and a query's output is written to its own row;
+  * symmetric queries (2A, 2C): a coarse query entry of level l >= 1 whose
+    span lies in block b attends to the same selected entries and to the
+    block's own level-l keys up to itself - the level-0 rule applied to level
+    l - and its output goes back to its own slot of an output pyramid (the
+    inverse of the gather).  How a model merges the levels of that pyramid is
+    not the attention's to decide and is not modelled;
   * each stored coarse level is the exact mean of its level-0 rows rounded
     once to the workload element type.
 """
@@ -160,3 +165,55 @@ def prefill(Q, K, V, levels, factor, q_block, top_k, store="bf16", blocks=None):
         out[lo:min(N, lo + q_block)] = prefill_block(Q, K, V, kc, vc, sel, b, q_block,
                                                      levels, factor)
     return out, kc, vc, sels
+
+
+def coarse_block(QC, KC, VC, K, V, sel, block, q_block, levels, factor, scale=None):
+    """Outputs of the coarse query entries of one block, one [n_l, d] array
+    per level l = 1 .. L-1 (n_l = the block's level-0 length / p^l): entry j
+    of level l in the block attends to the block's selected entries ``sel``
+    (rows of level-0 K/V or of the coarse levels KC/VC) and to the block's own
+    level-l keys up to and including itself.  QC, KC, VC: coarse levels 1 ..
+    L-1 as lists of [N / p^l, d] arrays."""
+    N, d = np.asarray(K).shape
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    Ks = entry_rows(sel, K, KC, N, levels, factor)
+    Vs = entry_rows(sel, V, VC, N, levels, factor)
+    lo0 = q_block * block
+    hi0 = min(N, lo0 + q_block)
+    outs = []
+    for lvl in range(1, levels):
+        span = factor ** lvl
+        lo, hi = lo0 // span, hi0 // span
+        Qb = np.asarray(QC[lvl - 1][lo:hi], np.float64)
+        Kt = np.concatenate([Ks, np.asarray(KC[lvl - 1][lo:hi], np.float64)])
+        Vt = np.concatenate([Vs, np.asarray(VC[lvl - 1][lo:hi], np.float64)])
+        a = (Qb @ Kt.T) * scale
+        rows = np.arange(hi - lo)[:, None]
+        cols = np.arange(hi - lo)[None, :]
+        a[:, len(Ks):] = np.where(cols <= rows, a[:, len(Ks):], -np.inf)
+        w = np.exp(a - a.max(axis=1, keepdims=True))
+        outs.append((w / w.sum(axis=1, keepdims=True)) @ Vt)
+    return outs
+
+
+def prefill_coarse(Q, K, V, levels, factor, q_block, top_k, store="bf16", blocks=None):
+    """The coarse queries' outputs for one (sequence, head), scattered back to
+    their slots: [O_1, ..., O_{L-1}] with O_l [N / p^l, d] (rows of blocks not
+    visited are NaN), on the same pyramid and selections as ``prefill``."""
+    Q = np.asarray(Q, np.float64)
+    N, d = Q.shape
+    qc = pyramid_levels(Q, levels, factor, store)
+    kc = pyramid_levels(K, levels, factor, store)
+    vc = pyramid_levels(V, levels, factor, store)
+    sc = pyramid_scores(Q, K, levels, factor)
+    nb = (N + q_block - 1) // q_block
+    blocks = range(nb) if blocks is None else blocks
+    outs = [np.full((N // factor ** l, d), np.nan) for l in range(1, levels)]
+    for b in blocks:
+        sel = block_select(sc, b, N, levels, factor, q_block, top_k)
+        per = coarse_block(qc, kc, vc, K, V, sel, b, q_block, levels, factor)
+        for lvl in range(1, levels):
+            span = factor ** lvl
+            lo = q_block * b // span
+            outs[lvl - 1][lo:lo + per[lvl - 1].shape[0]] = per[lvl - 1]
+    return outs

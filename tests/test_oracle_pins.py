@@ -499,6 +499,95 @@ def test_prefill_block_matches_sdpa_on_gathered_rows():
         np.testing.assert_allclose(out[i], sdpa64(Q[i], Kt, Vt)[0], atol=1e-12)
 
 
+# ---------------------------------------------------------------- coarse queries (symmetric 2A/2C)
+def _span_means(X, levels, factor):
+    """Coarse levels 1 .. L-1 of X as plain reshaped means (no rounding)."""
+    X = np.asarray(X, np.float64)
+    return [X.reshape(-1, factor ** l, X.shape[1]).mean(axis=1) for l in range(1, levels)]
+
+
+def test_coarse_queries_are_sdpa_on_gathered_rows():
+    """Each coarse query of a block: torch SDPA over the block's selected rows
+    followed by its own level's rows of the block up to itself."""
+    rng = np.random.default_rng(31)
+    N, d, L, p, qb = 128, 16, 3, 2, 16
+    Q, K, V = (rng.standard_normal((N, d)) for _ in range(3))
+    qc, kc, vc = (_span_means(X, L, p) for X in (Q, K, V))
+    sc = oracle.pyramid_scores(Q, K, L, p)
+    for blk in (0, 3, 7):
+        sel = oracle.block_select(sc, blk, N, L, p, qb, 12)
+        Ks = LH.entry_rows(sel, K, kc, N, L, p)
+        Vs = LH.entry_rows(sel, V, vc, N, L, p)
+        outs = oracle.coarse_block(qc, kc, vc, K, V, sel, blk, qb, L, p)
+        for lvl in (1, 2):
+            lo = qb * blk // p ** lvl
+            n = qb // p ** lvl
+            assert outs[lvl - 1].shape == (n, d)
+            for j in range(n):
+                Kt = np.concatenate([Ks, kc[lvl - 1][lo:lo + j + 1]])
+                Vt = np.concatenate([Vs, vc[lvl - 1][lo:lo + j + 1]])
+                np.testing.assert_allclose(outs[lvl - 1][j], sdpa64(qc[lvl - 1][lo + j], Kt, Vt)[0],
+                                           atol=1e-12)
+
+
+def test_coarse_queries_of_first_block_are_causal_sdpa_per_level():
+    """Block 0 sees nothing before it: each level's coarse queries are plain
+    causal attention over that level's rows of the block; the first entry of
+    each level sees only itself."""
+    rng = np.random.default_rng(32)
+    N, d, L, p, qb = 64, 8, 3, 4, 32
+    Q, K, V = (rng.standard_normal((N, d)) for _ in range(3))
+    qc, kc, vc = (_span_means(X, L, p) for X in (Q, K, V))
+    outs = oracle.coarse_block(qc, kc, vc, K, V, np.zeros(0, np.int64), 0, qb, L, p)
+    for lvl in (1, 2):
+        n = qb // p ** lvl
+        ref = sdpa64(qc[lvl - 1][:n], kc[lvl - 1][:n], vc[lvl - 1][:n], causal=True)
+        np.testing.assert_allclose(outs[lvl - 1], ref, atol=1e-12)
+        np.testing.assert_allclose(outs[lvl - 1][0], vc[lvl - 1][0], atol=1e-14)
+
+
+def test_coarse_queries_constant_values_and_list_order():
+    """Equal value rows give that row for every coarse query; the order of
+    the selected list does not matter (attention over a set)."""
+    rng = np.random.default_rng(33)
+    N, d, L, p, qb = 96, 8, 2, 4, 16
+    Q, K = rng.standard_normal((N, d)), rng.standard_normal((N, d))
+    c = rng.standard_normal(d)
+    V = np.tile(c, (N, 1))
+    qc, kc, vc = (_span_means(X, L, p) for X in (Q, K, V))
+    sc = oracle.pyramid_scores(Q, K, L, p)
+    sel = oracle.block_select(sc, 4, N, L, p, qb, 9)
+    outs = oracle.coarse_block(qc, kc, vc, K, V, sel, 4, qb, L, p)
+    np.testing.assert_allclose(outs[0], np.tile(c, (qb // p, 1)), atol=1e-12)
+    V = rng.standard_normal((N, d))
+    vc = _span_means(V, L, p)
+    a = oracle.coarse_block(qc, kc, vc, K, V, sel, 4, qb, L, p)[0]
+    b = oracle.coarse_block(qc, kc, vc, K, V, sel[::-1].copy(), 4, qb, L, p)[0]
+    np.testing.assert_allclose(a, b, atol=1e-12)
+
+
+def test_prefill_coarse_scatters_each_block_to_its_own_slots():
+    """The pipeline writes a block's coarse outputs to the rows its entries
+    occupy in each level and nothing else; with L = 1 there are none."""
+    rng = np.random.default_rng(34)
+    N, d, L, p, qb, K = 128, 8, 3, 2, 16, 10
+    Q, K_, V = (rng.standard_normal((N, d)) for _ in range(3))
+    outs = oracle.prefill_coarse(Q, K_, V, L, p, qb, K, store=None, blocks=[2, 5])
+    qc, kc, vc = (_span_means(X, L, p) for X in (Q, K_, V))
+    sc = oracle.pyramid_scores(Q, K_, L, p)
+    for lvl in (1, 2):
+        span = p ** lvl
+        done = np.zeros(N // span, bool)
+        for blk in (2, 5):
+            sel = oracle.block_select(sc, blk, N, L, p, qb, K)
+            ref = oracle.coarse_block(qc, kc, vc, K_, V, sel, blk, qb, L, p)[lvl - 1]
+            lo = qb * blk // span
+            np.testing.assert_allclose(outs[lvl - 1][lo:lo + qb // span], ref, atol=1e-12)
+            done[lo:lo + qb // span] = True
+        assert np.isnan(outs[lvl - 1][~done]).all() and not np.isnan(outs[lvl - 1][done]).any()
+    assert oracle.prefill_coarse(Q, K_, V, 1, p, qb, K, store=None) == []
+
+
 # ---------------------------------------------------------------- three-level pyramid, by hand
 def _hand_value(v):
     """Numbers of the hand fixtures: plain, a fraction "a/b", or 2 sqrt(2) ln 2."""
