@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_VERSION 4
+#define SPARSE_ATTN_VERSION 5
 
 /* Size of the static device scratch array behind sparse_attn_decode_noalloc
  * (one per GPU the library runs on, held until the process ends). */
@@ -182,6 +182,8 @@ typedef struct sa_buffers {
   float* grad_q;        /* [B,H,N,d] fp32    gradient w.r.t. level-0 Q           */
   float* grad_k;        /* [B,H,N,d] fp32    gradient w.r.t. level-0 K           */
   float* grad_v;        /* [B,H,N,d] fp32    gradient w.r.t. level-0 V           */
+  /* coarse-query outputs of the pyramid prefill (sparse_attn_prefill_coarse)   */
+  float* out_pyr;       /* [B,H,Nc,d] fp32   one row per coarse entry, as pyr_q  */
 } sa_buffers;
 
 /*
@@ -333,6 +335,27 @@ int32_t sparse_attn_decode_noalloc(const sa_params* params, const sa_buffers* bu
 int32_t sparse_attn_prefill_chunked(const sa_params* params, const sa_buffers* bufs,
                                     void* workspace, size_t* workspace_bytes,
                                     void* hip_stream);
+
+/*
+ * sparse_attn_prefill_coarse - the coarse queries of the pyramid-selection
+ * prefill (Lighthouse summary, 2A: Q, K and V are aggregated symmetrically;
+ * 2C: the gathered entries attend as one subsequence and each output is
+ * scattered back to where its entry came from).  For every block of q_block
+ * level-0 positions and every level l = 1 .. levels-1, each coarse query
+ * entry j of level l whose span lies in the block (rows of pyr_q) attends to
+ * the block's selected entries (as in sparse_attn_prefill_chunked) plus the
+ * block's own level-l entries up to and including j (rows of pyr_k / pyr_v),
+ * with scale 1/sqrt(d); the fp32 result goes to row j of level l in out_pyr
+ * (the pyr_q layout).  Level-0 outputs are sparse_attn_prefill_chunked's;
+ * how a model combines the levels is left to the caller.  Reads pyr_q,
+ * pyr_k, pyr_v, k_cache, v_cache, blk_idx, blk_count; writes out_pyr.  Same
+ * requirements as sparse_attn_prefill_chunked, with n_q_heads == n_kv_heads;
+ * levels = 1 has no coarse queries and returns SA_OK with nothing written.
+ * No workspace; no backward (sparse_attn_prefill_backward covers the level-0
+ * outputs only).
+ */
+int32_t sparse_attn_prefill_coarse(const sa_params* params, const sa_buffers* bufs,
+                                   void* hip_stream);
 
 /*
  * sparse_attn_prefill_backward - gradients of the pyramid-selection prefill

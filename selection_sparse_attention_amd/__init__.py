@@ -34,7 +34,7 @@ SEL_TOPP, SEL_TOPK, SEL_ROUTE2, SEL_PYRAMID_TOPK, SEL_ROUTE2_PREFILL, SEL_TOPK_B
 EXPORTED = ("sparse_attn_index_build", "sparse_attn_select", "sparse_attn_decode",
             "sparse_attn_decode_noalloc", "sparse_attn_prefill_chunked",
             "sparse_attn_prefill_heads", "sparse_attn_prefill_backward",
-            "sparse_attn_tier_fetch",
+            "sparse_attn_prefill_coarse", "sparse_attn_tier_fetch",
             "sparse_attn_status_string", "sparse_attn_version")
 
 
@@ -60,7 +60,7 @@ class Params(ctypes.Structure):
 _BUF_FIELDS = ["q_pre", "k_pre", "q", "k_cache", "v_cache", "proj_q", "proj_k", "q_idx",
                "k_idx", "chunk_sum", "group_sum", "pyr_q", "pyr_k", "pyr_v", "pyr_scores",
                "sel_idx", "sel_count", "blk_idx", "blk_count", "out",
-               "grad_out", "lse", "grad_q", "grad_k", "grad_v"]
+               "grad_out", "lse", "grad_q", "grad_k", "grad_v", "out_pyr"]
 
 
 class Buffers(ctypes.Structure):
@@ -104,6 +104,9 @@ _lib.sparse_attn_tier_fetch.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(B
                                         ctypes.POINTER(Tier), ctypes.c_void_p]
 _lib.sparse_attn_tier_fetch.restype = ctypes.c_int32
 _lib.sparse_attn_prefill_heads.restype = ctypes.c_int32
+_lib.sparse_attn_prefill_coarse.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(Buffers),
+                                            ctypes.c_void_p]
+_lib.sparse_attn_prefill_coarse.restype = ctypes.c_int32
 _lib.sparse_attn_status_string.argtypes = [ctypes.c_int32]
 _lib.sparse_attn_status_string.restype = ctypes.c_char_p
 _lib.sparse_attn_version.restype = ctypes.c_int32
@@ -331,6 +334,14 @@ def tier_fetch(params: Params, bufs: Buffers, tier: Tier, stream=None):
     write the lists as rows of the device tier (tier.rows)."""
     _check(_lib.sparse_attn_tier_fetch(ctypes.byref(params), ctypes.byref(bufs), ctypes.byref(tier),
                                        _stream(stream)), "tier_fetch")
+
+
+def prefill_coarse(params: Params, bufs: Buffers, stream=None):
+    """Coarse queries of the pyramid prefill: every coarse entry of a block
+    attends to the block's list and its own level's entries of the block up
+    to itself; outputs to bufs.out_pyr (no workspace)."""
+    _check(_lib.sparse_attn_prefill_coarse(ctypes.byref(params), ctypes.byref(bufs),
+                                           _stream(stream)), "prefill_coarse")
 
 
 def prefill_heads(params: Params, bufs: Buffers, stream=None):

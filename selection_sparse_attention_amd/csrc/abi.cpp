@@ -618,6 +618,37 @@ int32_t sparse_attn_prefill_chunked(const sa_params* p, const sa_buffers* b, voi
   return hip_status(sa::launch_prefill(a, p->head_dim, static_cast<hipStream_t>(stream)));
 }
 
+int32_t sparse_attn_prefill_coarse(const sa_params* p, const sa_buffers* b, void* stream) {
+  int32_t st = check_common(p, b);
+  if (st) return st;
+  PyrGeom pg;
+  if ((st = pyramid_geom(p, &pg, false))) return st;
+  if (p->q_block < 1 || p->q_block % pg.top_span || p->block_top_k < 1) return SA_ERR_INVALID_ARG;
+  if (p->dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+  if (p->head_dim != 128 || p->q_block != 128) return SA_ERR_UNSUPPORTED;
+  if (p->block_top_k > 8192) return SA_ERR_UNSUPPORTED;
+  if (p->n_ctx >= (1 << 23)) return SA_ERR_UNSUPPORTED;
+  if (p->levels == 1) return SA_OK;                        // no coarse queries
+  if (!b->k_cache || !b->v_cache || !b->blk_idx || !b->blk_count || !b->pyr_q || !b->pyr_k ||
+      !b->pyr_v || !b->out_pyr)
+    return SA_ERR_INVALID_ARG;
+  sa::PrefillArgs a{};
+  a.q = b->pyr_q; a.k = b->k_cache; a.v = b->v_cache; a.pk = b->pyr_k; a.pv = b->pyr_v;
+  a.blk_idx = b->blk_idx; a.blk_count = b->blk_count; a.out = b->out_pyr; a.lse = nullptr;
+  a.B = p->batch; a.H = p->n_q_heads; a.N = p->n_ctx; a.Nc = pg.Nc; a.nblk = pg.nblk;
+  a.K = p->block_top_k; a.q_block = p->q_block;
+  a.Hkv = p->n_kv_heads; a.G = 1; a.kv_stride = p->n_ctx;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->head_dim));
+  a.pq = b->pyr_q; a.out_c = b->out_pyr; a.coarse = 1; a.levels = p->levels;
+  int span = 1;
+  for (int l = 0; l < 8; ++l) {
+    a.c_off[l] = (l >= 1 && l < p->levels) ? pg.off[l] - p->n_ctx : 0;
+    a.c_span[l] = span;
+    if (l + 1 < p->levels) span *= p->factor;
+  }
+  return hip_status(sa::launch_prefill(a, p->head_dim, static_cast<hipStream_t>(stream)));
+}
+
 int32_t sparse_attn_tier_fetch(const sa_params* p, const sa_buffers* b, const sa_tier* t,
                                void* stream) {
   int32_t st = check_common(p, b);

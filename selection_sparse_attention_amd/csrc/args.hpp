@@ -190,6 +190,14 @@ struct PrefillArgs {
   int32_t n_cls[2];                              // heads in each class
   int32_t units0;                                // workgroups of class 0
   uint8_t cls_heads[2][kMaxPrefillHeads];        // the heads of each class
+  // coarse-query mode (lists, coarse != 0): the block's coarse query entries
+  // of levels 1 .. levels-1 (rows of pq, level 1 first) attend in place of
+  // its level-0 queries, each to the list and to the block's own entries of
+  // its level up to itself; outputs to out_c [B,H,Nc,d]
+  const void* pq;
+  float* out_c;
+  int32_t coarse, levels;
+  int32_t c_off[8], c_span[8];                   // per level l >= 1: first coarse row, p^l
 };
 
 // Backward pass of the pyramid prefill: inputs as the forward's, the

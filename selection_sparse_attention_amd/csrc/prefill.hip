@@ -9,6 +9,10 @@
 // and K/V belong to the head's KV head: GQA heads share both; a pyramid has
 // one query head per KV head):
 //   out[i] = sum_j softmax_j(q_i . k_j / sqrt(d)) v_j      (fp32)
+// The coarse-query mode applies the same rule to the block's coarse query
+// entries (2A: the pyramid is symmetric in Q, K and V): entry j of level l
+// sees the block's list and the block's own level-l keys up to j, and its
+// output goes to its own row of the output pyramid.
 //
 // gfx950 design, one 256-thread workgroup per (block, head), wave w owning
 // queries 32w .. 32w+31:
@@ -99,6 +103,36 @@ __device__ __forceinline__ float max_over_lane_groups(float v) {
   return max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Coarse-query mode: own entry u of a block whose level-0 part has nq rows
+// starting at q0 (the block's level-1 entries first, then level 2, ...) ->
+// its coarse row (-1 past the last), and in `first` the first own entry of
+// its level.  Per-level tables are read with constant indices only.
+__device__ __forceinline__ int coarse_entry(const PrefillArgs& a, int q0, int nq, int u, int& first) {
+  int row = -1, acc = 0;
+  first = 0;
+#pragma unroll
+  for (int l = 1; l < 8; ++l) {
+    if (l < a.levels) {
+      const int n = nq / a.c_span[l];
+      if (row < 0 && u < acc + n) {
+        row = a.c_off[l] + q0 / a.c_span[l] + (u - acc);
+        first = acc;
+      }
+      acc += n;
+    }
+  }
+  return row;
+}
+
+// coarse query entries of a block with nq level-0 rows
+__device__ __forceinline__ int coarse_count(const PrefillArgs& a, int nq) {
+  int acc = 0;
+#pragma unroll
+  for (int l = 1; l < 8; ++l)
+    if (l < a.levels) acc += nq / a.c_span[l];
+  return acc;
+}
+
 // HEADS = false: pyramid selection (each block's entry list from blk_idx,
 // then the block's own keys).  HEADS = true: head-split prefill, no list:
 // a block's key sequence is implicit - positions [0, A) (the sinks, A =
@@ -162,6 +196,11 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     list = a.blk_idx + ((int64_t)kvh * a.nblk + blk) * a.K;
     T = c_sel + nq;
   }
+  // queries of the tile: the block's level-0 rows, or (coarse mode) its
+  // coarse entries, which are also its own keys after the list
+  const bool coarse = !HEADS && a.coarse != 0;
+  const int nqv = coarse ? coarse_count(a, nq) : nq;
+  if (coarse) T = c_sel + nqv;
   const int ntiles = (T + kKT - 1) / kKT;
   const int64_t kv_rows = HEADS ? (int64_t)a.kv_stride : (int64_t)a.N;
   const uint16_t* qb = reinterpret_cast<const uint16_t*>(a.q) + (int64_t)bh * a.N * kD;
@@ -180,14 +219,22 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
 
   // ---- query fragments (B operand of S^T = K Q^T): query 32w + 16nt + l16,
   //      dims 32 jg + 8 s .. +8
+  //      (coarse mode: the entry's row of pq, its coarse row in crow and the
+  //      first own entry of its level in qlo; level-0 mode: qlo = 0)
   bf16x8p qf[2][4];
+  int crow[2] = {0, 0}, qlo[2] = {0, 0};
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int ql = 32 * wid + 16 * nt + l16;
+    const uint16_t* qrow = qb + (int64_t)(q0 + ql) * kD;
+    if (coarse && ql < nqv) {
+      crow[nt] = coarse_entry(a, q0, nq, ql, qlo[nt]);
+      qrow = reinterpret_cast<const uint16_t*>(a.pq) + ((int64_t)bh * a.Nc + crow[nt]) * kD;
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       uint4 w = make_uint4(0, 0, 0, 0);
-      if (ql < nq) w = *reinterpret_cast<const uint4*>(qb + (int64_t)(q0 + ql) * kD + 32 * jg + 8 * s);
+      if (ql < nqv) w = *reinterpret_cast<const uint4*>(qrow + 32 * jg + 8 * s);
       qf[nt][s] = __builtin_bit_cast(bf16x8p, w);
     }
   }
@@ -208,7 +255,12 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
         if ((unsigned)f < (unsigned)a.N) r = (uint32_t)f * kRowBytes;
         else if ((unsigned)(f - a.N) < (unsigned)a.Nc) r = (uint32_t)(f - a.N) * kRowBytes | kCoarse;
       } else if (e < T) {
-        r = (uint32_t)(q0 + e - c_sel) * kRowBytes;
+        if (coarse) {
+          int first;
+          r = (uint32_t)coarse_entry(a, q0, nq, e - c_sel, first) * kRowBytes | kCoarse;
+        } else {
+          r = (uint32_t)(q0 + e - c_sel) * kRowBytes;
+        }
       }
       s_seq[e] = r;
     }
@@ -333,9 +385,11 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
             bool ok;
             if constexpr (HEADS) {
               const int j = pos(e), qi = q0 + ql;
-              ok = e < T && j <= qi && (j < S || j > qi - W);
+              ok = (e < T) & (j <= qi) & ((j < S) | (j > qi - W));
             } else {
-              ok = (e < c_sel) || (e < T && (e - c_sel) <= ql);
+              // bitwise, not short-circuit: one compare chain and one select
+              const int u = e - c_sel;
+              ok = (e < c_sel) | ((e < T) & (u <= ql) & (u >= qlo[nt]));
             }
             s[mt][nt][i] = ok ? s[mt][nt][i] : -INFINITY;
           }
@@ -501,13 +555,16 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     lt += __shfl_xor(lt, 16);
     lt += __shfl_xor(lt, 32);
     const int ql = 32 * wid + 16 * nt + l16;
-    if (ql < nq) {
+    if (ql < nqv) {
       // the row's log-sum-exp (natural log) for the backward pass: the
       // weights were 2^(s sc - m), so the denominator is 2^m lt
-      if (a.lse != nullptr && jg == 0)
+      if (a.lse != nullptr && !coarse && jg == 0)
         a.lse[(int64_t)bh * a.N + q0 + ql] = (m[nt] + log2f(lt)) * 0.6931471805599453f;
       const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
-      float* orow = ob + (int64_t)(q0 + ql) * kD;
+      // the scatter back: a level-0 query's own row, or the coarse entry's
+      // own row of the output pyramid
+      float* orow = coarse ? a.out_c + ((int64_t)bh * a.Nc + crow[nt]) * kD
+                           : ob + (int64_t)(q0 + ql) * kD;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const f32x4p v = o[dt][nt] * inv;
@@ -521,6 +578,17 @@ hipError_t launch_prefill(const PrefillArgs& a, int d, hipStream_t s) {
   if (d != kD || a.q_block != 128 || a.K > kListMax) return hipErrorInvalidValue;
   if (a.G < 1 || a.H != a.Hkv * a.G || (a.G > 1 && a.Nc > 0)) return hipErrorInvalidValue;
   if (a.N >= kMaxRows || a.Nc >= kMaxRows) return hipErrorInvalidValue;
+  if (a.coarse) {
+    // the block's coarse entries fit one query tile (sum of 128 / p^l < 128)
+    // and every level's spans tile the block
+    if (a.levels < 2 || a.levels > 8 || !a.pq || !a.out_c || a.Nc < 1) return hipErrorInvalidValue;
+    int n = 0;
+    for (int l = 1; l < a.levels; ++l) {
+      if (a.c_span[l] < 2 || a.q_block % a.c_span[l] || a.N % a.c_span[l]) return hipErrorInvalidValue;
+      n += a.q_block / a.c_span[l];
+    }
+    if (n > 128) return hipErrorInvalidValue;
+  }
   const int nh = a.B * a.H;
   const int hpx = (nh + 7) / 8;
   dim3 grid(8 * hpx * a.nblk);

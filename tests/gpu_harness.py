@@ -134,6 +134,8 @@ class PrefillRun:
                                        device=DEV)
         self.t["blk_count"] = torch.full((B, H, self.nblk), -1, dtype=torch.int32, device=DEV)
         self.t["out"] = torch.full((B, H, N, d), float("nan"), dtype=torch.float32, device=DEV)
+        self.t["out_pyr"] = torch.full((B, H, max(nc, 1), d), float("nan"), dtype=torch.float32,
+                                       device=DEV)
         self.params = sa.params_from_config(cfg)
         self.ws_sel = sa.Workspace(DEV)
         self.ws_pf = sa.Workspace(DEV)
@@ -142,7 +144,8 @@ class PrefillRun:
         t = self.t
         return sa.make_buffers(q=t["q"], k_cache=t["k"], v_cache=t["v"], pyr_q=t["pq"],
                                pyr_k=t["pk"], pyr_v=t["pv"], pyr_scores=t["scores"],
-                               blk_idx=t["blk_idx"], blk_count=t["blk_count"], out=t["out"])
+                               blk_idx=t["blk_idx"], blk_count=t["blk_count"], out=t["out"],
+                               out_pyr=t["out_pyr"])
 
     def pyramid(self):
         sa.index_build(self.params, self.bufs(), sa.IDX_PYRAMID, 0, self.cfg.n_ctx)
@@ -152,3 +155,6 @@ class PrefillRun:
 
     def prefill(self):
         sa.prefill_chunked(self.params, self.bufs(), self.ws_pf)
+
+    def coarse(self):
+        sa.prefill_coarse(self.params, self.bufs())

@@ -359,6 +359,34 @@ def test_prefill_backward_validation_and_size():
         setattr(b, name, FAKE)
 
 
+def test_prefill_coarse_validation():
+    """The coarse-query prefill: one level means no coarse queries (SA_OK,
+    nothing launched); grouped heads, fp32, d = 64, a list longer than 8192,
+    a length the top span does not divide and a missing coarse buffer are
+    refused before anything is launched."""
+    b = _full_bufs()
+    b.out_pyr = FAKE
+    ok = dict(batch=2, n_q_heads=4, n_kv_heads=4, head_dim=128, n_ctx=1024, levels=3, factor=4,
+              q_block=128, block_top_k=300)
+    pf = sa.make_params(**{**ok, "levels": 1})
+    assert sa.raw_call("prefill_coarse", ctypes.byref(pf), ctypes.byref(b), None) == sa.SA_OK
+    for kw, code in ((dict(n_kv_heads=2), sa.SA_ERR_INVALID_ARG),
+                     (dict(dtype="fp32"), sa.SA_ERR_UNSUPPORTED),
+                     (dict(head_dim=64), sa.SA_ERR_UNSUPPORTED),
+                     (dict(block_top_k=8193), sa.SA_ERR_UNSUPPORTED),
+                     (dict(q_block=64), sa.SA_ERR_UNSUPPORTED),
+                     (dict(n_ctx=1000), sa.SA_ERR_INVALID_ARG)):
+        pf = sa.make_params(**{**ok, **kw})
+        assert sa.raw_call("prefill_coarse", ctypes.byref(pf), ctypes.byref(b), None) == code, kw
+    pf = sa.make_params(**ok)
+    for name in ("pyr_q", "pyr_k", "pyr_v", "out_pyr", "blk_idx", "blk_count"):
+        keep = getattr(b, name)
+        setattr(b, name, None)
+        assert sa.raw_call("prefill_coarse", ctypes.byref(pf), ctypes.byref(b), None) == \
+            sa.SA_ERR_INVALID_ARG, name
+        setattr(b, name, keep)
+
+
 def test_tier_fetch_validation():
     """The tier fetch refuses, before anything runs: heads that are not all
     routed, per-head sets, a chunk that groups do not divide, fewer warm
