@@ -84,11 +84,14 @@ def traffic_record(kernel, workload, sha):
 
 # ----------------------------------------------------------------- decode
 class DecodeInstance:
-    def __init__(self, cfg, seed, sa, torch, workloads, alpha=1.0, like=None, per_head=False):
+    def __init__(self, cfg, seed, sa, torch, workloads, alpha=1.0, like=None, per_head=False,
+                 ws=None):
         """One step's device buffers.  ``like``: copy another instance's
         inputs (same values at new addresses, so the Infinity Cache holds
         nothing of this one when the other has just run).  ``per_head``:
-        every query head selects its own set."""
+        every query head selects its own set.  ``ws``: the (selection,
+        decode) workspaces, shared by instances run one after another on one
+        stream as a model's layers would share them (own ones if None)."""
         B, Hq, Hkv, d, n = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_ctx
         self.cfg = cfg
         self.per_head = per_head
@@ -119,8 +122,8 @@ class DecodeInstance:
             v_cache=t["v_cache"], proj_q=t["proj"], proj_k=t["proj"], q_idx=t["q_idx"],
             k_idx=t["k_idx"], chunk_sum=t.get("chunk_sum"), group_sum=t.get("group_sum"),
             sel_idx=t["sel_idx"], sel_count=t["sel_count"], out=t["out"])
-        self.ws_sel = sa.Workspace("cuda")
-        self.ws_dec = sa.Workspace("cuda")
+        self.ws_sel, self.ws_dec = ws if ws is not None else (sa.Workspace("cuda"),
+                                                              sa.Workspace("cuda"))
         self.sa = sa
         # prefill-time index over the whole history (not part of a step)
         if cfg.routed:
@@ -231,7 +234,12 @@ def run_decode(args, torch, sa, workloads, workload=None, steps=None, warmup=Non
     kinds = cfg.head_kind()
     log(f"[bench] generating {instances} instance(s) of {cfg.name} (alpha {alpha}"
         f"{', per-head sets' if per_head else ''})")
-    insts = [DecodeInstance(cfg, 1000 + i, sa, torch, workloads, alpha=alpha, per_head=per_head)
+    # the instances stand for the layers of a model run one after another on
+    # one stream: their inputs are distinct (cold), their workspaces are one
+    # pair, as a layer loop reuses its scratch
+    ws = (sa.Workspace("cuda"), sa.Workspace("cuda"))
+    insts = [DecodeInstance(cfg, 1000 + i, sa, torch, workloads, alpha=alpha, per_head=per_head,
+                            ws=ws)
              for i in range(instances)]
     # one step of each, then copies until a round of the rotation touches
     # >= 1 GiB (so no step finds its rows in the 256 MB Infinity Cache)
@@ -247,6 +255,7 @@ def run_decode(args, torch, sa, workloads, workload=None, steps=None, warmup=Non
     base = len(insts)
     while len(insts) < want:
         insts.append(DecodeInstance(cfg, 0, sa, torch, workloads, like=insts[len(insts) % base],
+                                    ws=ws,
                                     per_head=per_head))
     if len(insts) > base:
         log(f"[bench] {len(insts) - base} copies added: {len(insts)} instances, "
