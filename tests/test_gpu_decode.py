@@ -159,6 +159,46 @@ def test_select_strict_gap_variant():
         assert cnt[0, g] == m and np.array_equal(idx[0, g, :m], ref)
 
 
+def _check_topk_sets(cfg, inp, run):
+    idx, cnt = run.sets()
+    k, q = np64(inp["k_idx"]), np64(inp["q_idx"])
+    for b in range(cfg.batch):
+        for g in _ret_groups(cfg):
+            ref, m = oracle.select_topk(_oracle_logits(cfg, k, q, b, g), cfg.top_k)
+            assert cnt[b, g] == m, (b, g, cnt[b, g], m)
+            assert np.array_equal(idx[b, g, :m], ref), (b, g)
+
+
+def _run_lattice_select(cfg, inp):
+    run = DecodeRun(cfg, {}, n_cap=cfg.n_ctx)
+    run.t["k_idx"].copy_(to_dev(inp["k_idx"], cfg.dtype))
+    run.t["q_idx"].copy_(inp["q_idx"].to(DEV))
+    run.select()
+    torch.cuda.synchronize()
+    return run
+
+
+@pytest.mark.parametrize("spread", [False, True])
+@pytest.mark.parametrize("n,k", [(131072, 2048), (32768, 2048), (9000, 700)])
+def test_select_topk_one_tile_holds_the_top(n, k, spread):
+    """The row's highest keys all sit in its first tile: the first 1.5 k
+    positions get keys along the sign of the group's index query (equal
+    logits, or shifted half a step up and so spread), so one workgroup holds
+    the whole top k and the others none of it.  The sets stay exact."""
+    cfg = workloads.LLAMA_128K_TOPK.with_(batch=2, n_ctx=n, top_k=k)
+    log("select top-k, top in one tile", n, k, spread)
+    inp = workloads.lattice_index_inputs(cfg, 5, k_amp=8, q_amp=4)
+    G, m = cfg.gqa, (3 * k) // 2
+    for b in range(cfg.batch):
+        for g in _ret_groups(cfg):
+            sgn = torch.sign(inp["q_idx"][b, g * G:(g + 1) * G].mean(0))
+            if spread:
+                inp["k_idx"][b, g, :m] = (inp["k_idx"][b, g, :m] + 0.5 * sgn).clamp(-1.0, 1.0)
+            else:
+                inp["k_idx"][b, g, :m] = sgn
+    _check_topk_sets(cfg, inp, _run_lattice_select(cfg, inp))
+
+
 # ------------------------------------------------------------------ selector, crowded cuts
 def _select_exact(cfg, inp, mode):
     run = DecodeRun(cfg, {}, n_cap=cfg.n_ctx)
