@@ -141,9 +141,14 @@ class DecodeInstance:
             # the step completes at most one chunk: rebuild the last one
             t0 = (n // cfg.chunk) * cfg.chunk - 1 if n % cfg.chunk == 0 else n - 1
             sa.index_build(self.params, self.bufs, sa.IDX_CHUNK_SUMMARY, max(0, t0), n)
+            sa.select(self.params, self.bufs, self.sel_mode, self.ws_sel)
+        elif cfg.dtype == "bf16":
+            # the new token's index key and the step's index queries are
+            # projected by the selection itself (the fused append)
+            sa.select(self.params, self.bufs, self.sel_mode | sa.SEL_APPEND, self.ws_sel)
         else:
             sa.index_build(self.params, self.bufs, sa.IDX_LOWRANK, n - 1, n)
-        sa.select(self.params, self.bufs, self.sel_mode, self.ws_sel)
+            sa.select(self.params, self.bufs, self.sel_mode, self.ws_sel)
 
     def decode(self):
         self.sa.decode(self.params, self.bufs, self.ws_dec)

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_VERSION 5
+#define SPARSE_ATTN_VERSION 6
 
 /* Size of the static device scratch array behind sparse_attn_decode_noalloc
  * (one per GPU the library runs on, held until the process ends). */
@@ -103,6 +103,16 @@ typedef enum {
   SA_SEL_ROUTE2_PREFILL = 4,/* routed groups, prefill: per query block (chunk) */
   SA_SEL_TOPK_BY_SCORE = 5  /* retrieval groups: top_k, listed by index score   */
 } sa_select_mode;
+
+/* OR'ed into SA_SEL_TOPP, SA_SEL_TOPK or SA_SEL_TOPK_BY_SCORE: the decode
+ * step's index append is fused into the selection.  Before ranking, the call
+ * projects the query heads of every selecting row into q_idx and token
+ * n_ctx - 1 into k_idx, with the same bits as sparse_attn_index_build(
+ * SA_IDX_LOWRANK, n_ctx - 1, n_ctx) (which then need not be called).  Reads
+ * q_pre, k_pre, proj_q and proj_k as well; bf16 caches only
+ * (SA_ERR_UNSUPPORTED otherwise); q_pre, k_pre, proj_q, proj_k and q_idx
+ * 16-byte aligned.  With any other mode it gives SA_ERR_INVALID_ARG. */
+#define SA_SEL_APPEND 0x100
 
 /* Host struct, read only during the call. */
 typedef struct sa_params {

@@ -30,6 +30,7 @@ SA_BF16, SA_FP32 = 0, 1
 HEAD_LOCAL, HEAD_RETRIEVAL, HEAD_ROUTED = 0, 1, 2
 IDX_LOWRANK, IDX_CHUNK_SUMMARY, IDX_PYRAMID = 0, 1, 2
 SEL_TOPP, SEL_TOPK, SEL_ROUTE2, SEL_PYRAMID_TOPK, SEL_ROUTE2_PREFILL, SEL_TOPK_BY_SCORE = 0, 1, 2, 3, 4, 5
+SEL_APPEND = 0x100      # OR'ed into SEL_TOPP / SEL_TOPK / SEL_TOPK_BY_SCORE: fused index append
 
 EXPORTED = ("sparse_attn_index_build", "sparse_attn_select", "sparse_attn_decode",
             "sparse_attn_decode_noalloc", "sparse_attn_prefill_chunked",

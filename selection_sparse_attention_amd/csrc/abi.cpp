@@ -421,6 +421,10 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
   int32_t st = check_common(p, b);
   if (st) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool append = (mode & SA_SEL_APPEND) != 0;
+  mode &= ~SA_SEL_APPEND;
+  if (append && mode != SA_SEL_TOPP && mode != SA_SEL_TOPK && mode != SA_SEL_TOPK_BY_SCORE)
+    return SA_ERR_INVALID_ARG;
   if (mode == SA_SEL_PYRAMID_TOPK) {
     PyrGeom pg;
     if ((st = pyramid_geom(p, &pg))) return st;
@@ -492,6 +496,13 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
     if (!b->q_idx || !b->k_idx || !b->sel_idx || !b->sel_count) return SA_ERR_INVALID_ARG;
     if (!aligned16(b->k_idx)) return SA_ERR_INVALID_ARG;
     if (W > wmax) return SA_ERR_UNSUPPORTED;
+    if (append) {
+      if (p->dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+      if (!b->k_pre || !b->q_pre || !b->proj_q || !b->proj_k) return SA_ERR_INVALID_ARG;
+      if (!aligned16(b->k_pre) || !aligned16(b->q_pre) || !aligned16(b->proj_q) || !aligned16(b->proj_k) ||
+          !aligned16(b->q_idx))
+        return SA_ERR_INVALID_ARG;
+    }
     const bool mass = mode == SA_SEL_TOPP;
     sw = carve_select(ws, rows, cand_stride);
     sa::SelectArgs a{};
@@ -510,6 +521,14 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
     }
     a.W = W;
     a.spin_limit = select_spin_limit();
+    if (append && per > 8) {
+      // 4096-token tiles: the append as its own launch (the same bits)
+      if ((st = sparse_attn_index_build(p, b, SA_IDX_LOWRANK, p->n_ctx - 1, p->n_ctx, stream))) return st;
+    }
+    a.append = (append && per <= 8) ? 1 : 0;
+    a.d = p->head_dim;
+    a.k_pre = b->k_pre; a.q_pre = b->q_pre; a.proj_q = b->proj_q; a.proj_k = b->proj_k;
+    a.q_idx_w = b->q_idx; a.k_idx_w = b->k_idx;
     a.hist_c = sw.hist_c; a.hist_m = sw.hist_m; a.ctl = sw.ctl; a.slot_a = sw.slot_a; a.slot_b = sw.slot_b;
     a.cand = sw.cand; a.cand_stride = cand_stride;
     a.groups = gl;

@@ -71,6 +71,16 @@ struct SelectArgs {
   int32_t W;             // workgroups per row
   int32_t kv_div;        // rows per KV group of k_idx (G with per-head sets, else 1)
   int32_t spin_limit;    // polls per cross-workgroup wait (< 0: every wait fails)
+  // fused append (bf16): project the rows' queries and token n - 1's index key
+  // first, as the index build's append would (q_idx / k_idx are then written)
+  int32_t append;
+  int32_t d;             // head dim (64 or 128) of k_pre / q_pre
+  const void* k_pre;     // [B,Hkv,n_cap,d]
+  const void* q_pre;     // [B,Hq,d]
+  const float* proj_q;   // [Hkv,16,d]
+  const float* proj_k;   // [Hkv,16,d]
+  float* q_idx_w;        // q_idx, written by the append
+  void* k_idx_w;         // k_idx, row n - 1 written by the append
   // workspace; everything but `cand` is zero between calls
   uint32_t* hist_c;      // [rows, 3, 4096] counts of the three global digits
   double* hist_m;        // [rows, 3, 4096] masses of the three global digits

@@ -47,6 +47,7 @@
 // the merged histogram is read; later digits use R directly.
 #include "args.hpp"
 #include "common.hpp"
+#include "index_project.hpp"
 
 namespace sa {
 
@@ -448,10 +449,37 @@ __device__ Cut cut_small(const SelectArgs& a, Cut ct, SelShared<MASS>& sh, int C
   return sh.fin;
 }
 
+// The fused append of one row (bf16 caches): the row's G query heads
+// projected into qrows (every workgroup; the first also stores q_idx) and,
+// in the workgroup holding token n - 1, that token's index key into knew
+// (bf16 bits) and k_idx - the index build's projection, so the same bits.
+template <int D>
+__device__ __forceinline__ void fused_append(const SelectArgs& a, int b, int g, int wg, float* qrows,
+                                             uint16_t* knew) {
+  const int kvg = g / a.kv_div;                              // KV group within the sequence
+  const int64_t qrow0 = (int64_t)b * a.Hq + (int64_t)g * a.G;
+  project_rows_mfma_st<D, 1, kThreads>(a.q_pre, a.proj_q + (int64_t)kvg * 16 * D, qrow0, 0, a.G,
+                                       [&](int r, int col, float v) __attribute__((always_inline)) {
+                                         qrows[r * 16 + col] = v;
+                                         if (wg == 0) a.q_idx_w[(qrow0 + r) * 16 + col] = v;
+                                       });
+  if (wg == a.W - 1) {
+    const int64_t krow0 = ((int64_t)b * (a.Hkv / a.kv_div) + kvg) * a.n_cap;
+    project_rows_mfma_st<D, 1, kThreads>(a.k_pre, a.proj_k + (int64_t)kvg * 16 * D, krow0, a.n - 1, a.n,
+                                         [&](int r, int col, float v) __attribute__((always_inline)) {
+                                           const uint16_t h = f32_to_bf16(v);
+                                           knew[col] = h;
+                                           reinterpret_cast<uint16_t*>(a.k_idx_w)[(krow0 + r) * 16 + col] = h;
+                                         });
+  }
+}
+
 // ------------------------------------------------------------------ the kernel
 template <typename T, bool MASS, int PER>
 __global__ __launch_bounds__(kThreads) void select_fused_kernel(SelectArgs a) {
   __shared__ SelShared<MASS> sh;
+  __shared__ float s_qrows[8 * 16];        // fused append: the row's query heads' q_idx
+  __shared__ uint16_t s_knew[16];          // fused append: token n - 1's index key
   const int row = blockIdx.y, wg = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
   int b, g;
@@ -482,10 +510,27 @@ __global__ __launch_bounds__(kThreads) void select_fused_kernel(SelectArgs a) {
       for (int i = 0; i < BATCH; ++i)
         kr[i].load(a.k_idx, krow + min(j0 + (i0 + i) * kThreads + tid, a.n - 1));
       if (i0 == 0) {
-        for (int hh = 0; hh < a.G; ++hh) {
-          const float* qp = a.q_idx + ((int64_t)b * a.Hq + g * a.G + hh) * 16;
+        bool fused = false;
+        // (4096-token tiles would spill with it: the host appends separately)
+        if constexpr (sizeof(T) == 2 && PER <= 8) {
+          if (a.append) {
+            // the projections overlap the index rows already in flight
+            if (a.d == 128) fused_append<128>(a, b, g, wg, s_qrows, s_knew);
+            else fused_append<64>(a, b, g, wg, s_qrows, s_knew);
+            __syncthreads();
+            for (int hh = 0; hh < a.G; ++hh) {
 #pragma unroll
-          for (int c = 0; c < 16; ++c) qb[c] += qp[c];
+              for (int c = 0; c < 16; ++c) qb[c] += s_qrows[hh * 16 + c];
+            }
+            fused = true;
+          }
+        }
+        if (!fused) {
+          for (int hh = 0; hh < a.G; ++hh) {
+            const float* qp = a.q_idx + ((int64_t)b * a.Hq + g * a.G + hh) * 16;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) qb[c] += qp[c];
+          }
         }
         const float invG = 1.0f / (float)a.G;
 #pragma unroll
@@ -493,6 +538,15 @@ __global__ __launch_bounds__(kThreads) void select_fused_kernel(SelectArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < BATCH; ++i) {
+        if constexpr (sizeof(T) == 2 && PER <= 8) {
+          // token n - 1 under the fused append: its key from the projection
+          // (the row loaded from k_idx predates it)
+          if (a.append && j0 + (i0 + i) * kThreads + tid == a.n - 1) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              kr[i].w[e >> 2][e & 3] = (uint32_t)s_knew[2 * e] | ((uint32_t)s_knew[2 * e + 1] << 16);
+          }
+        }
         float l = kr[i].dot(qb) * 0.25f;
         if (l == 0.f) l = 0.f;                  // fold -0 into +0
         const bool valid = j0 + (i0 + i) * kThreads + tid < a.n;

@@ -149,6 +149,29 @@ def test_missing_buffers_are_rejected():
     assert _decode(p, b, FAKE, need)[0] == sa.SA_ERR_INVALID_ARG
 
 
+def test_select_append_validation():
+    p = _decode_params()
+    _, need = _select(p, _full_bufs(), sa.SEL_TOPP | sa.SEL_APPEND)
+    assert need > 0
+    for mode in (sa.SEL_ROUTE2, sa.SEL_PYRAMID_TOPK, sa.SEL_ROUTE2_PREFILL):
+        assert _select(p, _full_bufs(), mode | sa.SEL_APPEND)[0] == sa.SA_ERR_INVALID_ARG
+    # fp32 caches: no fused append
+    pf = _decode_params(dtype="fp32")
+    _, nf = _select(pf, _full_bufs(), sa.SEL_TOPP | sa.SEL_APPEND)
+    assert _select(pf, _full_bufs(), sa.SEL_TOPP | sa.SEL_APPEND, FAKE, nf)[0] == \
+        sa.SA_ERR_UNSUPPORTED
+    # the projection's inputs, present and 16-byte aligned
+    for name in ("q_pre", "k_pre", "proj_q", "proj_k"):
+        b = _full_bufs()
+        setattr(b, name, None)
+        assert _select(p, b, sa.SEL_TOPP | sa.SEL_APPEND, FAKE, need)[0] == \
+            sa.SA_ERR_INVALID_ARG, name
+        b = _full_bufs()
+        setattr(b, name, FAKE + 8)
+        assert _select(p, b, sa.SEL_TOPP | sa.SEL_APPEND, FAKE, need)[0] == \
+            sa.SA_ERR_INVALID_ARG, name
+
+
 def test_decode_validation():
     b = _full_bufs()
     assert _decode(_decode_params(n_q_heads=6, n_kv_heads=2,

@@ -5,6 +5,7 @@ import pytest
 import torch
 
 import oracle
+import selection_sparse_attention_amd as sa
 import workloads
 from gpu_harness import DecodeRun, log, max_err, np64, np_inputs, to_dev, DEV
 
@@ -344,6 +345,49 @@ def test_decode_over_given_lists(cfg):
     err = max(max_err(out[b, h], o) for (b, h), o in ref.items())
     log("max err", err)
     assert err <= tol
+
+
+@pytest.mark.parametrize("cfg,per_head", [
+    (workloads.LLAMA_32K.with_(batch=2, n_ctx=5000), False),
+    (workloads.LLAMA_32K.with_(batch=2, n_ctx=5000, top_p=1.0, top_k=700), False),
+    (workloads.LLAMA_32K_S2O.with_(batch=2, n_ctx=6000, top_k=700), False),
+    (workloads.LLAMA_32K.with_(batch=2, n_ctx=4000), True),
+    (workloads.LLAMA_32K.with_(batch=1, n_ctx=3000, head_dim=64), False),
+    (workloads.LLAMA_32K.with_(batch=1, n_ctx=2049), False),
+], ids=["topp", "topk", "by-score", "per-head", "d64", "tile-edge"])
+def test_select_fused_append_equals_separate_append(cfg, per_head):
+    """Three decode steps (contexts n - 2, n - 1, n) two ways: the index
+    append as its own call, then the selection; and the selection with the
+    append fused in (SEL_APPEND).  The index keys and queries they store,
+    the counts and the lists are the same bits."""
+    log("fused append", cfg.name, cfg.n_ctx, cfg.head_dim, per_head)
+    inp = workloads.decode_inputs(cfg, 14)
+    runs = [DecodeRun(cfg, inp, per_head=per_head) for _ in range(2)]
+    n = cfg.n_ctx
+    mode = (sa.SEL_TOPK_BY_SCORE if cfg.s2o_tau > 0 else
+            (sa.SEL_TOPK if cfg.top_k > 0 else sa.SEL_TOPP))
+    for r in runs:
+        r.index(0, n - 3)
+    for t in (n - 2, n - 1, n):
+        for fused, r in enumerate(runs):
+            r.params.n_ctx = t
+            if fused:
+                sa.select(r.params, r.bufs(), mode | sa.SEL_APPEND, r.ws_sel)
+            else:
+                sa.index_build(r.params, r.bufs(), sa.IDX_LOWRANK, t - 1, t)
+                sa.select(r.params, r.bufs(), mode, r.ws_sel)
+        torch.cuda.synchronize()
+        a, b = runs
+        assert torch.equal(a.t["k_idx"], b.t["k_idx"]), t
+        assert torch.equal(a.t["q_idx"], b.t["q_idx"]), t
+        assert torch.equal(a.t["sel_count"], b.t["sel_count"]), t
+        cnt = a.t["sel_count"].cpu()
+        rows = [idx for idx in np.ndindex(*cnt.shape) if int(cnt[idx]) >= 0]   # selecting rows
+        assert len(rows) == cfg.batch * (cfg.n_ret_q_heads if per_head else
+                                         cfg.n_ret_q_heads // cfg.gqa)
+        for idx in rows:
+            c = int(cnt[idx])
+            assert torch.equal(a.t["sel_idx"][idx][:c], b.t["sel_idx"][idx][:c]), (t, idx)
 
 
 # ------------------------------------------------------------------ end to end
