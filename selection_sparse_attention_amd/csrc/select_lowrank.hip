@@ -449,28 +449,52 @@ __device__ Cut cut_small(const SelectArgs& a, Cut ct, SelShared<MASS>& sh, int C
   return sh.fin;
 }
 
-// The fused append of one row (bf16 caches): the row's G query heads
+// The fused append of one row (bf16 caches): the row's G <= 16 query heads
 // projected into qrows (every workgroup; the first also stores q_idx) and,
 // in the workgroup holding token n - 1, that token's index key into knew
-// (bf16 bits) and k_idx - the index build's projection, so the same bits.
+// (bf16 bits) and k_idx - the index build's projection step by step, so the
+// same bits.  Wave 0 issues every load (query rows, the key row, both
+// projectors) before the first product; the other waves return at once and
+// wait at the caller's barrier.
 template <int D>
 __device__ __forceinline__ void fused_append(const SelectArgs& a, int b, int g, int wg, float* qrows,
                                              uint16_t* knew) {
+  if ((threadIdx.x >> 6) != 0) return;
+  const int lane = threadIdx.x & 63, col = lane & 15, kb = lane >> 4;
   const int kvg = g / a.kv_div;                              // KV group within the sequence
   const int64_t qrow0 = (int64_t)b * a.Hq + (int64_t)g * a.G;
-  project_rows_mfma_st<D, 1, kThreads>(a.q_pre, a.proj_q + (int64_t)kvg * 16 * D, qrow0, 0, a.G,
-                                       [&](int r, int col, float v) __attribute__((always_inline)) {
-                                         qrows[r * 16 + col] = v;
-                                         if (wg == 0) a.q_idx_w[(qrow0 + r) * 16 + col] = v;
-                                       });
-  if (wg == a.W - 1) {
-    const int64_t krow0 = ((int64_t)b * (a.Hkv / a.kv_div) + kvg) * a.n_cap;
-    project_rows_mfma_st<D, 1, kThreads>(a.k_pre, a.proj_k + (int64_t)kvg * 16 * D, krow0, a.n - 1, a.n,
-                                         [&](int r, int col, float v) __attribute__((always_inline)) {
-                                           const uint16_t h = f32_to_bf16(v);
-                                           knew[col] = h;
-                                           reinterpret_cast<uint16_t*>(a.k_idx_w)[(krow0 + r) * 16 + col] = h;
-                                         });
+  const int64_t krow0 = ((int64_t)b * (a.Hkv / a.kv_div) + kvg) * a.n_cap;
+  const bool key = wg == a.W - 1;
+  vl_u32x4 qa[D / 32], ka[D / 32];
+  ProjSlices<D> pq, pk;
+  load_row_slices<D>(a.q_pre, qrow0, 0, a.G, qa);
+  pq.load(a.proj_q + (int64_t)kvg * 16 * D);
+  if (key) {
+    load_row_slices<D>(a.k_pre, krow0, a.n - 1, a.n, ka);
+    pk.load(a.proj_k + (int64_t)kvg * 16 * D);
+  }
+  {
+    ProjParts<D> pp;
+    pp.split(pq);
+    const ix_f32x4 c = pp.tile(qa);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * kb + i;
+      if (r < a.G) {
+        qrows[r * 16 + col] = c[i];
+        if (wg == 0) a.q_idx_w[(qrow0 + r) * 16 + col] = c[i];
+      }
+    }
+  }
+  if (key) {
+    ProjParts<D> pp;
+    pp.split(pk);
+    const ix_f32x4 c = pp.tile(ka);
+    if (kb == 0) {                                          // row n - 1: lanes 0-15, first value
+      const uint16_t h = f32_to_bf16(c[0]);
+      knew[col] = h;
+      reinterpret_cast<uint16_t*>(a.k_idx_w)[(krow0 + a.n - 1) * 16 + col] = h;
+    }
   }
 }
 
@@ -478,7 +502,7 @@ __device__ __forceinline__ void fused_append(const SelectArgs& a, int b, int g, 
 template <typename T, bool MASS, int PER>
 __global__ __launch_bounds__(kThreads) void select_fused_kernel(SelectArgs a) {
   __shared__ SelShared<MASS> sh;
-  __shared__ float s_qrows[8 * 16];        // fused append: the row's query heads' q_idx
+  __shared__ float s_qrows[16 * 16];       // fused append: the row's query heads' q_idx
   __shared__ uint16_t s_knew[16];          // fused append: token n - 1's index key
   const int row = blockIdx.y, wg = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
