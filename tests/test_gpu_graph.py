@@ -6,6 +6,7 @@ library records only kernel launches)."""
 import pytest
 import torch
 
+import selection_sparse_attention_amd as sa
 import workloads
 from gpu_harness import DEV, DecodeRun, PrefillRun
 
@@ -37,8 +38,13 @@ def _same(a, b, groups=None):
     (workloads.HGA_64K.with_(batch=2, n_ctx=8192), False),
     (workloads.LLAMA_32K.with_(batch=2, n_ctx=4096, top_p=1.0, top_k=300, s2o_tau=0.01), False),
     (workloads.LLAMA_32K.with_(batch=2, n_ctx=8192 + 77), True),
-], ids=["topp", "topk", "routed", "early-stop", "per-head"])
+    (workloads.LLAMA_32K.with_(batch=2, n_ctx=8192 + 77), "fused"),
+], ids=["topp", "topk", "routed", "early-stop", "per-head", "fused-append"])
 def test_decode_step_graph_replays_match_eager(cfg, per_head):
+    """With "fused", the step's index append is done by the selection
+    (SEL_APPEND); every replay also rewrites the index key and queries."""
+    fused = per_head == "fused"
+    per_head = per_head is True
     inp = workloads.decode_inputs(cfg, 21, device=DEV)
     run = DecodeRun(cfg, inp, per_head=per_head)
     n = cfg.n_ctx
@@ -51,12 +57,16 @@ def test_decode_step_graph_replays_match_eager(cfg, per_head):
         if cfg.routed:
             t0 = (n // cfg.chunk) * cfg.chunk - 1 if n % cfg.chunk == 0 else n - 1
             run.summaries(max(0, t0), n)
+        elif fused:
+            mode = sa.SEL_TOPK if cfg.top_k > 0 else sa.SEL_TOPP
+            sa.select(run.params, run.bufs(), mode | sa.SEL_APPEND, run.ws_sel)
         else:
             run.index(n - 1, n)
-        run.select()
+        if not fused:
+            run.select()
         run.decode()
 
-    keys = ["sel_idx", "sel_count", "out"]
+    keys = ["sel_idx", "sel_count", "out"] + (["k_idx", "q_idx"] if fused else [])
     kinds = cfg.head_kind()
     if per_head:
         groups = [h for h in range(cfg.n_q_heads) if kinds[h] != workloads.HEAD_LOCAL]
@@ -71,9 +81,17 @@ def test_decode_step_graph_replays_match_eager(cfg, per_head):
     with torch.cuda.graph(g):
         step()
     torch.cuda.synchronize()
+    G = cfg.gqa
     for rep in range(4):
         for k in keys:                      # eager work between replays
-            run.t[k].fill_(-7)
+            if k == "k_idx":                # the rows a step writes: token n - 1's
+                for gg in groups:
+                    run.t[k][:, gg, n - 1].fill_(-7)
+            elif k == "q_idx":              # and the selecting groups' query heads'
+                for gg in groups:
+                    run.t[k][:, gg * G:(gg + 1) * G].fill_(-7)
+            else:
+                run.t[k].fill_(-7)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
