@@ -537,6 +537,40 @@ def test_edge_cases(cfg):
     _pipeline_check(cfg, 5, require_exact_sets=False)
 
 
+def _random_decode_configs(count, seed):
+    """Seeded small decode layers with every shape knob varied: batch, GQA
+    group (1 to 8), head dim, dtype, retrieval-head count, top-p (with and
+    without a floor) or top-k, sinks, window, and ragged context lengths."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([g for g in (1, 2, 4, 8) if hkv * g <= 32]))
+        n = int(rng.integers(1, 6000))
+        sinks = int(rng.integers(0, 9))
+        window = int(rng.integers(0 if sinks else 1, 400))
+        kw = dict(name=f"random{i}", batch=int(rng.integers(1, 4)), n_q_heads=hkv * G,
+                  n_kv_heads=hkv, head_dim=int(rng.choice([64, 128])), n_ctx=n,
+                  dtype=str(rng.choice(["bf16", "fp32"])), rope_base=float(rng.choice([1e4, 5e5])),
+                  n_ret_q_heads=G * int(rng.integers(1, hkv + 1)), sinks=sinks, window=window,
+                  needles_per_head=int(rng.integers(0, 9)) if n > 16 else 0)
+        if rng.random() < 0.4:
+            kw.update(top_p=1.0, top_k=int(rng.integers(1, n + 1)), min_tokens=0)
+        else:
+            kw.update(top_p=float(rng.uniform(0.3, 0.99)), top_k=0,
+                      min_tokens=int(rng.integers(0, 100)) if rng.random() < 0.5 else 0)
+        out.append(workloads.LLAMA_32K.with_(**kw))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_decode_configs(16, 2024), ids=lambda c: c.name)
+def test_random_small_layers(cfg):
+    """The whole step (index, selection, attention) on seeded random layer
+    shapes against the oracle, as the end-to-end checks do at full size."""
+    log("random layer", cfg)
+    _pipeline_check(cfg, 31, require_exact_sets=False)
+
+
 def test_runs_are_bitwise_repeatable():
     cfg = workloads.LLAMA_32K.with_(batch=2, n_ctx=9000)
     inp = workloads.decode_inputs(cfg, 4)
