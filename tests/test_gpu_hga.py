@@ -106,6 +106,45 @@ def test_route_lattice_exact(cfg, amp):
             assert np.array_equal(idx[b, g, :len(ref)], ref), (b, g)
 
 
+def _random_route_configs(count, seed):
+    """Seeded routing shapes with every knob varied: chunk and group sizes,
+    top chunks and groups, sink and local chunks, GQA group, head dim,
+    dtype and ragged contexts (including none or fewer candidates than the
+    top count)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        chunk = int(rng.choice([16, 32, 64, 128]))
+        group = chunk // int(rng.choice([g for g in (1, 2, 4, 8) if chunk // g >= 2]))
+        gpc = chunk // group
+        hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        out.append(SMALL.with_(
+            batch=int(rng.integers(1, 3)), n_q_heads=hkv * G, n_kv_heads=hkv,
+            head_dim=int(rng.choice([64, 128])), dtype=str(rng.choice(["bf16", "fp32"])),
+            n_ctx=int(rng.integers(1, 20000)), chunk=chunk, group=group,
+            top_chunks=int(rng.integers(1, 65)), top_groups=int(rng.integers(1, gpc + 1)),
+            sink_chunks=int(rng.integers(0, 7)), local_chunks=int(rng.integers(0, 11))))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_route_configs(20, 7),
+                         ids=lambda c: f"c{c.chunk}g{c.group}t{c.top_chunks}x{c.top_groups}-n{c.n_ctx}")
+def test_route_random_shapes_exact(cfg):
+    """Exact lists on lattice inputs for seeded random routing shapes."""
+    amp = 2 if cfg.n_ctx % 2 else 16
+    log("route random", cfg.n_ctx, cfg.chunk, cfg.group, cfg.top_chunks, cfg.top_groups,
+        cfg.sink_chunks, cfg.local_chunks, cfg.gqa, cfg.head_dim, cfg.dtype, amp)
+    lat = workloads.lattice_summary_inputs(cfg, 77, amp=amp, q_amp=4)
+    idx, cnt = _run_route_lattice(cfg, lat)
+    q, cs, gs = np64(lat["q"]), np64(lat["chunk_sum"]), np64(lat["group_sum"])
+    for b in range(cfg.batch):
+        for g in range(cfg.n_kv_heads):
+            ref, _ = _route_oracle(cfg, q, cs, gs, b, g)
+            assert cnt[b, g] == len(ref), (b, g, cnt[b, g], len(ref))
+            assert np.array_equal(idx[b, g, :len(ref)], ref), (b, g)
+
+
 def test_route_strict_gap_variant():
     """Lattice inputs redrawn until every chunk and group cut falls between
     scores at least 1e-3 apart (no tie decides the set)."""
