@@ -156,6 +156,38 @@ def test_prefill_end_to_end_small():
     assert worst <= 2e-4
 
 
+def _random_prefill_configs(count, seed):
+    """Seeded pyramid prefill shapes: levels 1-5 with factor 2 or 4 (a span
+    of the top level divides the 128-query block), a budget K from 1 to a
+    full list, one or two sequences and heads, and contexts that end in a
+    ragged block."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        p = int(rng.choice([2, 4]))
+        L = int(rng.integers(1, (6 if p == 2 else 4) + 1))
+        span = p ** (L - 1)
+        n = span * int(rng.integers(max(1, 130 // span), 4096 // span + 1))
+        out.append(SMALL.with_(batch=int(rng.integers(1, 3)), n_heads=int(rng.integers(1, 3)),
+                               levels=L, factor=p, n_ctx=n,
+                               block_top_k=int(rng.integers(1, 1500 if rng.random() < 0.8 else 8193))))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_prefill_configs(12, 11),
+                         ids=lambda c: f"N{c.n_ctx}-L{c.levels}-p{c.factor}-K{c.block_top_k}-B{c.batch}H{c.n_heads}")
+def test_prefill_random_shapes(cfg):
+    """Pyramid, block selection and attention on seeded random shapes: every
+    block's set exact and every output within the bf16 tolerance."""
+    log("prefill random", cfg.batch, cfg.n_heads, cfg.n_ctx, cfg.levels, cfg.factor, cfg.block_top_k)
+    inp = workloads.prefill_inputs(cfg, 5)
+    run = PrefillRun(cfg, inp)
+    run.pyramid(); run.select(); run.prefill()
+    torch.cuda.synchronize()
+    blocks = {(b, h): list(range(run.nblk)) for b in range(cfg.batch) for h in range(cfg.n_heads)}
+    assert _check_prefill(cfg, run, _np(inp), blocks) <= BF16_TOL
+
+
 def test_prefill_largest_selection():
     """block_top_k at the largest list the attention kernel stages (8192): the
     late blocks see more entries than that, so their key sequence - the
