@@ -521,12 +521,14 @@ int32_t sparse_attn_select(const sa_params* p, const sa_buffers* b, int32_t mode
     }
     a.W = W;
     a.spin_limit = select_spin_limit();
-    if (append && (per > 8 || u.G > 16)) {
-      // 4096-token tiles, or more query heads per row than one projection
-      // tile holds: the append as its own launch (the same bits)
+    const bool fuse = append && !(per > 8 && mass) && u.G <= 16;
+    if (append && !fuse) {
+      // top-p over 4096-token tiles (registers), or more query heads per row
+      // than one projection tile holds: the append as its own launch (the
+      // same bits)
       if ((st = sparse_attn_index_build(p, b, SA_IDX_LOWRANK, p->n_ctx - 1, p->n_ctx, stream))) return st;
     }
-    a.append = (append && per <= 8 && u.G <= 16) ? 1 : 0;
+    a.append = fuse ? 1 : 0;
     a.d = p->head_dim;
     a.k_pre = b->k_pre; a.q_pre = b->q_pre; a.proj_q = b->proj_q; a.proj_k = b->proj_k;
     a.q_idx_w = b->q_idx; a.k_idx_w = b->k_idx;

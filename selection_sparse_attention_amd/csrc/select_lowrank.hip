@@ -535,8 +535,9 @@ __global__ __launch_bounds__(kThreads) void select_fused_kernel(SelectArgs a) {
         kr[i].load(a.k_idx, krow + min(j0 + (i0 + i) * kThreads + tid, a.n - 1));
       if (i0 == 0) {
         bool fused = false;
-        // (4096-token tiles would spill with it: the host appends separately)
-        if constexpr (sizeof(T) == 2 && PER <= 8) {
+        // (4096-token tiles with masses would spill with it: the host
+        // appends separately there)
+        if constexpr (sizeof(T) == 2 && (PER <= 8 || !MASS)) {
           if (a.append) {
             // the projections overlap the index rows already in flight
             if (a.d == 128) fused_append<128>(a, b, g, wg, s_qrows, s_knew);
@@ -562,7 +563,7 @@ __global__ __launch_bounds__(kThreads) void select_fused_kernel(SelectArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < BATCH; ++i) {
-        if constexpr (sizeof(T) == 2 && PER <= 8) {
+        if constexpr (sizeof(T) == 2 && (PER <= 8 || !MASS)) {
           // token n - 1 under the fused append: its key from the projection
           // (the row loaded from k_idx predates it)
           if (a.append && j0 + (i0 + i) * kThreads + tid == a.n - 1) {

@@ -354,7 +354,11 @@ def test_decode_over_given_lists(cfg):
     (workloads.LLAMA_32K.with_(batch=2, n_ctx=4000), True),
     (workloads.LLAMA_32K.with_(batch=1, n_ctx=3000, head_dim=64), False),
     (workloads.LLAMA_32K.with_(batch=1, n_ctx=2049), False),
-], ids=["topp", "topk", "by-score", "per-head", "d64", "tile-edge"])
+    # 40 per-head rows of 32K: 4096-token tiles (fused for top-k, separate for top-p)
+    (workloads.LLAMA_32K.with_(batch=5, top_p=1.0, top_k=700), True),
+    (workloads.LLAMA_32K.with_(batch=5), True),
+], ids=["topp", "topk", "by-score", "per-head", "d64", "tile-edge", "wide-tiles-topk",
+        "wide-tiles-topp"])
 def test_select_fused_append_equals_separate_append(cfg, per_head):
     """Three decode steps (contexts n - 2, n - 1, n) two ways: the index
     append as its own call, then the selection; and the selection with the
