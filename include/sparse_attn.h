@@ -28,7 +28,12 @@
  *    call returns.  Its only global state is the device address of the
  *    static scratch array of sparse_attn_decode_noalloc, looked up once per
  *    device.  Calls on different streams with disjoint output and workspace
- *    buffers may run concurrently.
+ *    buffers may run concurrently, with one exception: two top-p / top-k
+ *    selections (SA_SEL_TOPP, SA_SEL_TOPK, SA_SEL_TOPK_BY_SCORE) must not
+ *    overlap on one device.  Each keeps the workgroups of a row waiting for
+ *    one another and is sized to be resident on its own; two at once can
+ *    hold every slot with half-resident rows, and their bounded waits then
+ *    end in a reported failure (sel_count -1), not a hang.
  *  - Streams: all device work is enqueued on `hip_stream` (a hipStream_t; NULL
  *    means the default stream).  No call synchronises or copies device memory
  *    to the host; data-dependent sizes (selected counts) stay on the device.
