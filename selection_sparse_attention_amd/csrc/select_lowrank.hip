@@ -990,21 +990,31 @@ hipError_t launch_select_lowrank(const SelectArgs& a, int dtype, int per, hipStr
 // kS2oMax) in visit order for the early-stop decode: index logit descending,
 // then position ascending - the ranking the cut used, with every logit
 // recomputed by the same arithmetic (so equal keys stay equal).  One
-// workgroup per row: the (key, position) pairs are bitonic-sorted in LDS.
+// workgroup per row: a stable least-significant-digit radix sort of the
+// complemented order keys in LDS, four passes of 8 bits.  The list comes in
+// ascending positions and every pass keeps the order of equal digits, so
+// equal keys end in ascending positions.  In a pass, wave w takes elements
+// [512 w, 512 w + 512) in rounds of 64: an element's rank among the wave's
+// earlier elements with its digit comes from eight ballots and a running
+// per-(wave, digit) count; the digit's offset adds every wave's count of
+// smaller digits and the earlier waves' count of its own.
 constexpr int kOrderThreads = 1024;
+constexpr int kOrderWaves = kOrderThreads / 64;
+constexpr int kOrderRounds = kS2oMax / kOrderThreads;   // rounds of 64 per wave
 
 template <typename T>
 __global__ __launch_bounds__(kOrderThreads) void select_order_kernel(SelectArgs a) {
-  __shared__ uint64_t s_key[kS2oMax];
-  const int row = blockIdx.x, tid = threadIdx.x;
+  __shared__ uint32_t s_key[2][kS2oMax];
+  __shared__ int32_t s_pos[2][kS2oMax];
+  __shared__ uint32_t s_cnt[kOrderWaves][256];
+  __shared__ uint32_t s_scan[kOrderWaves];
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   int b, g;
   row_coords(a, row, b, g);
   const int64_t orow = ((int64_t)b * a.Hkv + g) * a.n_cap;
   const int cnt = a.sel_count[(int64_t)b * a.Hkv + g];
   if (cnt <= 1) return;                        // failed (negative), empty or one token
   const int m = min(cnt, kS2oMax);
-  int P = 2;
-  while (P < m) P <<= 1;
   float qb[16];
 #pragma unroll
   for (int c = 0; c < 16; ++c) qb[c] = 0.f;
@@ -1017,36 +1027,67 @@ __global__ __launch_bounds__(kOrderThreads) void select_order_kernel(SelectArgs 
 #pragma unroll
   for (int c = 0; c < 16; ++c) qb[c] *= invG;
   const int64_t krow = (((int64_t)b * a.Hkv + g) / a.kv_div) * a.n_cap;
-  // sorted ascending on the complement: keys descending, then positions
-  // ascending; padding (all ones) goes last
-  for (int i = tid; i < P; i += kOrderThreads) {
-    uint64_t v = ~0ull;
-    if (i < m) {
-      const int j = a.sel_idx[orow + i];
-      IdxRow<T> r;
-      r.load(a.k_idx, krow + min(max(j, 0), a.n - 1));
-      float l = r.dot(qb) * 0.25f;
-      if (l == 0.f) l = 0.f;
-      v = ~(((uint64_t)order_key(l) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j));
-    }
-    s_key[i] = v;
+  for (int i = tid; i < m; i += kOrderThreads) {
+    const int j = a.sel_idx[orow + i];
+    IdxRow<T> r;
+    r.load(a.k_idx, krow + min(max(j, 0), a.n - 1));
+    float l = r.dot(qb) * 0.25f;
+    if (l == 0.f) l = 0.f;
+    s_key[0][i] = ~order_key(l);               // ascending = logit descending
+    s_pos[0][i] = j;
   }
-  __syncthreads();
-  for (int k = 2; k <= P; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < P; i += kOrderThreads) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const uint64_t x = s_key[i], y = s_key[ixj];
-          const bool up = (i & k) == 0;
-          if ((x > y) == up) { s_key[i] = y; s_key[ixj] = x; }
-        }
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int cur = 0;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 8 * pass;
+    for (int i = tid; i < kOrderWaves * 256; i += kOrderThreads) (&s_cnt[0][0])[i] = 0u;
+    __syncthreads();
+    uint32_t rank[kOrderRounds], dig[kOrderRounds];
+#pragma unroll
+    for (int it = 0; it < kOrderRounds; ++it) {
+      const int e = wid * (kOrderRounds * 64) + it * 64 + lane;
+      const bool v = e < m;
+      const uint32_t d = v ? (s_key[cur][e] >> shift) & 255u : 0u;
+      uint64_t eq = __ballot(v);                 // lanes holding the same digit
+#pragma unroll
+      for (int bit = 0; bit < 8; ++bit) {
+        const uint64_t bb = __ballot((d >> bit) & 1u);
+        eq &= ((d >> bit) & 1u) ? bb : ~bb;
       }
-      __syncthreads();
+      const uint32_t before = s_cnt[wid][d];
+      rank[it] = before + (uint32_t)__popcll(eq & lt);
+      dig[it] = d;
+      // the digit's lowest lane adds the round's count (every lane of the
+      // wave has read the old count: one read instruction for all lanes)
+      if (v && (eq & lt) == 0ull) s_cnt[wid][d] = before + (uint32_t)__popcll(eq);
     }
+    __syncthreads();
+    uint32_t tot = 0;
+    if (tid < 256) {
+      for (int w = 0; w < kOrderWaves; ++w) {
+        const uint32_t c = s_cnt[w][tid];
+        s_cnt[w][tid] = tot;
+        tot += c;
+      }
+    }
+    uint32_t total;
+    const uint32_t base = block_exclusive_scan<uint32_t, kOrderThreads>(tid < 256 ? tot : 0u, s_scan, &total);
+    if (tid < 256)
+      for (int w = 0; w < kOrderWaves; ++w) s_cnt[w][tid] += base;
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < kOrderRounds; ++it) {
+      const int e = wid * (kOrderRounds * 64) + it * 64 + lane;
+      if (e < m) {
+        const uint32_t dst = s_cnt[wid][dig[it]] + rank[it];
+        s_key[cur ^ 1][dst] = s_key[cur][e];
+        s_pos[cur ^ 1][dst] = s_pos[cur][e];
+      }
+    }
+    __syncthreads();
+    cur ^= 1;
   }
-  for (int i = tid; i < m; i += kOrderThreads)
-    a.sel_idx[orow + i] = (int32_t)(0xFFFFFFFFu - (uint32_t)(~s_key[i]));
+  for (int i = tid; i < m; i += kOrderThreads) a.sel_idx[orow + i] = s_pos[cur][i];
 }
 
 hipError_t launch_select_order(const SelectArgs& a, int dtype, hipStream_t s) {
